@@ -1,0 +1,386 @@
+"""Plain CPU oracle for the rotated W2A4 linear and the KV4 quantizer.
+
+TEST INFRASTRUCTURE. Only the tests, the smoke check and the benchmark's CPU
+baseline may import this module. It shares no code with the HIP path (its own
+Hadamard matrix, its own packers, dense matmuls instead of butterflies) and is
+deliberately slow and literal. Arithmetic is float64 except where a floating
+point value decides an integer (a code, a rounding): there both sides take the
+decision in float32, the precision of the kernels.
+
+What the method computes comes from one source, the abstract of
+"Qift: Shift-Friendly No-Zero W2 Post-Training Quantization for Rotated
+W2A4/KV4 LLM Inference" (arXiv 2606.02823, abstract page). The abstract fixes:
+
+* weights and activations pass through a Hadamard rotation before scalar
+  quantization (the "Hadamard-rotated quantization pipeline");
+* the main two-bit level set is {+-0.5, +-1.5} (half-scale {+-1, +-3}); a
+  power-of-two variant uses {+-1, +-4}, applied by sign and shift;
+* one per-output-channel scale, no zero point, no groups, no learned codebook;
+* activations are 4-bit ("W2A4") and so is the KV cache ("KV4");
+* an inner/outer level ratio between 0.25 and 0.33 works well, {+-1, +-2}
+  does not; the standard two-bit set is {-2, -1, 0, +1}.
+
+It leaves open, and this oracle takes the plainest reading of:
+
+* Hadamard kind: Sylvester order, normalized by 1/sqrt(B) per block of B;
+* activation granularity: per token, symmetric, codes in [-7, 7], round half
+  to even, s_a = absmax / 7;
+* weight scale rule: s_n = absmax_n / 1.5 (MNZ), absmax_n / 4 (PoT),
+  absmax_n / 7 (4-bit layers of a mixed stack), rounded to the stored scale
+  dtype; codes are decided against the stored scale;
+* nearest level by exhaustive comparison; ties go to the inner level and a
+  zero weight goes to the positive inner level;
+* code bits: for MNZ the 2-bit code read as a two's-complement integer t gives
+  the half-scale level 2t+1; for PoT bit 1 is the sign and bit 0 selects the
+  shift by two (level +-(1 << 2*bit0));
+* packing layouts (the ``pack*`` functions below).
+
+Parity pins: every function here is checked in ``tests/test_oracle_pins.py``
+against closed forms, brute force and the values the abstract prints. The
+end-to-end accuracy of a quantized linear against the unquantized one has no
+value on the pages: parity unpinned (reported, not asserted).
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+# ---------------------------------------------------------------------------
+# level sets (Qift abstract: the main set, its half-scale form, the PoT variant)
+# ---------------------------------------------------------------------------
+
+#: per level kind: integer level for each 2-bit code, the factor kappa that
+#: turns the integer level into a multiple of the scale, and the divisor of
+#: the absmax scale rule (the outer real level).
+LEVEL_KINDS = {
+    # code t (two's complement 2-bit) -> half-scale level 2t+1; real = level/2
+    "mnz": {"code_to_int": (1, 3, -3, -1), "kappa": 0.5, "outer": 1.5},
+    # bit1 = sign, bit0 = shift by two: +1, +4, -1, -4
+    "pot": {"code_to_int": (1, 4, -1, -4), "kappa": 1.0, "outer": 4.0},
+    # 4-bit symmetric per-channel weights of the W4 layers of a mixed stack
+    "int4": {"code_to_int": None, "kappa": 1.0, "outer": 7.0},
+}
+
+#: preference order of codes for the nearest-level rule: inner before outer,
+#: positive before negative
+_PREFERENCE = {"mnz": (0, 3, 1, 2), "pot": (0, 2, 1, 3)}
+
+
+def real_levels(kind: str) -> np.ndarray:
+    """Real levels (multiples of the scale s) indexed by 2-bit code."""
+    info = LEVEL_KINDS[kind]
+    return np.array(info["code_to_int"], dtype=np.float64) * info["kappa"]
+
+
+# ---------------------------------------------------------------------------
+# Hadamard rotation
+# ---------------------------------------------------------------------------
+
+def hadamard(B: int) -> np.ndarray:
+    """Sylvester Hadamard matrix H_B (int64), H_1 = [1],
+    H_2n = [[H_n, H_n], [H_n, -H_n]], built by Kronecker products."""
+    if B < 1 or (B & (B - 1)) != 0:
+        raise ValueError("Hadamard block must be a power of two")
+    H = np.ones((1, 1), dtype=np.int64)
+    base = np.array([[1, 1], [1, -1]], dtype=np.int64)
+    while H.shape[0] < B:
+        H = np.kron(base, H)
+    return H
+
+
+def rotate(x: np.ndarray, B: int) -> np.ndarray:
+    """Block-diagonal rotation along the last axis: each run of B consecutive
+    features is multiplied by H_B / sqrt(B). float64, dense matmul."""
+    x = np.asarray(x, dtype=np.float64)
+    K = x.shape[-1]
+    if K % B != 0:
+        raise ValueError("block must divide K")
+    Q = hadamard(B).astype(np.float64) / math.sqrt(B)
+    lead = x.shape[:-1]
+    xb = x.reshape(-1, K // B, B)
+    return (xb @ Q).reshape(*lead, K)
+
+
+# ---------------------------------------------------------------------------
+# per-token symmetric 4-bit quantization (A4 and KV4)
+# ---------------------------------------------------------------------------
+
+def quant_sym4(xr32: np.ndarray):
+    """Per row: s = float32(absmax) / float32(7); q = clip(rint(x / s), -7, 7)
+    with float32 IEEE division and round half to even. A zero row gives s = 0
+    and q = 0. Returns (q int8 [R, K], s float32 [R])."""
+    xr32 = np.asarray(xr32, dtype=np.float32)
+    R, K = xr32.shape
+    q = np.zeros((R, K), dtype=np.int8)
+    s = np.zeros(R, dtype=np.float32)
+    for r in range(R):
+        a = np.float32(np.max(np.abs(xr32[r]))) if K > 0 else np.float32(0)
+        if a == 0:
+            continue
+        sr = np.float32(a) / np.float32(7.0)
+        s[r] = sr
+        q[r] = np.clip(np.rint(xr32[r] / sr), -7, 7).astype(np.int8)
+    return q, s
+
+
+def rotate_quant_act(X: np.ndarray, B: int):
+    """Online activation path: rotate along K in blocks of B (float64), round
+    the rotated values to float32, then quantize per token to int4.
+    Returns (q int8 [M, K], s_a float32 [M], x_rot float32 [M, K],
+    x_rot64 float64 [M, K])."""
+    xr64 = rotate(X, B)
+    xr32 = xr64.astype(np.float32)
+    q, s = quant_sym4(xr32)
+    return q, s, xr32, xr64
+
+
+# ---------------------------------------------------------------------------
+# offline weight quantization
+# ---------------------------------------------------------------------------
+
+def _store_scale(s32: np.ndarray, scale_dtype: str) -> np.ndarray:
+    if scale_dtype == "f32":
+        return s32.astype(np.float32)
+    if scale_dtype == "f16":
+        return s32.astype(np.float16)
+    raise ValueError(scale_dtype)
+
+
+def weight_scales(wr32: np.ndarray, kind: str, scale_dtype: str) -> np.ndarray:
+    """s_n = float32(absmax_n) / float32(outer level), rounded to the stored
+    dtype (float16 round-to-nearest-even, or float32)."""
+    a = np.max(np.abs(wr32.astype(np.float32)), axis=1).astype(np.float32)
+    s32 = a / np.float32(LEVEL_KINDS[kind]["outer"])
+    return _store_scale(s32.astype(np.float32), scale_dtype)
+
+
+def nearest_codes(wr32: np.ndarray, s_stored: np.ndarray, kind: str) -> np.ndarray:
+    """2-bit code of each weight: the code whose level * s is closest to w,
+    found by comparing all four distances (float64, exact for float32 w and a
+    float16/float32 s). Ties go to the earlier code in the preference order
+    (inner before outer, positive before negative)."""
+    w = wr32.astype(np.float32).astype(np.float64)
+    s = s_stored.astype(np.float64)[:, None]
+    lv = real_levels(kind)
+    order = _PREFERENCE[kind]
+    d = np.stack([np.abs(w - lv[c] * s) for c in order], axis=0)
+    pick = np.argmin(d, axis=0)  # first minimum = preferred code on ties
+    return np.asarray(order, dtype=np.int64)[pick]
+
+
+def int4_weight_codes(wr32: np.ndarray, s_stored: np.ndarray) -> np.ndarray:
+    """4-bit symmetric weight codes q = clip(rint(w / s), -7, 7) in float32
+    with the stored scale; s = 0 gives q = 0."""
+    w = wr32.astype(np.float32)
+    s = s_stored.astype(np.float32)
+    q = np.zeros(w.shape, dtype=np.int64)
+    for n in range(w.shape[0]):
+        if s[n] == 0:
+            continue
+        q[n] = np.clip(np.rint(w[n] / s[n]), -7, 7).astype(np.int64)
+    return q
+
+
+def quantize_weights(W: np.ndarray, B: int, kind: str, scale_dtype: str):
+    """Offline path for one linear W [N, K]: rotate each row along K in blocks
+    of B (float64), round to float32, scale rule, nearest code.
+    Returns (codes int64 [N, K] (2-bit codes, or int4 values for 'int4'),
+    scales [N] in the stored dtype, rotated float32 weights)."""
+    wr32 = rotate(W, B).astype(np.float32)
+    s = weight_scales(wr32, kind, scale_dtype)
+    if kind == "int4":
+        codes = int4_weight_codes(wr32, s)
+    else:
+        codes = nearest_codes(wr32, s, kind)
+    return codes, s, wr32
+
+
+def code_levels(codes: np.ndarray, kind: str) -> np.ndarray:
+    """Integer level of each code (half-scale for MNZ): int64."""
+    if kind == "int4":
+        return np.asarray(codes, dtype=np.int64)
+    table = np.array(LEVEL_KINDS[kind]["code_to_int"], dtype=np.int64)
+    return table[np.asarray(codes, dtype=np.int64)]
+
+
+# ---------------------------------------------------------------------------
+# packing (the oracle's own; the layouts are part of the interface)
+# ---------------------------------------------------------------------------
+
+def bit_offset_2b(i: int) -> int:
+    """Bit offset of the code of feature k = 16*j + i inside 32-bit word j:
+    byte b = (i >> 1) & 3 holds features 2b, 2b+1, 8+2b, 9+2b at bit pairs
+    0-1, 2-3, 4-5, 6-7."""
+    return 8 * ((i >> 1) & 3) + 4 * (i >> 3) + 2 * (i & 1)
+
+
+def pack_codes2(codes: np.ndarray) -> np.ndarray:
+    """int codes in [0, 4) [N, K] -> uint32 [N, K/16]."""
+    codes = np.asarray(codes, dtype=np.uint64)
+    N, K = codes.shape
+    if K % 16:
+        raise ValueError("K must be a multiple of 16")
+    words = np.zeros((N, K // 16), dtype=np.uint64)
+    for i in range(16):
+        words |= (codes[:, i::16] & 3) << np.uint64(bit_offset_2b(i))
+    return words.astype(np.uint32)
+
+
+def unpack_codes2(words: np.ndarray) -> np.ndarray:
+    """uint32 [N, K/16] -> int64 codes [N, K]."""
+    words = np.asarray(words, dtype=np.uint64)
+    N, W = words.shape
+    codes = np.zeros((N, W * 16), dtype=np.int64)
+    for i in range(16):
+        codes[:, i::16] = ((words >> np.uint64(bit_offset_2b(i))) & np.uint64(3)).astype(np.int64)
+    return codes
+
+
+def pack_int4(q: np.ndarray) -> np.ndarray:
+    """int values in [-8, 8) [R, K] -> uint8 [R, K/2]: element 2j in the low
+    nibble of byte j, element 2j+1 in the high nibble, two's complement."""
+    q = np.asarray(q, dtype=np.int64)
+    if q.shape[-1] % 2:
+        raise ValueError("K must be even")
+    nib = (q & 0xF).astype(np.uint8)
+    return (nib[..., 0::2] | (nib[..., 1::2] << 4)).astype(np.uint8)
+
+
+def unpack_int4(b: np.ndarray) -> np.ndarray:
+    """uint8 [R, K/2] -> int64 [R, K] sign-extended."""
+    b = np.asarray(b, dtype=np.int64)
+    lo = b & 0xF
+    hi = (b >> 4) & 0xF
+    out = np.empty(b.shape[:-1] + (b.shape[-1] * 2,), dtype=np.int64)
+    out[..., 0::2] = lo
+    out[..., 1::2] = hi
+    return np.where(out >= 8, out - 16, out)
+
+
+def pack_int4_words(q: np.ndarray) -> np.ndarray:
+    """4-bit weight codes [N, K] -> uint32 [N, K/8] (the int4 byte layout read
+    as little-endian 32-bit words: element i of a word at bits 4i..4i+3)."""
+    b = pack_int4(q)
+    N = b.shape[0]
+    b = np.ascontiguousarray(b).reshape(N, -1, 4).astype(np.uint32)
+    return (b[..., 0] | (b[..., 1] << 8) | (b[..., 2] << 16) | (b[..., 3] << 24)).astype(np.uint32)
+
+
+def pack_weights(codes: np.ndarray, kind: str) -> np.ndarray:
+    return pack_int4_words(codes) if kind == "int4" else pack_codes2(codes)
+
+
+# ---------------------------------------------------------------------------
+# the linear (decoded weight application)
+# ---------------------------------------------------------------------------
+
+def int_matmul(q: np.ndarray, lv: np.ndarray) -> np.ndarray:
+    """acc[m, n] = sum_k q[m, k] * lv[n, k], exactly (int64 result). Uses a
+    float64 matmul: every term and partial sum is an integer below 2**53, so
+    the result does not depend on summation order."""
+    a = np.asarray(q, dtype=np.float64) @ np.asarray(lv, dtype=np.float64).T
+    return np.rint(a).astype(np.int64)
+
+
+def linear(q: np.ndarray, s_a: np.ndarray, codes: np.ndarray, s_w: np.ndarray, kind: str):
+    """y = x_q W_q^T with integer accumulation: acc = q . level^T, then
+    y[m, n] = acc[m, n] * s_a[m] * s_w[n] * kappa (kappa = 1/2 for the
+    half-scale MNZ levels, 1 otherwise). Returns (acc int64, y float64)."""
+    lv = code_levels(codes, kind)
+    acc = int_matmul(q, lv)
+    kappa = LEVEL_KINDS[kind]["kappa"]
+    y = acc.astype(np.float64) * np.asarray(s_a, np.float64)[:, None] \
+        * np.asarray(s_w, np.float64)[None, :] * kappa
+    return acc, y
+
+
+# ---------------------------------------------------------------------------
+# KV4
+# ---------------------------------------------------------------------------
+
+def kv4_quant(KV: np.ndarray, B: int):
+    """KV [T, H, D]: rotate each head vector by H_B / sqrt(B) (B | D), then
+    per (token, head) symmetric int4 as for activations.
+    Returns (q int8 [T, H, D], s float32 [T, H], rotated float32)."""
+    KV = np.asarray(KV, dtype=np.float64)
+    T, H, D = KV.shape
+    q, s, xr32, _ = rotate_quant_act(KV.reshape(T * H, D), B)
+    return q.reshape(T, H, D), s.reshape(T, H), xr32.reshape(T, H, D)
+
+
+# ---------------------------------------------------------------------------
+# level-set analysis on a Gaussian source (Qift abstract: ratio analysis,
+# Lloyd, the standard set and {+-1, +-2})
+# ---------------------------------------------------------------------------
+
+def _phi(x: float) -> float:
+    if math.isinf(x):
+        return 0.0
+    return math.exp(-0.5 * x * x) / math.sqrt(2.0 * math.pi)
+
+
+def _Phi(x: float) -> float:
+    if x == math.inf:
+        return 1.0
+    if x == -math.inf:
+        return 0.0
+    return 0.5 * (1.0 + math.erf(x / math.sqrt(2.0)))
+
+
+def gaussian_mse(levels, s: float = 1.0) -> float:
+    """Mean squared error of nearest-level quantization of a standard normal
+    with reconstruction points s * levels, exactly from Phi and phi: on each
+    cell [a, b] around point c, the integral of (x - c)^2 phi(x) is
+    (Phi(b) - Phi(a)) + a phi(a) - b phi(b) - 2c (phi(a) - phi(b))
+    + c^2 (Phi(b) - Phi(a))."""
+    pts = sorted(float(v) * s for v in levels)
+    edges = [-math.inf] + [(pts[i] + pts[i + 1]) / 2 for i in range(len(pts) - 1)] + [math.inf]
+    total = 0.0
+    for c, a, b in zip(pts, edges[:-1], edges[1:]):
+        P = _Phi(b) - _Phi(a)
+        aphi = 0.0 if math.isinf(a) else a * _phi(a)
+        bphi = 0.0 if math.isinf(b) else b * _phi(b)
+        total += P + aphi - bphi - 2.0 * c * (_phi(a) - _phi(b)) + c * c * P
+    return total
+
+
+def best_scale_mse(levels, lo: float = 1e-3, hi: float = 5.0):
+    """(s*, MSE(s*)) minimising gaussian_mse(levels, s) over s (bounded scalar
+    minimisation, scipy)."""
+    from scipy.optimize import minimize_scalar
+    r = minimize_scalar(lambda s: gaussian_mse(levels, s), bounds=(lo, hi),
+                        method="bounded", options={"xatol": 1e-10})
+    return float(r.x), float(r.fun)
+
+
+def lloyd_gaussian(n_levels: int = 4, iters: int = 2000, tol: float = 1e-13):
+    """Lloyd iteration on a standard normal: cells at midpoints, each point
+    moved to the conditional mean (phi(a) - phi(b)) / (Phi(b) - Phi(a)).
+    Returns the sorted reconstruction points."""
+    pts = list(np.linspace(-1.5, 1.5, n_levels))
+    for _ in range(iters):
+        edges = [-math.inf] + [(pts[i] + pts[i + 1]) / 2 for i in range(n_levels - 1)] + [math.inf]
+        new = []
+        for a, b in zip(edges[:-1], edges[1:]):
+            P = _Phi(b) - _Phi(a)
+            new.append((_phi(a) - _phi(b)) / P)
+        delta = max(abs(u - v) for u, v in zip(new, pts))
+        pts = new
+        if delta < tol:
+            break
+    return np.array(pts)
+
+
+def inner_outer_ratio(levels) -> float:
+    """min |level| / max |level| of a symmetric no-zero set."""
+    m = np.abs(np.asarray(levels, dtype=np.float64))
+    return float(m.min() / m.max())
+
+
+def excess_kurtosis(x: np.ndarray) -> np.ndarray:
+    """Per-row excess kurtosis E[(x-mu)^4]/var^2 - 3."""
+    x = np.asarray(x, dtype=np.float64)
+    d = x - x.mean(axis=-1, keepdims=True)
+    v = (d ** 2).mean(axis=-1)
+    return (d ** 4).mean(axis=-1) / (v ** 2) - 3.0

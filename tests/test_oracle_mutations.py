@@ -1,0 +1,141 @@
+"""Planted mistakes in the CPU oracle must each fail at least one pin.
+
+Each mutation replaces one piece of ``oracle.qift_oracle`` (on the CPU, via
+monkeypatch) with a plausible slip: a wrong sign or index, a dropped term, a
+transposed operand, the wrong rounding. The pins of ``test_oracle_pins.py``
+are then run; the test passes only if some pin raises.
+"""
+import math
+
+import numpy as np
+import pytest
+
+from oracle import qift_oracle as O
+import test_oracle_pins as P
+
+
+def _wrong_sign_hadamard(B):
+    H = np.ones((1, 1), dtype=np.int64)
+    base = np.array([[1, -1], [1, 1]], dtype=np.int64)
+    while H.shape[0] < B:
+        H = np.kron(base, H)
+    return H
+
+
+def _unnormalized_rotate(x, B):
+    x = np.asarray(x, dtype=np.float64)
+    K = x.shape[-1]
+    Hm = O.hadamard(B).astype(np.float64)
+    return (x.reshape(-1, K // B, B) @ Hm).reshape(x.shape)
+
+
+def _strided_blocks_rotate(x, B):
+    # blocks taken as every (K/B)-th feature instead of contiguous runs
+    x = np.asarray(x, dtype=np.float64)
+    K = x.shape[-1]
+    Q = O.hadamard(B).astype(np.float64) / math.sqrt(B)
+    xb = x.reshape(-1, B, K // B).swapaxes(1, 2)
+    return (xb @ Q).swapaxes(1, 2).reshape(x.shape)
+
+
+def _round_half_up_quant(xr32):
+    xr32 = np.asarray(xr32, dtype=np.float32)
+    R, K = xr32.shape
+    q = np.zeros((R, K), dtype=np.int8)
+    s = np.zeros(R, dtype=np.float32)
+    for r in range(R):
+        a = np.float32(np.max(np.abs(xr32[r])))
+        if a == 0:
+            continue
+        s[r] = a / np.float32(7)
+        q[r] = np.clip(np.floor(xr32[r] / s[r] + np.float32(0.5)), -7, 7)
+    return q, s
+
+
+def _wrong_divisor_quant(xr32):
+    xr32 = np.asarray(xr32, dtype=np.float32)
+    R, K = xr32.shape
+    q = np.zeros((R, K), dtype=np.int8)
+    s = np.zeros(R, dtype=np.float32)
+    for r in range(R):
+        a = np.float32(np.max(np.abs(xr32[r])))
+        if a == 0:
+            continue
+        s[r] = a / np.float32(8)
+        q[r] = np.clip(np.rint(xr32[r] / s[r]), -7, 7)
+    return q, s
+
+
+def _transposed_int_matmul(q, lv):
+    a = np.asarray(q, dtype=np.float64) @ np.asarray(lv, dtype=np.float64)
+    return np.rint(a).astype(np.int64)
+
+
+def _natural_bit_offset(i):
+    return 2 * i
+
+
+def _swapped_pack_int4(q):
+    q = np.asarray(q, dtype=np.int64)
+    nib = (q & 0xF).astype(np.uint8)
+    return (nib[..., 1::2] | (nib[..., 0::2] << 4)).astype(np.uint8)
+
+
+def _gaussian_mse_cross_term_sign(levels, s=1.0):
+    pts = sorted(float(v) * s for v in levels)
+    edges = [-math.inf] + [(pts[i] + pts[i + 1]) / 2 for i in range(len(pts) - 1)] + [math.inf]
+    total = 0.0
+    for c, a, b in zip(pts, edges[:-1], edges[1:]):
+        P_ = O._Phi(b) - O._Phi(a)
+        aphi = 0.0 if math.isinf(a) else a * O._phi(a)
+        bphi = 0.0 if math.isinf(b) else b * O._phi(b)
+        total += P_ + aphi - bphi + 2.0 * c * (O._phi(a) - O._phi(b)) + c * c * P_
+    return total
+
+
+def _lloyd_wrong_centroid(n_levels=4, iters=2000, tol=1e-13):
+    pts = list(np.linspace(-1.5, 1.5, n_levels))
+    for _ in range(iters):
+        edges = [-math.inf] + [(pts[i] + pts[i + 1]) / 2 for i in range(n_levels - 1)] + [math.inf]
+        new = [(O._phi(a) - O._phi(b)) for a, b in zip(edges[:-1], edges[1:])]
+        pts = new
+    return np.array(pts)
+
+
+def _kinds_with(kind, **over):
+    d = {k: dict(v) for k, v in O.LEVEL_KINDS.items()}
+    d[kind].update(over)
+    return d
+
+
+MUTATIONS = {
+    "hadamard_wrong_sign": [("hadamard", _wrong_sign_hadamard)],
+    "rotate_unnormalized": [("rotate", _unnormalized_rotate)],
+    "rotate_strided_blocks": [("rotate", _strided_blocks_rotate)],
+    "act_round_half_up": [("quant_sym4", _round_half_up_quant)],
+    "act_divisor_8": [("quant_sym4", _wrong_divisor_quant)],
+    "ties_to_outer": [("_PREFERENCE", {"mnz": (1, 2, 0, 3), "pot": (1, 3, 0, 2)})],
+    "ties_to_negative": [("_PREFERENCE", {"mnz": (3, 0, 2, 1), "pot": (2, 0, 3, 1)})],
+    "pot_shift_sign_swapped": [("LEVEL_KINDS", _kinds_with("pot", code_to_int=(1, -4, -1, 4)))],
+    "mnz_sorted_mapping": [("LEVEL_KINDS", _kinds_with("mnz", code_to_int=(-3, -1, 1, 3)))],
+    "mnz_kappa_dropped": [("LEVEL_KINDS", _kinds_with("mnz", kappa=1.0))],
+    "mnz_scale_divisor_2": [("LEVEL_KINDS", _kinds_with("mnz", outer=2.0))],
+    "matmul_transposed": [("int_matmul", _transposed_int_matmul)],
+    "pack2_natural_order": [("bit_offset_2b", _natural_bit_offset)],
+    "pack4_nibbles_swapped": [("pack_int4", _swapped_pack_int4)],
+    "mse_cross_term_sign": [("gaussian_mse", _gaussian_mse_cross_term_sign)],
+    "lloyd_unnormalized_centroid": [("lloyd_gaussian", _lloyd_wrong_centroid)],
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_mutation_is_caught(name, monkeypatch):
+    for attr, repl in MUTATIONS[name]:
+        monkeypatch.setattr(O, attr, repl)
+    caught = []
+    for pin in P.ALL_PINS:
+        try:
+            pin()
+        except Exception as e:  # an assertion, or a shape error from a transposed operand
+            caught.append((pin.__name__, type(e).__name__))
+    assert caught, f"mutation {name} passed every pin"

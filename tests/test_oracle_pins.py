@@ -1,0 +1,586 @@
+"""Pins of the CPU oracle against what the pages and the mathematics fix.
+
+Every check here is independent of the oracle's own code path: closed forms,
+brute force, an independent butterfly transform, Monte Carlo, hand-worked
+fixtures under ``tests/golden/`` (each carries its citation), and the level
+sets printed in the Qift abstract. ``test_oracle_mutations.py`` plants
+mistakes in the oracle and checks that these pins catch each one.
+"""
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+from oracle import qift_oracle as O
+import synth_inputs as si
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+def popcount(v):
+    return bin(v).count("1")
+
+
+def butterfly_fwht(x):
+    """Independent in-place Walsh-Hadamard butterflies (natural order),
+    normalized by 1/sqrt(B); x [R, B]."""
+    y = np.array(x, dtype=np.float64, copy=True)
+    B = y.shape[-1]
+    h = 1
+    while h < B:
+        for i in range(0, B, 2 * h):
+            a = y[..., i:i + h].copy()
+            b = y[..., i + h:i + 2 * h].copy()
+            y[..., i:i + h] = a + b
+            y[..., i + h:i + 2 * h] = a - b
+        h *= 2
+    return y / math.sqrt(B)
+
+
+# --------------------------------------------------------------------------
+# Hadamard and rotation
+# --------------------------------------------------------------------------
+
+def pin_hadamard_orthogonal():
+    for b in range(0, 13):
+        B = 1 << b
+        H = O.hadamard(B)
+        assert H.shape == (B, B)
+        if B <= 512:
+            G = H.astype(np.int64) @ H.T.astype(np.int64)
+        else:  # exact in float64: entries +-1, sums <= 4096
+            Hf = H.astype(np.float64)
+            G = np.rint(Hf @ Hf.T).astype(np.int64)
+        assert np.array_equal(G, B * np.eye(B, dtype=np.int64)), B
+
+
+def pin_hadamard_entries():
+    for B in (1, 2, 4, 8, 16, 64, 256):
+        H = O.hadamard(B)
+        ref = np.array([[(-1) ** popcount(i & j) for j in range(B)] for i in range(B)])
+        assert np.array_equal(H, ref), B
+
+
+def pin_rotation_is_butterfly():
+    rng = np.random.default_rng(11)
+    for B in (1, 2, 8, 128, 256, 1024):
+        x = rng.standard_normal((3, 4 * B))
+        got = O.rotate(x, B)
+        ref = np.concatenate([butterfly_fwht(x[:, j * B:(j + 1) * B]) for j in range(4)], axis=1)
+        assert np.max(np.abs(got - ref)) <= 1e-12 * max(1.0, np.max(np.abs(ref))), B
+
+
+def pin_rotation_orthogonal():
+    rng = np.random.default_rng(12)
+    for B in (2, 16, 128, 256, 4096):
+        K = max(B, 256) * 2
+        x = rng.standard_normal((5, K))
+        w = rng.standard_normal((7, K))
+        xr = O.rotate(x, B)
+        assert np.allclose(O.rotate(xr, B), x, rtol=0, atol=1e-12)
+        assert np.allclose(np.linalg.norm(xr, axis=1), np.linalg.norm(x, axis=1), rtol=1e-13)
+        y0 = x @ w.T
+        y1 = xr @ O.rotate(w, B).T
+        assert np.max(np.abs(y1 - y0)) <= 1e-12 * np.max(np.abs(y0)) * K
+
+
+def test_hadamard_orthogonal():
+    pin_hadamard_orthogonal()
+
+
+def test_hadamard_entries():
+    pin_hadamard_entries()
+
+
+def test_rotation_is_butterfly():
+    pin_rotation_is_butterfly()
+
+
+def test_rotation_orthogonal():
+    pin_rotation_orthogonal()
+
+
+def test_rotation_gaussianizes_heavy_tails():
+    """Abstract: rotation mainly Gaussianizes the standardized weight shape
+    (excess kurtosis drops by orders of magnitude). Synthetic analogue:
+    Student-t rows (infinite-variance tails cut by sampling) lose almost all
+    excess kurtosis after a 256-block rotation."""
+    W = si.heavy_tailed_weights(64, 4096, seed=5, dof=4.0).astype(np.float64)
+    k0 = np.median(O.excess_kurtosis(W))
+    k1 = np.median(np.abs(O.excess_kurtosis(O.rotate(W, 4096))))
+    assert k0 > 1.0
+    assert k1 < 0.2 and k1 < k0 / 10
+
+
+# --------------------------------------------------------------------------
+# A4 activations
+# --------------------------------------------------------------------------
+
+def pin_activation_closed_form():
+    """x = c * e_j: every rotated value in j's block is +-c/sqrt(B), so the
+    codes are +-7 with sign (-1)^popcount(i & j) and zero elsewhere."""
+    for B, j, c in ((256, 37, 3.25), (128, 5, -2.0), (4096, 4000, 0.75), (16, 3, 100.0)):
+        K = 2 * B
+        x = np.zeros((1, K))
+        x[0, B + j] = c
+        q, s, xr32, _ = O.rotate_quant_act(x, B)
+        a = np.float32(abs(c) / math.sqrt(B))
+        assert s[0] == np.float32(a) / np.float32(7)
+        expect = np.zeros(K, dtype=np.int64)
+        for i in range(B):
+            expect[B + i] = 7 * (1 if c > 0 else -1) * (-1) ** popcount(i & j)
+        assert np.array_equal(q[0].astype(np.int64), expect), (B, j)
+
+
+def pin_rne_ties():
+    g = golden("rne_ties.json")
+    x = np.array([g["row"]])
+    q, s, _, _ = O.rotate_quant_act(x, g["had_block"])
+    assert s[0] == np.float32(g["scale"])
+    assert q[0].tolist() == g["codes"]
+
+
+def pin_zero_row():
+    q, s, _, _ = O.rotate_quant_act(np.zeros((2, 64)), 64)
+    assert np.all(q == 0) and np.all(s == 0)
+
+
+def pin_act_range_and_error():
+    """Codes lie in [-7, 7], the absmax element maps to +-7 and the
+    dequantized row is within s/2 of the rotated row everywhere."""
+    X = si.activations(8, 512, seed=3)
+    q, s, xr32, _ = O.rotate_quant_act(X.astype(np.float64), 256)
+    assert q.min() >= -7 and q.max() <= 7
+    for r in range(8):
+        i = np.argmax(np.abs(xr32[r]))
+        assert abs(int(q[r, i])) == 7
+        err = np.abs(q[r].astype(np.float64) * float(s[r]) - xr32[r].astype(np.float64))
+        assert err.max() <= 0.5 * float(s[r]) * (1 + 1e-6)
+
+
+def test_activation_closed_form():
+    pin_activation_closed_form()
+
+
+def test_rne_ties():
+    pin_rne_ties()
+
+
+def test_zero_row():
+    pin_zero_row()
+
+
+def test_act_range_and_error():
+    pin_act_range_and_error()
+
+
+# --------------------------------------------------------------------------
+# weights: level sets, nearest level, scale rule
+# --------------------------------------------------------------------------
+
+def pin_level_sets_match_page():
+    g = golden("level_sets.json")
+    assert sorted(O.real_levels("mnz").tolist()) == g["mnz"]
+    assert sorted(O.LEVEL_KINDS["mnz"]["code_to_int"]) == g["mnz_half_scale"]
+    assert sorted(O.real_levels("pot").tolist()) == g["pot"]
+    # half-scale reparameterization: integer level * kappa = real level
+    assert np.allclose(np.array(O.LEVEL_KINDS["mnz"]["code_to_int"]) * O.LEVEL_KINDS["mnz"]["kappa"],
+                       O.real_levels("mnz"))
+    # MNZ code read as 2-bit two's complement t gives half-scale level 2t+1
+    for c in range(4):
+        t = c - 4 if c >= 2 else c
+        assert O.code_levels(np.array([c]), "mnz")[0] == 2 * t + 1
+    # PoT sign-and-shift decode: bit1 = sign, bit0 = shift by two
+    for c in range(4):
+        sign = -1 if (c >> 1) & 1 else 1
+        assert O.code_levels(np.array([c]), "pot")[0] == sign * (1 << (2 * (c & 1)))
+
+
+def pin_level_ratios():
+    g = golden("level_sets.json")
+    lo, hi = g["effective_ratio_range"]
+    r_mnz = O.inner_outer_ratio(g["mnz"])
+    r_pot = O.inner_outer_ratio(g["pot"])
+    r_ctl = O.inner_outer_ratio(g["control_pm1_pm2"])
+    assert r_mnz == pytest.approx(1 / 3, abs=1e-15)
+    assert r_pot == pytest.approx(1 / 4, abs=1e-15)
+    # 0.33 read as a rounded 1/3
+    assert lo <= r_pot <= round(hi, 2) + 0.005 and lo <= r_mnz <= round(hi, 2) + 0.005
+    assert not (lo <= r_ctl <= hi + 0.005)
+
+
+def pin_weight_ties():
+    g = golden("weight_ties.json")
+    for kind in ("mnz", "pot"):
+        row = np.array([g[kind]["row"]], dtype=np.float32)
+        codes, s, _ = O.quantize_weights(row.astype(np.float64), 1, kind, "f32")
+        assert s[0] == np.float32(g[kind]["scale"]), kind
+        assert codes[0].tolist() == g[kind]["codes"], kind
+        codes16, s16, _ = O.quantize_weights(row.astype(np.float64), 1, kind, "f16")
+        assert s16.dtype == np.float16 and codes16[0].tolist() == g[kind]["codes"]
+
+
+def pin_nearest_level_brute_force():
+    """Exhaustive search over all 4^n code vectors of tiny rows (n = 4) for
+    the minimum total squared error; the oracle's codes must be one of the
+    minimizers, and must be the tie-rule choice where several exist."""
+    rng = np.random.default_rng(21)
+    for kind in ("mnz", "pot"):
+        lv = O.real_levels(kind)
+        inner = np.abs(lv).min()
+        for trial in range(60):
+            s = np.float32(rng.choice([1.0, 0.75, 0.015625, 3.0]))
+            # mixture of random values and exact midpoints / zeros
+            mids = [0.0, -0.0, s * (inner + np.abs(lv).max()) / 2, -s * (inner + np.abs(lv).max()) / 2]
+            w = rng.normal(0, float(s), 4).astype(np.float32)
+            for i in range(4):
+                if rng.random() < 0.4:
+                    w[i] = np.float32(rng.choice(mids))
+            got = O.nearest_codes(w[None, :], np.array([s], np.float32), kind)[0]
+            best, minimizers = None, []
+            for combo in itertools.product(range(4), repeat=4):
+                e = sum((float(w[i]) - lv[c] * float(s)) ** 2 for i, c in enumerate(combo))
+                if best is None or e < best - 1e-300:
+                    if best is None or e < best:
+                        best, minimizers = e, [combo]
+                elif e == best:
+                    minimizers.append(combo)
+            assert tuple(got) in minimizers, (kind, w, s, got, minimizers)
+            # tie rule, element-wise: the chosen level has the smallest
+            # magnitude among equally near levels, and is positive at w = 0
+            for i in range(4):
+                d = np.abs(float(w[i]) - lv * float(s))
+                near = [c for c in range(4) if d[c] == d.min()]
+                chosen = got[i]
+                assert chosen in near
+                assert abs(lv[chosen]) == min(abs(lv[c]) for c in near)
+                if float(w[i]) == 0.0:
+                    assert lv[chosen] > 0
+
+
+def pin_threshold_rule():
+    """Equivalent threshold form of the nearest level: MNZ outer iff |w| > s;
+    PoT outer iff 2|w| > 5s (exact); sign from w < 0."""
+    rng = np.random.default_rng(22)
+    w = (rng.normal(0, 1, (40, 64))).astype(np.float32)
+    s = np.abs(rng.normal(0.7, 0.2, 40)).astype(np.float16)
+    for kind, outer_if in (("mnz", lambda a, sv: a > sv), ("pot", lambda a, sv: 2 * a > 5 * sv)):
+        codes = O.nearest_codes(w, s, kind)
+        lv = O.code_levels(codes, kind)
+        a = np.abs(w.astype(np.float64))
+        sv = s.astype(np.float64)[:, None]
+        outer = outer_if(a, sv)
+        mag_outer = {"mnz": 3, "pot": 4}[kind]
+        assert np.array_equal(np.abs(lv) == mag_outer, outer)
+        neg = w < 0
+        assert np.array_equal(lv < 0, neg)
+
+
+def pin_constant_row():
+    """A constant row c*1 rotates to c*sqrt(B) at each block's first feature
+    and exactly 0 elsewhere (c a power of two keeps every partial sum exact):
+    leading features get the outer level with the sign of c, all others the
+    positive inner level."""
+    for kind, outer_code_pos, outer_code_neg in (("mnz", 1, 2), ("pot", 1, 3)):
+        for c in (0.25, -0.5):
+            W = np.full((2, 512), c)
+            codes, s, wr = O.quantize_weights(W, 256, kind, "f16")
+            for b in range(2):
+                assert codes[0, 256 * b] == (outer_code_pos if c > 0 else outer_code_neg)
+                assert np.all(codes[0, 256 * b + 1:256 * (b + 1)] == 0)
+
+
+def pin_scale_rule():
+    W = si.weights(16, 256, seed=4)
+    for kind, outer in (("mnz", 1.5), ("pot", 4.0), ("int4", 7.0)):
+        codes, s, wr = O.quantize_weights(W.astype(np.float64), 256, kind, "f16")
+        a = np.max(np.abs(O.rotate(W.astype(np.float64), 256)), axis=1)
+        assert np.allclose(s.astype(np.float64), a / outer, rtol=1e-3)
+        lv = O.code_levels(codes, kind)
+        # the element holding the absmax lands on the outer level
+        for n in range(16):
+            i = np.argmax(np.abs(wr[n]))
+            assert abs(lv[n, i]) == {"mnz": 3, "pot": 4, "int4": 7}[kind]
+
+
+def pin_int4_weights():
+    rng = np.random.default_rng(23)
+    w = rng.normal(0, 0.02, (6, 64)).astype(np.float32)
+    codes, s, wr = O.quantize_weights(w.astype(np.float64), 1, "int4", "f32")
+    assert codes.min() >= -7 and codes.max() <= 7
+    for n in range(6):
+        err = np.abs(codes[n] * float(s[n]) - wr[n].astype(np.float64))
+        assert err.max() <= 0.5 * float(s[n]) * (1 + 1e-6)
+
+
+def test_level_sets_match_page():
+    pin_level_sets_match_page()
+
+
+def test_level_ratios():
+    pin_level_ratios()
+
+
+def test_weight_ties():
+    pin_weight_ties()
+
+
+def test_nearest_level_brute_force():
+    pin_nearest_level_brute_force()
+
+
+def test_threshold_rule():
+    pin_threshold_rule()
+
+
+def test_constant_row():
+    pin_constant_row()
+
+
+def test_scale_rule():
+    pin_scale_rule()
+
+
+def test_int4_weights():
+    pin_int4_weights()
+
+
+# --------------------------------------------------------------------------
+# Gaussian analysis: MSE ordering, Lloyd, ratio curve
+# --------------------------------------------------------------------------
+
+def pin_gaussian_mse_monte_carlo():
+    rng = np.random.default_rng(31)
+    x = rng.standard_normal(2_000_000)
+    for levels, s in (([-1.5, -0.5, 0.5, 1.5], 0.9), ([-4, -1, 1, 4], 0.4), ([-2, -1, 0, 1], 1.1)):
+        pts = np.sort(np.array(levels, float) * s)
+        idx = np.argmin(np.abs(x[:, None] - pts[None, :]), axis=1)
+        mc = np.mean((x - pts[idx]) ** 2)
+        assert O.gaussian_mse(levels, s) == pytest.approx(mc, rel=5e-3)
+
+
+def pin_gaussian_mse_closed_forms():
+    g = golden("gaussian_max_quantizer.json")
+    # two-level optimum +-sqrt(2/pi): MSE = 1 - 2/pi
+    c = math.sqrt(2 / math.pi)
+    assert O.gaussian_mse([-c, c]) == pytest.approx(1 - 2 / math.pi, abs=1e-12)
+    assert O.gaussian_mse(g["n2_output_levels"]) == pytest.approx(g["n2_mse"], abs=g["tolerance"])
+    assert O.gaussian_mse(g["n4_output_levels"]) == pytest.approx(g["n4_mse"], abs=g["tolerance"])
+    # a single level at 0 gives the variance
+    assert O.gaussian_mse([0.0]) == pytest.approx(1.0, abs=1e-12)
+
+
+def pin_mse_ordering():
+    """Abstract: the no-zero sets beat the standard {-2,-1,0,1} set; the
+    scale-invariant analysis compares each set at its best scale."""
+    g = golden("level_sets.json")
+    m = {k: O.best_scale_mse(g[k])[1] for k in ("mnz", "pot", "standard_w2", "control_pm1_pm2")}
+    assert m["mnz"] < m["standard_w2"]
+    assert m["pot"] < m["standard_w2"]
+    assert m["mnz"] < m["control_pm1_pm2"] and m["pot"] < m["control_pm1_pm2"]
+    assert m["mnz"] == pytest.approx(0.11885, abs=1e-4)
+    assert m["pot"] == pytest.approx(0.12049, abs=1e-4)
+    assert m["standard_w2"] == pytest.approx(0.14943, abs=1e-4)
+
+
+def pin_lloyd():
+    g = golden("gaussian_max_quantizer.json")
+    pts = O.lloyd_gaussian(4)
+    assert np.allclose(pts, g["n4_output_levels"], atol=g["tolerance"])
+    r = O.inner_outer_ratio(pts)
+    lo, hi = golden("level_sets.json")["effective_ratio_range"]
+    assert lo <= r <= 1 / 3 and abs(r - 0.30) < 0.005
+    assert O.gaussian_mse(pts) == pytest.approx(g["n4_mse"], abs=g["tolerance"])
+
+
+def pin_ratio_curve():
+    rs = np.linspace(0.15, 0.6, 91)
+    mse = [O.best_scale_mse([-1, -r, r, 1])[1] for r in rs]
+    r_best = rs[int(np.argmin(mse))]
+    assert 0.28 <= r_best <= 0.32
+    assert O.best_scale_mse([-1, -0.5, 0.5, 1])[1] > O.best_scale_mse([-1, -1 / 3, 1 / 3, 1])[1]
+
+
+def test_gaussian_mse_monte_carlo():
+    pin_gaussian_mse_monte_carlo()
+
+
+def test_gaussian_mse_closed_forms():
+    pin_gaussian_mse_closed_forms()
+
+
+def test_mse_ordering():
+    pin_mse_ordering()
+
+
+def test_lloyd():
+    pin_lloyd()
+
+
+def test_ratio_curve():
+    pin_ratio_curve()
+
+
+# --------------------------------------------------------------------------
+# packing
+# --------------------------------------------------------------------------
+
+def pin_packing_fixture():
+    g = golden("packing.json")
+    for case in g["codes2"]:
+        w = O.pack_codes2(np.array([case["codes"]]))
+        assert w.dtype == np.uint32 and int(w[0, 0]) == int(case["word"], 16), case
+        assert O.unpack_codes2(w)[0].tolist() == case["codes"]
+    for case in g["int4"]:
+        b = O.pack_int4(np.array([case["values"]]))
+        assert [int(v) for v in b[0]] == [int(h, 16) for h in case["bytes"]]
+        assert O.unpack_int4(b)[0].tolist() == case["values"]
+
+
+def pin_packing_roundtrip():
+    c = si.uniform_codes((5, 96), 4, seed=1)
+    assert np.array_equal(O.unpack_codes2(O.pack_codes2(c)), c)
+    q = si.uniform_int4((5, 96), seed=2, lo=-8, hi=7)
+    assert np.array_equal(O.unpack_int4(O.pack_int4(q)), q)
+    words = O.pack_int4_words(q)
+    assert words.shape == (5, 12)
+    assert np.array_equal(words.view(np.uint8).reshape(5, 48), O.pack_int4(q))
+
+
+def test_packing_fixture():
+    pin_packing_fixture()
+
+
+def test_packing_roundtrip():
+    pin_packing_roundtrip()
+
+
+# --------------------------------------------------------------------------
+# the linear
+# --------------------------------------------------------------------------
+
+def pin_linear_hand_example():
+    # q = [7, -3]; MNZ codes [1, 3] -> half-scale levels [3, -1]; acc = 24
+    # y = 24 * s_a * s_w * 1/2
+    acc, y = O.linear(np.array([[7, -3]]), np.array([0.5]), np.array([[1, 3]]), np.array([2.0]), "mnz")
+    assert acc[0, 0] == 24 and y[0, 0] == 12.0
+    # PoT: codes [1, 2] -> [4, -1]; acc = 28 + 3 = 31; kappa = 1
+    acc, y = O.linear(np.array([[7, -3]]), np.array([0.5]), np.array([[1, 2]]), np.array([2.0]), "pot")
+    assert acc[0, 0] == 31 and y[0, 0] == 31.0
+    # int4: levels are the values
+    acc, y = O.linear(np.array([[7, -3]]), np.array([1.0]), np.array([[-7, 5]]), np.array([0.25]), "int4")
+    assert acc[0, 0] == -64 and y[0, 0] == -16.0
+
+
+def pin_linear_brute_force():
+    rng = np.random.default_rng(41)
+    for kind in ("mnz", "pot", "int4"):
+        M, N, K = 3, 5, 32
+        q = rng.integers(-7, 8, (M, K))
+        codes = rng.integers(-7, 8, (N, K)) if kind == "int4" else rng.integers(0, 4, (N, K))
+        s_a = rng.uniform(0.1, 1, M)
+        s_w = rng.uniform(0.1, 1, N)
+        acc, y = O.linear(q, s_a, codes, s_w, kind)
+        table = {"mnz": {0: 1, 1: 3, 2: -3, 3: -1}, "pot": {0: 1, 1: 4, 2: -1, 3: -4}}
+        for m in range(M):
+            for n in range(N):
+                tot = 0
+                for k in range(K):
+                    lvl = int(codes[n, k]) if kind == "int4" else table[kind][int(codes[n, k])]
+                    tot += int(q[m, k]) * lvl
+                assert acc[m, n] == tot
+                kappa = 0.5 if kind == "mnz" else 1.0
+                assert y[m, n] == pytest.approx(tot * s_a[m] * s_w[n] * kappa, rel=1e-15)
+
+
+def pin_accumulator_bound():
+    K = 14336
+    q = np.full((1, K), 7)
+    codes = np.full((1, K), 1)  # +3 (MNZ) / +4 (PoT)
+    acc, _ = O.linear(q, np.ones(1), codes, np.ones(1), "mnz")
+    assert acc[0, 0] == 7 * 3 * K
+    acc, _ = O.linear(q, np.ones(1), codes, np.ones(1), "pot")
+    assert acc[0, 0] == 7 * 4 * K and acc[0, 0] < 2 ** 31
+
+
+def pin_end_to_end_function_preserving():
+    """With float64 weights and activations (no quantization) the rotated
+    product equals x W^T; quantizing adds error bounded by the codes."""
+    W, X, _ = si.small_linear_case()
+    Xd, Wd = X.astype(np.float64), W.astype(np.float64)
+    y0 = Xd @ Wd.T
+    y1 = O.rotate(Xd, 256) @ O.rotate(Wd, 256).T
+    assert np.max(np.abs(y1 - y0)) < 1e-12
+
+
+def test_linear_hand_example():
+    pin_linear_hand_example()
+
+
+def test_linear_brute_force():
+    pin_linear_brute_force()
+
+
+def test_accumulator_bound():
+    pin_accumulator_bound()
+
+
+def test_end_to_end_function_preserving():
+    pin_end_to_end_function_preserving()
+
+
+def test_end_to_end_small_case_informational():
+    """Relative L2 of the W2A4 output against x W^T on the CPU-sized case.
+    No value is printed on the pages: parity unpinned; checked only for
+    sanity (rotation must not make it worse)."""
+    W, X, _ = si.small_linear_case()
+    Xd, Wd = X.astype(np.float64), W.astype(np.float64)
+    yref = Xd @ Wd.T
+
+    def rel(B):
+        q, s_a, _, _ = O.rotate_quant_act(Xd, B)
+        codes, s_w, _ = O.quantize_weights(Wd, B, "mnz", "f32")
+        _, y = O.linear(q, s_a, codes, s_w, "mnz")
+        return np.linalg.norm(y - yref) / np.linalg.norm(yref)
+
+    r_rot, r_none = rel(256), rel(1)
+    assert r_rot < r_none < 1.5
+
+
+# --------------------------------------------------------------------------
+# KV4
+# --------------------------------------------------------------------------
+
+def pin_kv4():
+    KV = si.kv(6, 4, 128, seed=9).astype(np.float64)
+    q, s, xr = O.kv4_quant(KV, 128)
+    assert q.shape == (6, 4, 128) and s.shape == (6, 4)
+    for t in range(6):
+        for h in range(4):
+            ref = butterfly_fwht(KV[t, h][None, :])[0]
+            assert np.allclose(xr[t, h], ref.astype(np.float32), rtol=0, atol=1e-6)
+            a = np.float32(np.max(np.abs(xr[t, h])))
+            assert s[t, h] == a / np.float32(7)
+            assert np.max(np.abs(q[t, h])) == 7
+    # closed form: one-hot head vector
+    KV = np.zeros((1, 2, 128))
+    KV[0, 1, 9] = -4.0
+    q, s, _ = O.kv4_quant(KV, 128)
+    assert np.all(q[0, 0] == 0) and s[0, 0] == 0
+    expect = [-7 * (-1) ** popcount(i & 9) for i in range(128)]
+    assert q[0, 1].tolist() == expect
+
+
+def test_kv4():
+    pin_kv4()
+
+
+ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]
