@@ -1,0 +1,286 @@
+"""Python binding of libqift.so: the rotated W2A4 linear and KV4 on MI355X.
+
+The functions keep the names of the C ABI (``include/qift.h``) and do
+argument marshalling only: every step of the computation runs in the HIP
+kernels of ``libqift.so``. PyTorch provides device memory and the stream;
+outputs are allocated with ``torch.empty`` on the input's device unless the
+caller passes them. There is no fallback path: if the library has not been
+built (``python -m bit_quantized_fwht_amd.build``) every call raises
+``QiftUnavailable``, and every call raises ``QiftError`` on a non-OK status.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libqift.so")
+
+# enums (qift.h)
+QIFT_OK, QIFT_ERR_INVALID_ARG, QIFT_ERR_ALIGNMENT, QIFT_ERR_UNSUPPORTED, QIFT_ERR_HIP = range(5)
+QIFT_F32, QIFT_BF16, QIFT_F16, QIFT_I32 = range(4)
+LEVELS = {"mnz": 0, "pot": 1, "int4": 2}
+QIFT_MAX_ROW = 16384
+QIFT_MAX_HAD_BLOCK = 4096
+
+_TORCH_TO_QIFT = {torch.float32: QIFT_F32, torch.bfloat16: QIFT_BF16,
+                  torch.float16: QIFT_F16, torch.int32: QIFT_I32}
+
+
+class QiftError(RuntimeError):
+    def __init__(self, status: int, where: str, detail: str):
+        super().__init__(f"{where}: {status_string(status)}: {detail}")
+        self.status = status
+
+
+class QiftUnavailable(ImportError):
+    pass
+
+
+class qift_linear_desc(ctypes.Structure):
+    _fields_ = [("xq", ctypes.c_void_p), ("s_a", ctypes.c_void_p), ("codes", ctypes.c_void_p),
+                ("scales", ctypes.c_void_p), ("Y", ctypes.c_void_p), ("M", ctypes.c_int64),
+                ("K", ctypes.c_int64), ("N", ctypes.c_int64), ("levels", ctypes.c_int32),
+                ("reserved", ctypes.c_int32)]
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise QiftUnavailable(f"{LIB_PATH} is not built; run `python -m bit_quantized_fwht_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    c_st = ctypes.c_int
+    vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32
+    sig = {
+        "qift_quantize_weights": [vp, c_st, i64, i64, i32, c_st, vp, vp, c_st, vp],
+        "qift_rotate_quant_act": [vp, c_st, i64, i64, i32, vp, vp, vp, vp],
+        "qift_w2a4_linear": [vp, vp, i64, i64, vp, vp, c_st, c_st, i64, vp, c_st, vp],
+        "qift_kv4_quant": [vp, c_st, i64, i64, i64, i32, vp, vp, vp],
+        "qift_linear_group_workspace_bytes": [vp, i32, ctypes.POINTER(ctypes.c_size_t)],
+        "qift_linear_group_prepare": [vp, i32, c_st, c_st, vp, ctypes.c_size_t,
+                                      ctypes.POINTER(ctypes.c_int64), vp],
+        "qift_w2a4_linear_grouped": [vp, i64, vp],
+    }
+    for name, args in sig.items():
+        f = getattr(lib, name)
+        f.argtypes = args
+        f.restype = c_st
+    lib.qift_status_string.argtypes = [c_st]
+    lib.qift_status_string.restype = ctypes.c_char_p
+    lib.qift_last_error.argtypes = []
+    lib.qift_last_error.restype = ctypes.c_char_p
+    lib.qift_abi_version.argtypes = []
+    lib.qift_abi_version.restype = ctypes.c_int32
+    return lib
+
+
+class _Lib:
+    """libqift.so, loaded on first use; raises QiftUnavailable if missing."""
+
+    def __init__(self):
+        self._lib = None
+
+    def __getattr__(self, name):
+        if self._lib is None:
+            self._lib = _load()
+        return getattr(self._lib, name)
+
+    def handle(self):
+        if self._lib is None:
+            self._lib = _load()
+        return self._lib
+
+
+_C = _Lib()
+
+
+def load_library():
+    """Load libqift.so now (raises QiftUnavailable if it is not built)."""
+    return _C.handle()
+
+
+def status_string(status: int) -> str:
+    return _C.qift_status_string(status).decode()
+
+
+def last_error() -> str:
+    return _C.qift_last_error().decode()
+
+
+def abi_version() -> int:
+    return int(_C.qift_abi_version())
+
+
+def _check(status: int, where: str):
+    if status != QIFT_OK:
+        raise QiftError(status, where, last_error())
+
+
+def _stream(stream, device):
+    if stream is None:
+        return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+    if isinstance(stream, torch.cuda.Stream):
+        return ctypes.c_void_p(stream.cuda_stream)
+    return ctypes.c_void_p(int(stream))
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _dev_tensor(t, name, dtypes=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a GPU device (got {t.device})")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtypes is not None and t.dtype not in dtypes:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected one of {dtypes}")
+    return t
+
+
+def _levels(levels) -> int:
+    if isinstance(levels, str):
+        return LEVELS[levels]
+    return int(levels)
+
+
+def code_words_per_row(K: int, levels) -> int:
+    return K // 8 if _levels(levels) == LEVELS["int4"] else K // 16
+
+
+# ---------------------------------------------------------------------------
+# the four calls
+# ---------------------------------------------------------------------------
+
+def qift_quantize_weights(W, had_block: int, levels="mnz", scale_dtype=torch.float16,
+                          codes=None, scales=None, stream=None):
+    """W [N, K] float32/bfloat16 -> (codes int32 [N, K/16 or K/8] holding the
+    uint32 words, scales [N] in scale_dtype)."""
+    _dev_tensor(W, "W", (torch.float32, torch.bfloat16))
+    N, K = W.shape
+    lv = _levels(levels)
+    if codes is None:
+        codes = torch.empty((N, code_words_per_row(K, lv)), dtype=torch.int32, device=W.device)
+    if scales is None:
+        scales = torch.empty((N,), dtype=scale_dtype, device=W.device)
+    _dev_tensor(codes, "codes", (torch.int32,))
+    _dev_tensor(scales, "scales", (torch.float32, torch.float16))
+    st = _C.qift_quantize_weights(_ptr(W), _TORCH_TO_QIFT[W.dtype], N, K, had_block, lv,
+                                  _ptr(codes), _ptr(scales), _TORCH_TO_QIFT[scales.dtype],
+                                  _stream(stream, W.device))
+    _check(st, "qift_quantize_weights")
+    return codes, scales
+
+
+def qift_rotate_quant_act(X, had_block: int, xq=None, s_a=None, x_rot=None, want_x_rot=False,
+                          stream=None):
+    """X [M, K] float32/bfloat16 -> (xq uint8 [M, K/2], s_a float32 [M],
+    x_rot float32 [M, K] or None)."""
+    _dev_tensor(X, "X", (torch.float32, torch.bfloat16))
+    M, K = X.shape
+    if xq is None:
+        xq = torch.empty((M, K // 2), dtype=torch.uint8, device=X.device)
+    if s_a is None:
+        s_a = torch.empty((M,), dtype=torch.float32, device=X.device)
+    if x_rot is None and want_x_rot:
+        x_rot = torch.empty((M, K), dtype=torch.float32, device=X.device)
+    _dev_tensor(xq, "xq", (torch.uint8,))
+    _dev_tensor(s_a, "s_a", (torch.float32,))
+    if x_rot is not None:
+        _dev_tensor(x_rot, "x_rot", (torch.float32,))
+    st = _C.qift_rotate_quant_act(_ptr(X), _TORCH_TO_QIFT[X.dtype], M, K, had_block, _ptr(xq),
+                                  _ptr(s_a), _ptr(x_rot), _stream(stream, X.device))
+    _check(st, "qift_rotate_quant_act")
+    return xq, s_a, x_rot
+
+
+def qift_w2a4_linear(xq, s_a, codes, scales, levels="mnz", out_dtype=torch.float32, Y=None,
+                     N=None, stream=None):
+    """(xq [M, K/2], s_a [M], codes [N, ...], scales [N]) -> Y [M, N] in
+    out_dtype (float32, bfloat16, or int32 for the raw accumulator)."""
+    _dev_tensor(xq, "xq", (torch.uint8,))
+    _dev_tensor(s_a, "s_a", (torch.float32,))
+    _dev_tensor(codes, "codes", (torch.int32,))
+    _dev_tensor(scales, "scales", (torch.float32, torch.float16))
+    M, K = xq.shape[0], xq.shape[1] * 2
+    if N is None:
+        N = codes.shape[0]
+    if Y is None:
+        Y = torch.empty((M, N), dtype=out_dtype, device=xq.device)
+    _dev_tensor(Y, "Y", (torch.float32, torch.bfloat16, torch.int32))
+    st = _C.qift_w2a4_linear(_ptr(xq), _ptr(s_a), M, K, _ptr(codes), _ptr(scales),
+                             _TORCH_TO_QIFT[scales.dtype], _levels(levels), N, _ptr(Y),
+                             _TORCH_TO_QIFT[Y.dtype], _stream(stream, xq.device))
+    _check(st, "qift_w2a4_linear")
+    return Y
+
+
+def qift_kv4_quant(KV, had_block: int, kvq=None, scales=None, stream=None):
+    """KV [T, H, D] bfloat16/float32 -> (kvq uint8 [T, H, D/2], scales float32 [T, H])."""
+    _dev_tensor(KV, "KV", (torch.float32, torch.bfloat16))
+    T, H, D = KV.shape
+    if kvq is None:
+        kvq = torch.empty((T, H, D // 2), dtype=torch.uint8, device=KV.device)
+    if scales is None:
+        scales = torch.empty((T, H), dtype=torch.float32, device=KV.device)
+    _dev_tensor(kvq, "kvq", (torch.uint8,))
+    _dev_tensor(scales, "scales", (torch.float32,))
+    st = _C.qift_kv4_quant(_ptr(KV), _TORCH_TO_QIFT[KV.dtype], T, H, D, had_block, _ptr(kvq),
+                           _ptr(scales), _stream(stream, KV.device))
+    _check(st, "qift_kv4_quant")
+    return kvq, scales
+
+
+# ---------------------------------------------------------------------------
+# grouped linear
+# ---------------------------------------------------------------------------
+
+class LinearGroup:
+    """Many decode linears (M <= 16 each) run by one launch.
+
+    ``items`` is a sequence of dicts with keys xq, s_a, codes, scales, Y and
+    levels (tensors already allocated on one device). The plan lives in a
+    device workspace owned by this object; the tensors must stay alive.
+    """
+
+    def __init__(self, items, scale_dtype=torch.float16, y_dtype=torch.float32, stream=None):
+        n = len(items)
+        descs = (qift_linear_desc * max(n, 1))()
+        self._keep = []
+        device = None
+        for i, it in enumerate(items):
+            xq, codes = it["xq"], it["codes"]
+            device = xq.device
+            M, K = xq.shape[0], xq.shape[1] * 2
+            N = it.get("N", codes.shape[0])
+            for key in ("xq", "s_a", "codes", "scales", "Y"):
+                _dev_tensor(it[key], key)
+            descs[i] = qift_linear_desc(it["xq"].data_ptr(), it["s_a"].data_ptr(),
+                                        it["codes"].data_ptr(), it["scales"].data_ptr(),
+                                        it["Y"].data_ptr(), M, K, N, _levels(it["levels"]), 0)
+            self._keep.append(it)
+        nbytes = ctypes.c_size_t(0)
+        _check(_C.qift_linear_group_workspace_bytes(descs, n, ctypes.byref(nbytes)),
+               "qift_linear_group_workspace_bytes")
+        self.workspace = torch.empty((max(int(nbytes.value), 256),), dtype=torch.uint8, device=device)
+        tiles = ctypes.c_int64(0)
+        _check(_C.qift_linear_group_prepare(descs, n, _TORCH_TO_QIFT[scale_dtype],
+                                            _TORCH_TO_QIFT[y_dtype], _ptr(self.workspace),
+                                            self.workspace.numel(), ctypes.byref(tiles),
+                                            _stream(stream, device)),
+               "qift_linear_group_prepare")
+        self.launch_tiles = int(tiles.value)
+        self.device = device
+
+    def run(self, stream=None):
+        _check(_C.qift_w2a4_linear_grouped(_ptr(self.workspace), self.launch_tiles,
+                                           _stream(stream, self.device)),
+               "qift_w2a4_linear_grouped")
+
+
+__all__ = ["load_library", "QiftUnavailable", "qift_quantize_weights", "qift_rotate_quant_act", "qift_w2a4_linear", "qift_kv4_quant",
+           "LinearGroup", "QiftError", "qift_linear_desc", "LEVELS", "status_string", "last_error",
+           "abi_version", "code_words_per_row", "LIB_PATH"]

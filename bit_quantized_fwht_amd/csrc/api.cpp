@@ -1,0 +1,301 @@
+// C ABI of libqift: argument validation, dispatch to the HIP kernels, and the
+// host side of the grouped-linear plan. Every check runs before anything is
+// enqueued, so an invalid call touches neither the device nor the outputs.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <numeric>
+#include <string>
+#include <vector>
+
+#include "qift.h"
+#include "qift_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+qift_status fail(qift_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+qift_status ok() {
+  g_last_error.clear();
+  return QIFT_OK;
+}
+
+qift_status hip_result(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(QIFT_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+bool is_pow2(int64_t v) { return v > 0 && (v & (v - 1)) == 0; }
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+bool valid_levels(int lv) {
+  return lv == QIFT_LEVELS_MNZ || lv == QIFT_LEVELS_POT || lv == QIFT_LEVELS_INT4;
+}
+
+constexpr int64_t kMaxLinearK = 65536;
+constexpr int64_t kMaxGrid = 0x7fffffffLL;
+
+qift_status check_had_block(int64_t B, int64_t K, int64_t max_b) {
+  if (!is_pow2(B)) return fail(QIFT_ERR_INVALID_ARG, "had_block=%lld is not a power of two", (long long)B);
+  if (B > max_b) return fail(QIFT_ERR_UNSUPPORTED, "had_block=%lld exceeds %lld", (long long)B, (long long)max_b);
+  if (K % B != 0) return fail(QIFT_ERR_INVALID_ARG, "had_block=%lld does not divide K=%lld", (long long)B, (long long)K);
+  return QIFT_OK;
+}
+
+// Shared rules of qift_w2a4_linear and of each grouped descriptor.
+qift_status check_linear(const qift_linear_desc& d, qift_dtype scale_dtype, qift_dtype y_dtype) {
+  if (d.M < 0 || d.N < 0) return fail(QIFT_ERR_INVALID_ARG, "negative M or N");
+  if (d.K <= 0 || d.K % 64 != 0)
+    return fail(QIFT_ERR_INVALID_ARG, "K=%lld must be a positive multiple of 64", (long long)d.K);
+  if (d.K > kMaxLinearK)
+    return fail(QIFT_ERR_UNSUPPORTED, "K=%lld exceeds %lld", (long long)d.K, (long long)kMaxLinearK);
+  if (!valid_levels(d.levels)) return fail(QIFT_ERR_INVALID_ARG, "invalid levels %d", d.levels);
+  if (scale_dtype != QIFT_F32 && scale_dtype != QIFT_F16)
+    return fail(QIFT_ERR_INVALID_ARG, "scale_dtype must be F32 or F16");
+  if (y_dtype != QIFT_F32 && y_dtype != QIFT_BF16 && y_dtype != QIFT_I32)
+    return fail(QIFT_ERR_INVALID_ARG, "y_dtype must be F32, BF16 or I32");
+  if (d.M == 0 || d.N == 0) return QIFT_OK;
+  if (!d.xq || !d.s_a || !d.codes || !d.scales || !d.Y)
+    return fail(QIFT_ERR_INVALID_ARG, "null buffer");
+  if (!aligned(d.xq, 16) || !aligned(d.codes, 16))
+    return fail(QIFT_ERR_ALIGNMENT, "xq and codes must be 16-byte aligned");
+  if (!aligned(d.s_a, 4)) return fail(QIFT_ERR_ALIGNMENT, "s_a must be 4-byte aligned");
+  if (!aligned(d.scales, scale_dtype == QIFT_F16 ? 2 : 4) || !aligned(d.Y, y_dtype == QIFT_BF16 ? 2 : 4))
+    return fail(QIFT_ERR_ALIGNMENT, "scales or Y misaligned for its dtype");
+  if ((d.N + qift::kDecodeRowsPerTile - 1) / qift::kDecodeRowsPerTile > kMaxGrid)
+    return fail(QIFT_ERR_UNSUPPORTED, "N too large");
+  return QIFT_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t qift_abi_version(void) { return QIFT_ABI_VERSION; }
+
+const char* qift_last_error(void) { return g_last_error.c_str(); }
+
+const char* qift_status_string(qift_status s) {
+  switch (s) {
+    case QIFT_OK: return "QIFT_OK";
+    case QIFT_ERR_INVALID_ARG: return "QIFT_ERR_INVALID_ARG";
+    case QIFT_ERR_ALIGNMENT: return "QIFT_ERR_ALIGNMENT";
+    case QIFT_ERR_UNSUPPORTED: return "QIFT_ERR_UNSUPPORTED";
+    case QIFT_ERR_HIP: return "QIFT_ERR_HIP";
+  }
+  return "QIFT_ERR_UNKNOWN";
+}
+
+qift_status qift_quantize_weights(const void* W, qift_dtype w_dtype, int64_t N, int64_t K,
+                                  int32_t had_block, qift_levels levels, uint32_t* codes,
+                                  void* scales, qift_dtype scale_dtype, qift_stream stream) {
+  if (w_dtype != QIFT_F32 && w_dtype != QIFT_BF16)
+    return fail(QIFT_ERR_INVALID_ARG, "w_dtype must be F32 or BF16");
+  if (scale_dtype != QIFT_F32 && scale_dtype != QIFT_F16)
+    return fail(QIFT_ERR_INVALID_ARG, "scale_dtype must be F32 or F16");
+  if (!valid_levels(levels)) return fail(QIFT_ERR_INVALID_ARG, "invalid levels %d", (int)levels);
+  if (N < 0) return fail(QIFT_ERR_INVALID_ARG, "negative N");
+  if (K <= 0 || K % 64 != 0)
+    return fail(QIFT_ERR_INVALID_ARG, "K=%lld must be a positive multiple of 64", (long long)K);
+  if (K > QIFT_MAX_ROW)
+    return fail(QIFT_ERR_UNSUPPORTED, "K=%lld exceeds %d", (long long)K, QIFT_MAX_ROW);
+  qift_status st = check_had_block(had_block, K, QIFT_MAX_HAD_BLOCK);
+  if (st != QIFT_OK) return st;
+  if (N == 0) return ok();
+  if (N > kMaxGrid) return fail(QIFT_ERR_UNSUPPORTED, "N too large");
+  if (!W || !codes || !scales) return fail(QIFT_ERR_INVALID_ARG, "null buffer");
+  if (!aligned(codes, 16)) return fail(QIFT_ERR_ALIGNMENT, "codes must be 16-byte aligned");
+  if (!aligned(W, w_dtype == QIFT_F32 ? 4 : 2) || !aligned(scales, scale_dtype == QIFT_F16 ? 2 : 4))
+    return fail(QIFT_ERR_ALIGNMENT, "W or scales misaligned for its dtype");
+  return hip_result(qift::launch_quantize_weights(W, w_dtype == QIFT_BF16, N, K, had_block,
+                                                  (int)levels, codes, scales,
+                                                  scale_dtype == QIFT_F16,
+                                                  reinterpret_cast<hipStream_t>(stream)),
+                    "qift_quantize_weights launch");
+}
+
+qift_status qift_rotate_quant_act(const void* X, qift_dtype x_dtype, int64_t M, int64_t K,
+                                  int32_t had_block, uint8_t* xq, float* s_a, float* x_rot,
+                                  qift_stream stream) {
+  if (x_dtype != QIFT_F32 && x_dtype != QIFT_BF16)
+    return fail(QIFT_ERR_INVALID_ARG, "x_dtype must be F32 or BF16");
+  if (M < 0) return fail(QIFT_ERR_INVALID_ARG, "negative M");
+  if (K <= 0 || K % 2 != 0)
+    return fail(QIFT_ERR_INVALID_ARG, "K=%lld must be positive and even", (long long)K);
+  if (K > QIFT_MAX_ROW)
+    return fail(QIFT_ERR_UNSUPPORTED, "K=%lld exceeds %d", (long long)K, QIFT_MAX_ROW);
+  qift_status st = check_had_block(had_block, K, QIFT_MAX_HAD_BLOCK);
+  if (st != QIFT_OK) return st;
+  if (M == 0) return ok();
+  if (M > kMaxGrid) return fail(QIFT_ERR_UNSUPPORTED, "M too large");
+  if (!X || !xq || !s_a) return fail(QIFT_ERR_INVALID_ARG, "null buffer");
+  if (!aligned(xq, 16)) return fail(QIFT_ERR_ALIGNMENT, "xq must be 16-byte aligned");
+  if (!aligned(X, x_dtype == QIFT_F32 ? 4 : 2) || !aligned(s_a, 4) || (x_rot && !aligned(x_rot, 4)))
+    return fail(QIFT_ERR_ALIGNMENT, "X, s_a or x_rot misaligned for its dtype");
+  return hip_result(qift::launch_rotate_quant_act(X, x_dtype == QIFT_BF16, M, K, had_block, xq,
+                                                  s_a, x_rot,
+                                                  reinterpret_cast<hipStream_t>(stream)),
+                    "qift_rotate_quant_act launch");
+}
+
+qift_status qift_w2a4_linear(const uint8_t* xq, const float* s_a, int64_t M, int64_t K,
+                             const uint32_t* codes, const void* scales, qift_dtype scale_dtype,
+                             qift_levels levels, int64_t N, void* Y, qift_dtype y_dtype,
+                             qift_stream stream) {
+  qift_linear_desc d{};
+  d.xq = xq;
+  d.s_a = s_a;
+  d.codes = codes;
+  d.scales = scales;
+  d.Y = Y;
+  d.M = M;
+  d.K = K;
+  d.N = N;
+  d.levels = (int32_t)levels;
+  qift_status st = check_linear(d, scale_dtype, y_dtype);
+  if (st != QIFT_OK) return st;
+  if (M == 0 || N == 0) return ok();
+  if ((M + 127) / 128 > 65535) return fail(QIFT_ERR_UNSUPPORTED, "M too large");
+  const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const int sf16 = scale_dtype == QIFT_F16;
+  if (M <= 16) return hip_result(qift::launch_linear_decode(d, sf16, y_dtype, s), "qift_w2a4_linear decode launch");
+  return hip_result(qift::launch_linear_prefill(d, sf16, y_dtype, s), "qift_w2a4_linear prefill launch");
+}
+
+qift_status qift_kv4_quant(const void* KV, qift_dtype dtype, int64_t T, int64_t H, int64_t D,
+                           int32_t had_block, uint8_t* kvq, float* scales, qift_stream stream) {
+  if (dtype != QIFT_F32 && dtype != QIFT_BF16)
+    return fail(QIFT_ERR_INVALID_ARG, "dtype must be F32 or BF16");
+  if (T < 0 || H < 0) return fail(QIFT_ERR_INVALID_ARG, "negative T or H");
+  if (!(D == 16 || D == 32 || D == 64 || D == 128 || D == 256))
+    return fail(QIFT_ERR_UNSUPPORTED, "D=%lld must be 16, 32, 64, 128 or 256", (long long)D);
+  qift_status st = check_had_block(had_block, D, D);
+  if (st != QIFT_OK) return st;
+  const int64_t rows = T * H;
+  if (rows == 0) return ok();
+  if (rows / (256 / (D / 8)) + 1 > kMaxGrid) return fail(QIFT_ERR_UNSUPPORTED, "T*H too large");
+  if (!KV || !kvq || !scales) return fail(QIFT_ERR_INVALID_ARG, "null buffer");
+  if (!aligned(KV, 16) || !aligned(kvq, 16) || !aligned(scales, 4))
+    return fail(QIFT_ERR_ALIGNMENT, "KV and kvq must be 16-byte aligned, scales 4-byte");
+  return hip_result(qift::launch_kv4(KV, dtype == QIFT_BF16, rows, (int)D, had_block, kvq, scales,
+                                     reinterpret_cast<hipStream_t>(stream)),
+                    "qift_kv4_quant launch");
+}
+
+// --- grouped linear ------------------------------------------------------------
+
+static qift_status check_group(const qift_linear_desc* descs, int32_t count, qift_dtype scale_dtype,
+                               qift_dtype y_dtype, int64_t* total_tiles) {
+  if (count < 0) return fail(QIFT_ERR_INVALID_ARG, "negative count");
+  if (count > 0 && !descs) return fail(QIFT_ERR_INVALID_ARG, "null descriptor array");
+  int64_t tiles = 0;
+  for (int32_t i = 0; i < count; ++i) {
+    const qift_linear_desc& d = descs[i];
+    if (d.reserved != 0) return fail(QIFT_ERR_INVALID_ARG, "descriptor %d: reserved field must be 0", i);
+    qift_status st = check_linear(d, scale_dtype, y_dtype);
+    if (st != QIFT_OK) {
+      g_last_error = "descriptor " + std::to_string(i) + ": " + g_last_error;
+      return st;
+    }
+    if (d.M > 16) return fail(QIFT_ERR_UNSUPPORTED, "descriptor %d: grouped linears take M <= 16", i);
+    if (d.M > 0) tiles += (d.N + qift::kDecodeRowsPerTile - 1) / qift::kDecodeRowsPerTile;
+  }
+  if (tiles > kMaxGrid) return fail(QIFT_ERR_UNSUPPORTED, "too many tiles");
+  *total_tiles = tiles;
+  return QIFT_OK;
+}
+
+static size_t plan_bytes(int32_t count, int64_t tiles) {
+  size_t b = sizeof(qift::PlanHeader) + (size_t)count * sizeof(qift::PlanEntry) + (size_t)tiles * 4;
+  return (b + 255) & ~(size_t)255;
+}
+
+qift_status qift_linear_group_workspace_bytes(const qift_linear_desc* descs, int32_t count,
+                                              size_t* bytes) {
+  if (!bytes) return fail(QIFT_ERR_INVALID_ARG, "null bytes");
+  int64_t tiles = 0;
+  qift_status st = check_group(descs, count, QIFT_F32, QIFT_F32, &tiles);
+  if (st != QIFT_OK) return st;
+  *bytes = plan_bytes(count, tiles);
+  return ok();
+}
+
+qift_status qift_linear_group_prepare(const qift_linear_desc* descs, int32_t count,
+                                      qift_dtype scale_dtype, qift_dtype y_dtype, void* workspace,
+                                      size_t workspace_bytes, int64_t* launch_tiles,
+                                      qift_stream stream) {
+  if (!launch_tiles) return fail(QIFT_ERR_INVALID_ARG, "null launch_tiles");
+  int64_t tiles = 0;
+  qift_status st = check_group(descs, count, scale_dtype, y_dtype, &tiles);
+  if (st != QIFT_OK) return st;
+  const size_t need = plan_bytes(count, tiles);
+  if (!workspace) return fail(QIFT_ERR_INVALID_ARG, "null workspace");
+  if (!aligned(workspace, 256)) return fail(QIFT_ERR_ALIGNMENT, "workspace must be 256-byte aligned");
+  if (workspace_bytes < need)
+    return fail(QIFT_ERR_INVALID_ARG, "workspace has %zu bytes, plan needs %zu", workspace_bytes, need);
+
+  std::vector<uint8_t> host(need, 0);
+  auto* h = reinterpret_cast<qift::PlanHeader*>(host.data());
+  h->magic = qift::kPlanMagic;
+  h->count = count;
+  h->scale_f16 = scale_dtype == QIFT_F16;
+  h->y_dtype = (int32_t)y_dtype;
+  h->total_tiles = tiles;
+  h->entries_offset = sizeof(qift::PlanHeader);
+  h->tile_map_offset = sizeof(qift::PlanHeader) + (int64_t)count * sizeof(qift::PlanEntry);
+  auto* ent = reinterpret_cast<qift::PlanEntry*>(host.data() + h->entries_offset);
+  auto* map = reinterpret_cast<int32_t*>(host.data() + h->tile_map_offset);
+
+  // longest rows (largest K) first, so the longest tiles are dispatched first
+  std::vector<int32_t> order(count);
+  std::iota(order.begin(), order.end(), 0);
+  std::stable_sort(order.begin(), order.end(),
+                   [&](int32_t a, int32_t b) { return descs[a].K > descs[b].K; });
+  int64_t t = 0;
+  for (int32_t i = 0; i < count; ++i) {
+    ent[i].d = descs[i];
+    ent[i].tile_begin = 0;
+    ent[i].n_tiles = 0;
+  }
+  for (int32_t oi = 0; oi < count; ++oi) {
+    const int32_t i = order[oi];
+    const qift_linear_desc& d = descs[i];
+    const int64_t n = (d.M > 0) ? (d.N + qift::kDecodeRowsPerTile - 1) / qift::kDecodeRowsPerTile : 0;
+    ent[i].tile_begin = t;
+    ent[i].n_tiles = n;
+    for (int64_t k = 0; k < n; ++k) map[t + k] = i;
+    t += n;
+  }
+  const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  hipError_t e = hipMemcpyAsync(workspace, host.data(), need, hipMemcpyHostToDevice, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return hip_result(e, "qift_linear_group_prepare copy");
+  *launch_tiles = tiles;
+  return ok();
+}
+
+qift_status qift_w2a4_linear_grouped(const void* workspace, int64_t launch_tiles,
+                                     qift_stream stream) {
+  if (!workspace) return fail(QIFT_ERR_INVALID_ARG, "null workspace");
+  if (!aligned(workspace, 256)) return fail(QIFT_ERR_ALIGNMENT, "workspace must be 256-byte aligned");
+  if (launch_tiles < 0 || launch_tiles > kMaxGrid)
+    return fail(QIFT_ERR_INVALID_ARG, "launch_tiles out of range");
+  if (launch_tiles == 0) return ok();
+  return hip_result(qift::launch_linear_grouped(workspace, launch_tiles, 0, 0,
+                                                reinterpret_cast<hipStream_t>(stream)),
+                    "qift_w2a4_linear_grouped launch");
+}
+
+}  // extern "C"

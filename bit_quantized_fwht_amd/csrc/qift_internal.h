@@ -1,0 +1,144 @@
+// Internal declarations of libqift: device helpers shared by the kernels,
+// the grouped-linear plan layout, and the launchers called by api.cpp.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <hip/hip_bf16.h>
+#include <hip/hip_fp16.h>
+#include <stdint.h>
+
+#include "qift.h"
+
+namespace qift {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef unsigned int v4u __attribute__((ext_vector_type(4)));
+
+// ---------------------------------------------------------------------------
+// element loads / stores
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ float bf16_bits_to_float(uint16_t b) {
+  return __uint_as_float(((uint32_t)b) << 16);
+}
+
+// float32 -> bfloat16, round to nearest even (NaN kept quiet).
+__device__ __forceinline__ uint16_t float_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+__device__ __forceinline__ float load_scale(const void* p, int64_t i, int is_f16) {
+  if (is_f16) return __half2float(reinterpret_cast<const __half*>(p)[i]);
+  return reinterpret_cast<const float*>(p)[i];
+}
+
+// ---------------------------------------------------------------------------
+// matrix-core operands for v_mfma_i32_16x16x64_i8
+//
+// One lane supplies 16 int8 values (4 dwords) for 16 consecutive features
+// k0..k0+15. The order of those 16 values inside the dwords is free as long
+// as the activation (A) and weight (B) operands use the same one; the order
+// used everywhere is
+//   dword 0: k0+0, k0+2, k0+4, k0+6      dword 1: k0+1, k0+3, k0+5, k0+7
+//   dword 2: k0+8, k0+10, k0+12, k0+14   dword 3: k0+9, k0+11, k0+13, k0+15
+// which is what masks of the int4 and 2-bit packed layouts give directly.
+// ---------------------------------------------------------------------------
+
+// int4 pairs (two words, 16 features) -> 16*q per byte, exact.
+__device__ __forceinline__ v4i int4_operand(uint32_t x0, uint32_t x1) {
+  v4i a;
+  a[0] = (int)((x0 << 4) & 0xF0F0F0F0u);
+  a[1] = (int)(x0 & 0xF0F0F0F0u);
+  a[2] = (int)((x1 << 4) & 0xF0F0F0F0u);
+  a[3] = (int)(x1 & 0xF0F0F0F0u);
+  return a;
+}
+
+// 2-bit MNZ codes (one word, 16 features) -> 32*(2t+1) per byte: the code t
+// lands in the two top bits of its byte (64t as a signed byte) and bit 5 adds
+// 32.
+__device__ __forceinline__ v4i mnz_operand(uint32_t c) {
+  v4i b;
+  b[0] = (int)(((c << 6) & 0xC0C0C0C0u) | 0x20202020u);
+  b[1] = (int)(((c << 4) & 0xC0C0C0C0u) | 0x20202020u);
+  b[2] = (int)(((c << 2) & 0xC0C0C0C0u) | 0x20202020u);
+  b[3] = (int)((c & 0xC0C0C0C0u) | 0x20202020u);
+  return b;
+}
+
+// 2-bit PoT codes -> 16*level per byte through a 4-entry byte table
+// (+1, +4, -1, -4) * 16 selected by v_perm_b32.
+__device__ __forceinline__ v4i pot_operand(uint32_t c) {
+  const uint32_t lut = 0xC0F04010u;  // bytes: 0x10, 0x40, 0xF0, 0xC0
+  v4i b;
+  b[0] = (int)__builtin_amdgcn_perm(0u, lut, c & 0x03030303u);
+  b[1] = (int)__builtin_amdgcn_perm(0u, lut, (c >> 2) & 0x03030303u);
+  b[2] = (int)__builtin_amdgcn_perm(0u, lut, (c >> 4) & 0x03030303u);
+  b[3] = (int)__builtin_amdgcn_perm(0u, lut, (c >> 6) & 0x03030303u);
+  return b;
+}
+
+// Right shift that turns the matrix-core sum back into sum q * level:
+// MNZ 16 * 32 = 2^9, PoT 16 * 16 = 2^8, INT4 16 * 16 = 2^8.
+__host__ __device__ constexpr int acc_shift(int levels) { return levels == QIFT_LEVELS_MNZ ? 9 : 8; }
+__host__ __device__ constexpr float level_kappa(int levels) {
+  return levels == QIFT_LEVELS_MNZ ? 0.5f : 1.0f;
+}
+
+__device__ __forceinline__ v4i mfma16(v4i a, v4i b, v4i c) {
+  return __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, c, 0, 0, 0);
+}
+
+// ---------------------------------------------------------------------------
+// grouped linear plan (device copy lives in the caller's workspace)
+// ---------------------------------------------------------------------------
+
+struct PlanEntry {          // one linear
+  qift_linear_desc d;       // 72 bytes
+  int64_t tile_begin;       // first workgroup tile of this linear
+  int64_t n_tiles;
+};
+static_assert(sizeof(qift_linear_desc) == 72, "descriptor layout");
+static_assert(sizeof(PlanEntry) == 88, "plan entry layout");
+
+struct PlanHeader {
+  uint64_t magic;
+  int32_t count;
+  int32_t scale_f16;
+  int32_t y_dtype;
+  int32_t pad0;
+  int64_t total_tiles;
+  int64_t entries_offset;   // bytes from the workspace start
+  int64_t tile_map_offset;  // int32 per tile: index of its linear
+  int64_t pad1[2];
+};
+static_assert(sizeof(PlanHeader) == 64, "plan header layout");
+constexpr uint64_t kPlanMagic = 0x5146545f504c414eull;  // "QFT_PLAN"
+
+// decode kernel geometry: 256 threads = 4 waves, each wave 4 x 16 rows
+constexpr int kDecodeRowsPerWave = 64;
+constexpr int kDecodeWaves = 4;
+constexpr int kDecodeRowsPerTile = kDecodeRowsPerWave * kDecodeWaves;
+
+// ---------------------------------------------------------------------------
+// launchers (implemented in the .hip files; return a hipError_t)
+// ---------------------------------------------------------------------------
+
+hipError_t launch_rotate_quant_act(const void* X, int x_bf16, int64_t M, int64_t K, int had_block,
+                                   uint8_t* xq, float* s_a, float* x_rot, hipStream_t s);
+hipError_t launch_quantize_weights(const void* W, int w_bf16, int64_t N, int64_t K, int had_block,
+                                   int levels, uint32_t* codes, void* scales, int scale_f16,
+                                   hipStream_t s);
+hipError_t launch_kv4(const void* KV, int bf16, int64_t rows, int D, int had_block, uint8_t* kvq,
+                      float* scales, hipStream_t s);
+hipError_t launch_linear_decode(const qift_linear_desc& d, int scale_f16, int y_dtype,
+                                hipStream_t s);
+hipError_t launch_linear_prefill(const qift_linear_desc& d, int scale_f16, int y_dtype,
+                                 hipStream_t s);
+hipError_t launch_linear_grouped(const void* workspace, int64_t total_tiles, int scale_f16,
+                                 int y_dtype, hipStream_t s);
+
+}  // namespace qift

@@ -1,0 +1,290 @@
+// Row kernels of the rotated quantization pipeline:
+//  - rotate_quant_act: online activation path (block Walsh-Hadamard rotation
+//    along K, per-token absmax, symmetric int4, packed);
+//  - quantize_weights: offline weight path (same rotation, per-channel absmax
+//    scale, nearest no-zero level, packed 2-bit codes; or int4 weights).
+// Source of the method: "Qift: Shift-Friendly No-Zero W2 Post-Training
+// Quantization for Rotated W2A4/KV4 LLM Inference", abstract.
+//
+// One workgroup handles one row. The row is staged in LDS as float32; the
+// butterflies run in passes of up to four stages, each pass keeping 16 (or
+// fewer) elements in registers, so a block of 4096 takes three LDS round
+// trips instead of twelve.
+#include "qift_internal.h"
+
+namespace qift {
+
+constexpr int kRowThreads = 256;
+
+// --- staged row load: X[row] -> LDS float32 --------------------------------
+
+template <typename T>
+__device__ __forceinline__ void load_row(const T* __restrict__ src, float* row, int K, int tid);
+
+template <>
+__device__ __forceinline__ void load_row<float>(const float* __restrict__ src, float* row, int K,
+                                                int tid) {
+  if ((K & 3) == 0 && ((reinterpret_cast<uintptr_t>(src) & 15) == 0)) {
+    const float4* s4 = reinterpret_cast<const float4*>(src);
+    float4* r4 = reinterpret_cast<float4*>(row);
+    for (int i = tid; i < (K >> 2); i += kRowThreads) r4[i] = s4[i];
+  } else {
+    for (int i = tid; i < K; i += kRowThreads) row[i] = src[i];
+  }
+}
+
+template <>
+__device__ __forceinline__ void load_row<uint16_t>(const uint16_t* __restrict__ src, float* row,
+                                                   int K, int tid) {
+  if ((K & 7) == 0 && ((reinterpret_cast<uintptr_t>(src) & 15) == 0)) {
+    const uint4* s8 = reinterpret_cast<const uint4*>(src);
+    for (int i = tid; i < (K >> 3); i += kRowThreads) {
+      uint4 u = s8[i];
+      float4 lo, hi;
+      lo.x = __uint_as_float(u.x << 16);
+      lo.y = __uint_as_float(u.x & 0xffff0000u);
+      lo.z = __uint_as_float(u.y << 16);
+      lo.w = __uint_as_float(u.y & 0xffff0000u);
+      hi.x = __uint_as_float(u.z << 16);
+      hi.y = __uint_as_float(u.z & 0xffff0000u);
+      hi.z = __uint_as_float(u.w << 16);
+      hi.w = __uint_as_float(u.w & 0xffff0000u);
+      reinterpret_cast<float4*>(row)[2 * i] = lo;
+      reinterpret_cast<float4*>(row)[2 * i + 1] = hi;
+    }
+  } else {
+    for (int i = tid; i < K; i += kRowThreads) row[i] = bf16_bits_to_float(src[i]);
+  }
+}
+
+// --- butterflies --------------------------------------------------------------
+
+// One pass: stages 4p .. 4p+NS-1 of every Hadamard block of the row. Element
+// index bits [4p, 4p+NS) select the 2^NS elements a thread holds; they all
+// lie in the same block because 4p+NS <= log2(block).
+template <int NS>
+__device__ __forceinline__ void fwht_pass(float* row, int K, int p, int tid) {
+  constexpr int R = 1 << NS;
+  const int sh = 4 * p;
+  const int S = 1 << sh;
+  const int groups = K >> NS;
+  for (int grp = tid; grp < groups; grp += kRowThreads) {
+    const int low = grp & (S - 1);
+    const int high = grp >> sh;
+    const int base = (high << (sh + NS)) | low;
+    float v[R];
+#pragma unroll
+    for (int j = 0; j < R; ++j) v[j] = row[base + j * S];
+#pragma unroll
+    for (int st = 0; st < NS; ++st) {
+      const int h = 1 << st;
+#pragma unroll
+      for (int j = 0; j < R; ++j) {
+        if (!(j & h)) {
+          const float a = v[j], b = v[j + h];
+          v[j] = a + b;
+          v[j + h] = a - b;
+        }
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < R; ++j) row[base + j * S] = v[j];
+  }
+}
+
+// Unnormalized block transform of the LDS row; log2b = log2(block).
+__device__ __forceinline__ void fwht_row(float* row, int K, int log2b, int tid) {
+  for (int p = 0; 4 * p < log2b; ++p) {
+    const int ns = min(4, log2b - 4 * p);
+    switch (ns) {
+      case 1: fwht_pass<1>(row, K, p, tid); break;
+      case 2: fwht_pass<2>(row, K, p, tid); break;
+      case 3: fwht_pass<3>(row, K, p, tid); break;
+      default: fwht_pass<4>(row, K, p, tid); break;
+    }
+    __syncthreads();
+  }
+}
+
+// max |row[i]| * norm over the row (every thread gets the result).
+__device__ __forceinline__ float row_absmax(const float* row, int K, float norm, int tid,
+                                            float* red) {
+  float m = 0.f;
+  for (int i = tid; i < K; i += kRowThreads) m = fmaxf(m, fabsf(row[i]));
+  m *= norm;  // rounding is monotonic: max(|v|)*norm == max(|v*norm|)
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
+  if ((tid & 63) == 0) red[tid >> 6] = m;
+  __syncthreads();
+  float r = red[0];
+#pragma unroll
+  for (int w = 1; w < kRowThreads / 64; ++w) r = fmaxf(r, red[w]);
+  __syncthreads();
+  return r;
+}
+
+__device__ __forceinline__ int quant_int4(float x, float s) {
+  if (s == 0.f) return 0;
+  float q = rintf(__fdiv_rn(x, s));
+  q = fminf(fmaxf(q, -7.f), 7.f);
+  return (int)q;
+}
+
+// --- K1: rotate + per-token int4 ---------------------------------------------
+
+template <typename T>
+__global__ __launch_bounds__(kRowThreads) void rotate_quant_act_kernel(
+    const T* __restrict__ X, int K, int log2b, float norm, uint8_t* __restrict__ xq,
+    float* __restrict__ s_a, float* __restrict__ x_rot) {
+  extern __shared__ float row[];
+  __shared__ float red[kRowThreads / 64];
+  const int tid = threadIdx.x;
+  const int64_t m = blockIdx.x;
+  load_row<T>(X + m * K, row, K, tid);
+  __syncthreads();
+  fwht_row(row, K, log2b, tid);
+  const float amax = row_absmax(row, K, norm, tid, red);
+  const float s = __fdiv_rn(amax, 7.0f);
+  if (tid == 0) s_a[m] = s;
+  uint8_t* xq_row = xq + m * (int64_t)(K / 2);
+  if ((K & 7) == 0) {
+    uint32_t* w_row = reinterpret_cast<uint32_t*>(xq_row);
+    for (int g = tid; g < (K >> 3); g += kRowThreads) {
+      uint32_t word = 0;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float x = row[8 * g + i] * norm;
+        word |= ((uint32_t)quant_int4(x, s) & 0xFu) << (4 * i);
+        if (x_rot) x_rot[m * K + 8 * g + i] = x;
+      }
+      w_row[g] = word;
+    }
+  } else {
+    for (int j = tid; j < (K >> 1); j += kRowThreads) {
+      const float x0 = row[2 * j] * norm, x1 = row[2 * j + 1] * norm;
+      xq_row[j] = (uint8_t)(((uint32_t)quant_int4(x0, s) & 0xFu) |
+                            (((uint32_t)quant_int4(x1, s) & 0xFu) << 4));
+      if (x_rot) {
+        x_rot[m * K + 2 * j] = x0;
+        x_rot[m * K + 2 * j + 1] = x1;
+      }
+    }
+  }
+}
+
+// --- K0: rotate + per-channel scale + nearest level + pack ----------------------
+
+__device__ __forceinline__ uint32_t code_mnz(float w, float s) {
+  // 2-bit two's complement t with half-scale level 2t+1: +inner 00, +outer 01,
+  // -outer 10, -inner 11. |w| == s is a tie and goes to the inner level.
+  if (s == 0.f) return 0u;
+  const bool outer = fabsf(w) > s;
+  const bool neg = w < 0.f;
+  return neg ? (outer ? 2u : 3u) : (outer ? 1u : 0u);
+}
+
+__device__ __forceinline__ uint32_t code_pot(float w, float s) {
+  // bit 1 = sign, bit 0 = shift by two; outer iff |w| > 2.5 s, compared
+  // exactly in double (2|w| and 5s are exact there).
+  if (s == 0.f) return 0u;
+  const bool outer = 2.0 * (double)fabsf(w) > 5.0 * (double)s;
+  const bool neg = w < 0.f;
+  return ((neg ? 1u : 0u) << 1) | (outer ? 1u : 0u);
+}
+
+__device__ __forceinline__ int code_bit_offset(int i) {
+  return 8 * ((i >> 1) & 3) + 4 * (i >> 3) + 2 * (i & 1);
+}
+
+template <typename T>
+__global__ __launch_bounds__(kRowThreads) void quantize_weights_kernel(
+    const T* __restrict__ W, int K, int log2b, float norm, int levels, uint32_t* __restrict__ codes,
+    void* __restrict__ scales, int scale_f16) {
+  extern __shared__ float row[];
+  __shared__ float red[kRowThreads / 64];
+  const int tid = threadIdx.x;
+  const int64_t n = blockIdx.x;
+  load_row<T>(W + n * K, row, K, tid);
+  __syncthreads();
+  fwht_row(row, K, log2b, tid);
+  const float amax = row_absmax(row, K, norm, tid, red);
+  const float outer = levels == QIFT_LEVELS_MNZ ? 1.5f : (levels == QIFT_LEVELS_POT ? 4.0f : 7.0f);
+  const float s32 = __fdiv_rn(amax, outer);
+  float s;
+  if (scale_f16) {
+    const __half h = __float2half_rn(s32);
+    s = __half2float(h);
+    if (tid == 0) reinterpret_cast<__half*>(scales)[n] = h;
+  } else {
+    s = s32;
+    if (tid == 0) reinterpret_cast<float*>(scales)[n] = s32;
+  }
+  if (levels == QIFT_LEVELS_INT4) {
+    uint32_t* c_row = codes + n * (int64_t)(K / 8);
+    for (int g = tid; g < (K >> 3); g += kRowThreads) {
+      uint32_t word = 0;
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        word |= ((uint32_t)quant_int4(row[8 * g + i] * norm, s) & 0xFu) << (4 * i);
+      c_row[g] = word;
+    }
+  } else {
+    uint32_t* c_row = codes + n * (int64_t)(K / 16);
+    const bool pot = levels == QIFT_LEVELS_POT;
+    for (int g = tid; g < (K >> 4); g += kRowThreads) {
+      uint32_t word = 0;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float w = row[16 * g + i] * norm;
+        const uint32_t c = pot ? code_pot(w, s) : code_mnz(w, s);
+        word |= c << code_bit_offset(i);
+      }
+      c_row[g] = word;
+    }
+  }
+}
+
+// --- launchers -----------------------------------------------------------------
+
+static int ilog2(int v) {
+  int r = 0;
+  while ((1 << r) < v) ++r;
+  return r;
+}
+
+// 1/sqrt(B) rounded once to float32 (exact for even log2 B).
+static float had_norm(int B) { return (float)(1.0 / __builtin_sqrt((double)B)); }
+
+hipError_t launch_rotate_quant_act(const void* X, int x_bf16, int64_t M, int64_t K, int had_block,
+                                   uint8_t* xq, float* s_a, float* x_rot, hipStream_t s) {
+  const size_t lds = (size_t)K * sizeof(float);
+  const int lb = ilog2(had_block);
+  const float nrm = had_norm(had_block);
+  if (x_bf16)
+    hipLaunchKernelGGL(rotate_quant_act_kernel<uint16_t>, dim3((unsigned)M), dim3(kRowThreads),
+                       lds, s, reinterpret_cast<const uint16_t*>(X), (int)K, lb, nrm, xq, s_a,
+                       x_rot);
+  else
+    hipLaunchKernelGGL(rotate_quant_act_kernel<float>, dim3((unsigned)M), dim3(kRowThreads), lds,
+                       s, reinterpret_cast<const float*>(X), (int)K, lb, nrm, xq, s_a, x_rot);
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize_weights(const void* W, int w_bf16, int64_t N, int64_t K, int had_block,
+                                   int levels, uint32_t* codes, void* scales, int scale_f16,
+                                   hipStream_t s) {
+  const size_t lds = (size_t)K * sizeof(float);
+  const int lb = ilog2(had_block);
+  const float nrm = had_norm(had_block);
+  if (w_bf16)
+    hipLaunchKernelGGL(quantize_weights_kernel<uint16_t>, dim3((unsigned)N), dim3(kRowThreads),
+                       lds, s, reinterpret_cast<const uint16_t*>(W), (int)K, lb, nrm, levels,
+                       codes, scales, scale_f16);
+  else
+    hipLaunchKernelGGL(quantize_weights_kernel<float>, dim3((unsigned)N), dim3(kRowThreads), lds,
+                       s, reinterpret_cast<const float*>(W), (int)K, lb, nrm, levels, codes,
+                       scales, scale_f16);
+  return hipGetLastError();
+}
+
+}  // namespace qift

@@ -1,0 +1,223 @@
+/*
+ * qift.h -- C ABI of libqift.so: the rotated W2A4 linear layer and the KV4
+ * quantizer on AMD Instinct MI355X (gfx950).
+ *
+ * The method is the one of "Qift: Shift-Friendly No-Zero W2 Post-Training
+ * Quantization for Rotated W2A4/KV4 LLM Inference" (arXiv 2606.02823,
+ * abstract): weights and activations are rotated by a Hadamard transform,
+ * two-bit weights take a fixed no-zero level set ({+-0.5, +-1.5}, i.e.
+ * {+-1, +-3} at half scale, or the power-of-two {+-1, +-4} applied by sign and
+ * shift) with one scale per output channel and no zero point; activations and
+ * the KV cache are 4-bit.
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * - Every buffer argument is a DEVICE pointer owned by the caller. The library
+ *   allocates no device memory and keeps no state besides a cached device
+ *   property; it is safe to call from several host threads.
+ * - Calls are asynchronous: they validate, enqueue on `stream` and return.
+ *   Outputs are valid in stream order. `stream` is a hipStream_t passed as
+ *   void* (NULL = the null stream).
+ * - Arguments are validated before anything is launched. On an error the
+ *   call returns a non-zero status, launches nothing and writes nothing;
+ *   qift_last_error() then returns a description (per host thread).
+ * - Layouts are dense and row-major; no strides.
+ * - NaN or Inf inputs give unspecified (but memory-safe) results.
+ *
+ * Packed layouts
+ * --------------
+ * int4 (activations xq, KV codes, 4-bit weights): element 2j of a row sits in
+ *   the low nibble of byte j, element 2j+1 in the high nibble, two's
+ *   complement. Read as little-endian 32-bit words, element i of a word is at
+ *   bits 4i..4i+3. Values are in [-7, 7].
+ * 2-bit weight codes: row n of a [N, K] matrix is K/16 32-bit words; word j
+ *   holds features k = 16j..16j+15. Feature k = 16j + i sits at bit offset
+ *   8*((i>>1)&3) + 4*(i>>3) + 2*(i&1), i.e. byte b holds features
+ *   2b, 2b+1, 8+2b, 9+2b in bit pairs 0-1, 2-3, 4-5, 6-7. (This pairs each
+ *   code with the nibble order of the int4 activations so that both unpack
+ *   to matrix-core operands with shifts and masks only.)
+ * Code values:
+ *   QIFT_LEVELS_MNZ : the code read as a 2-bit two's-complement integer t
+ *                     gives the half-scale level 2t+1 in {-3,-1,+1,+3};
+ *                     weight = (2t+1) * s / 2, i.e. {+-0.5, +-1.5} * s.
+ *                     (00 -> +0.5s, 01 -> +1.5s, 10 -> -1.5s, 11 -> -0.5s)
+ *   QIFT_LEVELS_POT : bit 1 is the sign, bit 0 the shift by two:
+ *                     level = +-(1 << 2*bit0) in {+-1, +-4}; weight = level*s.
+ *                     (00 -> +s, 01 -> +4s, 10 -> -s, 11 -> -4s)
+ *   QIFT_LEVELS_INT4: 4-bit two's-complement weights in [-7, 7]
+ *                     (the 4-bit layers of an L-layer mixed W2/W4 stack).
+ *
+ * Hadamard rotation
+ * -----------------
+ * had_block = B, a power of two dividing K: every run of B consecutive
+ * features is multiplied by H_B / sqrt(B), H_B the Sylvester Hadamard matrix
+ * in natural order (H_1 = [1], H_2n = [[H, H], [H, -H]]). B = 1 is the
+ * identity. The same B must be used for a linear's weights and its input.
+ */
+#ifndef QIFT_H
+#define QIFT_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define QIFT_ABI_VERSION 1
+
+typedef enum {
+  QIFT_OK = 0,
+  QIFT_ERR_INVALID_ARG = 1, /* null pointer, bad size, bad enum value          */
+  QIFT_ERR_ALIGNMENT = 2,   /* a buffer is not aligned as documented           */
+  QIFT_ERR_UNSUPPORTED = 3, /* valid request outside this build's limits       */
+  QIFT_ERR_HIP = 4          /* the HIP runtime reported an error on launch     */
+} qift_status;
+
+typedef enum { QIFT_F32 = 0, QIFT_BF16 = 1, QIFT_F16 = 2, QIFT_I32 = 3 } qift_dtype;
+
+typedef enum {
+  QIFT_LEVELS_MNZ = 0,  /* {+-0.5, +-1.5} * s, 2-bit codes              */
+  QIFT_LEVELS_POT = 1,  /* {+-1, +-4} * s, 2-bit codes, sign-and-shift  */
+  QIFT_LEVELS_INT4 = 2  /* [-7, 7] * s, 4-bit codes                     */
+} qift_levels;
+
+typedef void* qift_stream; /* a hipStream_t */
+
+/* Largest K accepted by qift_quantize_weights and qift_rotate_quant_act, and
+ * largest Hadamard block. */
+#define QIFT_MAX_ROW 16384
+#define QIFT_MAX_HAD_BLOCK 4096
+
+/*
+ * qift_quantize_weights -- offline weight quantizer (Qift abstract: a fixed
+ * two-bit code-to-level mapping with the standard per-channel scale, no zero
+ * point, applied after the Hadamard rotation).
+ *
+ * For each row n of W [N, K]: rotate along K in blocks of had_block; take
+ * a = max_k |w'| (float32); s_n = a / 1.5 (MNZ), a / 4 (POT) or a / 7 (INT4)
+ * in float32, then rounded to scale_dtype (round to nearest even); codes are
+ * decided against that stored scale:
+ *   MNZ: outer level iff |w'| > s_n; POT: outer iff 2|w'| > 5 s_n (exact);
+ *        sign from w' < 0 (so -0 and ties go to the positive/inner level);
+ *   INT4: q = clamp(rint(w' / s_n), -7, 7), IEEE float32 division.
+ * A row with s_n == 0 gets code 0 (MNZ/POT: +inner) or q = 0 everywhere.
+ *
+ *   W       [N, K] float32 (QIFT_F32) or bfloat16 (QIFT_BF16)
+ *   K       multiple of 64, K <= QIFT_MAX_ROW; had_block | K
+ *   codes   out: [N, K/16] uint32 (MNZ, POT) or [N, K/8] uint32 (INT4);
+ *           16-byte aligned
+ *   scales  out: [N] float32 (QIFT_F32) or float16 (QIFT_F16)
+ * N = 0 is a no-op.
+ */
+qift_status qift_quantize_weights(const void* W, qift_dtype w_dtype, int64_t N, int64_t K,
+                                  int32_t had_block, qift_levels levels, uint32_t* codes,
+                                  void* scales, qift_dtype scale_dtype, qift_stream stream);
+
+/*
+ * qift_rotate_quant_act -- online activation path (Qift abstract: rotated
+ * W2A4 inference, 4-bit activations): rotate each token along K in blocks of
+ * had_block (float32 butterflies), then per token
+ *   s_a = max_k |x'| / 7 (IEEE float32), q = clamp(rint(x' / s_a), -7, 7)
+ * (round half to even, IEEE division); an all-zero token gives s_a = 0, q = 0.
+ *
+ *   X      [M, K] float32 (QIFT_F32) or bfloat16 (QIFT_BF16)
+ *   K      even, K <= QIFT_MAX_ROW; had_block | K
+ *   xq     out: [M, K/2] int4 pairs (layout above)
+ *   s_a    out: [M] float32
+ *   x_rot  out, optional (may be NULL): [M, K] float32 rotated activations
+ * M = 0 is a no-op.
+ */
+qift_status qift_rotate_quant_act(const void* X, qift_dtype x_dtype, int64_t M, int64_t K,
+                                  int32_t had_block, uint8_t* xq, float* s_a, float* x_rot,
+                                  qift_stream stream);
+
+/*
+ * qift_w2a4_linear -- decoded weight application (Qift abstract: "sign-and-
+ * shift decoded weight application" for the power-of-two set; the half-scale
+ * integer form for the main set):
+ *   acc[m, n] = sum_k q[m, k] * level[n, k]            (exact, int32)
+ *   Y[m, n]   = acc[m, n] * s_a[m] * s_w[n] * kappa    (float32)
+ * with level the integer level of the code (half-scale for MNZ) and
+ * kappa = 1/2 for MNZ, 1 for POT and INT4. y_dtype QIFT_I32 stores acc itself.
+ * M <= 16 runs the weight-streaming decode kernel, M > 16 the matrix-core
+ * prefill kernel; both give identical results.
+ *
+ *   xq, s_a   [M, K/2] int4, [M] float32 (as written by qift_rotate_quant_act)
+ *   K         multiple of 64, K <= 65536
+ *   codes     [N, K/16] (2-bit) or [N, K/8] (INT4) uint32; 16-byte aligned
+ *   scales    [N] float32 or float16 (scale_dtype)
+ *   Y         out: [M, N] float32, bfloat16 or int32 (y_dtype)
+ *   xq must be 16-byte aligned.
+ * M = 0 or N = 0 is a no-op.
+ */
+qift_status qift_w2a4_linear(const uint8_t* xq, const float* s_a, int64_t M, int64_t K,
+                             const uint32_t* codes, const void* scales, qift_dtype scale_dtype,
+                             qift_levels levels, int64_t N, void* Y, qift_dtype y_dtype,
+                             qift_stream stream);
+
+/*
+ * qift_kv4_quant -- KV4 (Qift abstract: rotated W2A4/KV4 inference): each
+ * head vector KV[t, h, :] is rotated in blocks of had_block along D, then
+ * quantized to int4 with its own scale s = max|v'| / 7, exactly as the
+ * activation path.
+ *
+ *   KV      [T, H, D] bfloat16 or float32; D in {16, 32, 64, 128, 256};
+ *           had_block | D
+ *   kvq     out: [T, H, D/2] int4 pairs
+ *   scales  out: [T, H] float32
+ * T*H = 0 is a no-op.
+ */
+qift_status qift_kv4_quant(const void* KV, qift_dtype dtype, int64_t T, int64_t H, int64_t D,
+                           int32_t had_block, uint8_t* kvq, float* scales, qift_stream stream);
+
+/*
+ * Grouped linear: many independent W2A4 linears (for example every linear of
+ * a decoder stack) in one launch. Each descriptor is one qift_w2a4_linear
+ * call with M <= 16; levels may differ between descriptors.
+ *
+ * 1. qift_linear_group_workspace_bytes(descs, count, &bytes) gives the size
+ *    of the device workspace the plan needs.
+ * 2. qift_linear_group_prepare validates every descriptor (same rules as
+ *    qift_w2a4_linear), builds the plan on the host and copies it into
+ *    `workspace` (device memory, 256-byte aligned, caller-owned) on `stream`,
+ *    then waits for that copy; the host array may be freed afterwards. It
+ *    writes to *launch_tiles the number of workgroup tiles of the plan.
+ *    Linears with larger K come first in the plan, so that the longest tiles
+ *    are dispatched first.
+ * 3. qift_w2a4_linear_grouped(workspace, launch_tiles, stream) runs every
+ *    linear of the plan; launch_tiles must be the value prepare returned.
+ *    The plan stays valid while the buffers it names stay allocated; their
+ *    contents may change between runs.
+ */
+typedef struct qift_linear_desc {
+  const uint8_t* xq;      /* [M, K/2] int4                         */
+  const float* s_a;       /* [M] float32                           */
+  const uint32_t* codes;  /* [N, K/16] or [N, K/8] uint32          */
+  const void* scales;     /* [N], dtype given to prepare           */
+  void* Y;                /* [M, N], dtype given to prepare        */
+  int64_t M, K, N;
+  int32_t levels;         /* a qift_levels value                   */
+  int32_t reserved;       /* must be 0                             */
+} qift_linear_desc;
+
+qift_status qift_linear_group_workspace_bytes(const qift_linear_desc* descs, int32_t count,
+                                              size_t* bytes);
+qift_status qift_linear_group_prepare(const qift_linear_desc* descs, int32_t count,
+                                      qift_dtype scale_dtype, qift_dtype y_dtype,
+                                      void* workspace, size_t workspace_bytes,
+                                      int64_t* launch_tiles, qift_stream stream);
+qift_status qift_w2a4_linear_grouped(const void* workspace, int64_t launch_tiles,
+                                     qift_stream stream);
+
+/* Human-readable name of a status, and the detail of this thread's last
+ * error (empty string if none). Both return static or thread-local storage. */
+const char* qift_status_string(qift_status s);
+const char* qift_last_error(void);
+int32_t qift_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QIFT_H */

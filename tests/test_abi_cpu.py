@@ -1,0 +1,184 @@
+"""Host-side checks of libqift.so that need no GPU: the library loads, it
+exports every function declared in include/qift.h, and invalid arguments are
+rejected with the documented status before anything is launched (these calls
+never reach the HIP runtime)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import bit_quantized_fwht_amd as q
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "qift.h")
+
+V = ctypes.c_void_p
+A16 = V(0x10000)   # fake, 16-byte aligned device addresses (never dereferenced)
+A16b = V(0x20000)
+A16c = V(0x30000)
+A16d = V(0x40000)
+A16e = V(0x50000)
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*(qift_[a-z_0-9]+)\s*\(",
+                                 text, flags=re.M)))
+
+
+def test_library_loads_and_exports_every_declared_symbol():
+    lib = q.load_library()
+    names = declared_functions()
+    assert "qift_w2a4_linear" in names and "qift_kv4_quant" in names
+    assert len(names) == 10, names
+    for n in names:
+        assert hasattr(lib, n), n
+    assert q.abi_version() == 1
+    for s in range(5):
+        assert q.status_string(s).startswith("QIFT_")
+
+
+def lin(**kw):
+    args = dict(xq=A16, s_a=A16b, M=4, K=256, codes=A16c, scales=A16d, sd=q.QIFT_F16, lv=0,
+                N=64, Y=A16e, yd=q.QIFT_F32)
+    args.update(kw)
+    return q._C.qift_w2a4_linear(args["xq"], args["s_a"], args["M"], args["K"], args["codes"],
+                                 args["scales"], args["sd"], args["lv"], args["N"], args["Y"],
+                                 args["yd"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(xq=None), q.QIFT_ERR_INVALID_ARG),
+    (dict(codes=None), q.QIFT_ERR_INVALID_ARG),
+    (dict(K=100), q.QIFT_ERR_INVALID_ARG),
+    (dict(K=0), q.QIFT_ERR_INVALID_ARG),
+    (dict(K=65536 + 64), q.QIFT_ERR_UNSUPPORTED),
+    (dict(M=-1), q.QIFT_ERR_INVALID_ARG),
+    (dict(lv=7), q.QIFT_ERR_INVALID_ARG),
+    (dict(sd=q.QIFT_BF16), q.QIFT_ERR_INVALID_ARG),
+    (dict(yd=q.QIFT_F16), q.QIFT_ERR_INVALID_ARG),
+    (dict(xq=V(0x10008)), q.QIFT_ERR_ALIGNMENT),
+    (dict(codes=V(0x30004)), q.QIFT_ERR_ALIGNMENT),
+    (dict(Y=V(0x50001)), q.QIFT_ERR_ALIGNMENT),
+])
+def test_linear_rejects(kw, status):
+    assert lin(**kw) == status
+    assert q.last_error() != ""
+
+
+def test_linear_empty_is_noop():
+    # M = 0 or N = 0: valid, nothing to do, no launch
+    assert lin(M=0, xq=None, s_a=None, codes=None, scales=None, Y=None) == q.QIFT_OK
+    assert lin(N=0) == q.QIFT_OK
+
+
+def rot(**kw):
+    args = dict(X=A16, xd=q.QIFT_BF16, M=2, K=256, B=256, xq=A16b, s_a=A16c, x_rot=None)
+    args.update(kw)
+    return q._C.qift_rotate_quant_act(args["X"], args["xd"], args["M"], args["K"], args["B"],
+                                      args["xq"], args["s_a"], args["x_rot"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(B=3), q.QIFT_ERR_INVALID_ARG),
+    (dict(B=0), q.QIFT_ERR_INVALID_ARG),
+    (dict(B=512), q.QIFT_ERR_INVALID_ARG),         # does not divide K=256
+    (dict(K=8192 * 2, B=8192), q.QIFT_ERR_UNSUPPORTED),
+    (dict(K=16384 + 2), q.QIFT_ERR_UNSUPPORTED),
+    (dict(K=255, B=1), q.QIFT_ERR_INVALID_ARG),
+    (dict(xd=q.QIFT_F16), q.QIFT_ERR_INVALID_ARG),
+    (dict(X=None), q.QIFT_ERR_INVALID_ARG),
+    (dict(xq=V(0x20004)), q.QIFT_ERR_ALIGNMENT),
+    (dict(x_rot=V(0x20002)), q.QIFT_ERR_ALIGNMENT),
+])
+def test_rotate_rejects(kw, status):
+    assert rot(**kw) == status
+
+
+def test_rotate_empty_is_noop():
+    assert rot(M=0, X=None, xq=None, s_a=None) == q.QIFT_OK
+
+
+def qw(**kw):
+    args = dict(W=A16, wd=q.QIFT_F32, N=8, K=256, B=256, lv=0, codes=A16b, scales=A16c,
+                sd=q.QIFT_F16)
+    args.update(kw)
+    return q._C.qift_quantize_weights(args["W"], args["wd"], args["N"], args["K"], args["B"],
+                                      args["lv"], args["codes"], args["scales"], args["sd"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(K=96), q.QIFT_ERR_INVALID_ARG),
+    (dict(lv=3), q.QIFT_ERR_INVALID_ARG),
+    (dict(sd=q.QIFT_I32), q.QIFT_ERR_INVALID_ARG),
+    (dict(wd=q.QIFT_I32), q.QIFT_ERR_INVALID_ARG),
+    (dict(codes=V(0x20008)), q.QIFT_ERR_ALIGNMENT),
+    (dict(B=6), q.QIFT_ERR_INVALID_ARG),
+    (dict(scales=None), q.QIFT_ERR_INVALID_ARG),
+])
+def test_quantize_weights_rejects(kw, status):
+    assert qw(**kw) == status
+
+
+def kv(**kw):
+    args = dict(KV=A16, d=q.QIFT_BF16, T=4, H=2, D=128, B=128, kvq=A16b, scales=A16c)
+    args.update(kw)
+    return q._C.qift_kv4_quant(args["KV"], args["d"], args["T"], args["H"], args["D"], args["B"],
+                               args["kvq"], args["scales"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(D=96, B=32), q.QIFT_ERR_UNSUPPORTED),
+    (dict(D=512, B=512), q.QIFT_ERR_UNSUPPORTED),
+    (dict(B=256), q.QIFT_ERR_UNSUPPORTED),
+    (dict(B=12), q.QIFT_ERR_INVALID_ARG),
+    (dict(KV=V(0x10002)), q.QIFT_ERR_ALIGNMENT),
+    (dict(kvq=None), q.QIFT_ERR_INVALID_ARG),
+    (dict(T=-1), q.QIFT_ERR_INVALID_ARG),
+])
+def test_kv4_rejects(kw, status):
+    assert kv(**kw) == status
+
+
+def test_kv4_empty_is_noop():
+    assert kv(T=0, KV=None, kvq=None, scales=None) == q.QIFT_OK
+
+
+def make_desc(**kw):
+    d = dict(xq=0x10000, s_a=0x20000, codes=0x30000, scales=0x40000, Y=0x50000, M=1, K=4096,
+             N=4096, levels=0, reserved=0)
+    d.update(kw)
+    return q.qift_linear_desc(d["xq"], d["s_a"], d["codes"], d["scales"], d["Y"], d["M"], d["K"],
+                              d["N"], d["levels"], d["reserved"])
+
+
+def test_group_workspace_and_rejects():
+    arr = (q.qift_linear_desc * 3)(make_desc(), make_desc(K=11008, N=4096), make_desc(N=11008))
+    nbytes = ctypes.c_size_t(0)
+    assert q._C.qift_linear_group_workspace_bytes(arr, 3, ctypes.byref(nbytes)) == q.QIFT_OK
+    tiles = 16 + 16 + 43
+    assert nbytes.value >= 64 + 3 * 88 + 4 * tiles and nbytes.value % 256 == 0
+    bad = (q.qift_linear_desc * 2)(make_desc(), make_desc(M=17))
+    assert q._C.qift_linear_group_workspace_bytes(bad, 2, ctypes.byref(nbytes)) == q.QIFT_ERR_UNSUPPORTED
+    assert "descriptor 1" in q.last_error()
+    bad = (q.qift_linear_desc * 1)(make_desc(reserved=1))
+    assert q._C.qift_linear_group_workspace_bytes(bad, 1, ctypes.byref(nbytes)) == q.QIFT_ERR_INVALID_ARG
+    bad = (q.qift_linear_desc * 1)(make_desc(codes=0x30008))
+    assert q._C.qift_linear_group_workspace_bytes(bad, 1, ctypes.byref(nbytes)) == q.QIFT_ERR_ALIGNMENT
+    tiles_out = ctypes.c_int64(0)
+    # too small a workspace, or misaligned: rejected before any copy
+    assert q._C.qift_linear_group_prepare(arr, 3, q.QIFT_F16, q.QIFT_F32, V(0x100000), 64,
+                                          ctypes.byref(tiles_out), None) == q.QIFT_ERR_INVALID_ARG
+    assert q._C.qift_linear_group_prepare(arr, 3, q.QIFT_F16, q.QIFT_F32, V(0x100010), 1 << 20,
+                                          ctypes.byref(tiles_out), None) == q.QIFT_ERR_ALIGNMENT
+    assert q._C.qift_w2a4_linear_grouped(None, 1, None) == q.QIFT_ERR_INVALID_ARG
+    assert q._C.qift_w2a4_linear_grouped(V(0x100000), -1, None) == q.QIFT_ERR_INVALID_ARG
+    assert q._C.qift_w2a4_linear_grouped(V(0x100000), 0, None) == q.QIFT_OK
+
+
+def test_binding_rejects_host_tensors():
+    import torch
+    with pytest.raises(ValueError):
+        q.qift_rotate_quant_act(torch.zeros(2, 256), 256)

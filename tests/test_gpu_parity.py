@@ -1,0 +1,403 @@
+"""GPU parity: every C-ABI call against the CPU oracle on the same seeded
+inputs.
+
+Bar (from the method's contract): packed codes, int4 activations and int32
+accumulators bit-exact when both sides see identical rotated inputs; rotated
+activations within 1e-5 relative; end-to-end float32 outputs within 1e-3
+relative L2, with at most 1e-4 of the codes flipped and only at rounding
+near-ties. Sizes span several tiles with ragged tails; the full LLaMA shapes
+are checked on sampled outputs.
+"""
+import numpy as np
+import pytest
+import torch
+
+import bit_quantized_fwht_amd as q
+from oracle import qift_oracle as O
+import synth_inputs as si
+from gpu_util import (DEV, say, to_dev, u32_to_dev, dev_u32, rel_l2, check_act_codes,
+                      check_weight_codes)
+
+pytestmark = pytest.mark.gpu
+
+SCALE_T = {"f16": torch.float16, "f32": torch.float32}
+
+
+def sync():
+    torch.cuda.synchronize()
+
+
+# ---------------------------------------------------------------------------
+# rotate + per-token int4 (qift_rotate_quant_act)
+# ---------------------------------------------------------------------------
+
+def gpu_rotate(X_t, B, want=True):
+    xq, s_a, xr = q.qift_rotate_quant_act(X_t, B, want_x_rot=want)
+    sync()
+    return O.unpack_int4(xq.cpu().numpy()), s_a.cpu().numpy(), (xr.cpu().numpy() if want else None)
+
+
+def test_rotate_small_linear_case():
+    W, X, _ = si.small_linear_case()
+    say("rotate small case M=16 K=256 B=256")
+    qg, sg, xg = gpu_rotate(to_dev(X), 256)
+    qo, so, xo32, xo64 = O.rotate_quant_act(X.astype(np.float64), 256)
+    for r in range(16):
+        row_err = np.abs(xg[r].astype(np.float64) - xo64[r])
+        assert row_err.max() <= 1e-5 * np.abs(xo64[r]).max()
+        assert rel_l2(xg[r], xo64[r]) <= 1e-5
+    assert np.allclose(sg, so, rtol=1e-6, atol=0)
+    check_act_codes(qg, qo, xo64, so)
+
+
+@pytest.mark.parametrize("B", [1, 2, 4, 8, 16, 32, 64, 128, 256, 512, 1024, 2048, 4096])
+def test_rotate_every_block_size(B):
+    M, K = 3, max(2 * B, 256)
+    X = si.activations(M, K, seed=100 + B, n_outliers=4)
+    say(f"rotate M={M} K={K} B={B}")
+    Xt = si.to_bf16(X).to(DEV)
+    qg, sg, xg = gpu_rotate(Xt, B)
+    Xv = si.bf16_values(Xt)
+    qo, so, xo32, xo64 = O.rotate_quant_act(Xv, B)
+    for r in range(M):
+        assert np.abs(xg[r] - xo64[r]).max() <= 1e-5 * np.abs(xo64[r]).max()
+    assert np.allclose(sg, so, rtol=1e-6, atol=0)
+    check_act_codes(qg, qo, xo64, so)
+
+
+@pytest.mark.parametrize("M,K", [(1, 64), (5, 10), (17, 256), (33, 4096), (7, 11008), (2, 14336),
+                                 (3, 16384), (4, 18), (2, 2)])
+def test_rotate_quant_bitexact_given_rotated_input(M, K):
+    """had_block = 1 and the oracle's float32 rotated values as input: the
+    quantizer must reproduce the oracle's codes and scales bit for bit."""
+    B = 256 if K % 256 == 0 else 2
+    X = si.activations(M, K, seed=7 * K + M, n_outliers=min(4, K // 2))
+    _, _, xr32, _ = O.rotate_quant_act(X.astype(np.float64), B)
+    say(f"bitexact quant M={M} K={K}")
+    qg, sg, xg = gpu_rotate(to_dev(xr32), 1)
+    qo, so = O.quant_sym4(xr32)
+    assert np.array_equal(sg.view(np.uint32), so.view(np.uint32))
+    assert np.array_equal(qg, qo.astype(np.int64))
+    assert np.array_equal(xg.view(np.uint32), xr32.view(np.uint32))
+
+
+def test_rotate_rne_ties_and_zero_rows():
+    import json, os
+    g = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "rne_ties.json")))
+    row = np.array(g["row"] + [0.0] * 6, dtype=np.float32)  # pad to 16
+    X = np.stack([row, np.zeros(16, np.float32), -row])
+    say("rne ties")
+    qg, sg, _ = gpu_rotate(to_dev(X), 1, want=False)
+    assert qg[0, :10].tolist() == g["codes"]
+    assert qg[2, :10].tolist() == [-c for c in g["codes"]]
+    assert sg[0] == 1.0 and sg[1] == 0.0 and np.all(qg[1] == 0)
+
+
+def test_rotate_one_hot_closed_form():
+    B, j, c = 4096, 1234, 2.5
+    X = np.zeros((2, 2 * B), np.float32)
+    X[1, B + j] = c
+    say("rotate one-hot B=4096")
+    qg, sg, xg = gpu_rotate(to_dev(X), B)
+    popc = np.array([bin(i & j).count("1") for i in range(B)])
+    expect = np.where(popc % 2 == 0, 7, -7)
+    assert np.array_equal(qg[1, B:], expect) and np.all(qg[1, :B] == 0)
+    assert np.all(qg[0] == 0) and sg[0] == 0
+
+
+# ---------------------------------------------------------------------------
+# weight quantizer (qift_quantize_weights)
+# ---------------------------------------------------------------------------
+
+def gpu_quant_weights(W_t, B, kind, sdt):
+    codes, scales = q.qift_quantize_weights(W_t, B, kind, SCALE_T[sdt])
+    sync()
+    words = dev_u32(codes)
+    c = O.unpack_int4(words.view(np.uint8).reshape(W_t.shape[0], -1)) if kind == "int4" \
+        else O.unpack_codes2(words)
+    return c, scales.float().cpu().numpy(), words
+
+
+@pytest.mark.parametrize("kind", ["mnz", "pot", "int4"])
+@pytest.mark.parametrize("sdt", ["f16", "f32"])
+@pytest.mark.parametrize("N,K", [(1, 64), (37, 256), (130, 4096), (5, 11008)])
+def test_quantize_weights_bitexact_given_rotated_input(kind, sdt, N, K):
+    B = 256 if K % 256 == 0 else 64
+    W = si.weights(N, K, seed=N * 31 + K, sigma=0.02)
+    wr32 = O.rotate(W.astype(np.float64), B).astype(np.float32)
+    say(f"bitexact weights {kind} {sdt} N={N} K={K}")
+    cg, sg, words = gpu_quant_weights(to_dev(wr32), 1, kind, sdt)
+    co, so, _ = O.quantize_weights(wr32.astype(np.float64), 1, kind, sdt)
+    assert np.array_equal(sg.astype(np.float32).view(np.uint32),
+                          so.astype(np.float32).view(np.uint32))
+    assert np.array_equal(cg, co)
+    assert np.array_equal(words, O.pack_weights(co, kind))
+
+
+@pytest.mark.parametrize("kind", ["mnz", "pot"])
+def test_quantize_weights_ties_and_zero_rows(kind):
+    import json, os
+    g = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "weight_ties.json")))[kind]
+    row = np.array(g["row"] * 4, np.float32)  # 64 features
+    W = np.stack([row, np.zeros(64, np.float32), -row, np.full(64, 1e-30, np.float32)])
+    say(f"weight ties {kind}")
+    for sdt in ("f16", "f32"):
+        cg, sg, _ = gpu_quant_weights(to_dev(W), 1, kind, sdt)
+        co, so, _ = O.quantize_weights(W.astype(np.float64), 1, kind, sdt)
+        assert cg[0, :16].tolist() == g["codes"]
+        assert np.array_equal(cg, co) and np.array_equal(sg, so.astype(np.float32))
+
+
+@pytest.mark.parametrize("kind", ["mnz", "pot", "int4"])
+def test_quantize_weights_rotated_small_case(kind):
+    W, _, _ = si.small_linear_case()
+    say(f"weights small case {kind}")
+    cg, sg, _ = gpu_quant_weights(to_dev(W), 256, kind, "f32")
+    co, so, wr32 = O.quantize_weights(W.astype(np.float64), 256, kind, "f32")
+    assert np.allclose(sg, so, rtol=1e-6, atol=0)
+    w64 = O.rotate(W.astype(np.float64), 256)
+    check_weight_codes(O.code_levels(cg, kind), O.code_levels(co, kind), w64, so, kind, s_gpu=sg)
+
+
+# ---------------------------------------------------------------------------
+# the linear (qift_w2a4_linear): int32 bit-exact on oracle-packed inputs
+# ---------------------------------------------------------------------------
+
+def random_linear_inputs(M, K, N, kind, seed):
+    qa = si.uniform_int4((M, K), seed=seed)
+    codes = si.uniform_int4((N, K), seed=seed + 1) if kind == "int4" \
+        else si.uniform_codes((N, K), 4, seed=seed + 1)
+    s_a = si.positive_scales(M, seed + 2)
+    s_w = si.positive_scales(N, seed + 3).astype(np.float16)
+    return qa, codes, s_a, s_w
+
+
+def run_linear(qa, codes, s_a, s_w, kind, out_dtype):
+    xq = torch.from_numpy(O.pack_int4(qa)).to(DEV)
+    cw = u32_to_dev(O.pack_weights(codes, kind))
+    Y = q.qift_w2a4_linear(xq, to_dev(s_a), cw, to_dev(s_w.astype(np.float32), torch.float16),
+                           kind, out_dtype)
+    sync()
+    return Y
+
+
+LIN_SHAPES = [(1, 64, 1), (1, 256, 17), (3, 320, 64), (4, 4096, 257), (8, 192, 300),
+              (16, 1024, 129), (17, 256, 130), (31, 128, 63), (64, 4096, 256), (129, 576, 200),
+              (200, 2048, 385)]
+
+
+@pytest.mark.parametrize("kind", ["mnz", "pot", "int4"])
+@pytest.mark.parametrize("M,K,N", LIN_SHAPES)
+def test_linear_int32_bitexact(kind, M, K, N):
+    qa, codes, s_a, s_w = random_linear_inputs(M, K, N, kind, seed=M * 1000 + K + N)
+    say(f"linear i32 {kind} M={M} K={K} N={N}")
+    Y = run_linear(qa, codes, s_a, s_w, kind, torch.int32).cpu().numpy()
+    acc, _ = O.linear(qa, s_a, codes, s_w.astype(np.float64), kind)
+    assert np.array_equal(Y.astype(np.int64), acc)
+
+
+@pytest.mark.parametrize("kind", ["mnz", "pot", "int4"])
+@pytest.mark.parametrize("M,K,N", [(1, 256, 33), (16, 512, 100), (40, 1024, 150)])
+def test_linear_float_epilogue(kind, M, K, N):
+    qa, codes, s_a, s_w = random_linear_inputs(M, K, N, kind, seed=5 + M + N)
+    say(f"linear f32/bf16 {kind} M={M} K={K} N={N}")
+    _, y = O.linear(qa, s_a, codes, s_w.astype(np.float64), kind)
+    Yf = run_linear(qa, codes, s_a, s_w, kind, torch.float32).cpu().numpy().astype(np.float64)
+    assert np.all(np.abs(Yf - y) <= 4e-7 * np.abs(y) + 1e-30)
+    Yb = run_linear(qa, codes, s_a, s_w, kind, torch.bfloat16).float().cpu().numpy()
+    assert np.all(np.abs(Yb - y) <= 2 ** -8 * np.abs(y) + 1e-30)
+
+
+def test_linear_extremes_do_not_overflow():
+    """All activations +-7 against all outer levels at the largest K."""
+    for kind, code in (("mnz", 1), ("pot", 1), ("int4", 7)):
+        M, K, N = 17, 65536, 16
+        qa = np.full((M, K), 7)
+        qa[1::2] = -7
+        codes = np.full((N, K), code)
+        s_a = np.ones(M, np.float32)
+        s_w = np.ones(N, np.float16)
+        say(f"linear extremes {kind}")
+        for m_sub in (16, 17):  # decode and prefill kernels
+            Y = run_linear(qa[:m_sub], codes, s_a[:m_sub], s_w, kind, torch.int32).cpu().numpy()
+            acc, _ = O.linear(qa[:m_sub], s_a[:m_sub], codes, s_w.astype(np.float64), kind)
+            assert np.array_equal(Y.astype(np.int64), acc)
+
+
+def test_linear_empty_batch():
+    xq = torch.empty((0, 128), dtype=torch.uint8, device=DEV)
+    Y = q.qift_w2a4_linear(xq, torch.empty(0, device=DEV), torch.zeros((8, 16), dtype=torch.int32,
+                           device=DEV), torch.ones(8, dtype=torch.float16, device=DEV), "mnz")
+    assert Y.shape == (0, 8)
+
+
+# ---------------------------------------------------------------------------
+# end to end: quantize weights, rotate + quantize activations, linear
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("kind", ["mnz", "pot", "int4"])
+def test_end_to_end_small_linear_case(kind):
+    W, X, _ = si.small_linear_case()
+    say(f"end to end small case {kind}")
+    cw, sw = q.qift_quantize_weights(to_dev(W), 256, kind, torch.float32)
+    xq, s_a, _ = q.qift_rotate_quant_act(to_dev(X), 256)
+    Y = q.qift_w2a4_linear(xq, s_a, cw, sw, kind, torch.float32)
+    sync()
+    qo, so, _, xo64 = O.rotate_quant_act(X.astype(np.float64), 256)
+    co, swo, _ = O.quantize_weights(W.astype(np.float64), 256, kind, "f32")
+    _, yo = O.linear(qo, so, co, swo.astype(np.float64), kind)
+    assert rel_l2(Y.cpu().numpy(), yo) <= 1e-3
+    check_act_codes(O.unpack_int4(xq.cpu().numpy()), qo, xo64, so)
+
+
+# ---------------------------------------------------------------------------
+# KV4 (qift_kv4_quant)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("D,B", [(128, 128), (128, 64), (128, 1), (64, 64), (256, 256), (16, 16),
+                                 (32, 8)])
+def test_kv4_matches_oracle(D, B):
+    T, H = 37, 5
+    KV = si.kv(T, H, D, seed=D + B)
+    KVt = si.to_bf16(KV).to(DEV)
+    say(f"kv4 T={T} H={H} D={D} B={B}")
+    kvq, sc = q.qift_kv4_quant(KVt, B)
+    sync()
+    qo, so, xr = O.kv4_quant(si.bf16_values(KVt), B)
+    qg = O.unpack_int4(kvq.cpu().numpy())
+    sg = sc.cpu().numpy()
+    assert np.allclose(sg, so, rtol=1e-6, atol=0)
+    xo64 = O.rotate(si.bf16_values(KVt).reshape(T * H, D), B).reshape(T, H, D)
+    check_act_codes(qg, qo, xo64, so)
+    if B == 1:
+        assert np.array_equal(qg, qo.astype(np.int64))
+
+
+def test_kv4_bitexact_given_rotated_input():
+    T, H, D = 9, 4, 128
+    KV = si.kv(T, H, D, seed=3)
+    _, _, xr32 = O.kv4_quant(KV.astype(np.float64), 128)
+    say("kv4 bitexact")
+    kvq, sc = q.qift_kv4_quant(to_dev(xr32), 1)
+    sync()
+    qo, so, _ = O.kv4_quant(xr32.astype(np.float64), 1)
+    assert np.array_equal(O.unpack_int4(kvq.cpu().numpy()), qo.astype(np.int64))
+    assert np.array_equal(sc.cpu().numpy().view(np.uint32), so.view(np.uint32))
+
+
+# ---------------------------------------------------------------------------
+# grouped launch == single calls
+# ---------------------------------------------------------------------------
+
+def test_grouped_matches_single_calls():
+    rng_shapes = [(1, 4096, 4096, "mnz"), (4, 11008, 4096, "mnz"), (8, 4096, 1000, "pot"),
+                  (16, 256, 300, "int4"), (3, 64, 17, "mnz"), (0, 128, 64, "mnz"),
+                  (2, 14336, 512, "pot")]
+    items, refs = [], []
+    for i, (M, K, N, kind) in enumerate(rng_shapes):
+        qa, codes, s_a, s_w = random_linear_inputs(M, K, N, kind, seed=900 + i)
+        xq = torch.from_numpy(O.pack_int4(qa)).to(DEV)
+        cw = u32_to_dev(O.pack_weights(codes, kind))
+        sa = to_dev(s_a)
+        swt = to_dev(s_w.astype(np.float32), torch.float16)
+        Y = torch.full((M, N), -1, dtype=torch.int32, device=DEV)
+        items.append(dict(xq=xq, s_a=sa, codes=cw, scales=swt, Y=Y, levels=kind))
+        refs.append(O.linear(qa, s_a, codes, s_w.astype(np.float64), kind)[0])
+    say("grouped linear")
+    grp = q.LinearGroup(items, scale_dtype=torch.float16, y_dtype=torch.int32)
+    for rep in range(3):
+        for it in items:
+            it["Y"].fill_(-1)
+        grp.run()
+        sync()
+        for it, ref in zip(items, refs):
+            assert np.array_equal(it["Y"].cpu().numpy().astype(np.int64), ref)
+
+
+# ---------------------------------------------------------------------------
+# full LLaMA shapes, sampled
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("M,K,N,kind", [
+    (1, 4096, 11008, "mnz"), (8, 11008, 4096, "mnz"), (4, 4096, 4096, "mnz"),
+    (1, 14336, 4096, "pot"), (16, 4096, 11008, "int4"),
+    (2048, 4096, 11008, "mnz"), (2048, 11008, 4096, "mnz"), (4096, 4096, 1024, "pot"),
+    (4096, 14336, 4096, "pot"),
+])
+def test_full_shape_linear_sampled(M, K, N, kind):
+    """Oracle-packed random codes and activations at the full shapes; the
+    oracle computes a sample of rows (all columns) and a sample of columns
+    (all rows) exactly."""
+    rng = np.random.default_rng(M + K + N)
+    qa = si.uniform_int4((M, K), seed=K + 1)
+    codes = si.uniform_int4((N, K), seed=N + 2) if kind == "int4" \
+        else si.uniform_codes((N, K), 4, seed=N + 2)
+    s_a = si.positive_scales(M, 3)
+    s_w = si.positive_scales(N, 4).astype(np.float16)
+    say(f"full shape linear {kind} M={M} K={K} N={N}")
+    Y = run_linear(qa, codes, s_a, s_w, kind, torch.int32).cpu().numpy().astype(np.int64)
+    rows = np.unique(np.concatenate([[0, M - 1], rng.choice(M, min(M, 24), replace=False)]))
+    cols = np.unique(np.concatenate([[0, N - 1], rng.choice(N, min(N, 24), replace=False)]))
+    acc_r, _ = O.linear(qa[rows], s_a[rows], codes, s_w.astype(np.float64), kind)
+    assert np.array_equal(Y[rows], acc_r)
+    acc_c, _ = O.linear(qa, s_a, codes[cols], s_w[cols].astype(np.float64), kind)
+    assert np.array_equal(Y[:, cols], acc_c)
+
+
+@pytest.mark.parametrize("N,K,B,kind,sigma", [(11008, 4096, 4096, "mnz", 0.02),
+                                               (4096, 11008, 256, "mnz", 0.02),
+                                               (4096, 14336, 1024, "pot", 0.015),
+                                               (1024, 4096, 4096, "int4", 0.02)])
+def test_full_shape_weight_quantizer_sampled(N, K, B, kind, sigma):
+    W_t = si.device_weights(N, K, seed=17, sigma=sigma, device=DEV)
+    say(f"full shape weights {kind} N={N} K={K} B={B}")
+    cg_t, sg_t = q.qift_quantize_weights(W_t, B, kind, torch.float16)
+    sync()
+    rows = np.unique(np.concatenate([[0, N - 1], np.random.default_rng(1).choice(N, 30, replace=False)]))
+    Wr = W_t[torch.from_numpy(rows).to(DEV)].cpu().numpy().astype(np.float64)
+    co, so, _ = O.quantize_weights(Wr, B, kind, "f16")
+    words = dev_u32(cg_t)[rows]
+    cg = O.unpack_int4(words.view(np.uint8).reshape(len(rows), -1)) if kind == "int4" \
+        else O.unpack_codes2(words)
+    sg = sg_t.float().cpu().numpy()[rows]
+    so32 = so.astype(np.float32)
+    assert np.all(np.abs(sg - so32) <= 2 ** -10 * so32)  # at most one float16 ulp
+    check_weight_codes(O.code_levels(cg, kind), O.code_levels(co, kind), O.rotate(Wr, B), so,
+                       kind, s_gpu=sg)
+
+
+def test_full_shape_kv4_sampled():
+    T, H, D = 4096, 32, 128
+    KV_t = si.device_kv(T, H, D, seed=5, device=DEV)
+    say("full shape kv4 [4096, 32, 128]")
+    kvq, sc = q.qift_kv4_quant(KV_t, 128)
+    sync()
+    ts = np.random.default_rng(2).choice(T, 64, replace=False)
+    sub = KV_t[torch.from_numpy(ts).to(DEV)].float().cpu().numpy().astype(np.float64)
+    qo, so, _ = O.kv4_quant(sub, 128)
+    qg = O.unpack_int4(kvq.cpu().numpy()[ts])
+    assert np.allclose(sc.cpu().numpy()[ts], so, rtol=1e-6, atol=0)
+    xo64 = O.rotate(sub.reshape(-1, D), 128).reshape(sub.shape)
+    check_act_codes(qg, qo, xo64, so)
+
+
+def test_full_shape_end_to_end_prefill():
+    """LLaMA-7B up_proj at M=2048: GPU weights + activations + GEMM against
+    the oracle on sampled tokens and channels (rel L2 <= 1e-3)."""
+    M, K, N, B = 2048, 4096, 11008, 4096
+    W_t = si.device_weights(N, K, seed=23, sigma=0.02, device=DEV)
+    X_t = si.device_activations(M, K, seed=24, device=DEV)
+    say("full shape end to end prefill")
+    cw, sw = q.qift_quantize_weights(W_t, B, "mnz", torch.float16)
+    xq, s_a, _ = q.qift_rotate_quant_act(X_t, B)
+    Y = q.qift_w2a4_linear(xq, s_a, cw, sw, "mnz", torch.float32)
+    sync()
+    rows = np.random.default_rng(3).choice(M, 8, replace=False)
+    cols = np.random.default_rng(4).choice(N, 256, replace=False)
+    Xs = X_t[torch.from_numpy(rows).to(DEV)].float().cpu().numpy().astype(np.float64)
+    Ws = W_t[torch.from_numpy(cols).to(DEV)].cpu().numpy().astype(np.float64)
+    qo, so, _, xo64 = O.rotate_quant_act(Xs, B)
+    co, swo, _ = O.quantize_weights(Ws, B, "mnz", "f16")
+    _, yo = O.linear(qo, so, co, swo.astype(np.float64), "mnz")
+    yg = Y.cpu().numpy()[np.ix_(rows, cols)]
+    assert rel_l2(yg, yo) <= 1e-3
