@@ -1,0 +1,419 @@
+"""Benchmark of the rotated W2A4 linear on one MI355X.
+
+Headline (``value``): decode weight-stream GB/s of a LLaMA-7B-shaped stack:
+32 decoder layers x 7 linears (q, k, v, o: 4096 -> 4096; gate, up:
+4096 -> 11008; down: 11008 -> 4096 with a 256-block Hadamard), 2-bit MNZ codes
+with float16 per-channel scales (1.6217 GB of codes + scales), synthetic
+N(0, 0.02^2) weights and bf16 N(0, 1) activations with 1% outlier channels
+x20. One step = one pass over the whole stack:
+  1. rotate + int4-quantize the 96 K=4096 layer inputs (one launch),
+  2. rotate + int4-quantize the 32 K=11008 down_proj inputs (one launch),
+  3. all 224 W2A4 linears (one grouped decode launch).
+value = algorithmic weight-stream bytes of one pass / step time.
+
+Also measured and reported under "extra": the same stack at M = 4, 8, 16;
+prefill int8-MFMA TOPS at M = 2048 (up_proj, down_proj); the
+LLaMA-3.1-8B-shaped power-of-two layer (decode over 32 layer copies, prefill
+at M = 4096); the mixed W2/W4 stack (layers 0-15 MNZ, 16-31 int4) at M = 16;
+KV4 of K and V [4096, 32, 128].
+
+``roofline`` describes the dominant kernel of the step (the grouped decode
+launch): algorithmic bytes per launch / its mean duration from HIP events on
+the launch stream. ``traffic`` comes from the committed rocprofv3 counter
+summary when it was taken on the current kernel source, else null.
+``cpu_baseline`` times the CPU oracle on a bounded sample of the same stack.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+INT8_PEAK_TOPS = 5000.0        # MI355X dense int8 MFMA, TOP/s
+METRIC = "W2A4 linear: decode weight-stream GB/s + prefill int8 TOPS, % of roofline"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "linear_grouped_decode_llama7b_counters.json")
+KERNEL_SRC = os.path.join(ROOT, "bit_quantized_fwht_amd", "csrc", "linear.hip")
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=100)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--m", type=int, default=1, help="tokens per decode step for the headline")
+    p.add_argument("--only-headline", action="store_true",
+                   help="skip the extra measurements and the CPU baseline (profiling runs)")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="also run a plain 1 GiB device copy (counter calibration)")
+    return p.parse_args()
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+# ---------------------------------------------------------------------------
+# workload construction
+# ---------------------------------------------------------------------------
+
+class DecodeStack:
+    """A stack of layers, each a list of (name, K, N, had_block, levels)."""
+
+    def __init__(self, q, torch, layers, M, sigma, dev, seed0=0, scale_dtype=None):
+        import synth_inputs as si
+        self.q, self.torch = q, torch
+        self.M = M
+        scale_dtype = scale_dtype or torch.float16
+        self.codes, self.scales = [], []
+        self.items = []
+        self.bytes = 0
+        # distinct inputs per layer: the q/k/v input, the o input, the gate/up
+        # input, the down input (as in a decoder layer)
+        groups = {}
+        for li, layer in enumerate(layers):
+            for name, K, N, B, lv in layer:
+                key = ("attn" if name in ("q_proj", "k_proj", "v_proj") else
+                       "o" if name == "o_proj" else "mlp" if name in ("gate_proj", "up_proj") else "down")
+                groups.setdefault((K, B), []).append((li, key))
+        # one stacked activation buffer per (K, block)
+        self.act = {}
+        for (K, B), users in groups.items():
+            slots = sorted(set(users))
+            n_rows = len(slots) * M
+            X = si.device_activations(n_rows, K, seed=seed0 + 31 * K + B, device=dev)
+            xq = torch.empty((n_rows, K // 2), dtype=torch.uint8, device=dev)
+            sa = torch.empty((n_rows,), dtype=torch.float32, device=dev)
+            self.act[(K, B)] = dict(X=X, xq=xq, sa=sa, slot={s: i for i, s in enumerate(slots)})
+        ytot = sum(M * N for layer in layers for (_, K, N, B, lv) in layer)
+        self.Y = torch.empty((ytot,), dtype=torch.float32, device=dev)
+        yoff = 0
+        for li, layer in enumerate(layers):
+            for idx, (name, K, N, B, lv) in enumerate(layer):
+                W = si.device_weights(N, K, seed=1000 * li + idx + seed0, sigma=sigma, device=dev)
+                c, s = q.qift_quantize_weights(W, B, lv, scale_dtype)
+                del W
+                key = ("attn" if name in ("q_proj", "k_proj", "v_proj") else
+                       "o" if name == "o_proj" else "mlp" if name in ("gate_proj", "up_proj") else "down")
+                a = self.act[(K, B)]
+                r0 = a["slot"][(li, key)] * M
+                Y = self.Y[yoff:yoff + M * N].view(M, N)
+                yoff += M * N
+                self.items.append(dict(xq=a["xq"][r0:r0 + M], s_a=a["sa"][r0:r0 + M], codes=c,
+                                       scales=s, Y=Y, levels=lv))
+                self.codes.append(c)
+                self.scales.append(s)
+                self.bytes += c.numel() * 4 + s.numel() * s.element_size()
+        torch.cuda.synchronize()
+        self.group = q.LinearGroup(self.items, scale_dtype=scale_dtype, y_dtype=torch.float32)
+
+    def rotate_all(self):
+        for (K, B), a in self.act.items():
+            self.q.qift_rotate_quant_act(a["X"], B, xq=a["xq"], s_a=a["sa"])
+
+    def step(self):
+        self.rotate_all()
+        self.group.run()
+
+
+def llama7b_layers(levels="mnz"):
+    import synth_inputs as si
+    return [[(n, K, N, B, levels) for (n, K, N, B) in si.LLAMA7B_LAYER] for _ in range(si.N_LAYERS)]
+
+
+def llama31_8b_layers(levels="pot"):
+    import synth_inputs as si
+    return [[(n, K, N, B, levels) for (n, K, N, B) in si.LLAMA31_8B_LAYER] for _ in range(si.N_LAYERS)]
+
+
+def mixed_layers():
+    import synth_inputs as si
+    return [[(n, K, N, B, "mnz" if li < 16 else "int4") for (n, K, N, B) in si.LLAMA7B_LAYER]
+            for li in range(si.N_LAYERS)]
+
+
+# ---------------------------------------------------------------------------
+# timing helpers
+# ---------------------------------------------------------------------------
+
+def time_fn(torch, fn, reps, warmup=3):
+    """Median, min and mean of per-call durations (ms) from HIP events on
+    the current stream."""
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(reps)]
+    for a, b in evs:
+        a.record()
+        fn()
+        b.record()
+    torch.cuda.synchronize()
+    t = np.array([a.elapsed_time(b) for a, b in evs])
+    return float(np.median(t)), float(t.min()), float(t.mean())
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(os.path.dirname(KERNEL_SRC))):
+        with open(os.path.join(os.path.dirname(KERNEL_SRC), f), "rb") as fh:
+            h.update(f.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profile(achieved_unit_bytes):
+    """HBM bytes per grouped launch from the committed counter summary, if
+    it was taken on the current kernel sources; else None."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            prof = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if prof.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return prof.get("hbm_bytes_per_launch")
+
+
+# ---------------------------------------------------------------------------
+# CPU baseline: the oracle on a bounded sample of the decode stack
+# ---------------------------------------------------------------------------
+
+def cpu_baseline(budget_s=15.0):
+    from oracle import qift_oracle as O
+    import synth_inputs as si
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = len(os.sched_getaffinity(0))
+    done_bytes = 0
+    n_lin = 0
+    t_total = 0.0
+    layer = si.LLAMA7B_LAYER
+    # setup (not timed): the timed work does not depend on the code values,
+    # so uniform codes of the layer's shapes are packed by the oracle's packer
+    prepared = []
+    for i, (name, K, N, B) in enumerate(layer):
+        codes = si.uniform_codes((N, K), 4, seed=200 + i)
+        words = O.pack_weights(codes, "mnz")
+        s_w = si.positive_scales(N, 300 + i).astype(np.float16)
+        X = si.activations(1, K, seed=400 + i)
+        prepared.append((K, N, B, words, s_w, X))
+        del codes
+    while t_total < budget_s:
+        for (K, N, B, words, s_w, X) in prepared:
+            t0 = time.perf_counter()
+            qa, s_a, _, _ = O.rotate_quant_act(X.astype(np.float64), B)
+            codes = O.unpack_weights(words, N, "mnz")
+            O.linear(qa, s_a, codes, s_w.astype(np.float64), "mnz")
+            t_total += time.perf_counter() - t0
+            done_bytes += words.nbytes + s_w.nbytes
+            n_lin += 1
+            if t_total >= budget_s:
+                break
+    return {"value": done_bytes / t_total / 1e9, "unit": "GB/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{n_lin} linears of one LLaMA-7B-shaped layer at M=1 (rotate+quantize the "
+                      f"input, unpack the oracle-packed 2-bit codes, exact integer matmul), "
+                      f"{t_total:.1f} s of CPU time; GB/s of packed codes+scales consumed"}
+
+
+# ---------------------------------------------------------------------------
+# main
+# ---------------------------------------------------------------------------
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported in this build "
+              f"(the path shards by output channel with no exchange; see DESIGN.md)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import bit_quantized_fwht_amd as q
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    q.load_library()
+
+    if args.copy_calibration:
+        src = torch.empty((1 << 30,), dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    log(f"building LLaMA-7B-shaped W2 stack, M={args.m}")
+    t0 = time.time()
+    stack = DecodeStack(q, torch, llama7b_layers("mnz"), args.m, 0.02, dev)
+    log(f"  built in {time.time() - t0:.1f}s: {len(stack.items)} linears, {stack.bytes / 1e9:.4f} GB")
+
+    for _ in range(args.warmup):
+        stack.step()
+    torch.cuda.synchronize()
+    # timed region: K steps; events around each grouped launch give the
+    # dominant kernel's mean duration
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for i in range(args.steps):
+        stack.rotate_all()
+        ev[i][0].record()
+        stack.group.run()
+        ev[i][1].record()
+    torch.cuda.synchronize()
+    t_total = time.perf_counter() - t_start
+    ms_step = t_total * 1e3 / args.steps
+    k_ms = np.array([a.elapsed_time(b) for a, b in ev])
+    k_mean = float(k_ms.mean())
+    value = stack.bytes / (ms_step * 1e-3) / 1e9
+    achieved = stack.bytes / (k_mean * 1e-3) / 1e9
+    log(f"decode M={args.m}: step {ms_step:.4f} ms ({value:.0f} GB/s); grouped kernel mean "
+        f"{k_mean:.4f} ms ({achieved:.0f} GB/s), median {np.median(k_ms):.4f} ms")
+
+    extra = {}
+    if not args.only_headline:
+        extra = measure_extras(q, torch, dev, stack, args)
+
+    traffic = traffic_from_profile(stack.bytes)
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                "kernel": "linear_grouped_kernel (decode, 224 linears)",
+                "algorithmic_bytes_per_launch": stack.bytes,
+                "mean_launch_ms": round(k_mean, 5)}
+    cpu = None
+    if not args.only_headline and not args.no_cpu_baseline:
+        log("timing the CPU oracle baseline")
+        cpu = cpu_baseline()
+        log(f"  oracle: {cpu['value']:.4f} GB/s on {cpu['cores']} threads")
+    out = {
+        "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "int8",
+        "data": "synthetic",
+        "config": {"workload": f"llama7b-shaped decode stack, 32 layers x 7 linears, W2 MNZ + fp16 "
+                               f"scales, A4, M={args.m} (rotate+quantize 2 launches + grouped linear)",
+                   "global_batch": args.m, "seq_len": 1, "parallelism": "single-gpu",
+                   "weight_stream_bytes": stack.bytes},
+        "roofline": roofline, "cpu_baseline": cpu, "extra": extra,
+    }
+    print(json.dumps(out), flush=True)
+
+
+def measure_extras(q, torch, dev, stack, args):
+    import synth_inputs as si
+    extra = {}
+    # headline stack at other batch sizes (same weights are rebuilt per M)
+    dec = {}
+    for M in (1, 4, 8, 16):
+        if M == args.m:
+            s = stack
+        else:
+            log(f"decode stack M={M}")
+            s = DecodeStack(q, torch, llama7b_layers("mnz"), M, 0.02, dev)
+        med, mn, _ = time_fn(torch, s.group.run, 30)
+        smed, _, _ = time_fn(torch, s.step, 30)
+        dec[f"M={M}"] = {"grouped_kernel_ms": round(med, 4), "kernel_GBps": round(s.bytes / med / 1e6, 1),
+                         "step_ms": round(smed, 4), "step_GBps": round(s.bytes / smed / 1e6, 1),
+                         "frac_of_hbm_peak": round(s.bytes / med / 1e6 / HBM_PEAK_GBS, 4)}
+        if s is not stack:
+            del s
+            torch.cuda.empty_cache()
+    extra["decode_llama7b_w2_mnz"] = dec
+
+    # prefill int8 MFMA GEMM, M = 2048
+    pre = {}
+    for name, K, N, B in (("up_proj", 4096, 11008, 4096), ("down_proj", 11008, 4096, 256)):
+        M = 2048
+        W = si.device_weights(N, K, seed=5, sigma=0.02, device=dev)
+        cw, sw = q.qift_quantize_weights(W, B, "mnz", torch.float16)
+        del W
+        X = si.device_activations(M, K, seed=6, device=dev)
+        xq, sa, _ = q.qift_rotate_quant_act(X, B)
+        Y = torch.empty((M, N), dtype=torch.float32, device=dev)
+        med, mn, _ = time_fn(torch, lambda: q.qift_w2a4_linear(xq, sa, cw, sw, "mnz", Y=Y), 30)
+        rmed, _, _ = time_fn(torch, lambda: q.qift_rotate_quant_act(X, B, xq=xq, s_a=sa), 30)
+        ops = 2.0 * M * N * K
+        pre[name] = {"M": M, "K": K, "N": N, "gemm_ms": round(med, 4),
+                     "TOPS": round(ops / med / 1e9, 1), "frac_of_int8_peak": round(ops / med / 1e9 / INT8_PEAK_TOPS, 4),
+                     "rotate_quant_ms": round(rmed, 4),
+                     "rotate_quant_GBps": round((M * K * 2 + M * K / 2 + 4 * M) / rmed / 1e6, 1)}
+        del cw, sw, X, xq, sa, Y
+    extra["prefill_llama7b_mnz"] = pre
+
+    # LLaMA-3.1-8B-shaped PoT layer: decode over 32 copies; prefill M = 4096
+    log("decode stack LLaMA-3.1-8B PoT")
+    s8 = DecodeStack(q, torch, llama31_8b_layers("pot"), 1, 0.015, dev, seed0=77)
+    med, _, _ = time_fn(torch, s8.group.run, 30)
+    pot = {"decode_M1_32_layers": {"bytes": s8.bytes, "grouped_kernel_ms": round(med, 4),
+                                   "kernel_GBps": round(s8.bytes / med / 1e6, 1),
+                                   "frac_of_hbm_peak": round(s8.bytes / med / 1e6 / HBM_PEAK_GBS, 4)}}
+    del s8
+    torch.cuda.empty_cache()
+    pf = {}
+    for name, K, N, B in si.LLAMA31_8B_LAYER:
+        if name in ("k_proj", "o_proj", "up_proj"):
+            continue  # same shapes as v_proj, q_proj, gate_proj
+        M = 4096
+        W = si.device_weights(N, K, seed=8, sigma=0.015, device=dev)
+        cw, sw = q.qift_quantize_weights(W, B, "pot", torch.float16)
+        del W
+        X = si.device_activations(M, K, seed=9, device=dev)
+        xq, sa, _ = q.qift_rotate_quant_act(X, B)
+        Y = torch.empty((M, N), dtype=torch.float32, device=dev)
+        med, _, _ = time_fn(torch, lambda: q.qift_w2a4_linear(xq, sa, cw, sw, "pot", Y=Y), 20)
+        ops = 2.0 * M * N * K
+        pf[name] = {"M": M, "K": K, "N": N, "gemm_ms": round(med, 4), "TOPS": round(ops / med / 1e9, 1),
+                    "frac_of_int8_peak": round(ops / med / 1e9 / INT8_PEAK_TOPS, 4)}
+        del cw, sw, X, xq, sa, Y
+    pot["prefill_M4096"] = pf
+    extra["llama31_8b_pot"] = pot
+
+    # mixed W2/W4 stack at M = 16
+    log("mixed W2/W4 stack M=16")
+    sm = DecodeStack(q, torch, mixed_layers(), 16, 0.02, dev, seed0=55)
+    med, _, _ = time_fn(torch, sm.group.run, 30)
+    smed, _, _ = time_fn(torch, sm.step, 30)
+    extra["mixed_w2_w4_llama7b_M16"] = {"bytes": sm.bytes, "grouped_kernel_ms": round(med, 4),
+                                        "kernel_GBps": round(sm.bytes / med / 1e6, 1),
+                                        "step_ms": round(smed, 4),
+                                        "frac_of_hbm_peak": round(sm.bytes / med / 1e6 / HBM_PEAK_GBS, 4)}
+    del sm
+    torch.cuda.empty_cache()
+
+    # KV4: K and V [4096, 32, 128] bf16, cycled over 4 buffer sets (> cache)
+    T, H, D = 4096, 32, 128
+    sets = [(si.device_kv(T, H, D, seed=60 + i, device=dev),
+             torch.empty((T, H, D // 2), dtype=torch.uint8, device=dev),
+             torch.empty((T, H), dtype=torch.float32, device=dev)) for i in range(8)]
+    it = [0]
+
+    def kv_step():
+        a = sets[it[0] % 8]
+        b = sets[(it[0] + 1) % 8]
+        q.qift_kv4_quant(a[0], D, kvq=a[1], scales=a[2])
+        q.qift_kv4_quant(b[0], D, kvq=b[1], scales=b[2])
+        it[0] += 2
+
+    med, _, _ = time_fn(torch, kv_step, 40)
+    kv_bytes = 2 * (T * H * D * 2 + T * H * D // 2 + T * H * 4)
+    extra["kv4_llama7b_K_and_V"] = {"T": T, "H": H, "D": D, "ms_K_and_V": round(med, 4),
+                                    "GBps": round(kv_bytes / med / 1e6, 1),
+                                    "frac_of_hbm_peak": round(kv_bytes / med / 1e6 / HBM_PEAK_GBS, 4)}
+    del sets
+    extra["context"] = {"qtea_lut_kernel_per_token_speedup_vs_fp16": 7.2,
+                        "note": "speedup printed for a different (ternary) method; hardware not stated"}
+    return extra
+
+
+if __name__ == "__main__":
+    main()

@@ -151,23 +151,32 @@ def code_words_per_row(K: int, levels) -> int:
     return K // 8 if _levels(levels) == LEVELS["int4"] else K // 16
 
 
+def padded_channels(N: int) -> int:
+    """Channels of a weight buffer: N rounded up to whole 16-channel tiles."""
+    return (N + 15) // 16 * 16
+
+
 # ---------------------------------------------------------------------------
 # the four calls
 # ---------------------------------------------------------------------------
 
 def qift_quantize_weights(W, had_block: int, levels="mnz", scale_dtype=torch.float16,
                           codes=None, scales=None, stream=None):
-    """W [N, K] float32/bfloat16 -> (codes int32 [N, K/16 or K/8] holding the
-    uint32 words, scales [N] in scale_dtype)."""
+    """W [N, K] float32/bfloat16 -> (codes int32 [Np, K/16 or K/8] holding the
+    uint32 words in the tiled layout (Np = N rounded up to 16), scales [N] in
+    scale_dtype)."""
     _dev_tensor(W, "W", (torch.float32, torch.bfloat16))
     N, K = W.shape
     lv = _levels(levels)
     if codes is None:
-        codes = torch.empty((N, code_words_per_row(K, lv)), dtype=torch.int32, device=W.device)
+        codes = torch.empty((padded_channels(N), code_words_per_row(K, lv)), dtype=torch.int32,
+                            device=W.device)
     if scales is None:
         scales = torch.empty((N,), dtype=scale_dtype, device=W.device)
     _dev_tensor(codes, "codes", (torch.int32,))
     _dev_tensor(scales, "scales", (torch.float32, torch.float16))
+    if codes.numel() < padded_channels(N) * code_words_per_row(K, lv) or scales.numel() < N:
+        raise ValueError("codes or scales buffer too small")
     st = _C.qift_quantize_weights(_ptr(W), _TORCH_TO_QIFT[W.dtype], N, K, had_block, lv,
                                   _ptr(codes), _ptr(scales), _TORCH_TO_QIFT[scales.dtype],
                                   _stream(stream, W.device))
@@ -207,7 +216,11 @@ def qift_w2a4_linear(xq, s_a, codes, scales, levels="mnz", out_dtype=torch.float
     _dev_tensor(scales, "scales", (torch.float32, torch.float16))
     M, K = xq.shape[0], xq.shape[1] * 2
     if N is None:
-        N = codes.shape[0]
+        N = scales.shape[0]
+    if codes.numel() < padded_channels(N) * code_words_per_row(K, levels) or scales.numel() < N:
+        raise ValueError("codes or scales buffer too small for N")
+    if s_a.numel() < M:
+        raise ValueError("s_a too small")
     if Y is None:
         Y = torch.empty((M, N), dtype=out_dtype, device=xq.device)
     _dev_tensor(Y, "Y", (torch.float32, torch.bfloat16, torch.int32))
@@ -255,7 +268,7 @@ class LinearGroup:
             xq, codes = it["xq"], it["codes"]
             device = xq.device
             M, K = xq.shape[0], xq.shape[1] * 2
-            N = it.get("N", codes.shape[0])
+            N = it.get("N", it["scales"].shape[0])
             for key in ("xq", "s_a", "codes", "scales", "Y"):
                 _dev_tensor(it[key], key)
             descs[i] = qift_linear_desc(it["xq"].data_ptr(), it["s_a"].data_ptr(),
@@ -283,4 +296,4 @@ class LinearGroup:
 
 __all__ = ["load_library", "QiftUnavailable", "qift_quantize_weights", "qift_rotate_quant_act", "qift_w2a4_linear", "qift_kv4_quant",
            "LinearGroup", "QiftError", "qift_linear_desc", "LEVELS", "status_string", "last_error",
-           "abi_version", "code_words_per_row", "LIB_PATH"]
+           "abi_version", "code_words_per_row", "padded_channels", "LIB_PATH"]

@@ -36,9 +36,8 @@ struct Fmt {
   static constexpr int kSteps = kLaneK / 16;            // MFMAs per code load
   static constexpr int kChunkK = 4 * kLaneK;            // features per wave step (4 lane groups)
   static constexpr int kShift = acc_shift(LV);
+  // 32-bit code words per channel row
   __device__ static __forceinline__ int64_t code_words(int64_t K) { return kInt4 ? K / 8 : K / 16; }
-  // word index of feature k inside a code row
-  __device__ static __forceinline__ int64_t code_word_of(int64_t k) { return kInt4 ? k / 8 : k / 16; }
 };
 
 template <int LV>
@@ -107,11 +106,13 @@ __device__ __forceinline__ void decode_wave(const qift_linear_desc& d, int64_t n
   for (int64_t t = 0; t < nchunks; ++t) {
     const int64_t kseg = t * F::kChunkK + (int64_t)g * F::kLaneK;
     const bool kval = kseg < K;
+    // tiled layout: 16-channel tile (n0 + 16 i) / 16, chunk t, lane's 16-byte
+    // unit at word 4 * lane -- one contiguous 1 KB per wave load
     uint4 cv[kDecodeTiles];
 #pragma unroll
     for (int i = 0; i < kDecodeTiles; ++i) {
-      const int64_t n = n0 + 16 * i + r16;
-      cv[i] = (kval && n < N) ? ld16(codes + n * cw + F::code_word_of(kseg)) : zero;
+      const int64_t tn = n0 + 16 * i;
+      cv[i] = (kval && tn < N) ? ld16(codes + (tn >> 4) * 16 * cw + t * 256 + 4 * lane) : zero;
     }
     uint4 a0 = zero, a1 = zero;
     if (kval && act_row) {
@@ -185,12 +186,11 @@ struct PrefillCfg {
   using F = Fmt<LV>;
   static constexpr int kBK = F::kChunkK;                  // features per LDS stage
   static constexpr int kARowBytes = kBK / 2;              // int4 activations
-  static constexpr int kBRowBytes = F::kInt4 ? kBK / 2 : kBK / 4;
   static constexpr int kAStride = kARowBytes + 16;        // padded: conflict-free 16 B reads
-  static constexpr int kBStride = kBRowBytes + 16;
   static constexpr int kALoads = kBM * kARowBytes / 16 / 256;  // 16-byte loads per thread
-  static constexpr int kBLoads = kBN * kBRowBytes / 16 / 256;
-  static constexpr int kLds = kBM * kAStride + kBN * kBStride;
+  // weights: one 1 KB tiled chunk per 16-channel tile, copied verbatim
+  static constexpr int kBLoads = (kBN / 16) * 1024 / 16 / 256;
+  static constexpr int kLds = kBM * kAStride + (kBN / 16) * 1024;
 };
 
 template <int LV>
@@ -208,7 +208,6 @@ __device__ __forceinline__ void prefill_tile(const qift_linear_desc& d, int64_t 
   const int64_t M = d.M, K = d.K, N = d.N;
   const int64_t cw = F::code_words(K);
   const int64_t arow = K / 2;       // bytes per activation row
-  const int64_t brow = cw * 4;      // bytes per code row
   uint8_t* As = lds;
   uint8_t* Bs = lds + kBM * C::kAStride;
 
@@ -220,7 +219,6 @@ __device__ __forceinline__ void prefill_tile(const qift_linear_desc& d, int64_t 
 
   uint4 ra[C::kALoads], rb[C::kBLoads];
   constexpr int kAChunks = C::kARowBytes / 16;  // 16-byte chunks per row
-  constexpr int kBChunks = C::kBRowBytes / 16;
 
   auto gload = [&](int64_t k0) {
 #pragma unroll
@@ -233,13 +231,12 @@ __device__ __forceinline__ void prefill_tile(const qift_linear_desc& d, int64_t 
     }
 #pragma unroll
     for (int i = 0; i < C::kBLoads; ++i) {
-      const int idx = tid + 256 * i;
-      const int row = idx / kBChunks, ch = idx % kBChunks;
-      const int64_t n = nt0 + row;
-      const int64_t kb = (F::kInt4 ? k0 / 2 : k0 / 4) + 16 * ch;
-      const int64_t kfeat = F::kInt4 ? 2 * kb : 4 * kb;
-      rb[i] = (n < N && kfeat < K) ? ld16(reinterpret_cast<const uint8_t*>(d.codes) + n * brow + kb)
-                                   : uint4{0u, 0u, 0u, 0u};
+      const int u = tid + 256 * i;       // 16-byte unit: tile u / 64, lane u % 64
+      const int64_t tn = nt0 + 16 * (u >> 6);
+      const int ul = u & 63;
+      const bool ok = tn < N && k0 + (int64_t)(ul >> 4) * F::kLaneK < K;
+      rb[i] = ok ? ld16(d.codes + (tn >> 4) * 16 * cw + (k0 / C::kBK) * 256 + 4 * ul)
+                 : uint4{0u, 0u, 0u, 0u};
     }
   };
   auto lstore = [&]() {
@@ -250,11 +247,8 @@ __device__ __forceinline__ void prefill_tile(const qift_linear_desc& d, int64_t 
       *reinterpret_cast<uint4*>(As + row * C::kAStride + 16 * ch) = ra[i];
     }
 #pragma unroll
-    for (int i = 0; i < C::kBLoads; ++i) {
-      const int idx = tid + 256 * i;
-      const int row = idx / kBChunks, ch = idx % kBChunks;
-      *reinterpret_cast<uint4*>(Bs + row * C::kBStride + 16 * ch) = rb[i];
-    }
+    for (int i = 0; i < C::kBLoads; ++i)
+      *reinterpret_cast<uint4*>(Bs + 16 * (tid + 256 * i)) = rb[i];
   };
 
   const int64_t nstages = (K + C::kBK - 1) / C::kBK;
@@ -275,7 +269,7 @@ __device__ __forceinline__ void prefill_tile(const qift_linear_desc& d, int64_t 
     }
 #pragma unroll
     for (int j = 0; j < kWaveTN; ++j)
-      fb[j] = *reinterpret_cast<const uint4*>(Bs + (wn + 16 * j + r16) * C::kBStride + 16 * g);
+      fb[j] = *reinterpret_cast<const uint4*>(Bs + ((wn >> 4) + j) * 1024 + 16 * lane);
 #pragma unroll
     for (int s = 0; s < F::kSteps; ++s) {
       v4i B[kWaveTN];

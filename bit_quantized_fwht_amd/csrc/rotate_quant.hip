@@ -196,14 +196,30 @@ __device__ __forceinline__ int code_bit_offset(int i) {
   return 8 * ((i >> 1) & 3) + 4 * (i >> 3) + 2 * (i & 1);
 }
 
+// Word w of channel row n in the 16-channel tiled weight layout (W words per
+// channel row): tile r = n / 16 holds 16 * W words; chunk c = w / 16 is 1 KB
+// (256 words) in which the 16-byte unit of lane (g, i) = ((w % 16) / 4, n % 16)
+// sits at word 4 * (16 g + i), word j = w % 4 inside it.
+__device__ __forceinline__ int64_t tiled_word(int64_t n, int64_t w, int64_t W) {
+  const int64_t r = n >> 4, i = n & 15;
+  const int64_t c = w >> 4, g = (w >> 2) & 3, j = w & 3;
+  return r * 16 * W + c * 256 + (16 * g + i) * 4 + j;
+}
+
 template <typename T>
 __global__ __launch_bounds__(kRowThreads) void quantize_weights_kernel(
-    const T* __restrict__ W, int K, int log2b, float norm, int levels, uint32_t* __restrict__ codes,
-    void* __restrict__ scales, int scale_f16) {
+    const T* __restrict__ W, int64_t N, int K, int log2b, float norm, int levels,
+    uint32_t* __restrict__ codes, void* __restrict__ scales, int scale_f16) {
   extern __shared__ float row[];
   __shared__ float red[kRowThreads / 64];
   const int tid = threadIdx.x;
   const int64_t n = blockIdx.x;
+  const bool int4 = levels == QIFT_LEVELS_INT4;
+  const int64_t words = int4 ? K / 8 : K / 16;
+  if (n >= N) {  // zero codes for the padding channels of the last tile
+    for (int w = tid; w < words; w += kRowThreads) codes[tiled_word(n, w, words)] = 0u;
+    return;
+  }
   load_row<T>(W + n * K, row, K, tid);
   __syncthreads();
   fwht_row(row, K, log2b, tid);
@@ -219,17 +235,15 @@ __global__ __launch_bounds__(kRowThreads) void quantize_weights_kernel(
     s = s32;
     if (tid == 0) reinterpret_cast<float*>(scales)[n] = s32;
   }
-  if (levels == QIFT_LEVELS_INT4) {
-    uint32_t* c_row = codes + n * (int64_t)(K / 8);
+  if (int4) {
     for (int g = tid; g < (K >> 3); g += kRowThreads) {
       uint32_t word = 0;
 #pragma unroll
       for (int i = 0; i < 8; ++i)
         word |= ((uint32_t)quant_int4(row[8 * g + i] * norm, s) & 0xFu) << (4 * i);
-      c_row[g] = word;
+      codes[tiled_word(n, g, words)] = word;
     }
   } else {
-    uint32_t* c_row = codes + n * (int64_t)(K / 16);
     const bool pot = levels == QIFT_LEVELS_POT;
     for (int g = tid; g < (K >> 4); g += kRowThreads) {
       uint32_t word = 0;
@@ -239,7 +253,7 @@ __global__ __launch_bounds__(kRowThreads) void quantize_weights_kernel(
         const uint32_t c = pot ? code_pot(w, s) : code_mnz(w, s);
         word |= c << code_bit_offset(i);
       }
-      c_row[g] = word;
+      codes[tiled_word(n, g, words)] = word;
     }
   }
 }
@@ -276,13 +290,14 @@ hipError_t launch_quantize_weights(const void* W, int w_bf16, int64_t N, int64_t
   const size_t lds = (size_t)K * sizeof(float);
   const int lb = ilog2(had_block);
   const float nrm = had_norm(had_block);
+  const unsigned grid = (unsigned)((N + 15) / 16 * 16);  // padded to whole 16-channel tiles
   if (w_bf16)
-    hipLaunchKernelGGL(quantize_weights_kernel<uint16_t>, dim3((unsigned)N), dim3(kRowThreads),
-                       lds, s, reinterpret_cast<const uint16_t*>(W), (int)K, lb, nrm, levels,
-                       codes, scales, scale_f16);
+    hipLaunchKernelGGL(quantize_weights_kernel<uint16_t>, dim3(grid), dim3(kRowThreads), lds, s,
+                       reinterpret_cast<const uint16_t*>(W), N, (int)K, lb, nrm, levels, codes,
+                       scales, scale_f16);
   else
-    hipLaunchKernelGGL(quantize_weights_kernel<float>, dim3((unsigned)N), dim3(kRowThreads), lds,
-                       s, reinterpret_cast<const float*>(W), (int)K, lb, nrm, levels, codes,
+    hipLaunchKernelGGL(quantize_weights_kernel<float>, dim3(grid), dim3(kRowThreads), lds, s,
+                       reinterpret_cast<const float*>(W), N, (int)K, lb, nrm, levels, codes,
                        scales, scale_f16);
   return hipGetLastError();
 }

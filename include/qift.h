@@ -30,12 +30,22 @@
  *   the low nibble of byte j, element 2j+1 in the high nibble, two's
  *   complement. Read as little-endian 32-bit words, element i of a word is at
  *   bits 4i..4i+3. Values are in [-7, 7].
- * 2-bit weight codes: row n of a [N, K] matrix is K/16 32-bit words; word j
- *   holds features k = 16j..16j+15. Feature k = 16j + i sits at bit offset
- *   8*((i>>1)&3) + 4*(i>>3) + 2*(i&1), i.e. byte b holds features
+ * 2-bit weight codes, in-word layout: the K codes of a channel row form K/16
+ *   32-bit words; word j holds features k = 16j..16j+15, feature 16j + i at
+ *   bit offset 8*((i>>1)&3) + 4*(i>>3) + 2*(i&1), i.e. byte b holds features
  *   2b, 2b+1, 8+2b, 9+2b in bit pairs 0-1, 2-3, 4-5, 6-7. (This pairs each
  *   code with the nibble order of the int4 activations so that both unpack
  *   to matrix-core operands with shifts and masks only.)
+ * 4-bit weight codes, in-word layout: K/8 words per channel row in the int4
+ *   order above (feature 8j + i at bits 4i of word j).
+ * Weight buffers, tiled layout: channels are grouped in tiles of 16 and
+ *   padded with zero codes to Np = ceil(N/16)*16; with W the words per channel
+ *   row (K/16 or K/8), word w of channel n is stored at index
+ *       (n/16) * 16*W  +  (w/16) * 256  +  (16*((w%16)/4) + n%16) * 4  +  w%4
+ *   so each tile is 16*W contiguous words and every 1 KB chunk of a tile is
+ *   the 64 16-byte units that one 64-lane wave loads for 16 channels x 256
+ *   features (2-bit) or x 128 features (4-bit); a short last chunk keeps only
+ *   its leading units. A weight buffer holds Np*W words.
  * Code values:
  *   QIFT_LEVELS_MNZ : the code read as a 2-bit two's-complement integer t
  *                     gives the half-scale level 2t+1 in {-3,-1,+1,+3};
@@ -105,7 +115,8 @@ typedef void* qift_stream; /* a hipStream_t */
  *
  *   W       [N, K] float32 (QIFT_F32) or bfloat16 (QIFT_BF16)
  *   K       multiple of 64, K <= QIFT_MAX_ROW; had_block | K
- *   codes   out: [N, K/16] uint32 (MNZ, POT) or [N, K/8] uint32 (INT4);
+ *   codes   out: Np*K/16 uint32 (MNZ, POT) or Np*K/8 uint32 (INT4), tiled
+ *           layout, Np = ceil(N/16)*16 (padding channels are written as 0);
  *           16-byte aligned
  *   scales  out: [N] float32 (QIFT_F32) or float16 (QIFT_F16)
  * N = 0 is a no-op.
@@ -145,7 +156,8 @@ qift_status qift_rotate_quant_act(const void* X, qift_dtype x_dtype, int64_t M, 
  *
  *   xq, s_a   [M, K/2] int4, [M] float32 (as written by qift_rotate_quant_act)
  *   K         multiple of 64, K <= 65536
- *   codes     [N, K/16] (2-bit) or [N, K/8] (INT4) uint32; 16-byte aligned
+ *   codes     Np*K/16 (2-bit) or Np*K/8 (INT4) uint32 in the tiled layout
+ *             written by qift_quantize_weights; 16-byte aligned
  *   scales    [N] float32 or float16 (scale_dtype)
  *   Y         out: [M, N] float32, bfloat16 or int32 (y_dtype)
  *   xq must be 16-byte aligned.
@@ -193,7 +205,7 @@ qift_status qift_kv4_quant(const void* KV, qift_dtype dtype, int64_t T, int64_t 
 typedef struct qift_linear_desc {
   const uint8_t* xq;      /* [M, K/2] int4                         */
   const float* s_a;       /* [M] float32                           */
-  const uint32_t* codes;  /* [N, K/16] or [N, K/8] uint32          */
+  const uint32_t* codes;  /* tiled, Np*K/16 or Np*K/8 uint32       */
   const void* scales;     /* [N], dtype given to prepare           */
   void* Y;                /* [M, N], dtype given to prepare        */
   int64_t M, K, N;

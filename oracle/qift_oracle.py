@@ -259,16 +259,73 @@ def unpack_int4(b: np.ndarray) -> np.ndarray:
 
 
 def pack_int4_words(q: np.ndarray) -> np.ndarray:
-    """4-bit weight codes [N, K] -> uint32 [N, K/8] (the int4 byte layout read
-    as little-endian 32-bit words: element i of a word at bits 4i..4i+3)."""
+    """4-bit weight codes [N, K] -> uint32 [N, K/8] in row order (the int4
+    byte layout read as little-endian 32-bit words: element i of a word at
+    bits 4i..4i+3)."""
     b = pack_int4(q)
     N = b.shape[0]
     b = np.ascontiguousarray(b).reshape(N, -1, 4).astype(np.uint32)
     return (b[..., 0] | (b[..., 1] << 8) | (b[..., 2] << 16) | (b[..., 3] << 24)).astype(np.uint32)
 
 
+def unpack_int4_words(words: np.ndarray) -> np.ndarray:
+    """uint32 [N, K/8] row-order words -> int64 [N, K]."""
+    w = np.ascontiguousarray(np.asarray(words, dtype=np.uint32))
+    return unpack_int4(w.view(np.uint8).reshape(w.shape[0], -1))
+
+
+# Weight codes in device memory are stored in row tiles of 16 output
+# channels. With W the 32-bit words of one channel row in row order (K/16
+# words for 2-bit codes, K/8 for 4-bit), F = 64 features per 16-byte unit for
+# 2-bit codes and 32 for 4-bit, and chunks of 4 units (4F features):
+#   tile r = channel // 16, lane-row i = channel % 16,
+#   chunk c, unit-group g (0..3) and word j (0..3) of the feature's word,
+#   tiled word index = r * (16 * W) + c * 256 + (16 * g + i) * 4 + j
+# i.e. one chunk is 1 KB holding 16 channels x 4F features, unit u = 16g + i
+# at byte 16u; a short last chunk holds only its first groups. Channels are
+# padded with zero codes to a multiple of 16.
+
+def _tiled_index(Np: int, W: int) -> np.ndarray:
+    """tiled word index of (channel n, row-order word w), [Np, W]."""
+    n = np.arange(Np)[:, None]
+    w = np.arange(W)[None, :]
+    r, i = n // 16, n % 16
+    c, rem = w // 16, w % 16
+    g, j = rem // 4, rem % 4
+    return r * (16 * W) + c * 256 + (16 * g + i) * 4 + j
+
+
+def tile_weight_words(rows: np.ndarray) -> np.ndarray:
+    """Row-order words [N, W] (W a multiple of 4) -> tiled words
+    [ceil(N/16)*16, W] (same words, tile order)."""
+    rows = np.asarray(rows, dtype=np.uint32)
+    N, W = rows.shape
+    if W % 4:
+        raise ValueError("words per row must be a multiple of 4")
+    Np = -(-N // 16) * 16
+    pad = np.zeros((Np, W), dtype=np.uint32)
+    pad[:N] = rows
+    out = np.zeros(Np * W, dtype=np.uint32)
+    out[_tiled_index(Np, W)] = pad
+    return out.reshape(Np, W)
+
+
+def untile_weight_words(tiled: np.ndarray, N: int) -> np.ndarray:
+    """Inverse of tile_weight_words: tiled [Np, W] -> row-order words [N, W]."""
+    tiled = np.asarray(tiled, dtype=np.uint32)
+    Np, W = tiled.shape
+    return tiled.reshape(-1)[_tiled_index(Np, W)][:N]
+
+
 def pack_weights(codes: np.ndarray, kind: str) -> np.ndarray:
-    return pack_int4_words(codes) if kind == "int4" else pack_codes2(codes)
+    """Codes [N, K] -> device layout: row-order words, then 16-channel tiles."""
+    rows = pack_int4_words(codes) if kind == "int4" else pack_codes2(codes)
+    return tile_weight_words(rows)
+
+
+def unpack_weights(tiled: np.ndarray, N: int, kind: str) -> np.ndarray:
+    rows = untile_weight_words(tiled, N)
+    return unpack_int4_words(rows) if kind == "int4" else unpack_codes2(rows)
 
 
 # ---------------------------------------------------------------------------

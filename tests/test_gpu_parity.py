@@ -113,8 +113,7 @@ def gpu_quant_weights(W_t, B, kind, sdt):
     codes, scales = q.qift_quantize_weights(W_t, B, kind, SCALE_T[sdt])
     sync()
     words = dev_u32(codes)
-    c = O.unpack_int4(words.view(np.uint8).reshape(W_t.shape[0], -1)) if kind == "int4" \
-        else O.unpack_codes2(words)
+    c = O.unpack_weights(words, W_t.shape[0], kind)
     return c, scales.float().cpu().numpy(), words
 
 
@@ -226,9 +225,19 @@ def test_linear_extremes_do_not_overflow():
 
 def test_linear_empty_batch():
     xq = torch.empty((0, 128), dtype=torch.uint8, device=DEV)
-    Y = q.qift_w2a4_linear(xq, torch.empty(0, device=DEV), torch.zeros((8, 16), dtype=torch.int32,
+    Y = q.qift_w2a4_linear(xq, torch.empty(0, device=DEV), torch.zeros((16, 16), dtype=torch.int32,
                            device=DEV), torch.ones(8, dtype=torch.float16, device=DEV), "mnz")
     assert Y.shape == (0, 8)
+
+
+def test_quantize_weights_writes_zero_padding_channels():
+    W = si.weights(20, 128, seed=2)
+    say("weight padding channels")
+    codes = torch.full((32, 8), -1, dtype=torch.int32, device=DEV)
+    q.qift_quantize_weights(to_dev(W), 128, "mnz", torch.float16, codes=codes)
+    sync()
+    rows = O.untile_weight_words(dev_u32(codes), 32)
+    assert np.all(rows[20:] == 0) and not np.all(rows[:20] == 0)
 
 
 # ---------------------------------------------------------------------------
@@ -356,9 +365,7 @@ def test_full_shape_weight_quantizer_sampled(N, K, B, kind, sigma):
     rows = np.unique(np.concatenate([[0, N - 1], np.random.default_rng(1).choice(N, 30, replace=False)]))
     Wr = W_t[torch.from_numpy(rows).to(DEV)].cpu().numpy().astype(np.float64)
     co, so, _ = O.quantize_weights(Wr, B, kind, "f16")
-    words = dev_u32(cg_t)[rows]
-    cg = O.unpack_int4(words.view(np.uint8).reshape(len(rows), -1)) if kind == "int4" \
-        else O.unpack_codes2(words)
+    cg = O.unpack_weights(dev_u32(cg_t), N, kind)[rows]
     sg = sg_t.float().cpu().numpy()[rows]
     so32 = so.astype(np.float32)
     assert np.all(np.abs(sg - so32) <= 2 ** -10 * so32)  # at most one float16 ulp

@@ -81,6 +81,15 @@ def _swapped_pack_int4(q):
     return (nib[..., 1::2] | (nib[..., 0::2] << 4)).astype(np.uint8)
 
 
+def _tiled_index_group_row_swapped(Np, W):
+    n = np.arange(Np)[:, None]
+    w = np.arange(W)[None, :]
+    r, i = n // 16, n % 16
+    c, rem = w // 16, w % 16
+    g, j = rem // 4, rem % 4
+    return r * (16 * W) + c * 256 + (16 * i + g) * 4 + j
+
+
 def _gaussian_mse_cross_term_sign(levels, s=1.0):
     pts = sorted(float(v) * s for v in levels)
     edges = [-math.inf] + [(pts[i] + pts[i + 1]) / 2 for i in range(len(pts) - 1)] + [math.inf]
@@ -123,6 +132,7 @@ MUTATIONS = {
     "matmul_transposed": [("int_matmul", _transposed_int_matmul)],
     "pack2_natural_order": [("bit_offset_2b", _natural_bit_offset)],
     "pack4_nibbles_swapped": [("pack_int4", _swapped_pack_int4)],
+    "tile_group_and_row_swapped": [("_tiled_index", _tiled_index_group_row_swapped)],
     "mse_cross_term_sign": [("gaussian_mse", _gaussian_mse_cross_term_sign)],
     "lloyd_unnormalized_centroid": [("lloyd_gaussian", _lloyd_wrong_centroid)],
 }

@@ -453,10 +453,35 @@ def pin_packing_roundtrip():
     words = O.pack_int4_words(q)
     assert words.shape == (5, 12)
     assert np.array_equal(words.view(np.uint8).reshape(5, 48), O.pack_int4(q))
+    for kind, cc in (("mnz", c[:, :64]), ("int4", q[:, :64])):
+        t = O.pack_weights(cc, kind)
+        assert t.shape[0] == 16 and np.array_equal(O.unpack_weights(t, 5, kind), cc)
+        assert np.all(O.untile_weight_words(t, 16)[5:] == 0)  # zero padding channels
+
+
+def pin_tiled_layout_fixture():
+    g = golden("packing.json")["tiled"]
+    for kind in ("mnz", "int4"):
+        spec = g[kind]
+        N, K = spec["N"], spec["K"]
+        for case in spec["cases"]:
+            codes = np.zeros((N, K), dtype=np.int64)
+            codes[case["n"], case["k"]] = 1
+            t = O.pack_weights(codes, kind)
+            assert t.shape == (-(-N // 16) * 16, K // (8 if kind == "int4" else 16))
+            flat = t.reshape(-1)
+            nz = np.flatnonzero(flat)
+            assert nz.tolist() == [case["word"]], (kind, case, nz)
+            assert int(flat[case["word"]]) == 1 << case["bit"], (kind, case)
+            assert np.array_equal(O.unpack_weights(t, N, kind), codes)
 
 
 def test_packing_fixture():
     pin_packing_fixture()
+
+
+def test_tiled_layout_fixture():
+    pin_tiled_layout_fixture()
 
 
 def test_packing_roundtrip():
