@@ -85,6 +85,16 @@ __device__ __forceinline__ uint4 ld16(const void* p) {
 
 constexpr int kDecodeTiles = kDecodeRowsPerWave / 16;  // 16-channel MFMA tiles per wave
 
+// weight-stream load: 16 bytes, optionally marked non-temporal (streamed once)
+__device__ __forceinline__ uint4 ld16_stream(const uint32_t* p) {
+#if QIFT_DECODE_NT
+  const v4u v = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(p));
+  return uint4{v[0], v[1], v[2], v[3]};
+#else
+  return ld16(p);
+#endif
+}
+
 template <int LV>
 __device__ __forceinline__ void decode_wave(const qift_linear_desc& d, int64_t n0, int scale_f16,
                                             int y_dtype, int lane) {
@@ -101,31 +111,51 @@ __device__ __forceinline__ void decode_wave(const qift_linear_desc& d, int64_t n
 #pragma unroll
   for (int i = 0; i < kDecodeTiles; ++i) acc[i] = v4i{0, 0, 0, 0};
 
-  const uint4 zero = {0u, 0u, 0u, 0u};
   const int64_t nchunks = (K + F::kChunkK - 1) / F::kChunkK;
-  for (int64_t t = 0; t < nchunks; ++t) {
+
+  // one K chunk of this lane: its 16-byte code unit of each tile and the
+  // matching 32 (or 16) bytes of its activation row
+  struct Chunk {
+    uint4 c[kDecodeTiles];
+    uint4 a0, a1;
+  };
+  auto load = [&](Chunk& ch, int64_t t) {
     const int64_t kseg = t * F::kChunkK + (int64_t)g * F::kLaneK;
-    const bool kval = kseg < K;
-    // tiled layout: 16-channel tile (n0 + 16 i) / 16, chunk t, lane's 16-byte
-    // unit at word 4 * lane -- one contiguous 1 KB per wave load
-    uint4 cv[kDecodeTiles];
+    const bool kval = t < nchunks && kseg < K;
+    // tiled layout: 16-channel tile (n0 + 16 i) / 16, chunk t, the lane's
+    // 16-byte unit at word 4 * lane -- one contiguous 1 KB per wave load
 #pragma unroll
     for (int i = 0; i < kDecodeTiles; ++i) {
       const int64_t tn = n0 + 16 * i;
-      cv[i] = (kval && tn < N) ? ld16(codes + (tn >> 4) * 16 * cw + t * 256 + 4 * lane) : zero;
+      ch.c[i] = (kval && tn < N) ? ld16_stream(codes + (tn >> 4) * 16 * cw + t * 256 + 4 * lane)
+                                 : uint4{0u, 0u, 0u, 0u};
     }
-    uint4 a0 = zero, a1 = zero;
+    ch.a0 = uint4{0u, 0u, 0u, 0u};
+    ch.a1 = uint4{0u, 0u, 0u, 0u};
     if (kval && act_row) {
       const uint8_t* ap = xq + (int64_t)r16 * (K / 2) + kseg / 2;
-      a0 = ld16(ap);
-      if constexpr (!F::kInt4) a1 = ld16(ap + 16);
+      ch.a0 = ld16(ap);
+      if constexpr (!F::kInt4) ch.a1 = ld16(ap + 16);
     }
+  };
+  auto compute = [&](const Chunk& ch) {
 #pragma unroll
     for (int s = 0; s < F::kSteps; ++s) {
-      const v4i A = act_operand(a0, a1, s);
+      const v4i A = act_operand(ch.a0, ch.a1, s);
 #pragma unroll
-      for (int i = 0; i < kDecodeTiles; ++i) acc[i] = mfma16(A, weight_operand<LV>(cv[i], s), acc[i]);
+      for (int i = 0; i < kDecodeTiles; ++i)
+        acc[i] = mfma16(A, weight_operand<LV>(ch.c[i], s), acc[i]);
     }
+  };
+  // two chunks in flight: the loads of chunk t+1 are issued before chunk t
+  // is consumed
+  Chunk x, y;
+  load(x, 0);
+  for (int64_t t = 0; t < nchunks; t += 2) {
+    load(y, t + 1);
+    compute(x);
+    load(x, t + 2);
+    if (t + 1 < nchunks) compute(y);
   }
 
   // epilogue: lane holds rows m = 4g + r of channel n0 + 16 i + r16

@@ -118,8 +118,15 @@ struct PlanHeader {
 static_assert(sizeof(PlanHeader) == 64, "plan header layout");
 constexpr uint64_t kPlanMagic = 0x5146545f504c414eull;  // "QFT_PLAN"
 
-// decode kernel geometry: 256 threads = 4 waves, each wave 4 x 16 rows
-constexpr int kDecodeRowsPerWave = 64;
+// decode kernel geometry: 256 threads = 4 waves, each wave QIFT_DECODE_TILES
+// x 16 output channels
+#ifndef QIFT_DECODE_TILES
+#define QIFT_DECODE_TILES 4
+#endif
+#ifndef QIFT_DECODE_NT
+#define QIFT_DECODE_NT 1
+#endif
+constexpr int kDecodeRowsPerWave = 16 * QIFT_DECODE_TILES;
 constexpr int kDecodeWaves = 4;
 constexpr int kDecodeRowsPerTile = kDecodeRowsPerWave * kDecodeWaves;
 
