@@ -41,14 +41,14 @@ struct Fmt {
 };
 
 template <int LV>
-__device__ __forceinline__ v4i weight_operand(const uint4& c, int step) {
+__device__ __forceinline__ v4i weight_operand(const uint4& c, int step, MnzMasks k) {
   if constexpr (LV == QIFT_LEVELS_INT4) {
     const uint32_t w0 = step == 0 ? c.x : c.z;
     const uint32_t w1 = step == 0 ? c.y : c.w;
     return int4_operand(w0, w1);
   } else {
     const uint32_t w = step == 0 ? c.x : (step == 1 ? c.y : (step == 2 ? c.z : c.w));
-    if constexpr (LV == QIFT_LEVELS_MNZ) return mnz_operand(w);
+    if constexpr (LV == QIFT_LEVELS_MNZ) return mnz_operand(w, k);
     else return pot_operand(w);
   }
 }
@@ -83,6 +83,13 @@ __device__ __forceinline__ uint4 ld16(const void* p) {
 // decode: M <= 16
 // ---------------------------------------------------------------------------
 
+#ifndef QIFT_PREFILL_MINBLOCKS
+#define QIFT_PREFILL_MINBLOCKS 2
+#endif
+#ifndef QIFT_DECODE_MINBLOCKS
+#define QIFT_DECODE_MINBLOCKS 2
+#endif
+
 constexpr int kDecodeTiles = kDecodeRowsPerWave / 16;  // 16-channel MFMA tiles per wave
 
 // weight-stream load: 16 bytes, optionally marked non-temporal (streamed once)
@@ -106,6 +113,7 @@ __device__ __forceinline__ void decode_wave(const qift_linear_desc& d, int64_t n
   const uint8_t* xq = d.xq;
   const uint32_t* codes = d.codes;
   const bool act_row = r16 < M;
+  const MnzMasks km = mnz_masks(d.reserved, lane);
 
   v4i acc[kDecodeTiles];
 #pragma unroll
@@ -144,7 +152,7 @@ __device__ __forceinline__ void decode_wave(const qift_linear_desc& d, int64_t n
       const v4i A = act_operand(ch.a0, ch.a1, s);
 #pragma unroll
       for (int i = 0; i < kDecodeTiles; ++i)
-        acc[i] = mfma16(A, weight_operand<LV>(ch.c[i], s), acc[i]);
+        acc[i] = mfma16(A, weight_operand<LV>(ch.c[i], s, km), acc[i]);
     }
   };
   // two chunks in flight: the loads of chunk t+1 are issued before chunk t
@@ -189,12 +197,12 @@ __device__ __forceinline__ void decode_dispatch(const qift_linear_desc& d, int64
   }
 }
 
-__global__ __launch_bounds__(256) void linear_decode_kernel(qift_linear_desc d, int scale_f16,
+__global__ __launch_bounds__(256, QIFT_DECODE_MINBLOCKS) void linear_decode_kernel(qift_linear_desc d, int scale_f16,
                                                             int y_dtype) {
   decode_dispatch(d, blockIdx.x, scale_f16, y_dtype);
 }
 
-__global__ __launch_bounds__(256) void linear_grouped_kernel(const uint8_t* __restrict__ ws) {
+__global__ __launch_bounds__(256, QIFT_DECODE_MINBLOCKS) void linear_grouped_kernel(const uint8_t* __restrict__ ws) {
   const PlanHeader* h = reinterpret_cast<const PlanHeader*>(ws);
   const int64_t tile = blockIdx.x;
   if (tile >= h->total_tiles) return;
@@ -208,19 +216,47 @@ __global__ __launch_bounds__(256) void linear_grouped_kernel(const uint8_t* __re
 // prefill: M > 16
 // ---------------------------------------------------------------------------
 
-constexpr int kBM = 128, kBN = 128;
-constexpr int kWaveTM = 4, kWaveTN = 4;  // 16x16 fragments per wave (64 x 64)
+// Workgroup = 2 x 2 waves; a wave computes kWaveTM x kWaveTN fragments of
+// 16 x 16, so the workgroup tile is (32 kWaveTM) tokens x (32 kWaveTN)
+// channels. Larger wave tiles amortize the operand unpacking (about 6 VALU
+// instructions per activation fragment and 7 per weight fragment per MFMA
+// step) over more MFMAs.
+#ifndef QIFT_PREFILL_TM
+#define QIFT_PREFILL_TM 4
+#endif
+#ifndef QIFT_PREFILL_TN
+#define QIFT_PREFILL_TN 4
+#endif
+#ifndef QIFT_PREFILL_DBUF
+#define QIFT_PREFILL_DBUF 0
+#endif
+#ifndef QIFT_PREFILL_DL
+#define QIFT_PREFILL_DL 1
+#endif
+#ifndef QIFT_PREFILL_SCHED
+#define QIFT_PREFILL_SCHED 0
+#endif
+constexpr int kWaveTM = QIFT_PREFILL_TM, kWaveTN = QIFT_PREFILL_TN;
+constexpr int kBM = 32 * kWaveTM, kBN = 32 * kWaveTN;
 
 template <int LV>
 struct PrefillCfg {
   using F = Fmt<LV>;
   static constexpr int kBK = F::kChunkK;                  // features per LDS stage
   static constexpr int kARowBytes = kBK / 2;              // int4 activations
-  static constexpr int kAStride = kARowBytes + 16;        // padded: conflict-free 16 B reads
-  static constexpr int kALoads = kBM * kARowBytes / 16 / 256;  // 16-byte loads per thread
+  // padded by 8 bytes: the 8-byte reads of 16 consecutive rows cover all 32
+  // banks once
+  static constexpr int kAStride = kARowBytes + 8;
+  static constexpr int kAUnits = kARowBytes / 16;         // 16-byte units per row
+  static constexpr int kALoads = kBM * kAUnits / 256;     // 16-byte loads per thread
   // weights: one 1 KB tiled chunk per 16-channel tile, copied verbatim
-  static constexpr int kBLoads = (kBN / 16) * 1024 / 16 / 256;
-  static constexpr int kLds = kBM * kAStride + (kBN / 16) * 1024;
+  static constexpr int kBLoads = (kBN / 16) * 64 / 256;
+  // one stage = A tile then B tile; two stages back to back
+  static constexpr int kBOffset = (kBM * kAStride + 15) / 16 * 16;
+  static constexpr int kStage = kBOffset + (kBN / 16) * 1024;
+  static constexpr int kLds = 2 * kStage;
+  static_assert(kALoads * 256 == kBM * kAUnits, "A tile load split");
+  static_assert(kBLoads * 256 == (kBN / 16) * 64, "B tile load split");
 };
 
 template <int LV>
@@ -233,13 +269,14 @@ __device__ __forceinline__ void prefill_tile(const qift_linear_desc& d, int64_t 
   const int wave = tid >> 6;
   const int r16 = lane & 15;
   const int g = lane >> 4;
-  const int wm = (wave >> 1) * 64;  // wave offset inside the tile, M side
-  const int wn = (wave & 1) * 64;   // N side
+  const int wm = (wave >> 1) * (16 * kWaveTM);  // wave offset inside the tile, M side
+  const int wn = (wave & 1) * (16 * kWaveTN);   // N side
   const int64_t M = d.M, K = d.K, N = d.N;
   const int64_t cw = F::code_words(K);
-  const int64_t arow = K / 2;       // bytes per activation row
-  uint8_t* As = lds;
-  uint8_t* Bs = lds + kBM * C::kAStride;
+  const int64_t arow = K / 2;                   // bytes per activation row
+  const MnzMasks km = mnz_masks(d.reserved, lane);
+  uint8_t* As = lds;                // stage buffer b: A at b * kStage, B after it
+  uint8_t* Bs = lds + C::kBOffset;
 
   v4i acc[kWaveTM][kWaveTN];
 #pragma unroll
@@ -247,17 +284,20 @@ __device__ __forceinline__ void prefill_tile(const qift_linear_desc& d, int64_t 
 #pragma unroll
     for (int j = 0; j < kWaveTN; ++j) acc[i][j] = v4i{0, 0, 0, 0};
 
+  // global -> registers for one stage. Out-of-range units load from the
+  // tile origin (always valid) and are zeroed afterwards, so the loads need
+  // no branches.
   uint4 ra[C::kALoads], rb[C::kBLoads];
-  constexpr int kAChunks = C::kARowBytes / 16;  // 16-byte chunks per row
-
   auto gload = [&](int64_t k0) {
 #pragma unroll
     for (int i = 0; i < C::kALoads; ++i) {
-      const int idx = tid + 256 * i;
-      const int row = idx / kAChunks, ch = idx % kAChunks;
+      const int u = tid + 256 * i;
+      const int row = u / C::kAUnits, ch = u % C::kAUnits;
       const int64_t m = m0 + row;
       const int64_t kb = k0 / 2 + 16 * ch;  // byte offset in the row
-      ra[i] = (m < M && 2 * kb < K) ? ld16(d.xq + m * arow + kb) : uint4{0u, 0u, 0u, 0u};
+      const bool ok = m < M && 2 * kb < K;
+      const uint4 v = ld16(d.xq + (ok ? m * arow + kb : 0));
+      ra[i] = ok ? v : uint4{0u, 0u, 0u, 0u};
     }
 #pragma unroll
     for (int i = 0; i < C::kBLoads; ++i) {
@@ -265,54 +305,90 @@ __device__ __forceinline__ void prefill_tile(const qift_linear_desc& d, int64_t 
       const int64_t tn = nt0 + 16 * (u >> 6);
       const int ul = u & 63;
       const bool ok = tn < N && k0 + (int64_t)(ul >> 4) * F::kLaneK < K;
-      rb[i] = ok ? ld16(d.codes + (tn >> 4) * 16 * cw + (k0 / C::kBK) * 256 + 4 * ul)
-                 : uint4{0u, 0u, 0u, 0u};
+      const uint4 v = ld16(d.codes + (ok ? (tn >> 4) * 16 * cw + (k0 / C::kBK) * 256 + 4 * ul : 0));
+      rb[i] = ok ? v : uint4{0u, 0u, 0u, 0u};
     }
   };
-  auto lstore = [&]() {
+  auto lstore = [&](int buf) {
+    uint8_t* as = As + buf * C::kStage;
+    uint8_t* bs = Bs + buf * C::kStage;
 #pragma unroll
     for (int i = 0; i < C::kALoads; ++i) {
-      const int idx = tid + 256 * i;
-      const int row = idx / kAChunks, ch = idx % kAChunks;
-      *reinterpret_cast<uint4*>(As + row * C::kAStride + 16 * ch) = ra[i];
+      const int u = tid + 256 * i;
+      const int row = u / C::kAUnits, ch = u % C::kAUnits;
+      uint2* dst = reinterpret_cast<uint2*>(as + row * C::kAStride + 16 * ch);
+      dst[0] = uint2{ra[i].x, ra[i].y};
+      dst[1] = uint2{ra[i].z, ra[i].w};
     }
 #pragma unroll
     for (int i = 0; i < C::kBLoads; ++i)
-      *reinterpret_cast<uint4*>(Bs + 16 * (tid + 256 * i)) = rb[i];
+      *reinterpret_cast<uint4*>(bs + 16 * (tid + 256 * i)) = rb[i];
+  };
+  auto compute = [&](int buf) {
+    const uint8_t* as = As + buf * C::kStage;
+    const uint8_t* bs = Bs + buf * C::kStage;
+    // this lane's weight units for the stage (16 bytes per fragment)
+    uint4 fb[kWaveTN];
+#pragma unroll
+    for (int j = 0; j < kWaveTN; ++j)
+      fb[j] = *reinterpret_cast<const uint4*>(bs + ((wn >> 4) + j) * 1024 + 16 * lane);
+#pragma unroll
+    for (int s = 0; s < F::kSteps; ++s) {
+      // activation fragments of this step: 8 bytes = 16 features per lane
+      v4i A[kWaveTM];
+#pragma unroll
+      for (int i = 0; i < kWaveTM; ++i) {
+        const uint2 a = *reinterpret_cast<const uint2*>(
+            as + (wm + 16 * i + r16) * C::kAStride + g * (F::kLaneK / 2) + 8 * s);
+        A[i] = int4_operand(a.x, a.y);
+      }
+#pragma unroll
+      for (int j = 0; j < kWaveTN; ++j) {
+        const v4i B = weight_operand<LV>(fb[j], s, km);
+#pragma unroll
+        for (int i = 0; i < kWaveTM; ++i) acc[i][j] = mfma16(A[i], B, acc[i][j]);
+      }
+#if QIFT_PREFILL_SCHED
+      // interleave: each MFMA followed by up to 2 VALU instructions
+#pragma unroll
+      for (int k = 0; k < kWaveTM * kWaveTN; ++k) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);  // VALU
+      }
+#endif
+    }
   };
 
   const int64_t nstages = (K + C::kBK - 1) / C::kBK;
+#if QIFT_PREFILL_DBUF
+  // two LDS stages: stage st is computed from buffer st % 2 while the loads
+  // of stage st + 1 (already in registers) go to the other buffer; one
+  // barrier per stage.
+  gload(0);
+  lstore(0);
+  if (nstages > 1) gload(C::kBK);
+  __syncthreads();
+  for (int64_t st = 0; st < nstages; ++st) {
+    const int buf = (int)(st & 1);
+    compute(buf);
+    if (st + 1 < nstages) {
+      lstore(buf ^ 1);
+      if (st + 2 < nstages) gload((st + 2) * C::kBK);
+    }
+    __syncthreads();
+  }
+#else
+  // one LDS stage; the next stage's global loads are in flight in registers
+  // while the current stage computes
   gload(0);
   for (int64_t st = 0; st < nstages; ++st) {
     __syncthreads();  // previous stage's LDS reads are done
-    lstore();
+    lstore(0);
     __syncthreads();
     if (st + 1 < nstages) gload((st + 1) * C::kBK);
-    // fragments of this lane: activations (segment g of each A row), codes
-    uint4 fa0[kWaveTM], fa1[kWaveTM], fb[kWaveTN];
-#pragma unroll
-    for (int i = 0; i < kWaveTM; ++i) {
-      const uint8_t* p = As + (wm + 16 * i + r16) * C::kAStride + g * (F::kLaneK / 2);
-      fa0[i] = *reinterpret_cast<const uint4*>(p);
-      if constexpr (!F::kInt4) fa1[i] = *reinterpret_cast<const uint4*>(p + 16);
-      else fa1[i] = uint4{0u, 0u, 0u, 0u};
-    }
-#pragma unroll
-    for (int j = 0; j < kWaveTN; ++j)
-      fb[j] = *reinterpret_cast<const uint4*>(Bs + ((wn >> 4) + j) * 1024 + 16 * lane);
-#pragma unroll
-    for (int s = 0; s < F::kSteps; ++s) {
-      v4i B[kWaveTN];
-#pragma unroll
-      for (int j = 0; j < kWaveTN; ++j) B[j] = weight_operand<LV>(fb[j], s);
-#pragma unroll
-      for (int i = 0; i < kWaveTM; ++i) {
-        const v4i A = act_operand(fa0[i], fa1[i], s);
-#pragma unroll
-        for (int j = 0; j < kWaveTN; ++j) acc[i][j] = mfma16(A, B[j], acc[i][j]);
-      }
-    }
+    compute(0);
   }
+#endif
 
   const float kappa = level_kappa(LV);
 #pragma unroll
@@ -332,6 +408,200 @@ __device__ __forceinline__ void prefill_tile(const qift_linear_desc& d, int64_t 
       }
     }
   }
+}
+
+// ---------------------------------------------------------------------------
+// prefill, direct-to-LDS path (K a multiple of 256)
+//
+// Stages of 256 features, double-buffered in LDS and filled with gfx950's
+// global_load_lds_dwordx4 (each lane's 16 bytes land at base + 16 * lane), so
+// the next stage streams in while the current one computes, with one barrier
+// per stage and no staging registers. Activation rows (128 bytes per stage)
+// are stored unpadded with an XOR swizzle: 16-byte unit c of row r sits in
+// slot c ^ (r % 8), which makes the 16-byte fragment reads of 8 consecutive
+// rows hit 8 different bank groups. Weight tiles are copied verbatim (their
+// tiled layout is already lane order).
+// ---------------------------------------------------------------------------
+
+constexpr int kDlBM = 128, kDlBN = 128;  // workgroup tile; 2 x 2 waves of 64 x 64
+constexpr int kDlTM = 4, kDlTN = 4;
+
+template <int LV>
+struct DlCfg {
+  static constexpr bool kInt4 = LV == QIFT_LEVELS_INT4;
+  static constexpr int kStageK = 256;
+  static constexpr int kABytes = kDlBM * 128;                       // 16 KB
+  static constexpr int kBChunks = kInt4 ? 2 : 1;                     // 1 KB chunks per tile
+  static constexpr int kBBytes = (kDlBN / 16) * kBChunks * 1024;    // 8 or 16 KB
+  static constexpr int kStage = kABytes + kBBytes;
+  static constexpr int kLds = 2 * kStage;
+  static constexpr int kAInstr = kABytes / 1024 / 4;                // per wave per stage
+  static constexpr int kBInstr = kBBytes / 1024 / 4;
+};
+
+// 16 bytes per lane from global memory straight into LDS at
+// lds_wave_base + 16 * lane (lds_wave_base must be the same for the whole wave)
+typedef __attribute__((address_space(3))) void lds_void;
+__device__ __forceinline__ void gl_lds16(const void* g, uint8_t* lds_wave_base) {
+  __builtin_amdgcn_global_load_lds(g, (lds_void*)lds_wave_base, 16, 0, 0);
+}
+
+template <int LV>
+__device__ __forceinline__ void prefill_tile_dl(const qift_linear_desc& d, int64_t m0,
+                                                int64_t nt0, int scale_f16, int y_dtype,
+                                                uint8_t* lds) {
+  using C = DlCfg<LV>;
+  using F = Fmt<LV>;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int r16 = lane & 15;
+  const int g = lane >> 4;
+  const int wm = (wave >> 1) * 64;
+  const int wn = (wave & 1) * 64;
+  const int64_t M = d.M, K = d.K, N = d.N;
+  const int64_t cw = F::code_words(K);
+  const int64_t arow = K / 2;
+  const int64_t np16 = (N + 15) >> 4;     // 16-channel tiles in the weight buffer
+  const MnzMasks km = mnz_masks(d.reserved, lane);
+
+  // per-lane source offsets that do not change between stages
+  // A: wave instruction p covers rows 8 (4 wave + p) .. +7; lane -> row
+  // 8(...) + lane / 8, slot lane % 8, global unit slot ^ (row % 8)
+  int64_t a_off[C::kAInstr];
+#pragma unroll
+  for (int p = 0; p < C::kAInstr; ++p) {
+    const int row = 8 * (wave * C::kAInstr + p) + (lane >> 3);
+    int64_t m = m0 + row;
+    m = m < M ? m : M - 1;                // rows past M only feed discarded outputs
+    const int c = (lane & 7) ^ (row & 7);
+    a_off[p] = m * arow + 16 * c;
+  }
+  // B: unit u = (wave * kBInstr + p) * 64 + lane = (tile, chunk) * 64 + lane
+  int64_t b_off[C::kBInstr];
+#pragma unroll
+  for (int p = 0; p < C::kBInstr; ++p) {
+    const int unit_blk = wave * C::kBInstr + p;
+    const int tile = unit_blk / C::kBChunks, chunk = unit_blk % C::kBChunks;
+    int64_t t = (nt0 >> 4) + tile;
+    t = t < np16 ? t : np16 - 1;          // tiles past N only feed discarded outputs
+    b_off[p] = t * 16 * cw + chunk * 256 + 4 * lane;
+  }
+  auto issue = [&](int64_t st, int buf) {
+    uint8_t* as = lds + buf * C::kStage;
+    uint8_t* bs = as + C::kABytes;
+#pragma unroll
+    for (int p = 0; p < C::kAInstr; ++p)
+      gl_lds16(d.xq + a_off[p] + st * 128, as + (wave * C::kAInstr + p) * 1024);
+#pragma unroll
+    for (int p = 0; p < C::kBInstr; ++p)
+      gl_lds16(d.codes + b_off[p] + st * C::kBChunks * 256, bs + (wave * C::kBInstr + p) * 1024);
+  };
+
+  v4i acc[kDlTM][kDlTN];
+#pragma unroll
+  for (int i = 0; i < kDlTM; ++i)
+#pragma unroll
+    for (int j = 0; j < kDlTN; ++j) acc[i][j] = v4i{0, 0, 0, 0};
+
+  auto compute = [&](int buf) {
+    const uint8_t* as = lds + buf * C::kStage;
+    const uint8_t* bs = as + C::kABytes;
+    uint4 fb[kDlTN];  // 2-bit: one unit covers the whole stage; int4: reloaded per half
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      // A: 16 bytes = 32 features per fragment for two MFMA steps
+      uint4 fa[kDlTM];
+#pragma unroll
+      for (int i = 0; i < kDlTM; ++i) {
+        const int row = wm + 16 * i + r16;
+        const int c = C::kInt4 ? 4 * h + g : 2 * g + h;
+        fa[i] = *reinterpret_cast<const uint4*>(as + row * 128 + 16 * (c ^ (row & 7)));
+      }
+      // B: the lane's 16-byte unit of each fragment's tile (chunk h for int4)
+#pragma unroll
+      for (int j = 0; j < kDlTN; ++j) {
+        const int tile = (wn >> 4) + j;
+        const int blk = C::kInt4 ? tile * 2 + h : tile;
+        if (C::kInt4 || h == 0)
+          fb[j] = *reinterpret_cast<const uint4*>(bs + blk * 1024 + 16 * lane);
+      }
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2) {
+        v4i A[kDlTM];
+#pragma unroll
+        for (int i = 0; i < kDlTM; ++i)
+          A[i] = s2 == 0 ? int4_operand(fa[i].x, fa[i].y) : int4_operand(fa[i].z, fa[i].w);
+        const int wstep = C::kInt4 ? s2 : 2 * h + s2;   // step inside the 16-byte B unit
+#pragma unroll
+        for (int j = 0; j < kDlTN; ++j) {
+          const v4i B = weight_operand<LV>(fb[j], wstep, km);
+#pragma unroll
+          for (int i = 0; i < kDlTM; ++i) acc[i][j] = mfma16(A[i], B, acc[i][j]);
+        }
+#if QIFT_PREFILL_SCHED
+#pragma unroll
+        for (int k = 0; k < kDlTM * kDlTN; ++k) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+          __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);  // VALU
+        }
+#endif
+      }
+    }
+  };
+
+  const int64_t nstages = K / C::kStageK;
+  issue(0, 0);
+  for (int64_t st = 0; st < nstages; ++st) {
+    __builtin_amdgcn_s_waitcnt(0);   // this wave's loads of stage st have landed
+    __syncthreads();                 // ... everyone's; and stage st-1 is consumed
+    if (st + 1 < nstages) issue(st + 1, (int)((st + 1) & 1));
+    compute((int)(st & 1));
+  }
+
+  const float kappa = level_kappa(LV);
+#pragma unroll
+  for (int j = 0; j < kDlTN; ++j) {
+    const int64_t n = nt0 + wn + 16 * j + r16;
+    if (n >= N) continue;
+    const float sw = load_scale(d.scales, n, scale_f16) * kappa;
+#pragma unroll
+    for (int i = 0; i < kDlTM; ++i) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int64_t m = m0 + wm + 16 * i + 4 * g + r;
+        if (m < M) {
+          const int a = acc[i][j][r] >> F::kShift;
+          store_y(d.Y, y_dtype, m * N + n, a, d.s_a[m] * sw);
+        }
+      }
+    }
+  }
+}
+
+// Tile order: with T tiles and T % 8 == 0, consecutive workgroups (which the
+// dispatcher spreads round-robin over the 8 XCDs) are mapped so that each XCD
+// works through a contiguous block of tiles, N-tile major, so the weight
+// panel of an N-tile and the activation panels stay in that XCD's L2.
+__device__ __forceinline__ void dl_tile_of(int64_t b, int64_t nM, int64_t nN, int64_t* tm,
+                                           int64_t* tn) {
+  const int64_t T = nM * nN;
+  int64_t t = b;
+  if ((T & 7) == 0) t = (b & 7) * (T >> 3) + (b >> 3);
+  *tn = t / nM;
+  *tm = t % nM;
+}
+
+// two workgroups per CU (<= 256 registers per lane) so that each SIMD has a
+// second wave to switch to while one waits on LDS or a barrier
+template <int LV>
+__global__ __launch_bounds__(256, QIFT_PREFILL_MINBLOCKS) void linear_prefill_dl_kernel(qift_linear_desc d, int scale_f16,
+                                                                int y_dtype) {
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[DlCfg<LV>::kLds];
+  const int64_t nM = (d.M + kDlBM - 1) / kDlBM, nN = (d.N + kDlBN - 1) / kDlBN;
+  int64_t tm, tn;
+  dl_tile_of(blockIdx.x, nM, nN, &tm, &tn);
+  prefill_tile_dl<LV>(d, tm * kDlBM, tn * kDlBN, scale_f16, y_dtype, lds);
 }
 
 template <int LV>
@@ -357,6 +627,26 @@ hipError_t launch_linear_decode(const qift_linear_desc& d, int scale_f16, int y_
 
 hipError_t launch_linear_prefill(const qift_linear_desc& d, int scale_f16, int y_dtype,
                                  hipStream_t s) {
+#if QIFT_PREFILL_DL
+  if (d.K % 256 == 0) {
+    const dim3 g1((unsigned)(((d.N + kDlBN - 1) / kDlBN) * ((d.M + kDlBM - 1) / kDlBM)));
+    switch (d.levels) {
+      case QIFT_LEVELS_MNZ:
+        hipLaunchKernelGGL(linear_prefill_dl_kernel<QIFT_LEVELS_MNZ>, g1, dim3(256), 0, s, d,
+                           scale_f16, y_dtype);
+        break;
+      case QIFT_LEVELS_POT:
+        hipLaunchKernelGGL(linear_prefill_dl_kernel<QIFT_LEVELS_POT>, g1, dim3(256), 0, s, d,
+                           scale_f16, y_dtype);
+        break;
+      default:
+        hipLaunchKernelGGL(linear_prefill_dl_kernel<QIFT_LEVELS_INT4>, g1, dim3(256), 0, s, d,
+                           scale_f16, y_dtype);
+        break;
+    }
+    return hipGetLastError();
+  }
+#endif
   const dim3 grid((unsigned)((d.N + kBN - 1) / kBN), (unsigned)((d.M + kBM - 1) / kBM));
   switch (d.levels) {
     case QIFT_LEVELS_MNZ:

@@ -57,15 +57,29 @@ __device__ __forceinline__ v4i int4_operand(uint32_t x0, uint32_t x1) {
   return a;
 }
 
+// The two masks of the MNZ operand held in vector registers. gfx9 VOP3
+// encodings take no literal constants, and the compiler only forms
+// v_and_or_b32 from (a & m) | o when m and o live in VGPRs; with literal or
+// scalar masks it emits v_and + v_or. The masks are therefore derived from a
+// per-lane value it cannot fold: zero * lane, with zero a descriptor field
+// that is always 0.
+struct MnzMasks {
+  uint32_t m, o;
+};
+__device__ __forceinline__ MnzMasks mnz_masks(int32_t zero, int lane) {
+  const uint32_t z = (uint32_t)zero * (uint32_t)lane;
+  return MnzMasks{0xC0C0C0C0u | z, 0x20202020u | z};
+}
+
 // 2-bit MNZ codes (one word, 16 features) -> 32*(2t+1) per byte: the code t
 // lands in the two top bits of its byte (64t as a signed byte) and bit 5 adds
-// 32.
-__device__ __forceinline__ v4i mnz_operand(uint32_t c) {
+// 32. Seven VALU instructions per 16 codes.
+__device__ __forceinline__ v4i mnz_operand(uint32_t c, MnzMasks k) {
   v4i b;
-  b[0] = (int)(((c << 6) & 0xC0C0C0C0u) | 0x20202020u);
-  b[1] = (int)(((c << 4) & 0xC0C0C0C0u) | 0x20202020u);
-  b[2] = (int)(((c << 2) & 0xC0C0C0C0u) | 0x20202020u);
-  b[3] = (int)((c & 0xC0C0C0C0u) | 0x20202020u);
+  b[0] = (int)(((c << 6) & k.m) | k.o);
+  b[1] = (int)(((c << 4) & k.m) | k.o);
+  b[2] = (int)(((c << 2) & k.m) | k.o);
+  b[3] = (int)((c & k.m) | k.o);
   return b;
 }
 
