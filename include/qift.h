@@ -144,9 +144,9 @@ qift_status qift_rotate_quant_act(const void* X, qift_dtype x_dtype, int64_t M, 
                                   qift_stream stream);
 
 /*
- * qift_w2a4_linear -- decoded weight application (Qift abstract: "sign-and-
- * shift decoded weight application" for the power-of-two set; the half-scale
- * integer form for the main set):
+ * qift_w2a4_linear -- the linear layer with decoded two-bit weights (Qift
+ * abstract: the power-of-two set is applied by sign and shift, the main set
+ * in its half-scale integer form):
  *   acc[m, n] = sum_k q[m, k] * level[n, k]            (exact, int32)
  *   Y[m, n]   = acc[m, n] * s_a[m] * s_w[n] * kappa    (float32)
  * with level the integer level of the code (half-scale for MNZ) and

@@ -12,7 +12,7 @@ What the method computes comes from one source, the abstract of
 W2A4/KV4 LLM Inference" (arXiv 2606.02823, abstract page). The abstract fixes:
 
 * weights and activations pass through a Hadamard rotation before scalar
-  quantization (the "Hadamard-rotated quantization pipeline");
+  quantization;
 * the main two-bit level set is {+-0.5, +-1.5} (half-scale {+-1, +-3}); a
   power-of-two variant uses {+-1, +-4}, applied by sign and shift;
 * one per-output-channel scale, no zero point, no groups, no learned codebook;

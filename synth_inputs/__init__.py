@@ -96,7 +96,7 @@ def weights(N: int, K: int, seed: int, sigma: float = 0.02) -> np.ndarray:
 def heavy_tailed_weights(N: int, K: int, seed: int, dof: float = 3.0,
                          sigma: float = 0.02) -> np.ndarray:
     """float32 [N, K] Student-t rows (excess kurtosis >> 0), scaled to sigma.
-    Used to show that rotation Gaussianizes a heavy-tailed row."""
+    Used to show that the rotation makes a heavy-tailed row close to Gaussian."""
     rng = np.random.default_rng(seed)
     return (sigma * rng.standard_t(dof, size=(N, K))).astype(np.float32)
 

@@ -109,10 +109,11 @@ def test_rotation_orthogonal():
 
 
 def test_rotation_gaussianizes_heavy_tails():
-    """Abstract: rotation mainly Gaussianizes the standardized weight shape
-    (excess kurtosis drops by orders of magnitude). Synthetic analogue:
-    Student-t rows (infinite-variance tails cut by sampling) lose almost all
-    excess kurtosis after a 256-block rotation."""
+    """The Qift abstract reports that after the Hadamard rotation the
+    standardized weight rows are close to Gaussian, their excess kurtosis
+    falling by orders of magnitude. Synthetic analogue: heavy-tailed
+    Student-t rows lose almost all excess kurtosis after a 4096-block
+    rotation."""
     W = si.heavy_tailed_weights(64, 4096, seed=5, dof=4.0).astype(np.float64)
     k0 = np.median(O.excess_kurtosis(W))
     k1 = np.median(np.abs(O.excess_kurtosis(O.rotate(W, 4096))))
