@@ -185,7 +185,7 @@ qift_status qift_kv4_quant(const void* KV, qift_dtype dtype, int64_t T, int64_t 
   if (st != QIFT_OK) return st;
   const int64_t rows = T * H;
   if (rows == 0) return ok();
-  if (rows / (256 / (D / 8)) + 1 > kMaxGrid) return fail(QIFT_ERR_UNSUPPORTED, "T*H too large");
+  if (rows / 8 + 1 > kMaxGrid) return fail(QIFT_ERR_UNSUPPORTED, "T*H too large");
   if (!KV || !kvq || !scales) return fail(QIFT_ERR_INVALID_ARG, "null buffer");
   if (!aligned(KV, 16) || !aligned(kvq, 16) || !aligned(scales, 4))
     return fail(QIFT_ERR_ALIGNMENT, "KV and kvq must be 16-byte aligned, scales 4-byte");

@@ -3,57 +3,66 @@
 // its own absmax scale (the "KV4" of rotated W2A4/KV4 inference, Qift
 // abstract).
 //
-// Layout on the GPU: a head vector of D elements is held by L = D/8 lanes,
-// 8 consecutive elements per lane, so one wave holds 64/L vectors. The first
-// three butterfly stages run inside a lane's registers, the remaining
-// log2(B)-3 stages between lanes with xor shuffles. Loads are 16 bytes per
-// lane (bf16) and the packed output is one 32-bit word per lane, both fully
-// coalesced; the kernel is bound by HBM bandwidth.
+// Layout on the GPU: a head vector of D elements is held by L = D/E lanes
+// with E = min(D, 32) consecutive elements each, so five butterfly stages run
+// inside a lane's registers and only log2(L) stages (xor 1 and 2 for
+// D = 128, quad permutes) cross lanes. A lane loads E*2 contiguous bytes
+// (bf16) and stores E/2 bytes of codes; the kernel is bound by HBM bandwidth.
 #include "qift_internal.h"
 
 namespace qift {
 
 constexpr int kKvThreads = 256;
 
-template <int L, typename T>
+template <int E, typename T>
+__device__ __forceinline__ void kv4_load(const T* __restrict__ src, float v[E]) {
+  if constexpr (sizeof(T) == 2) {
+#pragma unroll
+    for (int i = 0; i < E / 8; ++i) {
+      const uint4 u = reinterpret_cast<const uint4*>(src)[i];
+      const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        v[8 * i + 2 * k] = __uint_as_float(w[k] << 16);
+        v[8 * i + 2 * k + 1] = __uint_as_float(w[k] & 0xffff0000u);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < E / 4; ++i) {
+      const float4 f = reinterpret_cast<const float4*>(src)[i];
+      v[4 * i] = f.x;
+      v[4 * i + 1] = f.y;
+      v[4 * i + 2] = f.z;
+      v[4 * i + 3] = f.w;
+    }
+  }
+}
+
+template <int E, int L, typename T>
 __global__ __launch_bounds__(kKvThreads) void kv4_kernel(const T* __restrict__ KV, int64_t rows,
                                                          int log2b, float norm,
                                                          uint8_t* __restrict__ kvq,
                                                          float* __restrict__ scales) {
-  constexpr int D = 8 * L;
+  constexpr int D = E * L;
+  constexpr int kLogE = E == 32 ? 5 : 4;
   const int lane = threadIdx.x & (L - 1);
-  const int64_t r = (int64_t)blockIdx.x * (kKvThreads / L) + (threadIdx.x / L);
+  const int64_t r = (int64_t)blockIdx.x * (kKvThreads / L) + threadIdx.x / L;
   const bool live = r < rows;
-  float v[8];
+  float v[E];
   if (live) {
-    if constexpr (sizeof(T) == 2) {
-      const uint4 u = reinterpret_cast<const uint4*>(KV + r * D)[lane];
-      v[0] = __uint_as_float(u.x << 16);
-      v[1] = __uint_as_float(u.x & 0xffff0000u);
-      v[2] = __uint_as_float(u.y << 16);
-      v[3] = __uint_as_float(u.y & 0xffff0000u);
-      v[4] = __uint_as_float(u.z << 16);
-      v[5] = __uint_as_float(u.z & 0xffff0000u);
-      v[6] = __uint_as_float(u.w << 16);
-      v[7] = __uint_as_float(u.w & 0xffff0000u);
-    } else {
-      const float4* p = reinterpret_cast<const float4*>(KV + r * D) + 2 * lane;
-      const float4 a = p[0], b = p[1];
-      v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
-      v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
-    }
+    kv4_load<E, T>(KV + r * D + lane * E, v);
   } else {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) v[i] = 0.f;
+    for (int j = 0; j < E; ++j) v[j] = 0.f;
   }
-  // in-lane stages (strides 1, 2, 4)
-  const int in_lane = log2b < 3 ? log2b : 3;
+  // in-lane stages (strides 1 .. E/2)
 #pragma unroll
-  for (int st = 0; st < 3; ++st) {
-    if (st < in_lane) {
+  for (int st = 0; st < kLogE; ++st) {
+    if (st < log2b) {
       const int h = 1 << st;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
+      for (int j = 0; j < E; ++j) {
         if (!(j & h)) {
           const float a = v[j], b = v[j + h];
           v[j] = a + b;
@@ -62,51 +71,57 @@ __global__ __launch_bounds__(kKvThreads) void kv4_kernel(const T* __restrict__ K
       }
     }
   }
-  // cross-lane stages (strides 8 .. B/2): partner lane = lane ^ h
-  for (int h = 1; (8 * h) < (1 << log2b); h <<= 1) {
-    const bool upper = (lane & h) != 0;
+  // cross-lane stages (strides E .. B/2): partner lane = lane ^ h
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const float o = __shfl_xor(v[j], h, 64);
-      v[j] = upper ? (o - v[j]) : (v[j] + o);
+  for (int h = 1; h < L; h <<= 1) {
+    if ((E * h) < (1 << log2b)) {
+      const bool upper = (lane & h) != 0;
+#pragma unroll
+      for (int j = 0; j < E; ++j) {
+        const float o = __shfl_xor(v[j], h, 64);
+        v[j] = upper ? (o - v[j]) : (v[j] + o);
+      }
     }
   }
   float m = 0.f;
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
+  for (int j = 0; j < E; ++j) {
     v[j] *= norm;
     m = fmaxf(m, fabsf(v[j]));
   }
 #pragma unroll
   for (int off = 1; off < L; off <<= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
   const float s = __fdiv_rn(m, 7.0f);
-  uint32_t word = 0;
+  const float rs = s != 0.f ? __fdiv_rn(1.0f, s) : 0.f;
+  uint32_t words[E / 8];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    int q = 0;
-    if (s != 0.f) {
-      float t = rintf(__fdiv_rn(v[j], s));
-      t = fminf(fmaxf(t, -7.f), 7.f);
-      q = (int)t;
-    }
-    word |= ((uint32_t)q & 0xFu) << (4 * j);
+  for (int w = 0; w < E / 8; ++w) {
+    uint32_t word = 0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      word |= code_int4_recip(v[8 * w + j], s, rs) << (4 * j);
+    words[w] = word;
   }
   if (live) {
-    reinterpret_cast<uint32_t*>(kvq + r * (D / 2))[lane] = word;
+    uint8_t* dst = kvq + r * (D / 2) + lane * (E / 2);
+    if constexpr (E == 32)
+      *reinterpret_cast<uint4*>(dst) = uint4{words[0], words[1], words[2], words[3]};
+    else
+      *reinterpret_cast<uint2*>(dst) = uint2{words[0], words[1]};
     if (lane == 0) scales[r] = s;
   }
 }
 
-template <int L>
+template <int E, int L>
 static void launch_kv4_l(const void* KV, int bf16, int64_t rows, int log2b, float norm,
                          uint8_t* kvq, float* scales, hipStream_t s) {
   const int per_block = kKvThreads / L;
   const unsigned grid = (unsigned)((rows + per_block - 1) / per_block);
   if (bf16)
-    hipLaunchKernelGGL((kv4_kernel<L, uint16_t>), dim3(grid), dim3(kKvThreads), 0, s,
+    hipLaunchKernelGGL((kv4_kernel<E, L, uint16_t>), dim3(grid), dim3(kKvThreads), 0, s,
                        reinterpret_cast<const uint16_t*>(KV), rows, log2b, norm, kvq, scales);
   else
-    hipLaunchKernelGGL((kv4_kernel<L, float>), dim3(grid), dim3(kKvThreads), 0, s,
+    hipLaunchKernelGGL((kv4_kernel<E, L, float>), dim3(grid), dim3(kKvThreads), 0, s,
                        reinterpret_cast<const float*>(KV), rows, log2b, norm, kvq, scales);
 }
 
@@ -116,11 +131,11 @@ hipError_t launch_kv4(const void* KV, int bf16, int64_t rows, int D, int had_blo
   while ((1 << log2b) < had_block) ++log2b;
   const float norm = (float)(1.0 / __builtin_sqrt((double)had_block));
   switch (D) {
-    case 16: launch_kv4_l<2>(KV, bf16, rows, log2b, norm, kvq, scales, s); break;
-    case 32: launch_kv4_l<4>(KV, bf16, rows, log2b, norm, kvq, scales, s); break;
-    case 64: launch_kv4_l<8>(KV, bf16, rows, log2b, norm, kvq, scales, s); break;
-    case 128: launch_kv4_l<16>(KV, bf16, rows, log2b, norm, kvq, scales, s); break;
-    case 256: launch_kv4_l<32>(KV, bf16, rows, log2b, norm, kvq, scales, s); break;
+    case 16: launch_kv4_l<16, 1>(KV, bf16, rows, log2b, norm, kvq, scales, s); break;
+    case 32: launch_kv4_l<32, 1>(KV, bf16, rows, log2b, norm, kvq, scales, s); break;
+    case 64: launch_kv4_l<32, 2>(KV, bf16, rows, log2b, norm, kvq, scales, s); break;
+    case 128: launch_kv4_l<32, 4>(KV, bf16, rows, log2b, norm, kvq, scales, s); break;
+    case 256: launch_kv4_l<32, 8>(KV, bf16, rows, log2b, norm, kvq, scales, s); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -30,6 +30,27 @@ __device__ __forceinline__ uint16_t float_to_bf16_bits(float f) {
   return (uint16_t)(u >> 16);
 }
 
+// The 4-bit two's-complement code of clamp(rint(x / s), -7, 7), x / s the
+// IEEE float32 quotient, for |x| <= 7 s (so the clamp never binds), computed
+// as rint(x * r) with r = 1 / s except near a rounding tie:
+//  - for |x / s| <= 7.5, x * r is within 1.3e-6 of the correctly rounded
+//    quotient (two roundings of 2^-24 relative each), so when x * r is more
+//    than 1e-5 from a half-integer both round to the same integer;
+//  - within that window, or when x * r is not finite (1/s overflowing for a
+//    tiny s), the exact division decides;
+//  - rint uses the float adder: y + 1.5*2^23 rounds to nearest even and
+//    leaves rint(y) in the low mantissa bits in two's complement.
+// s == 0 gives code 0.
+__device__ __forceinline__ uint32_t code_int4_recip(float x, float s, float r) {
+  const float kMagic = 12582912.0f;  // 1.5 * 2^23
+  const float y = x * r;
+  const float ym = y + kMagic;
+  const float t = ym - kMagic;       // rint(y), exact
+  uint32_t code = __float_as_uint(ym) & 0xFu;
+  if (!(fabsf(y - t) <= 0.49999f)) code = (uint32_t)(int)rintf(__fdiv_rn(x, s)) & 0xFu;
+  return s == 0.f ? 0u : code;
+}
+
 __device__ __forceinline__ float load_scale(const void* p, int64_t i, int is_f16) {
   if (is_f16) return __half2float(reinterpret_cast<const __half*>(p)[i]);
   return reinterpret_cast<const float*>(p)[i];

@@ -145,6 +145,7 @@ __global__ __launch_bounds__(kRowThreads) void rotate_quant_act_kernel(
   fwht_row(row, K, log2b, tid);
   const float amax = row_absmax(row, K, norm, tid, red);
   const float s = __fdiv_rn(amax, 7.0f);
+  const float rs = s != 0.f ? __fdiv_rn(1.0f, s) : 0.f;
   if (tid == 0) s_a[m] = s;
   uint8_t* xq_row = xq + m * (int64_t)(K / 2);
   if ((K & 7) == 0) {
@@ -154,7 +155,7 @@ __global__ __launch_bounds__(kRowThreads) void rotate_quant_act_kernel(
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const float x = row[8 * g + i] * norm;
-        word |= ((uint32_t)quant_int4(x, s) & 0xFu) << (4 * i);
+        word |= code_int4_recip(x, s, rs) << (4 * i);
         if (x_rot) x_rot[m * K + 8 * g + i] = x;
       }
       w_row[g] = word;
@@ -162,12 +163,164 @@ __global__ __launch_bounds__(kRowThreads) void rotate_quant_act_kernel(
   } else {
     for (int j = tid; j < (K >> 1); j += kRowThreads) {
       const float x0 = row[2 * j] * norm, x1 = row[2 * j + 1] * norm;
-      xq_row[j] = (uint8_t)(((uint32_t)quant_int4(x0, s) & 0xFu) |
-                            (((uint32_t)quant_int4(x1, s) & 0xFu) << 4));
+      xq_row[j] = (uint8_t)(code_int4_recip(x0, s, rs) | (code_int4_recip(x1, s, rs) << 4));
       if (x_rot) {
         x_rot[m * K + 2 * j] = x0;
         x_rot[m * K + 2 * j + 1] = x1;
       }
+    }
+  }
+}
+
+// --- K1 fast path: K % 16 == 0 and block >= 16 ---------------------------------
+//
+// Element e of the row lives in LDS at e + e / 16 (one pad word per 16
+// floats). Each thread owns groups of 16 consecutive elements:
+//  1. global load (32 bytes bf16 / 64 bytes float) straight into registers,
+//     butterfly stages 0-3 in registers, padded store (the 16 stores of a
+//     thread hit 16 consecutive banks; neighbouring threads are 17 words
+//     apart, so a wave's stores are conflict-free);
+//  2. remaining stages in passes of up to four through LDS (padded, so the
+//     stride-16 and stride-256 passes are conflict-free as well);
+//  3. each thread reads its 16 consecutive elements back, the row absmax is
+//     reduced, and the thread quantizes and stores 16 codes as 8 bytes.
+
+__device__ __forceinline__ int pad16(int e) { return e + (e >> 4); }
+
+template <int NS>
+__device__ __forceinline__ void fwht_pass_padded(float* row, int K, int p, int tid) {
+  constexpr int R = 1 << NS;
+  const int sh = 4 * p;
+  const int S = 1 << sh;
+  const int groups = K >> NS;
+  for (int grp = tid; grp < groups; grp += kRowThreads) {
+    const int low = grp & (S - 1);
+    const int high = grp >> sh;
+    const int base = (high << (sh + NS)) | low;
+    float v[R];
+#pragma unroll
+    for (int j = 0; j < R; ++j) v[j] = row[pad16(base + j * S)];
+#pragma unroll
+    for (int st = 0; st < NS; ++st) {
+      const int h = 1 << st;
+#pragma unroll
+      for (int j = 0; j < R; ++j) {
+        if (!(j & h)) {
+          const float a = v[j], b = v[j + h];
+          v[j] = a + b;
+          v[j + h] = a - b;
+        }
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < R; ++j) row[pad16(base + j * S)] = v[j];
+  }
+}
+
+template <typename T>
+__device__ __forceinline__ void load16(const T* __restrict__ src, float v[16]);
+
+template <>
+__device__ __forceinline__ void load16<uint16_t>(const uint16_t* __restrict__ src, float v[16]) {
+  const uint4 a = reinterpret_cast<const uint4*>(src)[0];
+  const uint4 b = reinterpret_cast<const uint4*>(src)[1];
+  const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    v[2 * i] = __uint_as_float(w[i] << 16);
+    v[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+  }
+}
+
+template <>
+__device__ __forceinline__ void load16<float>(const float* __restrict__ src, float v[16]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float4 f = reinterpret_cast<const float4*>(src)[i];
+    v[4 * i] = f.x;
+    v[4 * i + 1] = f.y;
+    v[4 * i + 2] = f.z;
+    v[4 * i + 3] = f.w;
+  }
+}
+
+template <typename T>
+__global__ __launch_bounds__(kRowThreads) void rotate_quant_act_fast_kernel(
+    const T* __restrict__ X, int K, int log2b, float norm, uint8_t* __restrict__ xq,
+    float* __restrict__ s_a, float* __restrict__ x_rot) {
+  extern __shared__ float row[];
+  __shared__ float red[kRowThreads / 64];
+  const int tid = threadIdx.x;
+  const int64_t m = blockIdx.x;
+  const int groups = K >> 4;
+  const T* src = X + m * K;
+  // 1. load + stages 0..3 in registers
+  for (int grp = tid; grp < groups; grp += kRowThreads) {
+    float v[16];
+    load16<T>(src + 16 * grp, v);
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+      const int h = 1 << st;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        if (!(j & h)) {
+          const float a = v[j], b = v[j + h];
+          v[j] = a + b;
+          v[j + h] = a - b;
+        }
+      }
+    }
+    float* dst = row + 17 * grp;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) dst[j] = v[j];
+  }
+  __syncthreads();
+  // 2. stages 4.. through padded LDS
+  for (int p = 1; 4 * p < log2b; ++p) {
+    const int ns = min(4, log2b - 4 * p);
+    switch (ns) {
+      case 1: fwht_pass_padded<1>(row, K, p, tid); break;
+      case 2: fwht_pass_padded<2>(row, K, p, tid); break;
+      case 3: fwht_pass_padded<3>(row, K, p, tid); break;
+      default: fwht_pass_padded<4>(row, K, p, tid); break;
+    }
+    __syncthreads();
+  }
+  // 3. absmax over the row, then quantize 16 consecutive elements per thread
+  float mloc = 0.f;
+  for (int grp = tid; grp < groups; grp += kRowThreads) {
+    const float* s16 = row + 17 * grp;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) mloc = fmaxf(mloc, fabsf(s16[j]));
+  }
+  mloc *= norm;  // rounding is monotonic: max(|v|)*norm == max(|v*norm|)
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) mloc = fmaxf(mloc, __shfl_xor(mloc, off, 64));
+  if ((tid & 63) == 0) red[tid >> 6] = mloc;
+  __syncthreads();
+  float amax = red[0];
+#pragma unroll
+  for (int w = 1; w < kRowThreads / 64; ++w) amax = fmaxf(amax, red[w]);
+  const float s = __fdiv_rn(amax, 7.0f);
+  const float rs = s != 0.f ? __fdiv_rn(1.0f, s) : 0.f;
+  if (tid == 0) s_a[m] = s;
+  uint2* xrow = reinterpret_cast<uint2*>(xq + m * (int64_t)(K / 2));
+  for (int grp = tid; grp < groups; grp += kRowThreads) {
+    const float* s16 = row + 17 * grp;
+    float x[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) x[j] = s16[j] * norm;
+    uint32_t w0 = 0, w1 = 0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      w0 |= code_int4_recip(x[j], s, rs) << (4 * j);
+      w1 |= code_int4_recip(x[8 + j], s, rs) << (4 * j);
+    }
+    xrow[grp] = uint2{w0, w1};
+    if (x_rot) {
+      float4* xr = reinterpret_cast<float4*>(x_rot + m * K + 16 * grp);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) xr[i] = float4{x[4 * i], x[4 * i + 1], x[4 * i + 2], x[4 * i + 3]};
     }
   }
 }
@@ -271,9 +424,22 @@ static float had_norm(int B) { return (float)(1.0 / __builtin_sqrt((double)B)); 
 
 hipError_t launch_rotate_quant_act(const void* X, int x_bf16, int64_t M, int64_t K, int had_block,
                                    uint8_t* xq, float* s_a, float* x_rot, hipStream_t s) {
-  const size_t lds = (size_t)K * sizeof(float);
   const int lb = ilog2(had_block);
   const float nrm = had_norm(had_block);
+  const uintptr_t align = reinterpret_cast<uintptr_t>(X) | reinterpret_cast<uintptr_t>(xq) |
+                          reinterpret_cast<uintptr_t>(x_rot);
+  if (K % 16 == 0 && had_block >= 16 && (align & 15) == 0) {
+    const size_t lds = (size_t)(K + K / 16) * sizeof(float);
+    if (x_bf16)
+      hipLaunchKernelGGL(rotate_quant_act_fast_kernel<uint16_t>, dim3((unsigned)M),
+                         dim3(kRowThreads), lds, s, reinterpret_cast<const uint16_t*>(X), (int)K,
+                         lb, nrm, xq, s_a, x_rot);
+    else
+      hipLaunchKernelGGL(rotate_quant_act_fast_kernel<float>, dim3((unsigned)M), dim3(kRowThreads),
+                         lds, s, reinterpret_cast<const float*>(X), (int)K, lb, nrm, xq, s_a, x_rot);
+    return hipGetLastError();
+  }
+  const size_t lds = (size_t)K * sizeof(float);
   if (x_bf16)
     hipLaunchKernelGGL(rotate_quant_act_kernel<uint16_t>, dim3((unsigned)M), dim3(kRowThreads),
                        lds, s, reinterpret_cast<const uint16_t*>(X), (int)K, lb, nrm, xq, s_a,

@@ -81,6 +81,26 @@ def test_rotate_quant_bitexact_given_rotated_input(M, K):
     assert np.array_equal(xg.view(np.uint32), xr32.view(np.uint32))
 
 
+@pytest.mark.parametrize("M,K,B", [(3, 16, 16), (5, 256, 64), (17, 4096, 256), (2, 4096, 1024),
+                                   (4, 4096, 4096), (3, 11008, 256), (2, 14336, 1024),
+                                   (1, 16384, 4096), (33, 1024, 16)])
+def test_rotate_quant_bitexact_exact_rotation(M, K, B):
+    """Integer-valued inputs with an even log2(block): every butterfly sum is
+    an exact small integer and 1/sqrt(B) is a power of two, so the rotated
+    values are exact on both sides and codes, scales and rotated values must
+    agree bit for bit (this exercises the register-first kernel used for
+    blocks of 16 and more)."""
+    X = si.uniform_int4((M, K), seed=K + B + M, lo=-8, hi=8).astype(np.float32)
+    X[0, :3] = 0.0
+    say(f"bitexact exact-rotation M={M} K={K} B={B}")
+    for dt in (torch.float32, torch.bfloat16):
+        qg, sg, xg = gpu_rotate(to_dev(X, dt), B)
+        qo, so, xo32, _ = O.rotate_quant_act(X.astype(np.float64), B)
+        assert np.array_equal(xg.view(np.uint32), xo32.view(np.uint32))
+        assert np.array_equal(sg.view(np.uint32), so.view(np.uint32))
+        assert np.array_equal(qg, qo.astype(np.int64))
+
+
 def test_rotate_rne_ties_and_zero_rows():
     import json, os
     g = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "rne_ties.json")))
