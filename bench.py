@@ -12,7 +12,8 @@ x20. One step = one pass over the whole stack:
 value = algorithmic weight-stream bytes of one pass / step time.
 
 Also measured and reported under "extra": the same stack at M = 4, 8, 16;
-prefill int8-MFMA TOPS at M = 2048 (up_proj, down_proj); the
+prefill int8-MFMA TOPS at M = 2048 (up_proj, down_proj; bfloat16 output,
+and float32 output under the "_f32_out" keys); the
 LLaMA-3.1-8B-shaped power-of-two layer (decode over 32 layer copies, prefill
 at M = 4096); the mixed W2/W4 stack (layers 0-15 MNZ, 16-31 int4) at M = 16;
 KV4 of K and V [4096, 32, 128].
@@ -339,15 +340,20 @@ def measure_extras(q, torch, dev, stack, args):
         del W
         X = si.device_activations(M, K, seed=6, device=dev)
         xq, sa, _ = q.qift_rotate_quant_act(X, B)
-        Y = torch.empty((M, N), dtype=torch.float32, device=dev)
-        med, mn, _ = time_fn(torch, lambda: q.qift_w2a4_linear(xq, sa, cw, sw, "mnz", Y=Y), 30)
-        rmed, _, _ = time_fn(torch, lambda: q.qift_rotate_quant_act(X, B, xq=xq, s_a=sa), 30)
         ops = 2.0 * M * N * K
-        pre[name] = {"M": M, "K": K, "N": N, "gemm_ms": round(med, 4),
-                     "TOPS": round(ops / med / 1e9, 1), "frac_of_int8_peak": round(ops / med / 1e9 / INT8_PEAK_TOPS, 4),
-                     "rotate_quant_ms": round(rmed, 4),
-                     "rotate_quant_GBps": round((M * K * 2 + M * K / 2 + 4 * M) / rmed / 1e6, 1)}
-        del cw, sw, X, xq, sa, Y
+        pre[name] = {"M": M, "K": K, "N": N}
+        # bfloat16 output (the dtype of the layer's input activations) first,
+        # then float32 output for comparison
+        for tag, ydt in (("", torch.bfloat16), ("_f32_out", torch.float32)):
+            Y = torch.empty((M, N), dtype=ydt, device=dev)
+            med, _, _ = time_fn(torch, lambda: q.qift_w2a4_linear(xq, sa, cw, sw, "mnz", Y=Y), 30)
+            pre[name].update({"gemm_ms" + tag: round(med, 4), "TOPS" + tag: round(ops / med / 1e9, 1),
+                              "frac_of_int8_peak" + tag: round(ops / med / 1e9 / INT8_PEAK_TOPS, 4)})
+            del Y
+        rmed, _, _ = time_fn(torch, lambda: q.qift_rotate_quant_act(X, B, xq=xq, s_a=sa), 30)
+        pre[name].update({"rotate_quant_ms": round(rmed, 4),
+                          "rotate_quant_GBps": round((M * K * 2 + M * K / 2 + 4 * M) / rmed / 1e6, 1)})
+        del cw, sw, X, xq, sa
     extra["prefill_llama7b_mnz"] = pre
 
     # LLaMA-3.1-8B-shaped PoT layer: decode over 32 copies; prefill M = 4096
@@ -369,12 +375,15 @@ def measure_extras(q, torch, dev, stack, args):
         del W
         X = si.device_activations(M, K, seed=9, device=dev)
         xq, sa, _ = q.qift_rotate_quant_act(X, B)
-        Y = torch.empty((M, N), dtype=torch.float32, device=dev)
-        med, _, _ = time_fn(torch, lambda: q.qift_w2a4_linear(xq, sa, cw, sw, "pot", Y=Y), 20)
         ops = 2.0 * M * N * K
-        pf[name] = {"M": M, "K": K, "N": N, "gemm_ms": round(med, 4), "TOPS": round(ops / med / 1e9, 1),
-                    "frac_of_int8_peak": round(ops / med / 1e9 / INT8_PEAK_TOPS, 4)}
-        del cw, sw, X, xq, sa, Y
+        pf[name] = {"M": M, "K": K, "N": N}
+        for tag, ydt in (("", torch.bfloat16), ("_f32_out", torch.float32)):
+            Y = torch.empty((M, N), dtype=ydt, device=dev)
+            med, _, _ = time_fn(torch, lambda: q.qift_w2a4_linear(xq, sa, cw, sw, "pot", Y=Y), 20)
+            pf[name].update({"gemm_ms" + tag: round(med, 4), "TOPS" + tag: round(ops / med / 1e9, 1),
+                             "frac_of_int8_peak" + tag: round(ops / med / 1e9 / INT8_PEAK_TOPS, 4)})
+            del Y
+        del cw, sw, X, xq, sa
     pot["prefill_M4096"] = pf
     extra["llama31_8b_pot"] = pot
 

@@ -224,6 +224,8 @@ def qift_w2a4_linear(xq, s_a, codes, scales, levels="mnz", out_dtype=torch.float
     if Y is None:
         Y = torch.empty((M, N), dtype=out_dtype, device=xq.device)
     _dev_tensor(Y, "Y", (torch.float32, torch.bfloat16, torch.int32))
+    if Y.numel() < M * N:
+        raise ValueError("Y too small for [M, N]")
     st = _C.qift_w2a4_linear(_ptr(xq), _ptr(s_a), M, K, _ptr(codes), _ptr(scales),
                              _TORCH_TO_QIFT[scales.dtype], _levels(levels), N, _ptr(Y),
                              _TORCH_TO_QIFT[Y.dtype], _stream(stream, xq.device))

@@ -19,6 +19,8 @@
 //  prefill (M > 16): 128x128 output tiles, 4 waves of 64x64, packed operands
 //    staged through LDS (padded rows, conflict-free 16-byte reads) with the
 //    next K step prefetched into registers while the current one computes.
+#include <type_traits>
+
 #include "qift_internal.h"
 
 namespace qift {
@@ -216,27 +218,13 @@ __global__ __launch_bounds__(256, QIFT_DECODE_MINBLOCKS) void linear_grouped_ker
 // prefill: M > 16
 // ---------------------------------------------------------------------------
 
-// Workgroup = 2 x 2 waves; a wave computes kWaveTM x kWaveTN fragments of
+// General path (K a multiple of 64, tokens staged through registers):
+// workgroup = 2 x 2 waves; a wave computes kWaveTM x kWaveTN fragments of
 // 16 x 16, so the workgroup tile is (32 kWaveTM) tokens x (32 kWaveTN)
 // channels. Larger wave tiles amortize the operand unpacking (about 6 VALU
 // instructions per activation fragment and 7 per weight fragment per MFMA
 // step) over more MFMAs.
-#ifndef QIFT_PREFILL_TM
-#define QIFT_PREFILL_TM 4
-#endif
-#ifndef QIFT_PREFILL_TN
-#define QIFT_PREFILL_TN 4
-#endif
-#ifndef QIFT_PREFILL_DBUF
-#define QIFT_PREFILL_DBUF 0
-#endif
-#ifndef QIFT_PREFILL_DL
-#define QIFT_PREFILL_DL 1
-#endif
-#ifndef QIFT_PREFILL_SCHED
-#define QIFT_PREFILL_SCHED 0
-#endif
-constexpr int kWaveTM = QIFT_PREFILL_TM, kWaveTN = QIFT_PREFILL_TN;
+constexpr int kWaveTM = 4, kWaveTN = 4;
 constexpr int kBM = 32 * kWaveTM, kBN = 32 * kWaveTN;
 
 template <int LV>
@@ -251,10 +239,10 @@ struct PrefillCfg {
   static constexpr int kALoads = kBM * kAUnits / 256;     // 16-byte loads per thread
   // weights: one 1 KB tiled chunk per 16-channel tile, copied verbatim
   static constexpr int kBLoads = (kBN / 16) * 64 / 256;
-  // one stage = A tile then B tile; two stages back to back
+  // one stage = A tile then B tile
   static constexpr int kBOffset = (kBM * kAStride + 15) / 16 * 16;
   static constexpr int kStage = kBOffset + (kBN / 16) * 1024;
-  static constexpr int kLds = 2 * kStage;
+  static constexpr int kLds = kStage;
   static_assert(kALoads * 256 == kBM * kAUnits, "A tile load split");
   static_assert(kBLoads * 256 == (kBN / 16) * 64, "B tile load split");
 };
@@ -348,36 +336,10 @@ __device__ __forceinline__ void prefill_tile(const qift_linear_desc& d, int64_t 
 #pragma unroll
         for (int i = 0; i < kWaveTM; ++i) acc[i][j] = mfma16(A[i], B, acc[i][j]);
       }
-#if QIFT_PREFILL_SCHED
-      // interleave: each MFMA followed by up to 2 VALU instructions
-#pragma unroll
-      for (int k = 0; k < kWaveTM * kWaveTN; ++k) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-        __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);  // VALU
-      }
-#endif
     }
   };
 
   const int64_t nstages = (K + C::kBK - 1) / C::kBK;
-#if QIFT_PREFILL_DBUF
-  // two LDS stages: stage st is computed from buffer st % 2 while the loads
-  // of stage st + 1 (already in registers) go to the other buffer; one
-  // barrier per stage.
-  gload(0);
-  lstore(0);
-  if (nstages > 1) gload(C::kBK);
-  __syncthreads();
-  for (int64_t st = 0; st < nstages; ++st) {
-    const int buf = (int)(st & 1);
-    compute(buf);
-    if (st + 1 < nstages) {
-      lstore(buf ^ 1);
-      if (st + 2 < nstages) gload((st + 2) * C::kBK);
-    }
-    __syncthreads();
-  }
-#else
   // one LDS stage; the next stage's global loads are in flight in registers
   // while the current stage computes
   gload(0);
@@ -388,7 +350,6 @@ __device__ __forceinline__ void prefill_tile(const qift_linear_desc& d, int64_t 
     if (st + 1 < nstages) gload((st + 1) * C::kBK);
     compute(0);
   }
-#endif
 
   const float kappa = level_kappa(LV);
 #pragma unroll
@@ -413,18 +374,25 @@ __device__ __forceinline__ void prefill_tile(const qift_linear_desc& d, int64_t 
 // ---------------------------------------------------------------------------
 // prefill, direct-to-LDS path (K a multiple of 256)
 //
-// Stages of 256 features, double-buffered in LDS and filled with gfx950's
-// global_load_lds_dwordx4 (each lane's 16 bytes land at base + 16 * lane), so
-// the next stage streams in while the current one computes, with one barrier
-// per stage and no staging registers. Activation rows (128 bytes per stage)
-// are stored unpadded with an XOR swizzle: 16-byte unit c of row r sits in
-// slot c ^ (r % 8), which makes the 16-byte fragment reads of 8 consecutive
-// rows hit 8 different bank groups. Weight tiles are copied verbatim (their
-// tiled layout is already lane order).
+// Workgroup tile 128 tokens x 128 channels. Stages of 256 features are
+// double-buffered in LDS and filled with gfx950's global_load_lds_dwordx4
+// (each lane's 16 bytes land at base + 16 * lane), so the next stage streams
+// in while the current one computes, with one barrier per stage and no
+// staging registers. Activation rows (128 bytes per stage) are stored
+// unpadded with an XOR swizzle (slot of 16-byte unit c in row r is
+// c ^ ((r / 2) % 8)); weight tiles are copied verbatim, their tiled layout
+// already being lane order.
+//
+// Split K inside the workgroup: each wave sums a 128 x 64 block over half of
+// every stage's features (waves 0, 1: one half; waves 2, 3: the other). A
+// weight operand is then unpacked once per workgroup and reused by 8 MFMAs,
+// an activation operand twice and reused by 4: about 2.5 VALU instructions per
+// MFMA for the 2-bit formats against 3.3 for 2 x 2 waves of 64 x 64 blocks.
+// The two waves of a column block finally swap halves of their partial sums
+// through LDS, so that each wave adds up and stores one 64 x 64 block.
 // ---------------------------------------------------------------------------
 
-constexpr int kDlBM = 128, kDlBN = 128;  // workgroup tile; 2 x 2 waves of 64 x 64
-constexpr int kDlTM = 4, kDlTN = 4;
+constexpr int kDlBM = 128, kDlBN = 128;  // workgroup tile
 
 template <int LV>
 struct DlCfg {
@@ -446,38 +414,151 @@ __device__ __forceinline__ void gl_lds16(const void* g, uint8_t* lds_wave_base) 
   __builtin_amdgcn_global_load_lds(g, (lds_void*)lds_wave_base, 16, 0, 0);
 }
 
+// Epilogue of a wave's 64 x 64 block. The accumulators sit in MFMA output
+// order (a lane holds 4 rows of one column per 16 x 16 tile), which would make
+// every global store a 4-row scatter of 4-byte pieces. The block is instead
+// staged through a wave-private LDS region, 32 rows at a time, as int32 rows
+// padded to 68 words, and read back row-major so that each lane owns 4 (float32,
+// int32) or 8 (bfloat16) consecutive columns of one row and stores them as one
+// 16-byte piece; the scales are applied after the transpose, one activation
+// scale per row and the lane's channel scales once.
+constexpr int kEpiStride = 68;                        // words per staged row
+constexpr int kEpiWaveBytes = 32 * kEpiStride * 4;    // 8704 B per wave
+
+// The output type and the accumulator rows (I0 .. I0 + 3 of an accumulator
+// array of NI rows) are fixed at compile time, so that the row loop unrolls
+// and no register is selected at run time.
+template <int LV, int YD, int NI, int I0>
+__device__ __forceinline__ void epilogue_blk(const qift_linear_desc& d, const v4i (&acc)[NI][4],
+                                             int64_t mb, int64_t nb, int scale_f16,
+                                             uint8_t* lds_w, int lane) {
+  using F = Fmt<LV>;
+  constexpr bool kBf = YD == QIFT_BF16;
+  constexpr int kCpl = kBf ? 8 : 4;     // columns per lane
+  constexpr int kLpr = 64 / kCpl;       // lanes per staged row
+  constexpr int kRstep = 64 / kLpr;     // rows covered by one read of the wave
+  int* st = reinterpret_cast<int*>(lds_w);
+  const int r16 = lane & 15, g = lane >> 4;
+  const int64_t M = d.M, N = d.N;
+  const int c0 = (lane % kLpr) * kCpl;
+  const int rsub = lane / kLpr;
+  const int64_t n = nb + c0;
+  float sw[kCpl];
+  if constexpr (YD != QIFT_I32) {
+    const float kappa = level_kappa(LV);
+#pragma unroll
+    for (int e = 0; e < kCpl; ++e)
+      sw[e] = n + e < N ? load_scale(d.scales, n + e, scale_f16) * kappa : 0.f;
+  }
+  const bool vec = (N % kCpl) == 0 && n + kCpl <= N &&
+                   (reinterpret_cast<uintptr_t>(d.Y) & 15) == 0;
+#pragma unroll
+  for (int p = 0; p < 2; ++p) {
+#pragma unroll
+    for (int ii = 0; ii < 2; ++ii)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          st[(16 * ii + 4 * g + r) * kEpiStride + 16 * j + r16] =
+              acc[I0 + 2 * p + ii][j][r] >> F::kShift;
+    // one wave writes and reads its own region: its LDS operations complete in order
+#pragma unroll
+    for (int tr = 0; tr < 32 / kRstep; ++tr) {
+      const int row = rsub + kRstep * tr;
+      const int64_t m = mb + 32 * p + row;
+      int v[kCpl];
+#pragma unroll
+      for (int q = 0; q < kCpl; q += 4)
+        *reinterpret_cast<int4*>(&v[q]) =
+            *reinterpret_cast<const int4*>(&st[row * kEpiStride + c0 + q]);
+      if (m >= M) continue;
+      const int64_t o = m * N + n;
+      if constexpr (YD == QIFT_I32) {
+        int* y = reinterpret_cast<int*>(d.Y) + o;
+        if (vec) {
+          *reinterpret_cast<int4*>(y) = int4{v[0], v[1], v[2], v[3]};
+        } else {
+          for (int e = 0; e < 4; ++e)
+            if (n + e < N) y[e] = v[e];
+        }
+      } else {
+        const float sa = d.s_a[m];
+        float y[kCpl];
+#pragma unroll
+        for (int e = 0; e < kCpl; ++e) y[e] = (float)v[e] * (sa * sw[e]);
+        if constexpr (kBf) {
+          uint16_t* yo = reinterpret_cast<uint16_t*>(d.Y) + o;
+          if (vec) {
+            uint32_t w[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              w[e] = (uint32_t)float_to_bf16_bits(y[2 * e]) |
+                     ((uint32_t)float_to_bf16_bits(y[2 * e + 1]) << 16);
+            *reinterpret_cast<uint4*>(yo) = uint4{w[0], w[1], w[2], w[3]};
+          } else {
+            for (int e = 0; e < 8; ++e)
+              if (n + e < N) yo[e] = float_to_bf16_bits(y[e]);
+          }
+        } else {
+          float* yo = reinterpret_cast<float*>(d.Y) + o;
+          if (vec) {
+            *reinterpret_cast<float4*>(yo) = float4{y[0], y[1], y[2], y[3]};
+          } else {
+            for (int e = 0; e < 4; ++e)
+              if (n + e < N) yo[e] = y[e];
+          }
+        }
+      }
+    }
+  }
+}
+
+template <int LV, int NI, int I0>
+__device__ __forceinline__ void epilogue_any(const qift_linear_desc& d, const v4i (&acc)[NI][4],
+                                             int64_t mb, int64_t nb, int scale_f16, int y_dtype,
+                                             uint8_t* lds_w, int lane) {
+  if (y_dtype == QIFT_BF16)
+    epilogue_blk<LV, QIFT_BF16, NI, I0>(d, acc, mb, nb, scale_f16, lds_w, lane);
+  else if (y_dtype == QIFT_I32)
+    epilogue_blk<LV, QIFT_I32, NI, I0>(d, acc, mb, nb, scale_f16, lds_w, lane);
+  else
+    epilogue_blk<LV, QIFT_F32, NI, I0>(d, acc, mb, nb, scale_f16, lds_w, lane);
+}
+
+// A-tile slot of 16-byte unit c in row r: rows r and r + 1 share a swizzle
+// so that the 16 rows read by one 16-lane phase of a 16-byte LDS read land in
+// 16 different 16-byte bank groups (the row pitch is 128 B, two rows per
+// 256-byte bank line).
+__device__ __forceinline__ int sk_slot(int c, int row) { return c ^ ((row >> 1) & 7); }
+
 template <int LV>
-__device__ __forceinline__ void prefill_tile_dl(const qift_linear_desc& d, int64_t m0,
+__device__ __forceinline__ void prefill_tile_sk(const qift_linear_desc& d, int64_t m0,
                                                 int64_t nt0, int scale_f16, int y_dtype,
                                                 uint8_t* lds) {
   using C = DlCfg<LV>;
-  using F = Fmt<LV>;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int r16 = lane & 15;
   const int g = lane >> 4;
-  const int wm = (wave >> 1) * 64;
-  const int wn = (wave & 1) * 64;
+  const int kh = wave >> 1;              // which half of each stage's features
+  const int wn = (wave & 1) * 64;        // the wave's 64 channels in the tile
   const int64_t M = d.M, K = d.K, N = d.N;
-  const int64_t cw = F::code_words(K);
+  const int64_t cw = Fmt<LV>::code_words(K);
   const int64_t arow = K / 2;
-  const int64_t np16 = (N + 15) >> 4;     // 16-channel tiles in the weight buffer
+  const int64_t np16 = (N + 15) >> 4;
   const MnzMasks km = mnz_masks(d.reserved, lane);
 
-  // per-lane source offsets that do not change between stages
-  // A: wave instruction p covers rows 8 (4 wave + p) .. +7; lane -> row
-  // 8(...) + lane / 8, slot lane % 8, global unit slot ^ (row % 8)
   int64_t a_off[C::kAInstr];
 #pragma unroll
   for (int p = 0; p < C::kAInstr; ++p) {
     const int row = 8 * (wave * C::kAInstr + p) + (lane >> 3);
     int64_t m = m0 + row;
     m = m < M ? m : M - 1;                // rows past M only feed discarded outputs
-    const int c = (lane & 7) ^ (row & 7);
+    const int c = sk_slot(lane & 7, row);
     a_off[p] = m * arow + 16 * c;
   }
-  // B: unit u = (wave * kBInstr + p) * 64 + lane = (tile, chunk) * 64 + lane
   int64_t b_off[C::kBInstr];
 #pragma unroll
   for (int p = 0; p < C::kBInstr; ++p) {
@@ -498,54 +579,57 @@ __device__ __forceinline__ void prefill_tile_dl(const qift_linear_desc& d, int64
       gl_lds16(d.codes + b_off[p] + st * C::kBChunks * 256, bs + (wave * C::kBInstr + p) * 1024);
   };
 
-  v4i acc[kDlTM][kDlTN];
+  v4i acc[8][4];
 #pragma unroll
-  for (int i = 0; i < kDlTM; ++i)
+  for (int i = 0; i < 8; ++i)
 #pragma unroll
-    for (int j = 0; j < kDlTN; ++j) acc[i][j] = v4i{0, 0, 0, 0};
+    for (int j = 0; j < 4; ++j) acc[i][j] = v4i{0, 0, 0, 0};
 
-  auto compute = [&](int buf) {
+  // int4 weights: the lane's 16-byte unit of chunk kh (32 features, two
+  // steps); 2-bit weights: words 2 kh, 2 kh + 1 of the lane's 16-byte unit.
+  using BFrag = typename std::conditional<C::kInt4, uint4, uint2>::type;
+  struct Frag {
+    uint4 a[8];
+    BFrag b[4];
+  };
+  // reads all of a stage's fragments before the next stage's loads are
+  // issued (the compiler would otherwise wait for those loads first)
+  auto fetch = [&](int buf, Frag& f) {
     const uint8_t* as = lds + buf * C::kStage;
     const uint8_t* bs = as + C::kABytes;
-    uint4 fb[kDlTN];  // 2-bit: one unit covers the whole stage; int4: reloaded per half
+    const int c = C::kInt4 ? 4 * kh + g : 2 * g + kh;
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      // A: 16 bytes = 32 features per fragment for two MFMA steps
-      uint4 fa[kDlTM];
+    for (int i = 0; i < 8; ++i) {
+      const int row = 16 * ((i + 4 * kh) & 7) + r16;   // accumulator i <- row block i + 4 kh
+      f.a[i] = *reinterpret_cast<const uint4*>(as + row * 128 + 16 * sk_slot(c, row));
+    }
 #pragma unroll
-      for (int i = 0; i < kDlTM; ++i) {
-        const int row = wm + 16 * i + r16;
-        const int c = C::kInt4 ? 4 * h + g : 2 * g + h;
-        fa[i] = *reinterpret_cast<const uint4*>(as + row * 128 + 16 * (c ^ (row & 7)));
+    for (int j = 0; j < 4; ++j) {
+      const int tile = (wn >> 4) + j;
+      if constexpr (C::kInt4)
+        f.b[j] = *reinterpret_cast<const uint4*>(bs + (tile * 2 + kh) * 1024 + 16 * lane);
+      else
+        f.b[j] = *reinterpret_cast<const uint2*>(bs + tile * 1024 + 16 * lane + 8 * kh);
+    }
+  };
+  auto mma = [&](const Frag& f) {
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2) {
+      v4i B[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if constexpr (C::kInt4)
+          B[j] = s2 == 0 ? int4_operand(f.b[j].x, f.b[j].y) : int4_operand(f.b[j].z, f.b[j].w);
+        else if constexpr (LV == QIFT_LEVELS_MNZ)
+          B[j] = mnz_operand(s2 == 0 ? f.b[j].x : f.b[j].y, km);
+        else
+          B[j] = pot_operand(s2 == 0 ? f.b[j].x : f.b[j].y);
       }
-      // B: the lane's 16-byte unit of each fragment's tile (chunk h for int4)
 #pragma unroll
-      for (int j = 0; j < kDlTN; ++j) {
-        const int tile = (wn >> 4) + j;
-        const int blk = C::kInt4 ? tile * 2 + h : tile;
-        if (C::kInt4 || h == 0)
-          fb[j] = *reinterpret_cast<const uint4*>(bs + blk * 1024 + 16 * lane);
-      }
+      for (int i = 0; i < 8; ++i) {
+        const v4i A = s2 == 0 ? int4_operand(f.a[i].x, f.a[i].y) : int4_operand(f.a[i].z, f.a[i].w);
 #pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2) {
-        v4i A[kDlTM];
-#pragma unroll
-        for (int i = 0; i < kDlTM; ++i)
-          A[i] = s2 == 0 ? int4_operand(fa[i].x, fa[i].y) : int4_operand(fa[i].z, fa[i].w);
-        const int wstep = C::kInt4 ? s2 : 2 * h + s2;   // step inside the 16-byte B unit
-#pragma unroll
-        for (int j = 0; j < kDlTN; ++j) {
-          const v4i B = weight_operand<LV>(fb[j], wstep, km);
-#pragma unroll
-          for (int i = 0; i < kDlTM; ++i) acc[i][j] = mfma16(A[i], B, acc[i][j]);
-        }
-#if QIFT_PREFILL_SCHED
-#pragma unroll
-        for (int k = 0; k < kDlTM * kDlTN; ++k) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-          __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);  // VALU
-        }
-#endif
+        for (int j = 0; j < 4; ++j) acc[i][j] = mfma16(A, B[j], acc[i][j]);
       }
     }
   };
@@ -555,28 +639,43 @@ __device__ __forceinline__ void prefill_tile_dl(const qift_linear_desc& d, int64
   for (int64_t st = 0; st < nstages; ++st) {
     __builtin_amdgcn_s_waitcnt(0);   // this wave's loads of stage st have landed
     __syncthreads();                 // ... everyone's; and stage st-1 is consumed
+    Frag f;
+    fetch((int)(st & 1), f);
     if (st + 1 < nstages) issue(st + 1, (int)((st + 1) & 1));
-    compute((int)(st & 1));
+    mma(f);
   }
 
-  const float kappa = level_kappa(LV);
+  // Swap halves with the partner wave (same channels, other feature half).
+  // Accumulator i of wave kh holds row block (i + 4 kh) mod 8, so every wave
+  // keeps accumulators 0..3 (rows 64 kh .. 64 kh + 63) and sends 4..7, which
+  // are exactly the partner's kept rows; two rounds of 32 rows (8 KB per wave).
+  static_assert(4 * 8 * 64 * 16 <= C::kLds, "partial-sum exchange fits in the stage buffers");
+  static_assert(4 * kEpiWaveBytes <= C::kLds, "epilogue staging fits in the stage buffers");
+  int4* ex = reinterpret_cast<int4*>(lds);
+  const int partner = wave ^ 2;
+  __syncthreads();  // every wave is done reading the stage buffers
 #pragma unroll
-  for (int j = 0; j < kDlTN; ++j) {
-    const int64_t n = nt0 + wn + 16 * j + r16;
-    if (n >= N) continue;
-    const float sw = load_scale(d.scales, n, scale_f16) * kappa;
+  for (int sp = 0; sp < 2; ++sp) {
 #pragma unroll
-    for (int i = 0; i < kDlTM; ++i) {
+    for (int ii = 0; ii < 2; ++ii)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int64_t m = m0 + wm + 16 * i + 4 * g + r;
-        if (m < M) {
-          const int a = acc[i][j][r] >> F::kShift;
-          store_y(d.Y, y_dtype, m * N + n, a, d.s_a[m] * sw);
-        }
+      for (int j = 0; j < 4; ++j) {
+        const v4i v = acc[4 + 2 * sp + ii][j];
+        ex[(wave * 8 + ii * 4 + j) * 64 + lane] = int4{v[0], v[1], v[2], v[3]};
       }
-    }
+    __syncthreads();
+#pragma unroll
+    for (int ii = 0; ii < 2; ++ii)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int4 r = ex[(partner * 8 + ii * 4 + j) * 64 + lane];
+        v4i& a = acc[2 * sp + ii][j];
+        a = v4i{a[0] + r.x, a[1] + r.y, a[2] + r.z, a[3] + r.w};
+      }
+    __syncthreads();
   }
+  epilogue_any<LV, 8, 0>(d, acc, m0 + 64 * kh, nt0 + wn, scale_f16, y_dtype,
+                         lds + wave * kEpiWaveBytes, lane);
 }
 
 // Tile order: with T tiles and T % 8 == 0, consecutive workgroups (which the
@@ -595,13 +694,13 @@ __device__ __forceinline__ void dl_tile_of(int64_t b, int64_t nM, int64_t nN, in
 // two workgroups per CU (<= 256 registers per lane) so that each SIMD has a
 // second wave to switch to while one waits on LDS or a barrier
 template <int LV>
-__global__ __launch_bounds__(256, QIFT_PREFILL_MINBLOCKS) void linear_prefill_dl_kernel(qift_linear_desc d, int scale_f16,
-                                                                int y_dtype) {
+__global__ __launch_bounds__(256, QIFT_PREFILL_MINBLOCKS) void linear_prefill_sk_kernel(
+    qift_linear_desc d, int scale_f16, int y_dtype) {
   __shared__ __attribute__((aligned(1024))) uint8_t lds[DlCfg<LV>::kLds];
   const int64_t nM = (d.M + kDlBM - 1) / kDlBM, nN = (d.N + kDlBN - 1) / kDlBN;
   int64_t tm, tn;
   dl_tile_of(blockIdx.x, nM, nN, &tm, &tn);
-  prefill_tile_dl<LV>(d, tm * kDlBM, tn * kDlBN, scale_f16, y_dtype, lds);
+  prefill_tile_sk<LV>(d, tm * kDlBM, tn * kDlBN, scale_f16, y_dtype, lds);
 }
 
 template <int LV>
@@ -627,26 +726,24 @@ hipError_t launch_linear_decode(const qift_linear_desc& d, int scale_f16, int y_
 
 hipError_t launch_linear_prefill(const qift_linear_desc& d, int scale_f16, int y_dtype,
                                  hipStream_t s) {
-#if QIFT_PREFILL_DL
   if (d.K % 256 == 0) {
     const dim3 g1((unsigned)(((d.N + kDlBN - 1) / kDlBN) * ((d.M + kDlBM - 1) / kDlBM)));
     switch (d.levels) {
       case QIFT_LEVELS_MNZ:
-        hipLaunchKernelGGL(linear_prefill_dl_kernel<QIFT_LEVELS_MNZ>, g1, dim3(256), 0, s, d,
+        hipLaunchKernelGGL(linear_prefill_sk_kernel<QIFT_LEVELS_MNZ>, g1, dim3(256), 0, s, d,
                            scale_f16, y_dtype);
         break;
       case QIFT_LEVELS_POT:
-        hipLaunchKernelGGL(linear_prefill_dl_kernel<QIFT_LEVELS_POT>, g1, dim3(256), 0, s, d,
+        hipLaunchKernelGGL(linear_prefill_sk_kernel<QIFT_LEVELS_POT>, g1, dim3(256), 0, s, d,
                            scale_f16, y_dtype);
         break;
       default:
-        hipLaunchKernelGGL(linear_prefill_dl_kernel<QIFT_LEVELS_INT4>, g1, dim3(256), 0, s, d,
+        hipLaunchKernelGGL(linear_prefill_sk_kernel<QIFT_LEVELS_INT4>, g1, dim3(256), 0, s, d,
                            scale_f16, y_dtype);
         break;
     }
     return hipGetLastError();
   }
-#endif
   const dim3 grid((unsigned)((d.N + kBN - 1) / kBN), (unsigned)((d.M + kBM - 1) / kBM));
   switch (d.levels) {
     case QIFT_LEVELS_MNZ:

@@ -216,7 +216,8 @@ def test_linear_int32_bitexact(kind, M, K, N):
 
 
 @pytest.mark.parametrize("kind", ["mnz", "pot", "int4"])
-@pytest.mark.parametrize("M,K,N", [(1, 256, 33), (16, 512, 100), (40, 1024, 150)])
+@pytest.mark.parametrize("M,K,N", [(1, 256, 33), (16, 512, 100), (40, 1024, 150), (48, 512, 256),
+                                   (130, 768, 136), (33, 256, 1000)])
 def test_linear_float_epilogue(kind, M, K, N):
     qa, codes, s_a, s_w = random_linear_inputs(M, K, N, kind, seed=5 + M + N)
     say(f"linear f32/bf16 {kind} M={M} K={K} N={N}")
@@ -225,6 +226,25 @@ def test_linear_float_epilogue(kind, M, K, N):
     assert np.all(np.abs(Yf - y) <= 4e-7 * np.abs(y) + 1e-30)
     Yb = run_linear(qa, codes, s_a, s_w, kind, torch.bfloat16).float().cpu().numpy()
     assert np.all(np.abs(Yb - y) <= 2 ** -8 * np.abs(y) + 1e-30)
+
+
+@pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16, torch.int32])
+def test_linear_unaligned_output(out_dtype):
+    """An output view that starts one element into its buffer (not 16-byte
+    aligned) is written element by element, with the same values."""
+    M, K, N = 40, 512, 256
+    qa, codes, s_a, s_w = random_linear_inputs(M, K, N, "mnz", seed=77)
+    say(f"linear unaligned output {out_dtype}")
+    ref = run_linear(qa, codes, s_a, s_w, "mnz", out_dtype)
+    xq = torch.from_numpy(O.pack_int4(qa)).to(DEV)
+    cw = u32_to_dev(O.pack_weights(codes, "mnz"))
+    buf = torch.full((M * N + 1,), 3, dtype=out_dtype, device=DEV)
+    Y = buf[1:].view(M, N)
+    q.qift_w2a4_linear(xq, to_dev(s_a), cw, to_dev(s_w.astype(np.float32), torch.float16), "mnz",
+                       out_dtype, Y=Y)
+    sync()
+    assert torch.equal(Y, ref)
+    assert buf[0].item() == 3
 
 
 def test_linear_extremes_do_not_overflow():
