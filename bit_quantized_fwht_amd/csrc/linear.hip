@@ -420,8 +420,9 @@ __device__ __forceinline__ void gl_lds16(const void* g, uint8_t* lds_wave_base) 
 // staged through a wave-private LDS region, 32 rows at a time, as int32 rows
 // padded to 68 words, and read back row-major so that each lane owns 4 (float32,
 // int32) or 8 (bfloat16) consecutive columns of one row and stores them as one
-// 16-byte piece; the scales are applied after the transpose, one activation
-// scale per row and the lane's channel scales once.
+// 16-byte piece; the scales are applied after the transpose, from LDS tables
+// of the tile's activation scales (sa_t, by row) and channel scales times
+// kappa (sw_t, by column) that were fetched when the tile started.
 constexpr int kEpiStride = 68;                        // words per staged row
 constexpr int kEpiWaveBytes = 32 * kEpiStride * 4;    // 8704 B per wave
 
@@ -430,8 +431,8 @@ constexpr int kEpiWaveBytes = 32 * kEpiStride * 4;    // 8704 B per wave
 // and no register is selected at run time.
 template <int LV, int YD, int NI, int I0>
 __device__ __forceinline__ void epilogue_blk(const qift_linear_desc& d, const v4i (&acc)[NI][4],
-                                             int64_t mb, int64_t nb, int scale_f16,
-                                             uint8_t* lds_w, int lane) {
+                                             int64_t mb, int64_t nb, const float* sa_t,
+                                             const float* sw_t, uint8_t* lds_w, int lane) {
   using F = Fmt<LV>;
   constexpr bool kBf = YD == QIFT_BF16;
   constexpr int kCpl = kBf ? 8 : 4;     // columns per lane
@@ -445,10 +446,8 @@ __device__ __forceinline__ void epilogue_blk(const qift_linear_desc& d, const v4
   const int64_t n = nb + c0;
   float sw[kCpl];
   if constexpr (YD != QIFT_I32) {
-    const float kappa = level_kappa(LV);
 #pragma unroll
-    for (int e = 0; e < kCpl; ++e)
-      sw[e] = n + e < N ? load_scale(d.scales, n + e, scale_f16) * kappa : 0.f;
+    for (int e = 0; e < kCpl; ++e) sw[e] = sw_t[c0 + e];
   }
   const bool vec = (N % kCpl) == 0 && n + kCpl <= N &&
                    (reinterpret_cast<uintptr_t>(d.Y) & 15) == 0;
@@ -483,7 +482,7 @@ __device__ __forceinline__ void epilogue_blk(const qift_linear_desc& d, const v4
             if (n + e < N) y[e] = v[e];
         }
       } else {
-        const float sa = d.s_a[m];
+        const float sa = sa_t[32 * p + row];
         float y[kCpl];
 #pragma unroll
         for (int e = 0; e < kCpl; ++e) y[e] = (float)v[e] * (sa * sw[e]);
@@ -516,14 +515,15 @@ __device__ __forceinline__ void epilogue_blk(const qift_linear_desc& d, const v4
 
 template <int LV, int NI, int I0>
 __device__ __forceinline__ void epilogue_any(const qift_linear_desc& d, const v4i (&acc)[NI][4],
-                                             int64_t mb, int64_t nb, int scale_f16, int y_dtype,
-                                             uint8_t* lds_w, int lane) {
+                                             int64_t mb, int64_t nb, const float* sa_t,
+                                             const float* sw_t, int y_dtype, uint8_t* lds_w,
+                                             int lane) {
   if (y_dtype == QIFT_BF16)
-    epilogue_blk<LV, QIFT_BF16, NI, I0>(d, acc, mb, nb, scale_f16, lds_w, lane);
+    epilogue_blk<LV, QIFT_BF16, NI, I0>(d, acc, mb, nb, sa_t, sw_t, lds_w, lane);
   else if (y_dtype == QIFT_I32)
-    epilogue_blk<LV, QIFT_I32, NI, I0>(d, acc, mb, nb, scale_f16, lds_w, lane);
+    epilogue_blk<LV, QIFT_I32, NI, I0>(d, acc, mb, nb, sa_t, sw_t, lds_w, lane);
   else
-    epilogue_blk<LV, QIFT_F32, NI, I0>(d, acc, mb, nb, scale_f16, lds_w, lane);
+    epilogue_blk<LV, QIFT_F32, NI, I0>(d, acc, mb, nb, sa_t, sw_t, lds_w, lane);
 }
 
 // A-tile slot of 16-byte unit c in row r: rows r and r + 1 share a swizzle
@@ -535,7 +535,7 @@ __device__ __forceinline__ int sk_slot(int c, int row) { return c ^ ((row >> 1) 
 template <int LV>
 __device__ __forceinline__ void prefill_tile_sk(const qift_linear_desc& d, int64_t m0,
                                                 int64_t nt0, int scale_f16, int y_dtype,
-                                                uint8_t* lds) {
+                                                uint8_t* lds, float* scl) {
   using C = DlCfg<LV>;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -634,6 +634,18 @@ __device__ __forceinline__ void prefill_tile_sk(const qift_linear_desc& d, int64
     }
   };
 
+  // the epilogue's scales, fetched now so that their latency is hidden by the
+  // main loop: thread t < 128 holds the activation scale of row t of the
+  // tile, thread 128 + c the channel scale (times kappa) of column c
+  float pre_scale;
+  {
+    const int64_t m = m0 + tid, n = nt0 + (tid - 128);
+    if (tid < 128)
+      pre_scale = m < M ? d.s_a[m] : 0.f;
+    else
+      pre_scale = n < N ? load_scale(d.scales, n, scale_f16) * level_kappa(LV) : 0.f;
+  }
+
   const int64_t nstages = K / C::kStageK;
   issue(0, 0);
   for (int64_t st = 0; st < nstages; ++st) {
@@ -644,6 +656,7 @@ __device__ __forceinline__ void prefill_tile_sk(const qift_linear_desc& d, int64
     if (st + 1 < nstages) issue(st + 1, (int)((st + 1) & 1));
     mma(f);
   }
+  scl[tid] = pre_scale;              // read after the exchange's barriers
 
   // Swap halves with the partner wave (same channels, other feature half).
   // Accumulator i of wave kh holds row block (i + 4 kh) mod 8, so every wave
@@ -674,7 +687,7 @@ __device__ __forceinline__ void prefill_tile_sk(const qift_linear_desc& d, int64
       }
     __syncthreads();
   }
-  epilogue_any<LV, 8, 0>(d, acc, m0 + 64 * kh, nt0 + wn, scale_f16, y_dtype,
+  epilogue_any<LV, 8, 0>(d, acc, m0 + 64 * kh, nt0 + wn, scl + 64 * kh, scl + 128 + wn, y_dtype,
                          lds + wave * kEpiWaveBytes, lane);
 }
 
@@ -697,10 +710,11 @@ template <int LV>
 __global__ __launch_bounds__(256, QIFT_PREFILL_MINBLOCKS) void linear_prefill_sk_kernel(
     qift_linear_desc d, int scale_f16, int y_dtype) {
   __shared__ __attribute__((aligned(1024))) uint8_t lds[DlCfg<LV>::kLds];
+  __shared__ float scl[kDlBM + kDlBN];
   const int64_t nM = (d.M + kDlBM - 1) / kDlBM, nN = (d.N + kDlBN - 1) / kDlBN;
   int64_t tm, tn;
   dl_tile_of(blockIdx.x, nM, nN, &tm, &tn);
-  prefill_tile_sk<LV>(d, tm * kDlBM, tn * kDlBN, scale_f16, y_dtype, lds);
+  prefill_tile_sk<LV>(d, tm * kDlBM, tn * kDlBN, scale_f16, y_dtype, lds, scl);
 }
 
 template <int LV>
