@@ -39,6 +39,15 @@ class QiftUnavailable(ImportError):
     pass
 
 
+class qift_rotate_desc(ctypes.Structure):
+    _fields_ = [("X", ctypes.c_void_p), ("x_dtype", ctypes.c_int32), ("had_block", ctypes.c_int32),
+                ("M", ctypes.c_int64), ("K", ctypes.c_int64), ("xq", ctypes.c_void_p),
+                ("s_a", ctypes.c_void_p), ("x_rot", ctypes.c_void_p)]
+
+
+QIFT_MAX_ROTATE_BATCH = 8
+
+
 class qift_linear_desc(ctypes.Structure):
     _fields_ = [("xq", ctypes.c_void_p), ("s_a", ctypes.c_void_p), ("codes", ctypes.c_void_p),
                 ("scales", ctypes.c_void_p), ("Y", ctypes.c_void_p), ("M", ctypes.c_int64),
@@ -61,6 +70,7 @@ def _load():
         "qift_linear_group_prepare": [vp, i32, c_st, c_st, vp, ctypes.c_size_t,
                                       ctypes.POINTER(ctypes.c_int64), vp],
         "qift_w2a4_linear_grouped": [vp, i64, vp],
+        "qift_rotate_quant_act_batched": [vp, i32, vp],
     }
     for name, args in sig.items():
         f = getattr(lib, name)
@@ -196,14 +206,81 @@ def qift_rotate_quant_act(X, had_block: int, xq=None, s_a=None, x_rot=None, want
         s_a = torch.empty((M,), dtype=torch.float32, device=X.device)
     if x_rot is None and want_x_rot:
         x_rot = torch.empty((M, K), dtype=torch.float32, device=X.device)
-    _dev_tensor(xq, "xq", (torch.uint8,))
-    _dev_tensor(s_a, "s_a", (torch.float32,))
-    if x_rot is not None:
-        _dev_tensor(x_rot, "x_rot", (torch.float32,))
+    _check_rotate_buffers(M, K, xq, s_a, x_rot)
     st = _C.qift_rotate_quant_act(_ptr(X), _TORCH_TO_QIFT[X.dtype], M, K, had_block, _ptr(xq),
                                   _ptr(s_a), _ptr(x_rot), _stream(stream, X.device))
     _check(st, "qift_rotate_quant_act")
     return xq, s_a, x_rot
+
+
+def _check_rotate_buffers(M, K, xq, s_a, x_rot):
+    _dev_tensor(xq, "xq", (torch.uint8,))
+    _dev_tensor(s_a, "s_a", (torch.float32,))
+    if x_rot is not None:
+        _dev_tensor(x_rot, "x_rot", (torch.float32,))
+    if xq.numel() < M * (K // 2) or s_a.numel() < M or (x_rot is not None and x_rot.numel() < M * K):
+        raise ValueError("xq, s_a or x_rot too small for [M, K]")
+
+
+class RotateBatch:
+    """A fixed set of qift_rotate_quant_act_batched descriptors (inputs and
+    output buffers given once); run() enqueues the one call."""
+
+    def __init__(self, items):
+        items = list(items)
+        if not 0 < len(items) <= QIFT_MAX_ROTATE_BATCH:
+            raise ValueError(f"1..{QIFT_MAX_ROTATE_BATCH} matrices per batch")
+        self._descs = (qift_rotate_desc * len(items))()
+        self._keep = []
+        for j, it in enumerate(items):
+            X, had_block, xq, s_a = it[0], it[1], it[2], it[3]
+            x_rot = it[4] if len(it) > 4 else None
+            _dev_tensor(X, "X", (torch.float32, torch.bfloat16))
+            M, K = X.shape
+            _check_rotate_buffers(M, K, xq, s_a, x_rot)
+            self._descs[j] = qift_rotate_desc(_ptr(X), _TORCH_TO_QIFT[X.dtype], had_block, M, K,
+                                              _ptr(xq), _ptr(s_a), _ptr(x_rot))
+            self._keep.append((X, xq, s_a, x_rot))
+        self.device = items[0][0].device
+        self.count = len(items)
+
+    def run(self, stream=None):
+        st = _C.qift_rotate_quant_act_batched(ctypes.cast(self._descs, ctypes.c_void_p), self.count,
+                                              _stream(stream, self.device))
+        _check(st, "qift_rotate_quant_act_batched")
+
+
+def qift_rotate_quant_act_batched(items, stream=None):
+    """Several activation matrices in one call. items: sequence of
+    (X, had_block) or (X, had_block, xq, s_a, x_rot) with X [M, K]
+    float32/bfloat16 (None outputs are allocated; x_rot None means not
+    wanted). Returns [(xq, s_a, x_rot), ...] in the same order."""
+    items = list(items)
+    if len(items) > QIFT_MAX_ROTATE_BATCH:
+        raise ValueError(f"at most {QIFT_MAX_ROTATE_BATCH} matrices per call")
+    descs = (qift_rotate_desc * max(1, len(items)))()
+    outs = []
+    dev = None
+    for j, it in enumerate(items):
+        X, had_block = it[0], it[1]
+        xq, s_a, x_rot = (tuple(it[2:5]) + (None, None, None))[:3]
+        _dev_tensor(X, "X", (torch.float32, torch.bfloat16))
+        dev = X.device
+        M, K = X.shape
+        if xq is None:
+            xq = torch.empty((M, K // 2), dtype=torch.uint8, device=X.device)
+        if s_a is None:
+            s_a = torch.empty((M,), dtype=torch.float32, device=X.device)
+        _check_rotate_buffers(M, K, xq, s_a, x_rot)
+        descs[j] = qift_rotate_desc(_ptr(X), _TORCH_TO_QIFT[X.dtype], had_block, M, K, _ptr(xq),
+                                    _ptr(s_a), _ptr(x_rot))
+        outs.append((xq, s_a, x_rot))
+    if not items:
+        return outs
+    st = _C.qift_rotate_quant_act_batched(ctypes.cast(descs, ctypes.c_void_p), len(items),
+                                          _stream(stream, dev))
+    _check(st, "qift_rotate_quant_act_batched")
+    return outs
 
 
 def qift_w2a4_linear(xq, s_a, codes, scales, levels="mnz", out_dtype=torch.float32, Y=None,
@@ -296,6 +373,7 @@ class LinearGroup:
                "qift_w2a4_linear_grouped")
 
 
-__all__ = ["load_library", "QiftUnavailable", "qift_quantize_weights", "qift_rotate_quant_act", "qift_w2a4_linear", "qift_kv4_quant",
+__all__ = ["load_library", "QiftUnavailable", "qift_quantize_weights", "qift_rotate_quant_act",
+           "qift_rotate_quant_act_batched", "RotateBatch", "qift_w2a4_linear", "qift_kv4_quant",
            "LinearGroup", "QiftError", "qift_linear_desc", "LEVELS", "status_string", "last_error",
            "abi_version", "code_words_per_row", "padded_channels", "LIB_PATH"]

@@ -126,9 +126,9 @@ qift_status qift_quantize_weights(const void* W, qift_dtype w_dtype, int64_t N, 
                     "qift_quantize_weights launch");
 }
 
-qift_status qift_rotate_quant_act(const void* X, qift_dtype x_dtype, int64_t M, int64_t K,
-                                  int32_t had_block, uint8_t* xq, float* s_a, float* x_rot,
-                                  qift_stream stream) {
+static qift_status check_rotate(const void* X, qift_dtype x_dtype, int64_t M, int64_t K,
+                                int32_t had_block, const uint8_t* xq, const float* s_a,
+                                const float* x_rot) {
   if (x_dtype != QIFT_F32 && x_dtype != QIFT_BF16)
     return fail(QIFT_ERR_INVALID_ARG, "x_dtype must be F32 or BF16");
   if (M < 0) return fail(QIFT_ERR_INVALID_ARG, "negative M");
@@ -138,12 +138,58 @@ qift_status qift_rotate_quant_act(const void* X, qift_dtype x_dtype, int64_t M, 
     return fail(QIFT_ERR_UNSUPPORTED, "K=%lld exceeds %d", (long long)K, QIFT_MAX_ROW);
   qift_status st = check_had_block(had_block, K, QIFT_MAX_HAD_BLOCK);
   if (st != QIFT_OK) return st;
-  if (M == 0) return ok();
+  if (M == 0) return QIFT_OK;
   if (M > kMaxGrid) return fail(QIFT_ERR_UNSUPPORTED, "M too large");
   if (!X || !xq || !s_a) return fail(QIFT_ERR_INVALID_ARG, "null buffer");
   if (!aligned(xq, 16)) return fail(QIFT_ERR_ALIGNMENT, "xq must be 16-byte aligned");
   if (!aligned(X, x_dtype == QIFT_F32 ? 4 : 2) || !aligned(s_a, 4) || (x_rot && !aligned(x_rot, 4)))
     return fail(QIFT_ERR_ALIGNMENT, "X, s_a or x_rot misaligned for its dtype");
+  return QIFT_OK;
+}
+
+qift_status qift_rotate_quant_act_batched(const qift_rotate_desc* descs, int32_t count,
+                                          qift_stream stream) {
+  if (count < 0 || count > QIFT_MAX_ROTATE_BATCH)
+    return fail(QIFT_ERR_INVALID_ARG, "count=%d outside 0..%d", (int)count,
+                QIFT_MAX_ROTATE_BATCH);
+  if (count == 0) return ok();
+  if (!descs) return fail(QIFT_ERR_INVALID_ARG, "null descs");
+  int64_t total = 0;
+  for (int j = 0; j < count; ++j) {
+    const qift_rotate_desc& r = descs[j];
+    qift_status st = check_rotate(r.X, r.x_dtype, r.M, r.K, r.had_block, r.xq, r.s_a, r.x_rot);
+    if (st != QIFT_OK) return st;
+    total += r.M;
+  }
+  if (total > kMaxGrid) return fail(QIFT_ERR_UNSUPPORTED, "too many rows in total");
+  const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  qift::RotJob jobs[QIFT_MAX_ROTATE_BATCH];
+  int64_t rows[QIFT_MAX_ROTATE_BATCH];
+  int nj = 0;
+  for (int j = 0; j < count; ++j) {
+    const qift_rotate_desc& r = descs[j];
+    if (r.M == 0) continue;
+    if (qift::rotate_fast_ok(r.X, r.K, r.had_block, r.xq, r.x_rot)) {
+      jobs[nj] = qift::RotJob{r.X, r.xq, r.s_a, r.x_rot, (int)r.K, (int)r.had_block, 0, 0.f,
+                              r.x_dtype == QIFT_BF16};
+      rows[nj] = r.M;
+      ++nj;
+    } else {
+      hipError_t e = qift::launch_rotate_quant_act(r.X, r.x_dtype == QIFT_BF16, r.M, r.K,
+                                                   r.had_block, r.xq, r.s_a, r.x_rot, s);
+      if (e != hipSuccess) return hip_result(e, "qift_rotate_quant_act_batched launch");
+    }
+  }
+  return hip_result(qift::launch_rotate_quant_act_batched(jobs, rows, nj, s),
+                    "qift_rotate_quant_act_batched launch");
+}
+
+qift_status qift_rotate_quant_act(const void* X, qift_dtype x_dtype, int64_t M, int64_t K,
+                                  int32_t had_block, uint8_t* xq, float* s_a, float* x_rot,
+                                  qift_stream stream) {
+  qift_status st = check_rotate(X, x_dtype, M, K, had_block, xq, s_a, x_rot);
+  if (st != QIFT_OK) return st;
+  if (M == 0) return ok();
   return hip_result(qift::launch_rotate_quant_act(X, x_dtype == QIFT_BF16, M, K, had_block, xq,
                                                   s_a, x_rot,
                                                   reinterpret_cast<hipStream_t>(stream)),

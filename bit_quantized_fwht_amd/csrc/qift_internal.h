@@ -169,6 +169,22 @@ constexpr int kDecodeRowsPerTile = kDecodeRowsPerWave * kDecodeWaves;
 // launchers (implemented in the .hip files; return a hipError_t)
 // ---------------------------------------------------------------------------
 
+// one activation matrix of a batched rotate launch (row-kernel fast path)
+struct RotJob {
+  const void* X;
+  uint8_t* xq;
+  float* s_a;
+  float* x_rot;
+  int K;
+  int had_block;  // set by the caller; the launcher derives log2b and norm
+  int log2b;
+  float norm;
+  int bf16;
+};
+bool rotate_fast_ok(const void* X, int64_t K, int had_block, const uint8_t* xq,
+                    const float* x_rot);
+hipError_t launch_rotate_quant_act_batched(const RotJob* jobs, const int64_t* rows, int count,
+                                           hipStream_t s);
 hipError_t launch_rotate_quant_act(const void* X, int x_bf16, int64_t M, int64_t K, int had_block,
                                    uint8_t* xq, float* s_a, float* x_rot, hipStream_t s);
 hipError_t launch_quantize_weights(const void* W, int w_bf16, int64_t N, int64_t K, int had_block,

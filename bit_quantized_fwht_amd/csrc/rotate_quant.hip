@@ -244,35 +244,49 @@ __device__ __forceinline__ void load16<float>(const float* __restrict__ src, flo
   }
 }
 
+// One row on the fast path. A thread owns the groups tid, tid + 256, ... of
+// 16 consecutive elements (at most kFastMaxGroups of them, K <= 16384); all
+// of its global loads are issued before any group is transformed, so a long
+// row costs one memory latency rather than one per group.
+constexpr int kFastMaxGroups = 4;
+static_assert(kFastMaxGroups * 16 * kRowThreads >= QIFT_MAX_ROW, "fast path covers QIFT_MAX_ROW");
+
 template <typename T>
-__global__ __launch_bounds__(kRowThreads) void rotate_quant_act_fast_kernel(
-    const T* __restrict__ X, int K, int log2b, float norm, uint8_t* __restrict__ xq,
-    float* __restrict__ s_a, float* __restrict__ x_rot) {
-  extern __shared__ float row[];
-  __shared__ float red[kRowThreads / 64];
+__device__ __forceinline__ void rotate_row_fast(const T* __restrict__ src, int K, int log2b,
+                                                float norm, uint8_t* __restrict__ xq_row,
+                                                float* __restrict__ s_out,
+                                                float* __restrict__ xrot_row, float* row,
+                                                float* red) {
   const int tid = threadIdx.x;
-  const int64_t m = blockIdx.x;
   const int groups = K >> 4;
-  const T* src = X + m * K;
-  // 1. load + stages 0..3 in registers
-  for (int grp = tid; grp < groups; grp += kRowThreads) {
-    float v[16];
-    load16<T>(src + 16 * grp, v);
+  // 1. loads (a group past the row end reads group 0 and is discarded), then
+  //    stages 0..3 in registers and the padded LDS store
+  float v[kFastMaxGroups][16];
 #pragma unroll
-    for (int st = 0; st < 4; ++st) {
-      const int h = 1 << st;
+  for (int q = 0; q < kFastMaxGroups; ++q) {
+    const int grp = tid + q * kRowThreads;
+    load16<T>(src + 16 * (grp < groups ? grp : 0), v[q]);
+  }
 #pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        if (!(j & h)) {
-          const float a = v[j], b = v[j + h];
-          v[j] = a + b;
-          v[j + h] = a - b;
+  for (int q = 0; q < kFastMaxGroups; ++q) {
+    const int grp = tid + q * kRowThreads;
+    if (grp < groups) {
+#pragma unroll
+      for (int st = 0; st < 4; ++st) {
+        const int h = 1 << st;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          if (!(j & h)) {
+            const float a = v[q][j], b = v[q][j + h];
+            v[q][j] = a + b;
+            v[q][j + h] = a - b;
+          }
         }
       }
-    }
-    float* dst = row + 17 * grp;
+      float* dst = row + 17 * grp;
 #pragma unroll
-    for (int j = 0; j < 16; ++j) dst[j] = v[j];
+      for (int j = 0; j < 16; ++j) dst[j] = v[q][j];
+    }
   }
   __syncthreads();
   // 2. stages 4.. through padded LDS
@@ -303,8 +317,8 @@ __global__ __launch_bounds__(kRowThreads) void rotate_quant_act_fast_kernel(
   for (int w = 1; w < kRowThreads / 64; ++w) amax = fmaxf(amax, red[w]);
   const float s = __fdiv_rn(amax, 7.0f);
   const float rs = s != 0.f ? __fdiv_rn(1.0f, s) : 0.f;
-  if (tid == 0) s_a[m] = s;
-  uint2* xrow = reinterpret_cast<uint2*>(xq + m * (int64_t)(K / 2));
+  if (tid == 0) *s_out = s;
+  uint2* xrow = reinterpret_cast<uint2*>(xq_row);
   for (int grp = tid; grp < groups; grp += kRowThreads) {
     const float* s16 = row + 17 * grp;
     float x[16];
@@ -317,12 +331,53 @@ __global__ __launch_bounds__(kRowThreads) void rotate_quant_act_fast_kernel(
       w1 |= code_int4_recip(x[8 + j], s, rs) << (4 * j);
     }
     xrow[grp] = uint2{w0, w1};
-    if (x_rot) {
-      float4* xr = reinterpret_cast<float4*>(x_rot + m * K + 16 * grp);
+    if (xrot_row) {
+      float4* xr = reinterpret_cast<float4*>(xrot_row + 16 * grp);
 #pragma unroll
       for (int i = 0; i < 4; ++i) xr[i] = float4{x[4 * i], x[4 * i + 1], x[4 * i + 2], x[4 * i + 3]};
     }
   }
+}
+
+template <typename T>
+__global__ __launch_bounds__(kRowThreads) void rotate_quant_act_fast_kernel(
+    const T* __restrict__ X, int K, int log2b, float norm, uint8_t* __restrict__ xq,
+    float* __restrict__ s_a, float* __restrict__ x_rot) {
+  extern __shared__ float row[];
+  __shared__ float red[kRowThreads / 64];
+  const int64_t m = blockIdx.x;
+  rotate_row_fast<T>(X + m * K, K, log2b, norm, xq + m * (int64_t)(K / 2), s_a + m,
+                     x_rot ? x_rot + m * K : nullptr, row, red);
+}
+
+// Several activation matrices in one launch (workgroup b covers row b of the
+// concatenation of their rows), e.g. the inputs of all linears of a decode
+// step, which are too small to fill the chip one at a time.
+struct RotBatch {
+  RotJob job[QIFT_MAX_ROTATE_BATCH];
+  int64_t row_begin[QIFT_MAX_ROTATE_BATCH + 1];
+  int count;
+};
+
+__global__ __launch_bounds__(kRowThreads) void rotate_quant_act_batched_kernel(RotBatch bt) {
+  extern __shared__ float row[];
+  __shared__ float red[kRowThreads / 64];
+  const int64_t b = blockIdx.x;
+  int j = 0;
+#pragma unroll
+  for (int k = 1; k < QIFT_MAX_ROTATE_BATCH; ++k)
+    if (k < bt.count && b >= bt.row_begin[k]) j = k;
+  const RotJob& jb = bt.job[j];
+  const int64_t m = b - bt.row_begin[j];
+  const int K = jb.K;
+  uint8_t* xq_row = jb.xq + m * (int64_t)(K / 2);
+  float* xr = jb.x_rot ? jb.x_rot + m * K : nullptr;
+  if (jb.bf16)
+    rotate_row_fast<uint16_t>(reinterpret_cast<const uint16_t*>(jb.X) + m * K, K, jb.log2b,
+                              jb.norm, xq_row, jb.s_a + m, xr, row, red);
+  else
+    rotate_row_fast<float>(reinterpret_cast<const float*>(jb.X) + m * K, K, jb.log2b, jb.norm,
+                           xq_row, jb.s_a + m, xr, row, red);
 }
 
 // --- K0: rotate + per-channel scale + nearest level + pack ----------------------
@@ -426,9 +481,7 @@ hipError_t launch_rotate_quant_act(const void* X, int x_bf16, int64_t M, int64_t
                                    uint8_t* xq, float* s_a, float* x_rot, hipStream_t s) {
   const int lb = ilog2(had_block);
   const float nrm = had_norm(had_block);
-  const uintptr_t align = reinterpret_cast<uintptr_t>(X) | reinterpret_cast<uintptr_t>(xq) |
-                          reinterpret_cast<uintptr_t>(x_rot);
-  if (K % 16 == 0 && had_block >= 16 && (align & 15) == 0) {
+  if (rotate_fast_ok(X, K, had_block, xq, x_rot)) {
     const size_t lds = (size_t)(K + K / 16) * sizeof(float);
     if (x_bf16)
       hipLaunchKernelGGL(rotate_quant_act_fast_kernel<uint16_t>, dim3((unsigned)M),
@@ -447,6 +500,35 @@ hipError_t launch_rotate_quant_act(const void* X, int x_bf16, int64_t M, int64_t
   else
     hipLaunchKernelGGL(rotate_quant_act_kernel<float>, dim3((unsigned)M), dim3(kRowThreads), lds,
                        s, reinterpret_cast<const float*>(X), (int)K, lb, nrm, xq, s_a, x_rot);
+  return hipGetLastError();
+}
+
+bool rotate_fast_ok(const void* X, int64_t K, int had_block, const uint8_t* xq,
+                    const float* x_rot) {
+  const uintptr_t align = reinterpret_cast<uintptr_t>(X) | reinterpret_cast<uintptr_t>(xq) |
+                          reinterpret_cast<uintptr_t>(x_rot);
+  return K % 16 == 0 && had_block >= 16 && (align & 15) == 0;
+}
+
+hipError_t launch_rotate_quant_act_batched(const RotJob* jobs, const int64_t* rows, int count,
+                                           hipStream_t s) {
+  RotBatch bt{};
+  bt.count = count;
+  int64_t total = 0;
+  int64_t kmax = 0;
+  for (int j = 0; j < count; ++j) {
+    bt.job[j] = jobs[j];
+    bt.job[j].log2b = ilog2(jobs[j].had_block);
+    bt.job[j].norm = had_norm(jobs[j].had_block);
+    bt.row_begin[j] = total;
+    total += rows[j];
+    kmax = jobs[j].K > kmax ? jobs[j].K : kmax;
+  }
+  for (int j = count; j <= QIFT_MAX_ROTATE_BATCH; ++j) bt.row_begin[j] = total;
+  if (total == 0) return hipSuccess;
+  const size_t lds = (size_t)(kmax + kmax / 16) * sizeof(float);
+  hipLaunchKernelGGL(rotate_quant_act_batched_kernel, dim3((unsigned)total), dim3(kRowThreads),
+                     lds, s, bt);
   return hipGetLastError();
 }
 

@@ -144,6 +144,36 @@ qift_status qift_rotate_quant_act(const void* X, qift_dtype x_dtype, int64_t M, 
                                   qift_stream stream);
 
 /*
+ * qift_rotate_quant_act_batched -- qift_rotate_quant_act on up to
+ * QIFT_MAX_ROTATE_BATCH independent activation matrices in one call (the
+ * same online activation path; meant for the inputs of all linears of a
+ * decode step, a few token rows each, which cannot fill the GPU one by one).
+ * Each descriptor has the meaning, limits and results of the arguments of
+ * qift_rotate_quant_act; every descriptor is validated before anything is
+ * launched. Descriptors with K % 16 == 0, had_block >= 16 and 16-byte aligned
+ * X, xq (and x_rot if given) share one launch with one workgroup per row; any
+ * other descriptor gets a launch of its own. Outputs of different
+ * descriptors must not overlap.
+ *
+ *   descs  HOST array of count descriptors, read during the call only
+ *   count  0 .. QIFT_MAX_ROTATE_BATCH (0 is a no-op)
+ */
+#define QIFT_MAX_ROTATE_BATCH 8
+typedef struct {
+  const void* X;      /* [M, K] float32 or bfloat16 */
+  qift_dtype x_dtype; /* QIFT_F32 or QIFT_BF16 */
+  int32_t had_block;
+  int64_t M;
+  int64_t K;
+  uint8_t* xq;        /* out: [M, K/2] int4 pairs */
+  float* s_a;         /* out: [M] */
+  float* x_rot;       /* out, optional: [M, K] float32 */
+} qift_rotate_desc;
+
+qift_status qift_rotate_quant_act_batched(const qift_rotate_desc* descs, int32_t count,
+                                          qift_stream stream);
+
+/*
  * qift_w2a4_linear -- the linear layer with decoded two-bit weights (Qift
  * abstract: the power-of-two set is applied by sign and shift, the main set
  * in its half-scale integer form):

@@ -32,7 +32,7 @@ def test_library_loads_and_exports_every_declared_symbol():
     lib = q.load_library()
     names = declared_functions()
     assert "qift_w2a4_linear" in names and "qift_kv4_quant" in names
-    assert len(names) == 10, names
+    assert len(names) == 11, names
     for n in names:
         assert hasattr(lib, n), n
     assert q.abi_version() == 1
@@ -99,6 +99,45 @@ def test_rotate_rejects(kw, status):
 
 def test_rotate_empty_is_noop():
     assert rot(M=0, X=None, xq=None, s_a=None) == q.QIFT_OK
+
+
+def rot_batch(descs, count=None):
+    arr = (q.qift_rotate_desc * max(1, len(descs)))(*descs)
+    n = len(descs) if count is None else count
+    return q._C.qift_rotate_quant_act_batched(ctypes.cast(arr, ctypes.c_void_p), n, None)
+
+
+def rdesc(**kw):
+    args = dict(X=A16.value, x_dtype=q.QIFT_BF16, had_block=256, M=2, K=256, xq=A16b.value,
+                s_a=A16c.value, x_rot=None)
+    args.update(kw)
+    return q.qift_rotate_desc(**args)
+
+
+def test_rotate_batched_struct_matches_header():
+    # X, x_dtype, had_block, M, K, xq, s_a, x_rot with natural alignment
+    assert ctypes.sizeof(q.qift_rotate_desc) == 56
+    assert q.qift_rotate_desc.M.offset == 16 and q.qift_rotate_desc.xq.offset == 32
+
+
+@pytest.mark.parametrize("descs,count,status", [
+    ([rdesc()] * 9, None, q.QIFT_ERR_INVALID_ARG),                      # more than 8
+    ([rdesc()], -1, q.QIFT_ERR_INVALID_ARG),
+    ([rdesc(), rdesc(had_block=3)], None, q.QIFT_ERR_INVALID_ARG),      # second one invalid
+    ([rdesc(M=0), rdesc(K=16384 + 2)], None, q.QIFT_ERR_UNSUPPORTED),
+    ([rdesc(xq=0x20004)], None, q.QIFT_ERR_ALIGNMENT),
+    ([rdesc(X=None)], None, q.QIFT_ERR_INVALID_ARG),
+])
+def test_rotate_batched_rejects(descs, count, status):
+    assert rot_batch(descs, count) == status
+    assert q.last_error() != ""
+
+
+def test_rotate_batched_empty_is_noop():
+    assert rot_batch([], 0) == q.QIFT_OK
+    assert q._C.qift_rotate_quant_act_batched(None, 0, None) == q.QIFT_OK
+    # all descriptors with M = 0: validated, nothing launched
+    assert rot_batch([rdesc(M=0, X=None, xq=None, s_a=None)] * 3) == q.QIFT_OK
 
 
 def qw(**kw):

@@ -101,6 +101,29 @@ def test_rotate_quant_bitexact_exact_rotation(M, K, B):
         assert np.array_equal(qg, qo.astype(np.int64))
 
 
+def test_rotate_batched_matches_single_calls():
+    """One batched call over matrices of different K, block, dtype and row
+    count (one outside the shared launch's conditions, one empty) gives the
+    same bytes as one call per matrix."""
+    cases = [(3, 4096, 4096, torch.bfloat16, False), (5, 11008, 256, torch.float32, True),
+             (2, 256, 16, torch.bfloat16, True), (0, 512, 64, torch.bfloat16, False),
+             (4, 10, 2, torch.float32, True), (2, 16384, 4096, torch.bfloat16, False)]
+    say("rotate batched vs single")
+    items, refs = [], []
+    for i, (M, K, B, dt, want) in enumerate(cases):
+        X = torch.from_numpy(si.activations(M, K, seed=300 + i, n_outliers=min(3, K))).to(dt).to(DEV)
+        refs.append(q.qift_rotate_quant_act(X, B, want_x_rot=want))
+        x_rot = torch.full((M, K), 7.0, device=DEV) if want else None
+        items.append((X, B, None, None, x_rot))
+    outs = q.qift_rotate_quant_act_batched(items)
+    sync()
+    for (xq, sa, xr), (rxq, rsa, rxr), c in zip(outs, refs, cases):
+        assert torch.equal(xq, rxq), c
+        assert torch.equal(sa, rsa), c
+        if c[4]:
+            assert torch.equal(xr, rxr), c
+
+
 def test_rotate_rne_ties_and_zero_rows():
     import json, os
     g = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "rne_ties.json")))
