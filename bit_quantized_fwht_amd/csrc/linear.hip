@@ -491,9 +491,7 @@ __device__ __forceinline__ void epilogue_blk(const qift_linear_desc& d, const v4
           if (vec) {
             uint32_t w[4];
 #pragma unroll
-            for (int e = 0; e < 4; ++e)
-              w[e] = (uint32_t)float_to_bf16_bits(y[2 * e]) |
-                     ((uint32_t)float_to_bf16_bits(y[2 * e + 1]) << 16);
+            for (int e = 0; e < 4; ++e) w[e] = pack_bf16x2(y[2 * e], y[2 * e + 1]);
             *reinterpret_cast<uint4*>(yo) = uint4{w[0], w[1], w[2], w[3]};
           } else {
             for (int e = 0; e < 8; ++e)
@@ -579,11 +577,9 @@ __device__ __forceinline__ void prefill_tile_sk(const qift_linear_desc& d, int64
       gl_lds16(d.codes + b_off[p] + st * C::kBChunks * 256, bs + (wave * C::kBInstr + p) * 1024);
   };
 
+  // written first by the first stage's MFMAs, whose accumulator input is
+  // the constant 0 (no separate zeroing of 128 registers per tile)
   v4i acc[8][4];
-#pragma unroll
-  for (int i = 0; i < 8; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = v4i{0, 0, 0, 0};
 
   // int4 weights: the lane's 16-byte unit of chunk kh (32 features, two
   // steps); 2-bit weights: words 2 kh, 2 kh + 1 of the lane's 16-byte unit.
@@ -612,7 +608,7 @@ __device__ __forceinline__ void prefill_tile_sk(const qift_linear_desc& d, int64
         f.b[j] = *reinterpret_cast<const uint2*>(bs + tile * 1024 + 16 * lane + 8 * kh);
     }
   };
-  auto mma = [&](const Frag& f) {
+  auto mma = [&](const Frag& f, bool first) {
 #pragma unroll
     for (int s2 = 0; s2 < 2; ++s2) {
       v4i B[4];
@@ -629,7 +625,8 @@ __device__ __forceinline__ void prefill_tile_sk(const qift_linear_desc& d, int64
       for (int i = 0; i < 8; ++i) {
         const v4i A = s2 == 0 ? int4_operand(f.a[i].x, f.a[i].y) : int4_operand(f.a[i].z, f.a[i].w);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = mfma16(A, B[j], acc[i][j]);
+        for (int j = 0; j < 4; ++j)
+          acc[i][j] = mfma16(A, B[j], (first && s2 == 0) ? v4i{0, 0, 0, 0} : acc[i][j]);
       }
       // Issue order: each MFMA followed by two VALU instructions (the unpack
       // of later operands). Issue is in order within a wave, so a burst of
@@ -658,13 +655,21 @@ __device__ __forceinline__ void prefill_tile_sk(const qift_linear_desc& d, int64
 
   const int64_t nstages = K / C::kStageK;
   issue(0, 0);
-  for (int64_t st = 0; st < nstages; ++st) {
+  {
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    Frag f;
+    fetch(0, f);
+    if (nstages > 1) issue(1, 1);
+    mma(f, true);
+  }
+  for (int64_t st = 1; st < nstages; ++st) {
     __builtin_amdgcn_s_waitcnt(0);   // this wave's loads of stage st have landed
     __syncthreads();                 // ... everyone's; and stage st-1 is consumed
     Frag f;
     fetch((int)(st & 1), f);
     if (st + 1 < nstages) issue(st + 1, (int)((st + 1) & 1));
-    mma(f);
+    mma(f, false);
   }
   scl[tid] = pre_scale;              // read after the exchange's barriers
 

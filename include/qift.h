@@ -13,8 +13,9 @@
  * Conventions shared by every call
  * --------------------------------
  * - Every buffer argument is a DEVICE pointer owned by the caller. The library
- *   allocates no device memory and keeps no state besides a cached device
- *   property; it is safe to call from several host threads.
+ *   allocates no device memory and keeps no state (the plan of a grouped
+ *   launch lives in a caller-owned workspace); it is safe to call from several
+ *   host threads.
  * - Calls are asynchronous: they validate, enqueue on `stream` and return.
  *   Outputs are valid in stream order. `stream` is a hipStream_t passed as
  *   void* (NULL = the null stream).
