@@ -164,6 +164,26 @@ def time_fn(torch, fn, reps, warmup=3):
     return float(np.median(t)), float(t.min()), float(t.mean())
 
 
+def vendor_int8_gemm(torch, M, K, N, dev):
+    """Context only, not this library's path: the vendor int8 GEMM
+    (torch._int_mm, int8 [M, K] x int8 [K, N] -> int32, i.e. 8-bit weights
+    already expanded in memory, no unpack) on the same shape, best of the
+    N-major and K-major weight layouts."""
+    try:
+        a = torch.randint(-7, 8, (M, K), dtype=torch.int8, device=dev)
+        b = torch.randint(-3, 4, (K, N), dtype=torch.int8, device=dev)
+        best = None
+        for bb in (b, b.t().contiguous().t()):
+            torch._int_mm(a, bb)
+            med, _, _ = time_fn(torch, lambda: torch._int_mm(a, bb), 20)
+            best = med if best is None else min(best, med)
+        ops = 2.0 * M * N * K
+        return {"ms": round(best, 4), "TOPS": round(ops / best / 1e9, 1),
+                "frac_of_int8_peak": round(ops / best / 1e9 / INT8_PEAK_TOPS, 4)}
+    except Exception as e:  # not available in this torch build
+        return {"error": repr(e)[:120]}
+
+
 def kernel_source_hash():
     h = hashlib.sha256()
     for f in sorted(os.listdir(os.path.dirname(KERNEL_SRC))):
@@ -354,6 +374,7 @@ def measure_extras(q, torch, dev, stack, args):
         rmed, _, _ = time_fn(torch, lambda: q.qift_rotate_quant_act(X, B, xq=xq, s_a=sa), 30)
         pre[name].update({"rotate_quant_ms": round(rmed, 4),
                           "rotate_quant_GBps": round((M * K * 2 + M * K / 2 + 4 * M) / rmed / 1e6, 1)})
+        pre[name]["vendor_int8_gemm"] = vendor_int8_gemm(torch, M, K, N, dev)
         del cw, sw, X, xq, sa
     extra["prefill_llama7b_mnz"] = pre
 
@@ -384,6 +405,7 @@ def measure_extras(q, torch, dev, stack, args):
             pf[name].update({"gemm_ms" + tag: round(med, 4), "TOPS" + tag: round(ops / med / 1e9, 1),
                              "frac_of_int8_peak" + tag: round(ops / med / 1e9 / INT8_PEAK_TOPS, 4)})
             del Y
+        pf[name]["vendor_int8_gemm"] = vendor_int8_gemm(torch, M, K, N, dev)
         del cw, sw, X, xq, sa
     pot["prefill_M4096"] = pf
     extra["llama31_8b_pot"] = pot
