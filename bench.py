@@ -42,7 +42,10 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 INT8_PEAK_TOPS = 5000.0        # MI355X dense int8 MFMA, TOP/s
 METRIC = "W2A4 linear: decode weight-stream GB/s + prefill int8 TOPS, % of roofline"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "linear_grouped_decode_llama7b_counters.json")
-KERNEL_SRC = os.path.join(ROOT, "bit_quantized_fwht_amd", "csrc", "linear.hip")
+# the sources the grouped decode kernel is compiled from: the counter summary
+# is valid only for the code it was taken on
+KERNEL_SRCS = [os.path.join(ROOT, "bit_quantized_fwht_amd", "csrc", f)
+               for f in ("linear_decode.hip", "linear_common.h", "qift_internal.h")]
 
 
 def parse():
@@ -186,9 +189,9 @@ def vendor_int8_gemm(torch, M, K, N, dev):
 
 def kernel_source_hash():
     h = hashlib.sha256()
-    for f in sorted(os.listdir(os.path.dirname(KERNEL_SRC))):
-        with open(os.path.join(os.path.dirname(KERNEL_SRC), f), "rb") as fh:
-            h.update(f.encode() + fh.read())
+    for path in KERNEL_SRCS:
+        with open(path, "rb") as fh:
+            h.update(os.path.basename(path).encode() + fh.read())
     return h.hexdigest()[:16]
 
 

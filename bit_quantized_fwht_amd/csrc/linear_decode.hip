@@ -1,0 +1,166 @@
+// The rotated W2A4 linear, decode side (M <= 16): Y = (q . level^T) * s_a *
+// s_w * kappa with an exact int32 accumulator (Qift abstract: decoded weight
+// application of the no-zero two-bit level sets, per-channel scale, 4-bit
+// activations).
+//
+// A wave owns 64 output channels and walks K; every lane loads 16 bytes of
+// codes per 16-channel tile per step straight into registers (no LDS),
+// unpacks them into operands and issues one MFMA per 16 channels; the 16 rows
+// of the MFMA's other side carry the (at most 16) tokens. The accumulation
+// over K happens inside the matrix core, so no cross-lane reduction is needed.
+// The grouped kernel runs the decode tiles of several linears (one plan in a
+// caller-owned workspace) in one launch.
+#include "linear_common.h"
+
+namespace qift {
+
+// ---------------------------------------------------------------------------
+// decode: M <= 16
+// ---------------------------------------------------------------------------
+
+#ifndef QIFT_DECODE_MINBLOCKS
+#define QIFT_DECODE_MINBLOCKS 2
+#endif
+
+constexpr int kDecodeTiles = kDecodeRowsPerWave / 16;  // 16-channel MFMA tiles per wave
+
+// weight-stream load: 16 bytes, optionally marked non-temporal (streamed once)
+__device__ __forceinline__ uint4 ld16_stream(const uint32_t* p) {
+#if QIFT_DECODE_NT
+  const v4u v = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(p));
+  return uint4{v[0], v[1], v[2], v[3]};
+#else
+  return ld16(p);
+#endif
+}
+
+template <int LV>
+__device__ __forceinline__ void decode_wave(const qift_linear_desc& d, int64_t n0, int scale_f16,
+                                            int y_dtype, int lane) {
+  using F = Fmt<LV>;
+  const int r16 = lane & 15;
+  const int g = lane >> 4;
+  const int64_t M = d.M, K = d.K, N = d.N;
+  const int64_t cw = F::code_words(K);
+  const uint8_t* xq = d.xq;
+  const uint32_t* codes = d.codes;
+  const bool act_row = r16 < M;
+  const MnzMasks km = mnz_masks(d.reserved, lane);
+
+  v4i acc[kDecodeTiles];
+#pragma unroll
+  for (int i = 0; i < kDecodeTiles; ++i) acc[i] = v4i{0, 0, 0, 0};
+
+  const int64_t nchunks = (K + F::kChunkK - 1) / F::kChunkK;
+
+  // one K chunk of this lane: its 16-byte code unit of each tile and the
+  // matching 32 (or 16) bytes of its activation row
+  struct Chunk {
+    uint4 c[kDecodeTiles];
+    uint4 a0, a1;
+  };
+  auto load = [&](Chunk& ch, int64_t t) {
+    const int64_t kseg = t * F::kChunkK + (int64_t)g * F::kLaneK;
+    const bool kval = t < nchunks && kseg < K;
+    // tiled layout: 16-channel tile (n0 + 16 i) / 16, chunk t, the lane's
+    // 16-byte unit at word 4 * lane -- one contiguous 1 KB per wave load
+#pragma unroll
+    for (int i = 0; i < kDecodeTiles; ++i) {
+      const int64_t tn = n0 + 16 * i;
+      ch.c[i] = (kval && tn < N) ? ld16_stream(codes + (tn >> 4) * 16 * cw + t * 256 + 4 * lane)
+                                 : uint4{0u, 0u, 0u, 0u};
+    }
+    ch.a0 = uint4{0u, 0u, 0u, 0u};
+    ch.a1 = uint4{0u, 0u, 0u, 0u};
+    if (kval && act_row) {
+      const uint8_t* ap = xq + (int64_t)r16 * (K / 2) + kseg / 2;
+      ch.a0 = ld16(ap);
+      if constexpr (!F::kInt4) ch.a1 = ld16(ap + 16);
+    }
+  };
+  auto compute = [&](const Chunk& ch) {
+#pragma unroll
+    for (int s = 0; s < F::kSteps; ++s) {
+      const v4i A = act_operand(ch.a0, ch.a1, s);
+#pragma unroll
+      for (int i = 0; i < kDecodeTiles; ++i)
+        acc[i] = mfma16(A, weight_operand<LV>(ch.c[i], s, km), acc[i]);
+    }
+  };
+  // two chunks in flight: the loads of chunk t+1 are issued before chunk t
+  // is consumed
+  Chunk x, y;
+  load(x, 0);
+  for (int64_t t = 0; t < nchunks; t += 2) {
+    load(y, t + 1);
+    compute(x);
+    load(x, t + 2);
+    if (t + 1 < nchunks) compute(y);
+  }
+
+  // epilogue: lane holds rows m = 4g + r of channel n0 + 16 i + r16
+  const float kappa = level_kappa(LV);
+#pragma unroll
+  for (int i = 0; i < kDecodeTiles; ++i) {
+    const int64_t n = n0 + 16 * i + r16;
+    if (n >= N) continue;
+    const float sw = load_scale(d.scales, n, scale_f16) * kappa;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int m = 4 * g + r;
+      if (m < M) {
+        const int a = acc[i][r] >> F::kShift;
+        store_y(d.Y, y_dtype, (int64_t)m * N + n, a, d.s_a[m] * sw);
+      }
+    }
+  }
+}
+
+__device__ __forceinline__ void decode_dispatch(const qift_linear_desc& d, int64_t tile,
+                                                int scale_f16, int y_dtype) {
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int64_t n0 = tile * kDecodeRowsPerTile + (int64_t)wave * kDecodeRowsPerWave;
+  if (n0 >= d.N) return;
+  switch (d.levels) {
+    case QIFT_LEVELS_MNZ: decode_wave<QIFT_LEVELS_MNZ>(d, n0, scale_f16, y_dtype, lane); break;
+    case QIFT_LEVELS_POT: decode_wave<QIFT_LEVELS_POT>(d, n0, scale_f16, y_dtype, lane); break;
+    default: decode_wave<QIFT_LEVELS_INT4>(d, n0, scale_f16, y_dtype, lane); break;
+  }
+}
+
+__global__ __launch_bounds__(256, QIFT_DECODE_MINBLOCKS) void linear_decode_kernel(qift_linear_desc d, int scale_f16,
+                                                            int y_dtype) {
+  decode_dispatch(d, blockIdx.x, scale_f16, y_dtype);
+}
+
+__global__ __launch_bounds__(256, QIFT_DECODE_MINBLOCKS) void linear_grouped_kernel(const uint8_t* __restrict__ ws) {
+  const PlanHeader* h = reinterpret_cast<const PlanHeader*>(ws);
+  const int64_t tile = blockIdx.x;
+  if (tile >= h->total_tiles) return;
+  const int32_t e = reinterpret_cast<const int32_t*>(ws + h->tile_map_offset)[tile];
+  const PlanEntry* pe = reinterpret_cast<const PlanEntry*>(ws + h->entries_offset) + e;
+  const qift_linear_desc d = pe->d;
+  decode_dispatch(d, tile - pe->tile_begin, h->scale_f16, h->y_dtype);
+}
+
+// ---------------------------------------------------------------------------
+// launchers
+// ---------------------------------------------------------------------------
+
+hipError_t launch_linear_decode(const qift_linear_desc& d, int scale_f16, int y_dtype,
+                                hipStream_t s) {
+  const int64_t tiles = (d.N + kDecodeRowsPerTile - 1) / kDecodeRowsPerTile;
+  hipLaunchKernelGGL(linear_decode_kernel, dim3((unsigned)tiles), dim3(256), 0, s, d, scale_f16,
+                     y_dtype);
+  return hipGetLastError();
+}
+
+hipError_t launch_linear_grouped(const void* workspace, int64_t total_tiles, int, int,
+                                 hipStream_t s) {
+  hipLaunchKernelGGL(linear_grouped_kernel, dim3((unsigned)total_tiles), dim3(256), 0, s,
+                     reinterpret_cast<const uint8_t*>(workspace));
+  return hipGetLastError();
+}
+
+}  // namespace qift
