@@ -3,12 +3,25 @@
 // its own absmax scale (the "KV4" of rotated W2A4/KV4 inference, Qift
 // abstract).
 //
-// Layout on the GPU: a head vector of D elements is held by L = D/E lanes
-// with E = min(D, 32) consecutive elements each, so five butterfly stages run
-// inside a lane's registers and only log2(L) stages (xor 1 and 2 for
-// D = 128, quad permutes) cross lanes. A lane loads E*2 contiguous bytes
-// (bf16) and stores E/2 bytes of codes; the kernel is bound by HBM bandwidth.
-#include "qift_internal.h"
+// Layout on the GPU: a head vector of D elements is held by L = D/E lanes of
+// one quad (L <= 4) with E consecutive elements each (E = 16, 32 or 64), so
+// log2(E) butterfly stages run inside a lane's registers and at most two
+// (partners at lane xor 1 and xor 2) cross lanes, through DPP quad
+// permutations. A lane loads 2E (bf16) or 4E bytes and stores E/2 bytes of
+// codes. The kernel is bound by HBM bandwidth in principle and by VALU issue
+// in practice, so every step is written for the fewest instructions per
+// element:
+//  - a cross-lane butterfly costs one fused multiply-add per element: each
+//    lane keeps its values up to a sign sigma (true = sigma * stored). For
+//    partners with equal sigma, the lower lane's new value is
+//    stored + partner and the upper lane's is partner - stored
+//    = -(stored - partner); the upper lane therefore stores
+//    fma(partner, -1, stored) and flips its sigma. The results are the same
+//    float32 values as the plain butterfly, up to that sign;
+//  - the absmax ignores the sign; the quantizer folds sigma into 1 / s;
+//  - rounding and packing use the float adder and byte permutes
+//    (int4x8_rint), with the exact division only for near-tie groups.
+#include "quant_pack.h"
 
 namespace qift {
 
@@ -39,27 +52,62 @@ __device__ __forceinline__ void kv4_load(const T* __restrict__ src, float v[E]) 
   }
 }
 
-template <int E, int L, typename T>
+// value of lane (lane ^ H) of the same quad, H in {1, 2} (DPP quad_perm)
+template <int H>
+__device__ __forceinline__ float quad_xor(float x) {
+  constexpr int kCtrl = H == 1 ? 0xB1 : 0x4E;  // [1,0,3,2] or [2,3,0,1]
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), kCtrl, 0xF, 0xF, true));
+}
+
+// Cross-lane butterfly of eight values: v[j] = v[j] of lane (lane ^ H) * c +
+// v[j], one v_fmac_f32 with a DPP quad permutation of its first source per
+// value (the compiler keeps the permutation as a separate v_mov_b32_dpp and
+// a three-operand fma). The leading s_nop covers the two wait states a DPP
+// source needs after a VALU write; inside the block each instruction reads a
+// register no earlier instruction of the block wrote.
+#define QIFT_FMAC_DPP(i, PERM) "v_fmac_f32_dpp %" #i ", %" #i ", %8 " PERM " row_mask:0xf bank_mask:0xf\n\t"
+template <int H>
+__device__ __forceinline__ void quad_butterfly8(float* v, float c) {
+  if constexpr (H == 1) {
+    asm("s_nop 1\n\t" QIFT_FMAC_DPP(0, "quad_perm:[1,0,3,2]") QIFT_FMAC_DPP(1, "quad_perm:[1,0,3,2]")
+        QIFT_FMAC_DPP(2, "quad_perm:[1,0,3,2]") QIFT_FMAC_DPP(3, "quad_perm:[1,0,3,2]")
+        QIFT_FMAC_DPP(4, "quad_perm:[1,0,3,2]") QIFT_FMAC_DPP(5, "quad_perm:[1,0,3,2]")
+        QIFT_FMAC_DPP(6, "quad_perm:[1,0,3,2]") QIFT_FMAC_DPP(7, "quad_perm:[1,0,3,2]")
+        : "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3]), "+v"(v[4]), "+v"(v[5]), "+v"(v[6]),
+          "+v"(v[7])
+        : "v"(c));
+  } else {
+    asm("s_nop 1\n\t" QIFT_FMAC_DPP(0, "quad_perm:[2,3,0,1]") QIFT_FMAC_DPP(1, "quad_perm:[2,3,0,1]")
+        QIFT_FMAC_DPP(2, "quad_perm:[2,3,0,1]") QIFT_FMAC_DPP(3, "quad_perm:[2,3,0,1]")
+        QIFT_FMAC_DPP(4, "quad_perm:[2,3,0,1]") QIFT_FMAC_DPP(5, "quad_perm:[2,3,0,1]")
+        QIFT_FMAC_DPP(6, "quad_perm:[2,3,0,1]") QIFT_FMAC_DPP(7, "quad_perm:[2,3,0,1]")
+        : "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3]), "+v"(v[4]), "+v"(v[5]), "+v"(v[6]),
+          "+v"(v[7])
+        : "v"(c));
+  }
+}
+#undef QIFT_FMAC_DPP
+
+// kFull: the Hadamard block is the whole head vector (every stage runs; the
+// common case), so the stage conditions are compile-time constants.
+template <int E, int L, bool kFull, typename T>
 __global__ __launch_bounds__(kKvThreads) void kv4_kernel(const T* __restrict__ KV, int64_t rows,
                                                          int log2b, float norm,
                                                          uint8_t* __restrict__ kvq,
                                                          float* __restrict__ scales) {
+  static_assert(L == 1 || L == 2 || L == 4, "a head vector stays inside one quad");
   constexpr int D = E * L;
-  constexpr int kLogE = E == 32 ? 5 : 4;
+  constexpr int kLogE = E == 64 ? 6 : (E == 32 ? 5 : 4);
   const int lane = threadIdx.x & (L - 1);
   const int64_t r = (int64_t)blockIdx.x * (kKvThreads / L) + threadIdx.x / L;
-  const bool live = r < rows;
+  const bool live = r < rows;  // uniform over the quad
+  // a row past the end reads the last row; its results are not stored
   float v[E];
-  if (live) {
-    kv4_load<E, T>(KV + r * D + lane * E, v);
-  } else {
-#pragma unroll
-    for (int j = 0; j < E; ++j) v[j] = 0.f;
-  }
+  kv4_load<E, T>(KV + (live ? r : rows - 1) * D + lane * E, v);
   // in-lane stages (strides 1 .. E/2)
 #pragma unroll
   for (int st = 0; st < kLogE; ++st) {
-    if (st < log2b) {
+    if (kFull || st < log2b) {
       const int h = 1 << st;
 #pragma unroll
       for (int j = 0; j < E; ++j) {
@@ -71,16 +119,22 @@ __global__ __launch_bounds__(kKvThreads) void kv4_kernel(const T* __restrict__ K
       }
     }
   }
-  // cross-lane stages (strides E .. B/2): partner lane = lane ^ h
+  // cross-lane stages (strides E, 2E), values kept up to the sign sigma
+  float sigma = 1.f;
+  if constexpr (L >= 2) {
+    if (kFull || E < (1 << log2b)) {
+      const float c = (lane & 1) ? -1.f : 1.f;
 #pragma unroll
-  for (int h = 1; h < L; h <<= 1) {
-    if ((E * h) < (1 << log2b)) {
-      const bool upper = (lane & h) != 0;
+      for (int j = 0; j < E; j += 8) quad_butterfly8<1>(v + j, c);
+      sigma = c;
+    }
+  }
+  if constexpr (L == 4) {
+    if (kFull || 2 * E < (1 << log2b)) {
+      const float c = (lane & 2) ? -1.f : 1.f;
 #pragma unroll
-      for (int j = 0; j < E; ++j) {
-        const float o = __shfl_xor(v[j], h, 64);
-        v[j] = upper ? (o - v[j]) : (v[j] + o);
-      }
+      for (int j = 0; j < E; j += 8) quad_butterfly8<2>(v + j, c);
+      sigma *= c;
     }
   }
   float m = 0.f;
@@ -89,40 +143,64 @@ __global__ __launch_bounds__(kKvThreads) void kv4_kernel(const T* __restrict__ K
     v[j] *= norm;
     m = fmaxf(m, fabsf(v[j]));
   }
-#pragma unroll
-  for (int off = 1; off < L; off <<= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
+  if constexpr (L >= 2) m = fmaxf(m, quad_xor<1>(m));
+  if constexpr (L == 4) m = fmaxf(m, quad_xor<2>(m));
   const float s = __fdiv_rn(m, 7.0f);
   const float rs = s != 0.f ? __fdiv_rn(1.0f, s) : 0.f;
+  const float rl = sigma * rs;  // stored * rl == true value * rs, exactly
   uint32_t words[E / 8];
+  float dmax = 0.f;
 #pragma unroll
   for (int w = 0; w < E / 8; ++w) {
-    uint32_t word = 0;
+    float y[8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j)
-      word |= code_int4_recip(v[8 * w + j], s, rs) << (4 * j);
-    words[w] = word;
+    for (int j = 0; j < 8; ++j) y[j] = v[8 * w + j] * rl;
+    words[w] = int4x8_rint(y, dmax);
+  }
+  if (!(dmax <= 0.49999f) || !rint_path_ok(rs)) {
+    // a value within 1e-5 of a rounding tie (rare): exact division
+#pragma unroll
+    for (int w = 0; w < E / 8; ++w) {
+      float x[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) x[j] = sigma * v[8 * w + j];
+      words[w] = int4x8_exact(x, s);
+    }
   }
   if (live) {
     uint8_t* dst = kvq + r * (D / 2) + lane * (E / 2);
-    if constexpr (E == 32)
+    if constexpr (E == 64) {
+      reinterpret_cast<uint4*>(dst)[0] = uint4{words[0], words[1], words[2], words[3]};
+      reinterpret_cast<uint4*>(dst)[1] = uint4{words[4], words[5], words[6], words[7]};
+    } else if constexpr (E == 32) {
       *reinterpret_cast<uint4*>(dst) = uint4{words[0], words[1], words[2], words[3]};
-    else
+    } else {
       *reinterpret_cast<uint2*>(dst) = uint2{words[0], words[1]};
+    }
     if (lane == 0) scales[r] = s;
   }
+}
+
+template <int E, int L, bool kFull>
+static void launch_kv4_f(const void* KV, int bf16, int64_t rows, int log2b, float norm,
+                         uint8_t* kvq, float* scales, hipStream_t s) {
+  const int per_block = kKvThreads / L;
+  const unsigned grid = (unsigned)((rows + per_block - 1) / per_block);
+  if (bf16)
+    hipLaunchKernelGGL((kv4_kernel<E, L, kFull, uint16_t>), dim3(grid), dim3(kKvThreads), 0, s,
+                       reinterpret_cast<const uint16_t*>(KV), rows, log2b, norm, kvq, scales);
+  else
+    hipLaunchKernelGGL((kv4_kernel<E, L, kFull, float>), dim3(grid), dim3(kKvThreads), 0, s,
+                       reinterpret_cast<const float*>(KV), rows, log2b, norm, kvq, scales);
 }
 
 template <int E, int L>
 static void launch_kv4_l(const void* KV, int bf16, int64_t rows, int log2b, float norm,
                          uint8_t* kvq, float* scales, hipStream_t s) {
-  const int per_block = kKvThreads / L;
-  const unsigned grid = (unsigned)((rows + per_block - 1) / per_block);
-  if (bf16)
-    hipLaunchKernelGGL((kv4_kernel<E, L, uint16_t>), dim3(grid), dim3(kKvThreads), 0, s,
-                       reinterpret_cast<const uint16_t*>(KV), rows, log2b, norm, kvq, scales);
+  if ((1 << log2b) == E * L)
+    launch_kv4_f<E, L, true>(KV, bf16, rows, log2b, norm, kvq, scales, s);
   else
-    hipLaunchKernelGGL((kv4_kernel<E, L, float>), dim3(grid), dim3(kKvThreads), 0, s,
-                       reinterpret_cast<const float*>(KV), rows, log2b, norm, kvq, scales);
+    launch_kv4_f<E, L, false>(KV, bf16, rows, log2b, norm, kvq, scales, s);
 }
 
 hipError_t launch_kv4(const void* KV, int bf16, int64_t rows, int D, int had_block, uint8_t* kvq,
@@ -135,7 +213,7 @@ hipError_t launch_kv4(const void* KV, int bf16, int64_t rows, int D, int had_blo
     case 32: launch_kv4_l<32, 1>(KV, bf16, rows, log2b, norm, kvq, scales, s); break;
     case 64: launch_kv4_l<32, 2>(KV, bf16, rows, log2b, norm, kvq, scales, s); break;
     case 128: launch_kv4_l<32, 4>(KV, bf16, rows, log2b, norm, kvq, scales, s); break;
-    case 256: launch_kv4_l<32, 8>(KV, bf16, rows, log2b, norm, kvq, scales, s); break;
+    case 256: launch_kv4_l<64, 4>(KV, bf16, rows, log2b, norm, kvq, scales, s); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -10,7 +10,7 @@
 // butterflies run in passes of up to four stages, each pass keeping 16 (or
 // fewer) elements in registers, so a block of 4096 takes three LDS round
 // trips instead of twelve.
-#include "qift_internal.h"
+#include "quant_pack.h"
 
 namespace qift {
 
@@ -187,8 +187,10 @@ __global__ __launch_bounds__(kRowThreads) void rotate_quant_act_kernel(
 
 __device__ __forceinline__ int pad16(int e) { return e + (e >> 4); }
 
-template <int NS>
-__device__ __forceinline__ void fwht_pass_padded(float* row, int K, int p, int tid) {
+// kMax: also raise m to the largest |value| the pass writes
+template <int NS, bool kMax = false>
+__device__ __forceinline__ void fwht_pass_padded(float* row, int K, int p, int tid,
+                                                 float* m = nullptr) {
   constexpr int R = 1 << NS;
   const int sh = 4 * p;
   const int S = 1 << sh;
@@ -214,6 +216,10 @@ __device__ __forceinline__ void fwht_pass_padded(float* row, int K, int p, int t
     }
 #pragma unroll
     for (int j = 0; j < R; ++j) row[pad16(base + j * S)] = v[j];
+    if constexpr (kMax) {
+#pragma unroll
+      for (int j = 0; j < R; ++j) *m = fmaxf(*m, fabsf(v[j]));
+    }
   }
 }
 
@@ -267,6 +273,7 @@ __device__ __forceinline__ void rotate_row_fast(const T* __restrict__ src, int K
     const int grp = tid + q * kRowThreads;
     load16<T>(src + 16 * (grp < groups ? grp : 0), v[q]);
   }
+  float mloc = 0.f;  // largest |value| this thread wrote in the last stage
 #pragma unroll
   for (int q = 0; q < kFastMaxGroups; ++q) {
     const int grp = tid + q * kRowThreads;
@@ -286,27 +293,35 @@ __device__ __forceinline__ void rotate_row_fast(const T* __restrict__ src, int K
       float* dst = row + 17 * grp;
 #pragma unroll
       for (int j = 0; j < 16; ++j) dst[j] = v[q][j];
-    }
-  }
-  __syncthreads();
-  // 2. stages 4.. through padded LDS
-  for (int p = 1; 4 * p < log2b; ++p) {
-    const int ns = min(4, log2b - 4 * p);
-    switch (ns) {
-      case 1: fwht_pass_padded<1>(row, K, p, tid); break;
-      case 2: fwht_pass_padded<2>(row, K, p, tid); break;
-      case 3: fwht_pass_padded<3>(row, K, p, tid); break;
-      default: fwht_pass_padded<4>(row, K, p, tid); break;
-    }
-    __syncthreads();
-  }
-  // 3. absmax over the row, then quantize 16 consecutive elements per thread
-  float mloc = 0.f;
-  for (int grp = tid; grp < groups; grp += kRowThreads) {
-    const float* s16 = row + 17 * grp;
+      if (log2b <= 4) {
 #pragma unroll
-    for (int j = 0; j < 16; ++j) mloc = fmaxf(mloc, fabsf(s16[j]));
+        for (int j = 0; j < 16; ++j) mloc = fmaxf(mloc, fabsf(v[q][j]));
+      }
+    }
   }
+  // 2. stages 4.. through padded LDS; the last pass also takes the absmax
+  for (int p = 1; 4 * p < log2b; ++p) {
+    __syncthreads();
+    const int ns = min(4, log2b - 4 * p);
+    const bool last = 4 * (p + 1) >= log2b;
+    if (last) {
+      switch (ns) {
+        case 1: fwht_pass_padded<1, true>(row, K, p, tid, &mloc); break;
+        case 2: fwht_pass_padded<2, true>(row, K, p, tid, &mloc); break;
+        case 3: fwht_pass_padded<3, true>(row, K, p, tid, &mloc); break;
+        default: fwht_pass_padded<4, true>(row, K, p, tid, &mloc); break;
+      }
+    } else {
+      switch (ns) {
+        case 1: fwht_pass_padded<1>(row, K, p, tid); break;
+        case 2: fwht_pass_padded<2>(row, K, p, tid); break;
+        case 3: fwht_pass_padded<3>(row, K, p, tid); break;
+        default: fwht_pass_padded<4>(row, K, p, tid); break;
+      }
+    }
+  }
+  // 3. row absmax (the barrier also completes the last pass), then each
+  //    thread quantizes 16 consecutive elements
   mloc *= norm;  // rounding is monotonic: max(|v|)*norm == max(|v*norm|)
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) mloc = fmaxf(mloc, __shfl_xor(mloc, off, 64));
@@ -317,18 +332,23 @@ __device__ __forceinline__ void rotate_row_fast(const T* __restrict__ src, int K
   for (int w = 1; w < kRowThreads / 64; ++w) amax = fmaxf(amax, red[w]);
   const float s = __fdiv_rn(amax, 7.0f);
   const float rs = s != 0.f ? __fdiv_rn(1.0f, s) : 0.f;
+  const bool fast = rint_path_ok(rs);
   if (tid == 0) *s_out = s;
   uint2* xrow = reinterpret_cast<uint2*>(xq_row);
   for (int grp = tid; grp < groups; grp += kRowThreads) {
     const float* s16 = row + 17 * grp;
-    float x[16];
+    float x[16], y[16];
 #pragma unroll
-    for (int j = 0; j < 16; ++j) x[j] = s16[j] * norm;
-    uint32_t w0 = 0, w1 = 0;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      w0 |= code_int4_recip(x[j], s, rs) << (4 * j);
-      w1 |= code_int4_recip(x[8 + j], s, rs) << (4 * j);
+    for (int j = 0; j < 16; ++j) {
+      x[j] = s16[j] * norm;
+      y[j] = x[j] * rs;
+    }
+    float dmax = 0.f;
+    uint32_t w0 = int4x8_rint(y, dmax);
+    uint32_t w1 = int4x8_rint(y + 8, dmax);
+    if (!(dmax <= 0.49999f) || !fast) {  // a value near a rounding tie: exact division
+      w0 = int4x8_exact(x, s);
+      w1 = int4x8_exact(x + 8, s);
     }
     xrow[grp] = uint2{w0, w1};
     if (xrot_row) {

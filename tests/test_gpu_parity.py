@@ -345,6 +345,38 @@ def test_kv4_matches_oracle(D, B):
         assert np.array_equal(qg, qo.astype(np.int64))
 
 
+@pytest.mark.parametrize("D", [16, 64, 256])
+def test_kv4_exact_ties_after_rotation(D):
+    """Head vectors whose rotated values are exact rounding ties: z holds
+    half-integers times 2^e with max |z| = 7 * 2^e, and the input is
+    x = H_D z / sqrt(D), which the float32 butterflies map back to z exactly
+    (every partial sum is a short dyadic number; 1/sqrt(D) is a power of two
+    for D = 16, 64, 256). So s = 2^e exactly and x'/s are the ties, which
+    round half to even; D = 64 and 256 run the cross-lane stages."""
+    base = np.array([7.0, 0.5, 1.5, 2.5, 3.5, -0.5, -1.5, -2.5, 6.5, -7.0, 4.5, 5.5, -3.5, -4.5,
+                     -5.5, -6.5])
+    rng = np.random.default_rng(D)
+    rows = []
+    for e in (-3, 0, 5):
+        for _ in range(3):
+            z = np.concatenate([rng.permutation(base) for _ in range(D // 16)]) * 2.0 ** e
+            rows.append(z)
+    Z = np.stack(rows)
+    Hd = np.array([[(-1) ** bin(i & j).count("1") for j in range(D)] for i in range(D)], float)
+    X = (Z @ Hd.T) / np.sqrt(D)
+    assert np.array_equal(X.astype(np.float32).astype(np.float64), X)  # exact in float32
+    KV = X.reshape(len(rows), 1, D).astype(np.float32)
+    say(f"kv4 exact ties D={D}")
+    kvq, sc = q.qift_kv4_quant(to_dev(KV), D)
+    sync()
+    qg = O.unpack_int4(kvq.cpu().numpy()).reshape(len(rows), D)
+    expect = np.rint(Z / (Z.max(axis=1, keepdims=True) / 7.0))  # numpy rint: half to even
+    assert np.array_equal(qg, expect.astype(np.int64))
+    assert np.array_equal(sc.cpu().numpy().reshape(-1), Z.max(axis=1) / 7.0)
+    qo, so, _ = O.kv4_quant(KV.astype(np.float64), D)
+    assert np.array_equal(qg, qo.reshape(len(rows), D).astype(np.int64))
+
+
 def test_kv4_bitexact_given_rotated_input():
     T, H, D = 9, 4, 128
     KV = si.kv(T, H, D, seed=3)
