@@ -11,16 +11,12 @@
 // codes. The kernel is bound by HBM bandwidth in principle and by VALU issue
 // in practice, so every step is written for the fewest instructions per
 // element:
-//  - a cross-lane butterfly costs one fused multiply-add per element: each
-//    lane keeps its values up to a sign sigma (true = sigma * stored). For
-//    partners with equal sigma, the lower lane's new value is
-//    stored + partner and the upper lane's is partner - stored
-//    = -(stored - partner); the upper lane therefore stores
-//    fma(partner, -1, stored) and flips its sigma. The results are the same
-//    float32 values as the plain butterfly, up to that sign;
+//  - a cross-lane butterfly costs one DPP-fed fused multiply-add per element
+//    (lane_butterfly8: each lane keeps its values up to a sign sigma);
 //  - the absmax ignores the sign; the quantizer folds sigma into 1 / s;
 //  - rounding and packing use the float adder and byte permutes
 //    (int4x8_rint), with the exact division only for near-tie groups.
+#include "lane_butterfly.h"
 #include "quant_pack.h"
 
 namespace qift {
@@ -51,42 +47,6 @@ __device__ __forceinline__ void kv4_load(const T* __restrict__ src, float v[E]) 
     }
   }
 }
-
-// value of lane (lane ^ H) of the same quad, H in {1, 2} (DPP quad_perm)
-template <int H>
-__device__ __forceinline__ float quad_xor(float x) {
-  constexpr int kCtrl = H == 1 ? 0xB1 : 0x4E;  // [1,0,3,2] or [2,3,0,1]
-  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), kCtrl, 0xF, 0xF, true));
-}
-
-// Cross-lane butterfly of eight values: v[j] = v[j] of lane (lane ^ H) * c +
-// v[j], one v_fmac_f32 with a DPP quad permutation of its first source per
-// value (the compiler keeps the permutation as a separate v_mov_b32_dpp and
-// a three-operand fma). The leading s_nop covers the two wait states a DPP
-// source needs after a VALU write; inside the block each instruction reads a
-// register no earlier instruction of the block wrote.
-#define QIFT_FMAC_DPP(i, PERM) "v_fmac_f32_dpp %" #i ", %" #i ", %8 " PERM " row_mask:0xf bank_mask:0xf\n\t"
-template <int H>
-__device__ __forceinline__ void quad_butterfly8(float* v, float c) {
-  if constexpr (H == 1) {
-    asm("s_nop 1\n\t" QIFT_FMAC_DPP(0, "quad_perm:[1,0,3,2]") QIFT_FMAC_DPP(1, "quad_perm:[1,0,3,2]")
-        QIFT_FMAC_DPP(2, "quad_perm:[1,0,3,2]") QIFT_FMAC_DPP(3, "quad_perm:[1,0,3,2]")
-        QIFT_FMAC_DPP(4, "quad_perm:[1,0,3,2]") QIFT_FMAC_DPP(5, "quad_perm:[1,0,3,2]")
-        QIFT_FMAC_DPP(6, "quad_perm:[1,0,3,2]") QIFT_FMAC_DPP(7, "quad_perm:[1,0,3,2]")
-        : "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3]), "+v"(v[4]), "+v"(v[5]), "+v"(v[6]),
-          "+v"(v[7])
-        : "v"(c));
-  } else {
-    asm("s_nop 1\n\t" QIFT_FMAC_DPP(0, "quad_perm:[2,3,0,1]") QIFT_FMAC_DPP(1, "quad_perm:[2,3,0,1]")
-        QIFT_FMAC_DPP(2, "quad_perm:[2,3,0,1]") QIFT_FMAC_DPP(3, "quad_perm:[2,3,0,1]")
-        QIFT_FMAC_DPP(4, "quad_perm:[2,3,0,1]") QIFT_FMAC_DPP(5, "quad_perm:[2,3,0,1]")
-        QIFT_FMAC_DPP(6, "quad_perm:[2,3,0,1]") QIFT_FMAC_DPP(7, "quad_perm:[2,3,0,1]")
-        : "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3]), "+v"(v[4]), "+v"(v[5]), "+v"(v[6]),
-          "+v"(v[7])
-        : "v"(c));
-  }
-}
-#undef QIFT_FMAC_DPP
 
 // kFull: the Hadamard block is the whole head vector (every stage runs; the
 // common case), so the stage conditions are compile-time constants.
@@ -125,7 +85,7 @@ __global__ __launch_bounds__(kKvThreads) void kv4_kernel(const T* __restrict__ K
     if (kFull || E < (1 << log2b)) {
       const float c = (lane & 1) ? -1.f : 1.f;
 #pragma unroll
-      for (int j = 0; j < E; j += 8) quad_butterfly8<1>(v + j, c);
+      for (int j = 0; j < E; j += 8) lane_butterfly8<1>(v + j, c);
       sigma = c;
     }
   }
@@ -133,7 +93,7 @@ __global__ __launch_bounds__(kKvThreads) void kv4_kernel(const T* __restrict__ K
     if (kFull || 2 * E < (1 << log2b)) {
       const float c = (lane & 2) ? -1.f : 1.f;
 #pragma unroll
-      for (int j = 0; j < E; j += 8) quad_butterfly8<2>(v + j, c);
+      for (int j = 0; j < E; j += 8) lane_butterfly8<2>(v + j, c);
       sigma *= c;
     }
   }

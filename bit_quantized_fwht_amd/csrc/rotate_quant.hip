@@ -6,10 +6,11 @@
 // Source of the method: "Qift: Shift-Friendly No-Zero W2 Post-Training
 // Quantization for Rotated W2A4/KV4 LLM Inference", abstract.
 //
-// One workgroup handles one row. The row is staged in LDS as float32; the
-// butterflies run in passes of up to four stages, each pass keeping 16 (or
-// fewer) elements in registers, so a block of 4096 takes three LDS round
-// trips instead of twelve.
+// One workgroup handles one row. The general kernels stage the row in LDS as
+// float32 and run the butterflies in passes of up to four stages, each pass
+// keeping 16 (or fewer) elements in registers; the activation fast path keeps
+// the row in registers for the first eight stages (see below).
+#include "lane_butterfly.h"
 #include "quant_pack.h"
 
 namespace qift {
@@ -174,16 +175,15 @@ __global__ __launch_bounds__(kRowThreads) void rotate_quant_act_kernel(
 
 // --- K1 fast path: K % 16 == 0 and block >= 16 ---------------------------------
 //
-// Element e of the row lives in LDS at e + e / 16 (one pad word per 16
-// floats). Each thread owns groups of 16 consecutive elements:
-//  1. global load (32 bytes bf16 / 64 bytes float) straight into registers,
-//     butterfly stages 0-3 in registers, padded store (the 16 stores of a
-//     thread hit 16 consecutive banks; neighbouring threads are 17 words
-//     apart, so a wave's stores are conflict-free);
-//  2. remaining stages in passes of up to four through LDS (padded, so the
-//     stride-16 and stride-256 passes are conflict-free as well);
-//  3. each thread reads its 16 consecutive elements back, the row absmax is
-//     reduced, and the thread quantizes and stores 16 codes as 8 bytes.
+// Each thread owns groups of 16 consecutive elements, loaded straight into
+// registers (32 bytes bf16 / 64 bytes float). Butterfly stages 0-3 run inside
+// a group and stages 4-7 between the lanes holding neighbouring groups
+// (rotate_row_fast below), so rows with blocks up to 256 never touch LDS.
+// For larger blocks the row is staged in LDS with one pad word per 16 floats
+// (element e at e + e / 16): the 16 stores of a thread hit 16 consecutive
+// banks and neighbouring threads are 17 words apart, so a wave's stores, the
+// stride-256 pass of stages 8-11 and the final consecutive reads are all
+// conflict-free.
 
 __device__ __forceinline__ int pad16(int e) { return e + (e >> 4); }
 
@@ -254,8 +254,19 @@ __device__ __forceinline__ void load16<float>(const float* __restrict__ src, flo
 // 16 consecutive elements (at most kFastMaxGroups of them, K <= 16384); all
 // of its global loads are issued before any group is transformed, so a long
 // row costs one memory latency rather than one per group.
+//  - stages 0..3 (strides 1..8) inside a group, in registers;
+//  - stages 4..7 (strides 16..128 = groups 1..8 apart = lanes 1..8 apart)
+//    between lanes with DPP (lane_butterfly8; values kept up to a per-lane
+//    sign sigma);
+//  - blocks up to 256: the row never goes through LDS; absmax and
+//    quantization work on the registers;
+//  - larger blocks: the true values go to a padded LDS row, stages 8..11 run
+//    in one pass through it, and the quantization reads the row back.
 constexpr int kFastMaxGroups = 4;
 static_assert(kFastMaxGroups * 16 * kRowThreads >= QIFT_MAX_ROW, "fast path covers QIFT_MAX_ROW");
+
+// rows with log2(block) <= kRegLog2B need no LDS row buffer
+constexpr int kRegLog2B = 8;
 
 template <typename T>
 __device__ __forceinline__ void rotate_row_fast(const T* __restrict__ src, int K, int log2b,
@@ -265,19 +276,20 @@ __device__ __forceinline__ void rotate_row_fast(const T* __restrict__ src, int K
                                                 float* red) {
   const int tid = threadIdx.x;
   const int groups = K >> 4;
-  // 1. loads (a group past the row end reads group 0 and is discarded), then
-  //    stages 0..3 in registers and the padded LDS store
+  const int wave_g0 = tid & ~63;  // the wave's first group of round 0
+  // 1. loads (a group past the row end reads group 0 and is discarded)
   float v[kFastMaxGroups][16];
 #pragma unroll
   for (int q = 0; q < kFastMaxGroups; ++q) {
     const int grp = tid + q * kRowThreads;
     load16<T>(src + 16 * (grp < groups ? grp : 0), v[q]);
   }
-  float mloc = 0.f;  // largest |value| this thread wrote in the last stage
+  // 2. stages 0..3 in registers (rounds with no group of this wave skipped;
+  //    a partner group of a valid group is always valid, since K is a
+  //    multiple of the block)
 #pragma unroll
   for (int q = 0; q < kFastMaxGroups; ++q) {
-    const int grp = tid + q * kRowThreads;
-    if (grp < groups) {
+    if (wave_g0 + q * kRowThreads < groups) {
 #pragma unroll
       for (int st = 0; st < 4; ++st) {
         const int h = 1 << st;
@@ -290,38 +302,57 @@ __device__ __forceinline__ void rotate_row_fast(const T* __restrict__ src, int K
           }
         }
       }
-      float* dst = row + 17 * grp;
+    }
+  }
+  // 3. stages 4..7 between lanes
+  float sigma = 1.f;
+  const int lane_stages = min(log2b, kRegLog2B) - 4;
+#define QIFT_LANE_STAGE(H)                                                 \
+  {                                                                        \
+    const float c = (tid & (H)) ? -1.f : 1.f;                              \
+    _Pragma("unroll") for (int q = 0; q < kFastMaxGroups; ++q) {           \
+      if (wave_g0 + q * kRowThreads < groups) {                            \
+        lane_butterfly8<H>(v[q], c);                                       \
+        lane_butterfly8<H>(v[q] + 8, c);                                   \
+      }                                                                    \
+    }                                                                      \
+    sigma *= c;                                                            \
+  }
+  if (lane_stages >= 1) QIFT_LANE_STAGE(1)
+  if (lane_stages >= 2) QIFT_LANE_STAGE(2)
+  if (lane_stages >= 3) QIFT_LANE_STAGE(4)
+  if (lane_stages >= 4) QIFT_LANE_STAGE(8)
+#undef QIFT_LANE_STAGE
+  const bool in_regs = log2b <= kRegLog2B;
+  float mloc = 0.f;  // largest |value| of the row's last stage seen by this thread
+  if (in_regs) {
 #pragma unroll
-      for (int j = 0; j < 16; ++j) dst[j] = v[q][j];
-      if (log2b <= 4) {
+    for (int q = 0; q < kFastMaxGroups; ++q) {
+      if (tid + q * kRowThreads < groups) {
 #pragma unroll
         for (int j = 0; j < 16; ++j) mloc = fmaxf(mloc, fabsf(v[q][j]));
       }
     }
-  }
-  // 2. stages 4.. through padded LDS; the last pass also takes the absmax
-  for (int p = 1; 4 * p < log2b; ++p) {
-    __syncthreads();
-    const int ns = min(4, log2b - 4 * p);
-    const bool last = 4 * (p + 1) >= log2b;
-    if (last) {
-      switch (ns) {
-        case 1: fwht_pass_padded<1, true>(row, K, p, tid, &mloc); break;
-        case 2: fwht_pass_padded<2, true>(row, K, p, tid, &mloc); break;
-        case 3: fwht_pass_padded<3, true>(row, K, p, tid, &mloc); break;
-        default: fwht_pass_padded<4, true>(row, K, p, tid, &mloc); break;
-      }
-    } else {
-      switch (ns) {
-        case 1: fwht_pass_padded<1>(row, K, p, tid); break;
-        case 2: fwht_pass_padded<2>(row, K, p, tid); break;
-        case 3: fwht_pass_padded<3>(row, K, p, tid); break;
-        default: fwht_pass_padded<4>(row, K, p, tid); break;
+  } else {
+    // 4. stages 8.. in one pass through the padded LDS row
+#pragma unroll
+    for (int q = 0; q < kFastMaxGroups; ++q) {
+      const int grp = tid + q * kRowThreads;
+      if (grp < groups) {
+        float* dst = row + 17 * grp;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) dst[j] = sigma * v[q][j];
       }
     }
+    __syncthreads();
+    switch (log2b - 8) {
+      case 1: fwht_pass_padded<1, true>(row, K, 2, tid, &mloc); break;
+      case 2: fwht_pass_padded<2, true>(row, K, 2, tid, &mloc); break;
+      case 3: fwht_pass_padded<3, true>(row, K, 2, tid, &mloc); break;
+      default: fwht_pass_padded<4, true>(row, K, 2, tid, &mloc); break;
+    }
   }
-  // 3. row absmax (the barrier also completes the last pass), then each
-  //    thread quantizes 16 consecutive elements
+  // 5. row absmax (for the LDS path the barrier also completes the pass)
   mloc *= norm;  // rounding is monotonic: max(|v|)*norm == max(|v*norm|)
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) mloc = fmaxf(mloc, __shfl_xor(mloc, off, 64));
@@ -334,28 +365,46 @@ __device__ __forceinline__ void rotate_row_fast(const T* __restrict__ src, int K
   const float rs = s != 0.f ? __fdiv_rn(1.0f, s) : 0.f;
   const bool fast = rint_path_ok(rs);
   if (tid == 0) *s_out = s;
+  // 6. quantize 16 consecutive elements per group: x = the rotated value up
+  //    to sigma (sigma = 1 on the LDS path), y = x * sigma / s
+  const float sg = in_regs ? sigma : 1.f;
+  const float rl = sg * rs;
   uint2* xrow = reinterpret_cast<uint2*>(xq_row);
-  for (int grp = tid; grp < groups; grp += kRowThreads) {
-    const float* s16 = row + 17 * grp;
-    float x[16], y[16];
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      x[j] = s16[j] * norm;
-      y[j] = x[j] * rs;
+  for (int q = 0; q < kFastMaxGroups; ++q) {
+    const int grp = tid + q * kRowThreads;
+    if (grp >= groups) continue;
+    float x[16], y[16];
+    if (in_regs) {
+#pragma unroll
+      for (int j = 0; j < 16; ++j) x[j] = v[q][j] * norm;
+    } else {
+      const float* s16 = row + 17 * grp;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) x[j] = s16[j] * norm;
     }
+#pragma unroll
+    for (int j = 0; j < 16; ++j) y[j] = x[j] * rl;
     float dmax = 0.f;
     uint32_t w0 = int4x8_rint(y, dmax);
     uint32_t w1 = int4x8_rint(y + 8, dmax);
-    if (!(dmax <= 0.49999f) || !fast) {  // a value near a rounding tie: exact division
-      w0 = int4x8_exact(x, s);
-      w1 = int4x8_exact(x + 8, s);
+    if (!(dmax <= 0.49999f) || !fast || xrot_row) {
+      // the true rotated values; fma(x, sg, +0) also writes every zero as
+      // +0 (an upper lane's x - x comes back as -0 through its sign)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) x[j] = __builtin_fmaf(x[j], sg, 0.0f);
+      if (!(dmax <= 0.49999f) || !fast) {  // a value near a rounding tie: exact division
+        w0 = int4x8_exact(x, s);
+        w1 = int4x8_exact(x + 8, s);
+      }
+      if (xrot_row) {
+        float4* xr = reinterpret_cast<float4*>(xrot_row + 16 * grp);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          xr[i] = float4{x[4 * i], x[4 * i + 1], x[4 * i + 2], x[4 * i + 3]};
+      }
     }
     xrow[grp] = uint2{w0, w1};
-    if (xrot_row) {
-      float4* xr = reinterpret_cast<float4*>(xrot_row + 16 * grp);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) xr[i] = float4{x[4 * i], x[4 * i + 1], x[4 * i + 2], x[4 * i + 3]};
-    }
   }
 }
 
@@ -502,7 +551,7 @@ hipError_t launch_rotate_quant_act(const void* X, int x_bf16, int64_t M, int64_t
   const int lb = ilog2(had_block);
   const float nrm = had_norm(had_block);
   if (rotate_fast_ok(X, K, had_block, xq, x_rot)) {
-    const size_t lds = (size_t)(K + K / 16) * sizeof(float);
+    const size_t lds = lb > kRegLog2B ? (size_t)(K + K / 16) * sizeof(float) : 0;
     if (x_bf16)
       hipLaunchKernelGGL(rotate_quant_act_fast_kernel<uint16_t>, dim3((unsigned)M),
                          dim3(kRowThreads), lds, s, reinterpret_cast<const uint16_t*>(X), (int)K,
@@ -542,7 +591,7 @@ hipError_t launch_rotate_quant_act_batched(const RotJob* jobs, const int64_t* ro
     bt.job[j].norm = had_norm(jobs[j].had_block);
     bt.row_begin[j] = total;
     total += rows[j];
-    kmax = jobs[j].K > kmax ? jobs[j].K : kmax;
+    if (bt.job[j].log2b > kRegLog2B && rows[j] > 0) kmax = jobs[j].K > kmax ? jobs[j].K : kmax;
   }
   for (int j = count; j <= QIFT_MAX_ROTATE_BATCH; ++j) bt.row_begin[j] = total;
   if (total == 0) return hipSuccess;

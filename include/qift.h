@@ -138,6 +138,7 @@ qift_status qift_quantize_weights(const void* W, qift_dtype w_dtype, int64_t N, 
  *   xq     out: [M, K/2] int4 pairs (layout above)
  *   s_a    out: [M] float32
  *   x_rot  out, optional (may be NULL): [M, K] float32 rotated activations
+ *          (a value that is exactly zero is written as +0)
  * M = 0 is a no-op.
  */
 qift_status qift_rotate_quant_act(const void* X, qift_dtype x_dtype, int64_t M, int64_t K,

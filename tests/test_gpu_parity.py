@@ -136,6 +136,38 @@ def test_rotate_rne_ties_and_zero_rows():
     assert sg[0] == 1.0 and sg[1] == 0.0 and np.all(qg[1] == 0)
 
 
+def exact_tie_rows(D, B, seed):
+    """Rows z of rounding ties (half-integers times 2^e, max |z| = 7 * 2^e)
+    and inputs x with x = H_B z / sqrt(B) blockwise, which float32
+    butterflies map back to z exactly (every partial sum is a short dyadic
+    number; 1/sqrt(B) is a power of two for even log2 B)."""
+    base = np.array([7.0, 0.5, 1.5, 2.5, 3.5, -0.5, -1.5, -2.5, 6.5, -7.0, 4.5, 5.5, -3.5, -4.5,
+                     -5.5, -6.5])
+    rng = np.random.default_rng(seed)
+    rows = []
+    for e in (-3, 0, 5):
+        for _ in range(3):
+            rows.append(np.concatenate([rng.permutation(base) for _ in range(D // 16)]) * 2.0 ** e)
+    Z = np.stack(rows)
+    Hb = np.array([[(-1) ** bin(i & j).count("1") for j in range(B)] for i in range(B)], float)
+    X = (Z.reshape(len(rows), D // B, B) @ Hb.T).reshape(len(rows), D) / np.sqrt(B)
+    assert np.array_equal(X.astype(np.float32).astype(np.float64), X)  # exact in float32
+    expect = np.rint(Z / (Z.max(axis=1, keepdims=True) / 7.0))  # numpy rint: half to even
+    return X.astype(np.float32), Z, expect.astype(np.int64)
+
+
+@pytest.mark.parametrize("K,B", [(64, 16), (256, 64), (512, 256), (2048, 1024)])
+def test_rotate_exact_ties_after_rotation(K, B):
+    """Rotated values that are exact rounding ties, through the in-lane,
+    cross-lane and (B = 1024) LDS stages: codes round half to even."""
+    X, Z, expect = exact_tie_rows(K, B, seed=K + B)
+    say(f"rotate exact ties K={K} B={B}")
+    qg, sg, xg = gpu_rotate(to_dev(X), B)
+    assert np.array_equal(xg.astype(np.float64), Z)
+    assert np.array_equal(sg, (Z.max(axis=1) / 7.0).astype(np.float32))
+    assert np.array_equal(qg, expect)
+
+
 def test_rotate_one_hot_closed_form():
     B, j, c = 4096, 1234, 2.5
     X = np.zeros((2, 2 * B), np.float32)
@@ -353,28 +385,16 @@ def test_kv4_exact_ties_after_rotation(D):
     (every partial sum is a short dyadic number; 1/sqrt(D) is a power of two
     for D = 16, 64, 256). So s = 2^e exactly and x'/s are the ties, which
     round half to even; D = 64 and 256 run the cross-lane stages."""
-    base = np.array([7.0, 0.5, 1.5, 2.5, 3.5, -0.5, -1.5, -2.5, 6.5, -7.0, 4.5, 5.5, -3.5, -4.5,
-                     -5.5, -6.5])
-    rng = np.random.default_rng(D)
-    rows = []
-    for e in (-3, 0, 5):
-        for _ in range(3):
-            z = np.concatenate([rng.permutation(base) for _ in range(D // 16)]) * 2.0 ** e
-            rows.append(z)
-    Z = np.stack(rows)
-    Hd = np.array([[(-1) ** bin(i & j).count("1") for j in range(D)] for i in range(D)], float)
-    X = (Z @ Hd.T) / np.sqrt(D)
-    assert np.array_equal(X.astype(np.float32).astype(np.float64), X)  # exact in float32
-    KV = X.reshape(len(rows), 1, D).astype(np.float32)
+    X, Z, expect = exact_tie_rows(D, D, seed=D)
+    KV = X.reshape(len(Z), 1, D)
     say(f"kv4 exact ties D={D}")
     kvq, sc = q.qift_kv4_quant(to_dev(KV), D)
     sync()
-    qg = O.unpack_int4(kvq.cpu().numpy()).reshape(len(rows), D)
-    expect = np.rint(Z / (Z.max(axis=1, keepdims=True) / 7.0))  # numpy rint: half to even
-    assert np.array_equal(qg, expect.astype(np.int64))
+    qg = O.unpack_int4(kvq.cpu().numpy()).reshape(len(Z), D)
+    assert np.array_equal(qg, expect)
     assert np.array_equal(sc.cpu().numpy().reshape(-1), Z.max(axis=1) / 7.0)
     qo, so, _ = O.kv4_quant(KV.astype(np.float64), D)
-    assert np.array_equal(qg, qo.reshape(len(rows), D).astype(np.int64))
+    assert np.array_equal(qg, qo.reshape(len(Z), D).astype(np.int64))
 
 
 def test_kv4_bitexact_given_rotated_input():
