@@ -42,6 +42,7 @@ __device__ __forceinline__ void decode_wave(const qift_linear_desc& d, int64_t n
   const int g = lane >> 4;
   const int64_t M = d.M, K = d.K, N = d.N;
   const int64_t cw = F::code_words(K);
+  const int64_t tiles = (N + 15) >> 4;
   const uint8_t* xq = d.xq;
   const uint32_t* codes = d.codes;
   const bool act_row = r16 < M;
@@ -62,13 +63,16 @@ __device__ __forceinline__ void decode_wave(const qift_linear_desc& d, int64_t n
   auto load = [&](Chunk& ch, int64_t t) {
     const int64_t kseg = t * F::kChunkK + (int64_t)g * F::kLaneK;
     const bool kval = t < nchunks && kseg < K;
-    // tiled layout: 16-channel tile (n0 + 16 i) / 16, chunk t, the lane's
-    // 16-byte unit at word 4 * lane -- one contiguous 1 KB per wave load
+    // chunk-major tiled layout: chunk t of all tiles at t * 256 * tiles;
+    // in it, tile (n0 + 16 i) / 16 holds 16 * ut words with the lane's
+    // 16-byte unit at word 4 * lane -- one contiguous 1 KB per full chunk,
+    // and the wave's four tiles are adjacent
+    const int64_t ut = cw - 16 * t < 16 ? cw - 16 * t : 16;
+    const uint32_t* cbase = codes + t * 256 * tiles + 4 * lane;
 #pragma unroll
     for (int i = 0; i < kDecodeTiles; ++i) {
       const int64_t tn = n0 + 16 * i;
-      ch.c[i] = (kval && tn < N) ? ld16_stream(codes + (tn >> 4) * 16 * cw + t * 256 + 4 * lane)
-                                 : uint4{0u, 0u, 0u, 0u};
+      ch.c[i] = (kval && tn < N) ? ld16_stream(cbase + (tn >> 4) * 16 * ut) : uint4{0u, 0u, 0u, 0u};
     }
     ch.a0 = uint4{0u, 0u, 0u, 0u};
     ch.a1 = uint4{0u, 0u, 0u, 0u};

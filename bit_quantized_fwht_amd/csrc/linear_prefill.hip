@@ -62,6 +62,7 @@ __device__ __forceinline__ void prefill_tile(const qift_linear_desc& d, int64_t 
   const int wn = (wave & 1) * (16 * kWaveTN);   // N side
   const int64_t M = d.M, K = d.K, N = d.N;
   const int64_t cw = F::code_words(K);
+  const int64_t tiles = (N + 15) >> 4;          // 16-channel weight tiles
   const int64_t arow = K / 2;                   // bytes per activation row
   const MnzMasks km = mnz_masks(d.reserved, lane);
   uint8_t* As = lds;                // stage buffer b: A at b * kStage, B after it
@@ -94,7 +95,9 @@ __device__ __forceinline__ void prefill_tile(const qift_linear_desc& d, int64_t 
       const int64_t tn = nt0 + 16 * (u >> 6);
       const int ul = u & 63;
       const bool ok = tn < N && k0 + (int64_t)(ul >> 4) * F::kLaneK < K;
-      const uint4 v = ld16(d.codes + (ok ? (tn >> 4) * 16 * cw + (k0 / C::kBK) * 256 + 4 * ul : 0));
+      const int64_t c = k0 / C::kBK;       // chunk (16 words per channel unless last)
+      const int64_t uc = cw - 16 * c < 16 ? cw - 16 * c : 16;
+      const uint4 v = ld16(d.codes + (ok ? c * 256 * tiles + (tn >> 4) * 16 * uc + 4 * ul : 0));
       rb[i] = ok ? v : uint4{0u, 0u, 0u, 0u};
     }
   };
@@ -344,7 +347,6 @@ __device__ __forceinline__ void prefill_tile_sk(const qift_linear_desc& d, int64
   const int kh = wave >> 1;              // which half of each stage's features
   const int wn = (wave & 1) * 64;        // the wave's 64 channels in the tile
   const int64_t M = d.M, K = d.K, N = d.N;
-  const int64_t cw = Fmt<LV>::code_words(K);
   const int64_t arow = K / 2;
   const int64_t np16 = (N + 15) >> 4;
   const MnzMasks km = mnz_masks(d.reserved, lane);
@@ -365,7 +367,7 @@ __device__ __forceinline__ void prefill_tile_sk(const qift_linear_desc& d, int64
     const int tile = unit_blk / C::kBChunks, chunk = unit_blk % C::kBChunks;
     int64_t t = (nt0 >> 4) + tile;
     t = t < np16 ? t : np16 - 1;          // tiles past N only feed discarded outputs
-    b_off[p] = t * 16 * cw + chunk * 256 + 4 * lane;
+    b_off[p] = chunk * 256 * np16 + t * 256 + 4 * lane;  // full chunks: K % 256 == 0
   }
   auto issue = [&](int64_t st, int buf) {
     uint8_t* as = lds + buf * C::kStage;
@@ -375,7 +377,8 @@ __device__ __forceinline__ void prefill_tile_sk(const qift_linear_desc& d, int64
       gl_lds16(d.xq + a_off[p] + st * 128, as + (wave * C::kAInstr + p) * 1024);
 #pragma unroll
     for (int p = 0; p < C::kBInstr; ++p)
-      gl_lds16(d.codes + b_off[p] + st * C::kBChunks * 256, bs + (wave * C::kBInstr + p) * 1024);
+      gl_lds16(d.codes + b_off[p] + st * C::kBChunks * 256 * np16,
+               bs + (wave * C::kBInstr + p) * 1024);
   };
 
   // written first by the first stage's MFMAs, whose accumulator input is

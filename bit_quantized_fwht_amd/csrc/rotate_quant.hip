@@ -473,14 +473,17 @@ __device__ __forceinline__ int code_bit_offset(int i) {
   return 8 * ((i >> 1) & 3) + 4 * (i >> 3) + 2 * (i & 1);
 }
 
-// Word w of channel row n in the 16-channel tiled weight layout (W words per
-// channel row): tile r = n / 16 holds 16 * W words; chunk c = w / 16 is 1 KB
-// (256 words) in which the 16-byte unit of lane (g, i) = ((w % 16) / 4, n % 16)
-// sits at word 4 * (16 g + i), word j = w % 4 inside it.
-__device__ __forceinline__ int64_t tiled_word(int64_t n, int64_t w, int64_t W) {
+// Word w of channel row n in the chunk-major tiled weight layout (W words per
+// channel row, T tiles of 16 channels): chunk c = w / 16 of all tiles comes
+// first, 256 T words for every full chunk; in chunk c (u_c = min(16, W - 16c)
+// words per channel) tile r = n / 16 holds 16 u_c words, in which the 16-byte
+// unit of lane (g, i) = ((w % 16) / 4, n % 16) sits at word 4 * (16 g + i),
+// word j = w % 4 inside it.
+__device__ __forceinline__ int64_t tiled_word(int64_t n, int64_t w, int64_t W, int64_t T) {
   const int64_t r = n >> 4, i = n & 15;
   const int64_t c = w >> 4, g = (w >> 2) & 3, j = w & 3;
-  return r * 16 * W + c * 256 + (16 * g + i) * 4 + j;
+  const int64_t uc = W - 16 * c < 16 ? W - 16 * c : 16;
+  return c * 256 * T + r * 16 * uc + (16 * g + i) * 4 + j;
 }
 
 template <typename T>
@@ -493,8 +496,9 @@ __global__ __launch_bounds__(kRowThreads) void quantize_weights_kernel(
   const int64_t n = blockIdx.x;
   const bool int4 = levels == QIFT_LEVELS_INT4;
   const int64_t words = int4 ? K / 8 : K / 16;
+  const int64_t tiles = (N + 15) >> 4;
   if (n >= N) {  // zero codes for the padding channels of the last tile
-    for (int w = tid; w < words; w += kRowThreads) codes[tiled_word(n, w, words)] = 0u;
+    for (int w = tid; w < words; w += kRowThreads) codes[tiled_word(n, w, words, tiles)] = 0u;
     return;
   }
   load_row<T>(W + n * K, row, K, tid);
@@ -518,7 +522,7 @@ __global__ __launch_bounds__(kRowThreads) void quantize_weights_kernel(
 #pragma unroll
       for (int i = 0; i < 8; ++i)
         word |= ((uint32_t)quant_int4(row[8 * g + i] * norm, s) & 0xFu) << (4 * i);
-      codes[tiled_word(n, g, words)] = word;
+      codes[tiled_word(n, g, words, tiles)] = word;
     }
   } else {
     const bool pot = levels == QIFT_LEVELS_POT;
@@ -530,7 +534,7 @@ __global__ __launch_bounds__(kRowThreads) void quantize_weights_kernel(
         const uint32_t c = pot ? code_pot(w, s) : code_mnz(w, s);
         word |= c << code_bit_offset(i);
       }
-      codes[tiled_word(n, g, words)] = word;
+      codes[tiled_word(n, g, words, tiles)] = word;
     }
   }
 }

@@ -39,14 +39,18 @@
  *   to matrix-core operands with shifts and masks only.)
  * 4-bit weight codes, in-word layout: K/8 words per channel row in the int4
  *   order above (feature 8j + i at bits 4i of word j).
- * Weight buffers, tiled layout: channels are grouped in tiles of 16 and
- *   padded with zero codes to Np = ceil(N/16)*16; with W the words per channel
- *   row (K/16 or K/8), word w of channel n is stored at index
- *       (n/16) * 16*W  +  (w/16) * 256  +  (16*((w%16)/4) + n%16) * 4  +  w%4
- *   so each tile is 16*W contiguous words and every 1 KB chunk of a tile is
- *   the 64 16-byte units that one 64-lane wave loads for 16 channels x 256
- *   features (2-bit) or x 128 features (4-bit); a short last chunk keeps only
- *   its leading units. A weight buffer holds Np*W words.
+ * Weight buffers, tiled layout (chunk-major): channels are grouped in tiles
+ *   of 16 and padded with zero codes to Np = ceil(N/16)*16 (T = Np/16 tiles).
+ *   With W the words per channel row (K/16 or K/8), the row is cut into
+ *   chunks of 16 words (the last one may be shorter: u_c = min(16, W - 16c)
+ *   words); word w of channel n, with c = w/16, is stored at index
+ *       c * 256*T  +  (n/16) * 16*u_c  +  (16*((w%16)/4) + n%16) * 4  +  w%4
+ *   so chunk c of every tile comes before chunk c+1 of any tile, and inside
+ *   a chunk each tile holds the 16-byte units that one 64-lane wave loads for
+ *   16 channels x 256 features (2-bit) or x 128 features (4-bit): unit
+ *   16g + i (channel i, word group g) at byte 16*(16g + i). A weight buffer
+ *   holds Np*W words. (A decoder streams chunk c of all tiles together, so
+ *   the whole GPU reads one contiguous stretch of memory at a time.)
  * Code values:
  *   QIFT_LEVELS_MNZ : the code read as a 2-bit two's-complement integer t
  *                     gives the half-scale level 2t+1 in {-3,-1,+1,+3};
@@ -75,7 +79,7 @@
 extern "C" {
 #endif
 
-#define QIFT_ABI_VERSION 1
+#define QIFT_ABI_VERSION 2
 
 typedef enum {
   QIFT_OK = 0,

@@ -274,16 +274,17 @@ def unpack_int4_words(words: np.ndarray) -> np.ndarray:
     return unpack_int4(w.view(np.uint8).reshape(w.shape[0], -1))
 
 
-# Weight codes in device memory are stored in row tiles of 16 output
-# channels. With W the 32-bit words of one channel row in row order (K/16
-# words for 2-bit codes, K/8 for 4-bit), F = 64 features per 16-byte unit for
-# 2-bit codes and 32 for 4-bit, and chunks of 4 units (4F features):
+# Weight codes in device memory are stored in tiles of 16 output channels,
+# chunk-major. With W the 32-bit words of one channel row in row order (K/16
+# words for 2-bit codes, K/8 for 4-bit), T = Np/16 tiles, and the row cut into
+# chunks of 16 words (u_c = min(16, W - 16c) words in chunk c):
 #   tile r = channel // 16, lane-row i = channel % 16,
 #   chunk c, unit-group g (0..3) and word j (0..3) of the feature's word,
-#   tiled word index = r * (16 * W) + c * 256 + (16 * g + i) * 4 + j
-# i.e. one chunk is 1 KB holding 16 channels x 4F features, unit u = 16g + i
-# at byte 16u; a short last chunk holds only its first groups. Channels are
-# padded with zero codes to a multiple of 16.
+#   tiled word index = c * 256 * T + r * 16 * u_c + (16 * g + i) * 4 + j
+# i.e. chunk c of all tiles precedes chunk c + 1; a full chunk of a tile is
+# 1 KB holding 16 channels x 16 words, unit u = 16g + i at byte 16u; a short
+# last chunk holds only its first groups. Channels are padded with zero codes
+# to a multiple of 16.
 
 def _tiled_index(Np: int, W: int) -> np.ndarray:
     """tiled word index of (channel n, row-order word w), [Np, W]."""
@@ -292,7 +293,9 @@ def _tiled_index(Np: int, W: int) -> np.ndarray:
     r, i = n // 16, n % 16
     c, rem = w // 16, w % 16
     g, j = rem // 4, rem % 4
-    return r * (16 * W) + c * 256 + (16 * g + i) * 4 + j
+    T = Np // 16
+    uc = np.minimum(16, W - 16 * c)
+    return c * 256 * T + r * 16 * uc + (16 * g + i) * 4 + j
 
 
 def tile_weight_words(rows: np.ndarray) -> np.ndarray:

@@ -35,7 +35,7 @@ def test_library_loads_and_exports_every_declared_symbol():
     assert len(names) == 11, names
     for n in names:
         assert hasattr(lib, n), n
-    assert q.abi_version() == 1
+    assert q.abi_version() == 2
     for s in range(5):
         assert q.status_string(s).startswith("QIFT_")
 

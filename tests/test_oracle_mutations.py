@@ -87,7 +87,8 @@ def _tiled_index_group_row_swapped(Np, W):
     r, i = n // 16, n % 16
     c, rem = w // 16, w % 16
     g, j = rem // 4, rem % 4
-    return r * (16 * W) + c * 256 + (16 * i + g) * 4 + j
+    uc = np.minimum(16, W - 16 * c)
+    return c * 256 * (Np // 16) + r * 16 * uc + (16 * i + g) * 4 + j
 
 
 def _gaussian_mse_cross_term_sign(levels, s=1.0):
