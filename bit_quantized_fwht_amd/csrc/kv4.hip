@@ -4,10 +4,12 @@
 // abstract).
 //
 // Layout on the GPU: a head vector of D elements is held by L = D/E lanes of
-// one quad (L <= 4) with E consecutive elements each (E = 16, 32 or 64), so
-// log2(E) butterfly stages run inside a lane's registers and at most two
-// (partners at lane xor 1 and xor 2) cross lanes, through DPP quad
-// permutations. A lane loads 2E (bf16) or 4E bytes and stores E/2 bytes of
+// one quad with E consecutive elements each (E = min(D, 32); 64 for
+// D = 256), so log2(E) butterfly stages run inside a lane's registers and at
+// most two (partners at lane xor 1 and xor 2) cross lanes, through DPP quad
+// permutations. (64 elements per lane for D = 128 saves 12% of the
+// instructions but runs 25% slower: half the waves, each with twice the
+// serial work and loads spread over twice the span.) A lane loads 2E (bf16) or 4E bytes and stores E/2 bytes of
 // codes. The kernel is bound by HBM bandwidth in principle and by VALU issue
 // in practice, so every step is written for the fewest instructions per
 // element:
@@ -99,15 +101,15 @@ __global__ __launch_bounds__(kKvThreads) void kv4_kernel(const T* __restrict__ K
   }
   float m = 0.f;
 #pragma unroll
-  for (int j = 0; j < E; ++j) {
-    v[j] *= norm;
-    m = fmaxf(m, fabsf(v[j]));
-  }
+  for (int j = 0; j < E; ++j) m = fmaxf(m, fabsf(v[j]));
   if constexpr (L >= 2) m = fmaxf(m, quad_xor<1>(m));
   if constexpr (L == 4) m = fmaxf(m, quad_xor<2>(m));
+  m *= norm;  // rounding is monotonic: max(|v|) * norm == max(|v * norm|)
   const float s = __fdiv_rn(m, 7.0f);
   const float rs = s != 0.f ? __fdiv_rn(1.0f, s) : 0.f;
-  const float rl = sigma * rs;  // stored * rl == true value * rs, exactly
+  // y = stored * sigma * (norm / s), within four roundings of x' / s with
+  // x' = fl(v * norm) the rotated value (int4x8_rint's margin covers it)
+  const float rl = sigma * (norm * rs);
   uint32_t words[E / 8];
   float dmax = 0.f;
 #pragma unroll
@@ -123,7 +125,7 @@ __global__ __launch_bounds__(kKvThreads) void kv4_kernel(const T* __restrict__ K
     for (int w = 0; w < E / 8; ++w) {
       float x[8];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) x[j] = sigma * v[8 * w + j];
+      for (int j = 0; j < 8; ++j) x[j] = sigma * (v[8 * w + j] * norm);
       words[w] = int4x8_exact(x, s);
     }
   }

@@ -4,10 +4,11 @@
 // round half to even, packed as eight two's-complement nibbles in one word
 // (element j at bits 4j..4j+3).
 //
-// Fast path: y = x * r with r = 1 / s. For |x / s| <= 7.5, y is within
-// 1.3e-6 of the correctly rounded quotient (two roundings of 2^-24 relative
-// each), so whenever y is more than 1e-5 away from a half-integer both round
-// to the same integer. The caller tracks the largest |y - rint(y)| of a group
+// Fast path: y = x * r with r = 1 / s (or y = v * fl(norm * r) for x =
+// fl(v * norm)). For |x / s| <= 7.5, y is within 1.8e-6 of x / s (at most
+// four roundings of 2^-24 relative each), so whenever y is more than 1e-5
+// away from a half-integer, y, x / s and the correctly rounded quotient all
+// round to the same integer. The caller tracks the largest |y - rint(y)| of a group
 // and recomputes the group with the exact division when it exceeds 0.49999
 // (or when r is not finite, i.e. s is so small that 1 / s overflows).
 //

@@ -368,20 +368,22 @@ __device__ __forceinline__ void rotate_row_fast(const T* __restrict__ src, int K
   // 6. quantize 16 consecutive elements per group: x = the rotated value up
   //    to sigma (sigma = 1 on the LDS path), y = x * sigma / s
   const float sg = in_regs ? sigma : 1.f;
-  const float rl = sg * rs;
+  // y = v * sg * (norm / s): within four roundings of x' / s with
+  // x' = fl(v * norm) the rotated value (int4x8_rint's margin covers it)
+  const float rl = sg * (norm * rs);
   uint2* xrow = reinterpret_cast<uint2*>(xq_row);
 #pragma unroll
   for (int q = 0; q < kFastMaxGroups; ++q) {
     const int grp = tid + q * kRowThreads;
     if (grp >= groups) continue;
-    float x[16], y[16];
+    float x[16], y[16];  // x: the stored values (up to sg), then the rotated ones
     if (in_regs) {
 #pragma unroll
-      for (int j = 0; j < 16; ++j) x[j] = v[q][j] * norm;
+      for (int j = 0; j < 16; ++j) x[j] = v[q][j];
     } else {
       const float* s16 = row + 17 * grp;
 #pragma unroll
-      for (int j = 0; j < 16; ++j) x[j] = s16[j] * norm;
+      for (int j = 0; j < 16; ++j) x[j] = s16[j];
     }
 #pragma unroll
     for (int j = 0; j < 16; ++j) y[j] = x[j] * rl;
@@ -389,10 +391,11 @@ __device__ __forceinline__ void rotate_row_fast(const T* __restrict__ src, int K
     uint32_t w0 = int4x8_rint(y, dmax);
     uint32_t w1 = int4x8_rint(y + 8, dmax);
     if (!(dmax <= 0.49999f) || !fast || xrot_row) {
-      // the true rotated values; fma(x, sg, +0) also writes every zero as
-      // +0 (an upper lane's x - x comes back as -0 through its sign)
+      // the true rotated values fl(v * norm); fma(., sg, +0) also writes
+      // every zero as +0 (an upper lane's x - x comes back as -0 through its
+      // sign)
 #pragma unroll
-      for (int j = 0; j < 16; ++j) x[j] = __builtin_fmaf(x[j], sg, 0.0f);
+      for (int j = 0; j < 16; ++j) x[j] = __builtin_fmaf(x[j] * norm, sg, 0.0f);
       if (!(dmax <= 0.49999f) || !fast) {  // a value near a rounding tie: exact division
         w0 = int4x8_exact(x, s);
         w1 = int4x8_exact(x + 8, s);
