@@ -196,17 +196,26 @@ __device__ __forceinline__ void prefill_tile(const qift_linear_desc& d, int64_t 
 // through LDS, so that each wave adds up and stores one 64 x 64 block.
 // ---------------------------------------------------------------------------
 
-constexpr int kDlBM = 128, kDlBN = 128;  // workgroup tile
+constexpr int kDlBN = 128;  // workgroup tile: 16 RB tokens x 128 channels
 
-template <int LV>
+// Epilogue staging (defined with the epilogue below): 32 rows of 68 words per
+// wave.
+constexpr int kEpiStride = 68;                        // words per staged row
+constexpr int kEpiWaveBytes = 32 * kEpiStride * 4;    // 8704 B per wave
+
+// RB: 16-row blocks per wave and workgroup tile (8: 128 x 128 tiles; 4: 64 x
+// 128 tiles for launches whose 128 x 128 tiles would not fill the GPU).
+template <int LV, int RB>
 struct DlCfg {
+  static_assert(RB == 8 || RB == 4, "128- or 64-row tiles");
   static constexpr bool kInt4 = LV == QIFT_LEVELS_INT4;
+  static constexpr int kBM = 16 * RB;
   static constexpr int kStageK = 256;
-  static constexpr int kABytes = kDlBM * 128;                       // 16 KB
+  static constexpr int kABytes = kBM * 128;                         // 16 or 8 KB
   static constexpr int kBChunks = kInt4 ? 2 : 1;                     // 1 KB chunks per tile
   static constexpr int kBBytes = (kDlBN / 16) * kBChunks * 1024;    // 8 or 16 KB
   static constexpr int kStage = kABytes + kBBytes;
-  static constexpr int kLds = 2 * kStage;
+  static constexpr int kLds = 2 * kStage > 4 * kEpiWaveBytes ? 2 * kStage : 4 * kEpiWaveBytes;
   static constexpr int kAInstr = kABytes / 1024 / 4;                // per wave per stage
   static constexpr int kBInstr = kBBytes / 1024 / 4;
 };
@@ -227,13 +236,10 @@ __device__ __forceinline__ void gl_lds16(const void* g, uint8_t* lds_wave_base) 
 // 16-byte piece; the scales are applied after the transpose, from LDS tables
 // of the tile's activation scales (sa_t, by row) and channel scales times
 // kappa (sw_t, by column) that were fetched when the tile started.
-constexpr int kEpiStride = 68;                        // words per staged row
-constexpr int kEpiWaveBytes = 32 * kEpiStride * 4;    // 8704 B per wave
-
 // The output type and the accumulator rows (I0 .. I0 + 3 of an accumulator
 // array of NI rows) are fixed at compile time, so that the row loop unrolls
 // and no register is selected at run time.
-template <int LV, int YD, int NI, int I0>
+template <int LV, int YD, int NI, int I0, int NP>
 __device__ __forceinline__ void epilogue_blk(const qift_linear_desc& d, const v4i (&acc)[NI][4],
                                              int64_t mb, int64_t nb, const float* sa_t,
                                              const float* sw_t, uint8_t* lds_w, int lane) {
@@ -256,7 +262,7 @@ __device__ __forceinline__ void epilogue_blk(const qift_linear_desc& d, const v4
   const bool vec = (N % kCpl) == 0 && n + kCpl <= N &&
                    (reinterpret_cast<uintptr_t>(d.Y) & 15) == 0;
 #pragma unroll
-  for (int p = 0; p < 2; ++p) {
+  for (int p = 0; p < NP; ++p) {
 #pragma unroll
     for (int ii = 0; ii < 2; ++ii)
 #pragma unroll
@@ -315,17 +321,17 @@ __device__ __forceinline__ void epilogue_blk(const qift_linear_desc& d, const v4
   }
 }
 
-template <int LV, int NI, int I0>
+template <int LV, int NI, int I0, int NP>
 __device__ __forceinline__ void epilogue_any(const qift_linear_desc& d, const v4i (&acc)[NI][4],
                                              int64_t mb, int64_t nb, const float* sa_t,
                                              const float* sw_t, int y_dtype, uint8_t* lds_w,
                                              int lane) {
   if (y_dtype == QIFT_BF16)
-    epilogue_blk<LV, QIFT_BF16, NI, I0>(d, acc, mb, nb, sa_t, sw_t, lds_w, lane);
+    epilogue_blk<LV, QIFT_BF16, NI, I0, NP>(d, acc, mb, nb, sa_t, sw_t, lds_w, lane);
   else if (y_dtype == QIFT_I32)
-    epilogue_blk<LV, QIFT_I32, NI, I0>(d, acc, mb, nb, sa_t, sw_t, lds_w, lane);
+    epilogue_blk<LV, QIFT_I32, NI, I0, NP>(d, acc, mb, nb, sa_t, sw_t, lds_w, lane);
   else
-    epilogue_blk<LV, QIFT_F32, NI, I0>(d, acc, mb, nb, sa_t, sw_t, lds_w, lane);
+    epilogue_blk<LV, QIFT_F32, NI, I0, NP>(d, acc, mb, nb, sa_t, sw_t, lds_w, lane);
 }
 
 // A-tile slot of 16-byte unit c in row r: rows r and r + 1 share a swizzle
@@ -334,11 +340,12 @@ __device__ __forceinline__ void epilogue_any(const qift_linear_desc& d, const v4
 // 256-byte bank line).
 __device__ __forceinline__ int sk_slot(int c, int row) { return c ^ ((row >> 1) & 7); }
 
-template <int LV>
+template <int LV, int RB>
 __device__ __forceinline__ void prefill_tile_sk(const qift_linear_desc& d, int64_t m0,
                                                 int64_t nt0, int scale_f16, int y_dtype,
                                                 uint8_t* lds, float* scl) {
-  using C = DlCfg<LV>;
+  using C = DlCfg<LV, RB>;
+  constexpr int kHalf = RB / 2;          // row blocks each wave keeps after the swap
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -382,14 +389,14 @@ __device__ __forceinline__ void prefill_tile_sk(const qift_linear_desc& d, int64
   };
 
   // written first by the first stage's MFMAs, whose accumulator input is
-  // the constant 0 (no separate zeroing of 128 registers per tile)
-  v4i acc[8][4];
+  // the constant 0 (no separate zeroing of the accumulators per tile)
+  v4i acc[RB][4];
 
   // int4 weights: the lane's 16-byte unit of chunk kh (32 features, two
   // steps); 2-bit weights: words 2 kh, 2 kh + 1 of the lane's 16-byte unit.
   using BFrag = typename std::conditional<C::kInt4, uint4, uint2>::type;
   struct Frag {
-    uint4 a[8];
+    uint4 a[RB];
     BFrag b[4];
   };
   // reads all of a stage's fragments before the next stage's loads are
@@ -399,8 +406,9 @@ __device__ __forceinline__ void prefill_tile_sk(const qift_linear_desc& d, int64
     const uint8_t* bs = as + C::kABytes;
     const int c = C::kInt4 ? 4 * kh + g : 2 * g + kh;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int row = 16 * ((i + 4 * kh) & 7) + r16;   // accumulator i <- row block i + 4 kh
+    for (int i = 0; i < RB; ++i) {
+      // accumulator i <- row block i + RB/2 kh
+      const int row = 16 * ((i + kHalf * kh) & (RB - 1)) + r16;
       f.a[i] = *reinterpret_cast<const uint4*>(as + row * 128 + 16 * sk_slot(c, row));
     }
 #pragma unroll
@@ -426,7 +434,7 @@ __device__ __forceinline__ void prefill_tile_sk(const qift_linear_desc& d, int64
           B[j] = pot_operand(s2 == 0 ? f.b[j].x : f.b[j].y);
       }
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
+      for (int i = 0; i < RB; ++i) {
         const v4i A = s2 == 0 ? int4_operand(f.a[i].x, f.a[i].y) : int4_operand(f.a[i].z, f.a[i].w);
 #pragma unroll
         for (int j = 0; j < 4; ++j)
@@ -438,7 +446,7 @@ __device__ __forceinline__ void prefill_tile_sk(const qift_linear_desc& d, int64
       // last of them has issued; interleaved, the unpack runs while the
       // matrix core is busy. 4-5% faster than the compiler's own order.
 #pragma unroll
-      for (int k = 0; k < 32; ++k) {
+      for (int k = 0; k < 4 * RB; ++k) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
         __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);  // two VALU
       }
@@ -446,14 +454,14 @@ __device__ __forceinline__ void prefill_tile_sk(const qift_linear_desc& d, int64
   };
 
   // the epilogue's scales, fetched now so that their latency is hidden by the
-  // main loop: thread t < 128 holds the activation scale of row t of the
-  // tile, thread 128 + c the channel scale (times kappa) of column c
-  float pre_scale;
+  // main loop: thread t < kBM holds the activation scale of row t of the
+  // tile, thread kBM + c the channel scale (times kappa) of column c
+  float pre_scale = 0.f;
   {
-    const int64_t m = m0 + tid, n = nt0 + (tid - 128);
-    if (tid < 128)
+    const int64_t m = m0 + tid, n = nt0 + (tid - C::kBM);
+    if (tid < C::kBM)
       pre_scale = m < M ? d.s_a[m] : 0.f;
-    else
+    else if (tid < C::kBM + kDlBN)
       pre_scale = n < N ? load_scale(d.scales, n, scale_f16) * level_kappa(LV) : 0.f;
   }
 
@@ -475,24 +483,25 @@ __device__ __forceinline__ void prefill_tile_sk(const qift_linear_desc& d, int64
     if (st + 1 < nstages) issue(st + 1, (int)((st + 1) & 1));
     mma(f, false);
   }
-  scl[tid] = pre_scale;              // read after the exchange's barriers
+  if (tid < C::kBM + kDlBN) scl[tid] = pre_scale;  // read after the exchange's barriers
 
   // Swap halves with the partner wave (same channels, other feature half).
-  // Accumulator i of wave kh holds row block (i + 4 kh) mod 8, so every wave
-  // keeps accumulators 0..3 (rows 64 kh .. 64 kh + 63) and sends 4..7, which
-  // are exactly the partner's kept rows; two rounds of 32 rows (8 KB per wave).
+  // Accumulator i of wave kh holds row block (i + RB/2 kh) mod RB, so every
+  // wave keeps accumulators 0 .. RB/2 - 1 (its RB/2 row blocks) and sends the
+  // others, which are exactly the partner's kept rows; RB/4 rounds of 32 rows
+  // (8 KB per wave).
   static_assert(4 * 8 * 64 * 16 <= C::kLds, "partial-sum exchange fits in the stage buffers");
   static_assert(4 * kEpiWaveBytes <= C::kLds, "epilogue staging fits in the stage buffers");
   int4* ex = reinterpret_cast<int4*>(lds);
   const int partner = wave ^ 2;
   __syncthreads();  // every wave is done reading the stage buffers
 #pragma unroll
-  for (int sp = 0; sp < 2; ++sp) {
+  for (int sp = 0; sp < RB / 4; ++sp) {
 #pragma unroll
     for (int ii = 0; ii < 2; ++ii)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const v4i v = acc[4 + 2 * sp + ii][j];
+        const v4i v = acc[kHalf + 2 * sp + ii][j];
         ex[(wave * 8 + ii * 4 + j) * 64 + lane] = int4{v[0], v[1], v[2], v[3]};
       }
     __syncthreads();
@@ -506,8 +515,9 @@ __device__ __forceinline__ void prefill_tile_sk(const qift_linear_desc& d, int64
       }
     __syncthreads();
   }
-  epilogue_any<LV, 8, 0>(d, acc, m0 + 64 * kh, nt0 + wn, scl + 64 * kh, scl + 128 + wn, y_dtype,
-                         lds + wave * kEpiWaveBytes, lane);
+  epilogue_any<LV, RB, 0, RB / 4>(d, acc, m0 + 16 * kHalf * kh, nt0 + wn,
+                                  scl + 16 * kHalf * kh, scl + C::kBM + wn, y_dtype,
+                                  lds + wave * kEpiWaveBytes, lane);
 }
 
 // Tile order: with T tiles and T % 8 == 0, consecutive workgroups (which the
@@ -523,17 +533,19 @@ __device__ __forceinline__ void dl_tile_of(int64_t b, int64_t nM, int64_t nN, in
   *tm = t % nM;
 }
 
-// two workgroups per CU (<= 256 registers per lane) so that each SIMD has a
-// second wave to switch to while one waits on LDS or a barrier
-template <int LV>
-__global__ __launch_bounds__(256, QIFT_PREFILL_MINBLOCKS) void linear_prefill_sk_kernel(
+// 128-row tiles: two workgroups per CU (<= 256 registers per lane) so that
+// each SIMD has a second wave to switch to while one waits on LDS or a
+// barrier; 64-row tiles: three.
+template <int LV, int RB>
+__global__ __launch_bounds__(256, RB == 8 ? QIFT_PREFILL_MINBLOCKS : 3) void linear_prefill_sk_kernel(
     qift_linear_desc d, int scale_f16, int y_dtype) {
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[DlCfg<LV>::kLds];
-  __shared__ float scl[kDlBM + kDlBN];
-  const int64_t nM = (d.M + kDlBM - 1) / kDlBM, nN = (d.N + kDlBN - 1) / kDlBN;
+  using C = DlCfg<LV, RB>;
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[C::kLds];
+  __shared__ float scl[C::kBM + kDlBN];
+  const int64_t nM = (d.M + C::kBM - 1) / C::kBM, nN = (d.N + kDlBN - 1) / kDlBN;
   int64_t tm, tn;
   dl_tile_of(blockIdx.x, nM, nN, &tm, &tn);
-  prefill_tile_sk<LV>(d, tm * kDlBM, tn * kDlBN, scale_f16, y_dtype, lds, scl);
+  prefill_tile_sk<LV, RB>(d, tm * C::kBM, tn * kDlBN, scale_f16, y_dtype, lds, scl);
 }
 
 template <int LV>
@@ -545,24 +557,31 @@ __global__ __launch_bounds__(256) void linear_prefill_kernel(qift_linear_desc d,
   prefill_tile<LV>(d, m0, n0, scale_f16, y_dtype, lds);
 }
 
+// workgroup slots of one round of 128-row tiles: two per CU on 256 CUs
+constexpr int64_t kPrefillSlots = 512;
+
 hipError_t launch_linear_prefill(const qift_linear_desc& d, int scale_f16, int y_dtype,
                                  hipStream_t s) {
   if (d.K % 256 == 0) {
-    const dim3 g1((unsigned)(((d.N + kDlBN - 1) / kDlBN) * ((d.M + kDlBM - 1) / kDlBM)));
+    // 64-row tiles when 128-row tiles would leave workgroup slots (two per
+    // CU) empty
+    const int64_t nN = (d.N + kDlBN - 1) / kDlBN;
+    const bool small = ((d.M + 127) / 128) * nN < kPrefillSlots;
+    const int64_t bm = small ? 64 : 128;
+    const dim3 g1((unsigned)(nN * ((d.M + bm - 1) / bm)));
+#define QIFT_SK_LAUNCH(LVV)                                                                  \
+  if (small)                                                                                 \
+    hipLaunchKernelGGL((linear_prefill_sk_kernel<LVV, 4>), g1, dim3(256), 0, s, d, scale_f16, \
+                       y_dtype);                                                             \
+  else                                                                                       \
+    hipLaunchKernelGGL((linear_prefill_sk_kernel<LVV, 8>), g1, dim3(256), 0, s, d, scale_f16, \
+                       y_dtype);
     switch (d.levels) {
-      case QIFT_LEVELS_MNZ:
-        hipLaunchKernelGGL(linear_prefill_sk_kernel<QIFT_LEVELS_MNZ>, g1, dim3(256), 0, s, d,
-                           scale_f16, y_dtype);
-        break;
-      case QIFT_LEVELS_POT:
-        hipLaunchKernelGGL(linear_prefill_sk_kernel<QIFT_LEVELS_POT>, g1, dim3(256), 0, s, d,
-                           scale_f16, y_dtype);
-        break;
-      default:
-        hipLaunchKernelGGL(linear_prefill_sk_kernel<QIFT_LEVELS_INT4>, g1, dim3(256), 0, s, d,
-                           scale_f16, y_dtype);
-        break;
+      case QIFT_LEVELS_MNZ: QIFT_SK_LAUNCH(QIFT_LEVELS_MNZ) break;
+      case QIFT_LEVELS_POT: QIFT_SK_LAUNCH(QIFT_LEVELS_POT) break;
+      default: QIFT_SK_LAUNCH(QIFT_LEVELS_INT4) break;
     }
+#undef QIFT_SK_LAUNCH
     return hipGetLastError();
   }
   const dim3 grid((unsigned)((d.N + kBN - 1) / kBN), (unsigned)((d.M + kBM - 1) / kBM));

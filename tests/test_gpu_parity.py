@@ -255,9 +255,13 @@ def run_linear(qa, codes, s_a, s_w, kind, out_dtype):
     return Y
 
 
+# M <= 16: decode kernel; M > 16 with K % 256 == 0: prefill with 64-row tiles
+# when 128-row tiles number fewer than 512 (two per CU), else 128-row tiles
+# ((1000, 256, 8200): 8 x 65 tiles, ragged in M and N); other K: the general
+# prefill kernel
 LIN_SHAPES = [(1, 64, 1), (1, 256, 17), (3, 320, 64), (4, 4096, 257), (8, 192, 300),
               (16, 1024, 129), (17, 256, 130), (31, 128, 63), (64, 4096, 256), (129, 576, 200),
-              (200, 2048, 385)]
+              (200, 2048, 385), (1000, 256, 8200)]
 
 
 @pytest.mark.parametrize("kind", ["mnz", "pot", "int4"])
@@ -272,7 +276,7 @@ def test_linear_int32_bitexact(kind, M, K, N):
 
 @pytest.mark.parametrize("kind", ["mnz", "pot", "int4"])
 @pytest.mark.parametrize("M,K,N", [(1, 256, 33), (16, 512, 100), (40, 1024, 150), (48, 512, 256),
-                                   (130, 768, 136), (33, 256, 1000)])
+                                   (130, 768, 136), (33, 256, 1000), (1000, 256, 8200)])
 def test_linear_float_epilogue(kind, M, K, N):
     qa, codes, s_a, s_w = random_linear_inputs(M, K, N, kind, seed=5 + M + N)
     say(f"linear f32/bf16 {kind} M={M} K={K} N={N}")
