@@ -13,7 +13,8 @@ value = algorithmic weight-stream bytes of one pass / step time.
 
 Also measured and reported under "extra": the same stack at M = 4, 8, 16;
 prefill int8-MFMA TOPS at M = 2048 (up_proj, down_proj; bfloat16 output,
-and float32 output under the "_f32_out" keys); the
+and float32 output under the "_f32_out" keys) and for a 512-token up_proj
+chunk; the
 LLaMA-3.1-8B-shaped power-of-two layer (decode over 32 layer copies, prefill
 at M = 4096); the mixed W2/W4 stack (layers 0-15 MNZ, 16-31 int4) at M = 16;
 KV4 of K and V [4096, 32, 128].
@@ -355,10 +356,12 @@ def measure_extras(q, torch, dev, stack, args):
             torch.cuda.empty_cache()
     extra["decode_llama7b_w2_mnz"] = dec
 
-    # prefill int8 MFMA GEMM, M = 2048
+    # prefill int8 MFMA GEMM, M = 2048; and a 512-token chunk of up_proj (the
+    # 64-row tile path: 128-row tiles would leave workgroup slots empty)
     pre = {}
-    for name, K, N, B in (("up_proj", 4096, 11008, 4096), ("down_proj", 11008, 4096, 256)):
-        M = 2048
+    for name, K, N, B, M in (("up_proj", 4096, 11008, 4096, 2048),
+                             ("down_proj", 11008, 4096, 256, 2048),
+                             ("up_proj_M512", 4096, 11008, 4096, 512)):
         W = si.device_weights(N, K, seed=5, sigma=0.02, device=dev)
         cw, sw = q.qift_quantize_weights(W, B, "mnz", torch.float16)
         del W
