@@ -262,8 +262,8 @@ def cpu_baseline(budget_s=15.0):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported in this build "
-              f"(the path shards by output channel with no exchange; see DESIGN.md)", file=sys.stderr)
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the linear "
+              f"would shard by output channel with no exchange between GPUs)", file=sys.stderr)
         sys.exit(2)
     import torch
     import bit_quantized_fwht_amd as q

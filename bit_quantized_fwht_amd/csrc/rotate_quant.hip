@@ -276,7 +276,7 @@ __device__ __forceinline__ void rotate_row_fast(const T* __restrict__ src, int K
                                                 float* red) {
   const int tid = threadIdx.x;
   const int groups = K >> 4;
-  const int wave_g0 = tid & ~63;  // the wave's first group of round 0
+  const int wave_g0 = tid & ~63;  // the wave's first group (q = 0)
   // 1. loads (a group past the row end reads group 0 and is discarded)
   float v[kFastMaxGroups][16];
 #pragma unroll

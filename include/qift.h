@@ -85,7 +85,7 @@ typedef enum {
   QIFT_OK = 0,
   QIFT_ERR_INVALID_ARG = 1, /* null pointer, bad size, bad enum value          */
   QIFT_ERR_ALIGNMENT = 2,   /* a buffer is not aligned as documented           */
-  QIFT_ERR_UNSUPPORTED = 3, /* valid request outside this build's limits       */
+  QIFT_ERR_UNSUPPORTED = 3, /* valid request outside this library's limits     */
   QIFT_ERR_HIP = 4          /* the HIP runtime reported an error on launch     */
 } qift_status;
 
