@@ -34,9 +34,14 @@ __device__ __forceinline__ uint4 ld16_stream(const uint32_t* p) {
 #endif
 }
 
+// Output staging of one wave: 16 rows x 64 channels of int32, rows padded to
+// 68 words.
+constexpr int kDecEpiStride = 68;
+constexpr int kDecEpiWords = 16 * kDecEpiStride;
+
 template <int LV>
 __device__ __forceinline__ void decode_wave(const qift_linear_desc& d, int64_t n0, int scale_f16,
-                                            int y_dtype, int lane) {
+                                            int y_dtype, int lane, int* epi) {
   using F = Fmt<LV>;
   const int r16 = lane & 15;
   const int g = lane >> 4;
@@ -102,40 +107,83 @@ __device__ __forceinline__ void decode_wave(const qift_linear_desc& d, int64_t n
     if (t + 1 < nchunks) compute(y);
   }
 
-  // epilogue: lane holds rows m = 4g + r of channel n0 + 16 i + r16
+  // Epilogue. The lane holds rows m = 4g + r of channels n0 + 16 i + r16 (MFMA
+  // order), so direct stores would write 64-byte halves of cache lines, four
+  // rows apart (20% of the launch at M = 16). The wave's 16 x 64 block goes
+  // through its own LDS region instead and is stored row-major: each lane then
+  // owns 4 consecutive channels of one row and writes them as one piece.
   const float kappa = level_kappa(LV);
 #pragma unroll
-  for (int i = 0; i < kDecodeTiles; ++i) {
-    const int64_t n = n0 + 16 * i + r16;
-    if (n >= N) continue;
-    const float sw = load_scale(d.scales, n, scale_f16) * kappa;
+  for (int i = 0; i < kDecodeTiles; ++i)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int m = 4 * g + r;
-      if (m < M) {
-        const int a = acc[i][r] >> F::kShift;
-        store_y(d.Y, y_dtype, (int64_t)m * N + n, a, d.s_a[m] * sw);
+    for (int r = 0; r < 4; ++r)
+      epi[(4 * g + r) * kDecEpiStride + 16 * i + r16] = acc[i][r] >> F::kShift;
+  // one wave writes and reads its own region: its LDS operations complete in order
+  const int c0 = 4 * (lane & 15);
+  const int64_t n = n0 + c0;
+  float sw[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) sw[e] = n + e < N ? load_scale(d.scales, n + e, scale_f16) * kappa : 0.f;
+  const bool vec = (N & 3) == 0 && n + 4 <= N && (reinterpret_cast<uintptr_t>(d.Y) & 15) == 0;
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const int m = 4 * p + (lane >> 4);
+    if (m >= M) continue;
+    const int4 v = *reinterpret_cast<const int4*>(&epi[m * kDecEpiStride + c0]);
+    const int a[4] = {v.x, v.y, v.z, v.w};
+    const int64_t o = (int64_t)m * N + n;
+    if (y_dtype == QIFT_I32) {
+      int* y = reinterpret_cast<int*>(d.Y) + o;
+      if (vec) {
+        *reinterpret_cast<int4*>(y) = v;
+      } else {
+        for (int e = 0; e < 4; ++e)
+          if (n + e < N) y[e] = a[e];
+      }
+    } else {
+      const float sa = d.s_a[m];
+      float y[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) y[e] = (float)a[e] * (sa * sw[e]);
+      if (y_dtype == QIFT_BF16) {
+        uint16_t* yo = reinterpret_cast<uint16_t*>(d.Y) + o;
+        if (vec) {
+          *reinterpret_cast<uint2*>(yo) = uint2{pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3])};
+        } else {
+          for (int e = 0; e < 4; ++e)
+            if (n + e < N) yo[e] = float_to_bf16_bits(y[e]);
+        }
+      } else {
+        float* yo = reinterpret_cast<float*>(d.Y) + o;
+        if (vec) {
+          *reinterpret_cast<float4*>(yo) = float4{y[0], y[1], y[2], y[3]};
+        } else {
+          for (int e = 0; e < 4; ++e)
+            if (n + e < N) yo[e] = y[e];
+        }
       }
     }
   }
 }
 
 __device__ __forceinline__ void decode_dispatch(const qift_linear_desc& d, int64_t tile,
-                                                int scale_f16, int y_dtype) {
+                                                int scale_f16, int y_dtype, int* epi_all) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int64_t n0 = tile * kDecodeRowsPerTile + (int64_t)wave * kDecodeRowsPerWave;
   if (n0 >= d.N) return;
+  int* epi = epi_all + wave * kDecEpiWords;
   switch (d.levels) {
-    case QIFT_LEVELS_MNZ: decode_wave<QIFT_LEVELS_MNZ>(d, n0, scale_f16, y_dtype, lane); break;
-    case QIFT_LEVELS_POT: decode_wave<QIFT_LEVELS_POT>(d, n0, scale_f16, y_dtype, lane); break;
-    default: decode_wave<QIFT_LEVELS_INT4>(d, n0, scale_f16, y_dtype, lane); break;
+    case QIFT_LEVELS_MNZ: decode_wave<QIFT_LEVELS_MNZ>(d, n0, scale_f16, y_dtype, lane, epi); break;
+    case QIFT_LEVELS_POT: decode_wave<QIFT_LEVELS_POT>(d, n0, scale_f16, y_dtype, lane, epi); break;
+    default: decode_wave<QIFT_LEVELS_INT4>(d, n0, scale_f16, y_dtype, lane, epi); break;
   }
 }
 
 __global__ __launch_bounds__(256, QIFT_DECODE_MINBLOCKS) void linear_decode_kernel(qift_linear_desc d, int scale_f16,
                                                             int y_dtype) {
-  decode_dispatch(d, blockIdx.x, scale_f16, y_dtype);
+  __shared__ __attribute__((aligned(16))) int epi[kDecodeWaves * kDecEpiWords];
+  decode_dispatch(d, blockIdx.x, scale_f16, y_dtype, epi);
 }
 
 __global__ __launch_bounds__(256, QIFT_DECODE_MINBLOCKS) void linear_grouped_kernel(const uint8_t* __restrict__ ws) {
@@ -145,7 +193,8 @@ __global__ __launch_bounds__(256, QIFT_DECODE_MINBLOCKS) void linear_grouped_ker
   const int32_t e = reinterpret_cast<const int32_t*>(ws + h->tile_map_offset)[tile];
   const PlanEntry* pe = reinterpret_cast<const PlanEntry*>(ws + h->entries_offset) + e;
   const qift_linear_desc d = pe->d;
-  decode_dispatch(d, tile - pe->tile_begin, h->scale_f16, h->y_dtype);
+  __shared__ __attribute__((aligned(16))) int epi[kDecodeWaves * kDecEpiWords];
+  decode_dispatch(d, tile - pe->tile_begin, h->scale_f16, h->y_dtype, epi);
 }
 
 // ---------------------------------------------------------------------------

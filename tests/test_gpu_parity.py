@@ -287,13 +287,14 @@ def test_linear_float_epilogue(kind, M, K, N):
     assert np.all(np.abs(Yb - y) <= 2 ** -8 * np.abs(y) + 1e-30)
 
 
+@pytest.mark.parametrize("M", [7, 40])  # decode and prefill kernels
 @pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16, torch.int32])
-def test_linear_unaligned_output(out_dtype):
+def test_linear_unaligned_output(out_dtype, M):
     """An output view that starts one element into its buffer (not 16-byte
     aligned) is written element by element, with the same values."""
-    M, K, N = 40, 512, 256
+    K, N = 512, 256
     qa, codes, s_a, s_w = random_linear_inputs(M, K, N, "mnz", seed=77)
-    say(f"linear unaligned output {out_dtype}")
+    say(f"linear unaligned output {out_dtype} M={M}")
     ref = run_linear(qa, codes, s_a, s_w, "mnz", out_dtype)
     xq = torch.from_numpy(O.pack_int4(qa)).to(DEV)
     cw = u32_to_dev(O.pack_weights(codes, "mnz"))
