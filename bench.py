@@ -76,11 +76,12 @@ def log(*a):
 class DecodeStack:
     """A stack of layers, each a list of (name, K, N, had_block, levels)."""
 
-    def __init__(self, q, torch, layers, M, sigma, dev, seed0=0, scale_dtype=None):
+    def __init__(self, q, torch, layers, M, sigma, dev, seed0=0, scale_dtype=None, y_dtype=None):
         import synth_inputs as si
         self.q, self.torch = q, torch
         self.M = M
         scale_dtype = scale_dtype or torch.float16
+        y_dtype = y_dtype or torch.bfloat16
         self.codes, self.scales = [], []
         self.items = []
         self.bytes = 0
@@ -102,7 +103,10 @@ class DecodeStack:
             sa = torch.empty((n_rows,), dtype=torch.float32, device=dev)
             self.act[(K, B)] = dict(X=X, xq=xq, sa=sa, slot={s: i for i, s in enumerate(slots)})
         ytot = sum(M * N for layer in layers for (_, K, N, B, lv) in layer)
-        self.Y = torch.empty((ytot,), dtype=torch.float32, device=dev)
+        # bfloat16 outputs, the dtype of the model's activations (as for the
+        # prefill shapes); set y_dtype=torch.float32 for float32 outputs
+        self.y_dtype = y_dtype
+        self.Y = torch.empty((ytot,), dtype=y_dtype, device=dev)
         yoff = 0
         for li, layer in enumerate(layers):
             for idx, (name, K, N, B, lv) in enumerate(layer):
@@ -121,7 +125,7 @@ class DecodeStack:
                 self.scales.append(s)
                 self.bytes += c.numel() * 4 + s.numel() * s.element_size()
         torch.cuda.synchronize()
-        self.group = q.LinearGroup(self.items, scale_dtype=scale_dtype, y_dtype=torch.float32)
+        self.group = q.LinearGroup(self.items, scale_dtype=scale_dtype, y_dtype=y_dtype)
         # all stacked inputs (one matrix per (K, block)) in one batched launch
         self.rot = q.RotateBatch([(a["X"], B, a["xq"], a["sa"]) for (K, B), a in self.act.items()])
 
