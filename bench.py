@@ -259,6 +259,53 @@ def cpu_baseline(budget_s=15.0):
                       f"{t_total:.1f} s of CPU time; GB/s of packed codes+scales consumed"}
 
 
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def cpu_oracle_units():
+    """The oracle on bounded samples of the other measured units (rotate +
+    quantize, the prefill GEMM, KV4), each timed once; a few seconds each."""
+    from oracle import qift_oracle as O
+    import synth_inputs as si
+    out = {"cpu_model": cpu_model()}
+    # rotate + quantize: 512 of the 2048 up_proj input rows (K = 4096, block 4096)
+    M, K, B = 512, 4096, 4096
+    X = si.activations(M, K, seed=6)
+    t0 = time.perf_counter()
+    O.rotate_quant_act(X.astype(np.float64), B)
+    dt = time.perf_counter() - t0
+    out["rotate_quant_up_proj_input"] = {"rows": M, "K": K, "block": B, "s": round(dt, 3),
+                                         "GBps": round(M * (2.5 * K + 4) / dt / 1e9, 4)}
+    # prefill GEMM: 1024 of the 2048 up_proj rows against all 11008 channels
+    M, K, N = 1024, 4096, 11008
+    qa = si.uniform_int4((M, K), seed=7).astype(np.int8)
+    codes = si.uniform_codes((N, K), 4, seed=8)
+    s_a = si.positive_scales(M, 9).astype(np.float32)
+    s_w = si.positive_scales(N, 10).astype(np.float64)
+    t0 = time.perf_counter()
+    O.linear(qa, s_a, codes, s_w, "mnz")
+    dt = time.perf_counter() - t0
+    out["gemm_up_proj"] = {"rows": M, "K": K, "N": N, "s": round(dt, 3),
+                           "TOPS": round(2.0 * M * N * K / dt / 1e12, 5)}
+    # KV4: 2048 of the 4096 tokens, 32 heads x 128
+    T, H, D = 2048, 32, 128
+    KV = si.kv(T, H, D, seed=11)
+    t0 = time.perf_counter()
+    O.kv4_quant(KV, D)
+    dt = time.perf_counter() - t0
+    out["kv4"] = {"T": T, "H": H, "D": D, "s": round(dt, 3),
+                  "GBps": round(T * H * (2.5 * D + 4) / dt / 1e9, 4)}
+    return out
+
+
 # ---------------------------------------------------------------------------
 # main
 # ---------------------------------------------------------------------------
@@ -326,7 +373,10 @@ def main():
     if not args.only_headline and not args.no_cpu_baseline:
         log("timing the CPU oracle baseline")
         cpu = cpu_baseline()
+        cpu["cpu_model"] = cpu_model()
         log(f"  oracle: {cpu['value']:.4f} GB/s on {cpu['cores']} threads")
+        if extra:
+            extra["cpu_oracle_other_units"] = cpu_oracle_units()
     out = {
         "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 5),
@@ -339,6 +389,69 @@ def main():
         "roofline": roofline, "cpu_baseline": cpu, "extra": extra,
     }
     print(json.dumps(out), flush=True)
+
+
+def single_call_graphs(q, torch, st):
+    """The stack's linears as single qift_w2a4_linear calls in layer order,
+    captured into HIP graphs (all 224, and per distinct shape the calls of
+    that shape). Every replay is checked against the eager calls' output
+    before timing."""
+    def call(it):
+        q.qift_w2a4_linear(it["xq"], it["s_a"], it["codes"], it["scales"], it["levels"], Y=it["Y"])
+
+    st.rotate_all()
+    for it in st.items:
+        call(it)
+    torch.cuda.synchronize()
+    ref = st.Y.clone()
+
+    def capture(items):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for it in items:
+                call(it)
+        torch.cuda.synchronize()
+        return g
+
+    g_all = capture(st.items)
+    for _ in range(3):
+        st.Y.zero_()
+        torch.cuda.synchronize()
+        g_all.replay()
+        torch.cuda.synchronize()
+        if not torch.equal(st.Y, ref):
+            raise RuntimeError("graph replay of the single calls differs from the eager calls")
+    med, _, _ = time_fn(torch, g_all.replay, 30, warmup=10)
+    out = {"calls": len(st.items), "graph_ms": round(med, 4),
+           "GBps": round(st.bytes / med / 1e6, 1),
+           "frac_of_hbm_peak": round(st.bytes / med / 1e6 / HBM_PEAK_GBS, 4)}
+    del g_all
+    shapes = {}
+    for it in st.items:
+        K, N = it["xq"].shape[1] * 2, it["scales"].shape[0]
+        shapes.setdefault((K, N), []).append(it)
+    per = {}
+    for (K, N), items in shapes.items():
+        g = capture(items)
+        st.Y.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for it in items:
+            n0 = it["Y"].numel()
+            off = it["Y"].data_ptr() - st.Y.data_ptr()
+            el = st.Y.element_size()
+            if not torch.equal(st.Y[off // el:off // el + n0], ref[off // el:off // el + n0]):
+                raise RuntimeError(f"graph replay for shape {K}x{N} differs from the eager calls")
+        nbytes = sum(it["codes"].numel() * 4 + it["scales"].numel() * it["scales"].element_size()
+                     for it in items)
+        med, _, _ = time_fn(torch, g.replay, 30, warmup=10)
+        per[f"K={K},N={N}"] = {"calls": len(items), "us_per_call": round(med * 1e3 / len(items), 2),
+                               "GBps": round(nbytes / med / 1e6, 1),
+                               "frac_of_hbm_peak": round(nbytes / med / 1e6 / HBM_PEAK_GBS, 4)}
+        del g
+    out["per_shape"] = per
+    return out
 
 
 def measure_extras(q, torch, dev, stack, args):
@@ -361,6 +474,8 @@ def measure_extras(q, torch, dev, stack, args):
             del s
             torch.cuda.empty_cache()
     extra["decode_llama7b_w2_mnz"] = dec
+    if args.m == 1:
+        extra["decode_llama7b_w2_mnz"]["M=1_single_calls_hipgraph"] = single_call_graphs(q, torch, stack)
 
     # prefill int8 MFMA GEMM, M = 2048; and a 512-token chunk of up_proj (the
     # 64-row tile path: 128-row tiles would leave workgroup slots empty)
@@ -385,7 +500,8 @@ def measure_extras(q, torch, dev, stack, args):
             del Y
         rmed, _, _ = time_fn(torch, lambda: q.qift_rotate_quant_act(X, B, xq=xq, s_a=sa), 30)
         pre[name].update({"rotate_quant_ms": round(rmed, 4),
-                          "rotate_quant_GBps": round((M * K * 2 + M * K / 2 + 4 * M) / rmed / 1e6, 1)})
+                          "rotate_quant_GBps": round((M * K * 2 + M * K / 2 + 4 * M) / rmed / 1e6, 1),
+                          "TOPS_incl_rotate": round(ops / (pre[name]["gemm_ms"] + rmed) / 1e9, 1)})
         pre[name]["vendor_int8_gemm"] = vendor_int8_gemm(torch, M, K, N, dev)
         del cw, sw, X, xq, sa
     extra["prefill_llama7b_mnz"] = pre
@@ -450,10 +566,27 @@ def measure_extras(q, torch, dev, stack, args):
 
     med, _, _ = time_fn(torch, kv_step, 40)
     kv_bytes = 2 * (T * H * D * 2 + T * H * D // 2 + T * H * 4)
+    # the same pair of calls on one buffer set with a 512 MB write between
+    # repetitions (the caches hold none of the inputs); only the calls are timed
+    flush = torch.empty((1 << 29,), dtype=torch.uint8, device=dev)
+    a, b = sets[0], sets[1]
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(20)]
+    for i, (e0, e1) in enumerate(evs):
+        flush.fill_(i & 0xFF)
+        e0.record()
+        q.qift_kv4_quant(a[0], D, kvq=a[1], scales=a[2])
+        q.qift_kv4_quant(b[0], D, kvq=b[1], scales=b[2])
+        e1.record()
+    torch.cuda.synchronize()
+    fmed = float(np.median([e0.elapsed_time(e1) for e0, e1 in evs]))
     extra["kv4_llama7b_K_and_V"] = {"T": T, "H": H, "D": D, "ms_K_and_V": round(med, 4),
                                     "GBps": round(kv_bytes / med / 1e6, 1),
-                                    "frac_of_hbm_peak": round(kv_bytes / med / 1e6 / HBM_PEAK_GBS, 4)}
-    del sets
+                                    "frac_of_hbm_peak": round(kv_bytes / med / 1e6 / HBM_PEAK_GBS, 4),
+                                    "note": "cycled over 8 buffer sets (1.3 GB)",
+                                    "ms_K_and_V_after_flush": round(fmed, 4),
+                                    "GBps_after_flush": round(kv_bytes / fmed / 1e6, 1)}
+    del sets, flush
     extra["context"] = {"qtea_lut_kernel_per_token_speedup_vs_fp16": 7.2,
                         "note": "speedup printed for a different (ternary) method; hardware not stated"}
     return extra

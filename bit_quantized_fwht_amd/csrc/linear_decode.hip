@@ -198,12 +198,165 @@ __global__ __launch_bounds__(256, QIFT_DECODE_MINBLOCKS) void linear_grouped_ker
 }
 
 // ---------------------------------------------------------------------------
+// decode of one linear with few channels: K split over the waves of a
+// workgroup
+// ---------------------------------------------------------------------------
+
+// A linear call on its own (not grouped) has N / 256 workgroups of 64-channel
+// waves, 16 for N = 4096: 16 of 256 CUs would carry its whole weight stream.
+// Here a workgroup owns one 16-channel tile and its S waves take every S-th
+// K chunk (wave w: chunks w, w + S, ...), each with two chunks in flight; the
+// S partial int32 blocks are summed through LDS (integer sums, so the result
+// is the same as one wave walking all of K).
+template <int LV, int S>
+__global__ __launch_bounds__(64 * S) void linear_decode_splitk_kernel(qift_linear_desc d,
+                                                                      int scale_f16,
+                                                                      int y_dtype) {
+  using F = Fmt<LV>;
+  __shared__ __attribute__((aligned(16))) int red[S * 256];  // wave w: rows m, columns c at 256 w + 16 m + c
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int r16 = lane & 15;
+  const int g = lane >> 4;
+  const int64_t M = d.M, K = d.K, N = d.N;
+  const int64_t cw = F::code_words(K);
+  const int64_t tiles = (N + 15) >> 4;
+  const int64_t tn = blockIdx.x;  // 16-channel tile
+  const int64_t nchunks = (K + F::kChunkK - 1) / F::kChunkK;
+  const bool act_row = r16 < M;
+  const MnzMasks km = mnz_masks(d.reserved, lane);
+
+  struct Chunk {
+    uint4 c, a0, a1;
+  };
+  // chunk t of the tile: the lane's 16-byte code unit (chunk-major tiled
+  // layout: chunk t of tile tn at t * 256 * tiles + tn * 16 * ut words) and
+  // the matching 32 (or 16) bytes of its activation row
+  auto load = [&](Chunk& ch, int64_t t) {
+    const int64_t kseg = t * F::kChunkK + (int64_t)g * F::kLaneK;
+    const bool kval = t < nchunks && kseg < K;
+    const int64_t ut = cw - 16 * t < 16 ? cw - 16 * t : 16;
+    ch.c = kval ? ld16_stream(d.codes + t * 256 * tiles + tn * 16 * ut + 4 * lane)
+                : uint4{0u, 0u, 0u, 0u};
+    ch.a0 = uint4{0u, 0u, 0u, 0u};
+    ch.a1 = uint4{0u, 0u, 0u, 0u};
+    if (kval && act_row) {
+      const uint8_t* ap = d.xq + (int64_t)r16 * (K / 2) + kseg / 2;
+      ch.a0 = ld16(ap);
+      if constexpr (!F::kInt4) ch.a1 = ld16(ap + 16);
+    }
+  };
+  v4i acc = v4i{0, 0, 0, 0};
+  auto compute = [&](const Chunk& ch) {
+#pragma unroll
+    for (int s = 0; s < F::kSteps; ++s)
+      acc = mfma16(act_operand(ch.a0, ch.a1, s), weight_operand<LV>(ch.c, s, km), acc);
+  };
+  Chunk x, y;
+  load(x, wave);
+  for (int64_t t = wave; t < nchunks; t += 2 * S) {
+    load(y, t + S);
+    compute(x);
+    load(x, t + 2 * S);
+    if (t + S < nchunks) compute(y);
+  }
+
+  // partial sums: the lane holds rows 4g + r of column r16
+#pragma unroll
+  for (int r = 0; r < 4; ++r) red[256 * wave + 16 * (4 * g + r) + r16] = acc[r];
+  __syncthreads();
+  if (wave != 0) return;
+  // wave 0: lane -> row m = lane / 4, columns 4 (lane % 4) .. + 3
+  const int m = lane >> 2;
+  const int c0 = 4 * (lane & 3);
+  if (m >= M) return;
+  int a[4] = {0, 0, 0, 0};
+#pragma unroll
+  for (int w = 0; w < S; ++w) {
+    const int4 v = *reinterpret_cast<const int4*>(&red[256 * w + 16 * m + c0]);
+    a[0] += v.x;
+    a[1] += v.y;
+    a[2] += v.z;
+    a[3] += v.w;
+  }
+#pragma unroll
+  for (int e = 0; e < 4; ++e) a[e] >>= F::kShift;
+  const int64_t n = tn * 16 + c0;
+  const int64_t o = (int64_t)m * N + n;
+  const bool vec = (N & 3) == 0 && n + 4 <= N && (reinterpret_cast<uintptr_t>(d.Y) & 15) == 0;
+  if (y_dtype == QIFT_I32) {
+    int* yo = reinterpret_cast<int*>(d.Y) + o;
+    if (vec) {
+      *reinterpret_cast<int4*>(yo) = int4{a[0], a[1], a[2], a[3]};
+    } else {
+      for (int e = 0; e < 4; ++e)
+        if (n + e < N) yo[e] = a[e];
+    }
+    return;
+  }
+  const float kappa = level_kappa(LV);
+  const float sa = d.s_a[m];
+  float yv[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e)
+    yv[e] = n + e < N ? (float)a[e] * (sa * (load_scale(d.scales, n + e, scale_f16) * kappa)) : 0.f;
+  if (y_dtype == QIFT_BF16) {
+    uint16_t* yo = reinterpret_cast<uint16_t*>(d.Y) + o;
+    if (vec) {
+      *reinterpret_cast<uint2*>(yo) = uint2{pack_bf16x2(yv[0], yv[1]), pack_bf16x2(yv[2], yv[3])};
+    } else {
+      for (int e = 0; e < 4; ++e)
+        if (n + e < N) yo[e] = float_to_bf16_bits(yv[e]);
+    }
+  } else {
+    float* yo = reinterpret_cast<float*>(d.Y) + o;
+    if (vec) {
+      *reinterpret_cast<float4*>(yo) = float4{yv[0], yv[1], yv[2], yv[3]};
+    } else {
+      for (int e = 0; e < 4; ++e)
+        if (n + e < N) yo[e] = yv[e];
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
+
+// 64-channel waves when they alone give at least two workgroups per CU
+// (N >= 131072); else one 16-channel tile per workgroup with K split over
+// 4, 8 or 16 waves (by the number of K chunks, so that each wave has about
+// two chunks: the whole weight stream of the call is in flight at once)
+constexpr int64_t kDecodeWideMinTiles = 512;
+
+template <int LV>
+hipError_t launch_decode_splitk(const qift_linear_desc& d, int scale_f16, int y_dtype,
+                                hipStream_t s) {
+  using F = Fmt<LV>;
+  const dim3 grid((unsigned)((d.N + 15) / 16));
+  const int64_t nchunks = (d.K + F::kChunkK - 1) / F::kChunkK;
+  if (nchunks <= 8)
+    hipLaunchKernelGGL((linear_decode_splitk_kernel<LV, 4>), grid, dim3(256), 0, s, d, scale_f16,
+                       y_dtype);
+  else if (nchunks <= 16)
+    hipLaunchKernelGGL((linear_decode_splitk_kernel<LV, 8>), grid, dim3(512), 0, s, d, scale_f16,
+                       y_dtype);
+  else
+    hipLaunchKernelGGL((linear_decode_splitk_kernel<LV, 16>), grid, dim3(1024), 0, s, d,
+                       scale_f16, y_dtype);
+  return hipGetLastError();
+}
 
 hipError_t launch_linear_decode(const qift_linear_desc& d, int scale_f16, int y_dtype,
                                 hipStream_t s) {
   const int64_t tiles = (d.N + kDecodeRowsPerTile - 1) / kDecodeRowsPerTile;
+  if (tiles < kDecodeWideMinTiles) {
+    switch (d.levels) {
+      case QIFT_LEVELS_MNZ: return launch_decode_splitk<QIFT_LEVELS_MNZ>(d, scale_f16, y_dtype, s);
+      case QIFT_LEVELS_POT: return launch_decode_splitk<QIFT_LEVELS_POT>(d, scale_f16, y_dtype, s);
+      default: return launch_decode_splitk<QIFT_LEVELS_INT4>(d, scale_f16, y_dtype, s);
+    }
+  }
   hipLaunchKernelGGL(linear_decode_kernel, dim3((unsigned)tiles), dim3(256), 0, s, d, scale_f16,
                      y_dtype);
   return hipGetLastError();
