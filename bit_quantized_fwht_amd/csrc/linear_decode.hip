@@ -325,8 +325,11 @@ __global__ __launch_bounds__(64 * S) void linear_decode_splitk_kernel(qift_linea
 
 // 64-channel waves when they alone give at least two workgroups per CU
 // (N >= 131072); else one 16-channel tile per workgroup with K split over
-// 4, 8 or 16 waves (by the number of K chunks, so that each wave has about
-// two chunks: the whole weight stream of the call is in flight at once)
+// S = 4, 8 or 16 waves by the number of K chunks, so that each wave has about
+// two chunks: the whole weight stream of a LLaMA-sized call is in flight at
+// once. Each call of a LLaMA-7B-shaped stack (weights from HBM) in one HIP
+// graph: 4096 x 4096 4.3 us (S = 8), 4096 -> 11008 6.1 us (S = 8; 6.3 with
+// S = 4), 11008 -> 4096 5.8 us (S = 16; 6.9 with S = 8).
 constexpr int64_t kDecodeWideMinTiles = 512;
 
 template <int LV>
@@ -335,10 +338,11 @@ hipError_t launch_decode_splitk(const qift_linear_desc& d, int scale_f16, int y_
   using F = Fmt<LV>;
   const dim3 grid((unsigned)((d.N + 15) / 16));
   const int64_t nchunks = (d.K + F::kChunkK - 1) / F::kChunkK;
-  if (nchunks <= 8)
+  const int S = nchunks <= 8 ? 4 : nchunks <= 16 ? 8 : 16;
+  if (S == 4)
     hipLaunchKernelGGL((linear_decode_splitk_kernel<LV, 4>), grid, dim3(256), 0, s, d, scale_f16,
                        y_dtype);
-  else if (nchunks <= 16)
+  else if (S == 8)
     hipLaunchKernelGGL((linear_decode_splitk_kernel<LV, 8>), grid, dim3(512), 0, s, d, scale_f16,
                        y_dtype);
   else

@@ -256,13 +256,14 @@ def run_linear(qa, codes, s_a, s_w, kind, out_dtype):
 
 
 # M <= 16: decode with K split over 4, 8 or 16 waves (by the number of K
-# chunks) when 64-channel waves would give fewer than 512 workgroups, else
+# chunks: up to 8, 16, more) when 64-channel waves would give fewer than 512
+# workgroups, else
 # 64-channel waves ((2, 256, 131100): 513 workgroups, ragged N); M > 16 with
 # K % 256 == 0: prefill with 64-row tiles when 128-row tiles number fewer than
 # 512 (two per CU), else 128-row tiles ((1000, 256, 8200): 8 x 65 tiles,
 # ragged in M and N); other K: the general prefill kernel
 LIN_SHAPES = [(1, 64, 1), (1, 256, 17), (3, 320, 64), (4, 4096, 257), (8, 192, 300),
-              (16, 1024, 129), (5, 2304, 40), (2, 8448, 33), (2, 256, 131100),
+              (16, 1024, 129), (5, 2304, 40), (2, 8448, 33), (3, 3072, 4100), (2, 256, 131100),
               (17, 256, 130), (31, 128, 63), (64, 4096, 256), (129, 576, 200),
               (200, 2048, 385), (1000, 256, 8200)]
 
