@@ -35,6 +35,21 @@ It leaves open, and this oracle takes the plainest reading of:
   shift by two (level +-(1 << 2*bit0));
 * packing layouts (the ``pack*`` functions below).
 
+Level tables and the searched scale (the abstract compares level sets: the
+no-zero sets against the standard {-2, -1, 0, +1} set, the Lloyd-optimal
+inner/outer ratio near 0.30, and a scale-invariant analysis, i.e. each set at
+its best scale). Readings taken here:
+
+* a level table is four integers L[c] in [-15, 15], one per 2-bit code, and
+  the weight of code c is L[c] * s (so {1, 3, -3, -1} decodes MNZ codes and
+  {1, 4, -1, -4} PoT codes, with s the step);
+* nearest level as above, ties to the smaller |L|, then to the positive level,
+  then to the lower code;
+* the absmax scale rule divides by max |L|; the searched ("mse") rule tries
+  the 64 stored scales s_j = store(fl32(fl32(absmax / outer) * (64 - j) / 64)),
+  j = 0..63, codes decided against each, and keeps the one with the smallest
+  sum of squared errors (float64; the first on ties).
+
 Parity pins: every function here is checked in ``tests/test_oracle_pins.py``
 against closed forms, brute force and the values the abstract prints. The
 end-to-end accuracy of a quantized linear against the unquantized one has no
@@ -71,6 +86,33 @@ def real_levels(kind: str) -> np.ndarray:
     """Real levels (multiples of the scale s) indexed by 2-bit code."""
     info = LEVEL_KINDS[kind]
     return np.array(info["code_to_int"], dtype=np.float64) * info["kappa"]
+
+
+#: largest |level| of a level table
+LUT_MAX_LEVEL = 15
+
+
+def check_table(table) -> tuple:
+    """A level table: four integers in [-15, 15], not all zero."""
+    t = tuple(int(v) for v in table)
+    if len(t) != 4 or any(abs(v) > LUT_MAX_LEVEL for v in t) or all(v == 0 for v in t):
+        raise ValueError(f"bad level table {table!r}")
+    return t
+
+
+def table_preference(table) -> tuple:
+    """Codes in tie-break order: smaller |level| first, then positive (and
+    zero) before negative, then the lower code."""
+    t = check_table(table)
+    return tuple(sorted(range(4), key=lambda c: (abs(t[c]), t[c] < 0, c)))
+
+
+def _kind_levels(kind: str, table=None):
+    """(real level by code, tie-break order, outer level) of a 2-bit kind."""
+    if kind == "lut":
+        t = check_table(table)
+        return np.array(t, dtype=np.float64), table_preference(t), float(max(abs(v) for v in t))
+    return real_levels(kind), _PREFERENCE[kind], LEVEL_KINDS[kind]["outer"]
 
 
 # ---------------------------------------------------------------------------
@@ -147,23 +189,71 @@ def _store_scale(s32: np.ndarray, scale_dtype: str) -> np.ndarray:
     raise ValueError(scale_dtype)
 
 
-def weight_scales(wr32: np.ndarray, kind: str, scale_dtype: str) -> np.ndarray:
+def _outer(kind: str, table=None) -> float:
+    return LEVEL_KINDS["int4"]["outer"] if kind == "int4" else _kind_levels(kind, table)[2]
+
+
+def absmax_scales(wr32: np.ndarray, kind: str, scale_dtype: str, table=None) -> np.ndarray:
     """s_n = float32(absmax_n) / float32(outer level), rounded to the stored
     dtype (float16 round-to-nearest-even, or float32)."""
     a = np.max(np.abs(wr32.astype(np.float32)), axis=1).astype(np.float32)
-    s32 = a / np.float32(LEVEL_KINDS[kind]["outer"])
+    s32 = a / np.float32(_outer(kind, table))
     return _store_scale(s32.astype(np.float32), scale_dtype)
 
 
-def nearest_codes(wr32: np.ndarray, s_stored: np.ndarray, kind: str) -> np.ndarray:
+#: candidates of the searched scale: factors (64 - j) / 64 of the absmax scale
+MSE_GRID = 64
+
+
+def scale_candidates(wr32: np.ndarray, kind: str, scale_dtype: str, table=None) -> np.ndarray:
+    """[N, 64] stored candidate scales s_j = store(fl32(fl32(absmax / outer)
+    * (64 - j) / 64)), j = 0..63 (the factors are exact in float32)."""
+    a = np.max(np.abs(wr32.astype(np.float32)), axis=1).astype(np.float32)
+    base = (a / np.float32(_outer(kind, table))).astype(np.float32)
+    f = ((MSE_GRID - np.arange(MSE_GRID)) / MSE_GRID).astype(np.float32)
+    s32 = (base[:, None] * f[None, :]).astype(np.float32)
+    return _store_scale(s32, scale_dtype)
+
+
+def row_sq_error(w32: np.ndarray, s, kind: str, table=None) -> float:
+    """Sum over the row of (w - level(code) * s)^2 in float64, the codes
+    decided against the stored scale s."""
+    w32 = np.asarray(w32, dtype=np.float32)[None, :]
+    sv = np.asarray([s])
+    if kind == "int4":
+        lv = int4_weight_codes(w32, sv).astype(np.float64)
+    else:
+        codes = nearest_codes(w32, sv, kind, table)
+        lv = _kind_levels(kind, table)[0][codes]
+    d = w32.astype(np.float64) - lv * float(np.float64(sv[0]))
+    return float(np.sum(d * d))
+
+
+def weight_scales(wr32: np.ndarray, kind: str, scale_dtype: str, table=None,
+                  rule: str = "absmax") -> np.ndarray:
+    """Per-channel stored scales by the absmax rule, or by the searched rule:
+    the candidate of scale_candidates with the smallest row_sq_error (the
+    first one on ties)."""
+    if rule == "absmax":
+        return absmax_scales(wr32, kind, scale_dtype, table)
+    if rule != "mse":
+        raise ValueError(rule)
+    cand = scale_candidates(wr32, kind, scale_dtype, table)
+    out = cand[:, 0].copy()
+    for n in range(wr32.shape[0]):
+        errs = [row_sq_error(wr32[n], cand[n, j], kind, table) for j in range(MSE_GRID)]
+        out[n] = cand[n, int(np.argmin(errs))]
+    return out
+
+
+def nearest_codes(wr32: np.ndarray, s_stored: np.ndarray, kind: str, table=None) -> np.ndarray:
     """2-bit code of each weight: the code whose level * s is closest to w,
     found by comparing all four distances (float64, exact for float32 w and a
     float16/float32 s). Ties go to the earlier code in the preference order
     (inner before outer, positive before negative)."""
     w = wr32.astype(np.float32).astype(np.float64)
     s = s_stored.astype(np.float64)[:, None]
-    lv = real_levels(kind)
-    order = _PREFERENCE[kind]
+    lv, order, _ = _kind_levels(kind, table)
     d = np.stack([np.abs(w - lv[c] * s) for c in order], axis=0)
     pick = np.argmin(d, axis=0)  # first minimum = preferred code on ties
     return np.asarray(order, dtype=np.int64)[pick]
@@ -182,26 +272,37 @@ def int4_weight_codes(wr32: np.ndarray, s_stored: np.ndarray) -> np.ndarray:
     return q
 
 
-def quantize_weights(W: np.ndarray, B: int, kind: str, scale_dtype: str):
+def quantize_weights(W: np.ndarray, B: int, kind: str, scale_dtype: str, table=None,
+                     rule: str = "absmax"):
     """Offline path for one linear W [N, K]: rotate each row along K in blocks
-    of B (float64), round to float32, scale rule, nearest code.
+    of B (float64), round to float32, scale rule, nearest code. kind 'lut'
+    takes a level table.
     Returns (codes int64 [N, K] (2-bit codes, or int4 values for 'int4'),
     scales [N] in the stored dtype, rotated float32 weights)."""
     wr32 = rotate(W, B).astype(np.float32)
-    s = weight_scales(wr32, kind, scale_dtype)
+    s = weight_scales(wr32, kind, scale_dtype, table, rule)
     if kind == "int4":
         codes = int4_weight_codes(wr32, s)
     else:
-        codes = nearest_codes(wr32, s, kind)
+        codes = nearest_codes(wr32, s, kind, table)
     return codes, s, wr32
 
 
-def code_levels(codes: np.ndarray, kind: str) -> np.ndarray:
-    """Integer level of each code (half-scale for MNZ): int64."""
+def code_levels(codes: np.ndarray, kind: str, table=None) -> np.ndarray:
+    """Integer level of each code (half-scale for MNZ, the table's entry for
+    a level table): int64."""
     if kind == "int4":
         return np.asarray(codes, dtype=np.int64)
-    table = np.array(LEVEL_KINDS[kind]["code_to_int"], dtype=np.int64)
-    return table[np.asarray(codes, dtype=np.int64)]
+    if kind == "lut":
+        lut = np.array(check_table(table), dtype=np.int64)
+    else:
+        lut = np.array(LEVEL_KINDS[kind]["code_to_int"], dtype=np.int64)
+    return lut[np.asarray(codes, dtype=np.int64)]
+
+
+def level_kappa(kind: str) -> float:
+    """Factor from the integer level to the multiple of the scale."""
+    return 1.0 if kind == "lut" else LEVEL_KINDS[kind]["kappa"]
 
 
 # ---------------------------------------------------------------------------
@@ -343,13 +444,14 @@ def int_matmul(q: np.ndarray, lv: np.ndarray) -> np.ndarray:
     return np.rint(a).astype(np.int64)
 
 
-def linear(q: np.ndarray, s_a: np.ndarray, codes: np.ndarray, s_w: np.ndarray, kind: str):
+def linear(q: np.ndarray, s_a: np.ndarray, codes: np.ndarray, s_w: np.ndarray, kind: str,
+           table=None):
     """y = x_q W_q^T with integer accumulation: acc = q . level^T, then
     y[m, n] = acc[m, n] * s_a[m] * s_w[n] * kappa (kappa = 1/2 for the
     half-scale MNZ levels, 1 otherwise). Returns (acc int64, y float64)."""
-    lv = code_levels(codes, kind)
+    lv = code_levels(codes, kind, table)
     acc = int_matmul(q, lv)
-    kappa = LEVEL_KINDS[kind]["kappa"]
+    kappa = level_kappa(kind)
     y = acc.astype(np.float64) * np.asarray(s_a, np.float64)[:, None] \
         * np.asarray(s_w, np.float64)[None, :] * kappa
     return acc, y

@@ -112,6 +112,21 @@ def _lloyd_wrong_centroid(n_levels=4, iters=2000, tol=1e-13):
     return np.array(pts)
 
 
+def _table_preference_negative_first(table):
+    t = O.check_table(table)
+    return tuple(sorted(range(4), key=lambda c: (abs(t[c]), t[c] > 0, c)))
+
+
+def _row_abs_error(w32, s, kind, table=None):
+    w32 = np.asarray(w32, dtype=np.float32)[None, :]
+    sv = np.asarray([s])
+    if kind == "int4":
+        lv = O.int4_weight_codes(w32, sv).astype(np.float64)
+    else:
+        lv = O._kind_levels(kind, table)[0][O.nearest_codes(w32, sv, kind, table)]
+    return float(np.sum(np.abs(w32.astype(np.float64) - lv * float(sv[0]))))
+
+
 def _kinds_with(kind, **over):
     d = {k: dict(v) for k, v in O.LEVEL_KINDS.items()}
     d[kind].update(over)
@@ -136,6 +151,9 @@ MUTATIONS = {
     "tile_group_and_row_swapped": [("_tiled_index", _tiled_index_group_row_swapped)],
     "mse_cross_term_sign": [("gaussian_mse", _gaussian_mse_cross_term_sign)],
     "lloyd_unnormalized_centroid": [("lloyd_gaussian", _lloyd_wrong_centroid)],
+    "table_ties_to_negative": [("table_preference", _table_preference_negative_first)],
+    "mse_grid_32": [("MSE_GRID", 32)],
+    "mse_rule_abs_error": [("row_sq_error", _row_abs_error)],
 }
 
 

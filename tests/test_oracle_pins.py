@@ -431,6 +431,172 @@ def test_ratio_curve():
 
 
 # --------------------------------------------------------------------------
+# level tables and the searched scale
+# --------------------------------------------------------------------------
+
+def _exact_nearest(w, levels, s):
+    """Nearest table level in exact rational arithmetic; ties to the smaller
+    |level|, then the non-negative one, then the lower code."""
+    from fractions import Fraction
+    wf, sf = Fraction(float(w)), Fraction(float(s))
+    best = None
+    for c, L in enumerate(levels):
+        key = (abs(wf - L * sf), abs(L), L < 0, c)
+        if best is None or key < best[0]:
+            best = (key, c)
+    return best[1]
+
+
+def pin_table_tie_order():
+    # by hand: |L| first, then positive, then the code
+    assert O.table_preference((-2, -1, 0, 1)) == (2, 3, 1, 0)
+    assert O.table_preference((1, 3, -3, -1)) == (0, 3, 1, 2)
+    assert O.table_preference((1, 4, -1, -4)) == (0, 2, 1, 3)
+    assert O.table_preference((3, 3, -3, 10)) == (0, 1, 2, 3)
+    for bad in ((0, 0, 0, 0), (16, 1, 2, 3), (1, 2, 3)):
+        with pytest.raises(ValueError):
+            O.check_table(bad)
+
+
+def pin_table_nearest_exact():
+    """Nearest-level codes of a table against exact rational arithmetic, on
+    weights that include every midpoint between levels (exact ties)."""
+    rng = np.random.default_rng(41)
+    for table in ((-2, -1, 0, 1), (3, 10, -3, -10), (1, 3, -3, -1), (-7, 2, 2, 15), (0, 5, -5, 1)):
+        for s in (np.float32(0.25), np.float32(0.0371)):
+            mids = [(a + b) / 2 * float(s) for a in table for b in table]
+            w = np.concatenate([np.array(mids), rng.normal(0, 3 * float(s), 200),
+                                [0.0, -0.0, 20 * float(s), -20 * float(s)]]).astype(np.float32)
+            got = O.nearest_codes(w[None, :], np.array([s]), "lut", table)[0]
+            ref = [_exact_nearest(v, table, s) for v in w]
+            assert got.tolist() == ref, (table, s)
+
+
+def pin_table_reproduces_mnz_and_pot():
+    """The table {1, 3, -3, -1} at step s/2 decodes MNZ codes and {1, 4, -1, -4}
+    PoT codes: same codes, same linear outputs."""
+    W = si.weights(24, 256, seed=43).astype(np.float64)
+    W[0, :8] = 0.0
+    q = si.uniform_int4((3, 256), seed=44)
+    s_a = si.positive_scales(3, 45)
+    for kind, table, ratio in (("mnz", (1, 3, -3, -1), 0.5), ("pot", (1, 4, -1, -4), 1.0)):
+        c0, s0, _ = O.quantize_weights(W, 64, kind, "f16")
+        c1, s1, _ = O.quantize_weights(W, 64, "lut", "f16", table=table)
+        assert np.array_equal(c0, c1)
+        assert np.array_equal(s1.astype(np.float64), s0.astype(np.float64) * ratio)
+        _, y0 = O.linear(q, s_a, c0, s0.astype(np.float64), kind)
+        _, y1 = O.linear(q, s_a, c1, s1.astype(np.float64), "lut", table)
+        assert np.allclose(y0, y1, rtol=1e-15, atol=0)
+
+
+def _brute_mse_scale(w32, levels, outer, to_stored):
+    """Independent searched scale: 64 candidate factors, nearest level by
+    exact rationals, exact squared error; the first minimum."""
+    from fractions import Fraction
+    a = np.float32(np.max(np.abs(w32)))
+    base = np.float32(a / np.float32(outer))
+    best = None
+    for j in range(64):
+        s = to_stored(np.float32(base * np.float32((64 - j) / 64)))
+        err = Fraction(0)
+        for v in w32:
+            c = _exact_nearest(v, levels, s)
+            err += (Fraction(float(v)) - levels[c] * Fraction(float(s))) ** 2
+        if best is None or err < best[0]:
+            best = (err, s)
+    return best[1]
+
+
+def pin_mse_scale_brute_force():
+    rng = np.random.default_rng(47)
+    for table in ((-2, -1, 0, 1), (3, 10, -3, -10)):
+        for sdt, to_stored in (("f32", np.float32), ("f16", np.float16)):
+            w = rng.standard_normal((3, 16)).astype(np.float32)
+            w[2, 3] = 9.0  # an outlier: the search clips it
+            s = O.weight_scales(w, "lut", sdt, table, rule="mse")
+            outer = max(abs(v) for v in table)
+            for n in range(3):
+                assert s[n] == _brute_mse_scale(w[n], table, outer, to_stored), (table, sdt, n)
+    # MNZ through its own levels: real levels (2t+1)/2, outer 1.5
+    w = rng.standard_normal((2, 16)).astype(np.float32)
+    s = O.weight_scales(w, "mnz", "f32", rule="mse")
+    for n in range(2):
+        ref = _brute_mse_scale(w[n], (0.5, 1.5, -1.5, -0.5), 1.5, np.float32)
+        assert s[n] == ref
+
+
+def pin_mse_scale_matches_gaussian_optimum():
+    """On a long standard-normal row the searched scale reaches the closed-form
+    best-scale MSE of each level set (within the 1/64 grid and sampling)."""
+    x = np.random.default_rng(53).standard_normal((1, 1 << 16)).astype(np.float32)
+    g = golden("level_sets.json")
+    cases = (("mnz", None, g["mnz"]), ("lut", (-2, -1, 0, 1), g["standard_w2"]),
+             ("lut", (3, 10, -3, -10), [-10, -3, 3, 10]), ("pot", None, g["pot"]))
+    for kind, table, levels in cases:
+        s = O.weight_scales(x, kind, "f32", table, rule="mse")
+        mse = O.row_sq_error(x[0], s[0], kind, table) / x.shape[1]
+        best = O.best_scale_mse(levels)[1]
+        assert mse == pytest.approx(best, rel=0.02), (kind, table, mse, best)
+
+
+def pin_mse_rule_never_worse_than_absmax():
+    W = si.heavy_tailed_weights(12, 512, seed=55)
+    for kind, table in (("mnz", None), ("pot", None), ("int4", None), ("lut", (-2, -1, 0, 1))):
+        _, s_abs, wr = O.quantize_weights(W.astype(np.float64), 512, kind, "f16", table)
+        _, s_mse, _ = O.quantize_weights(W.astype(np.float64), 512, kind, "f16", table, "mse")
+        for n in range(12):
+            assert O.row_sq_error(wr[n], s_mse[n], kind, table) <= \
+                O.row_sq_error(wr[n], s_abs[n], kind, table)
+
+
+def pin_no_zero_sets_beat_standard_at_searched_scale():
+    """Abstract: the no-zero sets give lower error than the standard
+    {-2, -1, 0, +1} set; compared, as in its scale-invariant analysis, at
+    each set's best (searched) scale, on a rotated synthetic layer. Under the
+    absmax rules the order reverses (absmax / 1.5 leaves the MNZ inner levels
+    far too wide), which is why the comparison needs the searched scale."""
+    W = si.weights(32, 1024, seed=57).astype(np.float64)
+    err = {}
+    for name, kind, table in (("mnz", "mnz", None), ("pot", "pot", None),
+                              ("standard", "lut", (-2, -1, 0, 1)), ("pm1pm2", "lut", (-2, -1, 1, 2))):
+        for rule in ("mse", "absmax"):
+            _, s, wr = O.quantize_weights(W, 1024, kind, "f16", table, rule)
+            err[name, rule] = sum(O.row_sq_error(wr[n], s[n], kind, table) for n in range(32))
+    assert err["mnz", "mse"] < err["standard", "mse"]
+    assert err["pot", "mse"] < err["standard", "mse"]
+    assert err["mnz", "mse"] < err["pm1pm2", "mse"]
+    assert err["mnz", "absmax"] > err["standard", "absmax"]
+
+
+def test_table_tie_order():
+    pin_table_tie_order()
+
+
+def test_table_nearest_exact():
+    pin_table_nearest_exact()
+
+
+def test_table_reproduces_mnz_and_pot():
+    pin_table_reproduces_mnz_and_pot()
+
+
+def test_mse_scale_brute_force():
+    pin_mse_scale_brute_force()
+
+
+def test_mse_scale_matches_gaussian_optimum():
+    pin_mse_scale_matches_gaussian_optimum()
+
+
+def test_mse_rule_never_worse_than_absmax():
+    pin_mse_rule_never_worse_than_absmax()
+
+
+def test_no_zero_sets_beat_standard_at_searched_scale():
+    pin_no_zero_sets_beat_standard_at_searched_scale()
+
+
+# --------------------------------------------------------------------------
 # packing
 # --------------------------------------------------------------------------
 
