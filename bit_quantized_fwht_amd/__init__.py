@@ -21,7 +21,8 @@ LIB_PATH = os.path.join(_HERE, "libqift.so")
 # enums (qift.h)
 QIFT_OK, QIFT_ERR_INVALID_ARG, QIFT_ERR_ALIGNMENT, QIFT_ERR_UNSUPPORTED, QIFT_ERR_HIP = range(5)
 QIFT_F32, QIFT_BF16, QIFT_F16, QIFT_I32 = range(4)
-LEVELS = {"mnz": 0, "pot": 1, "int4": 2}
+LEVELS = {"mnz": 0, "pot": 1, "int4": 2, "lut": 3}
+SCALE_RULES = {"absmax": 0, "mse": 1}
 QIFT_MAX_ROW = 16384
 QIFT_MAX_HAD_BLOCK = 4096
 
@@ -63,6 +64,10 @@ def _load():
     vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32
     sig = {
         "qift_quantize_weights": [vp, c_st, i64, i64, i32, c_st, vp, vp, c_st, vp],
+        "qift_quantize_weights_ex": [vp, c_st, i64, i64, i32, c_st, ctypes.c_uint32, c_st, vp, vp,
+                                     c_st, vp],
+        "qift_w2a4_linear_ex": [vp, vp, i64, i64, vp, vp, c_st, c_st, ctypes.c_uint32, i64, vp,
+                                c_st, vp],
         "qift_rotate_quant_act": [vp, c_st, i64, i64, i32, vp, vp, vp, vp],
         "qift_w2a4_linear": [vp, vp, i64, i64, vp, vp, c_st, c_st, i64, vp, c_st, vp],
         "qift_kv4_quant": [vp, c_st, i64, i64, i64, i32, vp, vp, vp],
@@ -157,6 +162,25 @@ def _levels(levels) -> int:
     return int(levels)
 
 
+def level_table_word(table) -> int:
+    """Four integer levels (one per 2-bit code, each in [-15, 15]) -> the
+    uint32 level table of the C ABI (byte c = level of code c)."""
+    t = [int(v) for v in table]
+    if len(t) != 4:
+        raise ValueError("a level table has four entries")
+    return sum((v & 0xFF) << (8 * c) for c, v in enumerate(t))
+
+
+def _table_arg(levels, table) -> int:
+    if _levels(levels) == LEVELS["lut"]:
+        if table is None:
+            raise ValueError("levels='lut' needs a level table")
+        return level_table_word(table)
+    if table is not None:
+        raise ValueError("a level table is only used with levels='lut'")
+    return 0
+
+
 def code_words_per_row(K: int, levels) -> int:
     return K // 8 if _levels(levels) == LEVELS["int4"] else K // 16
 
@@ -171,10 +195,11 @@ def padded_channels(N: int) -> int:
 # ---------------------------------------------------------------------------
 
 def qift_quantize_weights(W, had_block: int, levels="mnz", scale_dtype=torch.float16,
-                          codes=None, scales=None, stream=None):
+                          codes=None, scales=None, stream=None, table=None, scale_rule="absmax"):
     """W [N, K] float32/bfloat16 -> (codes int32 [Np, K/16 or K/8] holding the
     uint32 words in the tiled layout (Np = N rounded up to 16), scales [N] in
-    scale_dtype)."""
+    scale_dtype). levels='lut' takes a level table (four integers);
+    scale_rule 'absmax' or 'mse' (qift_quantize_weights_ex)."""
     _dev_tensor(W, "W", (torch.float32, torch.bfloat16))
     N, K = W.shape
     lv = _levels(levels)
@@ -187,10 +212,11 @@ def qift_quantize_weights(W, had_block: int, levels="mnz", scale_dtype=torch.flo
     _dev_tensor(scales, "scales", (torch.float32, torch.float16))
     if codes.numel() < padded_channels(N) * code_words_per_row(K, lv) or scales.numel() < N:
         raise ValueError("codes or scales buffer too small")
-    st = _C.qift_quantize_weights(_ptr(W), _TORCH_TO_QIFT[W.dtype], N, K, had_block, lv,
-                                  _ptr(codes), _ptr(scales), _TORCH_TO_QIFT[scales.dtype],
-                                  _stream(stream, W.device))
-    _check(st, "qift_quantize_weights")
+    st = _C.qift_quantize_weights_ex(_ptr(W), _TORCH_TO_QIFT[W.dtype], N, K, had_block, lv,
+                                     _table_arg(lv, table), SCALE_RULES[scale_rule], _ptr(codes),
+                                     _ptr(scales), _TORCH_TO_QIFT[scales.dtype],
+                                     _stream(stream, W.device))
+    _check(st, "qift_quantize_weights_ex")
     return codes, scales
 
 
@@ -284,9 +310,10 @@ def qift_rotate_quant_act_batched(items, stream=None):
 
 
 def qift_w2a4_linear(xq, s_a, codes, scales, levels="mnz", out_dtype=torch.float32, Y=None,
-                     N=None, stream=None):
+                     N=None, stream=None, table=None):
     """(xq [M, K/2], s_a [M], codes [N, ...], scales [N]) -> Y [M, N] in
-    out_dtype (float32, bfloat16, or int32 for the raw accumulator)."""
+    out_dtype (float32, bfloat16, or int32 for the raw accumulator).
+    levels='lut' takes a level table (qift_w2a4_linear_ex)."""
     _dev_tensor(xq, "xq", (torch.uint8,))
     _dev_tensor(s_a, "s_a", (torch.float32,))
     _dev_tensor(codes, "codes", (torch.int32,))
@@ -303,10 +330,11 @@ def qift_w2a4_linear(xq, s_a, codes, scales, levels="mnz", out_dtype=torch.float
     _dev_tensor(Y, "Y", (torch.float32, torch.bfloat16, torch.int32))
     if Y.numel() < M * N:
         raise ValueError("Y too small for [M, N]")
-    st = _C.qift_w2a4_linear(_ptr(xq), _ptr(s_a), M, K, _ptr(codes), _ptr(scales),
-                             _TORCH_TO_QIFT[scales.dtype], _levels(levels), N, _ptr(Y),
-                             _TORCH_TO_QIFT[Y.dtype], _stream(stream, xq.device))
-    _check(st, "qift_w2a4_linear")
+    st = _C.qift_w2a4_linear_ex(_ptr(xq), _ptr(s_a), M, K, _ptr(codes), _ptr(scales),
+                                _TORCH_TO_QIFT[scales.dtype], _levels(levels),
+                                _table_arg(levels, table), N, _ptr(Y), _TORCH_TO_QIFT[Y.dtype],
+                                _stream(stream, xq.device))
+    _check(st, "qift_w2a4_linear_ex")
     return Y
 
 
@@ -334,7 +362,8 @@ class LinearGroup:
     """Many decode linears (M <= 16 each) run by one launch.
 
     ``items`` is a sequence of dicts with keys xq, s_a, codes, scales, Y and
-    levels (tensors already allocated on one device). The plan lives in a
+    levels, plus table for levels='lut' (tensors already allocated on one
+    device). The plan lives in a
     device workspace owned by this object; the tensors must stay alive.
     """
 
@@ -350,9 +379,11 @@ class LinearGroup:
             N = it.get("N", it["scales"].shape[0])
             for key in ("xq", "s_a", "codes", "scales", "Y"):
                 _dev_tensor(it[key], key)
+            tw = _table_arg(it["levels"], it.get("table"))  # the descriptor's int32 table word
             descs[i] = qift_linear_desc(it["xq"].data_ptr(), it["s_a"].data_ptr(),
                                         it["codes"].data_ptr(), it["scales"].data_ptr(),
-                                        it["Y"].data_ptr(), M, K, N, _levels(it["levels"]), 0)
+                                        it["Y"].data_ptr(), M, K, N, _levels(it["levels"]),
+                                        tw - (1 << 32) if tw >= 1 << 31 else tw)
             self._keep.append(it)
         nbytes = ctypes.c_size_t(0)
         _check(_C.qift_linear_group_workspace_bytes(descs, n, ctypes.byref(nbytes)),
@@ -376,4 +407,5 @@ class LinearGroup:
 __all__ = ["load_library", "QiftUnavailable", "qift_quantize_weights", "qift_rotate_quant_act",
            "qift_rotate_quant_act_batched", "RotateBatch", "qift_w2a4_linear", "qift_kv4_quant",
            "LinearGroup", "QiftError", "qift_linear_desc", "LEVELS", "status_string", "last_error",
-           "abi_version", "code_words_per_row", "padded_channels", "LIB_PATH"]
+           "abi_version", "code_words_per_row", "padded_channels", "LIB_PATH", "SCALE_RULES",
+           "level_table_word"]

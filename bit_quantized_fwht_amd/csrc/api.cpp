@@ -41,7 +41,26 @@ qift_status hip_result(hipError_t e, const char* what) {
 bool is_pow2(int64_t v) { return v > 0 && (v & (v - 1)) == 0; }
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 bool valid_levels(int lv) {
-  return lv == QIFT_LEVELS_MNZ || lv == QIFT_LEVELS_POT || lv == QIFT_LEVELS_INT4;
+  return lv == QIFT_LEVELS_MNZ || lv == QIFT_LEVELS_POT || lv == QIFT_LEVELS_INT4 ||
+         lv == QIFT_LEVELS_LUT;
+}
+
+// The table word of a call: a level table (four signed bytes, |L| <= 15, not
+// all zero) for QIFT_LEVELS_LUT, 0 for every other level kind.
+qift_status check_table(int levels, uint32_t table) {
+  if (levels != QIFT_LEVELS_LUT) {
+    if (table != 0) return fail(QIFT_ERR_INVALID_ARG, "level table given for levels %d", levels);
+    return QIFT_OK;
+  }
+  bool any = false;
+  for (int c = 0; c < 4; ++c) {
+    const int L = (int)(int8_t)((table >> (8 * c)) & 0xFFu);
+    if (L < -15 || L > 15)
+      return fail(QIFT_ERR_INVALID_ARG, "level table entry %d is %d, outside [-15, 15]", c, L);
+    any = any || L != 0;
+  }
+  if (!any) return fail(QIFT_ERR_INVALID_ARG, "level table is all zero");
+  return QIFT_OK;
 }
 
 constexpr int64_t kMaxLinearK = 65536;
@@ -62,6 +81,8 @@ qift_status check_linear(const qift_linear_desc& d, qift_dtype scale_dtype, qift
   if (d.K > kMaxLinearK)
     return fail(QIFT_ERR_UNSUPPORTED, "K=%lld exceeds %lld", (long long)d.K, (long long)kMaxLinearK);
   if (!valid_levels(d.levels)) return fail(QIFT_ERR_INVALID_ARG, "invalid levels %d", d.levels);
+  qift_status tst = check_table(d.levels, (uint32_t)d.reserved);
+  if (tst != QIFT_OK) return tst;
   if (scale_dtype != QIFT_F32 && scale_dtype != QIFT_F16)
     return fail(QIFT_ERR_INVALID_ARG, "scale_dtype must be F32 or F16");
   if (y_dtype != QIFT_F32 && y_dtype != QIFT_BF16 && y_dtype != QIFT_I32)
@@ -101,11 +122,23 @@ const char* qift_status_string(qift_status s) {
 qift_status qift_quantize_weights(const void* W, qift_dtype w_dtype, int64_t N, int64_t K,
                                   int32_t had_block, qift_levels levels, uint32_t* codes,
                                   void* scales, qift_dtype scale_dtype, qift_stream stream) {
+  return qift_quantize_weights_ex(W, w_dtype, N, K, had_block, levels, 0u, QIFT_SCALE_ABSMAX,
+                                  codes, scales, scale_dtype, stream);
+}
+
+qift_status qift_quantize_weights_ex(const void* W, qift_dtype w_dtype, int64_t N, int64_t K,
+                                     int32_t had_block, qift_levels levels, uint32_t level_table,
+                                     qift_scale_rule scale_rule, uint32_t* codes, void* scales,
+                                     qift_dtype scale_dtype, qift_stream stream) {
   if (w_dtype != QIFT_F32 && w_dtype != QIFT_BF16)
     return fail(QIFT_ERR_INVALID_ARG, "w_dtype must be F32 or BF16");
   if (scale_dtype != QIFT_F32 && scale_dtype != QIFT_F16)
     return fail(QIFT_ERR_INVALID_ARG, "scale_dtype must be F32 or F16");
   if (!valid_levels(levels)) return fail(QIFT_ERR_INVALID_ARG, "invalid levels %d", (int)levels);
+  qift_status tst = check_table((int)levels, level_table);
+  if (tst != QIFT_OK) return tst;
+  if (scale_rule != QIFT_SCALE_ABSMAX && scale_rule != QIFT_SCALE_MSE)
+    return fail(QIFT_ERR_INVALID_ARG, "invalid scale_rule %d", (int)scale_rule);
   if (N < 0) return fail(QIFT_ERR_INVALID_ARG, "negative N");
   if (K <= 0 || K % 64 != 0)
     return fail(QIFT_ERR_INVALID_ARG, "K=%lld must be a positive multiple of 64", (long long)K);
@@ -120,7 +153,8 @@ qift_status qift_quantize_weights(const void* W, qift_dtype w_dtype, int64_t N, 
   if (!aligned(W, w_dtype == QIFT_F32 ? 4 : 2) || !aligned(scales, scale_dtype == QIFT_F16 ? 2 : 4))
     return fail(QIFT_ERR_ALIGNMENT, "W or scales misaligned for its dtype");
   return hip_result(qift::launch_quantize_weights(W, w_dtype == QIFT_BF16, N, K, had_block,
-                                                  (int)levels, codes, scales,
+                                                  (int)levels, level_table,
+                                                  scale_rule == QIFT_SCALE_MSE, codes, scales,
                                                   scale_dtype == QIFT_F16,
                                                   reinterpret_cast<hipStream_t>(stream)),
                     "qift_quantize_weights launch");
@@ -200,7 +234,16 @@ qift_status qift_w2a4_linear(const uint8_t* xq, const float* s_a, int64_t M, int
                              const uint32_t* codes, const void* scales, qift_dtype scale_dtype,
                              qift_levels levels, int64_t N, void* Y, qift_dtype y_dtype,
                              qift_stream stream) {
+  return qift_w2a4_linear_ex(xq, s_a, M, K, codes, scales, scale_dtype, levels, 0u, N, Y, y_dtype,
+                             stream);
+}
+
+qift_status qift_w2a4_linear_ex(const uint8_t* xq, const float* s_a, int64_t M, int64_t K,
+                                const uint32_t* codes, const void* scales, qift_dtype scale_dtype,
+                                qift_levels levels, uint32_t level_table, int64_t N, void* Y,
+                                qift_dtype y_dtype, qift_stream stream) {
   qift_linear_desc d{};
+  d.reserved = (int32_t)level_table;
   d.xq = xq;
   d.s_a = s_a;
   d.codes = codes;
@@ -249,7 +292,6 @@ static qift_status check_group(const qift_linear_desc* descs, int32_t count, qif
   int64_t tiles = 0;
   for (int32_t i = 0; i < count; ++i) {
     const qift_linear_desc& d = descs[i];
-    if (d.reserved != 0) return fail(QIFT_ERR_INVALID_ARG, "descriptor %d: reserved field must be 0", i);
     qift_status st = check_linear(d, scale_dtype, y_dtype);
     if (st != QIFT_OK) {
       g_last_error = "descriptor " + std::to_string(i) + ": " + g_last_error;

@@ -30,7 +30,7 @@ struct Fmt {
 };
 
 template <int LV>
-__device__ __forceinline__ v4i weight_operand(const uint4& c, int step, MnzMasks k) {
+__device__ __forceinline__ v4i weight_operand(const uint4& c, int step, OpConsts k) {
   if constexpr (LV == QIFT_LEVELS_INT4) {
     const uint32_t w0 = step == 0 ? c.x : c.z;
     const uint32_t w1 = step == 0 ? c.y : c.w;
@@ -38,6 +38,7 @@ __device__ __forceinline__ v4i weight_operand(const uint4& c, int step, MnzMasks
   } else {
     const uint32_t w = step == 0 ? c.x : (step == 1 ? c.y : (step == 2 ? c.z : c.w));
     if constexpr (LV == QIFT_LEVELS_MNZ) return mnz_operand(w, k);
+    else if constexpr (LV == QIFT_LEVELS_LUT) return lut_operand(w, k.lut);
     else return pot_operand(w);
   }
 }

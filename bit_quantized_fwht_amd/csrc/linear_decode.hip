@@ -51,7 +51,7 @@ __device__ __forceinline__ void decode_wave(const qift_linear_desc& d, int64_t n
   const uint8_t* xq = d.xq;
   const uint32_t* codes = d.codes;
   const bool act_row = r16 < M;
-  const MnzMasks km = mnz_masks(d.reserved, lane);
+  const OpConsts km = op_consts(d.reserved, lane);
 
   v4i acc[kDecodeTiles];
 #pragma unroll
@@ -176,6 +176,7 @@ __device__ __forceinline__ void decode_dispatch(const qift_linear_desc& d, int64
   switch (d.levels) {
     case QIFT_LEVELS_MNZ: decode_wave<QIFT_LEVELS_MNZ>(d, n0, scale_f16, y_dtype, lane, epi); break;
     case QIFT_LEVELS_POT: decode_wave<QIFT_LEVELS_POT>(d, n0, scale_f16, y_dtype, lane, epi); break;
+    case QIFT_LEVELS_LUT: decode_wave<QIFT_LEVELS_LUT>(d, n0, scale_f16, y_dtype, lane, epi); break;
     default: decode_wave<QIFT_LEVELS_INT4>(d, n0, scale_f16, y_dtype, lane, epi); break;
   }
 }
@@ -224,7 +225,7 @@ __global__ __launch_bounds__(64 * S) void linear_decode_splitk_kernel(qift_linea
   const int64_t tn = blockIdx.x;  // 16-channel tile
   const int64_t nchunks = (K + F::kChunkK - 1) / F::kChunkK;
   const bool act_row = r16 < M;
-  const MnzMasks km = mnz_masks(d.reserved, lane);
+  const OpConsts km = op_consts(d.reserved, lane);
 
   struct Chunk {
     uint4 c, a0, a1;
@@ -358,6 +359,7 @@ hipError_t launch_linear_decode(const qift_linear_desc& d, int scale_f16, int y_
     switch (d.levels) {
       case QIFT_LEVELS_MNZ: return launch_decode_splitk<QIFT_LEVELS_MNZ>(d, scale_f16, y_dtype, s);
       case QIFT_LEVELS_POT: return launch_decode_splitk<QIFT_LEVELS_POT>(d, scale_f16, y_dtype, s);
+      case QIFT_LEVELS_LUT: return launch_decode_splitk<QIFT_LEVELS_LUT>(d, scale_f16, y_dtype, s);
       default: return launch_decode_splitk<QIFT_LEVELS_INT4>(d, scale_f16, y_dtype, s);
     }
   }

@@ -64,7 +64,7 @@ __device__ __forceinline__ void prefill_tile(const qift_linear_desc& d, int64_t 
   const int64_t cw = F::code_words(K);
   const int64_t tiles = (N + 15) >> 4;          // 16-channel weight tiles
   const int64_t arow = K / 2;                   // bytes per activation row
-  const MnzMasks km = mnz_masks(d.reserved, lane);
+  const OpConsts km = op_consts(d.reserved, lane);
   uint8_t* As = lds;                // stage buffer b: A at b * kStage, B after it
   uint8_t* Bs = lds + C::kBOffset;
 
@@ -361,7 +361,7 @@ __device__ __forceinline__ void prefill_tile_sk(const qift_linear_desc& d, int64
   const int64_t M = d.M, K = d.K, N = d.N;
   const int64_t arow = K / 2;
   const int64_t np16 = (N + 15) >> 4;
-  const MnzMasks km = mnz_masks(d.reserved, lane);
+  const OpConsts km = op_consts(d.reserved, lane);
 
   int64_t a_off[C::kAInstr];
 #pragma unroll
@@ -435,6 +435,8 @@ __device__ __forceinline__ void prefill_tile_sk(const qift_linear_desc& d, int64
           B[j] = s2 == 0 ? int4_operand(f.b[j].x, f.b[j].y) : int4_operand(f.b[j].z, f.b[j].w);
         else if constexpr (LV == QIFT_LEVELS_MNZ)
           B[j] = mnz_operand(s2 == 0 ? f.b[j].x : f.b[j].y, km);
+        else if constexpr (LV == QIFT_LEVELS_LUT)
+          B[j] = lut_operand(s2 == 0 ? f.b[j].x : f.b[j].y, km.lut);
         else
           B[j] = pot_operand(s2 == 0 ? f.b[j].x : f.b[j].y);
       }
@@ -584,6 +586,7 @@ hipError_t launch_linear_prefill(const qift_linear_desc& d, int scale_f16, int y
     switch (d.levels) {
       case QIFT_LEVELS_MNZ: QIFT_SK_LAUNCH(QIFT_LEVELS_MNZ) break;
       case QIFT_LEVELS_POT: QIFT_SK_LAUNCH(QIFT_LEVELS_POT) break;
+      case QIFT_LEVELS_LUT: QIFT_SK_LAUNCH(QIFT_LEVELS_LUT) break;
       default: QIFT_SK_LAUNCH(QIFT_LEVELS_INT4) break;
     }
 #undef QIFT_SK_LAUNCH
@@ -593,6 +596,10 @@ hipError_t launch_linear_prefill(const qift_linear_desc& d, int scale_f16, int y
   switch (d.levels) {
     case QIFT_LEVELS_MNZ:
       hipLaunchKernelGGL(linear_prefill_kernel<QIFT_LEVELS_MNZ>, grid, dim3(256), 0, s, d,
+                         scale_f16, y_dtype);
+      break;
+    case QIFT_LEVELS_LUT:
+      hipLaunchKernelGGL(linear_prefill_kernel<QIFT_LEVELS_LUT>, grid, dim3(256), 0, s, d,
                          scale_f16, y_dtype);
       break;
     case QIFT_LEVELS_POT:

@@ -81,24 +81,27 @@ __device__ __forceinline__ v4i int4_operand(uint32_t x0, uint32_t x1) {
   return a;
 }
 
-// The two masks of the MNZ operand held in vector registers. gfx9 VOP3
-// encodings take no literal constants, and the compiler only forms
-// v_and_or_b32 from (a & m) | o when m and o live in VGPRs; with literal or
-// scalar masks it emits v_and + v_or. The masks are therefore derived from a
-// per-lane value it cannot fold: zero * lane, with zero a descriptor field
-// that is always 0.
-struct MnzMasks {
-  uint32_t m, o;
+// Per-call operand constants, derived from the descriptor's table word (the
+// level table for QIFT_LEVELS_LUT, always 0 for the other levels):
+// - the two masks of the MNZ operand, held in vector registers. gfx9 VOP3
+//   encodings take no literal constants, and the compiler only forms
+//   v_and_or_b32 from (a & m) | o when m and o live in VGPRs; with literal or
+//   scalar masks it emits v_and + v_or. The masks are therefore derived from
+//   a per-lane value it cannot fold: word * lane, with word 0 for MNZ;
+// - the byte table of a level table: byte c = 8 * L[c] (|L| <= 15, so the
+//   byte is the exact signed value).
+struct OpConsts {
+  uint32_t m, o, lut;
 };
-__device__ __forceinline__ MnzMasks mnz_masks(int32_t zero, int lane) {
-  const uint32_t z = (uint32_t)zero * (uint32_t)lane;
-  return MnzMasks{0xC0C0C0C0u | z, 0x20202020u | z};
+__device__ __forceinline__ OpConsts op_consts(int32_t word, int lane) {
+  const uint32_t z = (uint32_t)word * (uint32_t)lane;
+  return OpConsts{0xC0C0C0C0u | z, 0x20202020u | z, ((uint32_t)word << 3) & 0xF8F8F8F8u};
 }
 
 // 2-bit MNZ codes (one word, 16 features) -> 32*(2t+1) per byte: the code t
 // lands in the two top bits of its byte (64t as a signed byte) and bit 5 adds
 // 32. Seven VALU instructions per 16 codes.
-__device__ __forceinline__ v4i mnz_operand(uint32_t c, MnzMasks k) {
+__device__ __forceinline__ v4i mnz_operand(uint32_t c, OpConsts k) {
   v4i b;
   b[0] = (int)(((c << 6) & k.m) | k.o);
   b[1] = (int)(((c << 4) & k.m) | k.o);
@@ -119,9 +122,23 @@ __device__ __forceinline__ v4i pot_operand(uint32_t c) {
   return b;
 }
 
+// 2-bit codes of a level table -> 8 * L[code] per byte through the per-call
+// byte table (the PoT decode with a run-time table).
+__device__ __forceinline__ v4i lut_operand(uint32_t c, uint32_t lut) {
+  v4i b;
+  b[0] = (int)__builtin_amdgcn_perm(0u, lut, c & 0x03030303u);
+  b[1] = (int)__builtin_amdgcn_perm(0u, lut, (c >> 2) & 0x03030303u);
+  b[2] = (int)__builtin_amdgcn_perm(0u, lut, (c >> 4) & 0x03030303u);
+  b[3] = (int)__builtin_amdgcn_perm(0u, lut, (c >> 6) & 0x03030303u);
+  return b;
+}
+
 // Right shift that turns the matrix-core sum back into sum q * level:
-// MNZ 16 * 32 = 2^9, PoT 16 * 16 = 2^8, INT4 16 * 16 = 2^8.
-__host__ __device__ constexpr int acc_shift(int levels) { return levels == QIFT_LEVELS_MNZ ? 9 : 8; }
+// MNZ 16 * 32 = 2^9, PoT 16 * 16 = 2^8, INT4 16 * 16 = 2^8, level table
+// 16 * 8 = 2^7.
+__host__ __device__ constexpr int acc_shift(int levels) {
+  return levels == QIFT_LEVELS_MNZ ? 9 : (levels == QIFT_LEVELS_LUT ? 7 : 8);
+}
 __host__ __device__ constexpr float level_kappa(int levels) {
   return levels == QIFT_LEVELS_MNZ ? 0.5f : 1.0f;
 }
@@ -191,8 +208,8 @@ hipError_t launch_rotate_quant_act_batched(const RotJob* jobs, const int64_t* ro
 hipError_t launch_rotate_quant_act(const void* X, int x_bf16, int64_t M, int64_t K, int had_block,
                                    uint8_t* xq, float* s_a, float* x_rot, hipStream_t s);
 hipError_t launch_quantize_weights(const void* W, int w_bf16, int64_t N, int64_t K, int had_block,
-                                   int levels, uint32_t* codes, void* scales, int scale_f16,
-                                   hipStream_t s);
+                                   int levels, uint32_t table, int mse_rule, uint32_t* codes,
+                                   void* scales, int scale_f16, hipStream_t s);
 hipError_t launch_kv4(const void* KV, int bf16, int64_t rows, int D, int had_block, uint8_t* kvq,
                       float* scales, hipStream_t s);
 hipError_t launch_linear_decode(const qift_linear_desc& d, int scale_f16, int y_dtype,

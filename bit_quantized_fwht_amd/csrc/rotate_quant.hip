@@ -472,6 +472,58 @@ __device__ __forceinline__ uint32_t code_pot(float w, float s) {
   return ((neg ? 1u : 0u) << 1) | (outer ? 1u : 0u);
 }
 
+// Level table: code of the level nearest to w, distances |w - L[c] * s| in
+// double (L[c] * s is exact there), the codes visited in the tie-break order
+// `pref` (byte r = the code of rank r: smaller |L|, then the non-negative
+// level, then the lower code) so that the first minimum wins.
+__device__ __forceinline__ uint32_t code_lut(float w, float s, uint32_t table, uint32_t pref) {
+  double best = __builtin_huge_val();
+  uint32_t code = pref & 3u;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const uint32_t c = (pref >> (8 * r)) & 3u;
+    const double L = (double)(int8_t)((table >> (8 * c)) & 0xFFu);
+    const double dist = fabs((double)w - L * (double)s);
+    if (dist < best) {
+      best = dist;
+      code = c;
+    }
+  }
+  return code;
+}
+
+__device__ __forceinline__ uint32_t code2(int levels, float w, float s, uint32_t table,
+                                          uint32_t pref) {
+  return levels == QIFT_LEVELS_MNZ ? code_mnz(w, s)
+         : levels == QIFT_LEVELS_POT ? code_pot(w, s)
+                                     : code_lut(w, s, table, pref);
+}
+
+// The multiple of the scale that 2-bit code c stands for.
+__device__ __forceinline__ double real_level(int levels, uint32_t c, uint32_t table) {
+  if (levels == QIFT_LEVELS_MNZ) return 0.5 * (double)(2 * (c >= 2u ? (int)c - 4 : (int)c) + 1);
+  if (levels == QIFT_LEVELS_POT) return ((c & 2u) ? -1.0 : 1.0) * ((c & 1u) ? 4.0 : 1.0);
+  return (double)(int8_t)((table >> (8 * c)) & 0xFFu);
+}
+
+// Sum of v over the workgroup in a fixed order (every thread gets the same
+// value).
+__device__ __forceinline__ double block_sum(double v, double* red, int tid) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+  if ((tid & 63) == 0) red[tid >> 6] = v;
+  __syncthreads();
+  double r = red[0];
+#pragma unroll
+  for (int w = 1; w < kRowThreads / 64; ++w) r += red[w];
+  __syncthreads();
+  return r;
+}
+
+__device__ __forceinline__ float stored_scale(float s32, int scale_f16) {
+  return scale_f16 ? __half2float(__float2half_rn(s32)) : s32;
+}
+
 __device__ __forceinline__ int code_bit_offset(int i) {
   return 8 * ((i >> 1) & 3) + 4 * (i >> 3) + 2 * (i & 1);
 }
@@ -489,12 +541,18 @@ __device__ __forceinline__ int64_t tiled_word(int64_t n, int64_t w, int64_t W, i
   return c * 256 * T + r * 16 * uc + (16 * g + i) * 4 + j;
 }
 
+// Candidates of the searched scale: fractions (64 - j) / 64 of the absmax
+// scale, j = 0 .. kScaleCandidates - 1.
+constexpr int kScaleCandidates = 64;
+
 template <typename T>
 __global__ __launch_bounds__(kRowThreads) void quantize_weights_kernel(
-    const T* __restrict__ W, int64_t N, int K, int log2b, float norm, int levels,
-    uint32_t* __restrict__ codes, void* __restrict__ scales, int scale_f16) {
+    const T* __restrict__ W, int64_t N, int K, int log2b, float norm, int levels, uint32_t table,
+    uint32_t pref, float outer, int mse_rule, uint32_t* __restrict__ codes,
+    void* __restrict__ scales, int scale_f16) {
   extern __shared__ float row[];
   __shared__ float red[kRowThreads / 64];
+  __shared__ double red64[kRowThreads / 64];
   const int tid = threadIdx.x;
   const int64_t n = blockIdx.x;
   const bool int4 = levels == QIFT_LEVELS_INT4;
@@ -508,16 +566,37 @@ __global__ __launch_bounds__(kRowThreads) void quantize_weights_kernel(
   __syncthreads();
   fwht_row(row, K, log2b, tid);
   const float amax = row_absmax(row, K, norm, tid, red);
-  const float outer = levels == QIFT_LEVELS_MNZ ? 1.5f : (levels == QIFT_LEVELS_POT ? 4.0f : 7.0f);
-  const float s32 = __fdiv_rn(amax, outer);
-  float s;
-  if (scale_f16) {
-    const __half h = __float2half_rn(s32);
-    s = __half2float(h);
-    if (tid == 0) reinterpret_cast<__half*>(scales)[n] = h;
-  } else {
-    s = s32;
-    if (tid == 0) reinterpret_cast<float*>(scales)[n] = s32;
+  float s32 = __fdiv_rn(amax, outer);
+  if (mse_rule) {
+    // least squares over the candidates s_j = fl32(s32 * (64 - j) / 64),
+    // each rounded to the stored dtype with codes decided against it; the
+    // first (largest) candidate wins ties
+    const float base = s32;
+    double best = __builtin_huge_val();
+    for (int j = 0; j < kScaleCandidates; ++j) {
+      const float cand = base * ((float)(kScaleCandidates - j) / (float)kScaleCandidates);
+      const float sj = stored_scale(cand, scale_f16);
+      double e = 0.0;
+      for (int i = tid; i < K; i += kRowThreads) {
+        const float w = row[i] * norm;
+        const double lv = int4 ? (double)quant_int4(w, sj)
+                               : real_level(levels, code2(levels, w, sj, table, pref), table);
+        const double d = (double)w - lv * (double)sj;
+        e += d * d;
+      }
+      e = block_sum(e, red64, tid);
+      if (e < best) {
+        best = e;
+        s32 = cand;
+      }
+    }
+  }
+  const float s = stored_scale(s32, scale_f16);
+  if (tid == 0) {
+    if (scale_f16)
+      reinterpret_cast<__half*>(scales)[n] = __float2half_rn(s32);
+    else
+      reinterpret_cast<float*>(scales)[n] = s32;
   }
   if (int4) {
     for (int g = tid; g < (K >> 3); g += kRowThreads) {
@@ -528,14 +607,12 @@ __global__ __launch_bounds__(kRowThreads) void quantize_weights_kernel(
       codes[tiled_word(n, g, words, tiles)] = word;
     }
   } else {
-    const bool pot = levels == QIFT_LEVELS_POT;
     for (int g = tid; g < (K >> 4); g += kRowThreads) {
       uint32_t word = 0;
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const float w = row[16 * g + i] * norm;
-        const uint32_t c = pot ? code_pot(w, s) : code_mnz(w, s);
-        word |= c << code_bit_offset(i);
+        word |= code2(levels, w, s, table, pref) << code_bit_offset(i);
       }
       codes[tiled_word(n, g, words, tiles)] = word;
     }
@@ -609,20 +686,40 @@ hipError_t launch_rotate_quant_act_batched(const RotJob* jobs, const int64_t* ro
 }
 
 hipError_t launch_quantize_weights(const void* W, int w_bf16, int64_t N, int64_t K, int had_block,
-                                   int levels, uint32_t* codes, void* scales, int scale_f16,
-                                   hipStream_t s) {
+                                   int levels, uint32_t table, int mse_rule, uint32_t* codes,
+                                   void* scales, int scale_f16, hipStream_t s) {
   const size_t lds = (size_t)K * sizeof(float);
   const int lb = ilog2(had_block);
   const float nrm = had_norm(had_block);
   const unsigned grid = (unsigned)((N + 15) / 16 * 16);  // padded to whole 16-channel tiles
+  // outer level of the absmax rule; for a level table max |L| and the codes
+  // in tie-break order (smaller |L|, non-negative first, lower code)
+  float outer = levels == QIFT_LEVELS_MNZ ? 1.5f : levels == QIFT_LEVELS_POT ? 4.0f : 7.0f;
+  uint32_t pref = 0;
+  if (levels == QIFT_LEVELS_LUT) {
+    int L[4], order[4] = {0, 1, 2, 3}, mx = 0;
+    for (int c = 0; c < 4; ++c) {
+      L[c] = (int)(int8_t)((table >> (8 * c)) & 0xFFu);
+      mx = L[c] < 0 ? (-L[c] > mx ? -L[c] : mx) : (L[c] > mx ? L[c] : mx);
+    }
+    auto key = [&](int c) { return (L[c] < 0 ? -L[c] : L[c]) * 16 + (L[c] < 0 ? 8 : 0) + c; };
+    for (int i = 1; i < 4; ++i)
+      for (int j = i; j > 0 && key(order[j]) < key(order[j - 1]); --j) {
+        const int tmp = order[j];
+        order[j] = order[j - 1];
+        order[j - 1] = tmp;
+      }
+    for (int r = 0; r < 4; ++r) pref |= (uint32_t)order[r] << (8 * r);
+    outer = (float)mx;
+  }
   if (w_bf16)
     hipLaunchKernelGGL(quantize_weights_kernel<uint16_t>, dim3(grid), dim3(kRowThreads), lds, s,
-                       reinterpret_cast<const uint16_t*>(W), N, (int)K, lb, nrm, levels, codes,
-                       scales, scale_f16);
+                       reinterpret_cast<const uint16_t*>(W), N, (int)K, lb, nrm, levels, table,
+                       pref, outer, mse_rule, codes, scales, scale_f16);
   else
     hipLaunchKernelGGL(quantize_weights_kernel<float>, dim3(grid), dim3(kRowThreads), lds, s,
-                       reinterpret_cast<const float*>(W), N, (int)K, lb, nrm, levels, codes,
-                       scales, scale_f16);
+                       reinterpret_cast<const float*>(W), N, (int)K, lb, nrm, levels, table, pref,
+                       outer, mse_rule, codes, scales, scale_f16);
   return hipGetLastError();
 }
 

@@ -61,6 +61,12 @@
  *                     (00 -> +s, 01 -> +4s, 10 -> -s, 11 -> -4s)
  *   QIFT_LEVELS_INT4: 4-bit two's-complement weights in [-7, 7]
  *                     (the 4-bit layers of an L-layer mixed W2/W4 stack).
+ *   QIFT_LEVELS_LUT : a level table (the level-set comparisons of the
+ *                     abstract: the standard {-2,-1,0,+1} set, a Lloyd-like
+ *                     {+-3, +-10}, ...): a uint32 whose byte c is the signed
+ *                     integer level L[c] in [-15, 15] of code c (not all
+ *                     zero); weight = L[c] * s. {1, 3, -3, -1} decodes MNZ
+ *                     codes at step s/2, {1, 4, -1, -4} PoT codes.
  *
  * Hadamard rotation
  * -----------------
@@ -79,7 +85,7 @@
 extern "C" {
 #endif
 
-#define QIFT_ABI_VERSION 2
+#define QIFT_ABI_VERSION 3
 
 typedef enum {
   QIFT_OK = 0,
@@ -94,8 +100,15 @@ typedef enum { QIFT_F32 = 0, QIFT_BF16 = 1, QIFT_F16 = 2, QIFT_I32 = 3 } qift_dt
 typedef enum {
   QIFT_LEVELS_MNZ = 0,  /* {+-0.5, +-1.5} * s, 2-bit codes              */
   QIFT_LEVELS_POT = 1,  /* {+-1, +-4} * s, 2-bit codes, sign-and-shift  */
-  QIFT_LEVELS_INT4 = 2  /* [-7, 7] * s, 4-bit codes                     */
+  QIFT_LEVELS_INT4 = 2, /* [-7, 7] * s, 4-bit codes                     */
+  QIFT_LEVELS_LUT = 3   /* table[code] * s, 2-bit codes (level table)   */
 } qift_levels;
+
+/* Per-channel scale rule of the weight quantizer. */
+typedef enum {
+  QIFT_SCALE_ABSMAX = 0, /* s = absmax / outer level                        */
+  QIFT_SCALE_MSE = 1     /* the best of 64 fractions of it (least squares)  */
+} qift_scale_rule;
 
 typedef void* qift_stream; /* a hipStream_t */
 
@@ -129,6 +142,34 @@ typedef void* qift_stream; /* a hipStream_t */
 qift_status qift_quantize_weights(const void* W, qift_dtype w_dtype, int64_t N, int64_t K,
                                   int32_t had_block, qift_levels levels, uint32_t* codes,
                                   void* scales, qift_dtype scale_dtype, qift_stream stream);
+
+/*
+ * qift_quantize_weights_ex -- qift_quantize_weights with a level table and a
+ * scale rule (Qift abstract: the inner/outer ratio analysis, the standard
+ * two-bit set as the baseline, and a scale-invariant comparison of level
+ * sets, i.e. each set at its best scale).
+ *
+ *   levels       any qift_levels value; QIFT_LEVELS_LUT uses level_table
+ *   level_table  QIFT_LEVELS_LUT: byte c = L[c] (signed, |L| <= 15, not all
+ *                zero); must be 0 for the other levels
+ *   scale_rule   QIFT_SCALE_ABSMAX: s = absmax / outer, outer = 1.5 (MNZ),
+ *                4 (POT), 7 (INT4), max |L| (LUT), as qift_quantize_weights.
+ *                QIFT_SCALE_MSE: the candidates
+ *                  s_j = store(fl32(fl32(absmax / outer) * (64 - j) / 64)),
+ *                j = 0..63 (store = rounding to scale_dtype), are each tried
+ *                with codes decided against s_j, and the one with the
+ *                smallest sum over the row of (w' - level * s_j)^2 (float64
+ *                sums) is kept, the largest on ties (up to the order of the
+ *                float64 sum, which may decide between candidates whose errors
+ *                differ in the last bits).
+ * LUT codes: the level nearest to w' (distances |w' - L[c] * s| in float64),
+ * ties to the smaller |L[c]|, then the non-negative level, then the lower
+ * code. Other arguments, layouts and errors as qift_quantize_weights.
+ */
+qift_status qift_quantize_weights_ex(const void* W, qift_dtype w_dtype, int64_t N, int64_t K,
+                                     int32_t had_block, qift_levels levels, uint32_t level_table,
+                                     qift_scale_rule scale_rule, uint32_t* codes, void* scales,
+                                     qift_dtype scale_dtype, qift_stream stream);
 
 /*
  * qift_rotate_quant_act -- online activation path (Qift abstract: rotated
@@ -205,6 +246,20 @@ qift_status qift_w2a4_linear(const uint8_t* xq, const float* s_a, int64_t M, int
                              qift_stream stream);
 
 /*
+ * qift_w2a4_linear_ex -- qift_w2a4_linear for any qift_levels value,
+ * including a level table (the level-set comparisons of the Qift abstract run
+ * through the same decoded linear): with QIFT_LEVELS_LUT,
+ *   acc[m, n] = sum_k q[m, k] * L[code[n, k]]   (exact, int32)
+ *   Y[m, n]   = acc[m, n] * s_a[m] * s_w[n]
+ * level_table as in qift_quantize_weights_ex (0 for the other levels). K is
+ * limited to 65536 as for the other levels (|sum| <= 7 * 15 * 65536).
+ */
+qift_status qift_w2a4_linear_ex(const uint8_t* xq, const float* s_a, int64_t M, int64_t K,
+                                const uint32_t* codes, const void* scales, qift_dtype scale_dtype,
+                                qift_levels levels, uint32_t level_table, int64_t N, void* Y,
+                                qift_dtype y_dtype, qift_stream stream);
+
+/*
  * qift_kv4_quant -- KV4 (Qift abstract: rotated W2A4/KV4 inference): each
  * head vector KV[t, h, :] is rotated in blocks of had_block along D, then
  * quantized to int4 with its own scale s = max|v'| / 7, exactly as the
@@ -246,7 +301,8 @@ typedef struct qift_linear_desc {
   void* Y;                /* [M, N], dtype given to prepare        */
   int64_t M, K, N;
   int32_t levels;         /* a qift_levels value                   */
-  int32_t reserved;       /* must be 0                             */
+  int32_t reserved;       /* QIFT_LEVELS_LUT: the level table;     */
+                          /* other levels: must be 0               */
 } qift_linear_desc;
 
 qift_status qift_linear_group_workspace_bytes(const qift_linear_desc* descs, int32_t count,

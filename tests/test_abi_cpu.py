@@ -32,10 +32,10 @@ def test_library_loads_and_exports_every_declared_symbol():
     lib = q.load_library()
     names = declared_functions()
     assert "qift_w2a4_linear" in names and "qift_kv4_quant" in names
-    assert len(names) == 11, names
+    assert len(names) == 13, names
     for n in names:
         assert hasattr(lib, n), n
-    assert q.abi_version() == 2
+    assert q.abi_version() == 3
     for s in range(5):
         assert q.status_string(s).startswith("QIFT_")
 
@@ -191,6 +191,64 @@ def make_desc(**kw):
     d.update(kw)
     return q.qift_linear_desc(d["xq"], d["s_a"], d["codes"], d["scales"], d["Y"], d["M"], d["K"],
                               d["N"], d["levels"], d["reserved"])
+
+
+def lin_ex(table, **kw):
+    args = dict(xq=A16, s_a=A16b, M=4, K=256, codes=A16c, scales=A16d, sd=q.QIFT_F16, lv=3,
+                N=64, Y=A16e, yd=q.QIFT_F32)
+    args.update(kw)
+    return q._C.qift_w2a4_linear_ex(args["xq"], args["s_a"], args["M"], args["K"], args["codes"],
+                                    args["scales"], args["sd"], args["lv"], table, args["N"],
+                                    args["Y"], args["yd"], None)
+
+
+@pytest.mark.parametrize("table,lv,status", [
+    (q.level_table_word((-2, -1, 0, 1)), 3, q.QIFT_OK),
+    (q.level_table_word((3, 10, -3, -10)), 3, q.QIFT_OK),
+    (q.level_table_word((15, -15, 0, 0)), 3, q.QIFT_OK),
+    (0, 3, q.QIFT_ERR_INVALID_ARG),                                # all zero
+    (q.level_table_word((16, 1, 1, 1)), 3, q.QIFT_ERR_INVALID_ARG),  # |L| > 15
+    (q.level_table_word((1, -16, 1, 1)), 3, q.QIFT_ERR_INVALID_ARG),
+    (q.level_table_word((1, 3, -3, -1)), 0, q.QIFT_ERR_INVALID_ARG),  # table with MNZ
+])
+def test_linear_ex_table_rules(table, lv, status):
+    # M = 0: a valid call is a no-op; invalid tables are rejected first
+    assert lin_ex(table, lv=lv, M=0) == status
+
+
+def test_linear_without_table_rejects_lut():
+    assert lin(lv=3, M=0) == q.QIFT_ERR_INVALID_ARG
+    assert "table" in q.last_error()
+
+
+def qw_ex(table, lv, rule, **kw):
+    args = dict(W=A16, wd=q.QIFT_F32, N=0, K=256, B=256, codes=A16c, scales=A16d, sd=q.QIFT_F16)
+    args.update(kw)
+    return q._C.qift_quantize_weights_ex(args["W"], args["wd"], args["N"], args["K"], args["B"],
+                                         lv, table, rule, args["codes"], args["scales"], args["sd"],
+                                         None)
+
+
+@pytest.mark.parametrize("table,lv,rule,status", [
+    (q.level_table_word((-2, -1, 0, 1)), 3, 0, q.QIFT_OK),
+    (q.level_table_word((-2, -1, 0, 1)), 3, 1, q.QIFT_OK),
+    (0, 0, 1, q.QIFT_OK),
+    (0, 2, 1, q.QIFT_OK),
+    (0, 3, 0, q.QIFT_ERR_INVALID_ARG),
+    (q.level_table_word((1, 4, -1, -4)), 1, 0, q.QIFT_ERR_INVALID_ARG),
+    (0, 0, 2, q.QIFT_ERR_INVALID_ARG),
+])
+def test_quantize_weights_ex_rules(table, lv, rule, status):
+    assert qw_ex(table, lv, rule) == status
+
+
+def test_group_accepts_level_tables():
+    nbytes = ctypes.c_size_t(0)
+    tw = q.level_table_word((3, 10, -3, -10))
+    ok = (q.qift_linear_desc * 2)(make_desc(), make_desc(levels=3, reserved=tw))
+    assert q._C.qift_linear_group_workspace_bytes(ok, 2, ctypes.byref(nbytes)) == q.QIFT_OK
+    bad = (q.qift_linear_desc * 1)(make_desc(levels=3, reserved=0))
+    assert q._C.qift_linear_group_workspace_bytes(bad, 1, ctypes.byref(nbytes)) == q.QIFT_ERR_INVALID_ARG
 
 
 def test_group_workspace_and_rejects():

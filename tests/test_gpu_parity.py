@@ -419,6 +419,150 @@ def test_kv4_bitexact_given_rotated_input():
 
 
 # ---------------------------------------------------------------------------
+# level tables (QIFT_LEVELS_LUT) and the searched scale
+# ---------------------------------------------------------------------------
+
+TABLES = [(-2, -1, 0, 1), (3, 10, -3, -10), (15, -15, 1, -1)]
+
+
+def run_linear_lut(qa, codes, s_a, s_w, table, out_dtype):
+    xq = torch.from_numpy(O.pack_int4(qa)).to(DEV)
+    cw = u32_to_dev(O.pack_weights(codes, "lut"))
+    Y = q.qift_w2a4_linear(xq, to_dev(s_a), cw, to_dev(s_w.astype(np.float32), torch.float16),
+                           "lut", out_dtype, table=table)
+    sync()
+    return Y
+
+
+# decode with K split over 4, 16 and 8 waves, 64-channel decode waves, prefill
+# with 64- and 128-row tiles, the general prefill kernel (K % 256 != 0)
+LUT_SHAPES = [(1, 256, 17), (4, 4096, 257), (3, 3072, 4100), (2, 256, 131100), (17, 256, 130),
+              (64, 4096, 256), (1000, 256, 8200), (129, 576, 200)]
+
+
+@pytest.mark.parametrize("table", TABLES)
+@pytest.mark.parametrize("M,K,N", LUT_SHAPES)
+def test_lut_linear_int32_bitexact(table, M, K, N):
+    qa, codes, s_a, s_w = random_linear_inputs(M, K, N, "lut", seed=M * 7 + K + N)
+    say(f"linear lut {table} M={M} K={K} N={N}")
+    Y = run_linear_lut(qa, codes, s_a, s_w, table, torch.int32).cpu().numpy()
+    acc, _ = O.linear(qa, s_a, codes, s_w.astype(np.float64), "lut", table)
+    assert np.array_equal(Y.astype(np.int64), acc)
+
+
+@pytest.mark.parametrize("M", [3, 40])  # decode and prefill kernels
+def test_lut_linear_float_epilogue(M):
+    K, N, table = 512, 200, (3, 10, -3, -10)
+    qa, codes, s_a, s_w = random_linear_inputs(M, K, N, "lut", seed=61 + M)
+    say(f"linear lut float M={M}")
+    _, y = O.linear(qa, s_a, codes, s_w.astype(np.float64), "lut", table)
+    Yf = run_linear_lut(qa, codes, s_a, s_w, table, torch.float32).cpu().numpy().astype(np.float64)
+    assert np.all(np.abs(Yf - y) <= 4e-7 * np.abs(y) + 1e-30)
+
+
+def test_lut_extremes_do_not_overflow():
+    """All activations +-7 against levels +-15 at the largest K."""
+    M, K, N = 17, 65536, 16
+    qa = np.full((M, K), 7)
+    qa[1::2] = -7
+    codes = np.zeros((N, K), np.int64)
+    codes[1::2] = 1
+    table = (15, -15, 1, -1)
+    s_a = np.ones(M, np.float32)
+    s_w = np.ones(N, np.float16)
+    say("linear lut extremes")
+    for m_sub in (16, 17):
+        Y = run_linear_lut(qa[:m_sub], codes, s_a[:m_sub], s_w, table, torch.int32).cpu().numpy()
+        acc, _ = O.linear(qa[:m_sub], s_a[:m_sub], codes, s_w.astype(np.float64), "lut", table)
+        assert np.array_equal(Y.astype(np.int64), acc)
+
+
+@pytest.mark.parametrize("kind,table", [("mnz", (1, 3, -3, -1)), ("pot", (1, 4, -1, -4))])
+def test_lut_decodes_mnz_and_pot_codes(kind, table):
+    """MNZ (PoT) codes read through the table {1, 3, -3, -1} ({1, 4, -1, -4})
+    give the MNZ (PoT) integer sums."""
+    for M, K, N in ((2, 1024, 100), (48, 512, 256)):
+        qa, codes, s_a, s_w = random_linear_inputs(M, K, N, kind, seed=71 + M)
+        say(f"lut decodes {kind} M={M}")
+        a = run_linear(qa, codes, s_a, s_w, kind, torch.int32)
+        b = run_linear_lut(qa, codes, s_a, s_w, table, torch.int32)
+        assert torch.equal(a, b)
+
+
+def test_lut_in_grouped_launch():
+    shapes = [(1, 4096, 1000, "mnz", None), (4, 512, 300, "lut", (3, 10, -3, -10)),
+              (16, 256, 64, "lut", (-2, -1, 0, 1)), (2, 1024, 200, "pot", None)]
+    items, refs = [], []
+    for i, (M, K, N, kind, table) in enumerate(shapes):
+        qa, codes, s_a, s_w = random_linear_inputs(M, K, N, kind, seed=950 + i)
+        Y = torch.full((M, N), -1, dtype=torch.int32, device=DEV)
+        items.append(dict(xq=torch.from_numpy(O.pack_int4(qa)).to(DEV), s_a=to_dev(s_a),
+                          codes=u32_to_dev(O.pack_weights(codes, kind)),
+                          scales=to_dev(s_w.astype(np.float32), torch.float16), Y=Y, levels=kind,
+                          table=table))
+        refs.append(O.linear(qa, s_a, codes, s_w.astype(np.float64), kind, table)[0])
+    say("grouped linear with level tables")
+    grp = q.LinearGroup(items, scale_dtype=torch.float16, y_dtype=torch.int32)
+    grp.run()
+    sync()
+    for it, ref in zip(items, refs):
+        assert np.array_equal(it["Y"].cpu().numpy().astype(np.int64), ref)
+
+
+@pytest.mark.parametrize("table", TABLES + [(0, 5, -5, 1), (2, 2, -2, -2)])
+@pytest.mark.parametrize("sdt", ["f16", "f32"])
+def test_lut_quantizer_bitexact_given_rotated_input(table, sdt):
+    N, K = 37, 512
+    W = si.weights(N, K, seed=81, sigma=0.02)
+    wr32 = O.rotate(W.astype(np.float64), 256).astype(np.float32)
+    # exact midpoints between levels (ties) in the first row, a zero row
+    s0 = O.absmax_scales(wr32[:1], "lut", sdt, table).astype(np.float64)[0]
+    mids = np.array([(a + b) / 2 * s0 for a in table for b in table], np.float32)
+    wr32[0, :mids.size] = mids
+    wr32[0, mids.size] = max(abs(v) for v in table) * s0  # keeps the absmax
+    wr32[1] = 0.0
+    say(f"lut weights {table} {sdt}")
+    codes, scales = q.qift_quantize_weights(to_dev(wr32), 1, "lut", SCALE_T[sdt], table=table)
+    sync()
+    co, so, _ = O.quantize_weights(wr32.astype(np.float64), 1, "lut", sdt, table)
+    assert np.array_equal(scales.float().cpu().numpy().view(np.uint32),
+                          so.astype(np.float32).view(np.uint32))
+    assert np.array_equal(O.unpack_weights(dev_u32(codes), N, "lut"), co)
+
+
+@pytest.mark.parametrize("kind,table", [("mnz", None), ("pot", None), ("int4", None),
+                                        ("lut", (-2, -1, 0, 1)), ("lut", (3, 10, -3, -10))])
+@pytest.mark.parametrize("sdt", ["f16", "f32"])
+def test_mse_scale_quantizer(kind, table, sdt):
+    """Searched scale: the GPU's choice is the oracle's least-squares
+    candidate (or one whose float64 error ties it to 1e-12), and the codes are
+    exactly the oracle's nearest codes for the GPU's scale."""
+    N, K = 24, 1024
+    W = si.heavy_tailed_weights(N, K, seed=83)
+    W[3] = 0.0
+    wr32 = O.rotate(W.astype(np.float64), 1024).astype(np.float32)
+    say(f"mse scale {kind} {table} {sdt}")
+    codes, scales = q.qift_quantize_weights(to_dev(wr32), 1, kind, SCALE_T[sdt], table=table,
+                                            scale_rule="mse")
+    sync()
+    sg = scales.cpu().numpy()
+    _, so, _ = O.quantize_weights(wr32.astype(np.float64), 1, kind, sdt, table, "mse")
+    cand = O.scale_candidates(wr32, kind, sdt, table)
+    for n in range(N):
+        assert sg[n] in cand[n]
+        if sg[n] != so[n]:
+            eg = O.row_sq_error(wr32[n], sg[n], kind, table)
+            eo = O.row_sq_error(wr32[n], so[n], kind, table)
+            assert eg <= eo * (1 + 1e-12), (n, sg[n], so[n], eg, eo)
+    cg = O.unpack_weights(dev_u32(codes), N, kind)
+    if kind == "int4":
+        co = O.int4_weight_codes(wr32, sg)
+    else:
+        co = O.nearest_codes(wr32, sg, kind, table)
+    assert np.array_equal(cg, co)
+
+
+# ---------------------------------------------------------------------------
 # grouped launch == single calls
 # ---------------------------------------------------------------------------
 
