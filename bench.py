@@ -17,7 +17,10 @@ and float32 output under the "_f32_out" keys) and for a 512-token up_proj
 chunk; the
 LLaMA-3.1-8B-shaped power-of-two layer (decode over 32 layer copies, prefill
 at M = 4096); the mixed W2/W4 stack (layers 0-15 MNZ, 16-31 int4) at M = 16;
-KV4 of K and V [4096, 32, 128].
+KV4 of K and V [4096, 32, 128]; the level sets of the abstract (MNZ, PoT, the
+standard {-2, -1, 0, 1} set, {+-1, +-2}, a Lloyd-like {+-3, +-10} table,
+int4) under the absmax and the searched scale, by the output error of a
+LLaMA-7B-shaped q_proj.
 
 ``roofline`` describes the dominant kernel of the step (the grouped decode
 launch): algorithmic bytes per launch / its mean duration from HIP events on
@@ -454,6 +457,68 @@ def single_call_graphs(q, torch, st):
     return out
 
 
+LEVEL_SETS = [("mnz", "mnz", None), ("pot", "pot", None), ("standard_w2", "lut", (-2, -1, 0, 1)),
+              ("pm1_pm2", "lut", (-2, -1, 1, 2)), ("lloyd_like_pm3_pm10", "lut", (3, 10, -3, -10)),
+              ("int4", "int4", None)]
+
+
+def level_set_comparison(q, torch, dev):
+    """The level sets of the Qift abstract on one LLaMA-7B-shaped q_proj
+    (4096 x 4096, N(0, 0.02^2) weights, block 4096) through the whole W2A4
+    path: relative L2 error of the quantized linear's float32 output against
+    the float32 product x W^T over 64 tokens (int4 activations in every case),
+    with the absmax and the searched (mse) scale; the weight quantizer's time
+    with each rule; and the decode / prefill speed of a level table."""
+    import synth_inputs as si
+    N, K, B, M = 4096, 4096, 4096, 64
+    W = si.device_weights(N, K, seed=91, sigma=0.02, device=dev)
+    X = si.device_activations(M, K, seed=92, device=dev)
+    Yref = X.float() @ W.t()
+    xq, sa, _ = q.qift_rotate_quant_act(X, B)
+    err, qt = {}, {}
+    for name, kind, table in LEVEL_SETS:
+        for rule in ("absmax", "mse"):
+            cw, sw = q.qift_quantize_weights(W, B, kind, torch.float16, table=table, scale_rule=rule)
+            Y = q.qift_w2a4_linear(xq, sa, cw, sw, kind, torch.float32, table=table)
+            err[f"{name}_{rule}"] = round(((Y - Yref).norm() / Yref.norm()).item(), 5)
+            if name in ("mnz", "standard_w2"):
+                med, _, _ = time_fn(torch, lambda: q.qift_quantize_weights(
+                    W, B, kind, torch.float16, codes=cw, scales=sw, table=table, scale_rule=rule), 5,
+                    warmup=1)
+                qt[f"{name}_{rule}_ms"] = round(med, 3)
+    out = {"rel_l2_output_error": err, "weight_quantizer": qt,
+           "mnz_beats_standard_at_searched_scale": err["mnz_mse"] < err["standard_w2_mse"]}
+    # speed: the level-table decode (single call, M = 1) and prefill (M = 2048)
+    # against MNZ on the up_proj shape
+    Wu = si.device_weights(11008, 4096, seed=93, sigma=0.02, device=dev)
+    table = (3, 10, -3, -10)
+    spd = {}
+    for M in (1, 2048):
+        Xu = si.device_activations(M, 4096, seed=94, device=dev)
+        xu, su, _ = q.qift_rotate_quant_act(Xu, 4096)
+        Yu = torch.empty((M, 11008), dtype=torch.bfloat16, device=dev)
+        for name, kind, tb in (("mnz", "mnz", None), ("lut", "lut", table)):
+            cw, sw = q.qift_quantize_weights(Wu, 4096, kind, torch.float16, table=tb)
+
+            def call():
+                q.qift_w2a4_linear(xu, su, cw, sw, kind, Y=Yu, table=tb)
+
+            if M == 1:  # 16 calls replayed from a HIP graph (no host time per call)
+                call()
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g):
+                    for _ in range(16):
+                        call()
+                med, _, _ = time_fn(torch, g.replay, 20, warmup=5)
+                spd[f"decode_M1_{name}_us_per_call"] = round(med * 1e3 / 16, 2)
+                del g
+            else:
+                med, _, _ = time_fn(torch, call, 30, warmup=5)
+                spd[f"prefill_M2048_{name}_TOPS"] = round(2.0 * M * 11008 * 4096 / med / 1e9, 1)
+    out["up_proj_speed"] = spd
+    return out
+
+
 def measure_extras(q, torch, dev, stack, args):
     import synth_inputs as si
     extra = {}
@@ -587,6 +652,7 @@ def measure_extras(q, torch, dev, stack, args):
                                     "ms_K_and_V_after_flush": round(fmed, 4),
                                     "GBps_after_flush": round(kv_bytes / fmed / 1e6, 1)}
     del sets, flush
+    extra["level_sets_llama7b_q_proj"] = level_set_comparison(q, torch, dev)
     extra["context"] = {"qtea_lut_kernel_per_token_speedup_vs_fp16": 7.2,
                         "note": "speedup printed for a different (ternary) method; hardware not stated"}
     return extra
