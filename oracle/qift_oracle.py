@@ -471,6 +471,30 @@ def kv4_quant(KV: np.ndarray, B: int):
     return q.reshape(T, H, D), s.reshape(T, H), xr32.reshape(T, H, D)
 
 
+def kv4_attention_decode(q: np.ndarray, k_codes: np.ndarray, k_scales: np.ndarray,
+                         v_codes: np.ndarray, v_scales: np.ndarray, B: int,
+                         softmax_scale: float) -> np.ndarray:
+    """Decode attention over a KV4 cache (the consumer of the 4-bit KV cache of
+    rotated W2A4/KV4 inference). The cache holds each head vector rotated by
+    H_B / sqrt(B) and quantized; the query is rotated by the same orthogonal
+    map, so q' . k' = q . k, scores are softmax_scale * (q' . k_hat'), the
+    output is the softmax-weighted sum of the dequantized rotated values,
+    rotated back (H_B / sqrt(B) is its own inverse). float64.
+
+    q [S, H, D]; codes [S, T, H, D] integers; scales [S, T, H].
+    Returns out [S, H, D]."""
+    q = np.asarray(q, dtype=np.float64)
+    kd = np.asarray(k_codes, np.float64) * np.asarray(k_scales, np.float64)[..., None]
+    vd = np.asarray(v_codes, np.float64) * np.asarray(v_scales, np.float64)[..., None]
+    qr = rotate(q, B)
+    s = np.einsum("shd,sthd->sht", qr, kd) * float(softmax_scale)
+    s = s - s.max(axis=2, keepdims=True)
+    p = np.exp(s)
+    p /= p.sum(axis=2, keepdims=True)
+    o_rot = np.einsum("sht,sthd->shd", p, vd)
+    return rotate(o_rot, B)
+
+
 # ---------------------------------------------------------------------------
 # level-set analysis on a Gaussian source (Qift abstract: ratio analysis,
 # Lloyd, the standard set and {+-1, +-2})

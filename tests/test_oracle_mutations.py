@@ -127,6 +127,26 @@ def _row_abs_error(w32, s, kind, table=None):
     return float(np.sum(np.abs(w32.astype(np.float64) - lv * float(sv[0]))))
 
 
+def _attention_not_rotated_back(q, k_codes, k_scales, v_codes, v_scales, B, softmax_scale):
+    q = np.asarray(q, dtype=np.float64)
+    kd = np.asarray(k_codes, np.float64) * np.asarray(k_scales, np.float64)[..., None]
+    vd = np.asarray(v_codes, np.float64) * np.asarray(v_scales, np.float64)[..., None]
+    s = np.einsum("shd,sthd->sht", O.rotate(q, B), kd) * float(softmax_scale)
+    p = np.exp(s - s.max(axis=2, keepdims=True))
+    p /= p.sum(axis=2, keepdims=True)
+    return np.einsum("sht,sthd->shd", p, vd)
+
+
+def _attention_query_unrotated(q, k_codes, k_scales, v_codes, v_scales, B, softmax_scale):
+    q = np.asarray(q, dtype=np.float64)
+    kd = np.asarray(k_codes, np.float64) * np.asarray(k_scales, np.float64)[..., None]
+    vd = np.asarray(v_codes, np.float64) * np.asarray(v_scales, np.float64)[..., None]
+    s = np.einsum("shd,sthd->sht", q, kd) * float(softmax_scale)
+    p = np.exp(s - s.max(axis=2, keepdims=True))
+    p /= p.sum(axis=2, keepdims=True)
+    return O.rotate(np.einsum("sht,sthd->shd", p, vd), B)
+
+
 def _kinds_with(kind, **over):
     d = {k: dict(v) for k, v in O.LEVEL_KINDS.items()}
     d[kind].update(over)
@@ -154,6 +174,8 @@ MUTATIONS = {
     "table_ties_to_negative": [("table_preference", _table_preference_negative_first)],
     "mse_grid_32": [("MSE_GRID", 32)],
     "mse_rule_abs_error": [("row_sq_error", _row_abs_error)],
+    "attention_not_rotated_back": [("kv4_attention_decode", _attention_not_rotated_back)],
+    "attention_query_unrotated": [("kv4_attention_decode", _attention_query_unrotated)],
 }
 
 

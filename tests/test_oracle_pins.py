@@ -597,6 +597,64 @@ def test_no_zero_sets_beat_standard_at_searched_scale():
 
 
 # --------------------------------------------------------------------------
+# decode attention over the KV4 cache
+# --------------------------------------------------------------------------
+
+def pin_kv4_attention_equals_unrotated_attention():
+    """Rotating the query and attending in the rotated domain, then rotating
+    back, equals plain softmax attention over the dequantized cache mapped
+    back to the original domain (orthogonality), with the softmax written out
+    directly."""
+    rng = np.random.default_rng(61)
+    S, T, H, D, B = 2, 37, 3, 128, 128
+    q = rng.standard_normal((S, H, D))
+    kc = rng.integers(-7, 8, (S, T, H, D))
+    vc = rng.integers(-7, 8, (S, T, H, D))
+    ks = rng.uniform(0.01, 0.3, (S, T, H))
+    vs = rng.uniform(0.01, 0.3, (S, T, H))
+    sc = 1 / math.sqrt(D)
+    got = O.kv4_attention_decode(q, kc, ks, vc, vs, B, sc)
+    Qm = O.hadamard(B) / math.sqrt(B)
+    ref = np.zeros((S, H, D))
+    for s_ in range(S):
+        for h in range(H):
+            k = (kc[s_, :, h] * ks[s_, :, h, None]) @ Qm  # back to the original domain
+            v = (vc[s_, :, h] * vs[s_, :, h, None]) @ Qm
+            z = (k @ q[s_, h]) * sc
+            w = np.exp(z - z.max())
+            ref[s_, h] = (w / w.sum()) @ v
+    assert np.max(np.abs(got - ref)) <= 1e-12 * np.max(np.abs(ref))
+
+
+def pin_kv4_attention_closed_forms():
+    rng = np.random.default_rng(62)
+    T, H, D = 9, 2, 64
+    vc = rng.integers(-7, 8, (1, T, H, D))
+    vs = rng.uniform(0.1, 1.0, (1, T, H))
+    # identical keys: uniform weights, the output is the mean of the values
+    kc = np.tile(rng.integers(-7, 8, (1, 1, H, D)), (1, T, 1, 1))
+    ks = np.full((1, T, H), 0.5)
+    q = rng.standard_normal((1, H, D))
+    out = O.kv4_attention_decode(q, kc, ks, vc, vs, 64, 0.125)
+    vmean = O.rotate((vc * vs[..., None]).mean(axis=1), 64)
+    assert np.allclose(out, vmean, rtol=0, atol=1e-12)
+    # one key aligned with the rotated query and a huge scale: that value wins
+    qr = O.rotate(q, 64)
+    kc2 = np.zeros((1, T, H, D), np.int64)
+    kc2[0, 4] = np.sign(qr[0]).astype(np.int64) * 7
+    out2 = O.kv4_attention_decode(q, kc2, np.ones((1, T, H)), vc, vs, 64, 50.0)
+    assert np.allclose(out2[0], O.rotate(vc[0, 4] * vs[0, 4, :, None], 64), atol=1e-9)
+
+
+def test_kv4_attention_equals_unrotated_attention():
+    pin_kv4_attention_equals_unrotated_attention()
+
+
+def test_kv4_attention_closed_forms():
+    pin_kv4_attention_closed_forms()
+
+
+# --------------------------------------------------------------------------
 # packing
 # --------------------------------------------------------------------------
 
