@@ -76,6 +76,9 @@ def _load():
                                       ctypes.POINTER(ctypes.c_int64), vp],
         "qift_w2a4_linear_grouped": [vp, i64, vp],
         "qift_rotate_quant_act_batched": [vp, i32, vp],
+        "qift_kv4_attention_workspace_bytes": [i64, i64, i64, i64, ctypes.POINTER(ctypes.c_size_t)],
+        "qift_kv4_attention_decode": [vp, c_st, i64, i64, i64, i64, i32, vp, vp, vp, vp,
+                                      ctypes.c_float, vp, c_st, vp, ctypes.c_size_t, vp],
     }
     for name, args in sig.items():
         f = getattr(lib, name)
@@ -354,6 +357,49 @@ def qift_kv4_quant(KV, had_block: int, kvq=None, scales=None, stream=None):
     return kvq, scales
 
 
+def qift_kv4_attention_workspace_bytes(S: int, T: int, H: int, D: int) -> int:
+    n = ctypes.c_size_t(0)
+    _check(_C.qift_kv4_attention_workspace_bytes(S, T, H, D, ctypes.byref(n)),
+           "qift_kv4_attention_workspace_bytes")
+    return int(n.value)
+
+
+def qift_kv4_attention_decode(q, kq, ks, vq, vs, had_block: int, softmax_scale=None, out=None,
+                              out_dtype=torch.float32, workspace=None, stream=None):
+    """Decode attention over a KV4 cache. q [S, H, D] (or [H, D]) float32 /
+    bfloat16; kq, vq [S, T, H, D/2] (or [T, H, D/2]) uint8; ks, vs [S, T, H]
+    (or [T, H]) float32 -> out [S, H, D] (or [H, D]). softmax_scale defaults
+    to 1/sqrt(D); workspace (uint8, device) is allocated if not given."""
+    _dev_tensor(q, "q", (torch.float32, torch.bfloat16))
+    single = q.dim() == 2
+    S = 1 if single else q.shape[0]
+    H, D = q.shape[-2], q.shape[-1]
+    T = kq.shape[-3]
+    for name, t_, dt in (("kq", kq, torch.uint8), ("vq", vq, torch.uint8), ("ks", ks, torch.float32),
+                         ("vs", vs, torch.float32)):
+        _dev_tensor(t_, name, (dt,))
+    if kq.numel() < S * T * H * (D // 2) or vq.numel() < S * T * H * (D // 2) or \
+            ks.numel() < S * T * H or vs.numel() < S * T * H:
+        raise ValueError("cache buffers too small for [S, T, H, D]")
+    if softmax_scale is None:
+        softmax_scale = 1.0 / float(D) ** 0.5
+    if out is None:
+        out = torch.empty(q.shape, dtype=out_dtype, device=q.device)
+    _dev_tensor(out, "out", (torch.float32, torch.bfloat16))
+    if out.numel() < S * H * D:
+        raise ValueError("out too small")
+    need = qift_kv4_attention_workspace_bytes(S, T, H, D)
+    if workspace is None:
+        workspace = torch.empty((max(need, 256),), dtype=torch.uint8, device=q.device)
+    _dev_tensor(workspace, "workspace", (torch.uint8,))
+    st = _C.qift_kv4_attention_decode(_ptr(q), _TORCH_TO_QIFT[q.dtype], S, T, H, D, had_block,
+                                      _ptr(kq), _ptr(ks), _ptr(vq), _ptr(vs), float(softmax_scale),
+                                      _ptr(out), _TORCH_TO_QIFT[out.dtype], _ptr(workspace),
+                                      workspace.numel(), _stream(stream, q.device))
+    _check(st, "qift_kv4_attention_decode")
+    return out
+
+
 # ---------------------------------------------------------------------------
 # grouped linear
 # ---------------------------------------------------------------------------
@@ -408,4 +454,4 @@ __all__ = ["load_library", "QiftUnavailable", "qift_quantize_weights", "qift_rot
            "qift_rotate_quant_act_batched", "RotateBatch", "qift_w2a4_linear", "qift_kv4_quant",
            "LinearGroup", "QiftError", "qift_linear_desc", "LEVELS", "status_string", "last_error",
            "abi_version", "code_words_per_row", "padded_channels", "LIB_PATH", "SCALE_RULES",
-           "level_table_word"]
+           "level_table_word", "qift_kv4_attention_decode", "qift_kv4_attention_workspace_bytes"]

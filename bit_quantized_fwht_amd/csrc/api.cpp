@@ -283,6 +283,61 @@ qift_status qift_kv4_quant(const void* KV, qift_dtype dtype, int64_t T, int64_t 
                     "qift_kv4_quant launch");
 }
 
+// --- decode attention over the KV4 cache ------------------------------------------
+
+static qift_status check_attention(int64_t S, int64_t T, int64_t H, int64_t D) {
+  if (S < 0 || T < 0 || H < 0) return fail(QIFT_ERR_INVALID_ARG, "negative S, T or H");
+  if (D != 128) return fail(QIFT_ERR_UNSUPPORTED, "D=%lld: attention takes D = 128", (long long)D);
+  if (H > 64) return fail(QIFT_ERR_UNSUPPORTED, "H=%lld exceeds 64", (long long)H);
+  if (S > 65535) return fail(QIFT_ERR_UNSUPPORTED, "S=%lld exceeds 65535", (long long)S);
+  if (S > 0 && (T < 1 || H < 1)) return fail(QIFT_ERR_UNSUPPORTED, "T and H must be at least 1");
+  return QIFT_OK;
+}
+
+qift_status qift_kv4_attention_workspace_bytes(int64_t S, int64_t T, int64_t H, int64_t D,
+                                               size_t* bytes) {
+  if (!bytes) return fail(QIFT_ERR_INVALID_ARG, "null bytes");
+  qift_status st = check_attention(S, T, H, D);
+  if (st != QIFT_OK) return st;
+  *bytes = S == 0 ? 0 : qift::kv4_attn_workspace_bytes(S, T, (int)H);
+  return ok();
+}
+
+qift_status qift_kv4_attention_decode(const void* q, qift_dtype q_dtype, int64_t S, int64_t T,
+                                      int64_t H, int64_t D, int32_t had_block,
+                                      const uint8_t* kq, const float* ks, const uint8_t* vq,
+                                      const float* vs, float softmax_scale, void* out,
+                                      qift_dtype out_dtype, void* workspace,
+                                      size_t workspace_bytes, qift_stream stream) {
+  if (q_dtype != QIFT_F32 && q_dtype != QIFT_BF16)
+    return fail(QIFT_ERR_INVALID_ARG, "q_dtype must be F32 or BF16");
+  if (out_dtype != QIFT_F32 && out_dtype != QIFT_BF16)
+    return fail(QIFT_ERR_INVALID_ARG, "out_dtype must be F32 or BF16");
+  qift_status st = check_attention(S, T, H, D);
+  if (st != QIFT_OK) return st;
+  st = check_had_block(had_block, D, D);
+  if (st != QIFT_OK) return st;
+  if (!(softmax_scale == softmax_scale) || softmax_scale > 3.4e38f || softmax_scale < -3.4e38f)
+    return fail(QIFT_ERR_INVALID_ARG, "softmax_scale must be finite");
+  if (S == 0) return ok();
+  if (!q || !kq || !ks || !vq || !vs || !out || !workspace)
+    return fail(QIFT_ERR_INVALID_ARG, "null buffer");
+  if (!aligned(kq, 16) || !aligned(vq, 16) || !aligned(workspace, 256))
+    return fail(QIFT_ERR_ALIGNMENT, "kq and vq must be 16-byte aligned, workspace 256-byte");
+  if (!aligned(q, q_dtype == QIFT_F32 ? 4 : 2) || !aligned(out, out_dtype == QIFT_F32 ? 4 : 2) ||
+      !aligned(ks, 4) || !aligned(vs, 4))
+    return fail(QIFT_ERR_ALIGNMENT, "q, out, ks or vs misaligned for its dtype");
+  const size_t need = qift::kv4_attn_workspace_bytes(S, T, (int)H);
+  if (workspace_bytes < need)
+    return fail(QIFT_ERR_INVALID_ARG, "workspace of %zu bytes, %zu needed", workspace_bytes, need);
+  return hip_result(qift::launch_kv4_attention(q, q_dtype == QIFT_BF16, S, T, (int)H, had_block,
+                                               kq, ks, vq, vs, softmax_scale, out,
+                                               out_dtype == QIFT_BF16,
+                                               reinterpret_cast<float*>(workspace),
+                                               reinterpret_cast<hipStream_t>(stream)),
+                    "qift_kv4_attention_decode launch");
+}
+
 // --- grouped linear ------------------------------------------------------------
 
 static qift_status check_group(const qift_linear_desc* descs, int32_t count, qift_dtype scale_dtype,

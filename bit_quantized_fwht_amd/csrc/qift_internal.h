@@ -212,6 +212,12 @@ hipError_t launch_quantize_weights(const void* W, int w_bf16, int64_t N, int64_t
                                    void* scales, int scale_f16, hipStream_t s);
 hipError_t launch_kv4(const void* KV, int bf16, int64_t rows, int D, int had_block, uint8_t* kvq,
                       float* scales, hipStream_t s);
+int64_t kv4_attn_tokens_per_run(int64_t S, int64_t T, int H);
+size_t kv4_attn_workspace_bytes(int64_t S, int64_t T, int H);
+hipError_t launch_kv4_attention(const void* q, int q_bf16, int64_t S, int64_t T, int H,
+                                int had_block, const uint8_t* kq, const float* ks,
+                                const uint8_t* vq, const float* vs, float softmax_scale,
+                                void* out, int out_bf16, float* part, hipStream_t s);
 hipError_t launch_linear_decode(const qift_linear_desc& d, int scale_f16, int y_dtype,
                                 hipStream_t s);
 hipError_t launch_linear_prefill(const qift_linear_desc& d, int scale_f16, int y_dtype,

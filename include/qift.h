@@ -275,6 +275,39 @@ qift_status qift_kv4_quant(const void* KV, qift_dtype dtype, int64_t T, int64_t 
                            int32_t had_block, uint8_t* kvq, float* scales, qift_stream stream);
 
 /*
+ * qift_kv4_attention_decode -- decode attention over a KV4 cache (the
+ * consumer of the 4-bit KV cache of rotated W2A4/KV4 inference, Qift
+ * abstract). The cache holds every head vector rotated by H_B / sqrt(B) and
+ * quantized (qift_kv4_quant); the query is rotated by the same orthogonal
+ * map, so for each sequence s and head h
+ *   score[t] = softmax_scale * sum_d q'[s,h,d] * kcode[s,t,h,d] * ks[s,t,h]
+ *   p        = softmax over t = 0 .. T-1 of score
+ *   o'[d]    = sum_t p[t] * vcode[s,t,h,d] * vs[s,t,h]
+ *   out[s,h] = o' rotated back by H_B / sqrt(B)
+ * in float32, q' = q rotated in blocks of had_block along D.
+ *
+ *   q          [S, H, D] float32 or bfloat16 (one query token per sequence)
+ *   kq, vq     [S, T, H, D/2] int4 pairs (per sequence, the layout
+ *              qift_kv4_quant writes for [T, H, D]); 16-byte aligned
+ *   ks, vs     [S, T, H] float32
+ *   had_block  the block the cache was rotated with (power of two, divides D)
+ *   out        [S, H, D] float32 or bfloat16
+ *   workspace  device memory of at least the size that
+ *              qift_kv4_attention_workspace_bytes returns, 256-byte aligned,
+ *              caller-owned; it holds partial results during the call
+ * Limits: D = 128, 1 <= H <= 64, T >= 1, S <= 65535 (outside them:
+ * QIFT_ERR_UNSUPPORTED). S = 0 is a no-op.
+ */
+qift_status qift_kv4_attention_workspace_bytes(int64_t S, int64_t T, int64_t H, int64_t D,
+                                               size_t* bytes);
+qift_status qift_kv4_attention_decode(const void* q, qift_dtype q_dtype, int64_t S, int64_t T,
+                                      int64_t H, int64_t D, int32_t had_block,
+                                      const uint8_t* kq, const float* ks, const uint8_t* vq,
+                                      const float* vs, float softmax_scale, void* out,
+                                      qift_dtype out_dtype, void* workspace,
+                                      size_t workspace_bytes, qift_stream stream);
+
+/*
  * Grouped linear: many independent W2A4 linears (for example every linear of
  * a decoder stack) in one launch. Each descriptor is one qift_w2a4_linear
  * call with M <= 16; levels may differ between descriptors.

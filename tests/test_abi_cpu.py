@@ -32,7 +32,7 @@ def test_library_loads_and_exports_every_declared_symbol():
     lib = q.load_library()
     names = declared_functions()
     assert "qift_w2a4_linear" in names and "qift_kv4_quant" in names
-    assert len(names) == 13, names
+    assert len(names) == 15, names
     for n in names:
         assert hasattr(lib, n), n
     assert q.abi_version() == 3
@@ -249,6 +249,49 @@ def test_group_accepts_level_tables():
     assert q._C.qift_linear_group_workspace_bytes(ok, 2, ctypes.byref(nbytes)) == q.QIFT_OK
     bad = (q.qift_linear_desc * 1)(make_desc(levels=3, reserved=0))
     assert q._C.qift_linear_group_workspace_bytes(bad, 1, ctypes.byref(nbytes)) == q.QIFT_ERR_INVALID_ARG
+
+
+def attn(**kw):
+    args = dict(q=A16, qd=q.QIFT_BF16, S=1, T=4096, H=32, D=128, B=128, kq=A16b, ks=A16c,
+                vq=A16d, vs=A16e, scale=0.088, out=V(0x60000), od=q.QIFT_F32, ws=V(0x70000),
+                wsb=1 << 30)
+    args.update(kw)
+    return q._C.qift_kv4_attention_decode(args["q"], args["qd"], args["S"], args["T"], args["H"],
+                                          args["D"], args["B"], args["kq"], args["ks"], args["vq"],
+                                          args["vs"], args["scale"], args["out"], args["od"],
+                                          args["ws"], args["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(D=64), q.QIFT_ERR_UNSUPPORTED),
+    (dict(H=65), q.QIFT_ERR_UNSUPPORTED),
+    (dict(T=0), q.QIFT_ERR_UNSUPPORTED),
+    (dict(S=-1), q.QIFT_ERR_INVALID_ARG),
+    (dict(B=96), q.QIFT_ERR_INVALID_ARG),
+    (dict(B=256), q.QIFT_ERR_UNSUPPORTED),
+    (dict(qd=q.QIFT_I32), q.QIFT_ERR_INVALID_ARG),
+    (dict(od=q.QIFT_F16), q.QIFT_ERR_INVALID_ARG),
+    (dict(kq=None), q.QIFT_ERR_INVALID_ARG),
+    (dict(ws=None), q.QIFT_ERR_INVALID_ARG),
+    (dict(kq=V(0x20008)), q.QIFT_ERR_ALIGNMENT),
+    (dict(ws=V(0x70010)), q.QIFT_ERR_ALIGNMENT),
+    (dict(wsb=64), q.QIFT_ERR_INVALID_ARG),
+    (dict(scale=float("nan")), q.QIFT_ERR_INVALID_ARG),
+    (dict(S=0, q=None, kq=None), q.QIFT_OK),
+])
+def test_kv4_attention_rejects(kw, status):
+    assert attn(**kw) == status
+
+
+def test_kv4_attention_workspace_bytes():
+    n = ctypes.c_size_t(0)
+    assert q._C.qift_kv4_attention_workspace_bytes(1, 4096, 32, 128, ctypes.byref(n)) == q.QIFT_OK
+    # 16 tokens per run: 256 runs x 32 heads x (2 + 128) floats
+    assert n.value == 256 * 32 * 130 * 4
+    assert q._C.qift_kv4_attention_workspace_bytes(8, 4096, 32, 128, ctypes.byref(n)) == q.QIFT_OK
+    assert n.value == 8 * 64 * 32 * 130 * 4  # 64 tokens per run: about 512 workgroups
+    assert q._C.qift_kv4_attention_workspace_bytes(1, 1, 64, 128, ctypes.byref(n)) == q.QIFT_OK
+    assert n.value == 64 * 130 * 4
 
 
 def test_group_workspace_and_rejects():

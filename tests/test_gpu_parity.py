@@ -563,6 +563,78 @@ def test_mse_scale_quantizer(kind, table, sdt):
 
 
 # ---------------------------------------------------------------------------
+# decode attention over the KV4 cache (qift_kv4_attention_decode)
+# ---------------------------------------------------------------------------
+
+def attention_inputs(S, T, H, D, seed):
+    rng = np.random.default_rng(seed)
+    qv = rng.standard_normal((S, H, D)).astype(np.float32)
+    kc = si.uniform_int4((S * T * H, D), seed=seed + 1).reshape(S, T, H, D)
+    vc = si.uniform_int4((S * T * H, D), seed=seed + 2).reshape(S, T, H, D)
+    ks = si.positive_scales(S * T * H, seed + 3, lo=0.01, hi=0.1).reshape(S, T, H).astype(np.float32)
+    vs = si.positive_scales(S * T * H, seed + 4, lo=0.01, hi=1.0).reshape(S, T, H).astype(np.float32)
+    return qv, kc, ks, vc, vs
+
+
+def run_attention(qv, kc, ks, vc, vs, B, scale, q_dtype=torch.float32, out_dtype=torch.float32):
+    S, T, H, D = kc.shape
+    pack = lambda c: torch.from_numpy(O.pack_int4(c.reshape(-1, D)).reshape(S, T, H, D // 2)).to(DEV)
+    out = q.qift_kv4_attention_decode(to_dev(qv).to(q_dtype), pack(kc), to_dev(ks), pack(vc),
+                                      to_dev(vs), B, scale, out_dtype=out_dtype)
+    sync()
+    return out.float().cpu().numpy().astype(np.float64)
+
+
+def check_attention(got, ref, tol):
+    err = np.abs(got - ref).max()
+    assert err <= tol * np.abs(ref).max(), (err, np.abs(ref).max())
+
+
+@pytest.mark.parametrize("S,T,H,B", [(1, 1, 1, 128), (2, 37, 3, 128), (1, 16, 32, 128),
+                                     (3, 100, 32, 64), (1, 1000, 64, 128), (2, 513, 5, 1),
+                                     (1, 4096, 32, 128)])
+def test_kv4_attention(S, T, H, B):
+    D = 128
+    qv, kc, ks, vc, vs = attention_inputs(S, T, H, D, seed=S * 100 + T + H)
+    say(f"kv4 attention S={S} T={T} H={H} B={B}")
+    got = run_attention(qv, kc, ks, vc, vs, B, 1 / np.sqrt(D))
+    ref = O.kv4_attention_decode(qv.astype(np.float64), kc, ks, vc, vs, B, 1 / np.sqrt(D))
+    check_attention(got, ref, 2e-5)
+
+
+def test_kv4_attention_peaked_and_bf16():
+    """A large softmax scale (a few tokens carry all the weight) stays stable;
+    bfloat16 query and output."""
+    S, T, H, D = 2, 300, 8, 128
+    qv, kc, ks, vc, vs = attention_inputs(S, T, H, D, seed=7)
+    say("kv4 attention peaked / bf16")
+    got = run_attention(qv, kc, ks, vc, vs, 128, 4.0)
+    ref = O.kv4_attention_decode(qv.astype(np.float64), kc, ks, vc, vs, 128, 4.0)
+    check_attention(got, ref, 5e-5)
+    qb = si.bf16_values(torch.from_numpy(qv).to(torch.bfloat16))  # rounded on the host
+    gotb = run_attention(qv, kc, ks, vc, vs, 128, 0.0884, torch.bfloat16, torch.bfloat16)
+    refb = O.kv4_attention_decode(qb, kc, ks, vc, vs, 128, 0.0884)
+    check_attention(gotb, refb, 2 ** -7)
+
+
+def test_kv4_attention_on_a_quantized_cache():
+    """K and V [4096, 32, 128] quantized by the oracle's KV4 (rotated, block
+    128), attention by the GPU against the oracle on those codes, and against
+    plain float64 attention on the unquantized K and V (reported bound)."""
+    T, H, D = 4096, 32, 128
+    K = si.kv(T, H, D, seed=31)
+    V = si.kv(T, H, D, seed=32)
+    qv = np.random.default_rng(33).standard_normal((1, H, D)).astype(np.float32)
+    kc, ksc, _ = O.kv4_quant(K.astype(np.float64), 128)
+    vc, vsc, _ = O.kv4_quant(V.astype(np.float64), 128)
+    say("kv4 attention on a KV4 cache [4096, 32, 128]")
+    got = run_attention(qv, kc[None], ksc[None], vc[None], vsc[None], 128, 1 / np.sqrt(D))
+    ref = O.kv4_attention_decode(qv.astype(np.float64), kc[None], ksc[None], vc[None], vsc[None],
+                                 128, 1 / np.sqrt(D))
+    check_attention(got, ref, 2e-5)
+
+
+# ---------------------------------------------------------------------------
 # grouped launch == single calls
 # ---------------------------------------------------------------------------
 
