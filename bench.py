@@ -457,6 +457,50 @@ def single_call_graphs(q, torch, st):
     return out
 
 
+def kv4_attention_bench(q, torch, dev):
+    """Decode attention over a KV4 cache of LLaMA-7B shape (H = 32, D = 128,
+    T = 4096 cached tokens) for S = 1 and 8 sequences: bytes read = the K and
+    V codes and scales; cycled over enough cache copies to exceed the 256 MB
+    last-level cache."""
+    T, H, D = 4096, 32, 128
+    out = {}
+    for S in (1, 8):
+        per_set = S * T * H * (D + 8)  # K and V codes (D/2 bytes each) + two float32 scales
+        n_sets = max(2, -(-600_000_000 // per_set))
+        g = torch.Generator(device=dev)
+        g.manual_seed(101 + S)
+        sets = []
+        for _ in range(n_sets):
+            kq = torch.randint(0, 256, (S, T, H, D // 2), dtype=torch.uint8, device=dev, generator=g)
+            vq = torch.randint(0, 256, (S, T, H, D // 2), dtype=torch.uint8, device=dev, generator=g)
+            ks = torch.rand((S, T, H), device=dev, generator=g) * 0.1
+            vs = torch.rand((S, T, H), device=dev, generator=g)
+            sets.append((kq, ks, vq, vs))
+        qv = torch.randn((S, H, D), device=dev, generator=g).to(torch.bfloat16)
+        o = torch.empty((S, H, D), dtype=torch.bfloat16, device=dev)
+        ws = torch.empty((q.qift_kv4_attention_workspace_bytes(S, T, H, D),), dtype=torch.uint8,
+                         device=dev)
+        # one call per cache copy, replayed from a HIP graph (no host time
+        # between calls)
+        for kq, ks, vq, vs in sets:
+            q.qift_kv4_attention_decode(qv, kq, ks, vq, vs, D, out=o, workspace=ws)
+        torch.cuda.synchronize()
+        gr = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gr):
+            for kq, ks, vq, vs in sets:
+                q.qift_kv4_attention_decode(qv, kq, ks, vq, vs, D, out=o, workspace=ws)
+        torch.cuda.synchronize()
+        med, _, _ = time_fn(torch, gr.replay, 20, warmup=3)
+        med /= n_sets
+        out[f"S={S}"] = {"T": T, "H": H, "D": D, "us_per_call": round(med * 1e3, 2),
+                         "GBps": round(per_set / med / 1e6, 1),
+                         "frac_of_hbm_peak": round(per_set / med / 1e6 / HBM_PEAK_GBS, 4),
+                         "cache_copies_cycled": n_sets}
+        del sets, ws, gr
+        torch.cuda.empty_cache()
+    return out
+
+
 LEVEL_SETS = [("mnz", "mnz", None), ("pot", "pot", None), ("standard_w2", "lut", (-2, -1, 0, 1)),
               ("pm1_pm2", "lut", (-2, -1, 1, 2)), ("lloyd_like_pm3_pm10", "lut", (3, 10, -3, -10)),
               ("int4", "int4", None)]
@@ -652,6 +696,7 @@ def measure_extras(q, torch, dev, stack, args):
                                     "ms_K_and_V_after_flush": round(fmed, 4),
                                     "GBps_after_flush": round(kv_bytes / fmed / 1e6, 1)}
     del sets, flush
+    extra["kv4_attention_decode_llama7b"] = kv4_attention_bench(q, torch, dev)
     extra["level_sets_llama7b_q_proj"] = level_set_comparison(q, torch, dev)
     extra["context"] = {"qtea_lut_kernel_per_token_speedup_vs_fp16": 7.2,
                         "note": "speedup printed for a different (ternary) method; hardware not stated"}

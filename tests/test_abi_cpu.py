@@ -286,10 +286,12 @@ def test_kv4_attention_rejects(kw, status):
 def test_kv4_attention_workspace_bytes():
     n = ctypes.c_size_t(0)
     assert q._C.qift_kv4_attention_workspace_bytes(1, 4096, 32, 128, ctypes.byref(n)) == q.QIFT_OK
-    # 16 tokens per run: 256 runs x 32 heads x (2 + 128) floats
-    assert n.value == 256 * 32 * 130 * 4
+    # about 512 workgroups of two heads: 32 runs of 128 tokens x 32 heads x (2 + 128) floats
+    assert n.value == 32 * 32 * 130 * 4
     assert q._C.qift_kv4_attention_workspace_bytes(8, 4096, 32, 128, ctypes.byref(n)) == q.QIFT_OK
-    assert n.value == 8 * 64 * 32 * 130 * 4  # 64 tokens per run: about 512 workgroups
+    assert n.value == 8 * 4 * 32 * 130 * 4  # 4 runs of 1024 tokens per sequence
+    assert q._C.qift_kv4_attention_workspace_bytes(1, 1 << 20, 32, 128, ctypes.byref(n)) == q.QIFT_OK
+    assert n.value == 32 * 32 * 130 * 4  # longer runs, not more of them
     assert q._C.qift_kv4_attention_workspace_bytes(1, 1, 64, 128, ctypes.byref(n)) == q.QIFT_OK
     assert n.value == 64 * 130 * 4
 
