@@ -563,6 +563,58 @@ def level_set_comparison(q, torch, dev):
     return out
 
 
+def layer_by_layer_decode(q, torch, dev, M=1):
+    """A dependent, layer-by-layer decode of the LLaMA-7B-shaped stack: per
+    layer four linears with the q/k/v and the gate/up weights concatenated
+    along N (qkv 4096 -> 12288, o 4096 -> 4096, gate+up 4096 -> 22016, down
+    11008 -> 4096), each input rotated and quantized first; 32 layers with
+    their own weights and inputs, replayed from one HIP graph: a rotation
+    call and a linear call per input."""
+    import synth_inputs as si
+    shapes = [("qkv", 4096, 12288, 4096), ("o", 4096, 4096, 4096),
+              ("gate_up", 4096, 22016, 4096), ("down", 11008, 4096, 256)]
+    items, nbytes = [], 0
+    for li in range(si.N_LAYERS):
+        for j, (name, K, N, B) in enumerate(shapes):
+            W = si.device_weights(N, K, seed=5000 + 10 * li + j, sigma=0.02, device=dev)
+            cw, sw = q.qift_quantize_weights(W, B, "mnz", torch.float16)
+            del W
+            X = si.device_activations(M, K, seed=7000 + 10 * li + j, device=dev)
+            items.append(dict(K=K, N=N, B=B, cw=cw, sw=sw, X=X,
+                              xq=torch.empty((M, K // 2), dtype=torch.uint8, device=dev),
+                              sa=torch.empty((M,), dtype=torch.float32, device=dev),
+                              Y=torch.empty((M, N), dtype=torch.bfloat16, device=dev)))
+            nbytes += cw.numel() * 4 + sw.numel() * 2
+    torch.cuda.synchronize()
+
+    def separate():
+        for it in items:
+            q.qift_rotate_quant_act(it["X"], it["B"], xq=it["xq"], s_a=it["sa"])
+            q.qift_w2a4_linear(it["xq"], it["sa"], it["cw"], it["sw"], "mnz", Y=it["Y"])
+
+    out = {"M": M, "layers": si.N_LAYERS, "weight_bytes": nbytes}
+    for name, fn in (("rotate_then_linear", separate),):
+        fn()
+        torch.cuda.synchronize()
+        ref = torch.cat([it["Y"].reshape(-1) for it in items])
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            fn()
+        torch.cuda.synchronize()
+        for it in items:
+            it["Y"].zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        if not torch.equal(torch.cat([it["Y"].reshape(-1) for it in items]), ref):
+            raise RuntimeError("graph replay differs from the eager calls")
+        med, _, _ = time_fn(torch, g.replay, 20, warmup=3)
+        out[name] = {"ms_per_pass": round(med, 4), "us_per_layer": round(med * 1e3 / si.N_LAYERS, 2),
+                     "GBps": round(nbytes / med / 1e6, 1),
+                     "frac_of_hbm_peak": round(nbytes / med / 1e6 / HBM_PEAK_GBS, 4)}
+        del g
+    return out
+
+
 def measure_extras(q, torch, dev, stack, args):
     import synth_inputs as si
     extra = {}
@@ -583,6 +635,10 @@ def measure_extras(q, torch, dev, stack, args):
             del s
             torch.cuda.empty_cache()
     extra["decode_llama7b_w2_mnz"] = dec
+    log("layer-by-layer decode (concatenated qkv and gate+up)")
+    extra["decode_llama7b_layer_by_layer"] = {f"M={M}": layer_by_layer_decode(q, torch, dev, M)
+                                              for M in (1, 8)}
+    torch.cuda.empty_cache()
     if args.m == 1:
         extra["decode_llama7b_w2_mnz"]["M=1_single_calls_hipgraph"] = single_call_graphs(q, torch, stack)
 

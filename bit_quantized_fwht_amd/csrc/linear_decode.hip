@@ -203,65 +203,19 @@ __global__ __launch_bounds__(256, QIFT_DECODE_MINBLOCKS) void linear_grouped_ker
 // workgroup
 // ---------------------------------------------------------------------------
 
-// A linear call on its own (not grouped) has N / 256 workgroups of 64-channel
-// waves, 16 for N = 4096: 16 of 256 CUs would carry its whole weight stream.
-// Here a workgroup owns one 16-channel tile and its S waves take every S-th
-// K chunk (wave w: chunks w, w + S, ...), each with two chunks in flight; the
-// S partial int32 blocks are summed through LDS (integer sums, so the result
-// is the same as one wave walking all of K).
+// Split-K epilogue: the S waves' partial int32 blocks are summed through
+// LDS (red, S * 256 ints); wave 0 applies the scales and stores.
 template <int LV, int S>
-__global__ __launch_bounds__(64 * S) void linear_decode_splitk_kernel(qift_linear_desc d,
-                                                                      int scale_f16,
-                                                                      int y_dtype) {
+__device__ __forceinline__ void splitk_epilogue(const qift_linear_desc& d, const float* s_a,
+                                                const v4i& acc, int scale_f16, int y_dtype,
+                                                int* red) {
   using F = Fmt<LV>;
-  __shared__ __attribute__((aligned(16))) int red[S * 256];  // wave w: rows m, columns c at 256 w + 16 m + c
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int r16 = lane & 15;
   const int g = lane >> 4;
-  const int64_t M = d.M, K = d.K, N = d.N;
-  const int64_t cw = F::code_words(K);
-  const int64_t tiles = (N + 15) >> 4;
-  const int64_t tn = blockIdx.x;  // 16-channel tile
-  const int64_t nchunks = (K + F::kChunkK - 1) / F::kChunkK;
-  const bool act_row = r16 < M;
-  const OpConsts km = op_consts(d.reserved, lane);
-
-  struct Chunk {
-    uint4 c, a0, a1;
-  };
-  // chunk t of the tile: the lane's 16-byte code unit (chunk-major tiled
-  // layout: chunk t of tile tn at t * 256 * tiles + tn * 16 * ut words) and
-  // the matching 32 (or 16) bytes of its activation row
-  auto load = [&](Chunk& ch, int64_t t) {
-    const int64_t kseg = t * F::kChunkK + (int64_t)g * F::kLaneK;
-    const bool kval = t < nchunks && kseg < K;
-    const int64_t ut = cw - 16 * t < 16 ? cw - 16 * t : 16;
-    ch.c = kval ? ld16_stream(d.codes + t * 256 * tiles + tn * 16 * ut + 4 * lane)
-                : uint4{0u, 0u, 0u, 0u};
-    ch.a0 = uint4{0u, 0u, 0u, 0u};
-    ch.a1 = uint4{0u, 0u, 0u, 0u};
-    if (kval && act_row) {
-      const uint8_t* ap = d.xq + (int64_t)r16 * (K / 2) + kseg / 2;
-      ch.a0 = ld16(ap);
-      if constexpr (!F::kInt4) ch.a1 = ld16(ap + 16);
-    }
-  };
-  v4i acc = v4i{0, 0, 0, 0};
-  auto compute = [&](const Chunk& ch) {
-#pragma unroll
-    for (int s = 0; s < F::kSteps; ++s)
-      acc = mfma16(act_operand(ch.a0, ch.a1, s), weight_operand<LV>(ch.c, s, km), acc);
-  };
-  Chunk x, y;
-  load(x, wave);
-  for (int64_t t = wave; t < nchunks; t += 2 * S) {
-    load(y, t + S);
-    compute(x);
-    load(x, t + 2 * S);
-    if (t + S < nchunks) compute(y);
-  }
-
+  const int64_t M = d.M, N = d.N;
+  const int64_t tn = blockIdx.x;
   // partial sums: the lane holds rows 4g + r of column r16
 #pragma unroll
   for (int r = 0; r < 4; ++r) red[256 * wave + 16 * (4 * g + r) + r16] = acc[r];
@@ -296,7 +250,7 @@ __global__ __launch_bounds__(64 * S) void linear_decode_splitk_kernel(qift_linea
     return;
   }
   const float kappa = level_kappa(LV);
-  const float sa = d.s_a[m];
+  const float sa = s_a[m];
   float yv[4];
 #pragma unroll
   for (int e = 0; e < 4; ++e)
@@ -318,6 +272,77 @@ __global__ __launch_bounds__(64 * S) void linear_decode_splitk_kernel(qift_linea
         if (n + e < N) yo[e] = yv[e];
     }
   }
+}
+
+
+// A linear call on its own (not grouped) has N / 256 workgroups of 64-channel
+// waves, 16 for N = 4096: 16 of 256 CUs would carry its whole weight stream.
+// Here a workgroup owns one 16-channel tile and its S waves take every S-th
+// K chunk (wave w: chunks w, w + S, ...), each with two chunks in flight; the
+// S partial int32 blocks are summed through LDS (integer sums, so the result
+// is the same as one wave walking all of K).
+template <int LV, int S>
+__device__ __forceinline__ void decode_splitk_tile(const qift_linear_desc& d, const uint8_t* xq,
+                                                   const float* s_a, int scale_f16, int y_dtype,
+                                                   int* red) {
+  using F = Fmt<LV>;
+  // red: wave w's partial block, rows m and columns c at 256 w + 16 m + c
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int r16 = lane & 15;
+  const int g = lane >> 4;
+  const int64_t M = d.M, K = d.K, N = d.N;
+  const int64_t cw = F::code_words(K);
+  const int64_t tiles = (N + 15) >> 4;
+  const int64_t tn = blockIdx.x;  // 16-channel tile
+  const int64_t nchunks = (K + F::kChunkK - 1) / F::kChunkK;
+  const bool act_row = r16 < M;
+  const OpConsts km = op_consts(d.reserved, lane);
+
+  struct Chunk {
+    uint4 c, a0, a1;
+  };
+  // chunk t of the tile: the lane's 16-byte code unit (chunk-major tiled
+  // layout: chunk t of tile tn at t * 256 * tiles + tn * 16 * ut words) and
+  // the matching 32 (or 16) bytes of its activation row
+  auto load = [&](Chunk& ch, int64_t t) {
+    const int64_t kseg = t * F::kChunkK + (int64_t)g * F::kLaneK;
+    const bool kval = t < nchunks && kseg < K;
+    const int64_t ut = cw - 16 * t < 16 ? cw - 16 * t : 16;
+    ch.c = kval ? ld16_stream(d.codes + t * 256 * tiles + tn * 16 * ut + 4 * lane)
+                : uint4{0u, 0u, 0u, 0u};
+    ch.a0 = uint4{0u, 0u, 0u, 0u};
+    ch.a1 = uint4{0u, 0u, 0u, 0u};
+    if (kval && act_row) {
+      const uint8_t* ap = xq + (int64_t)r16 * (K / 2) + kseg / 2;
+      ch.a0 = ld16(ap);
+      if constexpr (!F::kInt4) ch.a1 = ld16(ap + 16);
+    }
+  };
+  v4i acc = v4i{0, 0, 0, 0};
+  auto compute = [&](const Chunk& ch) {
+#pragma unroll
+    for (int s = 0; s < F::kSteps; ++s)
+      acc = mfma16(act_operand(ch.a0, ch.a1, s), weight_operand<LV>(ch.c, s, km), acc);
+  };
+  Chunk x, y;
+  load(x, wave);
+  for (int64_t t = wave; t < nchunks; t += 2 * S) {
+    load(y, t + S);
+    compute(x);
+    load(x, t + 2 * S);
+    if (t + S < nchunks) compute(y);
+  }
+
+  splitk_epilogue<LV, S>(d, s_a, acc, scale_f16, y_dtype, red);
+}
+
+template <int LV, int S>
+__global__ __launch_bounds__(64 * S) void linear_decode_splitk_kernel(qift_linear_desc d,
+                                                                      int scale_f16,
+                                                                      int y_dtype) {
+  __shared__ __attribute__((aligned(16))) int red[S * 256];
+  decode_splitk_tile<LV, S>(d, d.xq, d.s_a, scale_f16, y_dtype, red);
 }
 
 // ---------------------------------------------------------------------------
