@@ -635,6 +635,63 @@ def test_kv4_attention_on_a_quantized_cache():
 
 
 # ---------------------------------------------------------------------------
+# HIP graph capture of the library's launches
+# ---------------------------------------------------------------------------
+
+def test_calls_replay_from_a_hip_graph():
+    """Rotation, a single decode call, a prefill call, a grouped launch and
+    decode attention captured in one HIP graph: every replay (with eager work
+    and synchronizations between replays) equals the eager results."""
+    M1, M2, K, N = 2, 40, 1024, 200
+    qa1, codes, s_a1, s_w = random_linear_inputs(M1, K, N, "mnz", seed=501)
+    X = to_dev(si.activations(M2, K, seed=502))
+    cw = u32_to_dev(O.pack_weights(codes, "mnz"))
+    sw = to_dev(s_w.astype(np.float32), torch.float16)
+    xq1 = torch.from_numpy(O.pack_int4(qa1)).to(DEV)
+    sa1 = to_dev(s_a1)
+    xq2 = torch.empty((M2, K // 2), dtype=torch.uint8, device=DEV)
+    sa2 = torch.empty((M2,), dtype=torch.float32, device=DEV)
+    Y1 = torch.empty((M1, N), dtype=torch.bfloat16, device=DEV)
+    Y2 = torch.empty((M2, N), dtype=torch.float32, device=DEV)
+    Yg = torch.empty((M1, N), dtype=torch.int32, device=DEV)
+    grp = q.LinearGroup([dict(xq=xq1, s_a=sa1, codes=cw, scales=sw, Y=Yg, levels="mnz")],
+                        scale_dtype=torch.float16, y_dtype=torch.int32)
+    qv, kc, ks, vc, vs = attention_inputs(1, 300, 4, 128, seed=503)
+    kq = torch.from_numpy(O.pack_int4(kc.reshape(-1, 128)).reshape(1, 300, 4, 64)).to(DEV)
+    vq = torch.from_numpy(O.pack_int4(vc.reshape(-1, 128)).reshape(1, 300, 4, 64)).to(DEV)
+    qt, kst, vst = to_dev(qv), to_dev(ks), to_dev(vs)
+    ao = torch.empty((1, 4, 128), dtype=torch.float32, device=DEV)
+    ws = torch.empty((q.qift_kv4_attention_workspace_bytes(1, 300, 4, 128),), dtype=torch.uint8,
+                     device=DEV)
+
+    def work():
+        q.qift_rotate_quant_act(X, 1024, xq=xq2, s_a=sa2)
+        q.qift_w2a4_linear(xq2, sa2, cw, sw, "mnz", Y=Y2)
+        q.qift_w2a4_linear(xq1, sa1, cw, sw, "mnz", Y=Y1)
+        grp.run()
+        q.qift_kv4_attention_decode(qt, kq, kst, vq, vst, 128, out=ao, workspace=ws)
+
+    outs = (xq2, sa2, Y2, Y1, Yg, ao)
+    say("graph capture")
+    work()
+    sync()
+    ref = [o.clone() for o in outs]
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        work()
+    sync()
+    for rep in range(3):
+        for o in outs:
+            o.zero_()
+        Y2.add_(1.0)  # eager work between replays
+        sync()
+        g.replay()
+        sync()
+        for o, r in zip(outs, ref):
+            assert torch.equal(o, r), rep
+
+
+# ---------------------------------------------------------------------------
 # grouped launch == single calls
 # ---------------------------------------------------------------------------
 
