@@ -65,7 +65,48 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--copy-calibration", action="store_true",
                    help="also run a plain 1 GiB device copy (counter calibration)")
+    p.add_argument("--unit", choices=sorted(UNITS),
+                   help="run only this unit --steps times (for profiling runs) and exit")
     return p.parse_args()
+
+
+def unit_prefill_up_proj(q, torch, dev, steps):
+    """LLaMA-7B up_proj prefill: M = 2048, K = 4096, N = 11008, MNZ, bf16 out."""
+    import synth_inputs as si
+    W = si.device_weights(11008, 4096, seed=5, sigma=0.02, device=dev)
+    cw, sw = q.qift_quantize_weights(W, 4096, "mnz", torch.float16)
+    X = si.device_activations(2048, 4096, seed=6, device=dev)
+    xq, sa, _ = q.qift_rotate_quant_act(X, 4096)
+    Y = torch.empty((2048, 11008), dtype=torch.bfloat16, device=dev)
+    for _ in range(steps):
+        q.qift_w2a4_linear(xq, sa, cw, sw, "mnz", Y=Y)
+
+
+def unit_kv4(q, torch, dev, steps):
+    """KV4 of K and V [4096, 32, 128] bf16 (two launches per step)."""
+    import synth_inputs as si
+    K = si.device_kv(4096, 32, 128, seed=60, device=dev)
+    V = si.device_kv(4096, 32, 128, seed=61, device=dev)
+    for _ in range(steps):
+        q.qift_kv4_quant(K, 128)
+        q.qift_kv4_quant(V, 128)
+
+
+def unit_attention(q, torch, dev, steps):
+    """Decode attention over a KV4 cache: 8 sequences x 4096 tokens, H = 32, D = 128."""
+    S, T, H, D = 8, 4096, 32, 128
+    g = torch.Generator(device=dev)
+    g.manual_seed(109)
+    kq = torch.randint(0, 256, (S, T, H, D // 2), dtype=torch.uint8, device=dev, generator=g)
+    vq = torch.randint(0, 256, (S, T, H, D // 2), dtype=torch.uint8, device=dev, generator=g)
+    ks = torch.rand((S, T, H), device=dev, generator=g) * 0.1
+    vs = torch.rand((S, T, H), device=dev, generator=g)
+    qv = torch.randn((S, H, D), device=dev, generator=g).to(torch.bfloat16)
+    for _ in range(steps):
+        q.qift_kv4_attention_decode(qv, kq, ks, vq, vs, D)
+
+
+UNITS = {"prefill_up_proj": unit_prefill_up_proj, "kv4": unit_kv4, "attention": unit_attention}
 
 
 def log(*a):
@@ -332,6 +373,12 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
+
+    if args.unit:
+        UNITS[args.unit](q, torch, dev, args.steps)
+        torch.cuda.synchronize()
+        log(f"unit {args.unit}: {args.steps} steps")
+        return
 
     log(f"building LLaMA-7B-shaped W2 stack, M={args.m}")
     t0 = time.time()
