@@ -347,6 +347,25 @@ def cpu_oracle_units():
     dt = time.perf_counter() - t0
     out["kv4"] = {"T": T, "H": H, "D": D, "s": round(dt, 3),
                   "GBps": round(T * H * (2.5 * D + 4) / dt / 1e9, 4)}
+    # decode attention over a KV4 cache: one sequence of 1024 tokens, 32 heads
+    T, H, D = 1024, 32, 128
+    kc = si.uniform_int4((T * H, D), seed=12).reshape(1, T, H, D)
+    vc = si.uniform_int4((T * H, D), seed=13).reshape(1, T, H, D)
+    ksc = si.positive_scales(T * H, 14, 0.01, 0.1).reshape(1, T, H)
+    vsc = si.positive_scales(T * H, 15).reshape(1, T, H)
+    qv = si.activations(H, D, seed=16, n_outliers=0).reshape(1, H, D)
+    t0 = time.perf_counter()
+    O.kv4_attention_decode(qv, kc, ksc, vc, vsc, D, 1 / np.sqrt(D))
+    dt = time.perf_counter() - t0
+    out["kv4_attention"] = {"S": 1, "T": T, "H": H, "D": D, "s": round(dt, 3),
+                            "GBps": round(T * H * (D + 8) / dt / 1e9, 4)}
+    # the searched (least-squares) weight scale: 16 rows of K = 4096, MNZ
+    W = si.weights(16, 4096, seed=17)
+    t0 = time.perf_counter()
+    O.quantize_weights(W.astype(np.float64), 4096, "mnz", "f16", rule="mse")
+    dt = time.perf_counter() - t0
+    out["weight_quantizer_searched_scale"] = {"rows": 16, "K": 4096, "s": round(dt, 3),
+                                              "rows_per_s": round(16 / dt, 2)}
     return out
 
 
