@@ -50,6 +50,21 @@ its best scale). Readings taken here:
   j = 0..63, codes decided against each, and keeps the one with the smallest
   sum of squared errors (float64; the first on ties).
 
+Error-compensated quantization with the fixed levels (the Qift abstract
+reports the "GPTQ residual behavior" of its level sets; the QTEA abstract
+describes GPTQ-style column-by-column quantization, in which quantizing one
+column updates the ones after it; the algorithm itself is GPTQ's, restated
+here). Readings taken here:
+
+* H = X'^T X' from the calibration activations rotated like the weights (no
+  1/S or factor 2: a common factor of H changes nothing below); dead
+  features (H[k, k] = 0) get H[k, k] = 1 and weight 0; then
+  damp * mean(diag H) is added to the diagonal (damp = 0.01 by default);
+* the scales are fixed before the loop, by the plain quantizer's rule on the
+  rotated weights; features in natural order (no reordering by H);
+* each decision is the plain quantizer's on the current weight rounded to
+  float32; updates in float64.
+
 Parity pins: every function here is checked in ``tests/test_oracle_pins.py``
 against closed forms, brute force and the values the abstract prints. The
 end-to-end accuracy of a quantized linear against the unquantized one has no
@@ -286,6 +301,78 @@ def quantize_weights(W: np.ndarray, B: int, kind: str, scale_dtype: str, table=N
     else:
         codes = nearest_codes(wr32, s, kind, table)
     return codes, s, wr32
+
+
+def gptq_hessian(X: np.ndarray, B: int, damp: float):
+    """Second-order statistics of the layer input for error-compensated
+    quantization (GPTQ, the column-by-column quantizer the QTEA abstract
+    builds on and the Qift abstract evaluates): the calibration activations
+    X [S, K] rotated like the weights (float64), H = X'^T X'. A feature whose
+    diagonal entry is 0 never reaches the output: its diagonal becomes 1.
+    Then the mean of the diagonal times ``damp`` is added to every diagonal
+    entry. Returns (damped H [K, K] float64, dead feature mask [K])."""
+    xr = rotate(X, B)
+    H = xr.T @ xr
+    dead = np.diag(H) == 0
+    H[dead, dead] = 1.0
+    H = H + float(damp) * float(np.mean(np.diag(H))) * np.eye(H.shape[0])
+    return H, dead
+
+
+def gptq_factor(H: np.ndarray) -> np.ndarray:
+    """U, the upper triangular matrix with U^T U = H^-1 (Cholesky factor of
+    the inverse, transposed)."""
+    return np.linalg.cholesky(np.linalg.inv(H)).T
+
+
+def gptq_columns(wr32: np.ndarray, s: np.ndarray, U: np.ndarray, dead: np.ndarray, kind: str,
+                 table=None) -> np.ndarray:
+    """The column loop. Features are quantized one at a time in their natural
+    order. Feature k takes, per channel, the nearest level of its current
+    weight rounded to float32 (the decision of the plain quantizer); the
+    rounding error divided by U[k, k] is removed from the later features
+    along row k of U. Weights of dead features start at 0. float64 updates.
+    Returns codes int64 [N, K]."""
+    w = np.asarray(wr32, dtype=np.float32).astype(np.float64)
+    w[:, dead] = 0.0
+    N, K = w.shape
+    sd = np.asarray(s).astype(np.float64)
+    codes = np.zeros((N, K), dtype=np.int64)
+    for k in range(K):
+        col32 = w[:, k].astype(np.float32)[:, None]
+        if kind == "int4":
+            c = int4_weight_codes(col32, s)[:, 0]
+            deq = c.astype(np.float64) * sd
+        else:
+            c = nearest_codes(col32, s, kind, table)[:, 0]
+            deq = _kind_levels(kind, table)[0][c] * sd
+        codes[:, k] = c
+        err = (w[:, k] - deq) / U[k, k]
+        w[:, k + 1:] -= np.outer(err, U[k, k + 1:])
+    return codes
+
+
+def gptq_quantize_weights(W: np.ndarray, X: np.ndarray, B: int, kind: str, scale_dtype: str,
+                          table=None, rule: str = "absmax", damp: float = 0.01, rows=None,
+                          factor=None):
+    """Error-compensated quantization with the fixed levels. The per-channel
+    scales are those of ``quantize_weights`` (from the rotated float32
+    weights, before any update); H and its factor U come from the rotated
+    calibration activations X [S, K]; then ``gptq_columns``.
+    ``rows`` (optional indices) restricts the work to a few channels: every
+    channel is processed independently once U is known. ``factor`` = a
+    (U, dead) pair from an earlier call, reused.
+    Returns (codes int64 [R, K], scales [R] stored dtype, (U, dead))."""
+    W = np.asarray(W)
+    if rows is not None:
+        W = W[np.asarray(rows)]
+    wr32 = rotate(W, B).astype(np.float32)
+    s = weight_scales(wr32, kind, scale_dtype, table, rule)
+    if factor is None:
+        H, dead = gptq_hessian(X, B, damp)
+        factor = (gptq_factor(H), dead)
+    U, dead = factor
+    return gptq_columns(wr32, s, U, dead, kind, table), s, factor
 
 
 def code_levels(codes: np.ndarray, kind: str, table=None) -> np.ndarray:

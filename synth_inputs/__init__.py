@@ -16,7 +16,9 @@ Distributions used:
   (LLaMA-3.1-8B-shaped);
 * activations: i.i.d. N(0, 1) with a fixed set of outlier channels scaled by
   20 (4 channels for the 16x256 case, round(0.01*K) channels otherwise);
-* KV: i.i.d. N(0, 1) in bf16, [T, H, D].
+* KV: i.i.d. N(0, 1) in bf16, [T, H, D];
+* calibration activations (error-compensated weight quantization): N(0, 1)
+  plus a shared rank-8 part, outlier channels x20.
 """
 from __future__ import annotations
 
@@ -80,6 +82,24 @@ def activations(M: int, K: int, seed: int, n_outliers: int | None = None,
     every token."""
     rng = np.random.default_rng(seed)
     X = rng.standard_normal((M, K))
+    n = n_outlier_channels(K) if n_outliers is None else n_outliers
+    if n > 0:
+        ch = rng.choice(K, n, replace=False)
+        X[:, ch] *= outlier_gain
+    return X.astype(np.float32)
+
+
+def calibration_activations(S: int, K: int, seed: int, rank: int = 8,
+                            n_outliers: int | None = None,
+                            outlier_gain: float = 20.0) -> np.ndarray:
+    """float32 [S, K] calibration tokens: i.i.d. N(0, 1) plus a shared
+    low-rank part G V (G [S, rank], V [rank, K], both N(0, 1)), so that the
+    features are correlated, with ``n_outliers`` (default round(0.01 K))
+    seeded channels multiplied by ``outlier_gain``."""
+    rng = np.random.default_rng(seed)
+    X = rng.standard_normal((S, K))
+    if rank > 0:
+        X += rng.standard_normal((S, rank)) @ rng.standard_normal((rank, K))
     n = n_outlier_channels(K) if n_outliers is None else n_outliers
     if n > 0:
         ch = rng.choice(K, n, replace=False)

@@ -147,6 +147,52 @@ def _attention_query_unrotated(q, k_codes, k_scales, v_codes, v_scales, B, softm
     return O.rotate(np.einsum("sht,sthd->shd", p, vd), B)
 
 
+def _gptq_columns_variant(sign=1.0, divide=True):
+    def cols(wr32, s, U, dead, kind, table=None):
+        w = np.asarray(wr32, dtype=np.float32).astype(np.float64)
+        w[:, dead] = 0.0
+        N, K = w.shape
+        sd = np.asarray(s).astype(np.float64)
+        codes = np.zeros((N, K), dtype=np.int64)
+        for k in range(K):
+            col32 = w[:, k].astype(np.float32)[:, None]
+            if kind == "int4":
+                c = O.int4_weight_codes(col32, s)[:, 0]
+                deq = c.astype(np.float64) * sd
+            else:
+                c = O.nearest_codes(col32, s, kind, table)[:, 0]
+                deq = O._kind_levels(kind, table)[0][c] * sd
+            codes[:, k] = c
+            err = (w[:, k] - deq) / (U[k, k] if divide else 1.0)
+            w[:, k + 1:] -= sign * np.outer(err, U[k, k + 1:])
+        return codes
+    return cols
+
+
+def _gptq_factor_lower(H):
+    return np.linalg.cholesky(np.linalg.inv(H))
+
+
+def _gptq_factor_without_inverse(H):
+    return np.linalg.cholesky(H).T
+
+
+def _gptq_hessian_absolute_damping(X, B, damp):
+    xr = O.rotate(X, B)
+    H = xr.T @ xr
+    dead = np.diag(H) == 0
+    H[dead, dead] = 1.0
+    return H + float(damp) * np.eye(H.shape[0]), dead
+
+
+def _gptq_hessian_unrotated(X, B, damp):
+    X = np.asarray(X, dtype=np.float64)
+    H = X.T @ X
+    dead = np.diag(H) == 0
+    H[dead, dead] = 1.0
+    return H + float(damp) * float(np.mean(np.diag(H))) * np.eye(H.shape[0]), dead
+
+
 def _kinds_with(kind, **over):
     d = {k: dict(v) for k, v in O.LEVEL_KINDS.items()}
     d[kind].update(over)
@@ -176,6 +222,12 @@ MUTATIONS = {
     "mse_rule_abs_error": [("row_sq_error", _row_abs_error)],
     "attention_not_rotated_back": [("kv4_attention_decode", _attention_not_rotated_back)],
     "attention_query_unrotated": [("kv4_attention_decode", _attention_query_unrotated)],
+    "gptq_update_sign": [("gptq_columns", _gptq_columns_variant(sign=-1.0))],
+    "gptq_error_not_divided": [("gptq_columns", _gptq_columns_variant(divide=False))],
+    "gptq_factor_lower": [("gptq_factor", _gptq_factor_lower)],
+    "gptq_factor_without_inverse": [("gptq_factor", _gptq_factor_without_inverse)],
+    "gptq_damping_absolute": [("gptq_hessian", _gptq_hessian_absolute_damping)],
+    "gptq_hessian_unrotated": [("gptq_hessian", _gptq_hessian_unrotated)],
 }
 
 

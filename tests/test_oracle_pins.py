@@ -833,4 +833,161 @@ def test_kv4():
     pin_kv4()
 
 
+# --------------------------------------------------------------------------
+# error-compensated quantization with the fixed levels (GPTQ)
+# --------------------------------------------------------------------------
+
+GPTQ_KINDS = (("mnz", None), ("pot", None), ("int4", None), ("lut", (1, 3, -3, -1)),
+              ("lut", (0, 2, -1, -4)))
+
+
+def _dequant(codes, s, kind, table):
+    if kind == "int4":
+        return codes.astype(np.float64) * s.astype(np.float64)[:, None]
+    return O._kind_levels(kind, table)[0][codes] * s.astype(np.float64)[:, None]
+
+
+def _nearest_f32(w, s, kind, table):
+    col32 = np.asarray(w, dtype=np.float32)[:, None]
+    if kind == "int4":
+        return O.int4_weight_codes(col32, s)[:, 0]
+    return O.nearest_codes(col32, s, kind, table)[:, 0]
+
+
+def _sequential_least_squares_codes(W, X, B, kind, table, damp):
+    """GPTQ by its defining property, written without the Cholesky recursion:
+    when feature k is decided, the not yet decided weights of a row are the
+    minimizers of the output error (w - w0) H (w - w0)^T given the levels
+    already fixed, i.e. w_F = w0_F - H_FF^-1 H_FQ (q_Q - w0_Q) (a linear
+    solve per step); feature k then takes the nearest level of w_k."""
+    xr = O.rotate(X, B)
+    Hm = xr.T @ xr
+    Hm = Hm + damp * np.trace(Hm) / Hm.shape[0] * np.eye(Hm.shape[0])
+    w0 = O.rotate(W, B).astype(np.float32)
+    s = O.weight_scales(w0, kind, "f32", table, "absmax")
+    w0 = w0.astype(np.float64)
+    N, K = w0.shape
+    codes = np.zeros((N, K), dtype=np.int64)
+    for n in range(N):
+        deq = np.zeros(K)
+        for k in range(K):
+            dq = deq[:k] - w0[n, :k]
+            wk = w0[n, k:] - np.linalg.solve(Hm[k:, k:], Hm[k:, :k] @ dq)
+            c = _nearest_f32(wk[:1], s[n:n + 1], kind, table)[0]
+            codes[n, k] = c
+            deq[k] = _dequant(np.array([[c]]), s[n:n + 1], kind, table)[0, 0]
+    return codes, s
+
+
+def pin_gptq_identity_hessian_is_plain_quantizer():
+    """With H proportional to I no error is passed on: the codes and scales
+    are those of the plain quantizer."""
+    rng = np.random.default_rng(71)
+    K = 64
+    W = rng.normal(0, 0.02, (9, K))
+    for B in (1, 16, 64):
+        X = 3.0 * np.eye(K)  # rotated: 3 Q, so H = 9 I (+ damping)
+        for kind, table in GPTQ_KINDS:
+            for rule in ("absmax", "mse"):
+                c0, s0, _ = O.quantize_weights(W, B, kind, "f16", table, rule)
+                c1, s1, _ = O.gptq_quantize_weights(W, X, B, kind, "f16", table, rule)
+                assert np.array_equal(s0, s1), (B, kind, rule)
+                assert np.array_equal(c0, c1), (B, kind, rule)
+
+
+def pin_gptq_sequential_least_squares():
+    rng = np.random.default_rng(72)
+    N, K, S, B = 3, 24, 40, 8
+    W = rng.normal(0, 0.02, (N, K))
+    X = (rng.standard_normal((S, K)) + rng.standard_normal((S, 3)) @ rng.standard_normal((3, K)))
+    differs = False
+    for kind, table in GPTQ_KINDS:
+        ref, s_ref = _sequential_least_squares_codes(W, X, B, kind, table, 0.01)
+        got, s, _ = O.gptq_quantize_weights(W, X, B, kind, "f32", table)
+        assert np.array_equal(s, s_ref)
+        assert np.array_equal(got, ref), kind
+        plain, _, _ = O.quantize_weights(W, B, kind, "f32", table)
+        differs |= bool(np.any(plain != got))
+    assert differs  # the compensation changed some codes
+
+
+def pin_gptq_reduces_output_error():
+    """On correlated calibration tokens the output error ||(W' - deq) X'^T||
+    is below that of the plain quantizer."""
+    N, K, S, B = 24, 128, 256, 32
+    W = si.weights(N, K, 73)
+    X = si.calibration_activations(S, K, 74)
+    xr = O.rotate(X, B)
+    for kind, table in GPTQ_KINDS[:4]:
+        c0, s0, wr32 = O.quantize_weights(W, B, kind, "f32", table)
+        c1, s1, _ = O.gptq_quantize_weights(W, X, B, kind, "f32", table)
+        w = wr32.astype(np.float64)
+        e0 = np.sum(((w - _dequant(c0, s0, kind, table)) @ xr.T) ** 2)
+        e1 = np.sum(((w - _dequant(c1, s1, kind, table)) @ xr.T) ** 2)
+        assert e1 < 0.8 * e0, (kind, e1 / e0)
+
+
+def pin_gptq_dead_feature():
+    """A feature no calibration token uses: its weights are set to 0 before
+    the loop and receive no update, so its code is the nearest level of 0;
+    the scales still come from the full rows."""
+    rng = np.random.default_rng(75)
+    N, K, S = 5, 32, 50
+    W = rng.normal(0, 0.02, (N, K))
+    X = rng.standard_normal((S, K)) + rng.standard_normal((S, 2)) @ rng.standard_normal((2, K))
+    X[:, 7] = 0.0
+    for kind, table in GPTQ_KINDS:
+        c, s, _ = O.gptq_quantize_weights(W, X, 1, kind, "f32", table)
+        zero = _nearest_f32(np.zeros(N), s, kind, table)
+        assert np.array_equal(c[:, 7], zero), kind
+        _, s0, _ = O.quantize_weights(W, 1, kind, "f32", table)
+        assert np.array_equal(s, s0)
+
+
+def pin_gptq_scale_free_hessian():
+    """Multiplying the calibration tokens by 2 scales H by 4 exactly and the
+    damping with it: the codes do not change."""
+    rng = np.random.default_rng(76)
+    W = rng.normal(0, 0.02, (4, 48))
+    X = rng.standard_normal((60, 48)) + rng.standard_normal((60, 2)) @ rng.standard_normal((2, 48))
+    for kind, table in GPTQ_KINDS[:3]:
+        c1, _, _ = O.gptq_quantize_weights(W, X, 16, kind, "f32", table, damp=0.05)
+        c2, _, _ = O.gptq_quantize_weights(W, 2.0 * X, 16, kind, "f32", table, damp=0.05)
+        assert np.array_equal(c1, c2), kind
+
+
+def pin_gptq_rows_match_full():
+    """Rows are independent given H: a subset of channels gets the same codes
+    as in the full call."""
+    W = si.weights(20, 64, 77)
+    X = si.calibration_activations(90, 64, 78)
+    full, sf, _ = O.gptq_quantize_weights(W, X, 16, "mnz", "f16")
+    part, sp, _ = O.gptq_quantize_weights(W, X, 16, "mnz", "f16", rows=[3, 11, 19])
+    assert np.array_equal(part, full[[3, 11, 19]]) and np.array_equal(sp, sf[[3, 11, 19]])
+
+
+def test_gptq_identity_hessian_is_plain_quantizer():
+    pin_gptq_identity_hessian_is_plain_quantizer()
+
+
+def test_gptq_sequential_least_squares():
+    pin_gptq_sequential_least_squares()
+
+
+def test_gptq_reduces_output_error():
+    pin_gptq_reduces_output_error()
+
+
+def test_gptq_dead_feature():
+    pin_gptq_dead_feature()
+
+
+def test_gptq_scale_free_hessian():
+    pin_gptq_scale_free_hessian()
+
+
+def test_gptq_rows_match_full():
+    pin_gptq_rows_match_full()
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]
