@@ -79,6 +79,11 @@ def _load():
         "qift_kv4_attention_workspace_bytes": [i64, i64, i64, i64, ctypes.POINTER(ctypes.c_size_t)],
         "qift_kv4_attention_decode": [vp, c_st, i64, i64, i64, i64, i32, vp, vp, vp, vp,
                                       ctypes.c_float, vp, c_st, vp, ctypes.c_size_t, vp],
+        "qift_gptq_hessian_workspace_bytes": [i64, i64, ctypes.POINTER(ctypes.c_size_t)],
+        "qift_gptq_hessian": [vp, c_st, i64, i64, i32, i32, vp, vp, ctypes.c_size_t, vp],
+        "qift_gptq_workspace_bytes": [i64, i64, ctypes.POINTER(ctypes.c_size_t)],
+        "qift_gptq_quantize_weights": [vp, c_st, i64, i64, vp, i32, c_st, ctypes.c_uint32, c_st,
+                                       ctypes.c_double, vp, vp, c_st, vp, ctypes.c_size_t, vp],
     }
     for name, args in sig.items():
         f = getattr(lib, name)
@@ -220,6 +225,79 @@ def qift_quantize_weights(W, had_block: int, levels="mnz", scale_dtype=torch.flo
                                      _ptr(scales), _TORCH_TO_QIFT[scales.dtype],
                                      _stream(stream, W.device))
     _check(st, "qift_quantize_weights_ex")
+    return codes, scales
+
+
+def qift_gptq_hessian_workspace_bytes(S: int, K: int) -> int:
+    n = ctypes.c_size_t(0)
+    _check(_C.qift_gptq_hessian_workspace_bytes(S, K, ctypes.byref(n)),
+           "qift_gptq_hessian_workspace_bytes")
+    return int(n.value)
+
+
+def qift_gptq_hessian(X, had_block: int, H=None, accumulate=False, workspace=None, stream=None):
+    """Calibration activations X [S, K] float32/bfloat16 -> H = X'^T X'
+    (float64 [K, K], X' rotated along K in blocks of had_block); with
+    accumulate, X'^T X' is added to the given H. workspace (uint8, device) is
+    allocated if not given."""
+    _dev_tensor(X, "X", (torch.float32, torch.bfloat16))
+    S, K = X.shape
+    if H is None:
+        if accumulate:
+            raise ValueError("accumulate needs H")
+        H = torch.empty((K, K), dtype=torch.float64, device=X.device)
+    _dev_tensor(H, "H", (torch.float64,))
+    if H.numel() < K * K:
+        raise ValueError("H too small")
+    need = qift_gptq_hessian_workspace_bytes(S, K)
+    if workspace is None:
+        workspace = torch.empty((max(need, 256),), dtype=torch.uint8, device=X.device)
+    _dev_tensor(workspace, "workspace", (torch.uint8,))
+    st = _C.qift_gptq_hessian(_ptr(X), _TORCH_TO_QIFT[X.dtype], S, K, had_block,
+                              1 if accumulate else 0, _ptr(H), _ptr(workspace), workspace.numel(),
+                              _stream(stream, X.device))
+    _check(st, "qift_gptq_hessian")
+    return H
+
+
+def qift_gptq_workspace_bytes(N: int, K: int) -> int:
+    n = ctypes.c_size_t(0)
+    _check(_C.qift_gptq_workspace_bytes(N, K, ctypes.byref(n)), "qift_gptq_workspace_bytes")
+    return int(n.value)
+
+
+def qift_gptq_quantize_weights(W, H, had_block: int, levels="mnz", scale_dtype=torch.float16,
+                               table=None, scale_rule="absmax", damp=0.01, codes=None,
+                               scales=None, workspace=None, stream=None):
+    """Error-compensated quantization of W [N, K] float32/bfloat16 with the
+    Hessian H [K, K] float64 (qift_gptq_hessian): codes and scales in the
+    layout of qift_quantize_weights. workspace (uint8, device) is allocated if
+    not given."""
+    _dev_tensor(W, "W", (torch.float32, torch.bfloat16))
+    _dev_tensor(H, "H", (torch.float64,))
+    N, K = W.shape
+    if H.numel() < K * K:
+        raise ValueError("H too small")
+    lv = _levels(levels)
+    if codes is None:
+        codes = torch.empty((padded_channels(N), code_words_per_row(K, lv)), dtype=torch.int32,
+                            device=W.device)
+    if scales is None:
+        scales = torch.empty((N,), dtype=scale_dtype, device=W.device)
+    _dev_tensor(codes, "codes", (torch.int32,))
+    _dev_tensor(scales, "scales", (torch.float32, torch.float16))
+    if codes.numel() < padded_channels(N) * code_words_per_row(K, lv) or scales.numel() < N:
+        raise ValueError("codes or scales buffer too small")
+    need = qift_gptq_workspace_bytes(N, K)
+    if workspace is None:
+        workspace = torch.empty((max(need, 256),), dtype=torch.uint8, device=W.device)
+    _dev_tensor(workspace, "workspace", (torch.uint8,))
+    st = _C.qift_gptq_quantize_weights(_ptr(W), _TORCH_TO_QIFT[W.dtype], N, K, _ptr(H), had_block,
+                                       lv, _table_arg(lv, table), SCALE_RULES[scale_rule],
+                                       float(damp), _ptr(codes), _ptr(scales),
+                                       _TORCH_TO_QIFT[scales.dtype], _ptr(workspace),
+                                       workspace.numel(), _stream(stream, W.device))
+    _check(st, "qift_gptq_quantize_weights")
     return codes, scales
 
 
@@ -454,4 +532,6 @@ __all__ = ["load_library", "QiftUnavailable", "qift_quantize_weights", "qift_rot
            "qift_rotate_quant_act_batched", "RotateBatch", "qift_w2a4_linear", "qift_kv4_quant",
            "LinearGroup", "QiftError", "qift_linear_desc", "LEVELS", "status_string", "last_error",
            "abi_version", "code_words_per_row", "padded_channels", "LIB_PATH", "SCALE_RULES",
-           "level_table_word", "qift_kv4_attention_decode", "qift_kv4_attention_workspace_bytes"]
+           "level_table_word", "qift_kv4_attention_decode", "qift_kv4_attention_workspace_bytes",
+           "qift_gptq_hessian", "qift_gptq_hessian_workspace_bytes", "qift_gptq_quantize_weights",
+           "qift_gptq_workspace_bytes"]

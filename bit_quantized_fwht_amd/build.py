@@ -17,7 +17,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libqift.so")
 
-SOURCES = ["rotate_quant.hip", "kv4.hip", "kv4_attention.hip", "linear_decode.hip",
+SOURCES = ["rotate_quant.hip", "kv4.hip", "kv4_attention.hip", "gptq.hip", "linear_decode.hip",
            "linear_prefill.hip", "api.cpp"]
 
 HIPCC_FLAGS = [

@@ -338,6 +338,98 @@ qift_status qift_kv4_attention_decode(const void* q, qift_dtype q_dtype, int64_t
                     "qift_kv4_attention_decode launch");
 }
 
+// --- error-compensated weight quantization ----------------------------------------
+
+static qift_status check_gptq_shape(int64_t K, int32_t had_block) {
+  if (K <= 0 || K % 64 != 0)
+    return fail(QIFT_ERR_INVALID_ARG, "K=%lld must be a positive multiple of 64", (long long)K);
+  if (K > QIFT_MAX_ROW)
+    return fail(QIFT_ERR_UNSUPPORTED, "K=%lld exceeds %d", (long long)K, QIFT_MAX_ROW);
+  return check_had_block(had_block, K, QIFT_MAX_HAD_BLOCK);
+}
+
+qift_status qift_gptq_hessian_workspace_bytes(int64_t S, int64_t K, size_t* bytes) {
+  if (!bytes) return fail(QIFT_ERR_INVALID_ARG, "null bytes");
+  if (S < 0) return fail(QIFT_ERR_INVALID_ARG, "negative S");
+  if (K <= 0 || K % 64 != 0)
+    return fail(QIFT_ERR_INVALID_ARG, "K=%lld must be a positive multiple of 64", (long long)K);
+  if (K > QIFT_MAX_ROW)
+    return fail(QIFT_ERR_UNSUPPORTED, "K=%lld exceeds %d", (long long)K, QIFT_MAX_ROW);
+  *bytes = qift::gptq_hessian_workspace_bytes(S, K);
+  return ok();
+}
+
+qift_status qift_gptq_hessian(const void* X, qift_dtype x_dtype, int64_t S, int64_t K,
+                              int32_t had_block, int32_t accumulate, double* H, void* workspace,
+                              size_t workspace_bytes, qift_stream stream) {
+  if (x_dtype != QIFT_F32 && x_dtype != QIFT_BF16)
+    return fail(QIFT_ERR_INVALID_ARG, "x_dtype must be F32 or BF16");
+  if (S < 0) return fail(QIFT_ERR_INVALID_ARG, "negative S");
+  if (accumulate != 0 && accumulate != 1)
+    return fail(QIFT_ERR_INVALID_ARG, "accumulate must be 0 or 1");
+  qift_status st = check_gptq_shape(K, had_block);
+  if (st != QIFT_OK) return st;
+  if (S == 0 && accumulate) return ok();
+  if (!H || !workspace || (S > 0 && !X)) return fail(QIFT_ERR_INVALID_ARG, "null buffer");
+  if (!aligned(H, 8) || !aligned(workspace, 256) || (S > 0 && !aligned(X, x_dtype == QIFT_F32 ? 4 : 2)))
+    return fail(QIFT_ERR_ALIGNMENT, "H 8-byte, workspace 256-byte, X dtype-aligned");
+  const size_t need = qift::gptq_hessian_workspace_bytes(S, K);
+  if (workspace_bytes < need)
+    return fail(QIFT_ERR_INVALID_ARG, "workspace of %zu bytes, %zu needed", workspace_bytes, need);
+  return hip_result(qift::launch_gptq_hessian(X, x_dtype == QIFT_BF16, S, K, had_block,
+                                              accumulate, H, workspace,
+                                              reinterpret_cast<hipStream_t>(stream)),
+                    "qift_gptq_hessian launch");
+}
+
+qift_status qift_gptq_workspace_bytes(int64_t N, int64_t K, size_t* bytes) {
+  if (!bytes) return fail(QIFT_ERR_INVALID_ARG, "null bytes");
+  if (N < 0) return fail(QIFT_ERR_INVALID_ARG, "negative N");
+  if (K <= 0 || K % 64 != 0)
+    return fail(QIFT_ERR_INVALID_ARG, "K=%lld must be a positive multiple of 64", (long long)K);
+  if (K > QIFT_MAX_ROW)
+    return fail(QIFT_ERR_UNSUPPORTED, "K=%lld exceeds %d", (long long)K, QIFT_MAX_ROW);
+  *bytes = N == 0 ? 0 : qift::gptq_workspace_bytes(N, K);
+  return ok();
+}
+
+qift_status qift_gptq_quantize_weights(const void* W, qift_dtype w_dtype, int64_t N, int64_t K,
+                                       const double* H, int32_t had_block, qift_levels levels,
+                                       uint32_t level_table, qift_scale_rule scale_rule,
+                                       double damp, uint32_t* codes, void* scales,
+                                       qift_dtype scale_dtype, void* workspace,
+                                       size_t workspace_bytes, qift_stream stream) {
+  if (w_dtype != QIFT_F32 && w_dtype != QIFT_BF16)
+    return fail(QIFT_ERR_INVALID_ARG, "w_dtype must be F32 or BF16");
+  if (scale_dtype != QIFT_F32 && scale_dtype != QIFT_F16)
+    return fail(QIFT_ERR_INVALID_ARG, "scale_dtype must be F32 or F16");
+  if (!valid_levels(levels)) return fail(QIFT_ERR_INVALID_ARG, "invalid levels %d", (int)levels);
+  qift_status tst = check_table((int)levels, level_table);
+  if (tst != QIFT_OK) return tst;
+  if (scale_rule != QIFT_SCALE_ABSMAX && scale_rule != QIFT_SCALE_MSE)
+    return fail(QIFT_ERR_INVALID_ARG, "invalid scale_rule %d", (int)scale_rule);
+  if (!(damp > 0.0) || damp > 1e300) return fail(QIFT_ERR_INVALID_ARG, "damp must be > 0 and finite");
+  if (N < 0) return fail(QIFT_ERR_INVALID_ARG, "negative N");
+  qift_status st = check_gptq_shape(K, had_block);
+  if (st != QIFT_OK) return st;
+  if (N == 0) return ok();
+  if (N > kMaxGrid) return fail(QIFT_ERR_UNSUPPORTED, "N too large");
+  if (!W || !H || !codes || !scales || !workspace) return fail(QIFT_ERR_INVALID_ARG, "null buffer");
+  if (!aligned(codes, 16) || !aligned(workspace, 256) || !aligned(H, 8))
+    return fail(QIFT_ERR_ALIGNMENT, "codes 16-byte, workspace 256-byte, H 8-byte aligned");
+  if (!aligned(W, w_dtype == QIFT_F32 ? 4 : 2) || !aligned(scales, scale_dtype == QIFT_F16 ? 2 : 4))
+    return fail(QIFT_ERR_ALIGNMENT, "W or scales misaligned for its dtype");
+  const size_t need = qift::gptq_workspace_bytes(N, K);
+  if (workspace_bytes < need)
+    return fail(QIFT_ERR_INVALID_ARG, "workspace of %zu bytes, %zu needed", workspace_bytes, need);
+  return hip_result(qift::launch_gptq_quantize(W, w_dtype == QIFT_BF16, N, K, H, had_block,
+                                               (int)levels, level_table,
+                                               scale_rule == QIFT_SCALE_MSE, damp, codes, scales,
+                                               scale_dtype == QIFT_F16, workspace,
+                                               reinterpret_cast<hipStream_t>(stream)),
+                    "qift_gptq_quantize_weights launch");
+}
+
 // --- grouped linear ------------------------------------------------------------
 
 static qift_status check_group(const qift_linear_desc* descs, int32_t count, qift_dtype scale_dtype,

@@ -214,6 +214,14 @@ hipError_t launch_kv4(const void* KV, int bf16, int64_t rows, int D, int had_blo
                       float* scales, hipStream_t s);
 int64_t kv4_attn_tokens_per_run(int64_t S, int64_t T, int H);
 size_t kv4_attn_workspace_bytes(int64_t S, int64_t T, int H);
+size_t gptq_hessian_workspace_bytes(int64_t S, int64_t K);
+hipError_t launch_gptq_hessian(const void* X, int x_bf16, int64_t S, int64_t K, int had_block,
+                               int accumulate, double* H, void* workspace, hipStream_t s);
+size_t gptq_workspace_bytes(int64_t N, int64_t K);
+hipError_t launch_gptq_quantize(const void* W, int w_bf16, int64_t N, int64_t K,
+                                const double* H, int had_block, int levels, uint32_t table,
+                                int mse_rule, double damp, uint32_t* codes, void* scales,
+                                int scale_f16, void* workspace, hipStream_t s);
 hipError_t launch_kv4_attention(const void* q, int q_bf16, int64_t S, int64_t T, int H,
                                 int had_block, const uint8_t* kq, const float* ks,
                                 const uint8_t* vq, const float* vs, float softmax_scale,

@@ -10,7 +10,7 @@
 // float32 and run the butterflies in passes of up to four stages, each pass
 // keeping 16 (or fewer) elements in registers; the activation fast path keeps
 // the row in registers for the first eight stages (see below).
-#include "rotate_row.h"
+#include "weight_codes.h"
 
 namespace qift {
 
@@ -105,30 +105,6 @@ __device__ __forceinline__ void fwht_row(float* row, int K, int log2b, int tid) 
   }
 }
 
-// max |row[i]| * norm over the row (every thread gets the result).
-__device__ __forceinline__ float row_absmax(const float* row, int K, float norm, int tid,
-                                            float* red) {
-  float m = 0.f;
-  for (int i = tid; i < K; i += kRowThreads) m = fmaxf(m, fabsf(row[i]));
-  m *= norm;  // rounding is monotonic: max(|v|)*norm == max(|v*norm|)
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
-  if ((tid & 63) == 0) red[tid >> 6] = m;
-  __syncthreads();
-  float r = red[0];
-#pragma unroll
-  for (int w = 1; w < kRowThreads / 64; ++w) r = fmaxf(r, red[w]);
-  __syncthreads();
-  return r;
-}
-
-__device__ __forceinline__ int quant_int4(float x, float s) {
-  if (s == 0.f) return 0;
-  float q = rintf(__fdiv_rn(x, s));
-  q = fminf(fmaxf(q, -7.f), 7.f);
-  return (int)q;
-}
-
 // --- K1: rotate + per-token int4 ---------------------------------------------
 
 template <typename T>
@@ -214,99 +190,6 @@ __global__ __launch_bounds__(kRowThreads) void rotate_quant_act_batched_kernel(R
                            xq_row, jb.s_a + m, xr, row, red);
 }
 
-// --- K0: rotate + per-channel scale + nearest level + pack ----------------------
-
-__device__ __forceinline__ uint32_t code_mnz(float w, float s) {
-  // 2-bit two's complement t with half-scale level 2t+1: +inner 00, +outer 01,
-  // -outer 10, -inner 11. |w| == s is a tie and goes to the inner level.
-  if (s == 0.f) return 0u;
-  const bool outer = fabsf(w) > s;
-  const bool neg = w < 0.f;
-  return neg ? (outer ? 2u : 3u) : (outer ? 1u : 0u);
-}
-
-__device__ __forceinline__ uint32_t code_pot(float w, float s) {
-  // bit 1 = sign, bit 0 = shift by two; outer iff |w| > 2.5 s, compared
-  // exactly in double (2|w| and 5s are exact there).
-  if (s == 0.f) return 0u;
-  const bool outer = 2.0 * (double)fabsf(w) > 5.0 * (double)s;
-  const bool neg = w < 0.f;
-  return ((neg ? 1u : 0u) << 1) | (outer ? 1u : 0u);
-}
-
-// Level table: code of the level nearest to w, distances |w - L[c] * s| in
-// double (L[c] * s is exact there), the codes visited in the tie-break order
-// `pref` (byte r = the code of rank r: smaller |L|, then the non-negative
-// level, then the lower code) so that the first minimum wins.
-__device__ __forceinline__ uint32_t code_lut(float w, float s, uint32_t table, uint32_t pref) {
-  double best = __builtin_huge_val();
-  uint32_t code = pref & 3u;
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const uint32_t c = (pref >> (8 * r)) & 3u;
-    const double L = (double)(int8_t)((table >> (8 * c)) & 0xFFu);
-    const double dist = fabs((double)w - L * (double)s);
-    if (dist < best) {
-      best = dist;
-      code = c;
-    }
-  }
-  return code;
-}
-
-__device__ __forceinline__ uint32_t code2(int levels, float w, float s, uint32_t table,
-                                          uint32_t pref) {
-  return levels == QIFT_LEVELS_MNZ ? code_mnz(w, s)
-         : levels == QIFT_LEVELS_POT ? code_pot(w, s)
-                                     : code_lut(w, s, table, pref);
-}
-
-// The multiple of the scale that 2-bit code c stands for.
-__device__ __forceinline__ double real_level(int levels, uint32_t c, uint32_t table) {
-  if (levels == QIFT_LEVELS_MNZ) return 0.5 * (double)(2 * (c >= 2u ? (int)c - 4 : (int)c) + 1);
-  if (levels == QIFT_LEVELS_POT) return ((c & 2u) ? -1.0 : 1.0) * ((c & 1u) ? 4.0 : 1.0);
-  return (double)(int8_t)((table >> (8 * c)) & 0xFFu);
-}
-
-// Sum of v over the workgroup in a fixed order (every thread gets the same
-// value).
-__device__ __forceinline__ double block_sum(double v, double* red, int tid) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
-  if ((tid & 63) == 0) red[tid >> 6] = v;
-  __syncthreads();
-  double r = red[0];
-#pragma unroll
-  for (int w = 1; w < kRowThreads / 64; ++w) r += red[w];
-  __syncthreads();
-  return r;
-}
-
-__device__ __forceinline__ float stored_scale(float s32, int scale_f16) {
-  return scale_f16 ? __half2float(__float2half_rn(s32)) : s32;
-}
-
-__device__ __forceinline__ int code_bit_offset(int i) {
-  return 8 * ((i >> 1) & 3) + 4 * (i >> 3) + 2 * (i & 1);
-}
-
-// Word w of channel row n in the chunk-major tiled weight layout (W words per
-// channel row, T tiles of 16 channels): chunk c = w / 16 of all tiles comes
-// first, 256 T words for every full chunk; in chunk c (u_c = min(16, W - 16c)
-// words per channel) tile r = n / 16 holds 16 u_c words, in which the 16-byte
-// unit of lane (g, i) = ((w % 16) / 4, n % 16) sits at word 4 * (16 g + i),
-// word j = w % 4 inside it.
-__device__ __forceinline__ int64_t tiled_word(int64_t n, int64_t w, int64_t W, int64_t T) {
-  const int64_t r = n >> 4, i = n & 15;
-  const int64_t c = w >> 4, g = (w >> 2) & 3, j = w & 3;
-  const int64_t uc = W - 16 * c < 16 ? W - 16 * c : 16;
-  return c * 256 * T + r * 16 * uc + (16 * g + i) * 4 + j;
-}
-
-// Candidates of the searched scale: fractions (64 - j) / 64 of the absmax
-// scale, j = 0 .. kScaleCandidates - 1.
-constexpr int kScaleCandidates = 64;
-
 template <typename T>
 __global__ __launch_bounds__(kRowThreads) void quantize_weights_kernel(
     const T* __restrict__ W, int64_t N, int K, int log2b, float norm, int levels, uint32_t table,
@@ -327,32 +210,8 @@ __global__ __launch_bounds__(kRowThreads) void quantize_weights_kernel(
   load_row<T>(W + n * K, row, K, tid);
   __syncthreads();
   fwht_row(row, K, log2b, tid);
-  const float amax = row_absmax(row, K, norm, tid, red);
-  float s32 = __fdiv_rn(amax, outer);
-  if (mse_rule) {
-    // least squares over the candidates s_j = fl32(s32 * (64 - j) / 64),
-    // each rounded to the stored dtype with codes decided against it; the
-    // first (largest) candidate wins ties
-    const float base = s32;
-    double best = __builtin_huge_val();
-    for (int j = 0; j < kScaleCandidates; ++j) {
-      const float cand = base * ((float)(kScaleCandidates - j) / (float)kScaleCandidates);
-      const float sj = stored_scale(cand, scale_f16);
-      double e = 0.0;
-      for (int i = tid; i < K; i += kRowThreads) {
-        const float w = row[i] * norm;
-        const double lv = int4 ? (double)quant_int4(w, sj)
-                               : real_level(levels, code2(levels, w, sj, table, pref), table);
-        const double d = (double)w - lv * (double)sj;
-        e += d * d;
-      }
-      e = block_sum(e, red64, tid);
-      if (e < best) {
-        best = e;
-        s32 = cand;
-      }
-    }
-  }
+  const float s32 =
+      choose_scale(row, K, norm, levels, table, pref, outer, mse_rule, scale_f16, red, red64);
   const float s = stored_scale(s32, scale_f16);
   if (tid == 0) {
     if (scale_f16)
@@ -454,26 +313,8 @@ hipError_t launch_quantize_weights(const void* W, int w_bf16, int64_t N, int64_t
   const int lb = ilog2(had_block);
   const float nrm = had_norm(had_block);
   const unsigned grid = (unsigned)((N + 15) / 16 * 16);  // padded to whole 16-channel tiles
-  // outer level of the absmax rule; for a level table max |L| and the codes
-  // in tie-break order (smaller |L|, non-negative first, lower code)
-  float outer = levels == QIFT_LEVELS_MNZ ? 1.5f : levels == QIFT_LEVELS_POT ? 4.0f : 7.0f;
   uint32_t pref = 0;
-  if (levels == QIFT_LEVELS_LUT) {
-    int L[4], order[4] = {0, 1, 2, 3}, mx = 0;
-    for (int c = 0; c < 4; ++c) {
-      L[c] = (int)(int8_t)((table >> (8 * c)) & 0xFFu);
-      mx = L[c] < 0 ? (-L[c] > mx ? -L[c] : mx) : (L[c] > mx ? L[c] : mx);
-    }
-    auto key = [&](int c) { return (L[c] < 0 ? -L[c] : L[c]) * 16 + (L[c] < 0 ? 8 : 0) + c; };
-    for (int i = 1; i < 4; ++i)
-      for (int j = i; j > 0 && key(order[j]) < key(order[j - 1]); --j) {
-        const int tmp = order[j];
-        order[j] = order[j - 1];
-        order[j - 1] = tmp;
-      }
-    for (int r = 0; r < 4; ++r) pref |= (uint32_t)order[r] << (8 * r);
-    outer = (float)mx;
-  }
+  const float outer = level_outer_and_pref(levels, table, &pref);
   if (w_bf16)
     hipLaunchKernelGGL(quantize_weights_kernel<uint16_t>, dim3(grid), dim3(kRowThreads), lds, s,
                        reinterpret_cast<const uint16_t*>(W), N, (int)K, lb, nrm, levels, table,

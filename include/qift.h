@@ -85,7 +85,7 @@
 extern "C" {
 #endif
 
-#define QIFT_ABI_VERSION 3
+#define QIFT_ABI_VERSION 4
 
 typedef enum {
   QIFT_OK = 0,
@@ -306,6 +306,57 @@ qift_status qift_kv4_attention_decode(const void* q, qift_dtype q_dtype, int64_t
                                       const float* vs, float softmax_scale, void* out,
                                       qift_dtype out_dtype, void* workspace,
                                       size_t workspace_bytes, qift_stream stream);
+
+/*
+ * Error-compensated weight quantization with the fixed levels (GPTQ's
+ * column-by-column quantization, in which quantizing one column updates the
+ * columns after it: QTEA abstract; the Qift abstract reports the "GPTQ
+ * residual behavior" of its level sets). Offline, two calls:
+ *
+ * qift_gptq_hessian -- H (+)= X'^T X' for calibration activations X [S, K]
+ * (float32 or bfloat16), X' = X rotated along K in blocks of had_block
+ * (float64 butterflies), products and sums in float64 on the matrix cores.
+ * accumulate = 0 writes H, 1 adds to it (H summed over calibration batches).
+ *   H          [K, K] float64, symmetric (both triangles written), 8-byte aligned
+ *   workspace  device memory of qift_gptq_hessian_workspace_bytes(S, K)
+ *              bytes, 256-byte aligned, caller-owned (the rotated activations
+ *              of up to 4096 tokens at a time)
+ * Limits as qift_quantize_weights for K and had_block; S >= 0 (S = 0 with
+ * accumulate = 0 writes H = 0).
+ *
+ * qift_gptq_quantize_weights -- codes and scales of W [N, K] in the layout of
+ * qift_quantize_weights_ex (same levels, level_table, scale_rule, scale_dtype
+ * and limits; the result feeds qift_w2a4_linear unchanged):
+ *   1. W' = W rotated (float64 butterflies), rounded to float32;
+ *   2. s_n by scale_rule from the rows of W' (the plain quantizer's scales);
+ *   3. a feature k with H[k][k] = 0 gets H[k][k] = 1 and weight 0; then
+ *      damp * mean(diag H) is added to every diagonal entry;
+ *   4. U, upper triangular with U^T U = H^-1 (float64);
+ *   5. for k = 0 .. K-1 in order, per channel n: the code of the current
+ *      weight w[n][k] rounded to float32, decided against the stored s_n as
+ *      in qift_quantize_weights_ex; e = (w[n][k] - level * s_n) / U[k][k];
+ *      w[n][j] -= e * U[k][j] for every j > k (float64).
+ *   H          [K, K] float64 from qift_gptq_hessian (or any symmetric
+ *              positive semi-definite matrix); read only
+ *   damp       > 0 and finite (0.01 is customary)
+ *   workspace  qift_gptq_workspace_bytes(N, K) bytes of device memory,
+ *              256-byte aligned, caller-owned (float64 copies of W' and two
+ *              K x K matrices: 2.1 GB for N = 11008, K = 4096)
+ * The updates are blocked (64 features at a time) so their float64 rounding
+ * differs from the unblocked order; a code can then differ only where a
+ * weight lies within that rounding of a decision boundary. N = 0 is a no-op.
+ */
+qift_status qift_gptq_hessian_workspace_bytes(int64_t S, int64_t K, size_t* bytes);
+qift_status qift_gptq_hessian(const void* X, qift_dtype x_dtype, int64_t S, int64_t K,
+                              int32_t had_block, int32_t accumulate, double* H, void* workspace,
+                              size_t workspace_bytes, qift_stream stream);
+qift_status qift_gptq_workspace_bytes(int64_t N, int64_t K, size_t* bytes);
+qift_status qift_gptq_quantize_weights(const void* W, qift_dtype w_dtype, int64_t N, int64_t K,
+                                       const double* H, int32_t had_block, qift_levels levels,
+                                       uint32_t level_table, qift_scale_rule scale_rule,
+                                       double damp, uint32_t* codes, void* scales,
+                                       qift_dtype scale_dtype, void* workspace,
+                                       size_t workspace_bytes, qift_stream stream);
 
 /*
  * Grouped linear: many independent W2A4 linears (for example every linear of

@@ -32,10 +32,10 @@ def test_library_loads_and_exports_every_declared_symbol():
     lib = q.load_library()
     names = declared_functions()
     assert "qift_w2a4_linear" in names and "qift_kv4_quant" in names
-    assert len(names) == 15, names
+    assert len(names) == 19, names
     for n in names:
         assert hasattr(lib, n), n
-    assert q.abi_version() == 3
+    assert q.abi_version() == 4
     for s in range(5):
         assert q.status_string(s).startswith("QIFT_")
 
@@ -324,3 +324,84 @@ def test_binding_rejects_host_tensors():
     import torch
     with pytest.raises(ValueError):
         q.qift_rotate_quant_act(torch.zeros(2, 256), 256)
+
+
+# --- error-compensated quantization ---------------------------------------------
+
+def hess(**kw):
+    args = dict(X=A16, xd=q.QIFT_BF16, S=64, K=256, B=256, acc=0, H=A16b, ws=A16c,
+                wsb=1 << 30)
+    args.update(kw)
+    return q._C.qift_gptq_hessian(args["X"], args["xd"], args["S"], args["K"], args["B"],
+                                  args["acc"], args["H"], args["ws"], args["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(X=None), q.QIFT_ERR_INVALID_ARG),
+    (dict(H=None), q.QIFT_ERR_INVALID_ARG),
+    (dict(ws=None), q.QIFT_ERR_INVALID_ARG),
+    (dict(xd=q.QIFT_F16), q.QIFT_ERR_INVALID_ARG),
+    (dict(S=-1), q.QIFT_ERR_INVALID_ARG),
+    (dict(K=100), q.QIFT_ERR_INVALID_ARG),
+    (dict(K=16384 + 64), q.QIFT_ERR_UNSUPPORTED),
+    (dict(B=3), q.QIFT_ERR_INVALID_ARG),
+    (dict(acc=2), q.QIFT_ERR_INVALID_ARG),
+    (dict(wsb=100), q.QIFT_ERR_INVALID_ARG),
+    (dict(H=V(0x20004)), q.QIFT_ERR_ALIGNMENT),
+    (dict(ws=V(0x30080)), q.QIFT_ERR_ALIGNMENT),
+])
+def test_gptq_hessian_rejects(kw, status):
+    assert hess(**kw) == status
+    assert q.last_error() != ""
+
+
+def test_gptq_hessian_accumulate_nothing_is_noop():
+    assert hess(S=0, acc=1, X=None, H=None, ws=None) == q.QIFT_OK
+
+
+def gq(**kw):
+    args = dict(W=A16, wd=q.QIFT_F32, N=32, K=256, H=A16b, B=256, lv=0, table=0, rule=0,
+                damp=0.01, codes=A16c, scales=A16d, sd=q.QIFT_F16, ws=A16e, wsb=1 << 40)
+    args.update(kw)
+    return q._C.qift_gptq_quantize_weights(args["W"], args["wd"], args["N"], args["K"],
+                                           args["H"], args["B"], args["lv"], args["table"],
+                                           args["rule"], args["damp"], args["codes"],
+                                           args["scales"], args["sd"], args["ws"], args["wsb"],
+                                           None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(W=None), q.QIFT_ERR_INVALID_ARG),
+    (dict(H=None), q.QIFT_ERR_INVALID_ARG),
+    (dict(codes=None), q.QIFT_ERR_INVALID_ARG),
+    (dict(ws=None), q.QIFT_ERR_INVALID_ARG),
+    (dict(damp=0.0), q.QIFT_ERR_INVALID_ARG),
+    (dict(damp=-1.0), q.QIFT_ERR_INVALID_ARG),
+    (dict(damp=float("nan")), q.QIFT_ERR_INVALID_ARG),
+    (dict(damp=float("inf")), q.QIFT_ERR_INVALID_ARG),
+    (dict(lv=9), q.QIFT_ERR_INVALID_ARG),
+    (dict(lv=3, table=0), q.QIFT_ERR_INVALID_ARG),
+    (dict(table=5), q.QIFT_ERR_INVALID_ARG),
+    (dict(rule=7), q.QIFT_ERR_INVALID_ARG),
+    (dict(sd=q.QIFT_BF16), q.QIFT_ERR_INVALID_ARG),
+    (dict(K=80), q.QIFT_ERR_INVALID_ARG),
+    (dict(N=-1), q.QIFT_ERR_INVALID_ARG),
+    (dict(wsb=1000), q.QIFT_ERR_INVALID_ARG),
+    (dict(codes=V(0x30008)), q.QIFT_ERR_ALIGNMENT),
+    (dict(ws=V(0x50010)), q.QIFT_ERR_ALIGNMENT),
+])
+def test_gptq_quantize_rejects(kw, status):
+    assert gq(**kw) == status
+    assert q.last_error() != ""
+
+
+def test_gptq_empty_is_noop_and_workspace_sizes():
+    assert gq(N=0, W=None, codes=None, scales=None, ws=None) == q.QIFT_OK
+    assert q.qift_gptq_workspace_bytes(0, 256) == 0
+    # two K x K float64 matrices, float64 weights, the 64-feature panel, the
+    # errors of a column block, codes and flags
+    N, K = 11008, 4096
+    b = q.qift_gptq_workspace_bytes(N, K)
+    assert 8 * (2 * K * K + N * K) < b <= 8 * (2 * K * K + N * K) + N * K + 8 * 64 * (N + K) + K + 8 * 256
+    assert q.qift_gptq_hessian_workspace_bytes(100, 256) == 100 * 256 * 8
+    assert q.qift_gptq_hessian_workspace_bytes(10000, 256) == 4096 * 256 * 8
