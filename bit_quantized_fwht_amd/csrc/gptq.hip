@@ -81,8 +81,8 @@ __global__ __launch_bounds__(kGptqThreads) void rotate_rows_f64_kernel(
 // opB(k, n) = B[k ldb + n] or B[n ldb + k]. lower: only n <= m is computed
 // and written. 64 x 64 tiles, 16 features per LDS stage, four waves of 32 x
 // 32, each as 2 x 2 blocks of v_mfma_f64_16x16x4f64 (operand lane l: row or
-// column l % 16, feature l / 16; result register r of lane l: row 4 (l / 16)
-// + r, column l % 16).
+// column l % 16, feature l / 16; result register r of lane l: row l / 16 +
+// 4 r, column l % 16 -- the rows interleave, unlike the 32-bit results).
 
 struct GemmArgs {
   const double* A;
@@ -168,7 +168,7 @@ __global__ __launch_bounds__(kGptqThreads) void gemm_f64_kernel(GemmArgs g) {
     for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int64_t m = m0 + wm + 16 * i + 4 * kq + r;
+        const int64_t m = m0 + wm + 16 * i + kq + 4 * r;
         const int64_t n = n0 + wn + 16 * j + r16;
         if (m >= g.M || n >= g.N || (g.lower && n > m)) continue;
         double* c = g.C + m * g.ldc + n;
