@@ -44,6 +44,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 INT8_PEAK_TOPS = 5000.0        # MI355X dense int8 MFMA, TOP/s
+FP64_PEAK_TFLOPS = 78.6        # MI355X float64 (matrix cores and vector ALUs), TFLOP/s
 METRIC = "W2A4 linear: decode weight-stream GB/s + prefill int8 TOPS, % of roofline"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "linear_grouped_decode_llama7b_counters.json")
 # the sources the grouped decode kernel is compiled from: the counter summary
@@ -106,7 +107,31 @@ def unit_attention(q, torch, dev, steps):
         q.qift_kv4_attention_decode(qv, kq, ks, vq, vs, D)
 
 
-UNITS = {"prefill_up_proj": unit_prefill_up_proj, "kv4": unit_kv4, "attention": unit_attention}
+def gptq_inputs(torch, dev, N=11008, K=4096, S=2048, extra_tokens=0):
+    """LLaMA-7B up_proj weights (11008 x 4096, N(0, 0.02^2)), S correlated
+    calibration tokens (bf16) and extra_tokens more from the same draw
+    (float32, for evaluation), on the device."""
+    import synth_inputs as si
+    W = si.device_weights(N, K, seed=5, sigma=0.02, device=dev)
+    Xall = si.calibration_activations(S + extra_tokens, K, seed=41)
+    X = si.to_bf16(Xall[:S]).to(dev)
+    Xe = torch.from_numpy(Xall[S:]).to(dev)
+    return W, X, Xe
+
+
+def unit_gptq(q, torch, dev, steps):
+    """Error-compensated quantization of the LLaMA-7B up_proj (11008 x 4096,
+    block 4096, MNZ, fp16 scales) with 2048 calibration tokens: H, then the
+    codes, per step."""
+    W, X, _ = gptq_inputs(torch, dev)
+    ws = torch.empty((q.qift_gptq_workspace_bytes(*W.shape),), dtype=torch.uint8, device=dev)
+    for _ in range(steps):
+        H = q.qift_gptq_hessian(X, 4096)
+        q.qift_gptq_quantize_weights(W, H, 4096, "mnz", torch.float16, workspace=ws)
+
+
+UNITS = {"prefill_up_proj": unit_prefill_up_proj, "kv4": unit_kv4, "attention": unit_attention,
+         "gptq": unit_gptq}
 
 
 def log(*a):
@@ -366,6 +391,21 @@ def cpu_oracle_units():
     dt = time.perf_counter() - t0
     out["weight_quantizer_searched_scale"] = {"rows": 16, "K": 4096, "s": round(dt, 3),
                                               "rows_per_s": round(16 / dt, 2)}
+    # error-compensated quantization of the up_proj: H and its factor from 2048
+    # calibration tokens (once per layer input), then 8 of the 11008 channels
+    K, S = 4096, 2048
+    X = si.calibration_activations(S, K, seed=41)
+    t0 = time.perf_counter()
+    Hm, dead = O.gptq_hessian(X, K, 0.01)
+    factor = (O.gptq_factor(Hm), dead)
+    dt_f = time.perf_counter() - t0
+    W = si.weights(8, K, seed=18)
+    t0 = time.perf_counter()
+    O.gptq_quantize_weights(W, X, K, "mnz", "f16", factor=factor)
+    dt_r = time.perf_counter() - t0
+    out["gptq_up_proj"] = {"K": K, "calibration_tokens": S, "hessian_and_factor_s": round(dt_f, 3),
+                           "rows": 8, "rows_s": round(dt_r, 3),
+                           "rows_per_s": round(8 / dt_r, 2)}
     return out
 
 
@@ -629,6 +669,44 @@ def level_set_comparison(q, torch, dev):
     return out
 
 
+def gptq_bench(q, torch, dev):
+    """Error-compensated quantization of the LLaMA-7B up_proj with 2048
+    calibration tokens: the time of the Hessian and of the quantizer, their
+    float64 work (the symmetric product S K (K + 1); Cholesky and triangular
+    inverse 2 K^3 / 3; the column updates N K (K - 1)) as TFLOP/s against the
+    float64 peak, and the W2A4 output error of plain and compensated codes on
+    64 further tokens of the calibration distribution."""
+    N, K, S, B = 11008, 4096, 2048, 4096
+    W, X, Xe = gptq_inputs(torch, dev, N, K, S, extra_tokens=64)
+    hws = torch.empty((q.qift_gptq_hessian_workspace_bytes(S, K),), dtype=torch.uint8, device=dev)
+    ws = torch.empty((q.qift_gptq_workspace_bytes(N, K),), dtype=torch.uint8, device=dev)
+    H = torch.empty((K, K), dtype=torch.float64, device=dev)
+    h_ms, h_min, _ = time_fn(torch, lambda: q.qift_gptq_hessian(X, B, H=H, workspace=hws), 5, 1)
+    codes = torch.empty((N, K // 16), dtype=torch.int32, device=dev)
+    scales = torch.empty((N,), dtype=torch.float16, device=dev)
+    g_ms, g_min, _ = time_fn(torch, lambda: q.qift_gptq_quantize_weights(
+        W, H, B, "mnz", torch.float16, codes=codes, scales=scales, workspace=ws), 3, 1)
+    h_flop = S * K * (K + 1)
+    f_flop = 2 * K ** 3 / 3
+    u_flop = N * K * (K - 1)
+    # output error against the unquantized product, plain and compensated codes
+    ref = (Xe.double() @ W.double().T)
+    xq, s_a, _ = q.qift_rotate_quant_act(Xe, B)
+    errs = {}
+    for name, cs in (("plain", q.qift_quantize_weights(W, B, "mnz", torch.float16)),
+                     ("compensated", (codes, scales))):
+        Y = q.qift_w2a4_linear(xq, s_a, cs[0], cs[1], "mnz", N=N)
+        errs[name] = round(float(torch.linalg.norm(Y.double() - ref) / torch.linalg.norm(ref)), 4)
+    torch.cuda.synchronize()
+    del ws, hws
+    return {"N": N, "K": K, "calibration_tokens": S, "block": B, "levels": "mnz",
+            "hessian_ms": round(h_ms, 3), "hessian_TFLOPs": round(h_flop / h_ms / 1e9, 2),
+            "quantize_ms": round(g_ms, 3),
+            "quantize_TFLOPs": round((f_flop + u_flop) / g_ms / 1e9, 2),
+            "quantize_frac_of_fp64_peak": round((f_flop + u_flop) / g_ms / 1e9 / FP64_PEAK_TFLOPS, 4),
+            "w2a4_rel_l2_output_error": errs}
+
+
 def layer_by_layer_decode(q, torch, dev, M=1):
     """A dependent, layer-by-layer decode of the LLaMA-7B-shaped stack: per
     layer four linears with the q/k/v and the gate/up weights concatenated
@@ -835,6 +913,7 @@ def measure_extras(q, torch, dev, stack, args):
     del sets, flush
     extra["kv4_attention_decode_llama7b"] = kv4_attention_bench(q, torch, dev)
     extra["level_sets_llama7b_q_proj"] = level_set_comparison(q, torch, dev)
+    extra["gptq_llama7b_up_proj"] = gptq_bench(q, torch, dev)
     extra["context"] = {"qtea_lut_kernel_per_token_speedup_vs_fp16": 7.2,
                         "note": "speedup printed for a different (ternary) method; hardware not stated"}
     return extra

@@ -15,9 +15,10 @@
 //     damp * mean(diag H) is added to the diagonal;
 //  5. U with U^T U = H^-1, upper triangular: if J reverses the order of the
 //     features and J H J = L L^T (Cholesky), then U = J L^-1 J. So: a blocked
-//     Cholesky of the reversed H and a blocked inverse of the lower factor,
-//     both made of small in-LDS kernels for the 64 x 64 diagonal blocks and
-//     float64 matrix-core products for everything else;
+//     right-looking Cholesky of the reversed H and a blocked right-looking
+//     inverse of the lower factor, both made of small in-LDS kernels for the
+//     64-row diagonal steps and float64 matrix-core products of rank 64 for
+//     everything below them;
 //  6. the features in blocks of 64: one thread per channel row runs the 64
 //     decisions of the block with the row's 64 weights in registers, each
 //     decision's error divided by U[k][k] is removed from the later weights of
@@ -311,24 +312,29 @@ __global__ __launch_bounds__(kGptqThreads) void trsm_panel_kernel(double* __rest
   }
 }
 
-// Li[i0 + r][i0 + c] = (L_ii^-1)[r][c] for r >= c: L Y = I solved in LDS, one
-// row of Y per step (right-looking).
-__global__ __launch_bounds__(kGptqThreads) void trtri_diag_kernel(const double* __restrict__ A,
-                                                                  double* __restrict__ Li,
-                                                                  int64_t K, int64_t i0, int ib) {
+// Block row k0 .. k0 + kb - 1 of the inverse, in place: the rows hold the
+// right-hand side B (the identity minus the contributions of the earlier block
+// rows) and become Y with L_kk Y = B. One workgroup per 64 columns (columns
+// >= k0 + kb are zero and stay so), the 64 x 64 piece in LDS, one row of Y
+// per step (right-looking).
+__global__ __launch_bounds__(kGptqThreads) void trsm_rows_kernel(const double* __restrict__ A,
+                                                                 double* __restrict__ Li,
+                                                                 int64_t K, int64_t k0, int kb) {
   __shared__ double L[kTri][kTri + 1];
   __shared__ double Y[kTri][kTri + 1];
   const int tid = threadIdx.x;
+  const int64_t c0 = (int64_t)blockIdx.x * kTri;
+  const int cols = (int)(K - c0 < kTri ? K - c0 : kTri);
   for (int idx = tid; idx < kTri * kTri; idx += kGptqThreads) {
     const int r = idx / kTri, c = idx % kTri;
-    L[r][c] = (r < ib && c <= r) ? A[(i0 + r) * K + i0 + c] : (r == c ? 1.0 : 0.0);
-    Y[r][c] = r == c ? 1.0 : 0.0;
+    L[r][c] = (r < kb && c <= r) ? A[(k0 + r) * K + k0 + c] : (r == c ? 1.0 : 0.0);
+    Y[r][c] = (r < kb && c < cols) ? Li[(k0 + r) * K + c0 + c] : 0.0;
   }
   __syncthreads();
-  for (int q = 0; q < ib; ++q) {
+  for (int q = 0; q < kb; ++q) {
     if (tid < kTri) Y[q][tid] /= L[q][q];
     __syncthreads();
-    const int rem = ib - q - 1;
+    const int rem = kb - q - 1;
     for (int idx = tid; idx < rem * kTri; idx += kGptqThreads) {
       const int r = q + 1 + idx / kTri, c = idx % kTri;
       Y[r][c] -= L[r][q] * Y[q][c];
@@ -337,8 +343,15 @@ __global__ __launch_bounds__(kGptqThreads) void trtri_diag_kernel(const double* 
   }
   for (int idx = tid; idx < kTri * kTri; idx += kGptqThreads) {
     const int r = idx / kTri, c = idx % kTri;
-    if (r < ib && c <= r) Li[(i0 + r) * K + i0 + c] = Y[r][c];
+    if (r < kb && c < cols) Li[(k0 + r) * K + c0 + c] = Y[r][c];
   }
+}
+
+// Li = I
+__global__ void identity_kernel(double* __restrict__ Li, int64_t K) {
+  const int64_t i = (int64_t)blockIdx.y * 16 + (threadIdx.x >> 4);
+  const int64_t j = (int64_t)blockIdx.x * 16 + (threadIdx.x & 15);
+  if (i < K && j < K) Li[i * K + j] = i == j ? 1.0 : 0.0;
 }
 
 // --- 3. scales ------------------------------------------------------------------------
@@ -506,7 +519,7 @@ hipError_t launch_gptq_hessian(const void* X, int x_bf16, int64_t S, int64_t K, 
 
 namespace {
 struct GptqWork {
-  double *Wr, *A, *Li, *T, *E, *lam;
+  double *Wr, *A, *Li, *E, *lam;
   uint8_t *codes8, *dead;
 };
 
@@ -523,7 +536,6 @@ size_t carve(void* base, int64_t N, int64_t K, GptqWork* w) {
   w->Wr = reinterpret_cast<double*>(take((size_t)N * K * d));
   w->A = reinterpret_cast<double*>(take((size_t)K * K * d));
   w->Li = reinterpret_cast<double*>(take((size_t)K * K * d));
-  w->T = reinterpret_cast<double*>(take((size_t)kTri * K * d));
   w->E = reinterpret_cast<double*>(take((size_t)N * kColBlock * d));
   w->lam = reinterpret_cast<double*>(take(d));
   w->codes8 = reinterpret_cast<uint8_t*>(take((size_t)N * K));
@@ -572,19 +584,18 @@ hipError_t launch_gptq_quantize(const void* W, int w_bf16, int64_t N, int64_t K,
       if ((e = gemm_f64(g, s)) != hipSuccess) return e;
     }
   }
-  // 5b. Li = L^-1 by block rows: Li[i, :i] = -Li_ii (L[i, :i] Li[:i, :i])
-  hipLaunchKernelGGL(fill_f64_kernel, dim3(2048), dim3(256), 0, s, w.Li, K * K, 0.0);
-  for (int64_t i0 = 0; i0 < K; i0 += kTri) {
-    const int ib = (int)(K - i0 < kTri ? K - i0 : kTri);
-    if (i0 > 0) {
-      GemmArgs g{w.A + i0 * K, K, 0, w.Li, K, 0, w.T, K, ib, i0, i0, 1.0, 0.0, 0};
-      if ((e = gemm_f64(g, s)) != hipSuccess) return e;
-    }
-    hipLaunchKernelGGL(trtri_diag_kernel, dim3(1), dim3(kGptqThreads), 0, s, w.A, w.Li, K, i0,
-                       ib);
-    if (i0 > 0) {
-      GemmArgs g{w.Li + i0 * K + i0, K, 0, w.T, K, 0, w.Li + i0 * K, K, ib, i0, ib,
-                 -1.0, 0.0, 0};
+  // 5b. Li = L^-1, right-looking: block row k solved against L_kk, then
+  // removed from every later block row (Li[k0+kb:, :k0+kb] -= L[k0+kb:, k] Y_k)
+  hipLaunchKernelGGL(identity_kernel, grid16(K), dim3(256), 0, s, w.Li, K);
+  for (int64_t k0 = 0; k0 < K; k0 += kTri) {
+    const int kb = (int)(K - k0 < kTri ? K - k0 : kTri);
+    const int64_t ncols = k0 + kb;
+    hipLaunchKernelGGL(trsm_rows_kernel, dim3((unsigned)((ncols + kTri - 1) / kTri)),
+                       dim3(kGptqThreads), 0, s, w.A, w.Li, K, k0, kb);
+    const int64_t rest = K - k0 - kb;
+    if (rest > 0) {
+      GemmArgs g{w.A + (k0 + kb) * K + k0, K, 0, w.Li + k0 * K, K, 0, w.Li + (k0 + kb) * K, K,
+                 rest, ncols, kb, -1.0, 1.0, 0};
       if ((e = gemm_f64(g, s)) != hipSuccess) return e;
     }
   }

@@ -398,10 +398,10 @@ def test_gptq_quantize_rejects(kw, status):
 def test_gptq_empty_is_noop_and_workspace_sizes():
     assert gq(N=0, W=None, codes=None, scales=None, ws=None) == q.QIFT_OK
     assert q.qift_gptq_workspace_bytes(0, 256) == 0
-    # two K x K float64 matrices, float64 weights, the 64-feature panel, the
-    # errors of a column block, codes and flags
+    # two K x K float64 matrices, float64 weights, the errors of a column
+    # block, codes and flags
     N, K = 11008, 4096
     b = q.qift_gptq_workspace_bytes(N, K)
-    assert 8 * (2 * K * K + N * K) < b <= 8 * (2 * K * K + N * K) + N * K + 8 * 64 * (N + K) + K + 8 * 256
+    assert 8 * (2 * K * K + N * K) < b <= 8 * (2 * K * K + N * K) + N * K + 8 * 64 * N + K + 8 * 256
     assert q.qift_gptq_hessian_workspace_bytes(100, 256) == 100 * 256 * 8
     assert q.qift_gptq_hessian_workspace_bytes(10000, 256) == 4096 * 256 * 8
