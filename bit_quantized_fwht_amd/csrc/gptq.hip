@@ -250,101 +250,181 @@ __global__ void gptq_unreverse_kernel(const double* __restrict__ Li, int64_t K,
 
 // --- 5. Cholesky and the inverse of the lower factor ---------------------------------
 
-// Cholesky of the jb x jb diagonal block at (j0, j0) in place (lower part),
-// right-looking in LDS.
+// The 64 x 64 diagonal-step kernels below give each of 256 threads a 4 x 4
+// piece of the block in registers (rows 4 (t / 16) .., columns 4 (t % 16) ..);
+// the column (or row) that a step divides is passed through LDS, double
+// buffered by the step's parity so that one barrier per step orders both its
+// write and the previous step's reads. Outside the first jb (kb) rows and
+// columns the block is the identity.
+
+// Cholesky of the jb x jb diagonal block at (j0, j0) in place (lower part).
 __global__ __launch_bounds__(kGptqThreads) void potrf_diag_kernel(double* __restrict__ A,
                                                                   int64_t K, int64_t j0, int jb) {
-  __shared__ double L[kTri][kTri + 1];
+  __shared__ double col[2][kTri];
+  __shared__ double dg[2];
   const int tid = threadIdx.x;
-  for (int idx = tid; idx < jb * jb; idx += kGptqThreads) {
-    const int r = idx / jb, c = idx % jb;
-    L[r][c] = c <= r ? A[(j0 + r) * K + j0 + c] : 0.0;
-  }
-  __syncthreads();
-  for (int c = 0; c < jb; ++c) {
-    if (tid == 0) L[c][c] = sqrt(L[c][c]);
-    __syncthreads();
-    for (int r = c + 1 + tid; r < jb; r += kGptqThreads) L[r][c] /= L[c][c];
-    __syncthreads();
-    const int rem = jb - c - 1;
-    for (int idx = tid; idx < rem * rem; idx += kGptqThreads) {
-      const int r = c + 1 + idx / rem, q = c + 1 + idx % rem;
-      if (q <= r) L[r][q] -= L[r][c] * L[q][c];
+  const int rb = 4 * (tid >> 4), cb = 4 * (tid & 15);
+  double a[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int r = rb + i, c = cb + j;
+      a[i][j] = (r < jb && c <= r) ? A[(j0 + r) * K + j0 + c] : (r == c ? 1.0 : 0.0);
     }
-    __syncthreads();
+  for (int blk = 0; blk < kTri / 4; ++blk) {
+#pragma unroll
+    for (int cc = 0; cc < 4; ++cc) {
+      const int c = 4 * blk + cc, par = c & 1;
+      if (rb == 4 * blk && cb == 4 * blk) {  // owner of the diagonal entry
+        a[cc][cc] = sqrt(a[cc][cc]);
+        dg[par] = a[cc][cc];
+      }
+      __syncthreads();
+      if (cb == 4 * blk) {  // owners of column c
+        const double d = dg[par];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          if (rb + i > c) a[i][cc] /= d;
+          col[par][rb + i] = rb + i > c ? a[i][cc] : 0.0;
+        }
+      }
+      __syncthreads();
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const double lr = col[par][rb + i];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int q = cb + j;
+          if (q > c && rb + i >= q) a[i][j] -= lr * col[par][q];
+        }
+      }
+    }
   }
-  for (int idx = tid; idx < jb * jb; idx += kGptqThreads) {
-    const int r = idx / jb, c = idx % jb;
-    if (c <= r) A[(j0 + r) * K + j0 + c] = L[r][c];
-  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int r = rb + i, c = cb + j;
+      if (r < jb && c <= r) A[(j0 + r) * K + j0 + c] = a[i][j];
+    }
 }
 
 // Panel below the factored diagonal block: rows r >= j0 + jb get
-// A[r, j0 : j0+jb] <- A[r, j0 : j0+jb] L_jj^-T. A workgroup takes 64 rows into
-// LDS and solves them together, one feature per step (right-looking: once
-// x[r][c] is final it is removed from the later features of the row).
+// A[r, j0 : j0+jb] <- A[r, j0 : j0+jb] L_jj^-T. A workgroup solves 64 rows,
+// one feature (column) per step, right-looking: once column c is final it is
+// removed from the later columns.
 __global__ __launch_bounds__(kGptqThreads) void trsm_panel_kernel(double* __restrict__ A,
                                                                   int64_t K, int64_t j0, int jb) {
   __shared__ double L[kTri][kTri + 1];
-  __shared__ double X[kTri][kTri + 1];
+  __shared__ double col[2][kTri];
   const int tid = threadIdx.x;
+  const int rb = 4 * (tid >> 4), cb = 4 * (tid & 15);
   const int64_t r0 = j0 + jb + (int64_t)blockIdx.x * kTri;
   const int rows = (int)(K - r0 < kTri ? K - r0 : kTri);
   for (int idx = tid; idx < kTri * kTri; idx += kGptqThreads) {
     const int r = idx / kTri, c = idx % kTri;
     L[r][c] = (r < jb && c <= r) ? A[(j0 + r) * K + j0 + c] : (r == c ? 1.0 : 0.0);
-    X[r][c] = (r < rows && c < jb) ? A[(r0 + r) * K + j0 + c] : 0.0;
   }
-  __syncthreads();
-  for (int c = 0; c < jb; ++c) {
-    if (tid < kTri) X[tid][c] /= L[c][c];
-    __syncthreads();
-    const int rem = jb - c - 1;
-    for (int idx = tid; idx < kTri * rem; idx += kGptqThreads) {
-      const int r = idx / rem, q = c + 1 + idx % rem;
-      X[r][q] -= X[r][c] * L[q][c];
+  double x[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int r = rb + i, c = cb + j;
+      x[i][j] = (r < rows && c < jb) ? A[(r0 + r) * K + j0 + c] : 0.0;
     }
-    __syncthreads();
+  __syncthreads();
+  for (int blk = 0; blk < kTri / 4; ++blk) {
+#pragma unroll
+    for (int cc = 0; cc < 4; ++cc) {
+      const int c = 4 * blk + cc, par = c & 1;
+      if (cb == 4 * blk) {
+        const double d = L[c][c];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          x[i][cc] /= d;
+          col[par][rb + i] = x[i][cc];
+        }
+      }
+      __syncthreads();
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int q = cb + j;
+        if (q > c) {
+          const double l = L[q][c];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) x[i][j] -= col[par][rb + i] * l;
+        }
+      }
+    }
   }
-  for (int idx = tid; idx < kTri * kTri; idx += kGptqThreads) {
-    const int r = idx / kTri, c = idx % kTri;
-    if (r < rows && c < jb) A[(r0 + r) * K + j0 + c] = X[r][c];
-  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int r = rb + i, c = cb + j;
+      if (r < rows && c < jb) A[(r0 + r) * K + j0 + c] = x[i][j];
+    }
 }
 
 // Block row k0 .. k0 + kb - 1 of the inverse, in place: the rows hold the
 // right-hand side B (the identity minus the contributions of the earlier block
 // rows) and become Y with L_kk Y = B. One workgroup per 64 columns (columns
-// >= k0 + kb are zero and stay so), the 64 x 64 piece in LDS, one row of Y
-// per step (right-looking).
+// >= k0 + kb are zero and stay so), one row of Y per step (right-looking).
 __global__ __launch_bounds__(kGptqThreads) void trsm_rows_kernel(const double* __restrict__ A,
                                                                  double* __restrict__ Li,
                                                                  int64_t K, int64_t k0, int kb) {
   __shared__ double L[kTri][kTri + 1];
-  __shared__ double Y[kTri][kTri + 1];
+  __shared__ double row[2][kTri];
   const int tid = threadIdx.x;
+  const int rb = 4 * (tid >> 4), cb = 4 * (tid & 15);
   const int64_t c0 = (int64_t)blockIdx.x * kTri;
   const int cols = (int)(K - c0 < kTri ? K - c0 : kTri);
   for (int idx = tid; idx < kTri * kTri; idx += kGptqThreads) {
     const int r = idx / kTri, c = idx % kTri;
     L[r][c] = (r < kb && c <= r) ? A[(k0 + r) * K + k0 + c] : (r == c ? 1.0 : 0.0);
-    Y[r][c] = (r < kb && c < cols) ? Li[(k0 + r) * K + c0 + c] : 0.0;
   }
-  __syncthreads();
-  for (int q = 0; q < kb; ++q) {
-    if (tid < kTri) Y[q][tid] /= L[q][q];
-    __syncthreads();
-    const int rem = kb - q - 1;
-    for (int idx = tid; idx < rem * kTri; idx += kGptqThreads) {
-      const int r = q + 1 + idx / kTri, c = idx % kTri;
-      Y[r][c] -= L[r][q] * Y[q][c];
+  double y[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int r = rb + i, c = cb + j;
+      y[i][j] = (r < kb && c < cols) ? Li[(k0 + r) * K + c0 + c] : 0.0;
     }
-    __syncthreads();
+  __syncthreads();
+  for (int blk = 0; blk < kTri / 4; ++blk) {
+#pragma unroll
+    for (int qq = 0; qq < 4; ++qq) {
+      const int q = 4 * blk + qq, par = q & 1;
+      if (rb == 4 * blk) {
+        const double d = L[q][q];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          y[qq][j] /= d;
+          row[par][cb + j] = y[qq][j];
+        }
+      }
+      __syncthreads();
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = rb + i;
+        if (r > q) {
+          const double l = L[r][q];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) y[i][j] -= l * row[par][cb + j];
+        }
+      }
+    }
   }
-  for (int idx = tid; idx < kTri * kTri; idx += kGptqThreads) {
-    const int r = idx / kTri, c = idx % kTri;
-    if (r < kb && c < cols) Li[(k0 + r) * K + c0 + c] = Y[r][c];
-  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int r = rb + i, c = cb + j;
+      if (r < kb && c < cols) Li[(k0 + r) * K + c0 + c] = y[i][j];
+    }
 }
 
 // Li = I
@@ -382,7 +462,9 @@ __global__ __launch_bounds__(kRowThreads) void gptq_scales_kernel(
 // takes the code of its current weight rounded to float32 against the stored
 // scale; err = (w - level * s) / U[j][j] is kept in E and removed from the
 // later weights of the block along row j of U.
-__global__ __launch_bounds__(kGptqThreads) void gptq_block_kernel(
+constexpr int kBlockThreads = 256;  // (one-wave workgroups, spread over more CUs, ran 20% slower)
+
+__global__ __launch_bounds__(kBlockThreads) void gptq_block_kernel(
     double* __restrict__ Wr, int64_t N, int64_t K, int64_t b0, int bb,
     const double* __restrict__ U, const void* __restrict__ scales, int scale_f16, int levels,
     uint32_t table, uint32_t pref, const uint8_t* __restrict__ dead,
@@ -390,13 +472,13 @@ __global__ __launch_bounds__(kGptqThreads) void gptq_block_kernel(
   __shared__ double Ub[kColBlock][kColBlock + 1];
   __shared__ uint8_t dd[kColBlock];
   const int tid = threadIdx.x;
-  for (int idx = tid; idx < kColBlock * kColBlock; idx += kGptqThreads) {
+  for (int idx = tid; idx < kColBlock * kColBlock; idx += kBlockThreads) {
     const int j = idx / kColBlock, l = idx % kColBlock;
     Ub[j][l] = (j < bb && l < bb && l >= j) ? U[(b0 + j) * K + b0 + l] : (j == l ? 1.0 : 0.0);
   }
   if (tid < kColBlock) dd[tid] = tid < bb ? dead[b0 + tid] : 1;
   __syncthreads();
-  const int64_t n = (int64_t)blockIdx.x * kGptqThreads + tid;
+  const int64_t n = (int64_t)blockIdx.x * kBlockThreads + tid;
   if (n >= N) return;
   const float sf = scale_f16 ? __half2float(reinterpret_cast<const __half*>(scales)[n])
                              : reinterpret_cast<const float*>(scales)[n];
@@ -603,10 +685,10 @@ hipError_t launch_gptq_quantize(const void* W, int w_bf16, int64_t N, int64_t K,
   hipLaunchKernelGGL(gptq_unreverse_kernel, grid16(K), dim3(256), 0, s, w.Li, K, w.A);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   // 6. the column blocks
-  const unsigned rows_grid = (unsigned)((N + kGptqThreads - 1) / kGptqThreads);
+  const unsigned rows_grid = (unsigned)((N + kBlockThreads - 1) / kBlockThreads);
   for (int64_t b0 = 0; b0 < K; b0 += kColBlock) {
     const int bb = (int)(K - b0 < kColBlock ? K - b0 : kColBlock);
-    hipLaunchKernelGGL(gptq_block_kernel, dim3(rows_grid), dim3(kGptqThreads), 0, s, w.Wr, N, K,
+    hipLaunchKernelGGL(gptq_block_kernel, dim3(rows_grid), dim3(kBlockThreads), 0, s, w.Wr, N, K,
                        b0, bb, w.A, scales, scale_f16, levels, table, pref, w.dead, w.codes8,
                        w.E);
     const int64_t rest = K - b0 - bb;
