@@ -169,3 +169,17 @@ def test_codes_lower_linear_error():
             errs.append(rel_l2(Y.cpu().numpy(), ref))
         say(f"  {kind}: plain {errs[0]:.4f}, compensated {errs[1]:.4f}")
         assert errs[1] < 0.9 * errs[0], (kind, errs)
+
+
+def test_bfloat16_weights_and_tokens():
+    N, K, S, B = 37, 512, 400, 512
+    W = si.weights(N, K, seed=97)
+    X = si.calibration_activations(S, K, seed=98)
+    Wt, Xt = si.to_bf16(W).to(DEV), si.to_bf16(X).to(DEV)
+    say("gptq bf16 weights and tokens")
+    for kind, table in (("mnz", None), ("int4", None)):
+        cg, sg = gpu_gptq(Wt, Xt, B, kind, "f16", table)
+        co, so, _ = O.gptq_quantize_weights(si.bf16_values(Wt), si.bf16_values(Xt), B, kind,
+                                            "f16", table)
+        assert np.array_equal(sg.astype(np.float32), so.astype(np.float32))
+        assert np.array_equal(cg, co), kind
