@@ -413,7 +413,8 @@ qift_status qift_gptq_quantize_weights(const void* W, qift_dtype w_dtype, int64_
   qift_status st = check_gptq_shape(K, had_block);
   if (st != QIFT_OK) return st;
   if (N == 0) return ok();
-  if (N > kMaxGrid) return fail(QIFT_ERR_UNSUPPORTED, "N too large");
+  // the rotation launches one workgroup per segment of at least 64 features
+  if (N > kMaxGrid / (K / 64)) return fail(QIFT_ERR_UNSUPPORTED, "N too large");
   if (!W || !H || !codes || !scales || !workspace) return fail(QIFT_ERR_INVALID_ARG, "null buffer");
   if (!aligned(codes, 16) || !aligned(workspace, 256) || !aligned(H, 8))
     return fail(QIFT_ERR_ALIGNMENT, "codes 16-byte, workspace 256-byte, H 8-byte aligned");

@@ -344,7 +344,10 @@ qift_status qift_kv4_attention_decode(const void* q, qift_dtype q_dtype, int64_t
  *              K x K matrices: 2.1 GB for N = 11008, K = 4096)
  * The updates are blocked (64 features at a time) so their float64 rounding
  * differs from the unblocked order; a code can then differ only where a
- * weight lies within that rounding of a decision boundary. N = 0 is a no-op.
+ * weight lies within that rounding of a decision boundary. N = 0 is a no-op;
+ * N * K / 64 above 2^31 - 1 is QIFT_ERR_UNSUPPORTED. H must be positive
+ * definite after the damping (true for X'^T X' with damp > 0); otherwise
+ * the codes are undefined.
  */
 qift_status qift_gptq_hessian_workspace_bytes(int64_t S, int64_t K, size_t* bytes);
 qift_status qift_gptq_hessian(const void* X, qift_dtype x_dtype, int64_t S, int64_t K,

@@ -387,6 +387,7 @@ def gq(**kw):
     (dict(K=80), q.QIFT_ERR_INVALID_ARG),
     (dict(N=-1), q.QIFT_ERR_INVALID_ARG),
     (dict(wsb=1000), q.QIFT_ERR_INVALID_ARG),
+    (dict(N=1 << 30, K=4096), q.QIFT_ERR_UNSUPPORTED),
     (dict(codes=V(0x30008)), q.QIFT_ERR_ALIGNMENT),
     (dict(ws=V(0x50010)), q.QIFT_ERR_ALIGNMENT),
 ])
