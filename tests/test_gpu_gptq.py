@@ -183,3 +183,29 @@ def test_bfloat16_weights_and_tokens():
                                             "f16", table)
         assert np.array_equal(sg.astype(np.float32), so.astype(np.float32))
         assert np.array_equal(cg, co), kind
+
+
+def test_longest_k_lowers_output_error():
+    """LLaMA-3.1-8B down_proj rows (K = 14336, block 1024: 224 factorization
+    steps): the compensated codes give a smaller output error on the
+    calibration tokens than the plain codes (the property that defines the
+    method; the oracle's float64 inverse at this size is too slow for a
+    test). Errors are measured by the oracle's rotation and unpacking."""
+    N, K, S, B = 256, 14336, 4096, 1024
+    W = si.weights(N, K, seed=99, sigma=0.015)
+    X = si.calibration_activations(S, K, seed=100)
+    say("gptq K=14336 output error")
+    Wt, Xt = to_dev(W), si.to_bf16(X).to(DEV)
+    H = q.qift_gptq_hessian(Xt, B)
+    cg, sg = q.qift_gptq_quantize_weights(Wt, H, B, "pot", torch.float16)
+    cp, sp = q.qift_quantize_weights(Wt, B, "pot", torch.float16)
+    sync()
+    wr = O.rotate(W.astype(np.float64), B)
+    xr = O.rotate(si.bf16_values(Xt), B)
+    errs = []
+    for codes, scales in ((cp, sp), (cg, sg)):
+        c = O.unpack_weights(dev_u32(codes), N, "pot")
+        deq = O._kind_levels("pot")[0][c] * scales.double().cpu().numpy()[:, None]
+        errs.append(float(np.sum(((wr - deq) @ xr.T) ** 2)))
+    say(f"  plain {errs[0]:.4g}, compensated {errs[1]:.4g}")
+    assert np.isfinite(errs[1]) and errs[1] < 0.5 * errs[0]
