@@ -115,8 +115,11 @@ __global__ __launch_bounds__(kGptqThreads) void gemm_f64_kernel(GemmArgs g) {
 #pragma unroll
     for (int j = 0; j < 2; ++j) acc[i][j] = v4d{0.0, 0.0, 0.0, 0.0};
 
-  for (int64_t k0 = 0; k0 < g.K; k0 += kGK) {
-    // tile loads, the contiguous dimension across neighbouring threads
+  // the stage's tiles go global -> registers -> LDS; the next stage's global
+  // loads are issued before the current stage's products, so their latency
+  // is hidden (the contiguous dimension across neighbouring threads)
+  double ra[4], rb[4];
+  auto gload = [&](int64_t k0) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       int mm, kk;
@@ -128,9 +131,7 @@ __global__ __launch_bounds__(kGptqThreads) void gemm_f64_kernel(GemmArgs g) {
         mm = (tid >> 4) + 16 * i;
       }
       const int64_t m = m0 + mm, k = k0 + kk;
-      double v = 0.0;
-      if (m < g.M && k < g.K) v = g.ta ? g.A[k * g.lda + m] : g.A[m * g.lda + k];
-      As[kk][mm] = v;
+      ra[i] = (m < g.M && k < g.K) ? (g.ta ? g.A[k * g.lda + m] : g.A[m * g.lda + k]) : 0.0;
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -143,11 +144,23 @@ __global__ __launch_bounds__(kGptqThreads) void gemm_f64_kernel(GemmArgs g) {
         kk = (tid >> 6) + 4 * i;
       }
       const int64_t n = n0 + nn, k = k0 + kk;
-      double v = 0.0;
-      if (n < g.N && k < g.K) v = g.tb ? g.B[n * g.ldb + k] : g.B[k * g.ldb + n];
-      Bs[kk][nn] = v;
+      rb[i] = (n < g.N && k < g.K) ? (g.tb ? g.B[n * g.ldb + k] : g.B[k * g.ldb + n]) : 0.0;
     }
+  };
+  auto lstore = [&]() {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if (g.ta) As[(tid >> 6) + 4 * i][tid & 63] = ra[i];
+      else As[tid & 15][(tid >> 4) + 16 * i] = ra[i];
+      if (g.tb) Bs[tid & 15][(tid >> 4) + 16 * i] = rb[i];
+      else Bs[(tid >> 6) + 4 * i][tid & 63] = rb[i];
+    }
+  };
+  if (g.K > 0) gload(0);
+  for (int64_t k0 = 0; k0 < g.K; k0 += kGK) {
+    lstore();
     __syncthreads();
+    if (k0 + kGK < g.K) gload(k0 + kGK);
 #pragma unroll
     for (int ks = 0; ks < kGK; ks += 4) {
       double a[2], b[2];
