@@ -303,13 +303,19 @@ __global__ __launch_bounds__(kGptqThreads) void potrf_diag_kernel(double* __rest
         }
       }
       __syncthreads();
+      // branch-free: every entry reads the column and selects 0 where the
+      // update does not apply (per-entry branches cost more than the FMAs)
+      double cq[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) cq[j] = col[par][cb + j];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const double lr = col[par][rb + i];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const int q = cb + j;
-          if (q > c && rb + i >= q) a[i][j] -= lr * col[par][q];
+          const double f = (q > c && rb + i >= q) ? cq[j] : 0.0;
+          a[i][j] = __builtin_fma(-lr, f, a[i][j]);
         }
       }
     }
