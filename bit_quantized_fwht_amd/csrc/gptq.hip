@@ -370,11 +370,9 @@ __global__ __launch_bounds__(kGptqThreads) void trsm_panel_kernel(double* __rest
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int q = cb + j;
-        if (q > c) {
-          const double l = L[q][c];
+        const double l = q > c ? L[q][c] : 0.0;  // branch-free
 #pragma unroll
-          for (int i = 0; i < 4; ++i) x[i][j] -= col[par][rb + i] * l;
-        }
+        for (int i = 0; i < 4; ++i) x[i][j] = __builtin_fma(-col[par][rb + i], l, x[i][j]);
       }
     }
   }
@@ -429,11 +427,9 @@ __global__ __launch_bounds__(kGptqThreads) void trsm_rows_kernel(const double* _
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int r = rb + i;
-        if (r > q) {
-          const double l = L[r][q];
+        const double l = r > q ? L[r][q] : 0.0;  // branch-free
 #pragma unroll
-          for (int j = 0; j < 4; ++j) y[i][j] -= l * row[par][cb + j];
-        }
+        for (int j = 0; j < 4; ++j) y[i][j] = __builtin_fma(-l, row[par][cb + j], y[i][j]);
       }
     }
   }
