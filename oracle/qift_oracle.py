@@ -165,17 +165,20 @@ def rotate(x: np.ndarray, B: int) -> np.ndarray:
 
 def quant_sym4(xr32: np.ndarray):
     """Per row: s = float32(absmax) / float32(7); q = clip(rint(x / s), -7, 7)
-    with float32 IEEE division and round half to even. A zero row gives s = 0
-    and q = 0. Returns (q int8 [R, K], s float32 [R])."""
+    with float32 IEEE division and round half to even. A row whose scale is 0
+    gets q = 0: an all-zero row, and also a row whose absmax is at most
+    3 * 2^-149, for which absmax / 7 rounds to 0 (the zero-scale rule is
+    about the scale, not only about all-zero input).
+    Returns (q int8 [R, K], s float32 [R])."""
     xr32 = np.asarray(xr32, dtype=np.float32)
     R, K = xr32.shape
     q = np.zeros((R, K), dtype=np.int8)
     s = np.zeros(R, dtype=np.float32)
     for r in range(R):
         a = np.float32(np.max(np.abs(xr32[r]))) if K > 0 else np.float32(0)
-        if a == 0:
-            continue
         sr = np.float32(a) / np.float32(7.0)
+        if sr == 0:
+            continue
         s[r] = sr
         q[r] = np.clip(np.rint(xr32[r] / sr), -7, 7).astype(np.int8)
     return q, s

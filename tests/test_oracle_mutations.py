@@ -66,6 +66,46 @@ def _wrong_divisor_quant(xr32):
     return q, s
 
 
+def _unclamped_quant(xr32):
+    xr32 = np.asarray(xr32, dtype=np.float32)
+    R, K = xr32.shape
+    q = np.zeros((R, K), dtype=np.int64)
+    s = np.zeros(R, dtype=np.float32)
+    for r in range(R):
+        sr = np.float32(np.max(np.abs(xr32[r]))) / np.float32(7)
+        if sr == 0:
+            continue
+        s[r] = sr
+        q[r] = np.rint(xr32[r] / sr)
+    return q, s
+
+
+def _zero_rule_on_absmax_quant(xr32):
+    xr32 = np.asarray(xr32, dtype=np.float32)
+    R, K = xr32.shape
+    q = np.zeros((R, K), dtype=np.int64)
+    s = np.zeros(R, dtype=np.float32)
+    for r in range(R):
+        a = np.float32(np.max(np.abs(xr32[r])))
+        if a == 0:
+            continue
+        s[r] = a / np.float32(7)
+        with np.errstate(divide="ignore", invalid="ignore"):
+            q[r] = np.nan_to_num(np.clip(np.rint(xr32[r] / s[r]), -7, 7))
+    return q, s
+
+
+def _int4_weight_round_half_up(wr32, s_stored):
+    w = wr32.astype(np.float32)
+    s = s_stored.astype(np.float32)
+    q = np.zeros(w.shape, dtype=np.int64)
+    for n in range(w.shape[0]):
+        if s[n] == 0:
+            continue
+        q[n] = np.clip(np.floor(w[n] / s[n] + np.float32(0.5)), -7, 7).astype(np.int64)
+    return q
+
+
 def _transposed_int_matmul(q, lv):
     a = np.asarray(q, dtype=np.float64) @ np.asarray(lv, dtype=np.float64)
     return np.rint(a).astype(np.int64)
@@ -205,6 +245,9 @@ MUTATIONS = {
     "rotate_strided_blocks": [("rotate", _strided_blocks_rotate)],
     "act_round_half_up": [("quant_sym4", _round_half_up_quant)],
     "act_divisor_8": [("quant_sym4", _wrong_divisor_quant)],
+    "act_no_clamp": [("quant_sym4", _unclamped_quant)],
+    "int4_weight_round_half_up": [("int4_weight_codes", _int4_weight_round_half_up)],
+    "act_zero_rule_on_absmax": [("quant_sym4", _zero_rule_on_absmax_quant)],
     "ties_to_outer": [("_PREFERENCE", {"mnz": (1, 2, 0, 3), "pot": (1, 3, 0, 2)})],
     "ties_to_negative": [("_PREFERENCE", {"mnz": (3, 0, 2, 1), "pot": (2, 0, 3, 1)})],
     "pot_shift_sign_swapped": [("LEVEL_KINDS", _kinds_with("pot", code_to_int=(1, -4, -1, 4)))],

@@ -154,6 +154,20 @@ def pin_zero_row():
     assert np.all(q == 0) and np.all(s == 0)
 
 
+def pin_act_subnormal_scale():
+    """Rows at the bottom of the float32 range (tests/golden/subnormal_act.json,
+    worked by hand): a subnormal scale rounded below absmax / 7 puts |x / s|
+    above 7.5, which the clamp brings back to +-7; a scale that rounds to 0
+    gives codes 0."""
+    g = golden("subnormal_act.json")
+    unit = np.float32(2.0 ** -149)
+    for case in g["rows"]:
+        x = np.array(case["units"], np.float32) * unit
+        q, s = O.quant_sym4(x[None])
+        assert s[0] == np.float32(case["scale_units"]) * unit
+        assert q[0].tolist() == case["codes"], case
+
+
 def pin_act_range_and_error():
     """Codes lie in [-7, 7], the absmax element maps to +-7 and the
     dequantized row is within s/2 of the rotated row everywhere."""
@@ -177,6 +191,10 @@ def test_rne_ties():
 
 def test_zero_row():
     pin_zero_row()
+
+
+def test_act_subnormal_scale():
+    pin_act_subnormal_scale()
 
 
 def test_act_range_and_error():
@@ -322,6 +340,18 @@ def pin_int4_weights():
         assert err.max() <= 0.5 * float(s[n]) * (1 + 1e-6)
 
 
+def pin_int4_weight_ties():
+    """Exact half-integer ties of w / s (tests/golden/int4_weight_ties.json,
+    worked by hand) round half to even, for float16 and float32 scales."""
+    g = golden("int4_weight_ties.json")
+    for case in g["rows"]:
+        w = np.array([case["row"]], np.float64)
+        for sdt in ("f16", "f32"):
+            codes, s, _ = O.quantize_weights(w, 1, "int4", sdt)
+            assert float(s[0]) == case["scale"]
+            assert codes[0].tolist() == case["codes"], (sdt, case)
+
+
 def test_level_sets_match_page():
     pin_level_sets_match_page()
 
@@ -352,6 +382,10 @@ def test_scale_rule():
 
 def test_int4_weights():
     pin_int4_weights()
+
+
+def test_int4_weight_ties():
+    pin_int4_weight_ties()
 
 
 # --------------------------------------------------------------------------
