@@ -390,27 +390,59 @@ def qift_rotate_quant_act_batched(items, stream=None):
     return outs
 
 
+_LINEAR_DTYPES = (("xq", (torch.uint8,)), ("s_a", (torch.float32,)), ("codes", (torch.int32,)),
+                  ("scales", (torch.float32, torch.float16)),
+                  ("Y", (torch.float32, torch.bfloat16, torch.int32)))
+
+
+def _check_linear_buffers(bufs, N, levels, scale_dtype=None, y_dtype=None, placement=True):
+    """The buffers of one linear (dict with xq, s_a, codes, scales, Y):
+    dtypes, and sizes against M, K (from xq [M, K/2]) and N, checked before
+    their placement; then (placement=True) each must be a contiguous GPU
+    tensor. scale_dtype and y_dtype, if given, are the dtypes the call was
+    set up for (a grouped plan fixes them for every linear). Returns (M, K)."""
+    for name, dts in _LINEAR_DTYPES:
+        t = bufs[name]
+        if not isinstance(t, torch.Tensor):
+            raise TypeError(f"{name} must be a torch.Tensor")
+        if t.dtype not in dts:
+            raise TypeError(f"{name} has dtype {t.dtype}, expected one of {dts}")
+    xq, s_a, codes, scales, Y = (bufs[k] for k, _ in _LINEAR_DTYPES)
+    if scale_dtype is not None and scales.dtype != scale_dtype:
+        raise TypeError(f"scales has dtype {scales.dtype}, the call is set up for {scale_dtype}")
+    if y_dtype is not None and Y.dtype != y_dtype:
+        raise TypeError(f"Y has dtype {Y.dtype}, the call is set up for {y_dtype}")
+    if xq.dim() != 2:
+        raise ValueError("xq must be [M, K/2]")
+    M, K = xq.shape[0], xq.shape[1] * 2
+    if N < 0:
+        raise ValueError("negative N")
+    if s_a.numel() < M:
+        raise ValueError(f"s_a has {s_a.numel()} elements, M = {M} needed")
+    if scales.numel() < N:
+        raise ValueError(f"scales has {scales.numel()} elements, N = {N} needed")
+    need = padded_channels(N) * code_words_per_row(K, levels)
+    if codes.numel() < need:
+        raise ValueError(f"codes has {codes.numel()} words, {need} needed for N = {N}, K = {K}")
+    if Y.numel() < M * N:
+        raise ValueError(f"Y has {Y.numel()} elements, M * N = {M * N} needed")
+    if placement:
+        for name, _ in _LINEAR_DTYPES:
+            _dev_tensor(bufs[name], name)
+    return M, K
+
+
 def qift_w2a4_linear(xq, s_a, codes, scales, levels="mnz", out_dtype=torch.float32, Y=None,
                      N=None, stream=None, table=None):
     """(xq [M, K/2], s_a [M], codes [N, ...], scales [N]) -> Y [M, N] in
     out_dtype (float32, bfloat16, or int32 for the raw accumulator).
     levels='lut' takes a level table (qift_w2a4_linear_ex)."""
-    _dev_tensor(xq, "xq", (torch.uint8,))
-    _dev_tensor(s_a, "s_a", (torch.float32,))
-    _dev_tensor(codes, "codes", (torch.int32,))
-    _dev_tensor(scales, "scales", (torch.float32, torch.float16))
-    M, K = xq.shape[0], xq.shape[1] * 2
     if N is None:
         N = scales.shape[0]
-    if codes.numel() < padded_channels(N) * code_words_per_row(K, levels) or scales.numel() < N:
-        raise ValueError("codes or scales buffer too small for N")
-    if s_a.numel() < M:
-        raise ValueError("s_a too small")
     if Y is None:
-        Y = torch.empty((M, N), dtype=out_dtype, device=xq.device)
-    _dev_tensor(Y, "Y", (torch.float32, torch.bfloat16, torch.int32))
-    if Y.numel() < M * N:
-        raise ValueError("Y too small for [M, N]")
+        _dev_tensor(xq, "xq", (torch.uint8,))
+        Y = torch.empty((xq.shape[0], N), dtype=out_dtype, device=xq.device)
+    M, K = _check_linear_buffers(dict(xq=xq, s_a=s_a, codes=codes, scales=scales, Y=Y), N, levels)
     st = _C.qift_w2a4_linear_ex(_ptr(xq), _ptr(s_a), M, K, _ptr(codes), _ptr(scales),
                                 _TORCH_TO_QIFT[scales.dtype], _levels(levels),
                                 _table_arg(levels, table), N, _ptr(Y), _TORCH_TO_QIFT[Y.dtype],
@@ -496,13 +528,23 @@ class LinearGroup:
         descs = (qift_linear_desc * max(n, 1))()
         self._keep = []
         device = None
+        # dtypes and sizes of every item first, then their placement
+        for placement in (False, True):
+            for i, it in enumerate(items):
+                try:
+                    _check_linear_buffers(it, it.get("N", it["scales"].shape[0]), it["levels"],
+                                          scale_dtype, y_dtype, placement)
+                except (TypeError, ValueError) as e:
+                    raise type(e)(f"item {i}: {e}") from None
+                if placement:
+                    device = device or it["xq"].device
+                    for key, _ in _LINEAR_DTYPES:
+                        if it[key].device != device:
+                            raise ValueError(f"item {i}: {key} is on {it[key].device}, "
+                                             f"the group on {device}")
         for i, it in enumerate(items):
-            xq, codes = it["xq"], it["codes"]
-            device = xq.device
-            M, K = xq.shape[0], xq.shape[1] * 2
             N = it.get("N", it["scales"].shape[0])
-            for key in ("xq", "s_a", "codes", "scales", "Y"):
-                _dev_tensor(it[key], key)
+            M, K = it["xq"].shape[0], it["xq"].shape[1] * 2
             tw = _table_arg(it["levels"], it.get("table"))  # the descriptor's int32 table word
             descs[i] = qift_linear_desc(it["xq"].data_ptr(), it["s_a"].data_ptr(),
                                         it["codes"].data_ptr(), it["scales"].data_ptr(),

@@ -34,13 +34,16 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 }
 
 // The 4-bit two's-complement code of clamp(rint(x / s), -7, 7), x / s the
-// IEEE float32 quotient, for |x| <= 7 s (so the clamp never binds), computed
+// IEEE float32 quotient, for |x| <= absmax and s = fl(absmax / 7), computed
 // as rint(x * r) with r = 1 / s except near a rounding tie:
 //  - for |x / s| <= 7.5, x * r is within 1.3e-6 of the correctly rounded
 //    quotient (two roundings of 2^-24 relative each), so when x * r is more
 //    than 1e-5 from a half-integer both round to the same integer;
 //  - within that window, or when x * r is not finite (1/s overflowing for a
-//    tiny s), the exact division decides;
+//    tiny s), the exact division decides, clamped: a subnormal s can be
+//    rounded far enough below absmax / 7 that |x / s| > 7.5 (the clamp cannot
+//    bind while 1/s is finite, since s > 2^-128 keeps that rounding below
+//    2^-22 relative);
 //  - rint uses the float adder: y + 1.5*2^23 rounds to nearest even and
 //    leaves rint(y) in the low mantissa bits in two's complement.
 // s == 0 gives code 0.
@@ -50,7 +53,8 @@ __device__ __forceinline__ uint32_t code_int4_recip(float x, float s, float r) {
   const float ym = y + kMagic;
   const float t = ym - kMagic;       // rint(y), exact
   uint32_t code = __float_as_uint(ym) & 0xFu;
-  if (!(fabsf(y - t) <= 0.49999f)) code = (uint32_t)(int)rintf(__fdiv_rn(x, s)) & 0xFu;
+  if (!(fabsf(y - t) <= 0.49999f))
+    code = (uint32_t)min(max((int)rintf(__fdiv_rn(x, s)), -7), 7) & 0xFu;
   return s == 0.f ? 0u : code;
 }
 

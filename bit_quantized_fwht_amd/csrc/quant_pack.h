@@ -45,12 +45,18 @@ __device__ __forceinline__ uint32_t int4x8_rint(const float y[8], float& dmax) {
   return (lo | hi) ^ 0x88888888u;
 }
 
-// the same codes from the exact IEEE division (s == 0 gives 0)
+// the same codes from the exact IEEE division, clamped to [-7, 7] (s == 0
+// gives 0). The clamp binds only when s = fl(absmax / 7) is subnormal: its
+// rounding can then make |x / s| exceed 7.5 (absmax = 8 * 2^-149 gives
+// s = 2^-149 and x / s = 8).
 __device__ __forceinline__ uint32_t int4x8_exact(const float x[8], float s) {
   uint32_t w = 0;
   if (s == 0.f) return 0u;
 #pragma unroll
-  for (int j = 0; j < 8; ++j) w |= ((uint32_t)(int)rintf(__fdiv_rn(x[j], s)) & 0xFu) << (4 * j);
+  for (int j = 0; j < 8; ++j) {
+    const int q = min(max((int)rintf(__fdiv_rn(x[j], s)), -7), 7);
+    w |= ((uint32_t)q & 0xFu) << (4 * j);
+  }
   return w;
 }
 

@@ -176,7 +176,10 @@ qift_status qift_quantize_weights_ex(const void* W, qift_dtype w_dtype, int64_t 
  * W2A4 inference, 4-bit activations): rotate each token along K in blocks of
  * had_block (float32 butterflies), then per token
  *   s_a = max_k |x'| / 7 (IEEE float32), q = clamp(rint(x' / s_a), -7, 7)
- * (round half to even, IEEE division); an all-zero token gives s_a = 0, q = 0.
+ * (round half to even, IEEE division; the clamp binds only when s_a is
+ * subnormal, whose rounding can put |x' / s_a| above 7.5). A token whose s_a
+ * is 0 gets q = 0: an all-zero token, or one whose max |x'| is at most
+ * 3 * 2^-149, so that max |x'| / 7 rounds to 0.
  *
  *   X      [M, K] float32 (QIFT_F32) or bfloat16 (QIFT_BF16)
  *   K      even, K <= QIFT_MAX_ROW; had_block | K

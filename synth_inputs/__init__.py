@@ -139,6 +139,22 @@ def uniform_int4(shape, seed: int, lo: int = -7, hi: int = 7) -> np.ndarray:
     return rng.integers(lo, hi + 1, size=shape, dtype=np.int64)
 
 
+def subnormal_rows(R: int, K: int, seed: int) -> np.ndarray:
+    """float32 [R, K] rows at the bottom of the float32 range: row r holds
+    integer multiples of 2^-149 (the smallest subnormal) drawn uniformly in
+    [-m, m], m = 1 + (r mod 64), with +-m placed at one seeded position, so
+    the rows' absmax values run over m * 2^-149 for m = 1..64."""
+    rng = np.random.default_rng(seed)
+    tiny = np.float32(2.0 ** -149)
+    X = np.zeros((R, K), np.float32)
+    for r in range(R):
+        m = 1 + r % 64
+        k = rng.integers(-m, m + 1, K)
+        k[rng.integers(0, K)] = m if rng.integers(0, 2) else -m
+        X[r] = k.astype(np.float32) * tiny
+    return X
+
+
 def positive_scales(n: int, seed: int, lo: float = 0.01, hi: float = 2.0) -> np.ndarray:
     """float32 [n] drawn uniformly in [lo, hi)."""
     rng = np.random.default_rng(seed)

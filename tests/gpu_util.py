@@ -80,3 +80,31 @@ def check_weight_codes(lv_gpu, lv_orc, w_rot64, s, kind, frac=1e-4, s_gpu=None):
     assert np.all(near[diff]), "weight code mismatch away from a threshold"
     assert n_bad <= max(1, frac * lv_orc.size), f"{n_bad} of {lv_orc.size} weight codes flipped"
     return n_bad
+
+
+# ---------------------------------------------------------------------------
+# guarded output buffers: sentinel bytes before and after every output
+# ---------------------------------------------------------------------------
+
+CANARY_ELEMS = 64
+CANARY_BYTE = 0xA7
+
+
+def guarded(shape, dtype, offset=0):
+    """An output tensor of ``shape`` placed ``offset`` elements into a device
+    buffer that has CANARY_ELEMS more elements after it; every byte of the
+    buffer starts as CANARY_BYTE. Returns (view, guard) for check_guard."""
+    n = int(np.prod(shape)) if len(shape) else 1
+    buf = torch.empty(offset + n + CANARY_ELEMS, dtype=dtype, device=DEV)
+    buf.view(torch.uint8).fill_(CANARY_BYTE)
+    return buf[offset:offset + n].view(shape), (buf, offset, n)
+
+
+def check_guard(guard, name="output"):
+    """The sentinel bytes before and after the output are untouched."""
+    buf, offset, n = guard
+    es = buf.element_size()
+    b = buf.view(torch.uint8).cpu().numpy()
+    head, tail = b[:offset * es], b[(offset + n) * es:]
+    assert np.all(head == CANARY_BYTE), f"{name}: write before the start of the buffer"
+    assert np.all(tail == CANARY_BYTE), f"{name}: write past the end ({np.count_nonzero(tail != CANARY_BYTE)} bytes)"

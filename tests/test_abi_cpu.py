@@ -406,3 +406,53 @@ def test_gptq_empty_is_noop_and_workspace_sizes():
     assert 8 * (2 * K * K + N * K) < b <= 8 * (2 * K * K + N * K) + N * K + 8 * 64 * N + K + 8 * 256
     assert q.qift_gptq_hessian_workspace_bytes(100, 256) == 100 * 256 * 8
     assert q.qift_gptq_hessian_workspace_bytes(10000, 256) == 4096 * 256 * 8
+
+
+def _group_item(**over):
+    """Buffers of one grouped linear (M = 2, K = 256, N = 40, MNZ) as CPU
+    tensors: the binding checks dtypes and sizes before the device, so each
+    mismatch below is reported without a GPU."""
+    import torch
+    it = dict(xq=torch.zeros((2, 128), dtype=torch.uint8), s_a=torch.ones(2),
+              codes=torch.zeros((48, 16), dtype=torch.int32),
+              scales=torch.ones(40, dtype=torch.float16),
+              Y=torch.zeros((2, 40), dtype=torch.bfloat16), levels="mnz", N=40)
+    it.update(over)
+    return it
+
+
+@pytest.mark.parametrize("over,exc,match", [
+    (dict(Y="float32"), TypeError, "Y has dtype torch.float32, the call is set up for torch.bfloat16"),
+    (dict(scales="float32"), TypeError, "scales has dtype torch.float32"),
+    (dict(Y=(2, 39)), ValueError, "Y has 78 elements"),
+    (dict(scales=(39,)), ValueError, "scales has 39 elements"),
+    (dict(codes=(32, 16)), ValueError, "codes has 512 words, 768 needed"),
+    (dict(s_a=(1,)), ValueError, "s_a has 1 elements"),
+    (dict(xq="int8"), TypeError, "xq has dtype torch.int8"),
+    (dict(levels="int4"), ValueError, "codes has 768 words, 1536 needed"),
+    (dict(), ValueError, "must be on a GPU device"),
+])
+def test_linear_group_rejects_mismatched_items(over, exc, match):
+    import torch
+    fixed = {}
+    base = _group_item()
+    for k, v in over.items():
+        if k == "levels":
+            fixed[k] = v
+        elif isinstance(v, str):
+            fixed[k] = torch.zeros(base[k].shape, dtype=getattr(torch, v))
+        else:
+            fixed[k] = torch.zeros(v, dtype=base[k].dtype)
+    items = [_group_item(), _group_item(**fixed)]
+    with pytest.raises(exc, match=match):
+        q.LinearGroup(items, scale_dtype=torch.float16, y_dtype=torch.bfloat16)
+    if over:  # the first item is valid: the error names the second
+        with pytest.raises(exc, match="item 1"):
+            q.LinearGroup(items, scale_dtype=torch.float16, y_dtype=torch.bfloat16)
+
+
+def test_single_linear_rejects_small_buffers():
+    import torch
+    it = _group_item(Y=torch.zeros((2, 39), dtype=torch.float32))
+    with pytest.raises(ValueError, match="Y has 78 elements"):
+        q.qift_w2a4_linear(it["xq"], it["s_a"], it["codes"], it["scales"], Y=it["Y"], N=40)

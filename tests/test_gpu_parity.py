@@ -16,7 +16,7 @@ import bit_quantized_fwht_amd as q
 from oracle import qift_oracle as O
 import synth_inputs as si
 from gpu_util import (DEV, say, to_dev, u32_to_dev, dev_u32, rel_l2, check_act_codes,
-                      check_weight_codes)
+                      check_weight_codes, guarded, check_guard)
 
 pytestmark = pytest.mark.gpu
 
@@ -32,8 +32,18 @@ def sync():
 # ---------------------------------------------------------------------------
 
 def gpu_rotate(X_t, B, want=True):
-    xq, s_a, xr = q.qift_rotate_quant_act(X_t, B, want_x_rot=want)
+    """The rotation through the C ABI into guarded outputs (sentinel bytes
+    after xq, s_a and x_rot must stay untouched)."""
+    M, K = X_t.shape
+    xq, gq = guarded((M, K // 2), torch.uint8)
+    s_a, gs = guarded((M,), torch.float32)
+    xr, gx = guarded((M, K), torch.float32) if want else (None, None)
+    q.qift_rotate_quant_act(X_t, B, xq=xq, s_a=s_a, x_rot=xr)
     sync()
+    check_guard(gq, "xq")
+    check_guard(gs, "s_a")
+    if want:
+        check_guard(gx, "x_rot")
     return O.unpack_int4(xq.cpu().numpy()), s_a.cpu().numpy(), (xr.cpu().numpy() if want else None)
 
 
@@ -185,8 +195,13 @@ def test_rotate_one_hot_closed_form():
 # ---------------------------------------------------------------------------
 
 def gpu_quant_weights(W_t, B, kind, sdt):
-    codes, scales = q.qift_quantize_weights(W_t, B, kind, SCALE_T[sdt])
+    N, K = W_t.shape
+    codes, gc = guarded((q.padded_channels(N), q.code_words_per_row(K, kind)), torch.int32)
+    scales, gsc = guarded((N,), SCALE_T[sdt])
+    q.qift_quantize_weights(W_t, B, kind, SCALE_T[sdt], codes=codes, scales=scales)
     sync()
+    check_guard(gc, "codes")
+    check_guard(gsc, "scales")
     words = dev_u32(codes)
     c = O.unpack_weights(words, W_t.shape[0], kind)
     return c, scales.float().cpu().numpy(), words
@@ -247,11 +262,15 @@ def random_linear_inputs(M, K, N, kind, seed):
 
 
 def run_linear(qa, codes, s_a, s_w, kind, out_dtype):
+    """The linear through the C ABI into a guarded Y (sentinel bytes after
+    it must stay untouched)."""
     xq = torch.from_numpy(O.pack_int4(qa)).to(DEV)
     cw = u32_to_dev(O.pack_weights(codes, kind))
-    Y = q.qift_w2a4_linear(xq, to_dev(s_a), cw, to_dev(s_w.astype(np.float32), torch.float16),
-                           kind, out_dtype)
+    Y, gy = guarded((qa.shape[0], codes.shape[0]), out_dtype)
+    q.qift_w2a4_linear(xq, to_dev(s_a), cw, to_dev(s_w.astype(np.float32), torch.float16),
+                       kind, out_dtype, Y=Y)
     sync()
+    check_guard(gy, "Y")
     return Y
 
 
@@ -374,8 +393,12 @@ def test_kv4_matches_oracle(D, B):
     KV = si.kv(T, H, D, seed=D + B)
     KVt = si.to_bf16(KV).to(DEV)
     say(f"kv4 T={T} H={H} D={D} B={B}")
-    kvq, sc = q.qift_kv4_quant(KVt, B)
+    kvq, gk = guarded((T, H, D // 2), torch.uint8)
+    sc, gsc = guarded((T, H), torch.float32)
+    q.qift_kv4_quant(KVt, B, kvq=kvq, scales=sc)
     sync()
+    check_guard(gk, "kvq")
+    check_guard(gsc, "scales")
     qo, so, xr = O.kv4_quant(si.bf16_values(KVt), B)
     qg = O.unpack_int4(kvq.cpu().numpy())
     sg = sc.cpu().numpy()
@@ -428,9 +451,11 @@ TABLES = [(-2, -1, 0, 1), (3, 10, -3, -10), (15, -15, 1, -1)]
 def run_linear_lut(qa, codes, s_a, s_w, table, out_dtype):
     xq = torch.from_numpy(O.pack_int4(qa)).to(DEV)
     cw = u32_to_dev(O.pack_weights(codes, "lut"))
-    Y = q.qift_w2a4_linear(xq, to_dev(s_a), cw, to_dev(s_w.astype(np.float32), torch.float16),
-                           "lut", out_dtype, table=table)
+    Y, gy = guarded((qa.shape[0], codes.shape[0]), out_dtype)
+    q.qift_w2a4_linear(xq, to_dev(s_a), cw, to_dev(s_w.astype(np.float32), torch.float16),
+                       "lut", out_dtype, Y=Y, table=table)
     sync()
+    check_guard(gy, "Y")
     return Y
 
 

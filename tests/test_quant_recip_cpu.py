@@ -1,24 +1,34 @@
 """Host check of the argument behind the GPU's reciprocal shortcut for
 symmetric int4 quantization: the code of rint(x * (1/s)), rounded by adding
-1.5 * 2^23 in float32, with an exact division only within 1e-5 of a
-half-integer (or for non-finite products), equals the code of
-clamp(rint(x / s), -7, 7) with the IEEE float32 quotient, for s = absmax / 7
-and |x| <= absmax. Emulated in numpy float32 (IEEE)."""
+1.5 * 2^23 in float32, with an exact division (clamped to [-7, 7]) only
+within 1e-5 of a half-integer (or for non-finite products), equals the code
+of clamp(rint(x / s), -7, 7) with the IEEE float32 quotient, for
+s = absmax / 7 and |x| <= absmax. Emulated in numpy float32 (IEEE, with
+subnormals)."""
 import numpy as np
 
+from oracle import qift_oracle as O
 
 MAGIC = np.float32(12582912.0)  # 1.5 * 2^23
+TINY = np.float32(2.0 ** -149)  # the smallest positive subnormal float32
 
 
-def shortcut(x, s):
-    with np.errstate(over="ignore", invalid="ignore"):
+def shortcut(x, s, clamp_exact=True):
+    """The kernel's code decision (code_int4_recip / int4x8_rint with the
+    int4x8_exact fallback), emulated in float32."""
+    if s == 0:  # the kernels take r = 0 (every product 0) and code 0
+        return np.zeros(np.shape(x), np.int64)
+    with np.errstate(over="ignore", invalid="ignore", divide="ignore"):
         r = np.float32(1) / s
         y = (x * r).astype(np.float32)
         ym = (y + MAGIC).astype(np.float32)
         t = (ym - MAGIC).astype(np.float32)
         code = ym.view(np.uint32).astype(np.int64) & 0xF
         exact = ~(np.abs(y - t) <= np.float32(0.49999))
-        code_div = np.rint(x / s).astype(np.int64) & 0xF
+        q_div = np.rint(x / s).astype(np.int64)
+        if clamp_exact:
+            q_div = np.clip(q_div, -7, 7)
+        code_div = q_div & 0xF
     return np.where(exact, code_div, code)
 
 
@@ -36,3 +46,44 @@ def test_reciprocal_shortcut_matches_ieee_division():
         assert np.array_equal(shortcut(x, s), ref)
         total += x.size
     assert total > 5_000_000
+
+
+def subnormal_rows(seed=0):
+    """Rows whose absmax is m * 2^-149 for m = 1..64 (every value an integer
+    multiple of 2^-149, the largest +-m), plus rows at the top of the
+    subnormal range and just above it."""
+    rng = np.random.default_rng(seed)
+    rows = []
+    for m in range(1, 65):
+        k = rng.integers(-m, m + 1, 64)
+        k[rng.integers(0, 64)] = m if m % 2 else -m
+        rows.append(k.astype(np.float32) * TINY)
+    for a in (np.float32(2.0 ** -127), np.float32(2.0 ** -126), np.float32(2.0 ** -124)):
+        rows.append((rng.uniform(-1, 1, 64).astype(np.float32) * a).astype(np.float32))
+        rows[-1][0] = a
+    return np.stack(rows)
+
+
+def test_subnormal_scales_clamp_to_seven():
+    """With absmax = m * 2^-149, s = fl(absmax / 7) is subnormal and its
+    rounding can put |x / s| above 7.5 (m = 8: s = 2^-149, x / s = 8); the
+    oracle clamps to 7, and so must the kernel's exact-division fallback."""
+    X = subnormal_rows()
+    q_o, s_o = O.quant_sym4(X)
+    clamp_bound = 0
+    for r in range(X.shape[0]):
+        s = np.float32(np.max(np.abs(X[r]))) / np.float32(7)
+        assert s == s_o[r]
+        got = shortcut(X[r], s)
+        assert np.array_equal(got, q_o[r].astype(np.int64) & 0xF), r
+        with np.errstate(divide="ignore", invalid="ignore"):
+            clamp_bound += int(np.any(np.abs(np.rint(X[r] / s)) > 7))
+    # the rows do reach the clamp, and without it the codes would differ
+    assert clamp_bound >= 5
+    unclamped = np.stack([shortcut(X[r], np.float32(np.max(np.abs(X[r]))) / np.float32(7),
+                                   clamp_exact=False) for r in range(X.shape[0])])
+    assert not np.array_equal(unclamped, q_o.astype(np.int64) & 0xF)
+    # absmax 8 * 2^-149: the oracle gives +-7 where an unclamped 8 would read as -8
+    row8 = np.array([8, -8, 7, 1], np.float32) * TINY
+    q8, s8 = O.quant_sym4(row8[None])
+    assert s8[0] == TINY and q8[0].tolist() == [7, -7, 7, 1]
