@@ -73,8 +73,11 @@ qift_status check_had_block(int64_t B, int64_t K, int64_t max_b) {
   return QIFT_OK;
 }
 
-// Shared rules of qift_w2a4_linear and of each grouped descriptor.
-qift_status check_linear(const qift_linear_desc& d, qift_dtype scale_dtype, qift_dtype y_dtype) {
+// Shared rules of qift_w2a4_linear and of each grouped descriptor. With
+// dtypes_known = false (sizing a grouped plan, before its dtypes are given)
+// the dtype-dependent checks of scales and Y are left to the later call.
+qift_status check_linear(const qift_linear_desc& d, qift_dtype scale_dtype, qift_dtype y_dtype,
+                         bool dtypes_known = true) {
   if (d.M < 0 || d.N < 0) return fail(QIFT_ERR_INVALID_ARG, "negative M or N");
   if (d.K <= 0 || d.K % 64 != 0)
     return fail(QIFT_ERR_INVALID_ARG, "K=%lld must be a positive multiple of 64", (long long)d.K);
@@ -83,9 +86,9 @@ qift_status check_linear(const qift_linear_desc& d, qift_dtype scale_dtype, qift
   if (!valid_levels(d.levels)) return fail(QIFT_ERR_INVALID_ARG, "invalid levels %d", d.levels);
   qift_status tst = check_table(d.levels, (uint32_t)d.reserved);
   if (tst != QIFT_OK) return tst;
-  if (scale_dtype != QIFT_F32 && scale_dtype != QIFT_F16)
+  if (dtypes_known && scale_dtype != QIFT_F32 && scale_dtype != QIFT_F16)
     return fail(QIFT_ERR_INVALID_ARG, "scale_dtype must be F32 or F16");
-  if (y_dtype != QIFT_F32 && y_dtype != QIFT_BF16 && y_dtype != QIFT_I32)
+  if (dtypes_known && y_dtype != QIFT_F32 && y_dtype != QIFT_BF16 && y_dtype != QIFT_I32)
     return fail(QIFT_ERR_INVALID_ARG, "y_dtype must be F32, BF16 or I32");
   if (d.M == 0 || d.N == 0) return QIFT_OK;
   if (!d.xq || !d.s_a || !d.codes || !d.scales || !d.Y)
@@ -93,7 +96,8 @@ qift_status check_linear(const qift_linear_desc& d, qift_dtype scale_dtype, qift
   if (!aligned(d.xq, 16) || !aligned(d.codes, 16))
     return fail(QIFT_ERR_ALIGNMENT, "xq and codes must be 16-byte aligned");
   if (!aligned(d.s_a, 4)) return fail(QIFT_ERR_ALIGNMENT, "s_a must be 4-byte aligned");
-  if (!aligned(d.scales, scale_dtype == QIFT_F16 ? 2 : 4) || !aligned(d.Y, y_dtype == QIFT_BF16 ? 2 : 4))
+  if (dtypes_known && (!aligned(d.scales, scale_dtype == QIFT_F16 ? 2 : 4) ||
+                       !aligned(d.Y, y_dtype == QIFT_BF16 ? 2 : 4)))
     return fail(QIFT_ERR_ALIGNMENT, "scales or Y misaligned for its dtype");
   if ((d.N + qift::kDecodeRowsPerTile - 1) / qift::kDecodeRowsPerTile > kMaxGrid)
     return fail(QIFT_ERR_UNSUPPORTED, "N too large");
@@ -434,13 +438,14 @@ qift_status qift_gptq_quantize_weights(const void* W, qift_dtype w_dtype, int64_
 // --- grouped linear ------------------------------------------------------------
 
 static qift_status check_group(const qift_linear_desc* descs, int32_t count, qift_dtype scale_dtype,
-                               qift_dtype y_dtype, int64_t* total_tiles) {
+                               qift_dtype y_dtype, int64_t* total_tiles,
+                               bool dtypes_known = true) {
   if (count < 0) return fail(QIFT_ERR_INVALID_ARG, "negative count");
   if (count > 0 && !descs) return fail(QIFT_ERR_INVALID_ARG, "null descriptor array");
   int64_t tiles = 0;
   for (int32_t i = 0; i < count; ++i) {
     const qift_linear_desc& d = descs[i];
-    qift_status st = check_linear(d, scale_dtype, y_dtype);
+    qift_status st = check_linear(d, scale_dtype, y_dtype, dtypes_known);
     if (st != QIFT_OK) {
       g_last_error = "descriptor " + std::to_string(i) + ": " + g_last_error;
       return st;
@@ -462,7 +467,8 @@ qift_status qift_linear_group_workspace_bytes(const qift_linear_desc* descs, int
                                               size_t* bytes) {
   if (!bytes) return fail(QIFT_ERR_INVALID_ARG, "null bytes");
   int64_t tiles = 0;
-  qift_status st = check_group(descs, count, QIFT_F32, QIFT_F32, &tiles);
+  // the plan's size does not depend on the dtypes, which prepare checks
+  qift_status st = check_group(descs, count, QIFT_F32, QIFT_F32, &tiles, false);
   if (st != QIFT_OK) return st;
   *bytes = plan_bytes(count, tiles);
   return ok();

@@ -370,7 +370,9 @@ qift_status qift_gptq_quantize_weights(const void* W, qift_dtype w_dtype, int64_
  * call with M <= 16; levels may differ between descriptors.
  *
  * 1. qift_linear_group_workspace_bytes(descs, count, &bytes) gives the size
- *    of the device workspace the plan needs.
+ *    of the device workspace the plan needs (it checks each descriptor by
+ *    the rules that do not depend on the scale and output dtypes; prepare
+ *    checks those too).
  * 2. qift_linear_group_prepare validates every descriptor (same rules as
  *    qift_w2a4_linear), builds the plan on the host and copies it into
  *    `workspace` (device memory, 256-byte aligned, caller-owned) on `stream`,

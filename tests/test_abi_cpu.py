@@ -307,6 +307,12 @@ def test_group_workspace_and_rejects():
     assert "descriptor 1" in q.last_error()
     bad = (q.qift_linear_desc * 1)(make_desc(reserved=1))
     assert q._C.qift_linear_group_workspace_bytes(bad, 1, ctypes.byref(nbytes)) == q.QIFT_ERR_INVALID_ARG
+    # a 2-byte-aligned output suits a bfloat16 plan: sizing accepts it,
+    # prepare checks it against the plan's dtype
+    odd = (q.qift_linear_desc * 1)(make_desc(Y=0x50002))
+    assert q._C.qift_linear_group_workspace_bytes(odd, 1, ctypes.byref(nbytes)) == q.QIFT_OK
+    assert q._C.qift_linear_group_prepare(odd, 1, q.QIFT_F16, q.QIFT_F32, V(0x100000), 1 << 20,
+                                          ctypes.byref(ctypes.c_int64(0)), None) == q.QIFT_ERR_ALIGNMENT
     bad = (q.qift_linear_desc * 1)(make_desc(codes=0x30008))
     assert q._C.qift_linear_group_workspace_bytes(bad, 1, ctypes.byref(nbytes)) == q.QIFT_ERR_ALIGNMENT
     tiles_out = ctypes.c_int64(0)
