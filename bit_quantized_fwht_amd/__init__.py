@@ -25,6 +25,7 @@ LEVELS = {"mnz": 0, "pot": 1, "int4": 2, "lut": 3}
 SCALE_RULES = {"absmax": 0, "mse": 1}
 QIFT_MAX_ROW = 16384
 QIFT_MAX_HAD_BLOCK = 4096
+QIFT_ATTENTION_SCRATCH_BYTES = 16 * 1024 * 1024
 
 _TORCH_TO_QIFT = {torch.float32: QIFT_F32, torch.bfloat16: QIFT_BF16,
                   torch.float16: QIFT_F16, torch.int32: QIFT_I32}
@@ -79,6 +80,8 @@ def _load():
         "qift_kv4_attention_workspace_bytes": [i64, i64, i64, i64, ctypes.POINTER(ctypes.c_size_t)],
         "qift_kv4_attention_decode": [vp, c_st, i64, i64, i64, i64, i32, vp, vp, vp, vp,
                                       ctypes.c_float, vp, c_st, vp, ctypes.c_size_t, vp],
+        "qift_kv4_attention_decode_noalloc": [vp, c_st, i64, i64, i64, i64, i32, vp, vp, vp, vp,
+                                              ctypes.c_float, vp, c_st, vp],
         "qift_gptq_hessian_workspace_bytes": [i64, i64, ctypes.POINTER(ctypes.c_size_t)],
         "qift_gptq_hessian": [vp, c_st, i64, i64, i32, i32, vp, vp, ctypes.c_size_t, vp],
         "qift_gptq_workspace_bytes": [i64, i64, ctypes.POINTER(ctypes.c_size_t)],
@@ -510,6 +513,36 @@ def qift_kv4_attention_decode(q, kq, ks, vq, vs, had_block: int, softmax_scale=N
     return out
 
 
+def qift_kv4_attention_decode_noalloc(q, kq, ks, vq, vs, had_block: int, out,
+                                      softmax_scale=None, stream=None):
+    """qift_kv4_attention_decode without a workspace: the partial results go
+    to the library's fixed per-GPU array (QIFT_ATTENTION_SCRATCH_BYTES), and
+    nothing is allocated, here either: ``out`` [S, H, D] (or [H, D]) float32 /
+    bfloat16 must be given. Calls that overlap on one GPU race."""
+    _dev_tensor(q, "q", (torch.float32, torch.bfloat16))
+    single = q.dim() == 2
+    S = 1 if single else q.shape[0]
+    H, D = q.shape[-2], q.shape[-1]
+    T = kq.shape[-3]
+    for name, t_, dt in (("kq", kq, torch.uint8), ("vq", vq, torch.uint8), ("ks", ks, torch.float32),
+                         ("vs", vs, torch.float32)):
+        _dev_tensor(t_, name, (dt,))
+    if kq.numel() < S * T * H * (D // 2) or vq.numel() < S * T * H * (D // 2) or \
+            ks.numel() < S * T * H or vs.numel() < S * T * H:
+        raise ValueError("cache buffers too small for [S, T, H, D]")
+    _dev_tensor(out, "out", (torch.float32, torch.bfloat16))
+    if out.numel() < S * H * D:
+        raise ValueError("out too small")
+    if softmax_scale is None:
+        softmax_scale = 1.0 / float(D) ** 0.5
+    st = _C.qift_kv4_attention_decode_noalloc(_ptr(q), _TORCH_TO_QIFT[q.dtype], S, T, H, D,
+                                              had_block, _ptr(kq), _ptr(ks), _ptr(vq), _ptr(vs),
+                                              float(softmax_scale), _ptr(out),
+                                              _TORCH_TO_QIFT[out.dtype], _stream(stream, q.device))
+    _check(st, "qift_kv4_attention_decode_noalloc")
+    return out
+
+
 # ---------------------------------------------------------------------------
 # grouped linear
 # ---------------------------------------------------------------------------
@@ -575,5 +608,6 @@ __all__ = ["load_library", "QiftUnavailable", "qift_quantize_weights", "qift_rot
            "LinearGroup", "QiftError", "qift_linear_desc", "LEVELS", "status_string", "last_error",
            "abi_version", "code_words_per_row", "padded_channels", "LIB_PATH", "SCALE_RULES",
            "level_table_word", "qift_kv4_attention_decode", "qift_kv4_attention_workspace_bytes",
+           "qift_kv4_attention_decode_noalloc", "QIFT_ATTENTION_SCRATCH_BYTES",
            "qift_gptq_hessian", "qift_gptq_hessian_workspace_bytes", "qift_gptq_quantize_weights",
            "qift_gptq_workspace_bytes"]

@@ -307,12 +307,13 @@ qift_status qift_kv4_attention_workspace_bytes(int64_t S, int64_t T, int64_t H, 
   return ok();
 }
 
-qift_status qift_kv4_attention_decode(const void* q, qift_dtype q_dtype, int64_t S, int64_t T,
-                                      int64_t H, int64_t D, int32_t had_block,
-                                      const uint8_t* kq, const float* ks, const uint8_t* vq,
-                                      const float* vs, float softmax_scale, void* out,
-                                      qift_dtype out_dtype, void* workspace,
-                                      size_t workspace_bytes, qift_stream stream) {
+// Rules shared by both decode-attention entry points (everything except the
+// buffer of partial results).
+static qift_status check_attention_call(const void* q, qift_dtype q_dtype, int64_t S, int64_t T,
+                                        int64_t H, int64_t D, int32_t had_block,
+                                        const uint8_t* kq, const float* ks, const uint8_t* vq,
+                                        const float* vs, float softmax_scale, const void* out,
+                                        qift_dtype out_dtype) {
   if (q_dtype != QIFT_F32 && q_dtype != QIFT_BF16)
     return fail(QIFT_ERR_INVALID_ARG, "q_dtype must be F32 or BF16");
   if (out_dtype != QIFT_F32 && out_dtype != QIFT_BF16)
@@ -323,14 +324,28 @@ qift_status qift_kv4_attention_decode(const void* q, qift_dtype q_dtype, int64_t
   if (st != QIFT_OK) return st;
   if (!(softmax_scale == softmax_scale) || softmax_scale > 3.4e38f || softmax_scale < -3.4e38f)
     return fail(QIFT_ERR_INVALID_ARG, "softmax_scale must be finite");
-  if (S == 0) return ok();
-  if (!q || !kq || !ks || !vq || !vs || !out || !workspace)
-    return fail(QIFT_ERR_INVALID_ARG, "null buffer");
-  if (!aligned(kq, 16) || !aligned(vq, 16) || !aligned(workspace, 256))
-    return fail(QIFT_ERR_ALIGNMENT, "kq and vq must be 16-byte aligned, workspace 256-byte");
+  if (S == 0) return QIFT_OK;
+  if (!q || !kq || !ks || !vq || !vs || !out) return fail(QIFT_ERR_INVALID_ARG, "null buffer");
+  if (!aligned(kq, 16) || !aligned(vq, 16))
+    return fail(QIFT_ERR_ALIGNMENT, "kq and vq must be 16-byte aligned");
   if (!aligned(q, q_dtype == QIFT_F32 ? 4 : 2) || !aligned(out, out_dtype == QIFT_F32 ? 4 : 2) ||
       !aligned(ks, 4) || !aligned(vs, 4))
     return fail(QIFT_ERR_ALIGNMENT, "q, out, ks or vs misaligned for its dtype");
+  return QIFT_OK;
+}
+
+qift_status qift_kv4_attention_decode(const void* q, qift_dtype q_dtype, int64_t S, int64_t T,
+                                      int64_t H, int64_t D, int32_t had_block,
+                                      const uint8_t* kq, const float* ks, const uint8_t* vq,
+                                      const float* vs, float softmax_scale, void* out,
+                                      qift_dtype out_dtype, void* workspace,
+                                      size_t workspace_bytes, qift_stream stream) {
+  qift_status st = check_attention_call(q, q_dtype, S, T, H, D, had_block, kq, ks, vq, vs,
+                                        softmax_scale, out, out_dtype);
+  if (st != QIFT_OK) return st;
+  if (S == 0) return ok();
+  if (!workspace) return fail(QIFT_ERR_INVALID_ARG, "null workspace");
+  if (!aligned(workspace, 256)) return fail(QIFT_ERR_ALIGNMENT, "workspace must be 256-byte aligned");
   const size_t need = qift::kv4_attn_workspace_bytes(S, T, (int)H);
   if (workspace_bytes < need)
     return fail(QIFT_ERR_INVALID_ARG, "workspace of %zu bytes, %zu needed", workspace_bytes, need);
@@ -340,6 +355,32 @@ qift_status qift_kv4_attention_decode(const void* q, qift_dtype q_dtype, int64_t
                                                reinterpret_cast<float*>(workspace),
                                                reinterpret_cast<hipStream_t>(stream)),
                     "qift_kv4_attention_decode launch");
+}
+
+qift_status qift_kv4_attention_decode_noalloc(const void* q, qift_dtype q_dtype, int64_t S,
+                                              int64_t T, int64_t H, int64_t D, int32_t had_block,
+                                              const uint8_t* kq, const float* ks,
+                                              const uint8_t* vq, const float* vs,
+                                              float softmax_scale, void* out,
+                                              qift_dtype out_dtype, qift_stream stream) {
+  qift_status st = check_attention_call(q, q_dtype, S, T, H, D, had_block, kq, ks, vq, vs,
+                                        softmax_scale, out, out_dtype);
+  if (st != QIFT_OK) return st;
+  if (S == 0) return ok();
+  const size_t need = qift::kv4_attn_workspace_bytes(S, T, (int)H);
+  if (need > (size_t)QIFT_ATTENTION_SCRATCH_BYTES)
+    return fail(QIFT_ERR_UNSUPPORTED,
+                "partial results of %zu bytes exceed the fixed array of %zu bytes "
+                "(use qift_kv4_attention_decode with a workspace)",
+                need, (size_t)QIFT_ATTENTION_SCRATCH_BYTES);
+  float* part = nullptr;
+  hipError_t e = qift::kv4_attn_scratch(&part);
+  if (e != hipSuccess) return hip_result(e, "qift_kv4_attention_decode_noalloc: scratch address");
+  return hip_result(qift::launch_kv4_attention(q, q_dtype == QIFT_BF16, S, T, (int)H, had_block,
+                                               kq, ks, vq, vs, softmax_scale, out,
+                                               out_dtype == QIFT_BF16, part,
+                                               reinterpret_cast<hipStream_t>(stream)),
+                    "qift_kv4_attention_decode_noalloc launch");
 }
 
 // --- error-compensated weight quantization ----------------------------------------

@@ -21,6 +21,8 @@
 // partial results stay small (1/32 of the cache bytes there). Kernel 2 merges
 // the runs of each (sequence, head) with independent loads, divides by l and
 // rotates back.
+#include <mutex>
+
 #include "lane_butterfly.h"
 
 namespace qift {
@@ -331,6 +333,39 @@ static int ilog2_attn(int v) {
   int r = 0;
   while ((1 << r) < v) ++r;
   return r;
+}
+
+// ---------------------------------------------------------------------------
+// partial results of the allocation-free entry point
+// ---------------------------------------------------------------------------
+
+// One fixed array per GPU, held from the first use of this code object on
+// that GPU until the process ends. Every entry the combine kernel reads is
+// written by the partial kernel of the same call, so nothing needs clearing
+// between calls. In host code `scratch` names a host-side stand-in, not the
+// device array: kernels receive the address kv4_attn_scratch returns.
+static __device__ __align__(256) float scratch[QIFT_ATTENTION_SCRATCH_BYTES / sizeof(float)];
+
+constexpr int kScratchMaxDevices = 64;
+
+// The address of the current device's copy of `scratch`, looked up once per
+// device (with that device current) and kept.
+hipError_t kv4_attn_scratch(float** ptr) {
+  static std::mutex mu;
+  static float* addr[kScratchMaxDevices] = {};
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kScratchMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    addr[dev] = static_cast<float*>(p);
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
 }
 
 hipError_t launch_kv4_attention(const void* q, int q_bf16, int64_t S, int64_t T, int H,

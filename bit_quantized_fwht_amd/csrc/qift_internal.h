@@ -218,6 +218,7 @@ hipError_t launch_kv4(const void* KV, int bf16, int64_t rows, int D, int had_blo
                       float* scales, hipStream_t s);
 int64_t kv4_attn_tokens_per_run(int64_t S, int64_t T, int H);
 size_t kv4_attn_workspace_bytes(int64_t S, int64_t T, int H);
+hipError_t kv4_attn_scratch(float** ptr);
 size_t gptq_hessian_workspace_bytes(int64_t S, int64_t K);
 hipError_t launch_gptq_hessian(const void* X, int x_bf16, int64_t S, int64_t K, int had_block,
                                int accumulate, double* H, void* workspace, hipStream_t s);

@@ -14,7 +14,8 @@
  * --------------------------------
  * - Every buffer argument is a DEVICE pointer owned by the caller. The library
  *   allocates no device memory and keeps no state (the plan of a grouped
- *   launch lives in a caller-owned workspace); it is safe to call from several
+ *   launch lives in a caller-owned workspace), except the fixed per-GPU array
+ *   of qift_kv4_attention_decode_noalloc; it is safe to call from several
  *   host threads.
  * - Calls are asynchronous: they validate, enqueue on `stream` and return.
  *   Outputs are valid in stream order. `stream` is a hipStream_t passed as
@@ -85,7 +86,7 @@
 extern "C" {
 #endif
 
-#define QIFT_ABI_VERSION 4
+#define QIFT_ABI_VERSION 5
 
 typedef enum {
   QIFT_OK = 0,
@@ -309,6 +310,31 @@ qift_status qift_kv4_attention_decode(const void* q, qift_dtype q_dtype, int64_t
                                       const float* vs, float softmax_scale, void* out,
                                       qift_dtype out_dtype, void* workspace,
                                       size_t workspace_bytes, qift_stream stream);
+
+/*
+ * qift_kv4_attention_decode_noalloc -- qift_kv4_attention_decode for callers
+ * that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation): no workspace argument,
+ * and the call allocates nothing. Its partial results go to a fixed array of
+ * QIFT_ATTENTION_SCRATCH_BYTES in device memory, one per GPU, which the
+ * library holds from its first use on that GPU until the process ends; the
+ * array used is the current device's (the device of `stream` and of every
+ * buffer must be current). A call whose partial results need more
+ * (qift_kv4_attention_workspace_bytes above QIFT_ATTENTION_SCRATCH_BYTES,
+ * e.g. S * H beyond about 32000 (sequence, head) pairs) returns
+ * QIFT_ERR_UNSUPPORTED without launching. Every call on one GPU shares that
+ * GPU's array: calls ordered on one stream are safe, calls that overlap on
+ * one GPU (other streams, or host threads without ordering) race and give
+ * undefined results. Arguments, limits, results and errors otherwise as
+ * qift_kv4_attention_decode, whose kernels it runs.
+ */
+#define QIFT_ATTENTION_SCRATCH_BYTES (16u * 1024u * 1024u)
+qift_status qift_kv4_attention_decode_noalloc(const void* q, qift_dtype q_dtype, int64_t S,
+                                              int64_t T, int64_t H, int64_t D, int32_t had_block,
+                                              const uint8_t* kq, const float* ks,
+                                              const uint8_t* vq, const float* vs,
+                                              float softmax_scale, void* out,
+                                              qift_dtype out_dtype, qift_stream stream);
 
 /*
  * Error-compensated weight quantization with the fixed levels (GPTQ's

@@ -32,10 +32,10 @@ def test_library_loads_and_exports_every_declared_symbol():
     lib = q.load_library()
     names = declared_functions()
     assert "qift_w2a4_linear" in names and "qift_kv4_quant" in names
-    assert len(names) == 19, names
+    assert len(names) == 20, names
     for n in names:
         assert hasattr(lib, n), n
-    assert q.abi_version() == 4
+    assert q.abi_version() == 5
     for s in range(5):
         assert q.status_string(s).startswith("QIFT_")
 
@@ -462,3 +462,43 @@ def test_single_linear_rejects_small_buffers():
     it = _group_item(Y=torch.zeros((2, 39), dtype=torch.float32))
     with pytest.raises(ValueError, match="Y has 78 elements"):
         q.qift_w2a4_linear(it["xq"], it["s_a"], it["codes"], it["scales"], Y=it["Y"], N=40)
+
+
+def attn_noalloc(**kw):
+    a = dict(q=A16, qd=q.QIFT_F32, S=1, T=64, H=4, D=128, B=128, kq=A16b, ks=A16c, vq=A16d,
+             vs=A16e, scale=0.1, out=V(0x60000), od=q.QIFT_F32)
+    a.update(kw)
+    return q._C.qift_kv4_attention_decode_noalloc(a["q"], a["qd"], a["S"], a["T"], a["H"], a["D"],
+                                                  a["B"], a["kq"], a["ks"], a["vq"], a["vs"],
+                                                  a["scale"], a["out"], a["od"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(S=4096, T=4096, H=64), q.QIFT_ERR_UNSUPPORTED),  # partials above the fixed array
+    (dict(D=64), q.QIFT_ERR_UNSUPPORTED),
+    (dict(kq=None), q.QIFT_ERR_INVALID_ARG),
+    (dict(out=None), q.QIFT_ERR_INVALID_ARG),
+    (dict(vq=V(0x40008)), q.QIFT_ERR_ALIGNMENT),
+    (dict(B=3), q.QIFT_ERR_INVALID_ARG),
+    (dict(scale=float("inf")), q.QIFT_ERR_INVALID_ARG),
+])
+def test_kv4_attention_noalloc_rejects(kw, status):
+    """Rejected before any device call (the size limit included)."""
+    assert attn_noalloc(**kw) == status
+    assert q.last_error() != ""
+
+
+def test_kv4_attention_noalloc_limit_matches_workspace_rule():
+    """The largest partial-result size the fixed array takes is the one the
+    workspace entry point would ask for; S = 0 is a no-op."""
+    import ctypes as ct
+    n = ct.c_size_t(0)
+    limit = q.QIFT_ATTENTION_SCRATCH_BYTES
+    for S, T, H in ((1, 4096, 32), (8, 4096, 32), (64, 4096, 64), (500, 128, 64), (600, 128, 64)):
+        assert q._C.qift_kv4_attention_workspace_bytes(S, T, H, 128, ct.byref(n)) == q.QIFT_OK
+        st = attn_noalloc(S=S, T=T, H=H)
+        if n.value > limit:
+            assert st == q.QIFT_ERR_UNSUPPORTED and "exceed" in q.last_error()
+        else:
+            assert st != q.QIFT_ERR_UNSUPPORTED  # fits (the launch itself needs a GPU)
+    assert attn_noalloc(S=0, q=None, kq=None, out=None) == q.QIFT_OK
