@@ -130,8 +130,40 @@ def unit_gptq(q, torch, dev, steps):
         q.qift_gptq_quantize_weights(W, H, 4096, "mnz", torch.float16, workspace=ws)
 
 
+def unit_decode_layer_by_layer(q, torch, dev, steps):
+    """The 32-layer dependent decode at M = 1 (per layer: qkv, o, gate+up,
+    down, each a rotation call then a linear call) replayed from one HIP
+    graph, steps times."""
+    items, _ = layer_by_layer_items(q, torch, dev, 1)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for it in items:
+            q.qift_rotate_quant_act(it["X"], it["B"], xq=it["xq"], s_a=it["sa"])
+            q.qift_w2a4_linear(it["xq"], it["sa"], it["cw"], it["sw"], "mnz", Y=it["Y"])
+    for _ in range(steps):
+        g.replay()
+
+
+def unit_decode_single_4096(q, torch, dev, steps):
+    """One 4096 x 4096 MNZ linear at M = 1 (bf16 output), steps eager calls,
+    each on one of 64 weight copies (268 MB, past the last-level cache)."""
+    import synth_inputs as si
+    ws = []
+    for i in range(64):
+        W = si.device_weights(4096, 4096, seed=900 + i, sigma=0.02, device=dev)
+        ws.append(q.qift_quantize_weights(W, 4096, "mnz", torch.float16))
+        del W
+    X = si.device_activations(1, 4096, seed=901, device=dev)
+    xq, sa, _ = q.qift_rotate_quant_act(X, 4096)
+    Y = torch.empty((1, 4096), dtype=torch.bfloat16, device=dev)
+    for i in range(steps):
+        cw, sw = ws[i % 64]
+        q.qift_w2a4_linear(xq, sa, cw, sw, "mnz", Y=Y)
+
+
 UNITS = {"prefill_up_proj": unit_prefill_up_proj, "kv4": unit_kv4, "attention": unit_attention,
-         "gptq": unit_gptq}
+         "gptq": unit_gptq, "decode_layer_by_layer": unit_decode_layer_by_layer,
+         "decode_single_4096": unit_decode_single_4096}
 
 
 def log(*a):
@@ -707,19 +739,17 @@ def gptq_bench(q, torch, dev):
             "w2a4_rel_l2_output_error": errs}
 
 
-def layer_by_layer_decode(q, torch, dev, M=1):
-    """A dependent, layer-by-layer decode of the LLaMA-7B-shaped stack: per
-    layer four linears with the q/k/v and the gate/up weights concatenated
-    along N (qkv 4096 -> 12288, o 4096 -> 4096, gate+up 4096 -> 22016, down
-    11008 -> 4096), each input rotated and quantized first; 32 layers with
-    their own weights and inputs, replayed from one HIP graph: a rotation
-    call and a linear call per input."""
+LAYER_BY_LAYER_SHAPES = [("qkv", 4096, 12288, 4096), ("o", 4096, 4096, 4096),
+                         ("gate_up", 4096, 22016, 4096), ("down", 11008, 4096, 256)]
+
+
+def layer_by_layer_items(q, torch, dev, M):
+    """Weights, inputs and outputs of the 32-layer dependent decode (see
+    layer_by_layer_decode). Returns (items, weight bytes)."""
     import synth_inputs as si
-    shapes = [("qkv", 4096, 12288, 4096), ("o", 4096, 4096, 4096),
-              ("gate_up", 4096, 22016, 4096), ("down", 11008, 4096, 256)]
     items, nbytes = [], 0
     for li in range(si.N_LAYERS):
-        for j, (name, K, N, B) in enumerate(shapes):
+        for j, (name, K, N, B) in enumerate(LAYER_BY_LAYER_SHAPES):
             W = si.device_weights(N, K, seed=5000 + 10 * li + j, sigma=0.02, device=dev)
             cw, sw = q.qift_quantize_weights(W, B, "mnz", torch.float16)
             del W
@@ -730,6 +760,18 @@ def layer_by_layer_decode(q, torch, dev, M=1):
                               Y=torch.empty((M, N), dtype=torch.bfloat16, device=dev)))
             nbytes += cw.numel() * 4 + sw.numel() * 2
     torch.cuda.synchronize()
+    return items, nbytes
+
+
+def layer_by_layer_decode(q, torch, dev, M=1):
+    """A dependent, layer-by-layer decode of the LLaMA-7B-shaped stack: per
+    layer four linears with the q/k/v and the gate/up weights concatenated
+    along N (qkv 4096 -> 12288, o 4096 -> 4096, gate+up 4096 -> 22016, down
+    11008 -> 4096), each input rotated and quantized first; 32 layers with
+    their own weights and inputs, replayed from one HIP graph: a rotation
+    call and a linear call per input."""
+    import synth_inputs as si
+    items, nbytes = layer_by_layer_items(q, torch, dev, M)
 
     def separate():
         for it in items:

@@ -72,6 +72,8 @@ def _load():
         "qift_rotate_quant_act": [vp, c_st, i64, i64, i32, vp, vp, vp, vp],
         "qift_w2a4_linear": [vp, vp, i64, i64, vp, vp, c_st, c_st, i64, vp, c_st, vp],
         "qift_kv4_quant": [vp, c_st, i64, i64, i64, i32, vp, vp, vp],
+        "qift_rotate_w2a4_linear": [vp, c_st, i64, i64, i32, vp, vp, vp, vp, c_st, c_st,
+                                    ctypes.c_uint32, i64, vp, c_st, vp],
         "qift_linear_group_workspace_bytes": [vp, i32, ctypes.POINTER(ctypes.c_size_t)],
         "qift_linear_group_prepare": [vp, i32, c_st, c_st, vp, ctypes.c_size_t,
                                       ctypes.POINTER(ctypes.c_int64), vp],
@@ -454,6 +456,37 @@ def qift_w2a4_linear(xq, s_a, codes, scales, levels="mnz", out_dtype=torch.float
     return Y
 
 
+def qift_rotate_w2a4_linear(X, had_block: int, codes, scales, levels="mnz",
+                            out_dtype=torch.float32, Y=None, N=None, xq=None, s_a=None,
+                            stream=None, table=None):
+    """X [M, K] float32/bfloat16 -> (Y [M, N], xq [M, K/2], s_a [M]): the
+    rotation + int4 quantization of X and the linear in one call (one launch
+    for a single token row), with the results of qift_rotate_quant_act
+    followed by qift_w2a4_linear."""
+    _dev_tensor(X, "X", (torch.float32, torch.bfloat16))
+    M, K = X.shape
+    if N is None:
+        N = scales.shape[0]
+    if xq is None:
+        xq = torch.empty((M, K // 2), dtype=torch.uint8, device=X.device)
+    if s_a is None:
+        s_a = torch.empty((M,), dtype=torch.float32, device=X.device)
+    if Y is None:
+        Y = torch.empty((M, N), dtype=out_dtype, device=X.device)
+    _check_rotate_buffers(M, K, xq, s_a, None)
+    if xq.numel() != M * (K // 2):
+        raise ValueError("xq must hold exactly [M, K/2] (it is also the linear's input)")
+    _check_linear_buffers(dict(xq=xq.view(M, K // 2), s_a=s_a, codes=codes, scales=scales, Y=Y),
+                          N, levels)
+    st = _C.qift_rotate_w2a4_linear(_ptr(X), _TORCH_TO_QIFT[X.dtype], M, K, had_block, _ptr(xq),
+                                    _ptr(s_a), _ptr(codes), _ptr(scales),
+                                    _TORCH_TO_QIFT[scales.dtype], _levels(levels),
+                                    _table_arg(levels, table), N, _ptr(Y), _TORCH_TO_QIFT[Y.dtype],
+                                    _stream(stream, X.device))
+    _check(st, "qift_rotate_w2a4_linear")
+    return Y, xq, s_a
+
+
 def qift_kv4_quant(KV, had_block: int, kvq=None, scales=None, stream=None):
     """KV [T, H, D] bfloat16/float32 -> (kvq uint8 [T, H, D/2], scales float32 [T, H])."""
     _dev_tensor(KV, "KV", (torch.float32, torch.bfloat16))
@@ -609,5 +642,6 @@ __all__ = ["load_library", "QiftUnavailable", "qift_quantize_weights", "qift_rot
            "abi_version", "code_words_per_row", "padded_channels", "LIB_PATH", "SCALE_RULES",
            "level_table_word", "qift_kv4_attention_decode", "qift_kv4_attention_workspace_bytes",
            "qift_kv4_attention_decode_noalloc", "QIFT_ATTENTION_SCRATCH_BYTES",
+           "qift_rotate_w2a4_linear",
            "qift_gptq_hessian", "qift_gptq_hessian_workspace_bytes", "qift_gptq_quantize_weights",
            "qift_gptq_workspace_bytes"]

@@ -267,6 +267,45 @@ qift_status qift_w2a4_linear_ex(const uint8_t* xq, const float* s_a, int64_t M, 
   return hip_result(qift::launch_linear_prefill(d, sf16, y_dtype, s), "qift_w2a4_linear prefill launch");
 }
 
+qift_status qift_rotate_w2a4_linear(const void* X, qift_dtype x_dtype, int64_t M, int64_t K,
+                                    int32_t had_block, uint8_t* xq, float* s_a,
+                                    const uint32_t* codes, const void* scales,
+                                    qift_dtype scale_dtype, qift_levels levels,
+                                    uint32_t level_table, int64_t N, void* Y, qift_dtype y_dtype,
+                                    qift_stream stream) {
+  qift_status st = check_rotate(X, x_dtype, M, K, had_block, xq, s_a, nullptr);
+  if (st != QIFT_OK) return st;
+  qift_linear_desc d{};
+  d.reserved = (int32_t)level_table;
+  d.xq = xq;
+  d.s_a = s_a;
+  d.codes = codes;
+  d.scales = scales;
+  d.Y = Y;
+  d.M = M;
+  d.K = K;
+  d.N = N;
+  d.levels = (int32_t)levels;
+  st = check_linear(d, scale_dtype, y_dtype);
+  if (st != QIFT_OK) return st;
+  if (M == 0) return ok();
+  if ((M + 127) / 128 > 65535) return fail(QIFT_ERR_UNSUPPORTED, "M too large");
+  const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const int sf16 = scale_dtype == QIFT_F16;
+  // one token row on the fast rotation path: one fused launch
+  if (M == 1 && N > 0 && qift::rotate_fast_ok(X, K, had_block, xq, nullptr))
+    return hip_result(qift::launch_rotate_linear_decode(d, X, x_dtype == QIFT_BF16, had_block, sf16,
+                                                        y_dtype, s),
+                      "qift_rotate_w2a4_linear fused launch");
+  hipError_t e = qift::launch_rotate_quant_act(X, x_dtype == QIFT_BF16, M, K, had_block, xq, s_a,
+                                               nullptr, s);
+  if (e != hipSuccess) return hip_result(e, "qift_rotate_w2a4_linear rotation launch");
+  if (N == 0) return ok();
+  if (M <= 16)
+    return hip_result(qift::launch_linear_decode(d, sf16, y_dtype, s), "qift_rotate_w2a4_linear decode launch");
+  return hip_result(qift::launch_linear_prefill(d, sf16, y_dtype, s), "qift_rotate_w2a4_linear prefill launch");
+}
+
 qift_status qift_kv4_quant(const void* KV, qift_dtype dtype, int64_t T, int64_t H, int64_t D,
                            int32_t had_block, uint8_t* kvq, float* scales, qift_stream stream) {
   if (dtype != QIFT_F32 && dtype != QIFT_BF16)

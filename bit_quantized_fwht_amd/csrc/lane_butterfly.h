@@ -81,4 +81,21 @@ __device__ __forceinline__ float quad_xor(float x) {
   return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), kCtrl, 0xF, 0xF, true));
 }
 
+// Largest of the 64 lanes' values, returned to every lane, for non-negative
+// floats (whose bit patterns order like the values, so the max is exact):
+// DPP steps within each 16-lane row (quad permutes, half-row and row
+// mirrors), row broadcasts across rows (lane 15 into the next row, lane 31
+// into the upper two), then lane 63 read back. Replaces six shuffle rounds
+// through the LDS crossbar.
+__device__ __forceinline__ float wave_max_nonneg(float x) {
+  int v = __float_as_int(x);
+  v = max(v, __builtin_amdgcn_update_dpp(v, v, 0xB1, 0xF, 0xF, false));   // quad_perm [1,0,3,2]
+  v = max(v, __builtin_amdgcn_update_dpp(v, v, 0x4E, 0xF, 0xF, false));   // quad_perm [2,3,0,1]
+  v = max(v, __builtin_amdgcn_update_dpp(v, v, 0x141, 0xF, 0xF, false));  // row_half_mirror
+  v = max(v, __builtin_amdgcn_update_dpp(v, v, 0x140, 0xF, 0xF, false));  // row_mirror
+  v = max(v, __builtin_amdgcn_update_dpp(v, v, 0x142, 0xA, 0xF, false));  // row_bcast:15
+  v = max(v, __builtin_amdgcn_update_dpp(v, v, 0x143, 0xC, 0xF, false));  // row_bcast:31
+  return __int_as_float(__builtin_amdgcn_readlane(v, 63));
+}
+
 }  // namespace qift

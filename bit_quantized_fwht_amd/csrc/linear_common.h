@@ -45,14 +45,18 @@ __device__ __forceinline__ v4i weight_operand(const uint4& c, int step, OpConsts
 
 // activation operand for MFMA step `step` of a lane segment: 2-bit segments
 // carry 64 features = 32 bytes (a0, a1), int4-weight segments 32 features =
-// 16 bytes (a0 only).
-__device__ __forceinline__ v4i act_operand(const uint4& a0, const uint4& a1, int step) {
-  switch (step) {
-    case 0: return int4_operand(a0.x, a0.y);
-    case 1: return int4_operand(a0.z, a0.w);
-    case 2: return int4_operand(a1.x, a1.y);
-    default: return int4_operand(a1.z, a1.w);
-  }
+// 16 bytes (a0 only). am is the nibble mask: 0xF0F0F0F0 keeps the codes, 0
+// zeroes the operand (a segment past K, whose loads read a clamped address).
+__device__ __forceinline__ v4i act_operand(const uint4& a0, const uint4& a1, int step,
+                                           uint32_t am) {
+  const uint32_t x0 = step == 0 ? a0.x : step == 1 ? a0.z : step == 2 ? a1.x : a1.z;
+  const uint32_t x1 = step == 0 ? a0.y : step == 1 ? a0.w : step == 2 ? a1.y : a1.w;
+  v4i a;
+  a[0] = (int)((x0 << 4) & am);
+  a[1] = (int)(x0 & am);
+  a[2] = (int)((x1 << 4) & am);
+  a[3] = (int)(x1 & am);
+  return a;
 }
 
 __device__ __forceinline__ void store_y(void* Y, int y_dtype, int64_t idx, int acc, float scale) {
@@ -65,8 +69,18 @@ __device__ __forceinline__ void store_y(void* Y, int y_dtype, int64_t idx, int a
   }
 }
 
+// 16- and 8-byte stores through a global pointer (see as_global)
+typedef unsigned int v2u __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ void st16(void* p, uint32_t a, uint32_t b, uint32_t c, uint32_t e) {
+  *as_global_out(reinterpret_cast<v4u*>(p)) = v4u{a, b, c, e};
+}
+__device__ __forceinline__ void st8(void* p, uint32_t a, uint32_t b) {
+  *as_global_out(reinterpret_cast<v2u*>(p)) = v2u{a, b};
+}
+
 __device__ __forceinline__ uint4 ld16(const void* p) {
-  return *reinterpret_cast<const uint4*>(p);
+  const v4u v = *as_global(reinterpret_cast<const v4u*>(p));
+  return uint4{v[0], v[1], v[2], v[3]};
 }
 
 }  // namespace qift

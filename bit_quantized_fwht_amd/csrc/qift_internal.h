@@ -15,8 +15,36 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 typedef unsigned int v4u __attribute__((ext_vector_type(4)));
 
 // ---------------------------------------------------------------------------
+// workgroup barrier for LDS exchanges
+// ---------------------------------------------------------------------------
+
+// A workgroup barrier that orders LDS accesses only. __syncthreads() also
+// orders global memory, which on gfx9 means waiting for every outstanding
+// global load (one counter covers loads and stores): a barrier inside a
+// kernel that keeps a weight stream in flight would drain that stream.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// ---------------------------------------------------------------------------
 // element loads / stores
 // ---------------------------------------------------------------------------
+
+// A pointer the kernels know to point into device global memory. A pointer
+// read from memory (the descriptors of a grouped plan) is otherwise generic:
+// its accesses become flat instructions, which count against the LDS counter
+// as well, so a wait for any of them waits for every outstanding load, store
+// and LDS access.
+template <typename T>
+__device__ __forceinline__ const __attribute__((address_space(1))) T* as_global(const T* p) {
+  return (const __attribute__((address_space(1))) T*)p;
+}
+template <typename T>
+__device__ __forceinline__ __attribute__((address_space(1))) T* as_global_out(T* p) {
+  return (__attribute__((address_space(1))) T*)p;
+}
 
 __device__ __forceinline__ float bf16_bits_to_float(uint16_t b) {
   return __uint_as_float(((uint32_t)b) << 16);
@@ -61,6 +89,19 @@ __device__ __forceinline__ uint32_t code_int4_recip(float x, float s, float r) {
 __device__ __forceinline__ float load_scale(const void* p, int64_t i, int is_f16) {
   if (is_f16) return __half2float(reinterpret_cast<const __half*>(p)[i]);
   return reinterpret_cast<const float*>(p)[i];
+}
+
+// The same value without a branch on the dtype: two 16-bit loads (element i
+// of a float16 array twice, or the two halves of element i of a float32
+// array), both always issued. A load under a branch makes the compiler wait
+// for it where the branch ends, which serializes loads meant to overlap.
+__device__ __forceinline__ float load_scale_nb(const void* p, int64_t i, int is_f16) {
+  const auto h = as_global(reinterpret_cast<const uint16_t*>(p));
+  const int64_t j = is_f16 ? i : 2 * i;
+  const uint32_t lo = h[j];
+  const uint32_t hi = h[is_f16 ? j : j + 1];
+  const float f16v = __half2float(__ushort_as_half((unsigned short)lo));
+  return is_f16 ? f16v : __uint_as_float(lo | (hi << 16));
 }
 
 // ---------------------------------------------------------------------------
@@ -235,6 +276,8 @@ hipError_t launch_linear_decode(const qift_linear_desc& d, int scale_f16, int y_
                                 hipStream_t s);
 hipError_t launch_linear_prefill(const qift_linear_desc& d, int scale_f16, int y_dtype,
                                  hipStream_t s);
+hipError_t launch_rotate_linear_decode(const qift_linear_desc& d, const void* X, int x_bf16,
+                                       int had_block, int scale_f16, int y_dtype, hipStream_t s);
 hipError_t launch_linear_grouped(const void* workspace, int64_t total_tiles, int scale_f16,
                                  int y_dtype, hipStream_t s);
 

@@ -25,15 +25,15 @@ constexpr int kRowThreads = 256;
 
 __device__ __forceinline__ int pad16(int e) { return e + (e >> 4); }
 
-// kMax: also raise m to the largest |value| the pass writes
-template <int NS, bool kMax = false>
+// kMax: also raise m to the largest |value| the pass writes; NT threads
+template <int NS, bool kMax = false, int NT = kRowThreads>
 __device__ __forceinline__ void fwht_pass_padded(float* row, int K, int p, int tid,
                                                  float* m = nullptr) {
   constexpr int R = 1 << NS;
   const int sh = 4 * p;
   const int S = 1 << sh;
   const int groups = K >> NS;
-  for (int grp = tid; grp < groups; grp += kRowThreads) {
+  for (int grp = tid; grp < groups; grp += NT) {
     const int low = grp & (S - 1);
     const int high = grp >> sh;
     const int base = (high << (sh + NS)) | low;
@@ -61,14 +61,35 @@ __device__ __forceinline__ void fwht_pass_padded(float* row, int K, int p, int t
   }
 }
 
+// 16 consecutive elements as raw words (bfloat16: 8 words of two, float32: 16
+// words); widen16 turns them into floats. Keeping the two apart lets a caller
+// issue other loads between them without the compiler waiting for these.
 template <typename T>
-__device__ __forceinline__ void load16(const T* __restrict__ src, float v[16]);
+__device__ __forceinline__ void load16_raw(const T* __restrict__ src, uint32_t w[16]);
 
 template <>
-__device__ __forceinline__ void load16<uint16_t>(const uint16_t* __restrict__ src, float v[16]) {
+__device__ __forceinline__ void load16_raw<uint16_t>(const uint16_t* __restrict__ src,
+                                                     uint32_t w[16]) {
   const uint4 a = reinterpret_cast<const uint4*>(src)[0];
   const uint4 b = reinterpret_cast<const uint4*>(src)[1];
-  const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+  w[0] = a.x; w[1] = a.y; w[2] = a.z; w[3] = a.w;
+  w[4] = b.x; w[5] = b.y; w[6] = b.z; w[7] = b.w;
+}
+
+template <>
+__device__ __forceinline__ void load16_raw<float>(const float* __restrict__ src, uint32_t w[16]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint4 f = reinterpret_cast<const uint4*>(src)[i];
+    w[4 * i] = f.x; w[4 * i + 1] = f.y; w[4 * i + 2] = f.z; w[4 * i + 3] = f.w;
+  }
+}
+
+template <typename T>
+__device__ __forceinline__ void widen16(const uint32_t w[16], float v[16]);
+
+template <>
+__device__ __forceinline__ void widen16<uint16_t>(const uint32_t w[16], float v[16]) {
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     v[2 * i] = __uint_as_float(w[i] << 16);
@@ -77,21 +98,17 @@ __device__ __forceinline__ void load16<uint16_t>(const uint16_t* __restrict__ sr
 }
 
 template <>
-__device__ __forceinline__ void load16<float>(const float* __restrict__ src, float v[16]) {
+__device__ __forceinline__ void widen16<float>(const uint32_t w[16], float v[16]) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const float4 f = reinterpret_cast<const float4*>(src)[i];
-    v[4 * i] = f.x;
-    v[4 * i + 1] = f.y;
-    v[4 * i + 2] = f.z;
-    v[4 * i + 3] = f.w;
-  }
+  for (int i = 0; i < 16; ++i) v[i] = __uint_as_float(w[i]);
 }
 
-// One row on the fast path. A thread owns the groups tid, tid + 256, ... of
-// 16 consecutive elements (at most kFastMaxGroups of them, K <= 16384); all
-// of its global loads are issued before any group is transformed, so a long
-// row costs one memory latency rather than one per group.
+// One row on the fast path, by a workgroup of NT threads (256 for the
+// rotation kernels; 512 or 1024 inside a fused decode linear). A thread owns
+// the groups tid, tid + NT, ... of 16 consecutive elements (at most
+// kFastMaxGroups of them, K <= 16384); all of its global loads are issued
+// before any group is transformed, so a long row costs one memory latency
+// rather than one per group.
 //  - stages 0..3 (strides 1..8) inside a group, in registers;
 //  - stages 4..7 (strides 16..128 = groups 1..8 apart = lanes 1..8 apart)
 //    between lanes with DPP (lane_butterfly8; values kept up to a per-lane
@@ -106,29 +123,47 @@ static_assert(kFastMaxGroups * 16 * kRowThreads >= QIFT_MAX_ROW, "fast path cove
 // rows with log2(block) <= kRegLog2B need no LDS row buffer
 constexpr int kRegLog2B = 8;
 
-template <typename T>
-__device__ __forceinline__ void rotate_row_fast(const T* __restrict__ src, int K, int log2b,
-                                                float norm, uint8_t* __restrict__ xq_row,
-                                                float* __restrict__ s_out,
-                                                float* __restrict__ xrot_row, float* row,
-                                                float* red) {
+// groups of 16 elements a thread holds for a workgroup of NT threads
+template <int NT>
+struct RowGroups {
+  static constexpr int kQ = (kFastMaxGroups * kRowThreads + NT - 1) / NT;
+};
+
+// 1. loads (a group past the row end reads group 0 and is discarded), as raw
+// words; rotate_row_finish widens and transforms them
+template <typename T, int NT>
+__device__ __forceinline__ void rotate_row_load(const T* __restrict__ src, int K,
+                                                uint32_t raw[RowGroups<NT>::kQ][16]) {
+  const int tid = threadIdx.x;
+  const int groups = K >> 4;
+#pragma unroll
+  for (int q = 0; q < RowGroups<NT>::kQ; ++q) {
+    const int grp = tid + q * NT;
+    load16_raw<T>(src + 16 * (grp < groups ? grp : 0), raw[q]);
+  }
+}
+
+template <typename T, int NT>
+__device__ __forceinline__ void rotate_row_finish(const uint32_t raw[RowGroups<NT>::kQ][16],
+                                                  int K, int log2b, float norm,
+                                                  uint8_t* __restrict__ xq_row,
+                                                  float* __restrict__ s_out,
+                                                  float* __restrict__ xrot_row, float* row,
+                                                  float* red) {
+  constexpr int kQ = RowGroups<NT>::kQ;  // groups per thread
+  float v[kQ][16];
+#pragma unroll
+  for (int q = 0; q < kQ; ++q) widen16<T>(raw[q], v[q]);
   const bool in_regs = log2b <= kRegLog2B;
   const int tid = threadIdx.x;
   const int groups = K >> 4;
   const int wave_g0 = tid & ~63;  // the wave's first group (q = 0)
-  // 1. loads (a group past the row end reads group 0 and is discarded)
-  float v[kFastMaxGroups][16];
-#pragma unroll
-  for (int q = 0; q < kFastMaxGroups; ++q) {
-    const int grp = tid + q * kRowThreads;
-    load16<T>(src + 16 * (grp < groups ? grp : 0), v[q]);
-  }
   // 2. stages 0..3 in registers (rounds with no group of this wave skipped;
   //    a partner group of a valid group is always valid, since K is a
   //    multiple of the block)
 #pragma unroll
-  for (int q = 0; q < kFastMaxGroups; ++q) {
-    if (wave_g0 + q * kRowThreads < groups) {
+  for (int q = 0; q < kQ; ++q) {
+    if (wave_g0 + q * NT < groups) {
 #pragma unroll
       for (int st = 0; st < 4; ++st) {
         const int h = 1 << st;
@@ -149,8 +184,8 @@ __device__ __forceinline__ void rotate_row_fast(const T* __restrict__ src, int K
 #define QIFT_LANE_STAGE(H)                                                 \
   {                                                                        \
     const float c = (tid & (H)) ? -1.f : 1.f;                              \
-    _Pragma("unroll") for (int q = 0; q < kFastMaxGroups; ++q) {           \
-      if (wave_g0 + q * kRowThreads < groups) {                            \
+    _Pragma("unroll") for (int q = 0; q < kQ; ++q) {           \
+      if (wave_g0 + q * NT < groups) {                            \
         lane_butterfly8<H>(v[q], c);                                       \
         lane_butterfly8<H>(v[q] + 8, c);                                   \
       }                                                                    \
@@ -165,8 +200,8 @@ __device__ __forceinline__ void rotate_row_fast(const T* __restrict__ src, int K
   float mloc = 0.f;  // largest |value| of the row's last stage seen by this thread
   if (in_regs) {
 #pragma unroll
-    for (int q = 0; q < kFastMaxGroups; ++q) {
-      if (tid + q * kRowThreads < groups) {
+    for (int q = 0; q < kQ; ++q) {
+      if (tid + q * NT < groups) {
 #pragma unroll
         for (int j = 0; j < 16; ++j) mloc = fmaxf(mloc, fabsf(v[q][j]));
       }
@@ -174,31 +209,30 @@ __device__ __forceinline__ void rotate_row_fast(const T* __restrict__ src, int K
   } else {
     // 4. stages 8.. in one pass through the padded LDS row
 #pragma unroll
-    for (int q = 0; q < kFastMaxGroups; ++q) {
-      const int grp = tid + q * kRowThreads;
+    for (int q = 0; q < kQ; ++q) {
+      const int grp = tid + q * NT;
       if (grp < groups) {
         float* dst = row + 17 * grp;
 #pragma unroll
         for (int j = 0; j < 16; ++j) dst[j] = sigma * v[q][j];
       }
     }
-    __syncthreads();
+    lds_barrier();
     switch (log2b - 8) {
-      case 1: fwht_pass_padded<1, true>(row, K, 2, tid, &mloc); break;
-      case 2: fwht_pass_padded<2, true>(row, K, 2, tid, &mloc); break;
-      case 3: fwht_pass_padded<3, true>(row, K, 2, tid, &mloc); break;
-      default: fwht_pass_padded<4, true>(row, K, 2, tid, &mloc); break;
+      case 1: fwht_pass_padded<1, true, NT>(row, K, 2, tid, &mloc); break;
+      case 2: fwht_pass_padded<2, true, NT>(row, K, 2, tid, &mloc); break;
+      case 3: fwht_pass_padded<3, true, NT>(row, K, 2, tid, &mloc); break;
+      default: fwht_pass_padded<4, true, NT>(row, K, 2, tid, &mloc); break;
     }
   }
   // 5. row absmax (for the LDS path the barrier also completes the pass)
   mloc *= norm;  // rounding is monotonic: max(|v|)*norm == max(|v*norm|)
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) mloc = fmaxf(mloc, __shfl_xor(mloc, off, 64));
+  mloc = wave_max_nonneg(mloc);
   if ((tid & 63) == 0) red[tid >> 6] = mloc;
-  __syncthreads();
+  lds_barrier();
   float amax = red[0];
 #pragma unroll
-  for (int w = 1; w < kRowThreads / 64; ++w) amax = fmaxf(amax, red[w]);
+  for (int w = 1; w < NT / 64; ++w) amax = fmaxf(amax, red[w]);
   const float s = __fdiv_rn(amax, 7.0f);
   const float rs = s != 0.f ? __fdiv_rn(1.0f, s) : 0.f;
   const bool fast = rint_path_ok(rs);
@@ -211,8 +245,8 @@ __device__ __forceinline__ void rotate_row_fast(const T* __restrict__ src, int K
   const float rl = sg * (norm * rs);
   uint2* xrow = reinterpret_cast<uint2*>(xq_row);
 #pragma unroll
-  for (int q = 0; q < kFastMaxGroups; ++q) {
-    const int grp = tid + q * kRowThreads;
+  for (int q = 0; q < kQ; ++q) {
+    const int grp = tid + q * NT;
     if (grp >= groups) continue;
     float x[16], y[16];  // x: the stored values (up to sg), then the rotated ones
     if (in_regs) {
@@ -247,6 +281,17 @@ __device__ __forceinline__ void rotate_row_fast(const T* __restrict__ src, int K
     }
     xrow[grp] = uint2{w0, w1};
   }
+}
+
+template <typename T, int NT = kRowThreads>
+__device__ __forceinline__ void rotate_row_fast(const T* __restrict__ src, int K, int log2b,
+                                                float norm, uint8_t* __restrict__ xq_row,
+                                                float* __restrict__ s_out,
+                                                float* __restrict__ xrot_row, float* row,
+                                                float* red) {
+  uint32_t raw[RowGroups<NT>::kQ][16];
+  rotate_row_load<T, NT>(src, K, raw);
+  rotate_row_finish<T, NT>(raw, K, log2b, norm, xq_row, s_out, xrot_row, row, red);
 }
 
 }  // namespace qift

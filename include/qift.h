@@ -86,7 +86,7 @@
 extern "C" {
 #endif
 
-#define QIFT_ABI_VERSION 5
+#define QIFT_ABI_VERSION 6
 
 typedef enum {
   QIFT_OK = 0,
@@ -262,6 +262,29 @@ qift_status qift_w2a4_linear_ex(const uint8_t* xq, const float* s_a, int64_t M, 
                                 const uint32_t* codes, const void* scales, qift_dtype scale_dtype,
                                 qift_levels levels, uint32_t level_table, int64_t N, void* Y,
                                 qift_dtype y_dtype, qift_stream stream);
+
+/*
+ * qift_rotate_w2a4_linear -- the online activation path and the linear in
+ * one call (Qift abstract: rotated W2A4 inference), for a layer whose input
+ * is not yet quantized: exactly qift_rotate_quant_act(X, x_dtype, M, K,
+ * had_block, xq, s_a, NULL) followed by qift_w2a4_linear_ex(xq, s_a, M, K,
+ * codes, scales, scale_dtype, levels, level_table, N, Y, y_dtype), with the
+ * same results bit for bit (xq and s_a are written too). A single token row
+ * (M = 1) with K % 16 == 0, had_block >= 16 and 16-byte aligned X and xq runs
+ * as one launch in which every workgroup rotates and quantizes the row itself
+ * while its weights stream in; other calls run the two launches.
+ *   X, x_dtype, had_block, xq, s_a  as qift_rotate_quant_act (x_rot omitted)
+ *   the rest                        as qift_w2a4_linear_ex
+ * K must satisfy both calls' limits (a multiple of 64, at most
+ * QIFT_MAX_ROW). Errors as either call; M = 0 is a no-op, and N = 0 only
+ * writes xq and s_a.
+ */
+qift_status qift_rotate_w2a4_linear(const void* X, qift_dtype x_dtype, int64_t M, int64_t K,
+                                    int32_t had_block, uint8_t* xq, float* s_a,
+                                    const uint32_t* codes, const void* scales,
+                                    qift_dtype scale_dtype, qift_levels levels,
+                                    uint32_t level_table, int64_t N, void* Y, qift_dtype y_dtype,
+                                    qift_stream stream);
 
 /*
  * qift_kv4_quant -- KV4 (Qift abstract: rotated W2A4/KV4 inference): each

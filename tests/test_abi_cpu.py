@@ -32,10 +32,10 @@ def test_library_loads_and_exports_every_declared_symbol():
     lib = q.load_library()
     names = declared_functions()
     assert "qift_w2a4_linear" in names and "qift_kv4_quant" in names
-    assert len(names) == 20, names
+    assert len(names) == 21, names
     for n in names:
         assert hasattr(lib, n), n
-    assert q.abi_version() == 5
+    assert q.abi_version() == 6
     for s in range(5):
         assert q.status_string(s).startswith("QIFT_")
 
@@ -502,3 +502,33 @@ def test_kv4_attention_noalloc_limit_matches_workspace_rule():
         else:
             assert st != q.QIFT_ERR_UNSUPPORTED  # fits (the launch itself needs a GPU)
     assert attn_noalloc(S=0, q=None, kq=None, out=None) == q.QIFT_OK
+
+
+def rot_lin(**kw):
+    a = dict(X=A16, xd=q.QIFT_BF16, M=1, K=4096, B=4096, xq=A16b, s_a=A16c, codes=A16d,
+             scales=A16e, sd=q.QIFT_F16, lv=0, table=0, N=4096, Y=V(0x60000), yd=q.QIFT_BF16)
+    a.update(kw)
+    return q._C.qift_rotate_w2a4_linear(a["X"], a["xd"], a["M"], a["K"], a["B"], a["xq"], a["s_a"],
+                                        a["codes"], a["scales"], a["sd"], a["lv"], a["table"],
+                                        a["N"], a["Y"], a["yd"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(X=None), q.QIFT_ERR_INVALID_ARG),
+    (dict(xq=None), q.QIFT_ERR_INVALID_ARG),
+    (dict(codes=None), q.QIFT_ERR_INVALID_ARG),
+    (dict(K=4000, B=16), q.QIFT_ERR_INVALID_ARG),          # not a multiple of 64 (linear rule)
+    (dict(K=32768, B=4096), q.QIFT_ERR_UNSUPPORTED),       # above the rotation's row limit
+    (dict(B=3), q.QIFT_ERR_INVALID_ARG),
+    (dict(xd=q.QIFT_F16), q.QIFT_ERR_INVALID_ARG),
+    (dict(lv=3), q.QIFT_ERR_INVALID_ARG),                  # level table missing
+    (dict(yd=q.QIFT_F16), q.QIFT_ERR_INVALID_ARG),
+    (dict(xq=V(0x20008)), q.QIFT_ERR_ALIGNMENT),
+])
+def test_rotate_linear_rejects(kw, status):
+    assert rot_lin(**kw) == status
+    assert q.last_error() != ""
+
+
+def test_rotate_linear_empty_is_noop():
+    assert rot_lin(M=0, X=None, xq=None, s_a=None, codes=None, scales=None, Y=None) == q.QIFT_OK

@@ -205,12 +205,14 @@ def test_grouped_float_epilogue_llama_shapes(y_dtype):
 @pytest.mark.parametrize("y_dtype", [torch.float32, torch.bfloat16])
 @pytest.mark.parametrize("M,K,N,kind,off", [
     (1, 4096, 4096, "mnz", 0), (16, 11008, 4096, "mnz", 0), (4, 4096, 11008, "pot", 0),
-    (8, 4096, 4099, "mnz", 1), (16, 2048, 1001, "int4", 3),
+    (8, 4096, 4099, "mnz", 1), (16, 2048, 1001, "int4", 3), (2, 4096, 22010, "mnz", 2),
     (2, 256, 131100, "mnz", 0), (16, 256, 131104, "mnz", 0), (3, 512, 131101, "pot", 1)])
 def test_single_call_float_epilogue(y_dtype, M, K, N, kind, off):
     """One linear per call (M <= 16): the split-K decode kernel at LLaMA-7B
-    shapes and, for N >= 131072, the 64-channel-wave kernel, with float
-    outputs (ragged N and misaligned outputs included), guarded."""
+    shapes (one, two and four 16-channel tiles per workgroup; N = 22010 ends
+    in a workgroup whose last tile is partial) and, for N >= 131072, the
+    64-channel-wave kernel, with float outputs (ragged N and misaligned
+    outputs included), guarded."""
     codes, s_w, cw, swt = make_weights(K, N, kind, seed=K + N + M)
     qa = si.uniform_int4((M, K), seed=M + 3 * K)
     s_a = si.positive_scales(M, seed=M + 5)
