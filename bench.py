@@ -65,7 +65,8 @@ def parse():
                    help="skip the extra measurements and the CPU baseline (profiling runs)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--copy-calibration", action="store_true",
-                   help="also run a plain 1 GiB device copy (counter calibration)")
+                   help="first run the measurement copy kernel on 1 GiB three times (the "
+                        "reference reading for counter runs)")
     p.add_argument("--unit", choices=sorted(UNITS),
                    help="run only this unit --steps times (for profiling runs) and exit")
     return p.parse_args()
@@ -144,6 +145,19 @@ def unit_decode_layer_by_layer(q, torch, dev, steps):
         g.replay()
 
 
+def unit_decode_layer_by_layer_fused(q, torch, dev, steps):
+    """The same 32-layer dependent decode with each input's rotation and
+    linear in one call (qift_rotate_w2a4_linear), replayed steps times."""
+    items, _ = layer_by_layer_items(q, torch, dev, 1)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for it in items:
+            q.qift_rotate_w2a4_linear(it["X"], it["B"], it["cw"], it["sw"], "mnz", Y=it["Y"],
+                                      xq=it["xq"], s_a=it["sa"])
+    for _ in range(steps):
+        g.replay()
+
+
 def unit_decode_single_4096(q, torch, dev, steps):
     """One 4096 x 4096 MNZ linear at M = 1 (bf16 output), steps eager calls,
     each on one of 64 weight copies (268 MB, past the last-level cache)."""
@@ -161,8 +175,40 @@ def unit_decode_single_4096(q, torch, dev, steps):
         q.qift_w2a4_linear(xq, sa, cw, sw, "mnz", Y=Y)
 
 
-UNITS = {"prefill_up_proj": unit_prefill_up_proj, "kv4": unit_kv4, "attention": unit_attention,
+def unit_rotate_up_proj_input(q, torch, dev, steps):
+    """Rotate + int4-quantize the up_proj input of a 2048-token prefill:
+    X [2048, 4096] bf16, one 4096-point Hadamard block per row."""
+    import synth_inputs as si
+    X = si.device_activations(2048, 4096, seed=6, device=dev)
+    xq = torch.empty((2048, 2048), dtype=torch.uint8, device=dev)
+    sa = torch.empty((2048,), dtype=torch.float32, device=dev)
+    for _ in range(steps):
+        q.qift_rotate_quant_act(X, 4096, xq=xq, s_a=sa)
+
+
+COPY_BYTES = 1 << 30
+
+
+def unit_copy(q, torch, dev, steps):
+    """The measurement copy kernel on 1 GiB (1 GiB read + 1 GiB written per
+    launch): the reference reading for the HBM byte counters."""
+    src = torch.empty((COPY_BYTES,), dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(steps):
+        q.qift_measure_stream(src, dst)
+
+
+def unit_mfma_i8(q, torch, dev, steps):
+    """The int8 matrix-core loop (2048 workgroups x 4096 rounds), steps launches."""
+    clk = torch.zeros((4,), dtype=torch.int64, device=dev)
+    for _ in range(steps):
+        q.qift_measure_mfma_i8(MFMA_ITERS, MFMA_WORKGROUPS, clk)
+
+
+UNITS = {"prefill_up_proj": unit_prefill_up_proj, "rotate_up_proj_input": unit_rotate_up_proj_input,
+         "copy": unit_copy, "mfma_i8": unit_mfma_i8, "kv4": unit_kv4, "attention": unit_attention,
          "gptq": unit_gptq, "decode_layer_by_layer": unit_decode_layer_by_layer,
+         "decode_layer_by_layer_fused": unit_decode_layer_by_layer_fused,
          "decode_single_4096": unit_decode_single_4096}
 
 
@@ -295,6 +341,69 @@ def vendor_int8_gemm(torch, M, K, N, dev):
         return {"error": repr(e)[:120]}
 
 
+MFMA_ITERS = 4096
+MFMA_WORKGROUPS = 2048   # 8 waves per compute unit, 2 per SIMD
+
+
+def measured_peaks(q, torch, dev):
+    """On-box ceilings beside the published ones: the read-only and copy
+    rates of the measurement stream kernel (2 GiB read; 1 GiB copied), the
+    int8 matrix-core rate of a register-only MFMA loop, and the shader clock
+    read during that loop. Median of 20 timed launches each."""
+    out = {}
+    buf = torch.empty((2 << 30,), dtype=torch.uint8, device=dev)
+    med, mn, _ = time_fn(torch, lambda: q.qift_measure_stream(buf), 20, warmup=5)
+    out["hbm_read_GBps"] = round(buf.numel() / (med * 1e-3) / 1e9, 1)
+    out["hbm_read_GBps_best"] = round(buf.numel() / (mn * 1e-3) / 1e9, 1)
+    src, dst = buf[:COPY_BYTES], buf[COPY_BYTES:]
+    med, mn, _ = time_fn(torch, lambda: q.qift_measure_stream(src, dst), 20, warmup=5)
+    out["hbm_copy_GBps"] = round(2 * COPY_BYTES / (med * 1e-3) / 1e9, 1)
+    out["hbm_copy_GBps_best"] = round(2 * COPY_BYTES / (mn * 1e-3) / 1e9, 1)
+    del buf, src, dst
+    clk = torch.zeros((4,), dtype=torch.int64, device=dev)
+    med, mn, _ = time_fn(torch, lambda: q.qift_measure_mfma_i8(MFMA_ITERS, MFMA_WORKGROUPS, clk),
+                         20, warmup=5)
+    ops = 32.0 * 32768 * MFMA_ITERS * MFMA_WORKGROUPS
+    c = clk.cpu().tolist()
+    mhz = 100.0 * (c[2] - c[0]) / max(c[3] - c[1], 1)
+    out["int8_mfma_TOPS"] = round(ops / (med * 1e-3) / 1e12, 1)
+    out["int8_mfma_TOPS_best"] = round(ops / (mn * 1e-3) / 1e12, 1)
+    out["shader_clock_MHz_under_mfma"] = round(mhz, 0)
+    out["int8_TOPS_per_GHz"] = round(out["int8_mfma_TOPS"] / (mhz / 1e3), 1) if mhz > 0 else None
+    out["method"] = (f"qift_measure_stream (non-temporal 16-byte loads, 8192 x 256 threads) and "
+                     f"qift_measure_mfma_i8 ({MFMA_WORKGROUPS} workgroups x 4 waves x "
+                     f"{MFMA_ITERS} x 8 v_mfma_i32_16x16x64_i8); HIP events, median of 20")
+    return out
+
+
+def settle_clocks(fn, torch, min_s=0.3, max_s=3.0, window=20, tol=0.01):
+    """Untimed steps until the GPU clocks have settled: at least min_s of
+    steps, then until the mean of the last `window` steps is within `tol` of
+    the window before (at most max_s). Returns what it did."""
+    t0 = time.perf_counter()
+    times = []
+    reason = "cap"
+    while True:
+        a = time.perf_counter()
+        fn()
+        torch.cuda.synchronize()
+        times.append(time.perf_counter() - a)
+        el = time.perf_counter() - t0
+        if el >= min_s and len(times) >= 2 * window:
+            prev = float(np.mean(times[-2 * window:-window]))
+            last = float(np.mean(times[-window:]))
+            if abs(last - prev) <= tol * prev:
+                reason = "stable"
+                break
+        if el >= max_s:
+            break
+    return {"s": round(time.perf_counter() - t0, 3), "steps": len(times), "until": reason,
+            "first_step_ms": round(times[0] * 1e3, 4), "last_step_ms": round(times[-1] * 1e3, 4),
+            "why": "the clocks ramp after the weight quantization that builds the stack; "
+                   "synchronized untimed steps run until the step time is flat, before the "
+                   "--warmup steps and the timed steps"}
+
+
 def kernel_source_hash():
     h = hashlib.sha256()
     for path in KERNEL_SRCS:
@@ -321,13 +430,20 @@ def traffic_from_profile(achieved_unit_bytes):
 # ---------------------------------------------------------------------------
 
 def cpu_baseline(budget_s=15.0):
+    """The oracle on the host cores this process may run on (its affinity
+    set), with the BLAS pool limited to that many threads."""
+    from threadpoolctl import threadpool_limits
+    cores = len(os.sched_getaffinity(0))
+    with threadpool_limits(limits=cores):
+        out = _cpu_baseline(budget_s)
+    out["cores"] = cores
+    out["cores_source"] = "len(os.sched_getaffinity(0)); BLAS threads limited to it"
+    return out
+
+
+def _cpu_baseline(budget_s):
     from oracle import qift_oracle as O
     import synth_inputs as si
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:
-        threads = len(os.sched_getaffinity(0))
     done_bytes = 0
     n_lin = 0
     t_total = 0.0
@@ -353,22 +469,32 @@ def cpu_baseline(budget_s=15.0):
             n_lin += 1
             if t_total >= budget_s:
                 break
-    return {"value": done_bytes / t_total / 1e9, "unit": "GB/s", "cores": int(threads),
-            "kind": "oracle",
+    return {"value": done_bytes / t_total / 1e9, "unit": "GB/s", "kind": "oracle",
             "sample": f"{n_lin} linears of one LLaMA-7B-shaped layer at M=1 (rotate+quantize the "
                       f"input, unpack the oracle-packed 2-bit codes, exact integer matmul), "
                       f"{t_total:.1f} s of CPU time; GB/s of packed codes+scales consumed"}
 
 
 def cpu_model():
+    """The host CPU as /proc/cpuinfo names it, with its family/model/stepping
+    numbers (a virtualised host may give only a generic name) and the number
+    of CPUs online."""
+    info = {}
     try:
         with open("/proc/cpuinfo") as f:
             for line in f:
-                if line.startswith("model name"):
-                    return line.split(":", 1)[1].strip()
+                if ":" not in line:
+                    if info:
+                        break
+                    continue
+                k, v = (x.strip() for x in line.split(":", 1))
+                if k in ("model name", "cpu family", "model", "stepping") and k not in info:
+                    info[k] = v
     except OSError:
-        pass
-    return None
+        return None
+    name = info.get("model name", "unknown")
+    return (f"{name} (family {info.get('cpu family', '?')}, model {info.get('model', '?')}, "
+            f"stepping {info.get('stepping', '?')}; {os.cpu_count()} CPUs online)")
 
 
 def cpu_oracle_units():
@@ -458,12 +584,8 @@ def main():
     q.load_library()
 
     if args.copy_calibration:
-        src = torch.empty((1 << 30,), dtype=torch.uint8, device=dev)
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            dst.copy_(src)
+        unit_copy(q, torch, dev, 3)
         torch.cuda.synchronize()
-        del src, dst
 
     if args.unit:
         UNITS[args.unit](q, torch, dev, args.steps)
@@ -476,6 +598,8 @@ def main():
     stack = DecodeStack(q, torch, llama7b_layers("mnz"), args.m, 0.02, dev)
     log(f"  built in {time.time() - t0:.1f}s: {len(stack.items)} linears, {stack.bytes / 1e9:.4f} GB")
 
+    settle = settle_clocks(stack.step, torch)
+    log(f"  clocks settled: {settle['steps']} steps in {settle['s']} s ({settle['until']})")
     for _ in range(args.warmup):
         stack.step()
     torch.cuda.synchronize()
@@ -501,8 +625,14 @@ def main():
         f"{k_mean:.4f} ms ({achieved:.0f} GB/s), median {np.median(k_ms):.4f} ms")
 
     extra = {}
+    peaks = None
     if not args.only_headline:
         extra = measure_extras(q, torch, dev, stack, args)
+        log("measuring on-box peaks")
+        peaks = measured_peaks(q, torch, dev)
+        extra["measured_peaks"] = peaks
+        log(f"  read {peaks['hbm_read_GBps']} GB/s, copy {peaks['hbm_copy_GBps']} GB/s, "
+            f"int8 {peaks['int8_mfma_TOPS']} TOPS at {peaks['shader_clock_MHz_under_mfma']} MHz")
 
     traffic = traffic_from_profile(stack.bytes)
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -510,6 +640,9 @@ def main():
                 "kernel": "linear_grouped_kernel (decode, 224 linears)",
                 "algorithmic_bytes_per_launch": stack.bytes,
                 "mean_launch_ms": round(k_mean, 5)}
+    if peaks:
+        roofline["measured_read_peak"] = peaks["hbm_read_GBps"]
+        roofline["frac_of_measured_read_peak"] = round(achieved / peaks["hbm_read_GBps"], 4)
     cpu = None
     if not args.only_headline and not args.no_cpu_baseline:
         log("timing the CPU oracle baseline")
@@ -527,7 +660,7 @@ def main():
                                f"scales, A4, M={args.m} (rotate+quantize 1 batched launch + grouped linear)",
                    "global_batch": args.m, "seq_len": 1, "parallelism": "single-gpu",
                    "weight_stream_bytes": stack.bytes},
-        "roofline": roofline, "cpu_baseline": cpu, "extra": extra,
+        "settle": settle, "roofline": roofline, "cpu_baseline": cpu, "extra": extra,
     }
     print(json.dumps(out), flush=True)
 
@@ -778,11 +911,20 @@ def layer_by_layer_decode(q, torch, dev, M=1):
             q.qift_rotate_quant_act(it["X"], it["B"], xq=it["xq"], s_a=it["sa"])
             q.qift_w2a4_linear(it["xq"], it["sa"], it["cw"], it["sw"], "mnz", Y=it["Y"])
 
+    def fused():
+        for it in items:
+            q.qift_rotate_w2a4_linear(it["X"], it["B"], it["cw"], it["sw"], "mnz", Y=it["Y"],
+                                      xq=it["xq"], s_a=it["sa"])
+
     out = {"M": M, "layers": si.N_LAYERS, "weight_bytes": nbytes}
-    for name, fn in (("rotate_then_linear", separate),):
+    ref = None
+    for name, fn in (("rotate_then_linear", separate), ("rotate_linear_one_call", fused)):
         fn()
         torch.cuda.synchronize()
-        ref = torch.cat([it["Y"].reshape(-1) for it in items])
+        if ref is None:
+            ref = torch.cat([it["Y"].reshape(-1) for it in items])
+        elif not torch.equal(torch.cat([it["Y"].reshape(-1) for it in items]), ref):
+            raise RuntimeError("the one-call path differs from the two calls")
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
             fn()

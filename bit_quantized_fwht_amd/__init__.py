@@ -26,6 +26,7 @@ SCALE_RULES = {"absmax": 0, "mse": 1}
 QIFT_MAX_ROW = 16384
 QIFT_MAX_HAD_BLOCK = 4096
 QIFT_ATTENTION_SCRATCH_BYTES = 16 * 1024 * 1024
+QIFT_MEASURE_SINK_WORDS = 8192
 
 _TORCH_TO_QIFT = {torch.float32: QIFT_F32, torch.bfloat16: QIFT_BF16,
                   torch.float16: QIFT_F16, torch.int32: QIFT_I32}
@@ -89,6 +90,8 @@ def _load():
         "qift_gptq_workspace_bytes": [i64, i64, ctypes.POINTER(ctypes.c_size_t)],
         "qift_gptq_quantize_weights": [vp, c_st, i64, i64, vp, i32, c_st, ctypes.c_uint32, c_st,
                                        ctypes.c_double, vp, vp, c_st, vp, ctypes.c_size_t, vp],
+        "qift_measure_stream": [vp, vp, i64, i32, vp, vp],
+        "qift_measure_mfma_i8": [i64, i64, vp, vp, vp],
     }
     for name, args in sig.items():
         f = getattr(lib, name)
@@ -574,6 +577,44 @@ def qift_kv4_attention_decode_noalloc(q, kq, ks, vq, vs, had_block: int, out,
                                               _TORCH_TO_QIFT[out.dtype], _stream(stream, q.device))
     _check(st, "qift_kv4_attention_decode_noalloc")
     return out
+
+
+# ---------------------------------------------------------------------------
+# measurement calls (include/qift_measure.h): no step of the method
+# ---------------------------------------------------------------------------
+
+def _sink(device):
+    return torch.empty((QIFT_MEASURE_SINK_WORDS,), dtype=torch.int32, device=device)
+
+
+def qift_measure_stream(src, dst=None, sink=None, stream=None):
+    """Stream the bytes of ``src`` through the GPU: read only if ``dst`` is
+    None, else copy them into ``dst`` (same byte size, no overlap). For
+    timing the HBM rate; returns nothing useful."""
+    _dev_tensor(src, "src")
+    nbytes = src.numel() * src.element_size()
+    if dst is not None:
+        _dev_tensor(dst, "dst")
+        if dst.numel() * dst.element_size() != nbytes:
+            raise ValueError("dst must have the byte size of src")
+    sink = _sink(src.device) if sink is None else sink
+    st = _C.qift_measure_stream(_ptr(src), _ptr(dst), nbytes, 0 if dst is None else 1, _ptr(sink),
+                                _stream(stream, src.device))
+    _check(st, "qift_measure_stream")
+
+
+def qift_measure_mfma_i8(iters: int, workgroups: int, clk, sink=None, stream=None):
+    """Run iters x 8 int8 16x16x64 matrix-core instructions on each of
+    4 * workgroups waves (32768 operations each); ``clk`` (int64 [4] on the
+    GPU) receives the shader clock and the 100 MHz counter at the start and
+    end of the first wave."""
+    _dev_tensor(clk, "clk", (torch.int64,))
+    if clk.numel() < 4:
+        raise ValueError("clk must hold 4 int64")
+    sink = _sink(clk.device) if sink is None else sink
+    st = _C.qift_measure_mfma_i8(int(iters), int(workgroups), _ptr(sink), _ptr(clk),
+                                 _stream(stream, clk.device))
+    _check(st, "qift_measure_mfma_i8")
 
 
 # ---------------------------------------------------------------------------

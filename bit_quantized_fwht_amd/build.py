@@ -18,7 +18,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libqift.so")
 
 SOURCES = ["rotate_quant.hip", "kv4.hip", "kv4_attention.hip", "gptq.hip", "linear_decode.hip",
-           "linear_prefill.hip", "api.cpp"]
+           "linear_prefill.hip", "measure.hip", "api.cpp"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",

@@ -12,6 +12,7 @@
 #include <vector>
 
 #include "qift.h"
+#include "qift_measure.h"
 #include "qift_internal.h"
 
 namespace {
@@ -618,6 +619,38 @@ qift_status qift_w2a4_linear_grouped(const void* workspace, int64_t launch_tiles
   return hip_result(qift::launch_linear_grouped(workspace, launch_tiles, 0, 0,
                                                 reinterpret_cast<hipStream_t>(stream)),
                     "qift_w2a4_linear_grouped launch");
+}
+
+qift_status qift_measure_stream(const void* src, void* dst, int64_t bytes, int32_t mode,
+                                uint32_t* sink, qift_stream stream) {
+  if (mode != 0 && mode != 1) return fail(QIFT_ERR_INVALID_ARG, "mode must be 0 or 1");
+  if (bytes <= 0 || bytes % 16 != 0)
+    return fail(QIFT_ERR_INVALID_ARG, "bytes=%lld must be a positive multiple of 16", (long long)bytes);
+  if (!src || !sink || (mode == 1 && !dst)) return fail(QIFT_ERR_INVALID_ARG, "null buffer");
+  if (!aligned(src, 16) || (mode == 1 && !aligned(dst, 16)) || !aligned(sink, 4))
+    return fail(QIFT_ERR_ALIGNMENT, "src and dst must be 16-byte aligned, sink 4-byte");
+  if (mode == 1) {
+    const uintptr_t a = reinterpret_cast<uintptr_t>(src), b = reinterpret_cast<uintptr_t>(dst);
+    if (a < b + (uintptr_t)bytes && b < a + (uintptr_t)bytes)
+      return fail(QIFT_ERR_INVALID_ARG, "src and dst overlap");
+  }
+  return hip_result(qift::launch_measure_stream(src, mode == 1 ? dst : nullptr, bytes, mode, sink,
+                                                reinterpret_cast<hipStream_t>(stream)),
+                    "qift_measure_stream launch");
+}
+
+qift_status qift_measure_mfma_i8(int64_t iters, int64_t workgroups, uint32_t* sink,
+                                 uint64_t* clk, qift_stream stream) {
+  if (iters < 1 || iters > (int64_t(1) << 24))
+    return fail(QIFT_ERR_INVALID_ARG, "iters=%lld outside [1, 2^24]", (long long)iters);
+  if (workgroups < 1 || workgroups > (int64_t(1) << 20))
+    return fail(QIFT_ERR_INVALID_ARG, "workgroups=%lld outside [1, 2^20]", (long long)workgroups);
+  if (!sink || !clk) return fail(QIFT_ERR_INVALID_ARG, "null buffer");
+  if (!aligned(sink, 4) || !aligned(clk, 16))
+    return fail(QIFT_ERR_ALIGNMENT, "sink must be 4-byte aligned, clk 16-byte");
+  return hip_result(qift::launch_measure_mfma_i8(iters, workgroups, sink, clk,
+                                                 reinterpret_cast<hipStream_t>(stream)),
+                    "qift_measure_mfma_i8 launch");
 }
 
 }  // extern "C"

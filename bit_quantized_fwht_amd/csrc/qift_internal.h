@@ -278,6 +278,10 @@ hipError_t launch_linear_prefill(const qift_linear_desc& d, int scale_f16, int y
                                  hipStream_t s);
 hipError_t launch_rotate_linear_decode(const qift_linear_desc& d, const void* X, int x_bf16,
                                        int had_block, int scale_f16, int y_dtype, hipStream_t s);
+hipError_t launch_measure_stream(const void* src, void* dst, int64_t bytes, int mode,
+                                 uint32_t* sink, hipStream_t s);
+hipError_t launch_measure_mfma_i8(int64_t iters, int64_t workgroups, uint32_t* sink,
+                                  uint64_t* clk, hipStream_t s);
 hipError_t launch_linear_grouped(const void* workspace, int64_t total_tiles, int scale_f16,
                                  int y_dtype, hipStream_t s);
 

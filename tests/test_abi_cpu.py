@@ -12,6 +12,7 @@ import bit_quantized_fwht_amd as q
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "qift.h")
+MEASURE_HEADER = os.path.join(ROOT, "include", "qift_measure.h")
 
 V = ctypes.c_void_p
 A16 = V(0x10000)   # fake, 16-byte aligned device addresses (never dereferenced)
@@ -21,8 +22,8 @@ A16d = V(0x40000)
 A16e = V(0x50000)
 
 
-def declared_functions():
-    text = open(HEADER).read()
+def declared_functions(header=HEADER):
+    text = open(header).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*(qift_[a-z_0-9]+)\s*\(",
                                  text, flags=re.M)))
@@ -38,6 +39,31 @@ def test_library_loads_and_exports_every_declared_symbol():
     assert q.abi_version() == 6
     for s in range(5):
         assert q.status_string(s).startswith("QIFT_")
+
+
+def test_measurement_calls_exported_and_validated():
+    """The two measurement calls of include/qift_measure.h are exported and
+    reject bad arguments before any launch."""
+    lib = q.load_library()
+    names = declared_functions(MEASURE_HEADER)
+    assert names == ["qift_measure_mfma_i8", "qift_measure_stream"], names
+    for n in names:
+        assert hasattr(lib, n), n
+    ms, mm = q._C.qift_measure_stream, q._C.qift_measure_mfma_i8
+    assert ms(A16, A16b, 1024, 2, A16c, None) == q.QIFT_ERR_INVALID_ARG     # mode
+    assert ms(A16, A16b, 1000, 1, A16c, None) == q.QIFT_ERR_INVALID_ARG     # not a multiple of 16
+    assert ms(A16, A16b, 0, 0, A16c, None) == q.QIFT_ERR_INVALID_ARG
+    assert ms(None, A16b, 1024, 0, A16c, None) == q.QIFT_ERR_INVALID_ARG
+    assert ms(A16, None, 1024, 1, A16c, None) == q.QIFT_ERR_INVALID_ARG     # copy needs dst
+    assert ms(A16, A16b, 1024, 0, None, None) == q.QIFT_ERR_INVALID_ARG     # sink
+    assert ms(V(0x10008), A16b, 1024, 0, A16c, None) == q.QIFT_ERR_ALIGNMENT
+    assert ms(A16, V(0x10200), 1024, 1, A16c, None) == q.QIFT_ERR_INVALID_ARG  # overlap
+    assert mm(0, 16, A16, A16b, None) == q.QIFT_ERR_INVALID_ARG
+    assert mm(1 << 25, 16, A16, A16b, None) == q.QIFT_ERR_INVALID_ARG
+    assert mm(16, 0, A16, A16b, None) == q.QIFT_ERR_INVALID_ARG
+    assert mm(16, (1 << 20) + 1, A16, A16b, None) == q.QIFT_ERR_INVALID_ARG
+    assert mm(16, 16, None, A16b, None) == q.QIFT_ERR_INVALID_ARG
+    assert mm(16, 16, A16, V(0x20008), None) == q.QIFT_ERR_ALIGNMENT
 
 
 def lin(**kw):

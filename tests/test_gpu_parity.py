@@ -284,7 +284,7 @@ def run_linear(qa, codes, s_a, s_w, kind, out_dtype):
 LIN_SHAPES = [(1, 64, 1), (1, 256, 17), (3, 320, 64), (4, 4096, 257), (8, 192, 300),
               (16, 1024, 129), (5, 2304, 40), (2, 8448, 33), (3, 3072, 4100), (2, 256, 131100),
               (17, 256, 130), (31, 128, 63), (64, 4096, 256), (129, 576, 200),
-              (200, 2048, 385), (1000, 256, 8200), (1, 2048, 20000)]
+              (200, 2048, 385), (1000, 256, 8200), (1050, 256, 7300), (1, 2048, 20000)]
 
 
 @pytest.mark.parametrize("kind", ["mnz", "pot", "int4"])
