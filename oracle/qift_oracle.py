@@ -50,6 +50,22 @@ its best scale). Readings taken here:
   j = 0..63, codes decided against each, and keeps the one with the smallest
   sum of squared errors (float64; the first on ties).
 
+The conventional asymmetric two-bit grid with a zero point (the Qift abstract
+names it as the baseline that improves on the standard set and whose zero
+point Qift removes; it gives no formula). Readings taken here, the usual
+min-max uniform quantizer:
+
+* per channel, a 4-point uniform grid s * (c - z), c in {0, 1, 2, 3}, with an
+  integer zero point z;
+* the range of the rotated float32 row is widened to contain 0:
+  lo = min(min w, 0), hi = max(max w, 0); s = fl32(fl32(hi - lo) / 3),
+  rounded to the stored scale dtype; z = clip(rint(fl32(-lo / s)), 0, 3);
+* c = clip(rint(fl32(w / s)) + z, 0, 3), round half to even in float32;
+  s = 0 (an all-zero row, or a step below the stored dtype's range) gives
+  z = 0 and c = 0;
+* s and z are stored side by side: the 2N scale entries hold s_0..s_{N-1}
+  then z_0..z_{N-1} (z as a value of the scale dtype, exact).
+
 Error-compensated quantization with the fixed levels (the Qift abstract
 reports the "GPTQ residual behavior" of its level sets; the QTEA abstract
 describes GPTQ-style column-by-column quantization, in which quantizing one
@@ -290,14 +306,61 @@ def int4_weight_codes(wr32: np.ndarray, s_stored: np.ndarray) -> np.ndarray:
     return q
 
 
+def asym_minmax_params(wr32: np.ndarray, scale_dtype: str):
+    """Step and zero point of the asymmetric min-max grid, per channel:
+    lo = min(min w, 0), hi = max(max w, 0) over the float32 row,
+    s = store(fl32(fl32(hi - lo) / 3)), z = clip(rint(fl32(-lo / s)), 0, 3)
+    (z = 0 where s = 0). Returns (s [N] stored dtype, z [N] int64)."""
+    w = np.asarray(wr32, dtype=np.float32)
+    lo = np.minimum(w.min(axis=1), np.float32(0)).astype(np.float32)
+    hi = np.maximum(w.max(axis=1), np.float32(0)).astype(np.float32)
+    rng = (hi - lo).astype(np.float32)
+    s = _store_scale((rng / np.float32(3)).astype(np.float32), scale_dtype)
+    z = np.zeros(w.shape[0], dtype=np.int64)
+    for n in range(w.shape[0]):
+        sn = np.float32(s[n])
+        if sn == 0:
+            continue
+        z[n] = int(np.clip(np.rint(np.float32(-lo[n]) / sn), 0, 3))
+    return s, z
+
+
+def asym_codes(wr32: np.ndarray, s_stored: np.ndarray, z: np.ndarray) -> np.ndarray:
+    """Codes of the asymmetric grid: c = clip(rint(fl32(w / s)) + z, 0, 3),
+    decided in float32 with the stored step; 0 where s = 0."""
+    w = np.asarray(wr32, dtype=np.float32)
+    c = np.zeros(w.shape, dtype=np.int64)
+    for n in range(w.shape[0]):
+        sn = np.float32(s_stored[n])
+        if sn == 0:
+            continue
+        c[n] = np.clip(np.rint(w[n] / sn).astype(np.int64) + int(z[n]), 0, 3)
+    return c
+
+
+def split_asym_scales(s_w: np.ndarray):
+    """The 2N scale entries of the asymmetric grid -> (s [N], z [N] int64)."""
+    s_w = np.asarray(s_w)
+    N = s_w.shape[0] // 2
+    return s_w[:N], s_w[N:].astype(np.int64)
+
+
 def quantize_weights(W: np.ndarray, B: int, kind: str, scale_dtype: str, table=None,
                      rule: str = "absmax"):
     """Offline path for one linear W [N, K]: rotate each row along K in blocks
     of B (float64), round to float32, scale rule, nearest code. kind 'lut'
-    takes a level table.
+    takes a level table; kind 'asym' is the min-max grid with a zero point
+    (absmax rule only: its step comes from the range).
     Returns (codes int64 [N, K] (2-bit codes, or int4 values for 'int4'),
-    scales [N] in the stored dtype, rotated float32 weights)."""
+    scales [N] in the stored dtype ([2N] for 'asym': the steps, then the zero
+    points), rotated float32 weights)."""
     wr32 = rotate(W, B).astype(np.float32)
+    if kind == "asym":
+        if rule != "absmax":
+            raise ValueError("the asymmetric grid takes its step from the range")
+        s, z = asym_minmax_params(wr32, scale_dtype)
+        codes = asym_codes(wr32, s, z)
+        return codes, np.concatenate([s, z.astype(s.dtype)]), wr32
     s = weight_scales(wr32, kind, scale_dtype, table, rule)
     if kind == "int4":
         codes = int4_weight_codes(wr32, s)
@@ -366,6 +429,8 @@ def gptq_quantize_weights(W: np.ndarray, X: np.ndarray, B: int, kind: str, scale
     channel is processed independently once U is known. ``factor`` = a
     (U, dead) pair from an earlier call, reused.
     Returns (codes int64 [R, K], scales [R] stored dtype, (U, dead))."""
+    if kind == "asym":
+        raise ValueError("error-compensated quantization takes the fixed level sets only")
     W = np.asarray(W)
     if rows is not None:
         W = W[np.asarray(rows)]
@@ -392,7 +457,7 @@ def code_levels(codes: np.ndarray, kind: str, table=None) -> np.ndarray:
 
 def level_kappa(kind: str) -> float:
     """Factor from the integer level to the multiple of the scale."""
-    return 1.0 if kind == "lut" else LEVEL_KINDS[kind]["kappa"]
+    return 1.0 if kind in ("lut", "asym") else LEVEL_KINDS[kind]["kappa"]
 
 
 # ---------------------------------------------------------------------------
@@ -538,8 +603,14 @@ def linear(q: np.ndarray, s_a: np.ndarray, codes: np.ndarray, s_w: np.ndarray, k
            table=None):
     """y = x_q W_q^T with integer accumulation: acc = q . level^T, then
     y[m, n] = acc[m, n] * s_a[m] * s_w[n] * kappa (kappa = 1/2 for the
-    half-scale MNZ levels, 1 otherwise). Returns (acc int64, y float64)."""
-    lv = code_levels(codes, kind, table)
+    half-scale MNZ levels, 1 otherwise). For 'asym', s_w holds the 2N steps
+    and zero points and the level of code c in channel n is c - z_n.
+    Returns (acc int64, y float64)."""
+    if kind == "asym":
+        s_w, z = split_asym_scales(s_w)
+        lv = np.asarray(codes, dtype=np.int64) - z[:, None]
+    else:
+        lv = code_levels(codes, kind, table)
     acc = int_matmul(q, lv)
     kappa = level_kappa(kind)
     y = acc.astype(np.float64) * np.asarray(s_a, np.float64)[:, None] \

@@ -239,6 +239,57 @@ def _kinds_with(kind, **over):
     return d
 
 
+def _asym_params_not_widened(wr32, scale_dtype):
+    w = np.asarray(wr32, dtype=np.float32)
+    lo, hi = w.min(axis=1), w.max(axis=1)
+    s = O._store_scale(((hi - lo) / np.float32(3)).astype(np.float32), scale_dtype)
+    z = np.zeros(w.shape[0], dtype=np.int64)
+    for n in range(w.shape[0]):
+        if s[n] != 0:
+            z[n] = int(np.clip(np.rint(np.float32(-lo[n]) / np.float32(s[n])), 0, 3))
+    return s, z
+
+
+def _asym_params_zero_point_sign(wr32, scale_dtype):
+    s, z = _real_asym_params(wr32, scale_dtype)
+    return s, np.clip(-z, 0, 3)
+
+
+def _asym_params_divisor_4(wr32, scale_dtype):
+    w = np.asarray(wr32, dtype=np.float32)
+    lo = np.minimum(w.min(axis=1), np.float32(0))
+    hi = np.maximum(w.max(axis=1), np.float32(0))
+    s = O._store_scale(((hi - lo) / np.float32(4)).astype(np.float32), scale_dtype)
+    z = np.zeros(w.shape[0], dtype=np.int64)
+    for n in range(w.shape[0]):
+        if s[n] != 0:
+            z[n] = int(np.clip(np.rint(np.float32(-lo[n]) / np.float32(s[n])), 0, 3))
+    return s, z
+
+
+def _asym_codes_round_half_up(wr32, s_stored, z):
+    w = np.asarray(wr32, dtype=np.float32)
+    c = np.zeros(w.shape, dtype=np.int64)
+    for n in range(w.shape[0]):
+        sn = np.float32(s_stored[n])
+        if sn != 0:
+            c[n] = np.clip(np.floor(w[n] / sn + np.float32(0.5)).astype(np.int64) + int(z[n]), 0, 3)
+    return c
+
+
+def _linear_asym_without_zero_point(q, s_a, codes, s_w, kind, table=None):
+    if kind == "asym":
+        s, _ = O.split_asym_scales(s_w)
+        acc = _real_int_matmul(q, np.asarray(codes, np.int64))
+        return acc, acc * np.asarray(s_a, np.float64)[:, None] * np.asarray(s, np.float64)[None, :]
+    return _real_linear(q, s_a, codes, s_w, kind, table)
+
+
+_real_asym_params = O.asym_minmax_params
+_real_int_matmul = O.int_matmul
+_real_linear = O.linear
+
+
 MUTATIONS = {
     "hadamard_wrong_sign": [("hadamard", _wrong_sign_hadamard)],
     "rotate_unnormalized": [("rotate", _unnormalized_rotate)],
@@ -271,6 +322,11 @@ MUTATIONS = {
     "gptq_factor_without_inverse": [("gptq_factor", _gptq_factor_without_inverse)],
     "gptq_damping_absolute": [("gptq_hessian", _gptq_hessian_absolute_damping)],
     "gptq_hessian_unrotated": [("gptq_hessian", _gptq_hessian_unrotated)],
+    "asym_range_not_widened_to_zero": [("asym_minmax_params", _asym_params_not_widened)],
+    "asym_zero_point_sign": [("asym_minmax_params", _asym_params_zero_point_sign)],
+    "asym_step_divisor_4": [("asym_minmax_params", _asym_params_divisor_4)],
+    "asym_codes_round_half_up": [("asym_codes", _asym_codes_round_half_up)],
+    "asym_linear_without_zero_point": [("linear", _linear_asym_without_zero_point)],
 }
 
 

@@ -1024,4 +1024,107 @@ def test_gptq_rows_match_full():
     pin_gptq_rows_match_full()
 
 
+# --------------------------------------------------------------------------
+# the asymmetric min-max grid with a zero point (the baseline of the abstract)
+# --------------------------------------------------------------------------
+
+def pin_asym_hand_example():
+    """tests/golden/asym_minmax.json, worked by hand: steps, zero points and
+    codes for float32 and float16 steps, and the linear's accumulator."""
+    g = golden("asym_minmax.json")
+    rows = g["rows"]
+    W = np.array([r["row"] for r in rows], np.float64)
+    N = len(rows)
+    for sdt in ("f32", "f16"):
+        codes, sz, _ = O.quantize_weights(W, 1, "asym", sdt)
+        assert sz.shape == (2 * N,) and sz.dtype == (np.float32 if sdt == "f32" else np.float16)
+        for i, r in enumerate(rows):
+            assert float(sz[i]) == r["scale"][sdt], (sdt, r["name"])
+            assert float(sz[N + i]) == r["zero"], (sdt, r["name"])
+            assert codes[i].tolist() == r["codes"], (sdt, r["name"])
+    lin = g["linear"]
+    codes, sz, _ = O.quantize_weights(W[:3], 1, "asym", "f32")
+    acc, y = O.linear(np.array([lin["q"]]), np.array([lin["s_a"]]), codes, sz, "asym")
+    assert acc[0].tolist() == [lin["acc"][k] for k in "ABC"]
+    assert y[0].tolist() == [lin["y"][k] for k in "ABC"]
+
+
+def _asym_rows(rng, N, K):
+    """Rows with skewed ranges: shifted Gaussians, all-positive and
+    all-negative rows, and rows with a few exact grid points."""
+    W = rng.normal(0, 1, (N, K)) + rng.choice([-2.0, -0.5, 0.0, 0.7, 3.0], (N, 1))
+    W[0] = np.abs(W[0]) + 0.1
+    W[1] = -np.abs(W[1]) - 0.1
+    return W.astype(np.float32).astype(np.float64)
+
+
+def pin_asym_nearest_brute_force():
+    """Every code is the nearest of the four grid points s * (c - z) (exact
+    float64 distances), except within 2^-20 of a half-step tie where the
+    float32 division decides; z is the nearest integer to -lo / s; the grid's
+    ends reach lo and hi to within half a step; s is the range / 3."""
+    rng = np.random.default_rng(71)
+    W = _asym_rows(rng, 24, 48)
+    for sdt in ("f32", "f16"):
+        codes, sz, wr = O.quantize_weights(W, 1, "asym", sdt)
+        N = W.shape[0]
+        s = sz[:N].astype(np.float64)
+        z = sz[N:].astype(np.float64)
+        for n in range(N):
+            w = wr[n].astype(np.float64)
+            lo, hi = min(w.min(), 0.0), max(w.max(), 0.0)
+            assert s[n] == pytest.approx((hi - lo) / 3, rel=1e-3)
+            assert z[n] in (0, 1, 2, 3)
+            assert -z[n] * s[n] <= lo + 0.5 * s[n] * (1 + 1e-3)
+            assert (3 - z[n]) * s[n] >= hi - 0.5 * s[n] * (1 + 1e-3)
+            t = -lo / s[n]
+            if abs(t - math.floor(t) - 0.5) > 2 ** -20:
+                assert z[n] == min(max(math.floor(t + 0.5), 0), 3)
+            for k in range(w.size):
+                d = [abs(w[k] - (c - z[n]) * s[n]) for c in range(4)]
+                u = w[k] / s[n]
+                if abs(u - math.floor(u) - 0.5) <= 2 ** -20:
+                    continue
+                assert d[codes[n, k]] == min(d), (sdt, n, k, w[k], s[n], z[n], codes[n, k])
+
+
+def pin_asym_linear_zero_point_form():
+    """The linear over the asymmetric grid equals the zero-point form
+    sum q c - z sum q (integer arithmetic, element by element)."""
+    rng = np.random.default_rng(72)
+    M, N, K = 3, 6, 40
+    q = rng.integers(-7, 8, (M, K))
+    codes = rng.integers(0, 4, (N, K))
+    s = rng.uniform(0.1, 1, N).astype(np.float32)
+    z = rng.integers(0, 4, N)
+    s_a = rng.uniform(0.1, 1, M)
+    acc, y = O.linear(q, s_a, codes, np.concatenate([s, z.astype(np.float32)]), "asym")
+    for m in range(M):
+        sq = int(sum(int(v) for v in q[m]))
+        for n in range(N):
+            qc = sum(int(q[m, k]) * int(codes[n, k]) for k in range(K))
+            assert acc[m, n] == qc - int(z[n]) * sq
+            assert y[m, n] == pytest.approx(acc[m, n] * s_a[m] * float(s[n]), rel=1e-15)
+
+
+def test_asym_hand_example():
+    pin_asym_hand_example()
+
+
+def test_asym_nearest_brute_force():
+    pin_asym_nearest_brute_force()
+
+
+def test_asym_linear_zero_point_form():
+    pin_asym_linear_zero_point_form()
+
+
+def test_asym_rejects_searched_scale_and_gptq():
+    W = np.ones((2, 16))
+    with pytest.raises(ValueError):
+        O.quantize_weights(W, 1, "asym", "f16", rule="mse")
+    with pytest.raises(ValueError):
+        O.gptq_quantize_weights(W, np.ones((4, 16)), 1, "asym", "f16")
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]
