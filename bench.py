@@ -370,7 +370,8 @@ def measured_peaks(q, torch, dev):
     out["int8_mfma_TOPS_best"] = round(ops / (mn * 1e-3) / 1e12, 1)
     out["shader_clock_MHz_under_mfma"] = round(mhz, 0)
     out["int8_TOPS_per_GHz"] = round(out["int8_mfma_TOPS"] / (mhz / 1e3), 1) if mhz > 0 else None
-    out["method"] = (f"qift_measure_stream (non-temporal 16-byte loads, 8192 x 256 threads) and "
+    out["method"] = (f"qift_measure_stream (64 KB per workgroup, non-temporal 16-byte loads and "
+                     f"stores) and "
                      f"qift_measure_mfma_i8 ({MFMA_WORKGROUPS} workgroups x 4 waves x "
                      f"{MFMA_ITERS} x 8 v_mfma_i32_16x16x64_i8); HIP events, median of 20")
     return out
@@ -782,8 +783,10 @@ def level_set_comparison(q, torch, dev):
     (4096 x 4096, N(0, 0.02^2) weights, block 4096) through the whole W2A4
     path: relative L2 error of the quantized linear's float32 output against
     the float32 product x W^T over 64 tokens (int4 activations in every case),
-    with the absmax and the searched (mse) scale; the weight quantizer's time
-    with each rule; and the decode / prefill speed of a level table."""
+    with the absmax and the searched (mse) scale, and of the asymmetric
+    min-max grid with a zero point; the weight quantizer's time with each rule;
+    and the decode / prefill speed of a level table and of the asymmetric
+    grid."""
     import synth_inputs as si
     N, K, B, M = 4096, 4096, 4096, 64
     W = si.device_weights(N, K, seed=91, sigma=0.02, device=dev)
@@ -801,8 +804,17 @@ def level_set_comparison(q, torch, dev):
                     W, B, kind, torch.float16, codes=cw, scales=sw, table=table, scale_rule=rule), 5,
                     warmup=1)
                 qt[f"{name}_{rule}_ms"] = round(med, 3)
+    # the conventional asymmetric grid with a zero point (min-max step; it has
+    # no searched-scale form)
+    cw, sw = q.qift_quantize_weights(W, B, "asym", torch.float16)
+    Y = q.qift_w2a4_linear(xq, sa, cw, sw, "asym", torch.float32)
+    err["asym_minmax"] = round(((Y - Yref).norm() / Yref.norm()).item(), 5)
+    med, _, _ = time_fn(torch, lambda: q.qift_quantize_weights(
+        W, B, "asym", torch.float16, codes=cw, scales=sw), 5, warmup=1)
+    qt["asym_minmax_ms"] = round(med, 3)
     out = {"rel_l2_output_error": err, "weight_quantizer": qt,
-           "mnz_beats_standard_at_searched_scale": err["mnz_mse"] < err["standard_w2_mse"]}
+           "mnz_beats_standard_at_searched_scale": err["mnz_mse"] < err["standard_w2_mse"],
+           "asym_minmax_beats_standard_absmax": err["asym_minmax"] < err["standard_w2_absmax"]}
     # speed: the level-table decode (single call, M = 1) and prefill (M = 2048)
     # against MNZ on the up_proj shape
     Wu = si.device_weights(11008, 4096, seed=93, sigma=0.02, device=dev)
@@ -812,7 +824,7 @@ def level_set_comparison(q, torch, dev):
         Xu = si.device_activations(M, 4096, seed=94, device=dev)
         xu, su, _ = q.qift_rotate_quant_act(Xu, 4096)
         Yu = torch.empty((M, 11008), dtype=torch.bfloat16, device=dev)
-        for name, kind, tb in (("mnz", "mnz", None), ("lut", "lut", table)):
+        for name, kind, tb in (("mnz", "mnz", None), ("lut", "lut", table), ("asym", "asym", None)):
             cw, sw = q.qift_quantize_weights(Wu, 4096, kind, torch.float16, table=tb)
 
             def call():

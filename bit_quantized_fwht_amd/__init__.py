@@ -21,7 +21,7 @@ LIB_PATH = os.path.join(_HERE, "libqift.so")
 # enums (qift.h)
 QIFT_OK, QIFT_ERR_INVALID_ARG, QIFT_ERR_ALIGNMENT, QIFT_ERR_UNSUPPORTED, QIFT_ERR_HIP = range(5)
 QIFT_F32, QIFT_BF16, QIFT_F16, QIFT_I32 = range(4)
-LEVELS = {"mnz": 0, "pot": 1, "int4": 2, "lut": 3}
+LEVELS = {"mnz": 0, "pot": 1, "int4": 2, "lut": 3, "asym": 4}
 SCALE_RULES = {"absmax": 0, "mse": 1}
 QIFT_MAX_ROW = 16384
 QIFT_MAX_HAD_BLOCK = 4096
@@ -197,6 +197,18 @@ def _table_arg(levels, table) -> int:
     return 0
 
 
+def scale_entries(N: int, levels) -> int:
+    """Entries of a linear's scales buffer: N, or 2N for levels='asym' (the
+    steps, then the zero points)."""
+    return 2 * N if _levels(levels) == LEVELS["asym"] else N
+
+
+def default_channels(scales, levels) -> int:
+    """N of a linear whose N is not given: from its scales ([N], or the
+    [2, N] / [2N] steps and zero points of levels='asym')."""
+    return scales.numel() // 2 if _levels(levels) == LEVELS["asym"] else scales.shape[0]
+
+
 def code_words_per_row(K: int, levels) -> int:
     return K // 8 if _levels(levels) == LEVELS["int4"] else K // 16
 
@@ -215,7 +227,9 @@ def qift_quantize_weights(W, had_block: int, levels="mnz", scale_dtype=torch.flo
     """W [N, K] float32/bfloat16 -> (codes int32 [Np, K/16 or K/8] holding the
     uint32 words in the tiled layout (Np = N rounded up to 16), scales [N] in
     scale_dtype). levels='lut' takes a level table (four integers);
-    scale_rule 'absmax' or 'mse' (qift_quantize_weights_ex)."""
+    levels='asym' (the min-max grid with a zero point) returns scales [2, N]:
+    the steps, then the zero points; scale_rule 'absmax' or 'mse'
+    (qift_quantize_weights_ex)."""
     _dev_tensor(W, "W", (torch.float32, torch.bfloat16))
     N, K = W.shape
     lv = _levels(levels)
@@ -223,10 +237,12 @@ def qift_quantize_weights(W, had_block: int, levels="mnz", scale_dtype=torch.flo
         codes = torch.empty((padded_channels(N), code_words_per_row(K, lv)), dtype=torch.int32,
                             device=W.device)
     if scales is None:
-        scales = torch.empty((N,), dtype=scale_dtype, device=W.device)
+        shape = (2, N) if lv == LEVELS["asym"] else (N,)
+        scales = torch.empty(shape, dtype=scale_dtype, device=W.device)
     _dev_tensor(codes, "codes", (torch.int32,))
     _dev_tensor(scales, "scales", (torch.float32, torch.float16))
-    if codes.numel() < padded_channels(N) * code_words_per_row(K, lv) or scales.numel() < N:
+    if codes.numel() < padded_channels(N) * code_words_per_row(K, lv) or \
+            scales.numel() < scale_entries(N, lv):
         raise ValueError("codes or scales buffer too small")
     st = _C.qift_quantize_weights_ex(_ptr(W), _TORCH_TO_QIFT[W.dtype], N, K, had_block, lv,
                                      _table_arg(lv, table), SCALE_RULES[scale_rule], _ptr(codes),
@@ -291,10 +307,12 @@ def qift_gptq_quantize_weights(W, H, had_block: int, levels="mnz", scale_dtype=t
         codes = torch.empty((padded_channels(N), code_words_per_row(K, lv)), dtype=torch.int32,
                             device=W.device)
     if scales is None:
-        scales = torch.empty((N,), dtype=scale_dtype, device=W.device)
+        shape = (2, N) if lv == LEVELS["asym"] else (N,)
+        scales = torch.empty(shape, dtype=scale_dtype, device=W.device)
     _dev_tensor(codes, "codes", (torch.int32,))
     _dev_tensor(scales, "scales", (torch.float32, torch.float16))
-    if codes.numel() < padded_channels(N) * code_words_per_row(K, lv) or scales.numel() < N:
+    if codes.numel() < padded_channels(N) * code_words_per_row(K, lv) or \
+            scales.numel() < scale_entries(N, lv):
         raise ValueError("codes or scales buffer too small")
     need = qift_gptq_workspace_bytes(N, K)
     if workspace is None:
@@ -427,8 +445,9 @@ def _check_linear_buffers(bufs, N, levels, scale_dtype=None, y_dtype=None, place
         raise ValueError("negative N")
     if s_a.numel() < M:
         raise ValueError(f"s_a has {s_a.numel()} elements, M = {M} needed")
-    if scales.numel() < N:
-        raise ValueError(f"scales has {scales.numel()} elements, N = {N} needed")
+    if scales.numel() < scale_entries(N, levels):
+        raise ValueError(f"scales has {scales.numel()} elements, {scale_entries(N, levels)} "
+                         f"needed for N = {N}")
     need = padded_channels(N) * code_words_per_row(K, levels)
     if codes.numel() < need:
         raise ValueError(f"codes has {codes.numel()} words, {need} needed for N = {N}, K = {K}")
@@ -444,9 +463,10 @@ def qift_w2a4_linear(xq, s_a, codes, scales, levels="mnz", out_dtype=torch.float
                      N=None, stream=None, table=None):
     """(xq [M, K/2], s_a [M], codes [N, ...], scales [N]) -> Y [M, N] in
     out_dtype (float32, bfloat16, or int32 for the raw accumulator).
-    levels='lut' takes a level table (qift_w2a4_linear_ex)."""
+    levels='lut' takes a level table, levels='asym' the 2N steps and zero
+    points as scales (qift_w2a4_linear_ex)."""
     if N is None:
-        N = scales.shape[0]
+        N = default_channels(scales, levels)
     if Y is None:
         _dev_tensor(xq, "xq", (torch.uint8,))
         Y = torch.empty((xq.shape[0], N), dtype=out_dtype, device=xq.device)
@@ -469,7 +489,7 @@ def qift_rotate_w2a4_linear(X, had_block: int, codes, scales, levels="mnz",
     _dev_tensor(X, "X", (torch.float32, torch.bfloat16))
     M, K = X.shape
     if N is None:
-        N = scales.shape[0]
+        N = default_channels(scales, levels)
     if xq is None:
         xq = torch.empty((M, K // 2), dtype=torch.uint8, device=X.device)
     if s_a is None:
@@ -639,7 +659,8 @@ class LinearGroup:
         for placement in (False, True):
             for i, it in enumerate(items):
                 try:
-                    _check_linear_buffers(it, it.get("N", it["scales"].shape[0]), it["levels"],
+                    _check_linear_buffers(it, it.get("N", default_channels(it["scales"], it["levels"])),
+                                          it["levels"],
                                           scale_dtype, y_dtype, placement)
                 except (TypeError, ValueError) as e:
                     raise type(e)(f"item {i}: {e}") from None
@@ -650,7 +671,7 @@ class LinearGroup:
                             raise ValueError(f"item {i}: {key} is on {it[key].device}, "
                                              f"the group on {device}")
         for i, it in enumerate(items):
-            N = it.get("N", it["scales"].shape[0])
+            N = it.get("N", default_channels(it["scales"], it["levels"]))
             M, K = it["xq"].shape[0], it["xq"].shape[1] * 2
             tw = _table_arg(it["levels"], it.get("table"))  # the descriptor's int32 table word
             descs[i] = qift_linear_desc(it["xq"].data_ptr(), it["s_a"].data_ptr(),
@@ -681,7 +702,7 @@ __all__ = ["load_library", "QiftUnavailable", "qift_quantize_weights", "qift_rot
            "qift_rotate_quant_act_batched", "RotateBatch", "qift_w2a4_linear", "qift_kv4_quant",
            "LinearGroup", "QiftError", "qift_linear_desc", "LEVELS", "status_string", "last_error",
            "abi_version", "code_words_per_row", "padded_channels", "LIB_PATH", "SCALE_RULES",
-           "level_table_word", "qift_kv4_attention_decode", "qift_kv4_attention_workspace_bytes",
+           "level_table_word", "scale_entries", "qift_kv4_attention_decode", "qift_kv4_attention_workspace_bytes",
            "qift_kv4_attention_decode_noalloc", "QIFT_ATTENTION_SCRATCH_BYTES",
            "qift_rotate_w2a4_linear",
            "qift_gptq_hessian", "qift_gptq_hessian_workspace_bytes", "qift_gptq_quantize_weights",

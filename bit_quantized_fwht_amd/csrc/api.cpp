@@ -43,7 +43,7 @@ bool is_pow2(int64_t v) { return v > 0 && (v & (v - 1)) == 0; }
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 bool valid_levels(int lv) {
   return lv == QIFT_LEVELS_MNZ || lv == QIFT_LEVELS_POT || lv == QIFT_LEVELS_INT4 ||
-         lv == QIFT_LEVELS_LUT;
+         lv == QIFT_LEVELS_LUT || lv == QIFT_LEVELS_ASYM;
 }
 
 // The table word of a call: a level table (four signed bytes, |L| <= 15, not
@@ -144,6 +144,8 @@ qift_status qift_quantize_weights_ex(const void* W, qift_dtype w_dtype, int64_t 
   if (tst != QIFT_OK) return tst;
   if (scale_rule != QIFT_SCALE_ABSMAX && scale_rule != QIFT_SCALE_MSE)
     return fail(QIFT_ERR_INVALID_ARG, "invalid scale_rule %d", (int)scale_rule);
+  if (levels == QIFT_LEVELS_ASYM && scale_rule != QIFT_SCALE_ABSMAX)
+    return fail(QIFT_ERR_INVALID_ARG, "the asymmetric grid takes its step from the range (ABSMAX)");
   if (N < 0) return fail(QIFT_ERR_INVALID_ARG, "negative N");
   if (K <= 0 || K % 64 != 0)
     return fail(QIFT_ERR_INVALID_ARG, "K=%lld must be a positive multiple of 64", (long long)K);
@@ -489,6 +491,8 @@ qift_status qift_gptq_quantize_weights(const void* W, qift_dtype w_dtype, int64_
   if (scale_dtype != QIFT_F32 && scale_dtype != QIFT_F16)
     return fail(QIFT_ERR_INVALID_ARG, "scale_dtype must be F32 or F16");
   if (!valid_levels(levels)) return fail(QIFT_ERR_INVALID_ARG, "invalid levels %d", (int)levels);
+  if (levels == QIFT_LEVELS_ASYM)
+    return fail(QIFT_ERR_INVALID_ARG, "error-compensated quantization takes the fixed level sets");
   qift_status tst = check_table((int)levels, level_table);
   if (tst != QIFT_OK) return tst;
   if (scale_rule != QIFT_SCALE_ABSMAX && scale_rule != QIFT_SCALE_MSE)
@@ -624,8 +628,9 @@ qift_status qift_w2a4_linear_grouped(const void* workspace, int64_t launch_tiles
 qift_status qift_measure_stream(const void* src, void* dst, int64_t bytes, int32_t mode,
                                 uint32_t* sink, qift_stream stream) {
   if (mode != 0 && mode != 1) return fail(QIFT_ERR_INVALID_ARG, "mode must be 0 or 1");
-  if (bytes <= 0 || bytes % 16 != 0)
-    return fail(QIFT_ERR_INVALID_ARG, "bytes=%lld must be a positive multiple of 16", (long long)bytes);
+  if (bytes <= 0 || bytes % 16 != 0 || bytes > (int64_t(1) << 40))
+    return fail(QIFT_ERR_INVALID_ARG, "bytes=%lld must be a positive multiple of 16, at most 2^40",
+                (long long)bytes);
   if (!src || !sink || (mode == 1 && !dst)) return fail(QIFT_ERR_INVALID_ARG, "null buffer");
   if (!aligned(src, 16) || (mode == 1 && !aligned(dst, 16)) || !aligned(sink, 4))
     return fail(QIFT_ERR_ALIGNMENT, "src and dst must be 16-byte aligned, sink 4-byte");

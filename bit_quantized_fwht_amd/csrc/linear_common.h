@@ -29,8 +29,9 @@ struct Fmt {
   __device__ static __forceinline__ int64_t code_words(int64_t K) { return kInt4 ? K / 8 : K / 16; }
 };
 
+// lut: the byte table of the lane's channel (level-table kernels only)
 template <int LV>
-__device__ __forceinline__ v4i weight_operand(const uint4& c, int step, OpConsts k) {
+__device__ __forceinline__ v4i weight_operand(const uint4& c, int step, OpConsts k, uint32_t lut) {
   if constexpr (LV == QIFT_LEVELS_INT4) {
     const uint32_t w0 = step == 0 ? c.x : c.z;
     const uint32_t w1 = step == 0 ? c.y : c.w;
@@ -38,8 +39,29 @@ __device__ __forceinline__ v4i weight_operand(const uint4& c, int step, OpConsts
   } else {
     const uint32_t w = step == 0 ? c.x : (step == 1 ? c.y : (step == 2 ? c.z : c.w));
     if constexpr (LV == QIFT_LEVELS_MNZ) return mnz_operand(w, k);
-    else if constexpr (LV == QIFT_LEVELS_LUT) return lut_operand(w, k.lut);
+    else if constexpr (LV == QIFT_LEVELS_LUT) return lut_operand(w, lut);
     else return pot_operand(w);
+  }
+}
+
+// Byte tables of the level-table kernels, one per 16-channel tile a lane
+// decodes (T tiles, the lane's channel of tile i being chan(i)): the call's
+// table for QIFT_LEVELS_LUT; for QIFT_LEVELS_ASYM the table of the lane's
+// channel, from its zero point, which follows the N steps in the scales
+// (channels past N read channel N - 1). Other kernels ignore them.
+template <int LV, int T, typename Chan>
+__device__ __forceinline__ void tile_tables(const qift_linear_desc& d, OpConsts k, int scale_f16,
+                                            Chan chan, uint32_t (&lut)[T]) {
+#pragma unroll
+  for (int i = 0; i < T; ++i) lut[i] = k.lut;
+  if constexpr (LV == QIFT_LEVELS_LUT) {
+    if (d.levels == QIFT_LEVELS_ASYM) {
+#pragma unroll
+      for (int i = 0; i < T; ++i) {
+        const int64_t n = chan(i) < d.N ? chan(i) : d.N - 1;
+        lut[i] = asym_table(load_scale_nb(d.scales, d.N + n, scale_f16));
+      }
+    }
   }
 }
 

@@ -55,6 +55,8 @@ __device__ __forceinline__ void decode_wave(const qift_linear_desc& d, int64_t n
   const uint32_t* codes = d.codes;
   const bool act_row = r16 < M;
   const OpConsts km = op_consts(d.reserved, lane);
+  uint32_t lut[kDecodeTiles];
+  tile_tables<LV>(d, km, scale_f16, [&](int i) { return n0 + 16 * i + r16; }, lut);
 
   v4i acc[kDecodeTiles];
 #pragma unroll
@@ -103,7 +105,7 @@ __device__ __forceinline__ void decode_wave(const qift_linear_desc& d, int64_t n
       const v4i A = act_operand(ch.a0, ch.a1, s, ch.am);
 #pragma unroll
       for (int i = 0; i < kDecodeTiles; ++i)
-        acc[i] = mfma16(A, weight_operand<LV>(ch.c[i], s, km), acc[i]);
+        acc[i] = mfma16(A, weight_operand<LV>(ch.c[i], s, km, lut[i]), acc[i]);
     }
   };
   // two chunks in flight: the loads of chunk t+1 are issued before chunk t
@@ -205,7 +207,8 @@ __device__ __forceinline__ void decode_dispatch(const qift_linear_desc& d, int64
   switch (d.levels) {
     case QIFT_LEVELS_MNZ: decode_wave<QIFT_LEVELS_MNZ>(d, n0, scale_f16, y_dtype, lane, epi); break;
     case QIFT_LEVELS_POT: decode_wave<QIFT_LEVELS_POT>(d, n0, scale_f16, y_dtype, lane, epi); break;
-    case QIFT_LEVELS_LUT: decode_wave<QIFT_LEVELS_LUT>(d, n0, scale_f16, y_dtype, lane, epi); break;
+    case QIFT_LEVELS_LUT:
+    case QIFT_LEVELS_ASYM: decode_wave<QIFT_LEVELS_LUT>(d, n0, scale_f16, y_dtype, lane, epi); break;
     default: decode_wave<QIFT_LEVELS_INT4>(d, n0, scale_f16, y_dtype, lane, epi); break;
   }
 }
@@ -278,6 +281,8 @@ __device__ __forceinline__ void decode_splitk_tiles(const qift_linear_desc& d, i
   const int64_t nchunks = (K + F::kChunkK - 1) / F::kChunkK;
   const bool act_row = r16 < M;
   const OpConsts km = op_consts(d.reserved, lane);
+  uint32_t lut[G];
+  tile_tables<LV>(d, km, scale_f16, [&](int i) { return (tn0 + i) * 16 + r16; }, lut);
   const int64_t t0 = wave;  // the wave's chunks are t0, t0 + S, ...
 
   // chunk t of the workgroup's tiles: the lane's 16-byte code unit of each
@@ -327,7 +332,7 @@ __device__ __forceinline__ void decode_splitk_tiles(const qift_linear_desc& d, i
     for (int s = 0; s < F::kSteps; ++s) {
       const v4i A = act_operand(a0, a1, s, ch.am);
 #pragma unroll
-      for (int i = 0; i < G; ++i) acc[i] = mfma16(A, weight_operand<LV>(ch.c[i], s, km), acc[i]);
+      for (int i = 0; i < G; ++i) acc[i] = mfma16(A, weight_operand<LV>(ch.c[i], s, km, lut[i]), acc[i]);
     }
   };
 
@@ -566,14 +571,16 @@ hipError_t launch_rotate_linear_decode(const qift_linear_desc& d, const void* X,
     switch (d.levels) {
       case QIFT_LEVELS_MNZ: return launch_rotate_linear_lv<QIFT_LEVELS_MNZ, uint16_t>(d, X, log2b, norm, scale_f16, y_dtype, s);
       case QIFT_LEVELS_POT: return launch_rotate_linear_lv<QIFT_LEVELS_POT, uint16_t>(d, X, log2b, norm, scale_f16, y_dtype, s);
-      case QIFT_LEVELS_LUT: return launch_rotate_linear_lv<QIFT_LEVELS_LUT, uint16_t>(d, X, log2b, norm, scale_f16, y_dtype, s);
+      case QIFT_LEVELS_LUT:
+      case QIFT_LEVELS_ASYM: return launch_rotate_linear_lv<QIFT_LEVELS_LUT, uint16_t>(d, X, log2b, norm, scale_f16, y_dtype, s);
       default: return launch_rotate_linear_lv<QIFT_LEVELS_INT4, uint16_t>(d, X, log2b, norm, scale_f16, y_dtype, s);
     }
   }
   switch (d.levels) {
     case QIFT_LEVELS_MNZ: return launch_rotate_linear_lv<QIFT_LEVELS_MNZ, float>(d, X, log2b, norm, scale_f16, y_dtype, s);
     case QIFT_LEVELS_POT: return launch_rotate_linear_lv<QIFT_LEVELS_POT, float>(d, X, log2b, norm, scale_f16, y_dtype, s);
-    case QIFT_LEVELS_LUT: return launch_rotate_linear_lv<QIFT_LEVELS_LUT, float>(d, X, log2b, norm, scale_f16, y_dtype, s);
+    case QIFT_LEVELS_LUT:
+    case QIFT_LEVELS_ASYM: return launch_rotate_linear_lv<QIFT_LEVELS_LUT, float>(d, X, log2b, norm, scale_f16, y_dtype, s);
     default: return launch_rotate_linear_lv<QIFT_LEVELS_INT4, float>(d, X, log2b, norm, scale_f16, y_dtype, s);
   }
 }
@@ -585,7 +592,8 @@ hipError_t launch_linear_decode(const qift_linear_desc& d, int scale_f16, int y_
     switch (d.levels) {
       case QIFT_LEVELS_MNZ: return launch_decode_splitk<QIFT_LEVELS_MNZ>(d, scale_f16, y_dtype, s);
       case QIFT_LEVELS_POT: return launch_decode_splitk<QIFT_LEVELS_POT>(d, scale_f16, y_dtype, s);
-      case QIFT_LEVELS_LUT: return launch_decode_splitk<QIFT_LEVELS_LUT>(d, scale_f16, y_dtype, s);
+      case QIFT_LEVELS_LUT:
+      case QIFT_LEVELS_ASYM: return launch_decode_splitk<QIFT_LEVELS_LUT>(d, scale_f16, y_dtype, s);
       default: return launch_decode_splitk<QIFT_LEVELS_INT4>(d, scale_f16, y_dtype, s);
     }
   }

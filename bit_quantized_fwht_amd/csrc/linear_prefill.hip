@@ -65,6 +65,8 @@ __device__ __forceinline__ void prefill_tile(const qift_linear_desc& d, int64_t 
   const int64_t tiles = (N + 15) >> 4;          // 16-channel weight tiles
   const int64_t arow = K / 2;                   // bytes per activation row
   const OpConsts km = op_consts(d.reserved, lane);
+  uint32_t lut[kWaveTN];
+  tile_tables<LV>(d, km, scale_f16, [&](int j) { return nt0 + wn + 16 * j + r16; }, lut);
   uint8_t* As = lds;                // stage buffer b: A at b * kStage, B after it
   uint8_t* Bs = lds + C::kBOffset;
 
@@ -136,7 +138,7 @@ __device__ __forceinline__ void prefill_tile(const qift_linear_desc& d, int64_t 
       }
 #pragma unroll
       for (int j = 0; j < kWaveTN; ++j) {
-        const v4i B = weight_operand<LV>(fb[j], s, km);
+        const v4i B = weight_operand<LV>(fb[j], s, km, lut[j]);
 #pragma unroll
         for (int i = 0; i < kWaveTM; ++i) acc[i][j] = mfma16(A[i], B, acc[i][j]);
       }
@@ -362,6 +364,8 @@ __device__ __forceinline__ void prefill_tile_sk(const qift_linear_desc& d, int64
   const int64_t arow = K / 2;
   const int64_t np16 = (N + 15) >> 4;
   const OpConsts km = op_consts(d.reserved, lane);
+  uint32_t lut[4];
+  tile_tables<LV>(d, km, scale_f16, [&](int j) { return nt0 + wn + 16 * j + r16; }, lut);
 
   int64_t a_off[C::kAInstr];
 #pragma unroll
@@ -436,7 +440,7 @@ __device__ __forceinline__ void prefill_tile_sk(const qift_linear_desc& d, int64
         else if constexpr (LV == QIFT_LEVELS_MNZ)
           B[j] = mnz_operand(s2 == 0 ? f.b[j].x : f.b[j].y, km);
         else if constexpr (LV == QIFT_LEVELS_LUT)
-          B[j] = lut_operand(s2 == 0 ? f.b[j].x : f.b[j].y, km.lut);
+          B[j] = lut_operand(s2 == 0 ? f.b[j].x : f.b[j].y, lut[j]);
         else
           B[j] = pot_operand(s2 == 0 ? f.b[j].x : f.b[j].y);
       }
@@ -586,7 +590,8 @@ hipError_t launch_linear_prefill(const qift_linear_desc& d, int scale_f16, int y
     switch (d.levels) {
       case QIFT_LEVELS_MNZ: QIFT_SK_LAUNCH(QIFT_LEVELS_MNZ) break;
       case QIFT_LEVELS_POT: QIFT_SK_LAUNCH(QIFT_LEVELS_POT) break;
-      case QIFT_LEVELS_LUT: QIFT_SK_LAUNCH(QIFT_LEVELS_LUT) break;
+      case QIFT_LEVELS_LUT:
+      case QIFT_LEVELS_ASYM: QIFT_SK_LAUNCH(QIFT_LEVELS_LUT) break;
       default: QIFT_SK_LAUNCH(QIFT_LEVELS_INT4) break;
     }
 #undef QIFT_SK_LAUNCH
@@ -599,6 +604,7 @@ hipError_t launch_linear_prefill(const qift_linear_desc& d, int scale_f16, int y
                          scale_f16, y_dtype);
       break;
     case QIFT_LEVELS_LUT:
+    case QIFT_LEVELS_ASYM:
       hipLaunchKernelGGL(linear_prefill_kernel<QIFT_LEVELS_LUT>, grid, dim3(256), 0, s, d,
                          scale_f16, y_dtype);
       break;

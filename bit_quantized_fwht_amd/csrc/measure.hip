@@ -7,32 +7,39 @@ namespace qift {
 
 // MODE 0: read-only stream (every 16-byte unit loaded once and folded into
 // one value per thread, stored only if it equals an impossible pattern);
-// MODE 1: copy src -> dst. Grid-stride over 16-byte units, four per thread in
-// flight; the rounds where all four are in range run without bounds checks.
+// MODE 1: copy src -> dst. Workgroup b owns the contiguous units
+// [b * kUnitsPerGroup, (b + 1) * kUnitsPerGroup) (64 KB), its threads four
+// loads in flight each, non-temporal loads and stores; the rounds where all
+// four are in range run without bounds checks. (Measured on MI355X: this
+// blocked order reads about 15% faster than a grid-stride walk of the same
+// loads, and non-temporal loads about 10% faster than plain ones.)
+constexpr int64_t kUnitsPerGroup = 4096;
+
 template <int MODE>
 __global__ __launch_bounds__(256) void measure_stream_kernel(const v4u* __restrict__ src,
                                                              v4u* __restrict__ dst, int64_t n16,
                                                              uint32_t* __restrict__ sink) {
-  const int64_t stride = (int64_t)gridDim.x * 256;
-  int64_t base = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t lo = (int64_t)blockIdx.x * kUnitsPerGroup;
+  const int64_t hi = lo + kUnitsPerGroup < n16 ? lo + kUnitsPerGroup : n16;
+  int64_t i = lo + threadIdx.x;
   uint32_t acc = 0;
-  for (; base + 3 * stride < n16; base += 4 * stride) {
+  for (; i + 3 * 256 < hi; i += 4 * 256) {
     v4u v[4];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) v[u] = __builtin_nontemporal_load(as_global(src + base + u * stride));
+    for (int u = 0; u < 4; ++u) v[u] = __builtin_nontemporal_load(as_global(src + i + 256 * u));
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       if constexpr (MODE == 1) {
-        __builtin_nontemporal_store(v[u], as_global_out(dst + base + u * stride));
+        __builtin_nontemporal_store(v[u], as_global_out(dst + i + 256 * u));
       } else {
         acc ^= v[u][0] ^ v[u][1] ^ v[u][2] ^ v[u][3];
       }
     }
   }
-  for (; base < n16; base += stride) {
-    const v4u v = __builtin_nontemporal_load(as_global(src + base));
+  for (; i < hi; i += 256) {
+    const v4u v = __builtin_nontemporal_load(as_global(src + i));
     if constexpr (MODE == 1) {
-      __builtin_nontemporal_store(v, as_global_out(dst + base));
+      __builtin_nontemporal_store(v, as_global_out(dst + i));
     } else {
       acc ^= v[0] ^ v[1] ^ v[2] ^ v[3];
     }
@@ -84,8 +91,7 @@ __global__ __launch_bounds__(256) void measure_mfma_i8_kernel(int iters, uint32_
 hipError_t launch_measure_stream(const void* src, void* dst, int64_t bytes, int mode,
                                  uint32_t* sink, hipStream_t s) {
   const int64_t n16 = bytes / 16;
-  const int64_t blocks = (n16 + 256 * 4 - 1) / (256 * 4);
-  const unsigned grid = (unsigned)(blocks < 8192 ? blocks : 8192);
+  const unsigned grid = (unsigned)((n16 + kUnitsPerGroup - 1) / kUnitsPerGroup);
   if (mode == 1) {
     hipLaunchKernelGGL(measure_stream_kernel<1>, dim3(grid), dim3(256), 0, s,
                        reinterpret_cast<const v4u*>(src), reinterpret_cast<v4u*>(dst), n16, sink);

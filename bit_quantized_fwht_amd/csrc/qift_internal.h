@@ -178,6 +178,18 @@ __device__ __forceinline__ v4i lut_operand(uint32_t c, uint32_t lut) {
   return b;
 }
 
+// Byte table of one channel of the asymmetric grid (QIFT_LEVELS_ASYM):
+// byte c = 8 * (c - z), z the channel's zero point (an integer in [0, 3],
+// stored as a scale value; anything else is clamped, NaN reads as 0). The
+// four bytes are the window of the sequence 8 * (-3, -2, ..., 3) that starts
+// at 3 - z. The table then drives the level-table decode, lut_operand, so the
+// grid costs the matrix-core loop nothing: the zero point is folded into the
+// decoded levels instead of a correction z * sum q after the sum.
+__device__ __forceinline__ uint32_t asym_table(float zf) {
+  const int z = zf >= 3.f ? 3 : zf >= 2.f ? 2 : zf >= 1.f ? 1 : 0;
+  return (uint32_t)(0x0018100800F8F0E8ull >> (8 * (3 - z)));
+}
+
 // Right shift that turns the matrix-core sum back into sum q * level:
 // MNZ 16 * 32 = 2^9, PoT 16 * 16 = 2^8, INT4 16 * 16 = 2^8, level table
 // 16 * 8 = 2^7.

@@ -210,6 +210,32 @@ __global__ __launch_bounds__(kRowThreads) void quantize_weights_kernel(
   load_row<T>(W + n * K, row, K, tid);
   __syncthreads();
   fwht_row(row, K, log2b, tid);
+  if (levels == QIFT_LEVELS_ASYM) {
+    // the conventional min-max grid with a zero point: step (hi - lo) / 3 of
+    // the range widened to contain 0, zero point rint(-lo / s) in [0, 3]
+    // (both with the stored step), stored after the N steps
+    float lo, hi;
+    row_range0(row, K, norm, tid, red, lo, hi);
+    const float s32 = __fdiv_rn(__fsub_rn(hi, lo), 3.f);
+    const float s = stored_scale(s32, scale_f16);
+    const float z = s == 0.f ? 0.f : fminf(fmaxf(rintf(__fdiv_rn(-lo, s)), 0.f), 3.f);
+    if (tid == 0) {
+      if (scale_f16) {
+        reinterpret_cast<__half*>(scales)[n] = __float2half_rn(s32);
+        reinterpret_cast<__half*>(scales)[N + n] = __float2half_rn(z);
+      } else {
+        reinterpret_cast<float*>(scales)[n] = s32;
+        reinterpret_cast<float*>(scales)[N + n] = z;
+      }
+    }
+    for (int g = tid; g < (K >> 4); g += kRowThreads) {
+      uint32_t word = 0;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) word |= code_asym(row[16 * g + i] * norm, s, z) << code_bit_offset(i);
+      codes[tiled_word(n, g, words, tiles)] = word;
+    }
+    return;
+  }
   const float s32 =
       choose_scale(row, K, norm, levels, table, pref, outer, mse_rule, scale_f16, red, red64);
   const float s = stored_scale(s32, scale_f16);

@@ -27,6 +27,40 @@ __device__ __forceinline__ float row_absmax(const float* row, int K, float norm,
   return r;
 }
 
+// Largest v over the workgroup (every thread gets the result).
+__device__ __forceinline__ float block_max(float v, int tid, float* red) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
+  if ((tid & 63) == 0) red[tid >> 6] = v;
+  __syncthreads();
+  float r = red[0];
+#pragma unroll
+  for (int w = 1; w < kRowThreads / 64; ++w) r = fmaxf(r, red[w]);
+  __syncthreads();
+  return r;
+}
+
+// Range of the row (value i = row[i] * norm) widened to contain 0:
+// lo = min(min v, 0), hi = max(max v, 0) (every thread gets both).
+__device__ __forceinline__ void row_range0(const float* row, int K, float norm, int tid,
+                                           float* red, float& lo, float& hi) {
+  float mn = 0.f, mx = 0.f;
+  for (int i = tid; i < K; i += kRowThreads) {
+    mn = fminf(mn, row[i]);
+    mx = fmaxf(mx, row[i]);
+  }
+  // rounding is monotonic: min(v) * norm == min(v * norm), likewise max
+  hi = block_max(mx * norm, tid, red);
+  lo = -block_max(-(mn * norm), tid, red);
+}
+
+// Code of the asymmetric min-max grid: clip(rint(w / s) + z, 0, 3) in
+// float32 (z the zero point as a float); 0 when s = 0.
+__device__ __forceinline__ uint32_t code_asym(float w, float s, float z) {
+  if (s == 0.f) return 0u;
+  return (uint32_t)fminf(fmaxf(rintf(__fdiv_rn(w, s)) + z, 0.f), 3.f);
+}
+
 __device__ __forceinline__ int quant_int4(float x, float s) {
   if (s == 0.f) return 0;
   float q = rintf(__fdiv_rn(x, s));

@@ -68,6 +68,14 @@
  *                     integer level L[c] in [-15, 15] of code c (not all
  *                     zero); weight = L[c] * s. {1, 3, -3, -1} decodes MNZ
  *                     codes at step s/2, {1, 4, -1, -4} PoT codes.
+ *   QIFT_LEVELS_ASYM: the conventional asymmetric two-bit grid with a zero
+ *                     point, the baseline the abstract compares with: the
+ *                     code read as an unsigned integer c in {0,1,2,3} and
+ *                     the channel's integer zero point z_n in {0,1,2,3} give
+ *                     weight = (c - z_n) * s_n. Its scales buffer holds 2N
+ *                     values of the scale dtype: s_0 .. s_{N-1}, then
+ *                     z_0 .. z_{N-1} (a zero point outside {0,1,2,3} is
+ *                     clamped into it, a fractional one truncated).
  *
  * Hadamard rotation
  * -----------------
@@ -86,7 +94,7 @@
 extern "C" {
 #endif
 
-#define QIFT_ABI_VERSION 6
+#define QIFT_ABI_VERSION 7
 
 typedef enum {
   QIFT_OK = 0,
@@ -102,7 +110,8 @@ typedef enum {
   QIFT_LEVELS_MNZ = 0,  /* {+-0.5, +-1.5} * s, 2-bit codes              */
   QIFT_LEVELS_POT = 1,  /* {+-1, +-4} * s, 2-bit codes, sign-and-shift  */
   QIFT_LEVELS_INT4 = 2, /* [-7, 7] * s, 4-bit codes                     */
-  QIFT_LEVELS_LUT = 3   /* table[code] * s, 2-bit codes (level table)   */
+  QIFT_LEVELS_LUT = 3,  /* table[code] * s, 2-bit codes (level table)   */
+  QIFT_LEVELS_ASYM = 4  /* (c - z_n) * s, 2-bit codes, zero point z_n   */
 } qift_levels;
 
 /* Per-channel scale rule of the weight quantizer. */
@@ -137,7 +146,8 @@ typedef void* qift_stream; /* a hipStream_t */
  *   codes   out: Np*K/16 uint32 (MNZ, POT) or Np*K/8 uint32 (INT4), tiled
  *           layout, Np = ceil(N/16)*16 (padding channels are written as 0);
  *           16-byte aligned
- *   scales  out: [N] float32 (QIFT_F32) or float16 (QIFT_F16)
+ *   scales  out: [N] float32 (QIFT_F32) or float16 (QIFT_F16); [2N] for
+ *           QIFT_LEVELS_ASYM (the steps, then the zero points)
  * N = 0 is a no-op.
  */
 qift_status qift_quantize_weights(const void* W, qift_dtype w_dtype, int64_t N, int64_t K,
@@ -165,7 +175,15 @@ qift_status qift_quantize_weights(const void* W, qift_dtype w_dtype, int64_t N, 
  *                differ in the last bits).
  * LUT codes: the level nearest to w' (distances |w' - L[c] * s| in float64),
  * ties to the smaller |L[c]|, then the non-negative level, then the lower
- * code. Other arguments, layouts and errors as qift_quantize_weights.
+ * code.
+ * QIFT_LEVELS_ASYM (the min-max grid; scale_rule must be QIFT_SCALE_ABSMAX,
+ * else QIFT_ERR_INVALID_ARG): over the rotated float32 row,
+ *   lo = min(min w', 0), hi = max(max w', 0), s = fl32(fl32(hi - lo) / 3)
+ *   rounded to scale_dtype, z = clamp(rint(fl32(-lo / s)), 0, 3),
+ *   c = clamp(rint(fl32(w' / s)) + z, 0, 3)
+ * (IEEE float32 division, round half to even, the stored s); s = 0 gives
+ * z = 0 and c = 0. scales receives s_n at n and z_n at N + n.
+ * Other arguments, layouts and errors as qift_quantize_weights.
  */
 qift_status qift_quantize_weights_ex(const void* W, qift_dtype w_dtype, int64_t N, int64_t K,
                                      int32_t had_block, qift_levels levels, uint32_t level_table,
@@ -232,6 +250,9 @@ qift_status qift_rotate_quant_act_batched(const qift_rotate_desc* descs, int32_t
  *   Y[m, n]   = acc[m, n] * s_a[m] * s_w[n] * kappa    (float32)
  * with level the integer level of the code (half-scale for MNZ) and
  * kappa = 1/2 for MNZ, 1 for POT and INT4. y_dtype QIFT_I32 stores acc itself.
+ * (QIFT_LEVELS_ASYM, through qift_w2a4_linear_ex: level = c - z_n and
+ * kappa = 1, i.e. acc = sum q c - z_n sum q; scales holds the 2N steps and
+ * zero points.)
  * M <= 16 runs the weight-streaming decode kernel, M > 16 the matrix-core
  * prefill kernel; both give identical results.
  *
@@ -239,7 +260,7 @@ qift_status qift_rotate_quant_act_batched(const qift_rotate_desc* descs, int32_t
  *   K         multiple of 64, K <= 65536
  *   codes     Np*K/16 (2-bit) or Np*K/8 (INT4) uint32 in the tiled layout
  *             written by qift_quantize_weights; 16-byte aligned
- *   scales    [N] float32 or float16 (scale_dtype)
+ *   scales    [N] float32 or float16 (scale_dtype); [2N] for QIFT_LEVELS_ASYM
  *   Y         out: [M, N] float32, bfloat16 or int32 (y_dtype)
  *   xq must be 16-byte aligned.
  * M = 0 or N = 0 is a no-op.
@@ -377,8 +398,9 @@ qift_status qift_kv4_attention_decode_noalloc(const void* q, qift_dtype q_dtype,
  * accumulate = 0 writes H = 0).
  *
  * qift_gptq_quantize_weights -- codes and scales of W [N, K] in the layout of
- * qift_quantize_weights_ex (same levels, level_table, scale_rule, scale_dtype
- * and limits; the result feeds qift_w2a4_linear unchanged):
+ * qift_quantize_weights_ex (same levels except QIFT_LEVELS_ASYM, which is
+ * QIFT_ERR_INVALID_ARG here; same level_table, scale_rule, scale_dtype and
+ * limits; the result feeds qift_w2a4_linear unchanged):
  *   1. W' = W rotated (float64 butterflies), rounded to float32;
  *   2. s_n by scale_rule from the rows of W' (the plain quantizer's scales);
  *   3. a feature k with H[k][k] = 0 gets H[k][k] = 1 and weight 0; then

@@ -22,13 +22,13 @@ extern "C" {
  * and the matrix-core results live. */
 #define QIFT_MEASURE_SINK_WORDS 8192
 
-/* Streams `bytes` bytes (a positive multiple of 16) of src through the
- * vector memory path with non-temporal loads, four 16-byte loads in flight
- * per thread, at most 8192 workgroups of 256 threads striding over the
- * buffer. mode 0: read only (the HBM read rate: bytes / duration); mode 1:
- * copy to dst (2 * bytes / duration; dst must not overlap src). src and dst
- * 16-byte aligned; dst may be NULL in mode 0. sink: QIFT_MEASURE_SINK_WORDS
- * uint32. */
+/* Streams `bytes` bytes (a positive multiple of 16, at most 2^40) of src
+ * through the vector memory path: workgroup b of 256 threads owns the 64 KB
+ * at b * 65536, four non-temporal 16-byte loads in flight per thread.
+ * mode 0: read only (the HBM read rate: bytes / duration); mode 1: copy to
+ * dst with non-temporal stores (2 * bytes / duration; dst must not overlap
+ * src). src and dst 16-byte aligned; dst may be NULL in mode 0. sink:
+ * QIFT_MEASURE_SINK_WORDS uint32. */
 qift_status qift_measure_stream(const void* src, void* dst, int64_t bytes, int32_t mode,
                                 uint32_t* sink, qift_stream stream);
 

@@ -36,7 +36,7 @@ def test_library_loads_and_exports_every_declared_symbol():
     assert len(names) == 21, names
     for n in names:
         assert hasattr(lib, n), n
-    assert q.abi_version() == 6
+    assert q.abi_version() == 7
     for s in range(5):
         assert q.status_string(s).startswith("QIFT_")
 
@@ -53,6 +53,7 @@ def test_measurement_calls_exported_and_validated():
     assert ms(A16, A16b, 1024, 2, A16c, None) == q.QIFT_ERR_INVALID_ARG     # mode
     assert ms(A16, A16b, 1000, 1, A16c, None) == q.QIFT_ERR_INVALID_ARG     # not a multiple of 16
     assert ms(A16, A16b, 0, 0, A16c, None) == q.QIFT_ERR_INVALID_ARG
+    assert ms(A16, A16b, (1 << 40) + 16, 0, A16c, None) == q.QIFT_ERR_INVALID_ARG
     assert ms(None, A16b, 1024, 0, A16c, None) == q.QIFT_ERR_INVALID_ARG
     assert ms(A16, None, 1024, 1, A16c, None) == q.QIFT_ERR_INVALID_ARG     # copy needs dst
     assert ms(A16, A16b, 1024, 0, None, None) == q.QIFT_ERR_INVALID_ARG     # sink
@@ -242,6 +243,28 @@ def test_linear_ex_table_rules(table, lv, status):
     assert lin_ex(table, lv=lv, M=0) == status
 
 
+def test_linear_accepts_asym_and_rejects_a_table_with_it():
+    assert lin(lv=4, M=0) == q.QIFT_OK
+    assert q._C.qift_w2a4_linear_ex(A16, A16b, 0, 256, A16c, A16d, q.QIFT_F16, 4,
+                                    q.level_table_word((0, 1, 2, 3)), 64, A16e, q.QIFT_F32,
+                                    None) == q.QIFT_ERR_INVALID_ARG
+
+
+def test_asym_buffer_sizes_in_the_binding():
+    import torch
+    assert q.scale_entries(40, "asym") == 80 and q.scale_entries(40, "mnz") == 40
+    assert q.default_channels(torch.empty((2, 40)), "asym") == 40
+    assert q.default_channels(torch.empty((80,)), "asym") == 40
+    bufs = dict(xq=torch.empty((1, 128), dtype=torch.uint8), s_a=torch.empty((1,)),
+                codes=torch.empty((48, 16), dtype=torch.int32),
+                scales=torch.empty((40,), dtype=torch.float16),
+                Y=torch.empty((1, 40)))
+    with pytest.raises(ValueError, match="80"):
+        q._check_linear_buffers(bufs, 40, "asym", placement=False)
+    bufs["scales"] = torch.empty((2, 40), dtype=torch.float16)
+    assert q._check_linear_buffers(bufs, 40, "asym", placement=False) == (1, 256)
+
+
 def test_linear_without_table_rejects_lut():
     assert lin(lv=3, M=0) == q.QIFT_ERR_INVALID_ARG
     assert "table" in q.last_error()
@@ -263,6 +286,10 @@ def qw_ex(table, lv, rule, **kw):
     (0, 3, 0, q.QIFT_ERR_INVALID_ARG),
     (q.level_table_word((1, 4, -1, -4)), 1, 0, q.QIFT_ERR_INVALID_ARG),
     (0, 0, 2, q.QIFT_ERR_INVALID_ARG),
+    (0, 4, 0, q.QIFT_OK),                                  # asymmetric min-max grid
+    (0, 4, 1, q.QIFT_ERR_INVALID_ARG),                     # ... takes no searched scale
+    (q.level_table_word((0, 1, 2, 3)), 4, 0, q.QIFT_ERR_INVALID_ARG),  # ... nor a table
+    (0, 5, 0, q.QIFT_ERR_INVALID_ARG),
 ])
 def test_quantize_weights_ex_rules(table, lv, rule, status):
     assert qw_ex(table, lv, rule) == status
@@ -413,6 +440,7 @@ def gq(**kw):
     (dict(damp=float("inf")), q.QIFT_ERR_INVALID_ARG),
     (dict(lv=9), q.QIFT_ERR_INVALID_ARG),
     (dict(lv=3, table=0), q.QIFT_ERR_INVALID_ARG),
+    (dict(lv=4), q.QIFT_ERR_INVALID_ARG),      # the asymmetric grid: plain quantizer only
     (dict(table=5), q.QIFT_ERR_INVALID_ARG),
     (dict(rule=7), q.QIFT_ERR_INVALID_ARG),
     (dict(sd=q.QIFT_BF16), q.QIFT_ERR_INVALID_ARG),
