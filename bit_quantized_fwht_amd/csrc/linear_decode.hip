@@ -339,9 +339,12 @@ __device__ __forceinline__ void decode_splitk_tiles(const qift_linear_desc& d, i
   // the activation row's loads first (fused): the rotation can start on
   // them while the weight stream is still arriving (the scheduling barriers
   // keep the issue order: row, weights, scales)
-  uint32_t xraw[RowGroups<kFused ? NT : kRowThreads>::kQ][16];
+  // (one group of 16 elements per thread covers the row: 8 waves take rows of
+  // at most 16 chunks, K <= 4096, and 16 waves any K up to 16384)
+  static_assert(16 * NT >= (S == 16 ? QIFT_MAX_ROW : 16 * F::kChunkK), "one group per thread");
+  uint32_t xraw[1][16];
   if constexpr (kFused) {
-    rotate_row_load<XT, NT>(reinterpret_cast<const XT*>(fr.X), (int)K, xraw);
+    rotate_row_load<XT, NT, 1>(reinterpret_cast<const XT*>(fr.X), (int)K, xraw);
     __builtin_amdgcn_sched_barrier(0);
   }
 
@@ -373,7 +376,7 @@ __device__ __forceinline__ void decode_splitk_tiles(const qift_linear_desc& d, i
 
   if constexpr (kFused) {
     __builtin_amdgcn_sched_barrier(0);
-    rotate_row_finish<XT, NT>(xraw, (int)K, fr.log2b, fr.norm, fr.xq, fr.s, nullptr, fr.row,
+    rotate_row_finish<XT, NT, 1>(xraw, (int)K, fr.log2b, fr.norm, fr.xq, fr.s, nullptr, fr.row,
                               fr.red);
     lds_barrier();  // the row's codes and scale, for every wave; the weights stay in flight
     sa = *fr.s;
@@ -556,6 +559,7 @@ hipError_t launch_rotate_linear_lv(const qift_linear_desc& d, const void* X, int
   // 4096 -> 22016 10.0 us (G = 4), 11008 -> 4096 7.4 us
   using F = Fmt<LV>;
   const int64_t nchunks = (d.K + F::kChunkK - 1) / F::kChunkK;
+  // (8 waves hold one 16-element group of the row per thread up to 16 chunks)
   if (nchunks <= 16) return launch_rotate_linear_s<LV, 8, XT>(d, X, log2b, norm, scale_f16, y_dtype, s);
   return launch_rotate_linear_s<LV, 16, XT>(d, X, log2b, norm, scale_f16, y_dtype, s);
 }

@@ -147,17 +147,19 @@ __global__ __launch_bounds__(kRowThreads) void rotate_quant_act_kernel(
   }
 }
 
-// The fast path (rotate_row_fast) lives in rotate_row.h.
+// The fast path (rotate_row_fast) lives in rotate_row.h. Q: groups of 16
+// elements per thread, the fewest that cover the row (K <= 4096 Q), which
+// sizes the registers and so the number of resident workgroups.
 
-template <typename T>
+template <typename T, int Q>
 __global__ __launch_bounds__(kRowThreads) void rotate_quant_act_fast_kernel(
     const T* __restrict__ X, int K, int log2b, float norm, uint8_t* __restrict__ xq,
     float* __restrict__ s_a, float* __restrict__ x_rot) {
   extern __shared__ float row[];
   __shared__ float red[kRowThreads / 64];
   const int64_t m = blockIdx.x;
-  rotate_row_fast<T>(X + m * K, K, log2b, norm, xq + m * (int64_t)(K / 2), s_a + m,
-                     x_rot ? x_rot + m * K : nullptr, row, red);
+  rotate_row_fast<T, kRowThreads, Q>(X + m * K, K, log2b, norm, xq + m * (int64_t)(K / 2),
+                                     s_a + m, x_rot ? x_rot + m * K : nullptr, row, red);
 }
 
 // Several activation matrices in one launch (workgroup b covers row b of the
@@ -283,13 +285,23 @@ hipError_t launch_rotate_quant_act(const void* X, int x_bf16, int64_t M, int64_t
   const float nrm = had_norm(had_block);
   if (rotate_fast_ok(X, K, had_block, xq, x_rot)) {
     const size_t lds = lb > kRegLog2B ? (size_t)(K + K / 16) * sizeof(float) : 0;
-    if (x_bf16)
-      hipLaunchKernelGGL(rotate_quant_act_fast_kernel<uint16_t>, dim3((unsigned)M),
-                         dim3(kRowThreads), lds, s, reinterpret_cast<const uint16_t*>(X), (int)K,
-                         lb, nrm, xq, s_a, x_rot);
-    else
-      hipLaunchKernelGGL(rotate_quant_act_fast_kernel<float>, dim3((unsigned)M), dim3(kRowThreads),
-                         lds, s, reinterpret_cast<const float*>(X), (int)K, lb, nrm, xq, s_a, x_rot);
+    const int groups = (int)((K / 16 + kRowThreads - 1) / kRowThreads);  // per thread, 1..4
+#define QIFT_ROT_FAST(TT, QQ)                                                                \
+  hipLaunchKernelGGL((rotate_quant_act_fast_kernel<TT, QQ>), dim3((unsigned)M),             \
+                     dim3(kRowThreads), lds, s, reinterpret_cast<const TT*>(X), (int)K, lb, nrm, \
+                     xq, s_a, x_rot)
+    if (x_bf16) {
+      if (groups == 1) QIFT_ROT_FAST(uint16_t, 1);
+      else if (groups == 2) QIFT_ROT_FAST(uint16_t, 2);
+      else if (groups == 3) QIFT_ROT_FAST(uint16_t, 3);
+      else QIFT_ROT_FAST(uint16_t, 4);
+    } else {
+      if (groups == 1) QIFT_ROT_FAST(float, 1);
+      else if (groups == 2) QIFT_ROT_FAST(float, 2);
+      else if (groups == 3) QIFT_ROT_FAST(float, 3);
+      else QIFT_ROT_FAST(float, 4);
+    }
+#undef QIFT_ROT_FAST
     return hipGetLastError();
   }
   const size_t lds = (size_t)K * sizeof(float);

@@ -33,13 +33,19 @@ __device__ __forceinline__ void fwht_pass_padded(float* row, int K, int p, int t
   const int sh = 4 * p;
   const int S = 1 << sh;
   const int groups = K >> NS;
+  // for S >= 16 the padded index is affine in j: low + j S stays below
+  // 2^(sh + NS) and j S is a multiple of 16, so pad16(base + j S) =
+  // pad16(base) + j (S + S / 16), one base address and immediate offsets
+  const int pstride = S >= 16 ? S + (S >> 4) : 0;
   for (int grp = tid; grp < groups; grp += NT) {
     const int low = grp & (S - 1);
     const int high = grp >> sh;
     const int base = (high << (sh + NS)) | low;
+    float* const rb = row + pad16(base);
+    auto at = [&](int j) -> float& { return S >= 16 ? rb[j * pstride] : row[pad16(base + j * S)]; };
     float v[R];
 #pragma unroll
-    for (int j = 0; j < R; ++j) v[j] = row[pad16(base + j * S)];
+    for (int j = 0; j < R; ++j) v[j] = at(j);
 #pragma unroll
     for (int st = 0; st < NS; ++st) {
       const int h = 1 << st;
@@ -53,7 +59,7 @@ __device__ __forceinline__ void fwht_pass_padded(float* row, int K, int p, int t
       }
     }
 #pragma unroll
-    for (int j = 0; j < R; ++j) row[pad16(base + j * S)] = v[j];
+    for (int j = 0; j < R; ++j) at(j) = v[j];
     if constexpr (kMax) {
 #pragma unroll
       for (int j = 0; j < R; ++j) *m = fmaxf(*m, fabsf(v[j]));
@@ -123,7 +129,12 @@ static_assert(kFastMaxGroups * 16 * kRowThreads >= QIFT_MAX_ROW, "fast path cove
 // rows with log2(block) <= kRegLog2B need no LDS row buffer
 constexpr int kRegLog2B = 8;
 
-// groups of 16 elements a thread holds for a workgroup of NT threads
+// groups of 16 elements a thread holds for a workgroup of NT threads: enough
+// for the longest row (QIFT_MAX_ROW), or Q when the caller knows its rows
+// are shorter (K <= 16 Q NT). The registers are sized by it: at
+// K = 4096 one group per thread keeps a 256-thread rotation at about 40
+// VGPRs, so all eight of its workgroups per CU are resident at once (four
+// groups need about 110 and allow half of them).
 template <int NT>
 struct RowGroups {
   static constexpr int kQ = (kFastMaxGroups * kRowThreads + NT - 1) / NT;
@@ -131,26 +142,26 @@ struct RowGroups {
 
 // 1. loads (a group past the row end reads group 0 and is discarded), as raw
 // words; rotate_row_finish widens and transforms them
-template <typename T, int NT>
+template <typename T, int NT, int Q = RowGroups<NT>::kQ>
 __device__ __forceinline__ void rotate_row_load(const T* __restrict__ src, int K,
-                                                uint32_t raw[RowGroups<NT>::kQ][16]) {
+                                                uint32_t raw[Q][16]) {
   const int tid = threadIdx.x;
   const int groups = K >> 4;
 #pragma unroll
-  for (int q = 0; q < RowGroups<NT>::kQ; ++q) {
+  for (int q = 0; q < Q; ++q) {
     const int grp = tid + q * NT;
     load16_raw<T>(src + 16 * (grp < groups ? grp : 0), raw[q]);
   }
 }
 
-template <typename T, int NT>
-__device__ __forceinline__ void rotate_row_finish(const uint32_t raw[RowGroups<NT>::kQ][16],
+template <typename T, int NT, int Q = RowGroups<NT>::kQ>
+__device__ __forceinline__ void rotate_row_finish(const uint32_t raw[Q][16],
                                                   int K, int log2b, float norm,
                                                   uint8_t* __restrict__ xq_row,
                                                   float* __restrict__ s_out,
                                                   float* __restrict__ xrot_row, float* row,
                                                   float* red) {
-  constexpr int kQ = RowGroups<NT>::kQ;  // groups per thread
+  constexpr int kQ = Q;  // groups per thread
   float v[kQ][16];
 #pragma unroll
   for (int q = 0; q < kQ; ++q) widen16<T>(raw[q], v[q]);
@@ -283,15 +294,15 @@ __device__ __forceinline__ void rotate_row_finish(const uint32_t raw[RowGroups<N
   }
 }
 
-template <typename T, int NT = kRowThreads>
+template <typename T, int NT = kRowThreads, int Q = RowGroups<NT>::kQ>
 __device__ __forceinline__ void rotate_row_fast(const T* __restrict__ src, int K, int log2b,
                                                 float norm, uint8_t* __restrict__ xq_row,
                                                 float* __restrict__ s_out,
                                                 float* __restrict__ xrot_row, float* row,
                                                 float* red) {
-  uint32_t raw[RowGroups<NT>::kQ][16];
-  rotate_row_load<T, NT>(src, K, raw);
-  rotate_row_finish<T, NT>(raw, K, log2b, norm, xq_row, s_out, xrot_row, row, red);
+  uint32_t raw[Q][16];
+  rotate_row_load<T, NT, Q>(src, K, raw);
+  rotate_row_finish<T, NT, Q>(raw, K, log2b, norm, xq_row, s_out, xrot_row, row, red);
 }
 
 }  // namespace qift
