@@ -353,7 +353,10 @@ __device__ __forceinline__ void decode_splitk_tiles(const qift_linear_desc& d, i
   // requests its whole weight stream at the start; longer K repeats this in
   // groups. The first group is loaded without branches (clamped), so
   // nothing makes the compiler wait for it before the rotation.
-  constexpr int NC = 4 / G;
+  // (16 waves: 4 / G units, which keeps them within their registers; 8
+  // waves: at least two chunks in flight however many tiles)
+  constexpr int NC = S == 16 ? 4 / G : (4 / G > 2 ? 4 / G : 2);
+  static_assert(NC >= 1, "at least one chunk per wave in flight");
   Chunk buf[NC];
 #pragma unroll
   for (int c = 0; c < NC; ++c) load(buf[c], t0 + c * S);
@@ -532,22 +535,34 @@ hipError_t launch_decode_splitk(const qift_linear_desc& d, int scale_f16, int y_
 template <int LV, int S, typename XT>
 hipError_t launch_rotate_linear_s(const qift_linear_desc& d, const void* X, int log2b, float norm,
                                   int scale_f16, int y_dtype, hipStream_t s) {
-  // every workgroup rotates the row again: about one workgroup per CU
+  // every workgroup rotates the row again: about one workgroup per CU, so G
+  // is the smallest tile count per workgroup that keeps the grid within 256
+  // workgroups (8 waves: 1, 2, 3, 4 or 6 tiles; 16 waves: 1, 2 or 4)
   const int64_t tiles = (d.N + 15) / 16;
-  int G = 1;
-  while (G < 4 && (tiles + G - 1) / G > 256) G *= 2;
+  static constexpr int kG8[] = {1, 2, 3, 4, 6};
+  static constexpr int kG16[] = {1, 2, 4};
+  const int* gs = S == 16 ? kG16 : kG8;
+  const int ng = S == 16 ? 3 : 5;
+  int G = gs[ng - 1];
+  for (int i = 0; i < ng; ++i)
+    if ((tiles + gs[i] - 1) / gs[i] <= 256) {
+      G = gs[i];
+      break;
+    }
   const dim3 grid((unsigned)((tiles + G - 1) / G));
   const size_t lds = log2b > kRegLog2B ? (size_t)(d.K + d.K / 16) * sizeof(float) : 0;
   const XT* x = reinterpret_cast<const XT*>(X);
-  if (G == 1)
-    hipLaunchKernelGGL((rotate_linear_decode_kernel<LV, S, 1, XT>), grid, dim3(64 * S), lds, s, d,
-                       x, log2b, norm, scale_f16, y_dtype);
-  else if (G == 2)
-    hipLaunchKernelGGL((rotate_linear_decode_kernel<LV, S, 2, XT>), grid, dim3(64 * S), lds, s, d,
-                       x, log2b, norm, scale_f16, y_dtype);
-  else
-    hipLaunchKernelGGL((rotate_linear_decode_kernel<LV, S, 4, XT>), grid, dim3(64 * S), lds, s, d,
-                       x, log2b, norm, scale_f16, y_dtype);
+#define QIFT_ROT_LIN(GG)                                                                    \
+  hipLaunchKernelGGL((rotate_linear_decode_kernel<LV, S, GG, XT>), grid, dim3(64 * S), lds, s, \
+                     d, x, log2b, norm, scale_f16, y_dtype)
+  if (G == 1) QIFT_ROT_LIN(1);
+  else if (G == 2) QIFT_ROT_LIN(2);
+  else if (G == 4) QIFT_ROT_LIN(4);
+  else if constexpr (S == 8) {
+    if (G == 3) QIFT_ROT_LIN(3);
+    else QIFT_ROT_LIN(6);
+  }
+#undef QIFT_ROT_LIN
   return hipGetLastError();
 }
 
