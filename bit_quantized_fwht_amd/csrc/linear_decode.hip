@@ -341,7 +341,8 @@ __device__ __forceinline__ void decode_splitk_tiles(const qift_linear_desc& d, i
   // keep the issue order: row, weights, scales)
   // (one group of 16 elements per thread covers the row: 8 waves take rows of
   // at most 16 chunks, K <= 4096, and 16 waves any K up to 16384)
-  static_assert(16 * NT >= (S == 16 ? QIFT_MAX_ROW : 16 * F::kChunkK), "one group per thread");
+  static_assert(!kFused || 16 * NT >= (S == 16 ? QIFT_MAX_ROW : 16 * F::kChunkK),
+                "one group per thread");
   uint32_t xraw[1][16];
   if constexpr (kFused) {
     rotate_row_load<XT, NT, 1>(reinterpret_cast<const XT*>(fr.X), (int)K, xraw);
