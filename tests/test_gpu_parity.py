@@ -91,9 +91,12 @@ def test_rotate_quant_bitexact_given_rotated_input(M, K):
     assert np.array_equal(xg.view(np.uint32), xr32.view(np.uint32))
 
 
+# rows of 1, 2, 3 and 4 groups of 16 per thread (K up to 4096, 8192, 12288,
+# 16384; 4112 = 257 groups leaves one thread a second group)
 @pytest.mark.parametrize("M,K,B", [(3, 16, 16), (5, 256, 64), (17, 4096, 256), (2, 4096, 1024),
                                    (4, 4096, 4096), (3, 11008, 256), (2, 14336, 1024),
-                                   (1, 16384, 4096), (33, 1024, 16)])
+                                   (1, 16384, 4096), (33, 1024, 16), (5, 4112, 16),
+                                   (3, 6144, 1024), (2, 8192, 4096), (2, 12288, 4096)])
 def test_rotate_quant_bitexact_exact_rotation(M, K, B):
     """Integer-valued inputs with an even log2(block): every butterfly sum is
     an exact small integer and 1/sqrt(B) is a power of two, so the rotated
