@@ -42,16 +42,43 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build libqift.so)")
 
 
-def build(verbose: bool = False, extra_flags=None) -> str:
-    srcs = [os.path.join(CSRC, s) for s in SOURCES]
-    tmp = LIB + ".tmp"
-    cmd = [hipcc(), *HIPCC_FLAGS, *(extra_flags or []), "-I", INCLUDE, "-I", CSRC, "-o", tmp, *srcs]
+# per-source flags: the KV4 kernels keep their matrix-core results in
+# ordinary vector registers (the accumulation registers would need one extra
+# move per value, about a tenth of that kernel's vector instructions)
+SOURCE_FLAGS = {"kv4.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
+BUILD_DIR = os.path.join(ROOT, "_build")
+
+
+def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
-    res = subprocess.run(cmd, capture_output=True, text=True)
+    return subprocess.run(cmd, capture_output=True, text=True)
+
+
+def build(verbose: bool = False, extra_flags=None, jobs: int = 8) -> str:
+    """Compile every source to an object (in parallel), then link libqift.so."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    objs, cmds = [], []
+    for src in SOURCES:
+        obj = os.path.join(BUILD_DIR, src + ".o")
+        flags = [f for f in HIPCC_FLAGS if f != "-shared"]
+        cmds.append([hipcc(), *flags, *SOURCE_FLAGS.get(src, []), *(extra_flags or []), "-I", INCLUDE,
+                     "-I", CSRC, "-c", "-o", obj, os.path.join(CSRC, src)])
+        objs.append(obj)
+    with ThreadPoolExecutor(max_workers=max(1, min(jobs, len(cmds)))) as ex:
+        results = list(ex.map(lambda c: _run(c, verbose), cmds))
+    for cmd, res in zip(cmds, results):
+        if res.returncode != 0:
+            sys.stderr.write(res.stdout + res.stderr)
+            raise RuntimeError(f"hipcc failed on {cmd[-1]} with exit code {res.returncode}")
+    tmp = LIB + ".tmp"
+    res = _run([hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs], verbose)
     if res.returncode != 0:
         sys.stderr.write(res.stdout + res.stderr)
-        raise RuntimeError(f"hipcc failed with exit code {res.returncode}")
+        raise RuntimeError(f"linking libqift.so failed with exit code {res.returncode}")
     os.replace(tmp, LIB)
     return LIB
 

@@ -3,7 +3,12 @@
 // its own absmax scale (the "KV4" of rotated W2A4/KV4 inference, Qift
 // abstract).
 //
-// Layout on the GPU: a head vector of D elements is held by L = D/E lanes of
+// Two kernels: bfloat16 vectors of 64, 128 or 256 elements with a block of
+// at least 32 run the transform on the matrix cores (kv4_mfma_kernel, below:
+// about 9 vector instructions per element against 16.5); every other case
+// runs kv4_kernel, all butterflies.
+//
+// kv4_kernel's layout on the GPU: a head vector of D elements is held by L = D/E lanes of
 // one quad with E consecutive elements each (E = min(D, 32); 64 for
 // D = 256), so log2(E) butterfly stages run inside a lane's registers and at
 // most two (partners at lane xor 1 and xor 2) cross lanes, through DPP quad
@@ -143,6 +148,189 @@ __global__ __launch_bounds__(kKvThreads) void kv4_kernel(const T* __restrict__ K
   }
 }
 
+// ---------------------------------------------------------------------------
+// bfloat16 head vectors of D = 32 NCH elements with a block of 2^LB >= 32
+// elements: the transform on the matrix cores.
+//
+// Index bits split the block transform: for e = 32 c + k (chunk c, k < 32)
+// and i = 32 c' + i', (-1)^popcount(i & e) = (-1)^popcount(c' & c) *
+// (-1)^popcount(i' & k), so H_(2^LB) = H_(2^LB / 32) (x) H_32 over (chunk,
+// position in chunk). One v_mfma_f32_16x16x32_bf16 applies H_32 to one
+// chunk of 16 head vectors at once (the bfloat16 inputs times +-1 are exact
+// products, summed in float32), and LB - 5 butterfly stages across the
+// chunks, in each lane's registers, finish the block.
+//
+// A wave owns a tile of 16 head vectors. Operand B of chunk c is
+// X[t][32 c + k], which the MFMA layout gives lane (t = lane % 16, g = lane
+// / 16) as k = 8 g .. 8 g + 7: one 16-byte load of the row. Operand A holds
+// 16 rows of H_32 for each half h of the outputs; its row slots are permuted
+// (slot p <- output 8 (p / 4) + 4 h + p % 4) so that the four results of
+// slot rows 4 g .. 4 g + 3 that the MFMA leaves in lane (t, g) are, over
+// both halves, the eight consecutive outputs 8 g .. 8 g + 7 of the chunk:
+// one 32-bit word of codes per chunk and lane. The words of a vector are
+// regrouped through a wave-private LDS row so that each lane stores NCH
+// consecutive words (16 bytes of codes for D = 128, the 16 vectors' codes
+// one contiguous kilobyte). Absmax, scale and codes are the same arithmetic
+// as in kv4_kernel (sigma = 1).
+// ---------------------------------------------------------------------------
+
+// max over lanes l, l ^ 16, l ^ 32, l ^ 48 (gfx950 row-pair swaps)
+__device__ __forceinline__ float max_lanes_16_32(float m) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(m), __float_as_uint(m), false, false);
+  m = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(m), __float_as_uint(m), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
+constexpr int kKvMfmaWaves = 4;
+
+// One tile of 16 head vectors whose NCH 16-byte operand loads (xb) have been
+// issued: transform, quantize and store it.
+template <int NCH, int LB>
+__device__ __forceinline__ void kv4_mfma_tile(const v4u (&xb)[NCH], const v4u (&ha)[2], int64_t r0,
+                                              int64_t rows, float norm, uint8_t* __restrict__ kvq,
+                                              float* __restrict__ scales, uint32_t* stage, int t,
+                                              int g) {
+  constexpr int D = 32 * NCH;
+  constexpr int kPitch = 4 * NCH + 4;
+  // v[c][j]: output 32 c + 8 g + j of vector t (unnormalized)
+  float v[NCH][8];
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) {
+    const bf16x8_t b = __builtin_bit_cast(bf16x8_t, xb[c]);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const v4f y = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+          __builtin_bit_cast(bf16x8_t, ha[h]), b, v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v[c][4 * h + i] = y[i];
+    }
+  }
+  // butterflies across the chunks of a block (chunk strides 1 .. 2^(LB-6))
+#pragma unroll
+  for (int st = 0; st < LB - 5; ++st) {
+    const int hs = 1 << st;
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      if (!(c & hs)) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const float a = v[c][j], b = v[c + hs][j];
+          v[c][j] = a + b;
+          v[c + hs][j] = a - b;
+        }
+      }
+    }
+  }
+
+  float m = 0.f;
+#pragma unroll
+  for (int c = 0; c < NCH; ++c)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf(v[c][j]));
+  m = max_lanes_16_32(m);
+  m *= norm;  // rounding is monotonic: max(|v|) * norm == max(|v * norm|)
+  const float s = __fdiv_rn(m, 7.0f);
+  const float rs = s != 0.f ? __fdiv_rn(1.0f, s) : 0.f;
+  const float rl = norm * rs;
+  uint32_t words[NCH];
+  float dmax = 0.f;
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) words[c] = int4x8_rint_fma(v[c], rl, dmax);
+  if (!(dmax <= 0.49999f) || !rint_path_ok(rs)) {
+    // a value within 1e-5 of a rounding tie (rare): exact division
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      float x[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) x[j] = v[c][j] * norm;
+      words[c] = int4x8_exact(x, s);
+    }
+  }
+
+  // word c of lane (t, g) is word 4 c + g of vector t's code row; lane (t, g)
+  // stores words NCH g .. NCH g + NCH - 1 (the stage rows are the wave's
+  // own: its LDS accesses complete in order)
+  uint32_t* st = stage + t * kPitch;
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) st[4 * c + g] = words[c];
+  __builtin_amdgcn_wave_barrier();
+  const int64_t r = r0 + t;
+  if (r < rows) {
+    uint8_t* dst = kvq + r * (D / 2) + 4 * NCH * g;
+    if constexpr (NCH == 2) {
+      const uint2 o = *reinterpret_cast<const uint2*>(st + 2 * g);
+      *reinterpret_cast<uint2*>(dst) = o;
+    } else {
+#pragma unroll
+      for (int q = 0; q < NCH / 4; ++q) {
+        const uint4 o = *reinterpret_cast<const uint4*>(st + NCH * g + 4 * q);
+        __builtin_nontemporal_store(v4u{o.x, o.y, o.z, o.w}, reinterpret_cast<v4u*>(dst) + q);
+      }
+    }
+    if (g == 0) scales[r] = s;
+  }
+}
+
+// One tile of 16 head vectors per wave. (Waves that walk several tiles with
+// the next tile's loads in flight measured 5-10% slower on the LLaMA-shaped
+// K and V: the loads of all tiles are in flight at once either way, and a
+// streaming probe of the same bytes in the same pattern is only ~20% faster
+// than this kernel.)
+template <int NCH, int LB>
+__global__ __launch_bounds__(64 * kKvMfmaWaves) void kv4_mfma_kernel(
+    const uint16_t* __restrict__ KV, int64_t rows, float norm, uint8_t* __restrict__ kvq,
+    float* __restrict__ scales) {
+  static_assert(NCH == 2 || NCH == 4 || NCH == 8, "D = 64, 128 or 256");
+  static_assert(LB >= 5 && (1 << LB) <= 32 * NCH, "block between 32 and D");
+  constexpr int kPitch = 4 * NCH + 4;  // words per staged vector row (16-byte aligned)
+  __shared__ __attribute__((aligned(16))) uint32_t stage[kKvMfmaWaves][16 * kPitch];
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int t = lane & 15, g = lane >> 4;
+  const int64_t r0 = ((int64_t)blockIdx.x * kKvMfmaWaves + wave) * 16;
+  if (r0 >= rows) return;  // uniform over the wave; no workgroup barrier below
+  const int64_t r = r0 + t;
+  const int64_t rr = r < rows ? r : rows - 1;  // a row past the end reads the last row
+
+  v4u xb[NCH];
+  const auto src = as_global(reinterpret_cast<const v4u*>(KV + rr * (32 * NCH) + 8 * g));
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) xb[c] = __builtin_nontemporal_load(src + 4 * c);
+
+  // operand A of half h: lane (slot p = lane % 16, k group lane / 16) holds
+  // the eight bfloat16 entries H_32[i][8 (lane / 16) + j], i = 8 (p / 4) +
+  // 4 h + p % 4: the sign (-1)^popcount(i & k) is H_8[4 h + p % 4][j] times
+  // (-1)^popcount((p / 4) & (lane / 16)) (bits 0-2 and 3-4 of i and k)
+  v4u ha[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) ha[h] = h32_operand_bf16(4 * h + (t & 3), (t >> 2) & g);
+
+  kv4_mfma_tile<NCH, LB>(xb, ha, r0, rows, norm, kvq, scales, stage[wave], t, g);
+}
+
+template <int NCH, int LB>
+static void launch_kv4_mfma_lb(const void* KV, int64_t rows, int log2b, float norm, uint8_t* kvq,
+                               float* scales, hipStream_t s) {
+  if constexpr ((1 << LB) <= 32 * NCH) {
+    if (log2b == LB) {
+      const int64_t tiles = (rows + 15) / 16;
+      const dim3 grid((unsigned)((tiles + kKvMfmaWaves - 1) / kKvMfmaWaves));
+      hipLaunchKernelGGL((kv4_mfma_kernel<NCH, LB>), grid, dim3(64 * kKvMfmaWaves), 0, s,
+                         reinterpret_cast<const uint16_t*>(KV), rows, norm, kvq, scales);
+      return;
+    }
+    launch_kv4_mfma_lb<NCH, LB + 1>(KV, rows, log2b, norm, kvq, scales, s);
+  }
+}
+
+// log2b in [5, log2 D]
+template <int NCH>
+static void launch_kv4_mfma(const void* KV, int64_t rows, int log2b, float norm, uint8_t* kvq,
+                            float* scales, hipStream_t s) {
+  launch_kv4_mfma_lb<NCH, 5>(KV, rows, log2b, norm, kvq, scales, s);
+}
+
 template <int E, int L, bool kFull>
 static void launch_kv4_f(const void* KV, int bf16, int64_t rows, int log2b, float norm,
                          uint8_t* kvq, float* scales, hipStream_t s) {
@@ -170,6 +358,14 @@ hipError_t launch_kv4(const void* KV, int bf16, int64_t rows, int D, int had_blo
   int log2b = 0;
   while ((1 << log2b) < had_block) ++log2b;
   const float norm = (float)(1.0 / __builtin_sqrt((double)had_block));
+  // bfloat16 vectors of 64, 128 or 256 elements with a block of at least 32
+  // on the matrix cores
+  if (bf16 && had_block >= 32 && (D == 64 || D == 128 || D == 256)) {
+    if (D == 64) launch_kv4_mfma<2>(KV, rows, log2b, norm, kvq, scales, s);
+    else if (D == 128) launch_kv4_mfma<4>(KV, rows, log2b, norm, kvq, scales, s);
+    else launch_kv4_mfma<8>(KV, rows, log2b, norm, kvq, scales, s);
+    return hipGetLastError();
+  }
   switch (D) {
     case 16: launch_kv4_l<16, 1>(KV, bf16, rows, log2b, norm, kvq, scales, s); break;
     case 32: launch_kv4_l<32, 1>(KV, bf16, rows, log2b, norm, kvq, scales, s); break;

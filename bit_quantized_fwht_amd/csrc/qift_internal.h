@@ -86,6 +86,34 @@ __device__ __forceinline__ uint32_t code_int4_recip(float x, float s, float r) {
   return s == 0.f ? 0u : code;
 }
 
+// ---------------------------------------------------------------------------
+// Walsh-Hadamard operands for v_mfma_f32_16x16x32_bf16 (KV4)
+// ---------------------------------------------------------------------------
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+// Eight bfloat16 entries +-1 of a Walsh-Hadamard operand (two per word, the
+// lower index in the low half): row r of H_8 (r < 8), all signs flipped when
+// popcount(hi) is odd. Entry j is negative when popcount(r & j) is odd: for
+// j = 2 m + 1 that is the sign of j = 2 m times (-1)^(r & 1), and for j = 2 m
+// the sign is (-1)^(bit 1 of r * bit 0 of m + bit 2 of r * bit 1 of m).
+//
+// Operand A of H_32 for lane (slot p = lane % 16, k group q = lane / 16), the
+// rows permuted so that half h of the outputs puts output 8 (p / 4) + 4 h +
+// p % 4 in slot p: h32_operand_bf16(4 h + p % 4, (p / 4) & q), since
+// popcount(i & k) splits over bits 0-2 and 3-4 of i and k. With it, the four
+// results of slot rows 4 q' .. 4 q' + 3 that the MFMA leaves in lane
+// (column, q') are, over both halves, the eight consecutive outputs 8 q' ..
+// 8 q' + 7. The entries are exact, the products with bfloat16 inputs are
+// exact, and the MFMA sums them in float32.
+__device__ __forceinline__ v4u h32_operand_bf16(int r, int hi) {
+  const uint32_t c = 0x3F803F80u ^ ((__builtin_popcount(hi) & 1) ? 0x80008000u : 0u) ^
+                     ((r & 1) ? 0x80000000u : 0u);
+  const uint32_t b1 = (r & 2) ? 0x80008000u : 0u, b2 = (r & 4) ? 0x80008000u : 0u;
+  return v4u{c, c ^ b1, c ^ b2, c ^ b1 ^ b2};
+}
+
 __device__ __forceinline__ float load_scale(const void* p, int64_t i, int is_f16) {
   if (is_f16) return __half2float(reinterpret_cast<const __half*>(p)[i]);
   return reinterpret_cast<const float*>(p)[i];

@@ -45,6 +45,29 @@ __device__ __forceinline__ uint32_t int4x8_rint(const float y[8], float& dmax) {
   return (lo | hi) ^ 0x88888888u;
 }
 
+// codes of v[0..7] * r with each product rounded once, inside the adder
+// (fused multiply-add): 8 + rint(v r) in the low nibble of fl(v r + (1.5 *
+// 2^23 + 8)), and dmax raised to the largest |v r - rint(v r)|, also from a
+// fused multiply-add. v r is within 1.3e-6 of x / s wherever v * r is (one
+// rounding fewer), so the same 0.49999 margin decides when the exact
+// division must be used instead.
+__device__ __forceinline__ uint32_t int4x8_rint_fma(const float v[8], float r, float& dmax) {
+  uint32_t e[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const float ym = __builtin_fmaf(v[j], r, kRintMagic8);
+    const float t = ym - kRintMagic8;  // rint(v r), exact
+    dmax = fmaxf(dmax, fabsf(__builtin_fmaf(v[j], r, -t)));
+    e[j] = __float_as_uint(ym);
+  }
+  uint32_t p[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) p[i] = (e[2 * i + 1] << 4) + e[2 * i];
+  const uint32_t lo = __builtin_amdgcn_perm(p[1], p[0], 0x0c0c0400u);
+  const uint32_t hi = __builtin_amdgcn_perm(p[3], p[2], 0x04000c0cu);
+  return (lo | hi) ^ 0x88888888u;
+}
+
 // the same codes from the exact IEEE division, clamped to [-7, 7] (s == 0
 // gives 0). The clamp binds only when s = fl(absmax / 7) is subnormal: its
 // rounding can then make |x / s| exceed 7.5 (absmax = 8 * 2^-149 gives

@@ -432,6 +432,48 @@ def test_kv4_exact_ties_after_rotation(D):
     assert np.array_equal(qg, qo.reshape(len(Z), D).astype(np.int64))
 
 
+def sparse_tie_rows_bf16(D, B, seed):
+    """Head vectors z of rounding ties (half-integers times 2^e, max |z| =
+    7 * 2^e) with at most three nonzeros per block of B, and x = H_B z /
+    sqrt(B) blockwise: every x is a sum of at most three such values, a
+    number of at most 6 significant bits, so x is exact in bfloat16 and
+    the matrix-core transform (bfloat16 products, float32 sums) returns z
+    exactly (1/sqrt(B) is a power of two for even log2 B)."""
+    rng = np.random.default_rng(seed)
+    ties = np.array([0.5, 1.5, 2.5, 3.5, 4.5, 5.5, 6.5])
+    Hb = np.array([[(-1) ** bin(i & j).count("1") for j in range(B)] for i in range(B)], float)
+    rows = []
+    for e in (-3, 0, 5):
+        for _ in range(4):
+            z = np.zeros(D)
+            for b in range(D // B):
+                pos = rng.choice(B, 3, replace=False)
+                z[b * B + pos] = rng.choice(ties, 3) * rng.choice([-1.0, 1.0], 3)
+            z[rng.integers(D)] = 7.0 * rng.choice([-1.0, 1.0])
+            rows.append(z * 2.0 ** e)
+    Z = np.stack(rows)
+    X = (Z.reshape(len(rows), D // B, B) @ Hb.T).reshape(len(rows), D) / np.sqrt(B)
+    assert np.array_equal(si.bf16_values(si.to_bf16(X)), X)  # exact in bfloat16
+    expect = np.rint(Z / (np.abs(Z).max(axis=1, keepdims=True) / 7.0))  # half to even
+    return X, Z, expect.astype(np.int64)
+
+
+@pytest.mark.parametrize("D,B", [(64, 64), (128, 64), (256, 256), (256, 64)])
+def test_kv4_exact_ties_bf16_matrix_core(D, B):
+    """bfloat16 head vectors with a block of at least 32 take the matrix-core
+    transform; exact ties after it round half to even, as the oracle does."""
+    X, Z, expect = sparse_tie_rows_bf16(D, B, seed=D + B)
+    KV = si.to_bf16(X.reshape(len(Z), 1, D)).to(DEV)
+    say(f"kv4 bf16 exact ties D={D} B={B}")
+    kvq, sc = q.qift_kv4_quant(KV, B)
+    sync()
+    qg = O.unpack_int4(kvq.cpu().numpy()).reshape(len(Z), D)
+    assert np.array_equal(qg, expect)
+    assert np.array_equal(sc.cpu().numpy().reshape(-1), np.abs(Z).max(axis=1) / 7.0)
+    qo, so, _ = O.kv4_quant(X.reshape(len(Z), 1, D), B)
+    assert np.array_equal(qg, qo.reshape(len(Z), D).astype(np.int64))
+
+
 def test_kv4_bitexact_given_rotated_input():
     T, H, D = 9, 4, 128
     KV = si.kv(T, H, D, seed=3)
