@@ -5,7 +5,7 @@
 //
 // Two kernels: bfloat16 vectors of 64, 128 or 256 elements with a block of
 // at least 32 run the transform on the matrix cores (kv4_mfma_kernel, below:
-// about 9 vector instructions per element against 16.5); every other case
+// about 11 vector instructions per element against 16.5); every other case
 // runs kv4_kernel, all butterflies.
 //
 // kv4_kernel's layout on the GPU: a head vector of D elements is held by L = D/E lanes of
