@@ -99,6 +99,13 @@ __device__ __forceinline__ void st16(void* p, uint32_t a, uint32_t b, uint32_t c
 __device__ __forceinline__ void st8(void* p, uint32_t a, uint32_t b) {
   *as_global_out(reinterpret_cast<v2u*>(p)) = v2u{a, b};
 }
+// the same, non-temporal (written once, not read back by the kernel)
+__device__ __forceinline__ void st16_nt(void* p, uint32_t a, uint32_t b, uint32_t c, uint32_t e) {
+  __builtin_nontemporal_store(v4u{a, b, c, e}, as_global_out(reinterpret_cast<v4u*>(p)));
+}
+__device__ __forceinline__ void st8_nt(void* p, uint32_t a, uint32_t b) {
+  __builtin_nontemporal_store(v2u{a, b}, as_global_out(reinterpret_cast<v2u*>(p)));
+}
 
 __device__ __forceinline__ uint4 ld16(const void* p) {
   const v4u v = *as_global(reinterpret_cast<const v4u*>(p));
