@@ -411,6 +411,7 @@ __device__ __forceinline__ void prefill_tile_sk(const qift_linear_desc& d, int64
   // reads all of a stage's fragments before the next stage's loads are
   // issued (the compiler would otherwise wait for those loads first)
   auto fetch = [&](int buf, Frag& f) {
+    __builtin_amdgcn_s_setprio(1);
     const uint8_t* as = lds + buf * C::kStage;
     const uint8_t* bs = as + C::kABytes;
     const int c = C::kInt4 ? 4 * kh + g : 2 * g + kh;
@@ -429,7 +430,16 @@ __device__ __forceinline__ void prefill_tile_sk(const qift_linear_desc& d, int64
         f.b[j] = *reinterpret_cast<const uint2*>(bs + tile * 1024 + 16 * lane + 8 * kh);
     }
   };
+  // Wave priorities (s_setprio; the two workgroups of a CU put two waves on
+  // every SIMD): the matrix-core phase of a stage runs at 2, the fragment
+  // reads that feed it at 1, everything else (stage waits and barriers, the
+  // partial-sum swap, the epilogue) at 0. When both waves of a SIMD can
+  // issue, the one in its MFMA phase goes first and keeps the matrix core
+  // fed while the other's LDS reads, waits and stores fill its gaps: down_proj
+  // 0.48 -> 0.51 and the PoT gate 0.45 -> 0.50 of the int8 peak (one level
+  // for both phases was no faster than none).
   auto mma = [&](const Frag& f, bool first) {
+    __builtin_amdgcn_s_setprio(2);
 #pragma unroll
     for (int s2 = 0; s2 < 2; ++s2) {
       v4i B[4];
@@ -462,6 +472,7 @@ __device__ __forceinline__ void prefill_tile_sk(const qift_linear_desc& d, int64
         __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);  // two VALU
       }
     }
+    __builtin_amdgcn_s_setprio(0);
   };
 
   // the epilogue's scales, fetched now so that their latency is hidden by the
