@@ -84,6 +84,19 @@ def unit_prefill_up_proj(q, torch, dev, steps):
         q.qift_w2a4_linear(xq, sa, cw, sw, "mnz", Y=Y)
 
 
+def unit_prefill_down_proj(q, torch, dev, steps):
+    """LLaMA-7B down_proj prefill: M = 2048, K = 11008 (block 256), N = 4096,
+    MNZ, bf16 out."""
+    import synth_inputs as si
+    W = si.device_weights(4096, 11008, seed=5, sigma=0.02, device=dev)
+    cw, sw = q.qift_quantize_weights(W, 256, "mnz", torch.float16)
+    X = si.device_activations(2048, 11008, seed=6, device=dev)
+    xq, sa, _ = q.qift_rotate_quant_act(X, 256)
+    Y = torch.empty((2048, 4096), dtype=torch.bfloat16, device=dev)
+    for _ in range(steps):
+        q.qift_w2a4_linear(xq, sa, cw, sw, "mnz", Y=Y)
+
+
 def unit_kv4(q, torch, dev, steps):
     """KV4 of K and V [4096, 32, 128] bf16 (two launches per step)."""
     import synth_inputs as si
@@ -205,7 +218,8 @@ def unit_mfma_i8(q, torch, dev, steps):
         q.qift_measure_mfma_i8(MFMA_ITERS, MFMA_WORKGROUPS, clk)
 
 
-UNITS = {"prefill_up_proj": unit_prefill_up_proj, "rotate_up_proj_input": unit_rotate_up_proj_input,
+UNITS = {"prefill_up_proj": unit_prefill_up_proj, "prefill_down_proj": unit_prefill_down_proj,
+         "rotate_up_proj_input": unit_rotate_up_proj_input,
          "copy": unit_copy, "mfma_i8": unit_mfma_i8, "kv4": unit_kv4, "attention": unit_attention,
          "gptq": unit_gptq, "decode_layer_by_layer": unit_decode_layer_by_layer,
          "decode_layer_by_layer_fused": unit_decode_layer_by_layer_fused,
