@@ -112,18 +112,13 @@ __global__ __launch_bounds__(kKvThreads) void kv4_kernel(const T* __restrict__ K
   m *= norm;  // rounding is monotonic: max(|v|) * norm == max(|v * norm|)
   const float s = __fdiv_rn(m, 7.0f);
   const float rs = s != 0.f ? __fdiv_rn(1.0f, s) : 0.f;
-  // y = stored * sigma * (norm / s), within four roundings of x' / s with
-  // x' = fl(v * norm) the rotated value (int4x8_rint's margin covers it)
+  // stored * sigma * (norm / s) is within three roundings of x' / s with
+  // x' = fl(v * norm) the rotated value (int4x8_rint_fma's margin covers it)
   const float rl = sigma * (norm * rs);
   uint32_t words[E / 8];
   float dmax = 0.f;
 #pragma unroll
-  for (int w = 0; w < E / 8; ++w) {
-    float y[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) y[j] = v[8 * w + j] * rl;
-    words[w] = int4x8_rint(y, dmax);
-  }
+  for (int w = 0; w < E / 8; ++w) words[w] = int4x8_rint_fma(v + 8 * w, rl, dmax);
   if (!(dmax <= 0.49999f) || !rint_path_ok(rs)) {
     // a value within 1e-5 of a rounding tie (rare): exact division
 #pragma unroll

@@ -4,20 +4,23 @@
 // round half to even, packed as eight two's-complement nibbles in one word
 // (element j at bits 4j..4j+3).
 //
-// Fast path: y = x * r with r = 1 / s (or y = v * fl(norm * r) for x =
-// fl(v * norm)). For |x / s| <= 7.5, y is within 1.8e-6 of x / s (at most
-// four roundings of 2^-24 relative each), so whenever y is more than 1e-5
-// away from a half-integer, y, x / s and the correctly rounded quotient all
-// round to the same integer. The caller tracks the largest |y - rint(y)| of a group
-// and recomputes the group with the exact division when it exceeds 0.49999
-// (or when r is not finite, i.e. s is so small that 1 / s overflows).
+// Fast path: P = v * r exactly, with r = fl(norm * fl(1 / s)) for x =
+// fl(v * norm) (norm = 1 for an unrotated x = v). For |x / s| <= 7.5, P is
+// within 1.4e-6 of x / s (three roundings of 2^-24 relative each), so
+// whenever P is more than 1e-5 away from a half-integer, P, x / s and the
+// correctly rounded quotient all round to the same integer. The caller
+// tracks the largest |P - rint(P)| of a group and recomputes the group with
+// the exact division when it exceeds 0.49999 (or when r is not finite, i.e.
+// s is so small that 1 / s overflows).
 //
-// Rounding uses the float adder: y + (1.5 * 2^23 + 8) rounds y to the nearest
-// integer, ties to even (the constant is even), and leaves 8 + rint(y), a
-// value in [1, 15] for |y| <= 7.5, in the low nibble of the sum's bits with
-// nothing above it up to bit 22. Two such words combine into a byte with one
-// shift-and-add, four bytes into a word with two byte permutes, and the
-// offset of 8 turns into two's complement with one xor of 0x8 per nibble.
+// Rounding uses the float adder inside a fused multiply-add: fl(v * r +
+// (1.5 * 2^23 + 8)) rounds the exact product to the nearest integer, ties to
+// even (the constant is even), and leaves 8 + rint(P), a value in [1, 15]
+// for |P| <= 7.5, in the low nibble of the sum's bits with nothing above it
+// up to bit 22; a second fused multiply-add gives P - rint(P). Two such words
+// combine into a byte with one shift-and-add, four bytes into a word with two
+// byte permutes, and the offset of 8 turns into two's complement with one xor
+// of 0x8 per nibble.
 #pragma once
 
 #include "qift_internal.h"
@@ -26,31 +29,8 @@ namespace qift {
 
 constexpr float kRintMagic8 = 12582920.0f;  // 1.5 * 2^23 + 8
 
-// codes of y[0..7] (already multiplied by 1 / s); dmax is raised to the
-// largest |y[j] - rint(y[j])|
-__device__ __forceinline__ uint32_t int4x8_rint(const float y[8], float& dmax) {
-  uint32_t e[8];
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const float ym = y[j] + kRintMagic8;
-    const float t = ym - kRintMagic8;  // rint(y[j]), exact
-    dmax = fmaxf(dmax, fabsf(y[j] - t));
-    e[j] = __float_as_uint(ym);
-  }
-  uint32_t p[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) p[i] = (e[2 * i + 1] << 4) + e[2 * i];  // byte: two offset nibbles
-  const uint32_t lo = __builtin_amdgcn_perm(p[1], p[0], 0x0c0c0400u);  // bytes p0.b0, p1.b0, 0, 0
-  const uint32_t hi = __builtin_amdgcn_perm(p[3], p[2], 0x04000c0cu);  // bytes 0, 0, p2.b0, p3.b0
-  return (lo | hi) ^ 0x88888888u;
-}
-
-// codes of v[0..7] * r with each product rounded once, inside the adder
-// (fused multiply-add): 8 + rint(v r) in the low nibble of fl(v r + (1.5 *
-// 2^23 + 8)), and dmax raised to the largest |v r - rint(v r)|, also from a
-// fused multiply-add. v r is within 1.3e-6 of x / s wherever v * r is (one
-// rounding fewer), so the same 0.49999 margin decides when the exact
-// division must be used instead.
+// codes of v[0..7] * r (each product rounded once, inside the adder); dmax is
+// raised to the largest |v r - rint(v r)|
 __device__ __forceinline__ uint32_t int4x8_rint_fma(const float v[8], float r, float& dmax) {
   uint32_t e[8];
 #pragma unroll

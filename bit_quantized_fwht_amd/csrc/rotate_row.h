@@ -251,15 +251,15 @@ __device__ __forceinline__ void rotate_row_finish(const uint32_t raw[Q][16],
   // 6. quantize 16 consecutive elements per group: x = the rotated value up
   //    to sigma (sigma = 1 on the LDS path), y = x * sigma / s
   const float sg = in_regs ? sigma : 1.f;
-  // y = v * sg * (norm / s): within four roundings of x' / s with
-  // x' = fl(v * norm) the rotated value (int4x8_rint's margin covers it)
+  // v * sg * (norm / s) is within three roundings of x' / s with
+  // x' = fl(v * norm) the rotated value (int4x8_rint_fma's margin covers it)
   const float rl = sg * (norm * rs);
   uint2* xrow = reinterpret_cast<uint2*>(xq_row);
 #pragma unroll
   for (int q = 0; q < kQ; ++q) {
     const int grp = tid + q * NT;
     if (grp >= groups) continue;
-    float x[16], y[16];  // x: the stored values (up to sg), then the rotated ones
+    float x[16];  // x: the stored values (up to sg), then the rotated ones
     if (in_regs) {
 #pragma unroll
       for (int j = 0; j < 16; ++j) x[j] = v[q][j];
@@ -268,11 +268,10 @@ __device__ __forceinline__ void rotate_row_finish(const uint32_t raw[Q][16],
 #pragma unroll
       for (int j = 0; j < 16; ++j) x[j] = s16[j];
     }
-#pragma unroll
-    for (int j = 0; j < 16; ++j) y[j] = x[j] * rl;
+    // codes of x * rl, each product rounded once inside the adder
     float dmax = 0.f;
-    uint32_t w0 = int4x8_rint(y, dmax);
-    uint32_t w1 = int4x8_rint(y + 8, dmax);
+    uint32_t w0 = int4x8_rint_fma(x, rl, dmax);
+    uint32_t w1 = int4x8_rint_fma(x + 8, rl, dmax);
     if (!(dmax <= 0.49999f) || !fast || xrot_row) {
       // the true rotated values fl(v * norm); fma(., sg, +0) also writes
       // every zero as +0 (an upper lane's x - x comes back as -0 through its

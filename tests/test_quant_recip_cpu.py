@@ -4,12 +4,16 @@ symmetric int4 quantization: the code of rint(x * (1/s)), rounded by adding
 within 1e-5 of a half-integer (or for non-finite products), equals the code
 of clamp(rint(x / s), -7, 7) with the IEEE float32 quotient, for
 s = absmax / 7 and |x| <= absmax. Emulated in numpy float32 (IEEE, with
-subnormals)."""
+subnormals). Both forms the kernels use are checked: the product rounded to
+float32 before the adder (code_int4_recip), and the exact product rounded
+once inside a fused multiply-add (int4x8_rint_fma)."""
 import numpy as np
+import pytest
 
 from oracle import qift_oracle as O
 
 MAGIC = np.float32(12582912.0)  # 1.5 * 2^23
+MAGIC8 = np.float32(12582920.0)  # 1.5 * 2^23 + 8
 TINY = np.float32(2.0 ** -149)  # the smallest positive subnormal float32
 
 
@@ -32,7 +36,36 @@ def shortcut(x, s, clamp_exact=True):
     return np.where(exact, code_div, code)
 
 
-def test_reciprocal_shortcut_matches_ieee_division():
+def shortcut_fma(x, s, clamp_exact=True):
+    """int4x8_rint_fma with the int4x8_exact fallback, emulated: the exact
+    float32 x float32 product in float64 (48 significant bits, exact), plus
+    the constant, rounded once to float32 (a float64 rounding first can only
+    differ within 2^-29 of a half-integer, which the 0.49999 margin sends to
+    the exact division anyway); the margin from a second fused multiply-add,
+    P - rint(P), rounded once to float32."""
+    if s == 0:
+        return np.zeros(np.shape(x), np.int64)
+    with np.errstate(over="ignore", invalid="ignore", divide="ignore"):
+        r = np.float32(1) / s
+        P = x.astype(np.float64) * np.float64(r)
+        ym = (P + np.float64(MAGIC8)).astype(np.float32)
+        t = (ym - MAGIC8).astype(np.float32)
+        d = (P - t.astype(np.float64)).astype(np.float32)
+        code = (ym.view(np.uint32).astype(np.int64) & 0xF) ^ 0x8
+        exact = ~(np.abs(d) <= np.float32(0.49999)) | ~np.isfinite(np.float32(r))
+        q_div = np.rint(x / s).astype(np.int64)
+        if clamp_exact:
+            q_div = np.clip(q_div, -7, 7)
+        code_div = q_div & 0xF
+    return np.where(exact, code_div, code)
+
+
+DECISIONS = {"rounded_product": shortcut, "fused": shortcut_fma}
+
+
+@pytest.mark.parametrize("form", sorted(DECISIONS))
+def test_reciprocal_shortcut_matches_ieee_division(form):
+    shortcut = DECISIONS[form]
     rng = np.random.default_rng(0)
     total = 0
     for _ in range(60):
@@ -64,10 +97,12 @@ def subnormal_rows(seed=0):
     return np.stack(rows)
 
 
-def test_subnormal_scales_clamp_to_seven():
+@pytest.mark.parametrize("form", sorted(DECISIONS))
+def test_subnormal_scales_clamp_to_seven(form):
     """With absmax = m * 2^-149, s = fl(absmax / 7) is subnormal and its
     rounding can put |x / s| above 7.5 (m = 8: s = 2^-149, x / s = 8); the
     oracle clamps to 7, and so must the kernel's exact-division fallback."""
+    shortcut = DECISIONS[form]
     X = subnormal_rows()
     q_o, s_o = O.quant_sym4(X)
     clamp_bound = 0
