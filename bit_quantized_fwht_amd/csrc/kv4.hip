@@ -157,7 +157,11 @@ __global__ __launch_bounds__(kKvThreads) void kv4_kernel(const T* __restrict__ K
 //
 // A wave owns a tile of 16 head vectors. Operand B of chunk c is
 // X[t][32 c + k], which the MFMA layout gives lane (t = lane % 16, g = lane
-// / 16) as k = 8 g .. 8 g + 7: one 16-byte load of the row. Operand A holds
+// / 16) as k = 8 g .. 8 g + 7: one 16-byte piece of the row. The tile is
+// first copied to LDS in contiguous kilobytes (global_load_lds, the pieces
+// XOR-swizzled so that the operand reads are conflict-free): 4-6% faster for
+// 128- and 256-element vectors than loading the operand pieces straight into
+// registers, whose load instructions each cover 64 bytes of 16 vectors. Operand A holds
 // 16 rows of H_32 for each half h of the outputs; its row slots are permuted
 // (slot p <- output 8 (p / 4) + 4 h + p % 4) so that the four results of
 // slot rows 4 g .. 4 g + 3 that the MFMA leaves in lane (t, g) are, over
@@ -272,27 +276,36 @@ __device__ __forceinline__ void kv4_mfma_tile(const v4u (&xb)[NCH], const v4u (&
 // K and V: the loads of all tiles are in flight at once either way, and a
 // streaming probe of the same bytes in the same pattern is only ~20% faster
 // than this kernel.)
+typedef __attribute__((address_space(3))) void kv_lds_void;
+
 template <int NCH, int LB>
 __global__ __launch_bounds__(64 * kKvMfmaWaves) void kv4_mfma_kernel(
     const uint16_t* __restrict__ KV, int64_t rows, float norm, uint8_t* __restrict__ kvq,
     float* __restrict__ scales) {
   static_assert(NCH == 2 || NCH == 4 || NCH == 8, "D = 64, 128 or 256");
   static_assert(LB >= 5 && (1 << LB) <= 32 * NCH, "block between 32 and D");
-  constexpr int kPitch = 4 * NCH + 4;  // words per staged vector row (16-byte aligned)
-  __shared__ __attribute__((aligned(16))) uint32_t stage[kKvMfmaWaves][16 * kPitch];
+  constexpr int kPieces = 4 * NCH;     // 16-byte pieces per head vector
+  __shared__ __attribute__((aligned(1024))) uint8_t tile_lds[kKvMfmaWaves][1024 * NCH];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int t = lane & 15, g = lane >> 4;
   const int64_t r0 = ((int64_t)blockIdx.x * kKvMfmaWaves + wave) * 16;
   if (r0 >= rows) return;  // uniform over the wave; no workgroup barrier below
-  const int64_t r = r0 + t;
-  const int64_t rr = r < rows ? r : rows - 1;  // a row past the end reads the last row
-
-  v4u xb[NCH];
-  const auto src = as_global(reinterpret_cast<const v4u*>(KV + rr * (32 * NCH) + 8 * g));
+  uint8_t* wl = tile_lds[wave];
+  // the tile's 16 vectors, one contiguous kilobyte per instruction, straight
+  // to LDS: lane l of instruction q fills slot s = 64 q + l (vector s /
+  // kPieces, position j = s % kPieces) with piece j ^ (vector % kPieces), so
+  // that the operand reads below are conflict-free
 #pragma unroll
-  for (int c = 0; c < NCH; ++c) xb[c] = __builtin_nontemporal_load(src + 4 * c);
-
+  for (int q = 0; q < NCH; ++q) {
+    const int slot = 64 * q + lane;
+    const int tv = slot / kPieces, j = slot % kPieces;
+    const int p = j ^ (tv & (kPieces - 1));
+    int64_t r = r0 + tv;
+    r = r < rows ? r : rows - 1;  // a row past the end reads the last row
+    __builtin_amdgcn_global_load_lds(KV + r * (32 * NCH) + 8 * p, (kv_lds_void*)(wl + 1024 * q), 16,
+                                     0, 0);
+  }
   // operand A of half h: lane (slot p = lane % 16, k group lane / 16) holds
   // the eight bfloat16 entries H_32[i][8 (lane / 16) + j], i = 8 (p / 4) +
   // 4 h + p % 4: the sign (-1)^popcount(i & k) is H_8[4 h + p % 4][j] times
@@ -300,8 +313,15 @@ __global__ __launch_bounds__(64 * kKvMfmaWaves) void kv4_mfma_kernel(
   v4u ha[2];
 #pragma unroll
   for (int h = 0; h < 2; ++h) ha[h] = h32_operand_bf16(4 * h + (t & 3), (t >> 2) & g);
-
-  kv4_mfma_tile<NCH, LB>(xb, ha, r0, rows, norm, kvq, scales, stage[wave], t, g);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  // operand B of chunk c: piece 4 c + g of vector t
+  v4u xb[NCH];
+#pragma unroll
+  for (int c = 0; c < NCH; ++c)
+    xb[c] = *reinterpret_cast<const v4u*>(wl + 16 * (t * kPieces + ((4 * c + g) ^ (t & (kPieces - 1)))));
+  // (the code staging below reuses the wave's tile area: its LDS accesses
+  // complete in order)
+  kv4_mfma_tile<NCH, LB>(xb, ha, r0, rows, norm, kvq, scales, reinterpret_cast<uint32_t*>(wl), t, g);
 }
 
 template <int NCH, int LB>
