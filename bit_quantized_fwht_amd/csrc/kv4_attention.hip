@@ -171,14 +171,20 @@ __global__ __launch_bounds__(kAttnThreads) void kv4_attn_partial_kernel(
       dot += quad_xor<2>(dot);
       if (t0 + slot + kAttnP * (kAttnU * g + u) >= t1) continue;
       const float sc = dot * G.ks[u] * softmax_scale;
-      const float m_new = fmaxf(m, sc);
-      const float alpha = __expf(m - m_new);  // 0 on the first token (m = -inf)
-      const float p = __expf(sc - m_new);
-      l = l * alpha + p;
+      if (sc > m) {
+        // a new running maximum (every token early on, rarely later): the
+        // state is rescaled only then (0 on the first token, m = -inf)
+        const float alpha = __expf(m - sc);
+        l *= alpha;
+#pragma unroll
+        for (int j = 0; j < kAttnQ; ++j) acc[j] *= alpha;
+        m = sc;
+      }
+      const float p = __expf(sc - m);
+      l += p;
       const float pv = p * G.vs[u];
 #pragma unroll
-      for (int j = 0; j < kAttnQ; ++j) acc[j] = fmaf(acc[j], alpha, pv * int4_at(G.v[u], j));
-      m = m_new;
+      for (int j = 0; j < kAttnQ; ++j) acc[j] = fmaf(pv, int4_at(G.v[u], j), acc[j]);
     }
   };
   Grp ga, gb;
