@@ -389,8 +389,8 @@ def test_end_to_end_small_linear_case(kind):
 # KV4 (qift_kv4_quant)
 # ---------------------------------------------------------------------------
 
-@pytest.mark.parametrize("D,B", [(128, 128), (128, 64), (128, 1), (64, 64), (256, 256), (16, 16),
-                                 (32, 8)])
+@pytest.mark.parametrize("D,B", [(128, 128), (128, 64), (128, 32), (128, 1), (64, 64), (64, 32),
+                                 (256, 256), (256, 32), (16, 16), (32, 8)])
 def test_kv4_matches_oracle(D, B):
     T, H = 37, 5
     KV = si.kv(T, H, D, seed=D + B)
