@@ -34,39 +34,33 @@ constexpr int kAttnPart = 2 + kAttnD;   // floats per (run, head): m, l, o'[D]
 constexpr int kAttnG = 2;               // heads per workgroup
 constexpr int kAttnP = kAttnThreads / (4 * kAttnG);  // token slots (32)
 
-template <typename T>
-__device__ __forceinline__ float attn_ld(const T* p, int64_t i);
-template <>
-__device__ __forceinline__ float attn_ld<float>(const float* p, int64_t i) {
-  return p[i];
-}
-template <>
-__device__ __forceinline__ float attn_ld<uint16_t>(const uint16_t* p, int64_t i) {
-  return bf16_bits_to_float(p[i]);
-}
+__device__ __forceinline__ float attn_f32(float v) { return v; }
+__device__ __forceinline__ float attn_f32(uint16_t v) { return bf16_bits_to_float(v); }
 
-// Unnormalized block Walsh-Hadamard transform, blocks of 2^log2b along the
-// n floats of an LDS array (n a multiple of the block), by the whole
-// workgroup of nthr threads.
-__device__ __forceinline__ void lds_fwht(float* x, int n, int log2b, int tid, int nthr) {
-  for (int st = 0; st < log2b; ++st) {
-    const int h = 1 << st;
-    for (int p = tid; p < n / 2; p += nthr) {
-      const int i = (p >> st) * 2 * h + (p & (h - 1));
-      const float a = x[i], b = x[i + h];
-      x[i] = a + b;
-      x[i + h] = a - b;
+// 16 times the 32 int4 codes in 16 bytes (element 2j in the low nibble of
+// byte j, so element i of a word at bits 4i..4i+3). Each nibble is put in
+// the high half of a byte whose low half is 0, whose value as a signed byte
+// is then 16 times the code: odd elements are there already (a mask of the
+// word), even ones move up by one shift and the same mask, and the conversion
+// reads its byte straight from the masked word, sign-extended (one
+// v_cvt_f32_i32 with a byte-select source per element, against a bit-field
+// extract and a conversion). The empty asm statements hide the masked words
+// from the optimizer, which would otherwise rewrite some of the byte reads
+// into separate shifts and masks. The factor 16 is a power of two: it is
+// taken out of the other operand or of the sum, exactly.
+__device__ __forceinline__ void int4x32_x16(const uint4& u, float (&c)[32]) {
+  const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    uint32_t odd = w[i] & 0xF0F0F0F0u, even = (w[i] << 4) & 0xF0F0F0F0u;
+    asm("" : "+v"(odd));
+    asm("" : "+v"(even));
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      c[8 * i + 2 * b] = (float)(int8_t)(even >> (8 * b));
+      c[8 * i + 2 * b + 1] = (float)(int8_t)(odd >> (8 * b));
     }
-    __syncthreads();
   }
-}
-
-// code e of the 32 int4 codes in 16 bytes (element 2j in the low nibble of
-// byte j, so element i of a word at bits 4i..4i+3), sign-extended: the nibble
-// is shifted to the top of the word and shifted back arithmetically
-__device__ __forceinline__ float int4_at(const uint4& u, int e) {
-  const uint32_t w = e < 8 ? u.x : e < 16 ? u.y : e < 24 ? u.z : u.w;
-  return (float)((int32_t)(w << (28 - 4 * (e & 7))) >> 28);
 }
 
 // Merge of two online-softmax states (m, l, acc): weights exp(m - M), a state
@@ -105,9 +99,54 @@ __global__ __launch_bounds__(kAttnThreads) void kv4_attn_partial_kernel(
   const int64_t sq = blockIdx.z;
   const int nh = H - h0 < kAttnG ? H - h0 : kAttnG;  // heads of this workgroup
 
+  const int slot = tid / kPairs;
+  const int hq = tid - slot * kPairs;
+  const int hl = hq >> 2, quarter = hq & 3;
+  const int head = h0 + (hl < nh ? hl : 0);  // a missing head reads head h0 and is discarded
+  const int64_t t0 = run * tpr;
+  const int64_t t1 = t0 + tpr < T ? t0 + tpr : T;
+  const int64_t row_bytes = (int64_t)H * (kAttnD / 2);
+  const uint8_t* kbase = kq + head * (kAttnD / 2) + quarter * 16;
+  const uint8_t* vbase = vq + head * (kAttnD / 2) + quarter * 16;
+  // the slot's tokens t0 + slot + 32 i; group g holds i = kAttnU g ..
+  // kAttnU (g + 1) - 1; a token past t1 is not counted
+  const int64_t n_iter = (t1 - t0 + kAttnP - 1) / kAttnP;
+  const int64_t n_grp = (n_iter + kAttnU - 1) / kAttnU;
+  struct Grp {
+    uint4 k[kAttnU], v[kAttnU];
+    float ks[kAttnU], vs[kAttnU];
+  };
+  // every lane loads from a valid row: a token past the run reads the run's
+  // last row, and compute() skips it after its dot product (whose quad sum
+  // every lane takes part in), so the loads need no per-lane branch and no
+  // zeroing; groups past the last are skipped by a branch that is the same
+  // for the whole workgroup, except the first two (a run of one group reads
+  // its last row for group 1), so that the query's wait below counts exactly
+  // the sixteen loads issued after it
+  auto load = [&](Grp& G, int64_t g) {
+#pragma unroll
+    for (int u = 0; u < kAttnU; ++u) {
+      const int64_t t = t0 + slot + kAttnP * (kAttnU * g + u);
+      const int64_t row = sq * T + (t < t1 ? t : t1 - 1);
+      G.k[u] = *reinterpret_cast<const uint4*>(kbase + row * row_bytes);
+      G.v[u] = *reinterpret_cast<const uint4*>(vbase + row * row_bytes);
+      G.ks[u] = ks[row * H + head];
+      G.vs[u] = vs[row * H + head];
+    }
+  };
+  // the query is requested first and the first two groups right after it,
+  // so that the query's latency and theirs overlap (the query is waited for
+  // alone: loads complete in order)
+  const TQ xq = q[(sq * H + h0) * kAttnD + (tid < nh * kAttnD ? tid : 0)];
+  __builtin_amdgcn_sched_barrier(0);  // the query's load first
+  Grp ga, gb;
+  load(ga, 0);
+  load(gb, 1);
+  __builtin_amdgcn_sched_barrier(0);  // all seventeen loads issued before the query is used
+
   // rotated queries of the workgroup's heads: element i = tid (two heads of
   // 128); stages on index bits 0-5 by lane shuffles, bit 6 through LDS
-  float x = tid < nh * kAttnD ? attn_ld<TQ>(q, (sq * H + h0) * kAttnD + tid) : 0.f;
+  float x = tid < nh * kAttnD ? attn_f32(xq) : 0.f;
   for (int st = 0; st < log2b && st < 6; ++st) {
     const float y = __shfl_xor(x, 1 << st, 64);
     x = (tid >> st) & 1 ? y - x : x + y;
@@ -120,53 +159,30 @@ __global__ __launch_bounds__(kAttnThreads) void kv4_attn_partial_kernel(
     qr[tid] = (tid & 64) ? y - x : x + y;
     __syncthreads();
   }
-
-  const int slot = tid / kPairs;
-  const int hq = tid - slot * kPairs;
-  const int hl = hq >> 2, quarter = hq & 3;
-  const int head = h0 + (hl < nh ? hl : 0);  // a missing head reads head h0 and is discarded
+  // the thread's 32 query values, divided by 16 against the codes' factor
+  // of 16 (int4x32_x16): the products, and so the dot products, are unchanged
+  const float qn = norm * 0.0625f;
   float qv[kAttnQ];
 #pragma unroll
-  for (int j = 0; j < kAttnQ; ++j) qv[j] = qr[hl * kAttnD + quarter * kAttnQ + j] * norm;
+  for (int j = 0; j < kAttnQ; ++j) qv[j] = qr[hl * kAttnD + quarter * kAttnQ + j] * qn;
 
-  const int64_t t0 = run * tpr;
-  const int64_t t1 = t0 + tpr < T ? t0 + tpr : T;
+  // online softmax; acc holds 16 times the weighted sum of the values (codes
+  // times 16), taken out when the run's state is written
   float m = -__builtin_huge_valf(), l = 0.f;
   float acc[kAttnQ];
 #pragma unroll
   for (int j = 0; j < kAttnQ; ++j) acc[j] = 0.f;
 
-  const int64_t row_bytes = (int64_t)H * (kAttnD / 2);
-  const uint8_t* kbase = kq + head * (kAttnD / 2) + quarter * 16;
-  const uint8_t* vbase = vq + head * (kAttnD / 2) + quarter * 16;
-  // the slot's tokens t0 + slot + 32 i; group g holds i = 4g .. 4g + 3; a
-  // token past t1 is not loaded (zero codes and scales) and not counted
-  const int64_t n_iter = (t1 - t0 + kAttnP - 1) / kAttnP;
-  const int64_t n_grp = (n_iter + kAttnU - 1) / kAttnU;
-  struct Grp {
-    uint4 k[kAttnU], v[kAttnU];
-    float ks[kAttnU], vs[kAttnU];
-  };
-  auto load = [&](Grp& G, int64_t g) {
-#pragma unroll
-    for (int u = 0; u < kAttnU; ++u) {
-      const int64_t t = t0 + slot + kAttnP * (kAttnU * g + u);
-      const bool ok = t < t1;
-      const int64_t row = sq * T + t;
-      G.k[u] = ok ? *reinterpret_cast<const uint4*>(kbase + row * row_bytes) : uint4{0u, 0u, 0u, 0u};
-      G.v[u] = ok ? *reinterpret_cast<const uint4*>(vbase + row * row_bytes) : uint4{0u, 0u, 0u, 0u};
-      G.ks[u] = ok ? ks[row * H + head] : 0.f;
-      G.vs[u] = ok ? vs[row * H + head] : 0.f;
-    }
-  };
   // per token: the dot product of the thread's quarter, the quad sum (DPP),
   // then one online-softmax update of (m, l, acc)
   auto compute = [&](const Grp& G, int64_t g) {
 #pragma unroll
     for (int u = 0; u < kAttnU; ++u) {
+      float c[kAttnQ];
+      int4x32_x16(G.k[u], c);
       float dot = 0.f;
 #pragma unroll
-      for (int j = 0; j < kAttnQ; ++j) dot = fmaf(qv[j], int4_at(G.k[u], j), dot);
+      for (int j = 0; j < kAttnQ; ++j) dot = fmaf(qv[j], c[j], dot);
       dot += quad_xor<1>(dot);
       dot += quad_xor<2>(dot);
       if (t0 + slot + kAttnP * (kAttnU * g + u) >= t1) continue;
@@ -183,17 +199,18 @@ __global__ __launch_bounds__(kAttnThreads) void kv4_attn_partial_kernel(
       const float p = __expf(sc - m);
       l += p;
       const float pv = p * G.vs[u];
+      int4x32_x16(G.v[u], c);
 #pragma unroll
-      for (int j = 0; j < kAttnQ; ++j) acc[j] = fmaf(pv, int4_at(G.v[u], j), acc[j]);
+      for (int j = 0; j < kAttnQ; ++j) acc[j] = fmaf(pv, c[j], acc[j]);
     }
   };
-  Grp ga, gb;
-  load(ga, 0);
   for (int64_t g = 0; g < n_grp; g += 2) {
-    load(gb, g + 1);
     compute(ga, g);
-    load(ga, g + 2);
-    if (g + 1 < n_grp) compute(gb, g + 1);
+    if (g + 2 < n_grp) load(ga, g + 2);
+    if (g + 1 < n_grp) {
+      compute(gb, g + 1);
+      if (g + 3 < n_grp) load(gb, g + 3);
+    }
   }
 
   // merge the token slots of each (head, quarter): the 8 slots of a wave
@@ -236,82 +253,94 @@ __global__ __launch_bounds__(kAttnThreads) void kv4_attn_partial_kernel(
       dst[0] = M;
       dst[1] = L;
     }
-    dst[2 + pq * kAttnQ + j] = o;
+    dst[2 + pq * kAttnQ + j] = o * 0.0625f;  // the codes' factor of 16
   }
 }
 
 // Kernel 2: grid (H, S), 256 threads. Merge the runs of one (sequence, head),
-// divide by the softmax sum and rotate back. Runs are taken 64 at a time:
-// thread (run, quarter) loads its 32 partial outputs at once, scales them by
-// the run's weight and parks them in LDS; 128 threads then sum over the runs.
-constexpr int kAttnMaxRuns = 1024;
+// divide by the softmax sum and rotate back. Runs are taken 64 at a time
+// (one pass for up to 64 runs): thread (run, quarter) loads the run's m and l
+// and its 32 partial outputs together, the chunk's maximum comes from
+// shuffles and one LDS exchange, the outputs weighted by exp(m_r - M) are
+// parked in LDS and 128 threads sum over the runs; chunks after the first
+// are merged into the running state as two online-softmax states are. The
+// back rotation runs on the 128 sums in registers: index bits 0-5 by lane
+// shuffles, bit 6 through LDS.
 constexpr int kAttnCombineThreads = 256;
 __global__ __launch_bounds__(kAttnCombineThreads) void kv4_attn_combine_kernel(
     const float* __restrict__ part, int64_t runs, int H, int log2b, float norm,
     void* __restrict__ out, int out_bf16) {
-  __shared__ float o[kAttnD];
-  __shared__ float wr[kAttnMaxRuns];  // run weights exp(m_r - M), 0 for an empty run
-  __shared__ float red[kAttnCombineThreads / 64];
+  constexpr int kWaves = kAttnCombineThreads / 64;
   __shared__ float cell[64 * (kAttnD + 1)];  // [run][d], padded rows
-  const int tid = threadIdx.x;
+  __shared__ float red[2][kWaves];           // per wave: chunk maximum, chunk sum of l
+  __shared__ float xo[kAttnD];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t head = blockIdx.x, sq = blockIdx.y;
   const float* p0 = part + (sq * runs * H + head) * kAttnPart;
   const int64_t stride = (int64_t)H * kAttnPart;
-  // the maximum of the runs' m
-  float mx = -__builtin_huge_valf();
-  for (int64_t r = tid; r < runs; r += kAttnCombineThreads) mx = fmaxf(mx, p0[r * stride]);
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 64));
-  if ((tid & 63) == 0) red[tid >> 6] = mx;
-  __syncthreads();
-  float M = red[0];
-#pragma unroll
-  for (int w = 1; w < kAttnCombineThreads / 64; ++w) M = fmaxf(M, red[w]);
-  // run weights and the total sum
-  float lsum = 0.f;
-  for (int64_t r = tid; r < runs; r += kAttnCombineThreads) {
-    const float lr = p0[r * stride + 1];
-    const float w = lr > 0.f ? __expf(p0[r * stride] - M) : 0.f;
-    wr[r] = w;
-    lsum = fmaf(lr, w, lsum);
-  }
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) lsum += __shfl_xor(lsum, off, 64);
-  __syncthreads();  // every thread has read M from red; the weights are in wr
-  if ((tid & 63) == 0) red[tid >> 6] = lsum;
-  __syncthreads();
-  float L = red[0];
-#pragma unroll
-  for (int w = 1; w < kAttnCombineThreads / 64; ++w) L += red[w];
-  // weighted sum of the partial outputs, 64 runs at a time
   const int rl = tid >> 2, qd = (tid & 3) * kAttnQ;
-  float acc = 0.f;  // thread d < 128: dimension d
+  // running state over the chunks so far; thread d < 128 holds dimension d
+  float M = -__builtin_huge_valf(), L = 0.f, acc = 0.f;
   for (int64_t r0 = 0; r0 < runs; r0 += 64) {
     const int64_t r = r0 + rl;
-    if (r < runs) {
-      const float2* src = reinterpret_cast<const float2*>(p0 + r * stride + 2 + qd);
-      float2 v[kAttnQ / 2];
+    const bool ok = r < runs;
+    const float* src = p0 + (ok ? r : r0) * stride;  // a missing run reads run r0, weighs 0
+    const float mr0 = src[0], lr0 = src[1];
+    float2 v[kAttnQ / 2];
 #pragma unroll
-      for (int i = 0; i < kAttnQ / 2; ++i) v[i] = src[i];
-      const float w = wr[r];
+    for (int i = 0; i < kAttnQ / 2; ++i) v[i] = reinterpret_cast<const float2*>(src + 2 + qd)[i];
+    const float mr = ok ? mr0 : -__builtin_huge_valf();
+    const float lr = ok ? lr0 : 0.f;
+    // the chunk's maximum (the four threads of a run hold the same m)
+    float mc = mr;
 #pragma unroll
-      for (int i = 0; i < kAttnQ / 2; ++i) {
-        cell[rl * (kAttnD + 1) + qd + 2 * i] = v[i].x * w;
-        cell[rl * (kAttnD + 1) + qd + 2 * i + 1] = v[i].y * w;
-      }
-    }
+    for (int off = 32; off >= 4; off >>= 1) mc = fmaxf(mc, __shfl_xor(mc, off, 64));
+    if (lane == 0) red[0][wave] = mc;
     __syncthreads();
+#pragma unroll
+    for (int wv = 0; wv < kWaves; ++wv) mc = fmaxf(mc, red[0][wv]);
+    const float Mn = fmaxf(M, mc);
+    const float w = lr > 0.f ? __expf(mr - Mn) : 0.f;
+#pragma unroll
+    for (int i = 0; i < kAttnQ / 2; ++i) {
+      cell[rl * (kAttnD + 1) + qd + 2 * i] = v[i].x * w;
+      cell[rl * (kAttnD + 1) + qd + 2 * i + 1] = v[i].y * w;
+    }
+    float ls = (tid & 3) == 0 ? lr * w : 0.f;
+#pragma unroll
+    for (int off = 32; off >= 4; off >>= 1) ls += __shfl_xor(ls, off, 64);
+    if (lane == 0) red[1][wave] = ls;
+    __syncthreads();
+    // the state so far, rescaled to the new maximum (weight 0 before the first chunk)
+    const float a = L > 0.f ? __expf(M - Mn) : 0.f;
+    float lc = 0.f;
+#pragma unroll
+    for (int wv = 0; wv < kWaves; ++wv) lc += red[1][wv];
+    L = fmaf(L, a, lc);
     if (tid < kAttnD) {
       const int64_t nr = runs - r0 < 64 ? runs - r0 : 64;
-      for (int64_t i = 0; i < nr; ++i) acc += cell[i * (kAttnD + 1) + tid];
+      float sum = 0.f;
+      for (int64_t i = 0; i < nr; ++i) sum += cell[i * (kAttnD + 1) + tid];
+      acc = fmaf(acc, a, sum);
     }
-    __syncthreads();
+    M = Mn;
+    __syncthreads();  // cell and red are written again by the next chunk
   }
-  if (tid < kAttnD) o[tid] = acc / L;
-  __syncthreads();
-  lds_fwht(o, kAttnD, log2b, tid, kAttnCombineThreads);
+  float y = tid < kAttnD ? acc / L : 0.f;
+  for (int st = 0; st < log2b && st < 6; ++st) {
+    const float z = __shfl_xor(y, 1 << st, 64);
+    y = (tid >> st) & 1 ? z - y : y + z;
+  }
+  if (log2b > 6) {
+    if (tid < kAttnD) xo[tid] = y;
+    __syncthreads();
+    if (tid < kAttnD) {
+      const float z = xo[tid ^ 64];
+      y = (tid & 64) ? z - y : y + z;
+    }
+  }
   if (tid >= kAttnD) return;
-  const float y = o[tid] * norm;
+  y *= norm;
   const int64_t idx = (sq * H + head) * kAttnD + tid;
   if (out_bf16)
     reinterpret_cast<uint16_t*>(out)[idx] = float_to_bf16_bits(y);

@@ -674,9 +674,11 @@ def check_attention(got, ref, tol):
     assert err <= tol * np.abs(ref).max(), (err, np.abs(ref).max())
 
 
+# (1, 3000, 2) and (1, 8192, 1) split each head into 94 and 256 runs of 32
+# tokens: the merge then takes its runs in chunks of 64, the last one ragged
 @pytest.mark.parametrize("S,T,H,B", [(1, 1, 1, 128), (2, 37, 3, 128), (1, 16, 32, 128),
                                      (3, 100, 32, 64), (1, 1000, 64, 128), (2, 513, 5, 1),
-                                     (1, 4096, 32, 128)])
+                                     (1, 4096, 32, 128), (1, 3000, 2, 128), (1, 8192, 1, 64)])
 def test_kv4_attention(S, T, H, B):
     D = 128
     qv, kc, ks, vc, vs = attention_inputs(S, T, H, D, seed=S * 100 + T + H)
