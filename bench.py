@@ -98,13 +98,12 @@ def unit_prefill_down_proj(q, torch, dev, steps):
 
 
 def unit_kv4(q, torch, dev, steps):
-    """KV4 of K and V [4096, 32, 128] bf16 (two launches per step)."""
+    """KV4 of K and V [4096, 32, 128] bf16 of one layer (one launch per step)."""
     import synth_inputs as si
     K = si.device_kv(4096, 32, 128, seed=60, device=dev)
     V = si.device_kv(4096, 32, 128, seed=61, device=dev)
     for _ in range(steps):
-        q.qift_kv4_quant(K, 128)
-        q.qift_kv4_quant(V, 128)
+        q.qift_kv4_quant_kv(K, V, 128)
 
 
 def unit_attention(q, torch, dev, steps):
@@ -1105,38 +1104,43 @@ def measure_extras(q, torch, dev, stack, args):
     del sm
     torch.cuda.empty_cache()
 
-    # KV4: K and V [4096, 32, 128] bf16, cycled over 8 buffer sets (> cache)
+    # KV4: K and V [4096, 32, 128] bf16 of one layer, cycled over 4 layers'
+    # K and V (8 buffer sets, 1.3 GB: more than the caches hold)
     T, H, D = 4096, 32, 128
     sets = [(si.device_kv(T, H, D, seed=60 + i, device=dev),
              torch.empty((T, H, D // 2), dtype=torch.uint8, device=dev),
              torch.empty((T, H), dtype=torch.float32, device=dev)) for i in range(8)]
-
-    # all 8 sets, K then V, replayed from one HIP graph: per pair of calls
-    med, _ = time_graph(torch, [lambda a=a: q.qift_kv4_quant(a[0], D, kvq=a[1], scales=a[2])
-                                for a in sets], reps=20)
-    med *= 2
+    layers = [(sets[2 * i], sets[2 * i + 1]) for i in range(4)]
+    pair = lambda a, b: q.qift_kv4_quant_kv(a[0], b[0], D, kq=a[1], ks=a[2], vq=b[1], vs=b[2])
+    # one call per layer (K and V in one launch), the 4 calls replayed from one HIP graph
+    med, _ = time_graph(torch, [lambda a=a, b=b: pair(a, b) for a, b in layers], reps=20)
+    # the same tensors with one qift_kv4_quant call each (two launches per layer)
+    med2, _ = time_graph(torch, [lambda a=a: q.qift_kv4_quant(a[0], D, kvq=a[1], scales=a[2])
+                                 for a in sets], reps=20)
+    med2 *= 2
     kv_bytes = 2 * (T * H * D * 2 + T * H * D // 2 + T * H * 4)
-    # the same pair of calls on one buffer set with a 512 MB write between
-    # repetitions (the caches hold none of the inputs); only the calls are timed
+    # the pair call on one layer with a 512 MB write between repetitions (the
+    # caches hold none of the inputs); only the calls are timed
     flush = torch.empty((1 << 29,), dtype=torch.uint8, device=dev)
-    a, b = sets[0], sets[1]
+    a, b = layers[0]
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(20)]
     for i, (e0, e1) in enumerate(evs):
         flush.fill_(i & 0xFF)
         e0.record()
-        q.qift_kv4_quant(a[0], D, kvq=a[1], scales=a[2])
-        q.qift_kv4_quant(b[0], D, kvq=b[1], scales=b[2])
+        pair(a, b)
         e1.record()
     torch.cuda.synchronize()
     fmed = float(np.median([e0.elapsed_time(e1) for e0, e1 in evs]))
     extra["kv4_llama7b_K_and_V"] = {"T": T, "H": H, "D": D, "ms_K_and_V": round(med, 4),
                                     "GBps": round(kv_bytes / med / 1e6, 1),
                                     "frac_of_hbm_peak": round(kv_bytes / med / 1e6 / HBM_PEAK_GBS, 4),
-                                    "note": "cycled over 8 buffer sets (1.3 GB), the 8 calls replayed from one HIP graph",
+                                    "note": "qift_kv4_quant_kv (K and V of a layer in one launch), cycled over 4 layers' K and V (1.3 GB), the 4 calls replayed from one HIP graph",
+                                    "ms_K_and_V_two_calls": round(med2, 4),
+                                    "frac_of_hbm_peak_two_calls": round(kv_bytes / med2 / 1e6 / HBM_PEAK_GBS, 4),
                                     "ms_K_and_V_after_flush": round(fmed, 4),
                                     "GBps_after_flush": round(kv_bytes / fmed / 1e6, 1)}
-    del sets, flush
+    del sets, layers, flush
     extra["kv4_attention_decode_llama7b"] = kv4_attention_bench(q, torch, dev)
     extra["level_sets_llama7b_q_proj"] = level_set_comparison(q, torch, dev)
     extra["gptq_llama7b_up_proj"] = gptq_bench(q, torch, dev)

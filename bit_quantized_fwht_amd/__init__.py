@@ -73,6 +73,7 @@ def _load():
         "qift_rotate_quant_act": [vp, c_st, i64, i64, i32, vp, vp, vp, vp],
         "qift_w2a4_linear": [vp, vp, i64, i64, vp, vp, c_st, c_st, i64, vp, c_st, vp],
         "qift_kv4_quant": [vp, c_st, i64, i64, i64, i32, vp, vp, vp],
+        "qift_kv4_quant_kv": [vp, vp, c_st, i64, i64, i64, i32, vp, vp, vp, vp, vp],
         "qift_rotate_w2a4_linear": [vp, c_st, i64, i64, i32, vp, vp, vp, vp, c_st, c_st,
                                     ctypes.c_uint32, i64, vp, c_st, vp],
         "qift_linear_group_workspace_bytes": [vp, i32, ctypes.POINTER(ctypes.c_size_t)],
@@ -526,6 +527,28 @@ def qift_kv4_quant(KV, had_block: int, kvq=None, scales=None, stream=None):
     return kvq, scales
 
 
+def qift_kv4_quant_kv(K, V, had_block: int, kq=None, ks=None, vq=None, vs=None, stream=None):
+    """K and V [T, H, D] (same shape and dtype, bfloat16/float32) of one layer
+    in one call -> (kq, ks, vq, vs): the results of qift_kv4_quant on each."""
+    _dev_tensor(K, "K", (torch.float32, torch.bfloat16))
+    _dev_tensor(V, "V", (K.dtype,))
+    if K.shape != V.shape or K.device != V.device:
+        raise ValueError("K and V must have the same shape and device")
+    T, H, D = K.shape
+    outs = []
+    for name, t, shape, dt in (("kq", kq, (T, H, D // 2), torch.uint8), ("ks", ks, (T, H), torch.float32),
+                               ("vq", vq, (T, H, D // 2), torch.uint8), ("vs", vs, (T, H), torch.float32)):
+        if t is None:
+            t = torch.empty(shape, dtype=dt, device=K.device)
+        _dev_tensor(t, name, (dt,))
+        outs.append(t)
+    kq, ks, vq, vs = outs
+    st = _C.qift_kv4_quant_kv(_ptr(K), _ptr(V), _TORCH_TO_QIFT[K.dtype], T, H, D, had_block,
+                              _ptr(kq), _ptr(ks), _ptr(vq), _ptr(vs), _stream(stream, K.device))
+    _check(st, "qift_kv4_quant_kv")
+    return kq, ks, vq, vs
+
+
 def qift_kv4_attention_workspace_bytes(S: int, T: int, H: int, D: int) -> int:
     n = ctypes.c_size_t(0)
     _check(_C.qift_kv4_attention_workspace_bytes(S, T, H, D, ctypes.byref(n)),
@@ -700,6 +723,7 @@ class LinearGroup:
 
 __all__ = ["load_library", "QiftUnavailable", "qift_quantize_weights", "qift_rotate_quant_act",
            "qift_rotate_quant_act_batched", "RotateBatch", "qift_w2a4_linear", "qift_kv4_quant",
+           "qift_kv4_quant_kv",
            "LinearGroup", "QiftError", "qift_linear_desc", "LEVELS", "status_string", "last_error",
            "abi_version", "code_words_per_row", "padded_channels", "LIB_PATH", "SCALE_RULES",
            "level_table_word", "scale_entries", "qift_kv4_attention_decode", "qift_kv4_attention_workspace_bytes",

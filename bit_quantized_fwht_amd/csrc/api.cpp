@@ -309,8 +309,8 @@ qift_status qift_rotate_w2a4_linear(const void* X, qift_dtype x_dtype, int64_t M
   return hip_result(qift::launch_linear_prefill(d, sf16, y_dtype, s), "qift_rotate_w2a4_linear prefill launch");
 }
 
-qift_status qift_kv4_quant(const void* KV, qift_dtype dtype, int64_t T, int64_t H, int64_t D,
-                           int32_t had_block, uint8_t* kvq, float* scales, qift_stream stream) {
+static qift_status check_kv4(const void* KV, qift_dtype dtype, int64_t T, int64_t H, int64_t D,
+                             int32_t had_block, const uint8_t* kvq, const float* scales) {
   if (dtype != QIFT_F32 && dtype != QIFT_BF16)
     return fail(QIFT_ERR_INVALID_ARG, "dtype must be F32 or BF16");
   if (T < 0 || H < 0) return fail(QIFT_ERR_INVALID_ARG, "negative T or H");
@@ -319,14 +319,44 @@ qift_status qift_kv4_quant(const void* KV, qift_dtype dtype, int64_t T, int64_t 
   qift_status st = check_had_block(had_block, D, D);
   if (st != QIFT_OK) return st;
   const int64_t rows = T * H;
-  if (rows == 0) return ok();
+  if (rows == 0) return QIFT_OK;
   if (rows / 8 + 1 > kMaxGrid) return fail(QIFT_ERR_UNSUPPORTED, "T*H too large");
   if (!KV || !kvq || !scales) return fail(QIFT_ERR_INVALID_ARG, "null buffer");
   if (!aligned(KV, 16) || !aligned(kvq, 16) || !aligned(scales, 4))
     return fail(QIFT_ERR_ALIGNMENT, "KV and kvq must be 16-byte aligned, scales 4-byte");
-  return hip_result(qift::launch_kv4(KV, dtype == QIFT_BF16, rows, (int)D, had_block, kvq, scales,
+  return QIFT_OK;
+}
+
+qift_status qift_kv4_quant(const void* KV, qift_dtype dtype, int64_t T, int64_t H, int64_t D,
+                           int32_t had_block, uint8_t* kvq, float* scales, qift_stream stream) {
+  qift_status st = check_kv4(KV, dtype, T, H, D, had_block, kvq, scales);
+  if (st != QIFT_OK) return st;
+  if (T * H == 0) return ok();
+  return hip_result(qift::launch_kv4(KV, dtype == QIFT_BF16, T * H, (int)D, had_block, kvq, scales,
                                      reinterpret_cast<hipStream_t>(stream)),
                     "qift_kv4_quant launch");
+}
+
+static bool ranges_overlap(const void* a, const void* b, size_t bytes) {
+  const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+  return x < y + bytes && y < x + bytes;
+}
+
+qift_status qift_kv4_quant_kv(const void* K, const void* V, qift_dtype dtype, int64_t T,
+                              int64_t H, int64_t D, int32_t had_block, uint8_t* kq, float* ks,
+                              uint8_t* vq, float* vs, qift_stream stream) {
+  qift_status st = check_kv4(K, dtype, T, H, D, had_block, kq, ks);
+  if (st != QIFT_OK) return st;
+  st = check_kv4(V, dtype, T, H, D, had_block, vq, vs);
+  if (st != QIFT_OK) return st;
+  const int64_t rows = T * H;
+  if (rows == 0) return ok();
+  if (ranges_overlap(kq, vq, (size_t)(rows * (D / 2))) ||
+      ranges_overlap(ks, vs, (size_t)rows * sizeof(float)))
+    return fail(QIFT_ERR_INVALID_ARG, "the outputs of K and V overlap");
+  return hip_result(qift::launch_kv4_pair(K, V, dtype == QIFT_BF16, rows, (int)D, had_block, kq, ks,
+                                          vq, vs, reinterpret_cast<hipStream_t>(stream)),
+                    "qift_kv4_quant_kv launch");
 }
 
 // --- decode attention over the KV4 cache ------------------------------------------

@@ -271,6 +271,14 @@ __device__ __forceinline__ void kv4_mfma_tile(const v4u (&xb)[NCH], const v4u (&
   }
 }
 
+// The tensors of one launch of the matrix-core kernel: one, or the K and V
+// caches of a layer (same shape), each with its codes and scales.
+struct KvSet {
+  const uint16_t* kv[2];
+  uint8_t* q[2];
+  float* s[2];
+};
+
 // One tile of 16 head vectors per wave. (Waves that walk several tiles with
 // the next tile's loads in flight measured 5-10% slower on the LLaMA-shaped
 // K and V: the loads of all tiles are in flight at once either way, and a
@@ -279,9 +287,8 @@ __device__ __forceinline__ void kv4_mfma_tile(const v4u (&xb)[NCH], const v4u (&
 typedef __attribute__((address_space(3))) void kv_lds_void;
 
 template <int NCH, int LB>
-__global__ __launch_bounds__(64 * kKvMfmaWaves) void kv4_mfma_kernel(
-    const uint16_t* __restrict__ KV, int64_t rows, float norm, uint8_t* __restrict__ kvq,
-    float* __restrict__ scales) {
+__global__ __launch_bounds__(64 * kKvMfmaWaves) void kv4_mfma_kernel(KvSet set, int64_t rows,
+                                                                     int64_t blocks, float norm) {
   static_assert(NCH == 2 || NCH == 4 || NCH == 8, "D = 64, 128 or 256");
   static_assert(LB >= 5 && (1 << LB) <= 32 * NCH, "block between 32 and D");
   constexpr int kPieces = 4 * NCH;     // 16-byte pieces per head vector
@@ -289,7 +296,12 @@ __global__ __launch_bounds__(64 * kKvMfmaWaves) void kv4_mfma_kernel(
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int t = lane & 15, g = lane >> 4;
-  const int64_t r0 = ((int64_t)blockIdx.x * kKvMfmaWaves + wave) * 16;
+  // workgroups 0 .. blocks - 1 take tensor 0, the next blocks tensor 1
+  const int which = blockIdx.x >= blocks;
+  const uint16_t* __restrict__ KV = which ? set.kv[1] : set.kv[0];
+  uint8_t* __restrict__ kvq = which ? set.q[1] : set.q[0];
+  float* __restrict__ scales = which ? set.s[1] : set.s[0];
+  const int64_t r0 = (((int64_t)blockIdx.x - which * blocks) * kKvMfmaWaves + wave) * 16;
   if (r0 >= rows) return;  // uniform over the wave; no workgroup barrier below
   uint8_t* wl = tile_lds[wave];
   // the tile's 16 vectors, one contiguous kilobyte per instruction, straight
@@ -325,25 +337,32 @@ __global__ __launch_bounds__(64 * kKvMfmaWaves) void kv4_mfma_kernel(
 }
 
 template <int NCH, int LB>
-static void launch_kv4_mfma_lb(const void* KV, int64_t rows, int log2b, float norm, uint8_t* kvq,
-                               float* scales, hipStream_t s) {
+static void launch_kv4_mfma_lb(const KvSet& set, int count, int64_t rows, int log2b, float norm,
+                               hipStream_t s) {
   if constexpr ((1 << LB) <= 32 * NCH) {
     if (log2b == LB) {
       const int64_t tiles = (rows + 15) / 16;
-      const dim3 grid((unsigned)((tiles + kKvMfmaWaves - 1) / kKvMfmaWaves));
-      hipLaunchKernelGGL((kv4_mfma_kernel<NCH, LB>), grid, dim3(64 * kKvMfmaWaves), 0, s,
-                         reinterpret_cast<const uint16_t*>(KV), rows, norm, kvq, scales);
+      const int64_t blocks = (tiles + kKvMfmaWaves - 1) / kKvMfmaWaves;
+      hipLaunchKernelGGL((kv4_mfma_kernel<NCH, LB>), dim3((unsigned)(count * blocks)),
+                         dim3(64 * kKvMfmaWaves), 0, s, set, rows, blocks, norm);
       return;
     }
-    launch_kv4_mfma_lb<NCH, LB + 1>(KV, rows, log2b, norm, kvq, scales, s);
+    launch_kv4_mfma_lb<NCH, LB + 1>(set, count, rows, log2b, norm, s);
   }
 }
 
-// log2b in [5, log2 D]
-template <int NCH>
-static void launch_kv4_mfma(const void* KV, int64_t rows, int log2b, float norm, uint8_t* kvq,
-                            float* scales, hipStream_t s) {
-  launch_kv4_mfma_lb<NCH, 5>(KV, rows, log2b, norm, kvq, scales, s);
+// bfloat16 vectors of 64, 128 or 256 elements with a block of at least 32 run
+// on the matrix cores
+static bool kv4_mfma_ok(int bf16, int D, int had_block) {
+  return bf16 && had_block >= 32 && (D == 64 || D == 128 || D == 256);
+}
+
+// count tensors (1 or 2) of rows vectors each in one launch; log2b in [5, log2 D]
+static void launch_kv4_mfma(const KvSet& set, int count, int64_t rows, int D, int log2b,
+                            float norm, hipStream_t s) {
+  if (D == 64) launch_kv4_mfma_lb<2, 5>(set, count, rows, log2b, norm, s);
+  else if (D == 128) launch_kv4_mfma_lb<4, 5>(set, count, rows, log2b, norm, s);
+  else launch_kv4_mfma_lb<8, 5>(set, count, rows, log2b, norm, s);
 }
 
 template <int E, int L, bool kFull>
@@ -368,17 +387,20 @@ static void launch_kv4_l(const void* KV, int bf16, int64_t rows, int log2b, floa
     launch_kv4_f<E, L, false>(KV, bf16, rows, log2b, norm, kvq, scales, s);
 }
 
-hipError_t launch_kv4(const void* KV, int bf16, int64_t rows, int D, int had_block, uint8_t* kvq,
-                      float* scales, hipStream_t s) {
+static int kv4_log2(int had_block) {
   int log2b = 0;
   while ((1 << log2b) < had_block) ++log2b;
+  return log2b;
+}
+
+hipError_t launch_kv4(const void* KV, int bf16, int64_t rows, int D, int had_block, uint8_t* kvq,
+                      float* scales, hipStream_t s) {
+  const int log2b = kv4_log2(had_block);
   const float norm = (float)(1.0 / __builtin_sqrt((double)had_block));
-  // bfloat16 vectors of 64, 128 or 256 elements with a block of at least 32
-  // on the matrix cores
-  if (bf16 && had_block >= 32 && (D == 64 || D == 128 || D == 256)) {
-    if (D == 64) launch_kv4_mfma<2>(KV, rows, log2b, norm, kvq, scales, s);
-    else if (D == 128) launch_kv4_mfma<4>(KV, rows, log2b, norm, kvq, scales, s);
-    else launch_kv4_mfma<8>(KV, rows, log2b, norm, kvq, scales, s);
+  if (kv4_mfma_ok(bf16, D, had_block)) {
+    const KvSet set{{reinterpret_cast<const uint16_t*>(KV), nullptr}, {kvq, nullptr},
+                    {scales, nullptr}};
+    launch_kv4_mfma(set, 1, rows, D, log2b, norm, s);
     return hipGetLastError();
   }
   switch (D) {
@@ -390,6 +412,24 @@ hipError_t launch_kv4(const void* KV, int bf16, int64_t rows, int D, int had_blo
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
+}
+
+// K and V of one layer: one launch on the matrix-core path (each launch has a
+// ramp at its start and a tail at its end that one launch of twice the rows
+// pays once), else one launch each
+hipError_t launch_kv4_pair(const void* K, const void* V, int bf16, int64_t rows, int D,
+                           int had_block, uint8_t* kq, float* ks, uint8_t* vq, float* vs,
+                           hipStream_t s) {
+  if (kv4_mfma_ok(bf16, D, had_block)) {
+    const KvSet set{{reinterpret_cast<const uint16_t*>(K), reinterpret_cast<const uint16_t*>(V)},
+                    {kq, vq}, {ks, vs}};
+    launch_kv4_mfma(set, 2, rows, D, kv4_log2(had_block),
+                    (float)(1.0 / __builtin_sqrt((double)had_block)), s);
+    return hipGetLastError();
+  }
+  hipError_t e = launch_kv4(K, bf16, rows, D, had_block, kq, ks, s);
+  if (e != hipSuccess) return e;
+  return launch_kv4(V, bf16, rows, D, had_block, vq, vs, s);
 }
 
 }  // namespace qift

@@ -297,6 +297,9 @@ hipError_t launch_quantize_weights(const void* W, int w_bf16, int64_t N, int64_t
                                    void* scales, int scale_f16, hipStream_t s);
 hipError_t launch_kv4(const void* KV, int bf16, int64_t rows, int D, int had_block, uint8_t* kvq,
                       float* scales, hipStream_t s);
+hipError_t launch_kv4_pair(const void* K, const void* V, int bf16, int64_t rows, int D,
+                           int had_block, uint8_t* kq, float* ks, uint8_t* vq, float* vs,
+                           hipStream_t s);
 int64_t kv4_attn_tokens_per_run(int64_t S, int64_t T, int H);
 size_t kv4_attn_workspace_bytes(int64_t S, int64_t T, int H);
 hipError_t kv4_attn_scratch(float** ptr);

@@ -94,7 +94,7 @@
 extern "C" {
 #endif
 
-#define QIFT_ABI_VERSION 7
+#define QIFT_ABI_VERSION 8
 
 typedef enum {
   QIFT_OK = 0,
@@ -321,6 +321,26 @@ qift_status qift_rotate_w2a4_linear(const void* X, qift_dtype x_dtype, int64_t M
  */
 qift_status qift_kv4_quant(const void* KV, qift_dtype dtype, int64_t T, int64_t H, int64_t D,
                            int32_t had_block, uint8_t* kvq, float* scales, qift_stream stream);
+
+/*
+ * qift_kv4_quant_kv -- qift_kv4_quant on the K and V caches of one layer in
+ * one call (the KV4 of rotated W2A4/KV4 inference, Qift abstract): K and V
+ * are quantized exactly as two qift_kv4_quant calls would, with the same
+ * results. On the matrix-core path (bfloat16, D = 64, 128 or 256,
+ * had_block >= 32) both tensors share one launch, which pays the ramp at the
+ * start and the tail at the end of a launch once instead of twice; other
+ * shapes run two launches.
+ *
+ *   K, V      [T, H, D], both of dtype (bfloat16 or float32), 16-byte aligned
+ *   kq, vq    out: [T, H, D/2] int4 pairs of K and of V, 16-byte aligned
+ *   ks, vs    out: [T, H] float32 scales of K and of V
+ * Limits and errors as qift_kv4_quant; in addition kq and vq must not
+ * overlap, nor ks and vs (QIFT_ERR_INVALID_ARG), and no output may overlap
+ * K or V (not checked). T*H = 0 is a no-op.
+ */
+qift_status qift_kv4_quant_kv(const void* K, const void* V, qift_dtype dtype, int64_t T,
+                              int64_t H, int64_t D, int32_t had_block, uint8_t* kq, float* ks,
+                              uint8_t* vq, float* vs, qift_stream stream);
 
 /*
  * qift_kv4_attention_decode -- decode attention over a KV4 cache (the

@@ -33,10 +33,10 @@ def test_library_loads_and_exports_every_declared_symbol():
     lib = q.load_library()
     names = declared_functions()
     assert "qift_w2a4_linear" in names and "qift_kv4_quant" in names
-    assert len(names) == 21, names
+    assert len(names) == 22, names
     for n in names:
         assert hasattr(lib, n), n
-    assert q.abi_version() == 7
+    assert q.abi_version() == 8
     for s in range(5):
         assert q.status_string(s).startswith("QIFT_")
 
@@ -210,6 +210,37 @@ def test_kv4_rejects(kw, status):
 
 def test_kv4_empty_is_noop():
     assert kv(T=0, KV=None, kvq=None, scales=None) == q.QIFT_OK
+
+
+def kv_pair(**kw):
+    args = dict(K=A16, Vt=A16b, d=q.QIFT_BF16, T=4, H=2, D=128, B=128, kq=A16c, ks=A16d,
+                vq=A16e, vs=V(0x60000))
+    args.update(kw)
+    return q._C.qift_kv4_quant_kv(args["K"], args["Vt"], args["d"], args["T"], args["H"],
+                                  args["D"], args["B"], args["kq"], args["ks"], args["vq"],
+                                  args["vs"], None)
+
+
+# T * H = 8 vectors of D = 128: 512 bytes of codes and 32 bytes of scales each
+@pytest.mark.parametrize("kw,status", [
+    (dict(D=96, B=32), q.QIFT_ERR_UNSUPPORTED),
+    (dict(B=256), q.QIFT_ERR_UNSUPPORTED),
+    (dict(B=12), q.QIFT_ERR_INVALID_ARG),
+    (dict(d=q.QIFT_I32), q.QIFT_ERR_INVALID_ARG),
+    (dict(Vt=V(0x20002)), q.QIFT_ERR_ALIGNMENT),
+    (dict(vq=V(0x50008)), q.QIFT_ERR_ALIGNMENT),
+    (dict(K=None), q.QIFT_ERR_INVALID_ARG),
+    (dict(vs=None), q.QIFT_ERR_INVALID_ARG),
+    (dict(H=-1), q.QIFT_ERR_INVALID_ARG),
+    (dict(vq=V(0x30000 + 496)), q.QIFT_ERR_INVALID_ARG),   # V's codes overlap K's by 16 bytes
+    (dict(vs=V(0x40000 + 28)), q.QIFT_ERR_INVALID_ARG),    # V's scales overlap K's by 4 bytes
+])
+def test_kv4_pair_rejects(kw, status):
+    assert kv_pair(**kw) == status
+
+
+def test_kv4_pair_empty_is_noop():
+    assert kv_pair(T=0, K=None, Vt=None, kq=None, ks=None, vq=None, vs=None) == q.QIFT_OK
 
 
 def make_desc(**kw):

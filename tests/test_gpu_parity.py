@@ -412,6 +412,41 @@ def test_kv4_matches_oracle(D, B):
         assert np.array_equal(qg, qo.astype(np.int64))
 
 
+@pytest.mark.parametrize("D,B,dt", [(128, 128, "bf16"), (128, 32, "bf16"), (64, 64, "bf16"),
+                                    (256, 64, "bf16"), (128, 64, "f32"), (32, 8, "bf16")])
+def test_kv4_pair_matches_two_calls_and_oracle(D, B, dt):
+    """qift_kv4_quant_kv: K and V of one layer in one call (one launch on the
+    matrix-core path, bfloat16 with a block of at least 32; two otherwise)
+    give exactly the codes and scales of two qift_kv4_quant calls, and the
+    oracle's. T * H = 185 vectors: the last 16-vector tile of each tensor is
+    partial. K's and V's codes sit back to back in one buffer, and so do
+    their scales (adjacent outputs), with canaries after V's."""
+    T, H = 37, 5
+    cast = si.to_bf16 if dt == "bf16" else (lambda a: torch.from_numpy(a))
+    Kt = cast(si.kv(T, H, D, seed=3 * D + B)).to(DEV)
+    Vt = cast(si.kv(T, H, D, seed=3 * D + B + 1)).to(DEV)
+    say(f"kv4 pair T={T} H={H} D={D} B={B} {dt}")
+    n = T * H
+    codes, gq = guarded((2 * n, D // 2), torch.uint8)
+    scs, gs = guarded((2 * n,), torch.float32)
+    kq, vq = codes[:n].view(T, H, D // 2), codes[n:].view(T, H, D // 2)
+    ks, vs = scs[:n].view(T, H), scs[n:].view(T, H)
+    q.qift_kv4_quant_kv(Kt, Vt, B, kq=kq, ks=ks, vq=vq, vs=vs)
+    k1, s1 = q.qift_kv4_quant(Kt, B)
+    v1, t1 = q.qift_kv4_quant(Vt, B)
+    sync()
+    check_guard(gq, "codes")
+    check_guard(gs, "scales")
+    assert torch.equal(kq, k1) and torch.equal(vq, v1)
+    assert torch.equal(ks, s1) and torch.equal(vs, t1)
+    for X, cq, sc in ((Kt, kq, ks), (Vt, vq, vs)):
+        xv = si.bf16_values(X) if dt == "bf16" else X.cpu().numpy().astype(np.float64)
+        qo, so, _ = O.kv4_quant(xv, B)
+        assert np.allclose(sc.cpu().numpy(), so, rtol=1e-6, atol=0)
+        xo64 = O.rotate(xv.reshape(T * H, D), B).reshape(T, H, D)
+        check_act_codes(O.unpack_int4(cq.cpu().numpy()), qo, xo64, so)
+
+
 @pytest.mark.parametrize("D", [16, 64, 256])
 def test_kv4_exact_ties_after_rotation(D):
     """Head vectors whose rotated values are exact rounding ties: z holds
