@@ -357,6 +357,30 @@ def time_graph(torch, calls, reps=20, warmup=3):
     return med / len(calls), mn / len(calls)
 
 
+def fused_prefill_shapes(q, torch, dev, levels, M, sigma, shapes):
+    """Prefill GEMMs of linears that read the same input, with their weights
+    concatenated along N (one launch; per-channel scales make the codes those
+    of the separate linears): bfloat16 output, M tokens."""
+    import synth_inputs as si
+    out = {}
+    for name, K, N, B in shapes:
+        W = si.device_weights(N, K, seed=5, sigma=sigma, device=dev)
+        cw, sw = q.qift_quantize_weights(W, B, levels, torch.float16)
+        del W
+        X = si.device_activations(M, K, seed=6, device=dev)
+        xq, sa, _ = q.qift_rotate_quant_act(X, B)
+        Y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        med, _, _ = time_fn(torch, lambda: q.qift_w2a4_linear(xq, sa, cw, sw, levels, Y=Y), 20,
+                            warmup=PREFILL_WARMUP)
+        ops = 2.0 * M * N * K
+        out[name] = {"M": M, "K": K, "N": N, "gemm_ms": round(med, 4),
+                     "TOPS": round(ops / med / 1e9, 1),
+                     "frac_of_int8_peak": round(ops / med / 1e9 / INT8_PEAK_TOPS, 4)}
+        del cw, sw, X, xq, sa, Y
+        torch.cuda.empty_cache()
+    return out
+
+
 def vendor_int8_gemm(torch, M, K, N, dev):
     """Context only, not this library's path: the vendor int8 GEMM
     (torch._int_mm, int8 [M, K] x int8 [K, N] -> int32, i.e. 8-bit weights
@@ -1057,6 +1081,11 @@ def measure_extras(q, torch, dev, stack, args):
                           "TOPS_incl_rotate": round(ops / (pre[name]["gemm_ms"] + rmed) / 1e9, 1)})
         pre[name]["vendor_int8_gemm"] = vendor_int8_gemm(torch, M, K, N, dev)
         del cw, sw, X, xq, sa
+    # the linears of a layer that read the same input, as one GEMM over their
+    # concatenated weights (as a prefill step runs them): q/k/v and gate/up
+    pre["fused"] = fused_prefill_shapes(q, torch, dev, "mnz", 2048, 0.02,
+                                        (("qkv_proj", 4096, 3 * 4096, 4096),
+                                         ("gate_up_proj", 4096, 2 * 11008, 4096)))
     extra["prefill_llama7b_mnz"] = pre
 
     # LLaMA-3.1-8B-shaped PoT layer: decode over 32 copies; prefill M = 4096
@@ -1089,6 +1118,11 @@ def measure_extras(q, torch, dev, stack, args):
             del Y
         pf[name]["vendor_int8_gemm"] = vendor_int8_gemm(torch, M, K, N, dev)
         del cw, sw, X, xq, sa
+    # k/v (1024 channels each: 256 tiles of 128 x 128, half a round of
+    # workgroup slots) and q/k/v as one GEMM each, as a prefill step runs them
+    pf["fused"] = fused_prefill_shapes(q, torch, dev, "pot", 4096, 0.015,
+                                       (("kv_proj", 4096, 2 * 1024, 4096),
+                                        ("qkv_proj", 4096, 4096 + 2 * 1024, 4096)))
     pot["prefill_M4096"] = pf
     extra["llama31_8b_pot"] = pot
 
