@@ -13,7 +13,8 @@
 // quarter of D) pair and one of 32 token slots: it holds 32 rotated query
 // values, reads 16 bytes of K and 16 bytes of V codes per token, sums its
 // quarter of the dot product (the four quarters meet by DPP quad moves) and
-// keeps an online softmax (running max m, sum l, 32 accumulators), four
+// keeps an online softmax (reference point m, kept within a fixed slack of
+// the running maximum, sum l, 32 accumulators), four
 // tokens' loads in flight. The token
 // slots of a head are merged through LDS and the workgroup writes (m, l,
 // o'[D]) per head. Runs are sized for about 512 workgroups in all, so a head
@@ -82,6 +83,11 @@ __device__ __forceinline__ void attn_merge(float& m, float& l, float* acc, float
 // need 226 registers instead of 162; a once-per-group softmax rescale with
 // 4-token groups needs 256 and runs 35% slower)
 constexpr int kAttnU = 2;
+// how far a score may exceed the state's reference point before the state is
+// rescaled: p = exp(score - m) <= e^8, so l and acc stay far inside the
+// float32 range (at most T e^8 times the values of a state kept at the
+// running maximum)
+constexpr float kAttnSlack = 8.0f;
 template <typename TQ>
 __global__ __launch_bounds__(kAttnThreads) void kv4_attn_partial_kernel(
     const TQ* __restrict__ q, int64_t T, int H, int log2b, float norm, float softmax_scale,
@@ -119,10 +125,9 @@ __global__ __launch_bounds__(kAttnThreads) void kv4_attn_partial_kernel(
   // every lane loads from a valid row: a token past the run reads the run's
   // last row, and compute() skips it after its dot product (whose quad sum
   // every lane takes part in), so the loads need no per-lane branch and no
-  // zeroing; groups past the last are skipped by a branch that is the same
-  // for the whole workgroup, except the first two (a run of one group reads
-  // its last row for group 1), so that the query's wait below counts exactly
-  // the sixteen loads issued after it
+  // zeroing. Groups past the last are not loaded, except group 1 of a run
+  // of one group (its last row again), so that the query's wait below counts
+  // exactly the sixteen loads issued after it
   auto load = [&](Grp& G, int64_t g) {
 #pragma unroll
     for (int u = 0; u < kAttnU; ++u) {
@@ -185,18 +190,25 @@ __global__ __launch_bounds__(kAttnThreads) void kv4_attn_partial_kernel(
       for (int j = 0; j < kAttnQ; ++j) dot = fmaf(qv[j], c[j], dot);
       dot += quad_xor<1>(dot);
       dot += quad_xor<2>(dot);
-      if (t0 + slot + kAttnP * (kAttnU * g + u) >= t1) continue;
-      const float sc = dot * G.ks[u] * softmax_scale;
-      if (sc > m) {
-        // a new running maximum (every token early on, rarely later): the
-        // state is rescaled only then (0 on the first token, m = -inf)
+      // a token past the run takes the score -inf and the weight 0 (no
+      // branch: a branch around the update made the compiler wait for more
+      // of the other group's loads)
+      const bool valid = t0 + slot + kAttnP * (kAttnU * g + u) < t1;
+      const float sc = valid ? dot * G.ks[u] * softmax_scale : -__builtin_huge_valf();
+      if (sc > m + kAttnSlack) {
+        // the reference point m of the state moves only when a score exceeds
+        // it by more than the slack (the first token, with m = -inf; rarely
+        // later): a wave takes this branch whenever one of its lanes does, so
+        // moving m on every new maximum rescaled the state on most tokens.
+        // Every term of l and acc carries the same factor exp(-m), which
+        // cancels in acc / l and in the merges; p stays below exp(slack).
         const float alpha = __expf(m - sc);
         l *= alpha;
 #pragma unroll
         for (int j = 0; j < kAttnQ; ++j) acc[j] *= alpha;
         m = sc;
       }
-      const float p = __expf(sc - m);
+      const float p = valid ? __expf(sc - m) : 0.f;
       l += p;
       const float pv = p * G.vs[u];
       int4x32_x16(G.v[u], c);
@@ -204,14 +216,24 @@ __global__ __launch_bounds__(kAttnThreads) void kv4_attn_partial_kernel(
       for (int j = 0; j < kAttnQ; ++j) acc[j] = fmaf(pv, c[j], acc[j]);
     }
   };
-  for (int64_t g = 0; g < n_grp; g += 2) {
+  // steady state: every load of the loop body is unconditional, so the wait
+  // for a group counts exactly the other group's loads issued after it (a
+  // load under a branch made the compiler wait for all loads where the
+  // branches met, emptying the second buffer); the last two or three groups
+  // follow the loop
+  int64_t g = 0;
+  for (; g + 3 < n_grp; g += 2) {
     compute(ga, g);
-    if (g + 2 < n_grp) load(ga, g + 2);
-    if (g + 1 < n_grp) {
-      compute(gb, g + 1);
-      if (g + 3 < n_grp) load(gb, g + 3);
-    }
+    load(ga, g + 2);
+    __builtin_amdgcn_sched_barrier(0);  // issued before the other group is used
+    compute(gb, g + 1);
+    load(gb, g + 3);
+    __builtin_amdgcn_sched_barrier(0);
   }
+  compute(ga, g);
+  if (g + 2 < n_grp) load(ga, g + 2);
+  if (g + 1 < n_grp) compute(gb, g + 1);
+  if (g + 2 < n_grp) compute(ga, g + 2);
 
   // merge the token slots of each (head, quarter): the 8 slots of a wave
   // (lanes 8 apart) by shuffles, then the 4 waves through LDS
