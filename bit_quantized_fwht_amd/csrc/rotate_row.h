@@ -218,14 +218,21 @@ __device__ __forceinline__ void rotate_row_finish(const uint32_t raw[Q][16],
       }
     }
   } else {
-    // 4. stages 8.. in one pass through the padded LDS row
+    // 4. stages 8.. in one pass through the padded LDS row. The values go in
+    //    up to their sign sigma, which depends only on the low four bits of
+    //    the group index (the lane bits of stages 4-7; NT is a multiple of
+    //    16). A thread of the pass combines elements 256 apart, i.e. groups
+    //    16 apart, which share those bits and so sigma: the pass's sums are
+    //    the true ones times that common sigma, and every group comes back
+    //    with the sigma it went in with, which the quantizer folds into its
+    //    reciprocal as in the register path (16 fewer multiplies a group).
 #pragma unroll
     for (int q = 0; q < kQ; ++q) {
       const int grp = tid + q * NT;
       if (grp < groups) {
         float* dst = row + 17 * grp;
 #pragma unroll
-        for (int j = 0; j < 16; ++j) dst[j] = sigma * v[q][j];
+        for (int j = 0; j < 16; ++j) dst[j] = v[q][j];
       }
     }
     lds_barrier();
@@ -249,8 +256,8 @@ __device__ __forceinline__ void rotate_row_finish(const uint32_t raw[Q][16],
   const bool fast = rint_path_ok(rs);
   if (tid == 0) *s_out = s;
   // 6. quantize 16 consecutive elements per group: x = the rotated value up
-  //    to sigma (sigma = 1 on the LDS path), y = x * sigma / s
-  const float sg = in_regs ? sigma : 1.f;
+  //    to sigma (on both paths), y = x * sigma / s
+  const float sg = sigma;
   // v * sg * (norm / s) is within three roundings of x' / s with
   // x' = fl(v * norm) the rotated value (int4x8_rint_fma's margin covers it)
   const float rl = sg * (norm * rs);
