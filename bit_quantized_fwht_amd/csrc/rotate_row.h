@@ -15,7 +15,7 @@ constexpr int kRowThreads = 256;
 //
 // Each thread owns groups of 16 consecutive elements, loaded straight into
 // registers (32 bytes bf16 / 64 bytes float). Butterfly stages 0-3 run inside
-// a group and stages 4-7 between the lanes holding neighbouring groups
+// a group and stages 4-7 between the lanes holding the partner groups
 // (rotate_row_fast below), so rows with blocks up to 256 never touch LDS.
 // For larger blocks the row is staged in LDS with one pad word per 16 floats
 // (element e at e + e / 16): the 16 stores of a thread hit 16 consecutive
@@ -111,23 +111,34 @@ __device__ __forceinline__ void widen16<float>(const uint32_t w[16], float v[16]
 
 // One row on the fast path, by a workgroup of NT threads (256 for the
 // rotation kernels; 512 or 1024 inside a fused decode linear). A thread owns
-// the groups tid, tid + NT, ... of 16 consecutive elements (at most
+// the groups row_group_of(tid) + q NT, q = 0, 1, ..., of 16 consecutive
+// elements (at most
 // kFastMaxGroups of them, K <= 16384); all of its global loads are issued
 // before any group is transformed, so a long row costs one memory latency
 // rather than one per group.
 //  - stages 0..3 (strides 1..8) inside a group, in registers;
-//  - stages 4..7 (strides 16..128 = groups 1..8 apart = lanes 1..8 apart)
-//    between lanes with DPP (lane_butterfly8; values kept up to a per-lane
-//    sign sigma);
+//  - stages 4..7 (strides 16..128 = groups 1, 2, 4, 8 apart = lanes 1, 2,
+//    7, 8 apart with the layout of row_group_of) between lanes with DPP
+//    (lane_butterfly8; values kept up to a per-lane sign sigma);
 //  - blocks up to 256: the row never goes through LDS; absmax and
 //    quantization work on the registers;
-//  - larger blocks: the true values go to a padded LDS row, stages 8..11 run
-//    in one pass through it, and the quantization reads the row back.
+//  - larger blocks: the values (up to sigma) go to a padded LDS row, stages
+//    8..11 run in one pass through it, and the quantization reads the row
+//    back.
 constexpr int kFastMaxGroups = 4;
 static_assert(kFastMaxGroups * 16 * kRowThreads >= QIFT_MAX_ROW, "fast path covers QIFT_MAX_ROW");
 
 // rows with log2(block) <= kRegLog2B need no LDS row buffer
 constexpr int kRegLog2B = 8;
+
+// The group of 16 elements that lane position t of a row holds (q = 0):
+// within each run of 16 lanes, lanes with bit 2 set hold the groups with
+// their two low index bits inverted (g = t ^ 3 there, else t; a change of
+// basis of the index bits over GF(2), its own inverse). The partner groups
+// of the lane stages, g ^ 1, g ^ 2, g ^ 4 and g ^ 8, then sit in lanes t ^ 1,
+// t ^ 2, t ^ 7 and t ^ 8, each of which one DPP operand reads (with the
+// plain layout, g ^ 4 in lane t ^ 4 took two DPP moves).
+__device__ __forceinline__ int row_group_of(int t) { return t ^ (((t >> 2) & 1) * 3); }
 
 // groups of 16 elements a thread holds for a workgroup of NT threads: enough
 // for the longest row (QIFT_MAX_ROW), or Q when the caller knows its rows
@@ -145,11 +156,11 @@ struct RowGroups {
 template <typename T, int NT, int Q = RowGroups<NT>::kQ>
 __device__ __forceinline__ void rotate_row_load(const T* __restrict__ src, int K,
                                                 uint32_t raw[Q][16]) {
-  const int tid = threadIdx.x;
+  const int tg = row_group_of(threadIdx.x);
   const int groups = K >> 4;
 #pragma unroll
   for (int q = 0; q < Q; ++q) {
-    const int grp = tid + q * NT;
+    const int grp = tg + q * NT;
     load16_raw<T>(src + 16 * (grp < groups ? grp : 0), raw[q]);
   }
 }
@@ -167,6 +178,7 @@ __device__ __forceinline__ void rotate_row_finish(const uint32_t raw[Q][16],
   for (int q = 0; q < kQ; ++q) widen16<T>(raw[q], v[q]);
   const bool in_regs = log2b <= kRegLog2B;
   const int tid = threadIdx.x;
+  const int tg = row_group_of(tid);  // this thread's group for q = 0
   const int groups = K >> 4;
   const int wave_g0 = tid & ~63;  // the wave's first group (q = 0)
   // 2. stages 0..3 in registers (rounds with no group of this wave skipped;
@@ -189,30 +201,31 @@ __device__ __forceinline__ void rotate_row_finish(const uint32_t raw[Q][16],
       }
     }
   }
-  // 3. stages 4..7 between lanes
+  // 3. stages 4..7 between lanes: group index bit H, partner in lane ^ M
+  //    (row_group_of); the upper group of a pair (bit H set) flips its sign
   float sigma = 1.f;
   const int lane_stages = min(log2b, kRegLog2B) - 4;
-#define QIFT_LANE_STAGE(H)                                                 \
+#define QIFT_LANE_STAGE(H, M)                                              \
   {                                                                        \
-    const float c = (tid & (H)) ? -1.f : 1.f;                              \
-    _Pragma("unroll") for (int q = 0; q < kQ; ++q) {           \
-      if (wave_g0 + q * NT < groups) {                            \
-        lane_butterfly8<H>(v[q], c);                                       \
-        lane_butterfly8<H>(v[q] + 8, c);                                   \
+    const float c = (tg & (H)) ? -1.f : 1.f;                               \
+    _Pragma("unroll") for (int q = 0; q < kQ; ++q) {                      \
+      if (wave_g0 + q * NT < groups) {                                     \
+        lane_butterfly8<M>(v[q], c);                                       \
+        lane_butterfly8<M>(v[q] + 8, c);                                   \
       }                                                                    \
     }                                                                      \
     sigma *= c;                                                            \
   }
-  if (lane_stages >= 1) QIFT_LANE_STAGE(1)
-  if (lane_stages >= 2) QIFT_LANE_STAGE(2)
-  if (lane_stages >= 3) QIFT_LANE_STAGE(4)
-  if (lane_stages >= 4) QIFT_LANE_STAGE(8)
+  if (lane_stages >= 1) QIFT_LANE_STAGE(1, 1)
+  if (lane_stages >= 2) QIFT_LANE_STAGE(2, 2)
+  if (lane_stages >= 3) QIFT_LANE_STAGE(4, 7)
+  if (lane_stages >= 4) QIFT_LANE_STAGE(8, 8)
 #undef QIFT_LANE_STAGE
   float mloc = 0.f;  // largest |value| of the row's last stage seen by this thread
   if (in_regs) {
 #pragma unroll
     for (int q = 0; q < kQ; ++q) {
-      if (tid + q * NT < groups) {
+      if (tg + q * NT < groups) {
 #pragma unroll
         for (int j = 0; j < 16; ++j) mloc = fmaxf(mloc, fabsf(v[q][j]));
       }
@@ -228,7 +241,7 @@ __device__ __forceinline__ void rotate_row_finish(const uint32_t raw[Q][16],
     //    reciprocal as in the register path (16 fewer multiplies a group).
 #pragma unroll
     for (int q = 0; q < kQ; ++q) {
-      const int grp = tid + q * NT;
+      const int grp = tg + q * NT;
       if (grp < groups) {
         float* dst = row + 17 * grp;
 #pragma unroll
@@ -264,7 +277,7 @@ __device__ __forceinline__ void rotate_row_finish(const uint32_t raw[Q][16],
   uint2* xrow = reinterpret_cast<uint2*>(xq_row);
 #pragma unroll
   for (int q = 0; q < kQ; ++q) {
-    const int grp = tid + q * NT;
+    const int grp = tg + q * NT;
     if (grp >= groups) continue;
     float x[16];  // x: the stored values (up to sg), then the rotated ones
     if (in_regs) {
