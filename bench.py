@@ -406,7 +406,7 @@ MFMA_WORKGROUPS = 2048   # 8 waves per compute unit, 2 per SIMD
 
 
 def measured_peaks(q, torch, dev):
-    """On-box ceilings beside the published ones: the read-only and copy
+    """Measured ceilings of this GPU beside the published ones: the read-only and copy
     rates of the measurement stream kernel (2 GiB read; 1 GiB copied), the
     int8 matrix-core rate of a register-only MFMA loop, and the shader clock
     read during that loop. Median of 20 timed launches each."""
@@ -689,7 +689,7 @@ def main():
     peaks = None
     if not args.only_headline:
         extra = measure_extras(q, torch, dev, stack, args)
-        log("measuring on-box peaks")
+        log("measuring the GPU's own ceilings")
         peaks = measured_peaks(q, torch, dev)
         extra["measured_peaks"] = peaks
         log(f"  read {peaks['hbm_read_GBps']} GB/s, copy {peaks['hbm_copy_GBps']} GB/s, "
