@@ -48,6 +48,20 @@ __device__ __forceinline__ uint32_t int4x8_rint_fma(const float v[8], float r, f
   return (lo | hi) ^ 0x88888888u;
 }
 
+// the same for four values: codes of v[0..3] * r in the low 16 bits
+__device__ __forceinline__ uint32_t int4x4_rint_fma(const float v[4], float r, float& dmax) {
+  uint32_t e[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const float ym = __builtin_fmaf(v[j], r, kRintMagic8);
+    const float t = ym - kRintMagic8;
+    dmax = fmaxf(dmax, fabsf(__builtin_fmaf(v[j], r, -t)));
+    e[j] = __float_as_uint(ym);
+  }
+  const uint32_t p0 = (e[1] << 4) + e[0], p1 = (e[3] << 4) + e[2];
+  return __builtin_amdgcn_perm(p1, p0, 0x0c0c0400u) ^ 0x8888u;
+}
+
 // the same codes from the exact IEEE division, clamped to [-7, 7] (s == 0
 // gives 0). The clamp binds only when s = fl(absmax / 7) is subnormal: its
 // rounding can then make |x / s| exceed 7.5 (absmax = 8 * 2^-149 gives
@@ -57,6 +71,18 @@ __device__ __forceinline__ uint32_t int4x8_exact(const float x[8], float s) {
   if (s == 0.f) return 0u;
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
+    const int q = min(max((int)rintf(__fdiv_rn(x[j], s)), -7), 7);
+    w |= ((uint32_t)q & 0xFu) << (4 * j);
+  }
+  return w;
+}
+
+// four values: int4x8_exact's codes in the low 16 bits
+__device__ __forceinline__ uint32_t int4x4_exact(const float x[4], float s) {
+  uint32_t w = 0;
+  if (s == 0.f) return 0u;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
     const int q = min(max((int)rintf(__fdiv_rn(x[j], s)), -7), 7);
     w |= ((uint32_t)q & 0xFu) << (4 * j);
   }

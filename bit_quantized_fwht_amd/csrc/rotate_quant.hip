@@ -162,6 +162,143 @@ __global__ __launch_bounds__(kRowThreads) void rotate_quant_act_fast_kernel(
                                      s_a + m, x_rot ? x_rot + m * K : nullptr, row, red);
 }
 
+// Rows of K = 4096 bfloat16 values with one block of 4096: the first five
+// butterfly stages on the matrix cores. For element e = 32 c + k (chunk c,
+// k < 32) the Hadamard sign (-1)^popcount(i & e) splits over (c, k), so H_4096
+// = H_128 (x) H_32: one v_mfma_f32_16x16x32_bf16 applies H_32 to 16 chunks at
+// once, straight from the loaded bfloat16 words (entries +-1: exact products,
+// summed in float32), which replaces the widening and the five stages of
+// strides 1 .. 16 (six of about 24 vector instructions per element). The
+// operand A rows are permuted as for the KV4 matrix-core kernel
+// (h32_operand_bf16), so lane (t = lane % 16, g = lane / 16) receives the
+// outputs 8 g .. 8 g + 7 of the chunk in column t. The seven stages across
+// chunks follow:
+//  - chunk bits 0-3 between the lanes of a 16-lane row with DPP
+//    (lane_butterfly8, values kept up to a sign sigma); the chunk of column t
+//    is 32 w + 16 a + row_group_of(t) (wave w, tile a), so the partners sit at
+//    lane ^ 1, ^ 2, ^ 7, ^ 8;
+//  - chunk bit 4 (the wave's two tiles) in registers;
+//  - chunk bits 5, 6 (the four waves) in one pass through a padded LDS row
+//    (element e at e + 4 (e / 32)): thread T combines the runs of four
+//    elements at 4 T + 1024 j, j = 0..3, whose chunks share bits 0-3 and so
+//    sigma = (-1)^popcount(chunk & 15).
+// Each thread then quantizes its four runs (16 bits of codes each); absmax,
+// scale, codes and the near-tie fallback are the arithmetic of the other
+// rotation kernels.
+constexpr int kMfmaRowK = 4096;
+constexpr int kMfmaRowLds = kMfmaRowK + kMfmaRowK / 8;  // floats, with the pad
+
+__global__ __launch_bounds__(kRowThreads) void rotate_quant_act_mfma4096_kernel(
+    const uint16_t* __restrict__ X, float norm, uint8_t* __restrict__ xq,
+    float* __restrict__ s_a, float* __restrict__ x_rot) {
+  __shared__ __attribute__((aligned(16))) float row[kMfmaRowLds];
+  __shared__ float red[kRowThreads / 64];
+  const int64_t m = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, w = tid >> 6;
+  const int t = lane & 15, g = lane >> 4;
+  const uint16_t* __restrict__ src = X + m * kMfmaRowK;
+  // operand B of tile a: elements 8 g .. 8 g + 7 of chunk c[a] (16 bytes)
+  const int rg = row_group_of(t);
+  int c[2];
+  v4u xb[2];
+#pragma unroll
+  for (int a = 0; a < 2; ++a) {
+    c[a] = 32 * w + 16 * a + rg;
+    xb[a] = *reinterpret_cast<const v4u*>(src + 32 * c[a] + 8 * g);
+  }
+  v4u ha[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) ha[h] = h32_operand_bf16(4 * h + (t & 3), (t >> 2) & g);
+  // v[a][j]: output 32 c[a] + 8 g + j, unnormalized
+  float v[2][8];
+#pragma unroll
+  for (int a = 0; a < 2; ++a) {
+    const bf16x8_t b = __builtin_bit_cast(bf16x8_t, xb[a]);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const v4f y = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+          __builtin_bit_cast(bf16x8_t, ha[h]), b, v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v[a][4 * h + i] = y[i];
+    }
+  }
+  // chunk bits 0-3 between lanes (upper lane of a pair: c = -1)
+#define QIFT_MFMA_ROW_STAGE(H, M)                         {                                                         const float cs = (rg & (H)) ? -1.f : 1.f;               lane_butterfly8<M>(v[0], cs);                           lane_butterfly8<M>(v[1], cs);                         }
+  QIFT_MFMA_ROW_STAGE(1, 1)
+  QIFT_MFMA_ROW_STAGE(2, 2)
+  QIFT_MFMA_ROW_STAGE(4, 7)
+  QIFT_MFMA_ROW_STAGE(8, 8)
+#undef QIFT_MFMA_ROW_STAGE
+  // chunk bit 4: the two tiles
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const float p = v[0][j], q = v[1][j];
+    v[0][j] = p + q;
+    v[1][j] = p - q;
+  }
+  // chunk bits 5, 6 through LDS
+#pragma unroll
+  for (int a = 0; a < 2; ++a) {
+    float* dst = row + 36 * c[a] + 8 * g;
+    *reinterpret_cast<float4*>(dst) = float4{v[a][0], v[a][1], v[a][2], v[a][3]};
+    *reinterpret_cast<float4*>(dst + 4) = float4{v[a][4], v[a][5], v[a][6], v[a][7]};
+  }
+  lds_barrier();
+  float x[4][4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int e = 4 * tid + 1024 * j;
+    const float4 f = *reinterpret_cast<const float4*>(row + e + 4 * (e >> 5));
+    x[j][0] = f.x; x[j][1] = f.y; x[j][2] = f.z; x[j][3] = f.w;
+  }
+#pragma unroll
+  for (int h = 1; h < 4; h <<= 1)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if (!(j & h)) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float p = x[j][i], q = x[j + h][i];
+          x[j][i] = p + q;
+          x[j + h][i] = p - q;
+        }
+      }
+  float mloc = 0.f;
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) mloc = fmaxf(mloc, fabsf(x[j][i]));
+  mloc *= norm;  // rounding is monotonic: max(|v|)*norm == max(|v*norm|)
+  mloc = wave_max_nonneg(mloc);
+  if (lane == 0) red[w] = mloc;
+  lds_barrier();
+  const float amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  const float s = __fdiv_rn(amax, 7.0f);
+  const float rs = s != 0.f ? __fdiv_rn(1.0f, s) : 0.f;
+  const bool fast = rint_path_ok(rs);
+  if (tid == 0) s_a[m] = s;
+  // sigma of this thread's chunks (tid / 8 + 32 j: bits 0-3 = (tid / 8) & 15)
+  const float sg = (__builtin_popcount((tid >> 3) & 15) & 1) ? -1.f : 1.f;
+  const float rl = sg * (norm * rs);
+  uint16_t* xrow = reinterpret_cast<uint16_t*>(xq + m * (kMfmaRowK / 2));
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    float dmax = 0.f;
+    uint32_t code = int4x4_rint_fma(x[j], rl, dmax);
+    const int e = 4 * tid + 1024 * j;
+    if (!(dmax <= 0.49999f) || !fast || x_rot) {
+      float xr[4];  // the true rotated values; fma(., sg, +0) writes zeros as +0
+#pragma unroll
+      for (int i = 0; i < 4; ++i) xr[i] = __builtin_fmaf(x[j][i] * norm, sg, 0.0f);
+      if (!(dmax <= 0.49999f) || !fast) code = int4x4_exact(xr, s);
+      if (x_rot)
+        *reinterpret_cast<float4*>(x_rot + m * kMfmaRowK + e) = float4{xr[0], xr[1], xr[2], xr[3]};
+    }
+    xrow[e / 4] = (uint16_t)code;
+  }
+}
+
 // Several activation matrices in one launch (workgroup b covers row b of the
 // concatenation of their rows), e.g. the inputs of all linears of a decode
 // step, which are too small to fill the chip one at a time.
@@ -283,6 +420,11 @@ hipError_t launch_rotate_quant_act(const void* X, int x_bf16, int64_t M, int64_t
                                    uint8_t* xq, float* s_a, float* x_rot, hipStream_t s) {
   const int lb = ilog2(had_block);
   const float nrm = had_norm(had_block);
+  if (x_bf16 && K == kMfmaRowK && had_block == kMfmaRowK && rotate_fast_ok(X, K, had_block, xq, x_rot)) {
+    hipLaunchKernelGGL(rotate_quant_act_mfma4096_kernel, dim3((unsigned)M), dim3(kRowThreads), 0, s,
+                       reinterpret_cast<const uint16_t*>(X), nrm, xq, s_a, x_rot);
+    return hipGetLastError();
+  }
   if (rotate_fast_ok(X, K, had_block, xq, x_rot)) {
     const size_t lds = lb > kRegLog2B ? (size_t)(K + K / 16) * sizeof(float) : 0;
     const int groups = (int)((K / 16 + kRowThreads - 1) / kRowThreads);  // per thread, 1..4
