@@ -299,6 +299,141 @@ __global__ __launch_bounds__(kRowThreads) void rotate_quant_act_mfma4096_kernel(
   }
 }
 
+// Rows of bfloat16 values with a block of 2^LB = 256, 512 or 1024 elements
+// (any K that is a multiple of the block, up to QIFT_MAX_ROW): the same
+// matrix-core split, with the whole block inside one wave's two tiles of 16
+// chunks, so no stage goes through LDS. The row is cut into groups of 32
+// chunks (1024 elements); wave w takes groups w, w + 4, ... (at most P).
+// Lane (t, g) holds, for group p and tile a, the outputs 8 g .. 8 g + 7 of
+// chunk 32 p + 16 a + row_group_of(t): after H_32 on the matrix cores, chunk
+// bits 0 .. LB - 6 (at most 3) run between lanes by DPP and, for a block of
+// 1024, chunk bit 4 between the tiles in registers. The eight consecutive
+// outputs a lane holds per chunk are one word of codes, stored as they are.
+// Chunks past the row end (K % 1024 != 0, blocks of 256 only) are loaded
+// from chunk 0, never mix with valid ones (their tile half differs in chunk
+// bit 3, which no stage of a 256-block touches), and are neither counted in
+// the absmax nor stored.
+template <int LB, int P>
+__global__ __launch_bounds__(kRowThreads) void rotate_quant_act_mfma_groups_kernel(
+    const uint16_t* __restrict__ X, int K, float norm, uint8_t* __restrict__ xq,
+    float* __restrict__ s_a, float* __restrict__ x_rot) {
+  static_assert(LB >= 8 && LB <= 10, "blocks of 256, 512 or 1024 elements");
+  __shared__ float red[kRowThreads / 64];
+  const int64_t m = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, w = tid >> 6;
+  const int t = lane & 15, g = lane >> 4;
+  const int rg = row_group_of(t);
+  const int nchunks = K >> 5;
+  const uint16_t* __restrict__ src = X + m * K;
+  int c[P][2];
+  bool ok[P][2];
+  v4u xb[P][2];
+#pragma unroll
+  for (int p = 0; p < P; ++p)
+#pragma unroll
+    for (int a = 0; a < 2; ++a) {
+      c[p][a] = 32 * (w + 4 * p) + 16 * a + rg;
+      ok[p][a] = c[p][a] < nchunks;
+      xb[p][a] = *reinterpret_cast<const v4u*>(src + 32 * (ok[p][a] ? c[p][a] : 0) + 8 * g);
+    }
+  v4u ha[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) ha[h] = h32_operand_bf16(4 * h + (t & 3), (t >> 2) & g);
+  // waves with fewer groups skip the rest (uniform per wave)
+  const int ng = ((nchunks + 31) >> 5) - w;  // groups of this wave: ceil(ng / 4)
+  float v[P][2][8];
+#pragma unroll
+  for (int p = 0; p < P; ++p) {
+    if (4 * p >= ng) break;
+#pragma unroll
+    for (int a = 0; a < 2; ++a) {
+      const bf16x8_t b = __builtin_bit_cast(bf16x8_t, xb[p][a]);
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const v4f y = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            __builtin_bit_cast(bf16x8_t, ha[h]), b, v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[p][a][4 * h + i] = y[i];
+      }
+    }
+  }
+  float sigma = 1.f;
+#define QIFT_MFMA_GROUP_STAGE(H, MM)                     \
+  {                                                      \
+    const float cs = (rg & (H)) ? -1.f : 1.f;            \
+    _Pragma("unroll") for (int p = 0; p < P; ++p) {      \
+      if (4 * p < ng) {                                  \
+        lane_butterfly8<MM>(v[p][0], cs);                \
+        lane_butterfly8<MM>(v[p][1], cs);                \
+      }                                                  \
+    }                                                    \
+    sigma *= cs;                                         \
+  }
+  QIFT_MFMA_GROUP_STAGE(1, 1)
+  QIFT_MFMA_GROUP_STAGE(2, 2)
+  QIFT_MFMA_GROUP_STAGE(4, 7)
+  if constexpr (LB >= 9) QIFT_MFMA_GROUP_STAGE(8, 8)
+#undef QIFT_MFMA_GROUP_STAGE
+  if constexpr (LB == 10) {
+#pragma unroll
+    for (int p = 0; p < P; ++p) {
+      if (4 * p >= ng) break;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float x0 = v[p][0][j], x1 = v[p][1][j];
+        v[p][0][j] = x0 + x1;
+        v[p][1][j] = x0 - x1;
+      }
+    }
+  }
+  float mloc = 0.f;
+#pragma unroll
+  for (int p = 0; p < P; ++p) {
+    if (4 * p >= ng) break;
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+      if (ok[p][a]) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) mloc = fmaxf(mloc, fabsf(v[p][a][j]));
+      }
+  }
+  mloc *= norm;  // rounding is monotonic: max(|v|)*norm == max(|v*norm|)
+  mloc = wave_max_nonneg(mloc);
+  if (lane == 0) red[w] = mloc;
+  lds_barrier();
+  const float amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  const float s = __fdiv_rn(amax, 7.0f);
+  const float rs = s != 0.f ? __fdiv_rn(1.0f, s) : 0.f;
+  const bool fast = rint_path_ok(rs);
+  if (tid == 0) s_a[m] = s;
+  const float rl = sigma * (norm * rs);
+  uint32_t* xrow = reinterpret_cast<uint32_t*>(xq + m * (int64_t)(K / 2));
+#pragma unroll
+  for (int p = 0; p < P; ++p) {
+    if (4 * p >= ng) break;
+#pragma unroll
+    for (int a = 0; a < 2; ++a) {
+      if (!ok[p][a]) continue;
+      float dmax = 0.f;
+      uint32_t code = int4x8_rint_fma(v[p][a], rl, dmax);
+      const int e = 32 * c[p][a] + 8 * g;
+      if (!(dmax <= 0.49999f) || !fast || x_rot) {
+        float xr[8];  // the true rotated values; fma(., sigma, +0) writes zeros as +0
+#pragma unroll
+        for (int i = 0; i < 8; ++i) xr[i] = __builtin_fmaf(v[p][a][i] * norm, sigma, 0.0f);
+        if (!(dmax <= 0.49999f) || !fast) code = int4x8_exact(xr, s);
+        if (x_rot) {
+          float4* xo = reinterpret_cast<float4*>(x_rot + m * K + e);
+          xo[0] = float4{xr[0], xr[1], xr[2], xr[3]};
+          xo[1] = float4{xr[4], xr[5], xr[6], xr[7]};
+        }
+      }
+      xrow[e / 8] = code;
+    }
+  }
+}
+
 // Several activation matrices in one launch (workgroup b covers row b of the
 // concatenation of their rows), e.g. the inputs of all linears of a decode
 // step, which are too small to fill the chip one at a time.
@@ -423,6 +558,19 @@ hipError_t launch_rotate_quant_act(const void* X, int x_bf16, int64_t M, int64_t
   if (x_bf16 && K == kMfmaRowK && had_block == kMfmaRowK && rotate_fast_ok(X, K, had_block, xq, x_rot)) {
     hipLaunchKernelGGL(rotate_quant_act_mfma4096_kernel, dim3((unsigned)M), dim3(kRowThreads), 0, s,
                        reinterpret_cast<const uint16_t*>(X), nrm, xq, s_a, x_rot);
+    return hipGetLastError();
+  }
+  // the group kernel where it measured faster than the register-path kernel:
+  // blocks of 1024 in rows of more than 12288 elements (four groups per
+  // wave; 4096 x 14336: 42.7 against 52.2 us). With fewer groups per wave,
+  // or blocks of 256 (2048 x 11008: 17.1 against 14.7 us), its registers
+  // (120 at three groups) cost more resident workgroups than the matrix
+  // cores save.
+  if (x_bf16 && lb == 10 && K > 12288 && K <= QIFT_MAX_ROW &&
+      rotate_fast_ok(X, K, had_block, xq, x_rot)) {
+    hipLaunchKernelGGL((rotate_quant_act_mfma_groups_kernel<10, 4>), dim3((unsigned)M),
+                       dim3(kRowThreads), 0, s, reinterpret_cast<const uint16_t*>(X), (int)K, nrm,
+                       xq, s_a, x_rot);
     return hipGetLastError();
   }
   if (rotate_fast_ok(X, K, had_block, xq, x_rot)) {

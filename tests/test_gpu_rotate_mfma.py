@@ -1,5 +1,6 @@
-"""The matrix-core rotation of bfloat16 rows with K = 4096 and one block of
-4096 (the inputs of the K = 4096 linears of LLaMA-shaped prefill): rotated
+"""The matrix-core rotation of bfloat16 rows: K = 4096 with one block of 4096
+(the inputs of the K = 4096 linears of LLaMA-shaped prefill), and blocks of
+256, 512 and 1024 for any K (the K = 11008 and K = 14336 inputs): rotated
 values against the float64 oracle, the quantizer bit-exact on the kernel's
 own rotated values, exact rounding ties and degenerate rows against the
 oracle."""
@@ -108,3 +109,88 @@ def test_mfma_rotation_degenerate_rows():
     assert np.array_equal(sg.view(np.uint32), so.view(np.uint32))
     assert np.array_equal(qg, qo.astype(np.int64))
     assert np.array_equal(xg, xo32)
+
+
+# ---------------------------------------------------------------------------
+# blocks of 256, 512 and 1024: rows of more than 12288 elements with blocks of
+# 1024 run the matrix-core group kernel (four groups of 1024 elements per
+# wave), the others the register-path kernel; both are held to the same bar
+# ---------------------------------------------------------------------------
+
+def rotate_kb(Xt, Bk, want_rot=True):
+    M, Kk = Xt.shape
+    xq, gq = guarded((M, Kk // 2), torch.uint8)
+    s_a, gs = guarded((M,), torch.float32)
+    xr, gx = guarded((M, Kk), torch.float32) if want_rot else (None, None)
+    q.qift_rotate_quant_act(Xt, Bk, xq=xq, s_a=s_a, x_rot=xr)
+    sync()
+    check_guard(gq, "xq")
+    check_guard(gs, "s_a")
+    if want_rot:
+        check_guard(gx, "x_rot")
+    return (O.unpack_int4(xq.cpu().numpy()), s_a.cpu().numpy(),
+            xr.cpu().numpy() if want_rot else None)
+
+
+@pytest.mark.parametrize("M,Kk,Bk", [(2048, 11008, 256), (1024, 14336, 1024), (64, 4096, 512),
+                                     (33, 2048, 1024), (5, 256, 256), (9, 16384, 256),
+                                     (7, 16384, 1024), (3, 13312, 1024)])
+def test_mfma_group_rotation_rows(M, Kk, Bk):
+    """bfloat16 rows with outlier channels: rotated values within 1e-5 of the
+    float64 rotation on sampled rows, codes equal to the oracle's except at
+    near-ties, codes and scales bit-exact against the oracle's quantizer on
+    the kernel's own rotated values, with and without the rotated output."""
+    Xt = si.device_activations(M, Kk, seed=M + Kk + Bk, device=DEV)
+    say(f"matrix-core group rotation M={M} K={Kk} B={Bk}")
+    qg, sg, xg = rotate_kb(Xt, Bk)
+    qn, sn, _ = rotate_kb(Xt, Bk, want_rot=False)
+    assert np.array_equal(qn, qg) and np.array_equal(sn.view(np.uint32), sg.view(np.uint32))
+    qo_self, so_self = O.quant_sym4(xg)
+    assert np.array_equal(sg.view(np.uint32), so_self.view(np.uint32))
+    assert np.array_equal(qg, qo_self.astype(np.int64))
+    rng = np.random.default_rng(M + Bk)
+    rows = np.unique(np.concatenate([[0, M - 1], rng.choice(M, min(M, 24), replace=False)]))
+    Xv = Xt[torch.from_numpy(rows).to(DEV)].float().cpu().numpy().astype(np.float64)
+    qo, so, _, xo64 = O.rotate_quant_act(Xv, Bk)
+    for i in range(len(rows)):
+        assert np.abs(xg[rows[i]] - xo64[i]).max() <= 1e-5 * np.abs(xo64[i]).max()
+    assert np.allclose(sg[rows], so, rtol=1e-6, atol=0)
+    check_act_codes(qg[rows], qo, xo64, so)
+
+
+def block_hadamard_row(Kk, Bk, blk, i):
+    """Row with H_B row i in block blk and zeros elsewhere."""
+    r = np.zeros(Kk)
+    e = np.arange(Bk)
+    pc = np.array([bin(int(v)).count("1") for v in (e & i)])
+    r[blk * Bk:(blk + 1) * Bk] = np.where(pc % 2 == 0, 1.0, -1.0)
+    return r
+
+
+@pytest.mark.parametrize("Kk,Bk", [(11008, 256), (14336, 1024), (4096, 256), (16384, 1024)])
+def test_mfma_group_rotation_exact_ties(Kk, Bk):
+    """alpha h_i + beta h_j inside one block (the last block of the row
+    among them) rotates to exactly sqrt(B) alpha and sqrt(B) beta (blocks
+    whose sqrt is a power of two, so the normalization is exact); with
+    alpha = 7 the scale is sqrt(B) and the code at j is rint(beta), half to
+    even; zero, constant and subnormal rows equal the oracle's too."""
+    nb = Kk // Bk
+    cases = [(7.0, 1.5, 0, 5, 77), (7.0, 2.5, nb - 1, 100, 3), (-7.0, -0.5, nb // 2, 0, Bk - 1),
+             (7.0, 3.5, nb - 1, Bk - 2, 1), (7.0, -6.5, 1, 64, 65)]
+    rows = [a * block_hadamard_row(Kk, Bk, blk, i) + b * block_hadamard_row(Kk, Bk, blk, j)
+            for a, b, blk, i, j in cases]
+    rng = np.random.default_rng(Kk)
+    tiny = 2.0 ** -133
+    rows += [np.zeros(Kk), np.full(Kk, 3.0), tiny * rng.integers(-100, 101, Kk).astype(np.float64)]
+    X = np.stack(rows)
+    Xt = torch.from_numpy(X.astype(np.float32)).to(DEV).to(torch.bfloat16)
+    assert np.array_equal(Xt.float().cpu().numpy(), X)  # bfloat16-exact
+    say(f"matrix-core group rotation exact ties K={Kk} B={Bk}")
+    qg, sg, xg = rotate_kb(Xt, Bk)
+    qo, so, xo32, _ = O.rotate_quant_act(X, Bk)
+    assert np.array_equal(xg, xo32)
+    assert np.array_equal(sg.view(np.uint32), so.view(np.uint32))
+    assert np.array_equal(qg, qo.astype(np.int64))
+    for r, (a, b, blk, i, j) in enumerate(cases):
+        assert qg[r, blk * Bk + i] == (7 if a > 0 else -7)
+        assert qg[r, blk * Bk + j] == int(np.rint(b))
