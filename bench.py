@@ -1117,6 +1117,15 @@ def measure_extras(q, torch, dev, stack, args):
                              "frac_of_int8_peak" + tag: round(ops / med / 1e9 / INT8_PEAK_TOPS, 4)})
             del Y
         pf[name]["vendor_int8_gemm"] = vendor_int8_gemm(torch, M, K, N, dev)
+        if name == "down_proj":
+            # the rotation of this GEMM's input (K = 14336, blocks of 1024)
+            rmed, _ = time_graph(torch, [lambda: q.qift_rotate_quant_act(X, B, xq=xq, s_a=sa)] * 20)
+            rbytes = M * K * 2 + M * K / 2 + 4 * M
+            pf[name].update({"rotate_quant_ms": round(rmed, 4),
+                             "rotate_quant_GBps": round(rbytes / rmed / 1e6, 1),
+                             "rotate_quant_frac_of_hbm_peak": round(rbytes / rmed / 1e6 / HBM_PEAK_GBS, 4),
+                             "rotate_quant_timing": "per call, 20 calls replayed from a HIP graph",
+                             "TOPS_incl_rotate": round(ops / (pf[name]["gemm_ms"] + rmed) / 1e9, 1)})
         del cw, sw, X, xq, sa
     # k/v (1024 channels each: 256 tiles of 128 x 128, half a round of
     # workgroup slots) and q/k/v as one GEMM each, as a prefill step runs them
