@@ -340,12 +340,12 @@ __global__ __launch_bounds__(kRowThreads) void rotate_quant_act_mfma_groups_kern
   v4u ha[2];
 #pragma unroll
   for (int h = 0; h < 2; ++h) ha[h] = h32_operand_bf16(4 * h + (t & 3), (t >> 2) & g);
-  // waves with fewer groups skip the rest (uniform per wave)
-  const int ng = ((nchunks + 31) >> 5) - w;  // groups of this wave: ceil(ng / 4)
+  // every group is transformed, past the row end too (on chunk 0's values,
+  // never counted or stored): without a branch per group the compiler keeps
+  // all loads at the top, one memory latency per row instead of one per group
   float v[P][2][8];
 #pragma unroll
   for (int p = 0; p < P; ++p) {
-    if (4 * p >= ng) break;
 #pragma unroll
     for (int a = 0; a < 2; ++a) {
       const bf16x8_t b = __builtin_bit_cast(bf16x8_t, xb[p][a]);
@@ -363,10 +363,8 @@ __global__ __launch_bounds__(kRowThreads) void rotate_quant_act_mfma_groups_kern
   {                                                      \
     const float cs = (rg & (H)) ? -1.f : 1.f;            \
     _Pragma("unroll") for (int p = 0; p < P; ++p) {      \
-      if (4 * p < ng) {                                  \
-        lane_butterfly8<MM>(v[p][0], cs);                \
-        lane_butterfly8<MM>(v[p][1], cs);                \
-      }                                                  \
+      lane_butterfly8<MM>(v[p][0], cs);                  \
+      lane_butterfly8<MM>(v[p][1], cs);                  \
     }                                                    \
     sigma *= cs;                                         \
   }
@@ -378,7 +376,6 @@ __global__ __launch_bounds__(kRowThreads) void rotate_quant_act_mfma_groups_kern
   if constexpr (LB == 10) {
 #pragma unroll
     for (int p = 0; p < P; ++p) {
-      if (4 * p >= ng) break;
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const float x0 = v[p][0][j], x1 = v[p][1][j];
@@ -390,7 +387,6 @@ __global__ __launch_bounds__(kRowThreads) void rotate_quant_act_mfma_groups_kern
   float mloc = 0.f;
 #pragma unroll
   for (int p = 0; p < P; ++p) {
-    if (4 * p >= ng) break;
 #pragma unroll
     for (int a = 0; a < 2; ++a)
       if (ok[p][a]) {
@@ -411,7 +407,6 @@ __global__ __launch_bounds__(kRowThreads) void rotate_quant_act_mfma_groups_kern
   uint32_t* xrow = reinterpret_cast<uint32_t*>(xq + m * (int64_t)(K / 2));
 #pragma unroll
   for (int p = 0; p < P; ++p) {
-    if (4 * p >= ng) break;
 #pragma unroll
     for (int a = 0; a < 2; ++a) {
       if (!ok[p][a]) continue;
@@ -560,17 +555,33 @@ hipError_t launch_rotate_quant_act(const void* X, int x_bf16, int64_t M, int64_t
                        reinterpret_cast<const uint16_t*>(X), nrm, xq, s_a, x_rot);
     return hipGetLastError();
   }
-  // the group kernel where it measured faster than the register-path kernel:
-  // blocks of 1024 in rows of more than 12288 elements (four groups per
-  // wave; 4096 x 14336: 42.7 against 52.2 us). With fewer groups per wave,
-  // or blocks of 256 (2048 x 11008: 17.1 against 14.7 us), its registers
-  // (120 at three groups) cost more resident workgroups than the matrix
-  // cores save.
-  if (x_bf16 && lb == 10 && K > 12288 && K <= QIFT_MAX_ROW &&
+  // bfloat16 rows with blocks of 256, 512 or 1024: the group kernel, with
+  // ceil(K / 4096) groups of 1024 elements per wave (one memory latency per
+  // row: every load is issued before the first transform). Against the
+  // register-path kernel: 4096 x 14336 (block 1024) 28.8 against 51.6 us,
+  // 2048 x 11008 (block 256) 13.1 against 14.5 us, 2048 x 4096 (block 1024)
+  // 6.4 against 7.7 us.
+  if (x_bf16 && lb >= 8 && lb <= 10 && K <= QIFT_MAX_ROW &&
       rotate_fast_ok(X, K, had_block, xq, x_rot)) {
-    hipLaunchKernelGGL((rotate_quant_act_mfma_groups_kernel<10, 4>), dim3((unsigned)M),
-                       dim3(kRowThreads), 0, s, reinterpret_cast<const uint16_t*>(X), (int)K, nrm,
-                       xq, s_a, x_rot);
+    const int P = (int)((K + 4095) / 4096);  // 1 .. 4
+#define QIFT_ROT_GROUPS(LBB, PP)                                                          \
+  hipLaunchKernelGGL((rotate_quant_act_mfma_groups_kernel<LBB, PP>), dim3((unsigned)M),  \
+                     dim3(kRowThreads), 0, s, reinterpret_cast<const uint16_t*>(X), (int)K, \
+                     nrm, xq, s_a, x_rot)
+#define QIFT_ROT_GROUPS_P(LBB)            \
+  if (P == 1) QIFT_ROT_GROUPS(LBB, 1);    \
+  else if (P == 2) QIFT_ROT_GROUPS(LBB, 2); \
+  else if (P == 3) QIFT_ROT_GROUPS(LBB, 3); \
+  else QIFT_ROT_GROUPS(LBB, 4);
+    if (lb == 8) {
+      QIFT_ROT_GROUPS_P(8)
+    } else if (lb == 9) {
+      QIFT_ROT_GROUPS_P(9)
+    } else {
+      QIFT_ROT_GROUPS_P(10)
+    }
+#undef QIFT_ROT_GROUPS_P
+#undef QIFT_ROT_GROUPS
     return hipGetLastError();
   }
   if (rotate_fast_ok(X, K, had_block, xq, x_rot)) {

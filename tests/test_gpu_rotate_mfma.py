@@ -112,9 +112,9 @@ def test_mfma_rotation_degenerate_rows():
 
 
 # ---------------------------------------------------------------------------
-# blocks of 256, 512 and 1024: rows of more than 12288 elements with blocks of
-# 1024 run the matrix-core group kernel (four groups of 1024 elements per
-# wave), the others the register-path kernel; both are held to the same bar
+# blocks of 256, 512 and 1024 (rotate_quant_act_mfma_groups_kernel): K up to
+# 16384, one to four groups of 1024 elements per wave, K = 11008 ending in a
+# half-filled group, K = 13312 with waves of three and four groups
 # ---------------------------------------------------------------------------
 
 def rotate_kb(Xt, Bk, want_rot=True):
