@@ -309,10 +309,11 @@ __global__ __launch_bounds__(kRowThreads) void rotate_quant_act_mfma4096_kernel(
 // bits 0 .. LB - 6 (at most 3) run between lanes by DPP and, for a block of
 // 1024, chunk bit 4 between the tiles in registers. The eight consecutive
 // outputs a lane holds per chunk are one word of codes, stored as they are.
-// Chunks past the row end (K % 1024 != 0, blocks of 256 only) are loaded
-// from chunk 0, never mix with valid ones (their tile half differs in chunk
-// bit 3, which no stage of a 256-block touches), and are neither counted in
-// the absmax nor stored.
+// Chunks past the row end (K % 1024 != 0: blocks of 256 or 512) are loaded
+// from chunk 0 and never mix with valid ones: a row ends on a block
+// boundary, and the stages of a 256-block stay inside a tile half (chunk
+// bit 3 fixed), those of a 512-block inside a tile. They are neither counted
+// in the absmax nor stored.
 template <int LB, int P>
 __global__ __launch_bounds__(kRowThreads) void rotate_quant_act_mfma_groups_kernel(
     const uint16_t* __restrict__ X, int K, float norm, uint8_t* __restrict__ xq,

@@ -113,8 +113,9 @@ def test_mfma_rotation_degenerate_rows():
 
 # ---------------------------------------------------------------------------
 # blocks of 256, 512 and 1024 (rotate_quant_act_mfma_groups_kernel): K up to
-# 16384, one to four groups of 1024 elements per wave, K = 11008 ending in a
-# half-filled group, K = 13312 with waves of three and four groups
+# 16384, one to four groups of 1024 elements per wave, rows ending in a
+# partial group (K = 11008 and 2816 with blocks of 256, 1536 and 11264 with
+# blocks of 512), K = 13312 with waves of three and four groups
 # ---------------------------------------------------------------------------
 
 def rotate_kb(Xt, Bk, want_rot=True):
@@ -134,7 +135,8 @@ def rotate_kb(Xt, Bk, want_rot=True):
 
 @pytest.mark.parametrize("M,Kk,Bk", [(2048, 11008, 256), (1024, 14336, 1024), (64, 4096, 512),
                                      (33, 2048, 1024), (5, 256, 256), (9, 16384, 256),
-                                     (7, 16384, 1024), (3, 13312, 1024)])
+                                     (7, 16384, 1024), (3, 13312, 1024), (5, 1536, 512),
+                                     (3, 11264, 512), (4, 2816, 256)])
 def test_mfma_group_rotation_rows(M, Kk, Bk):
     """bfloat16 rows with outlier channels: rotated values within 1e-5 of the
     float64 rotation on sampled rows, codes equal to the oracle's except at
