@@ -198,6 +198,17 @@ def unit_rotate_up_proj_input(q, torch, dev, steps):
         q.qift_rotate_quant_act(X, 4096, xq=xq, s_a=sa)
 
 
+def unit_rotate_down_proj_input(q, torch, dev, steps):
+    """Rotate + int4-quantize the down_proj input of a 2048-token prefill:
+    X [2048, 11008] bf16, blocks of 256 (the matrix-core group kernel)."""
+    import synth_inputs as si
+    X = si.device_activations(2048, 11008, seed=6, device=dev)
+    xq = torch.empty((2048, 5504), dtype=torch.uint8, device=dev)
+    sa = torch.empty((2048,), dtype=torch.float32, device=dev)
+    for _ in range(steps):
+        q.qift_rotate_quant_act(X, 256, xq=xq, s_a=sa)
+
+
 COPY_BYTES = 1 << 30
 
 
@@ -218,6 +229,7 @@ def unit_mfma_i8(q, torch, dev, steps):
 
 
 UNITS = {"prefill_up_proj": unit_prefill_up_proj, "prefill_down_proj": unit_prefill_down_proj,
+         "rotate_down_proj_input": unit_rotate_down_proj_input,
          "rotate_up_proj_input": unit_rotate_up_proj_input,
          "copy": unit_copy, "mfma_i8": unit_mfma_i8, "kv4": unit_kv4, "attention": unit_attention,
          "gptq": unit_gptq, "decode_layer_by_layer": unit_decode_layer_by_layer,
