@@ -218,7 +218,13 @@ qift_status qift_rotate_quant_act(const void* X, qift_dtype x_dtype, int64_t M, 
  * same online activation path; meant for the inputs of all linears of a
  * decode step, a few token rows each, which cannot fill the GPU one by one).
  * Each descriptor has the meaning, limits and results of the arguments of
- * qift_rotate_quant_act; every descriptor is validated before anything is
+ * qift_rotate_quant_act (the shared launch sums every butterfly stage in
+ * float32 registers, where qift_rotate_quant_act sums the first five stages
+ * of bfloat16 rows with blocks of 256 or more on the matrix cores: the two
+ * agree bit for bit whenever those 32-element sums are exact in float32,
+ * and otherwise differ by float32 rounding in the rotated values, within the
+ * rotation's tolerance, and in a code only where such a difference meets a
+ * rounding near-tie); every descriptor is validated before anything is
  * launched. Descriptors with K % 16 == 0, had_block >= 16 and 16-byte aligned
  * X, xq (and x_rot if given) share one launch with one workgroup per row; any
  * other descriptor gets a launch of its own. Outputs of different
@@ -290,10 +296,15 @@ qift_status qift_w2a4_linear_ex(const uint8_t* xq, const float* s_a, int64_t M, 
  * is not yet quantized: exactly qift_rotate_quant_act(X, x_dtype, M, K,
  * had_block, xq, s_a, NULL) followed by qift_w2a4_linear_ex(xq, s_a, M, K,
  * codes, scales, scale_dtype, levels, level_table, N, Y, y_dtype), with the
- * same results bit for bit (xq and s_a are written too). A single token row
- * (M = 1) with K % 16 == 0, had_block >= 16 and 16-byte aligned X and xq runs
- * as one launch in which every workgroup rotates and quantizes the row itself
- * while its weights stream in; other calls run the two launches.
+ * same results (xq and s_a are written too). A single token row (M = 1) with
+ * K % 16 == 0, had_block >= 16 and 16-byte aligned X and xq runs as one
+ * launch in which every workgroup rotates and quantizes the row itself while
+ * its weights stream in (summing every butterfly stage in float32 registers:
+ * for a bfloat16 row with a block of 256 or more, which qift_rotate_quant_act
+ * rotates partly on the matrix cores, the results agree bit for bit whenever
+ * the 32-element sums of the first five stages are exact in float32, and
+ * otherwise may differ in a code only where a float32 rounding difference
+ * meets a rounding near-tie); other calls run the two launches.
  *   X, x_dtype, had_block, xq, s_a  as qift_rotate_quant_act (x_rot omitted)
  *   the rest                        as qift_w2a4_linear_ex
  * K must satisfy both calls' limits (a multiple of 64, at most
